@@ -1,0 +1,361 @@
+"""Pins of the CPU oracle against what the format, the mathematics and the
+pages fix -- never against the oracle itself.  No GPU needed.
+
+Each test names the plausible oracle mistake it would catch.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from oracle.chunked import gdn_chunked
+from fp8_state_qat_amd import inputs as gi
+
+
+# ---------------------------------------------------------------------------
+# E4M3 rounding
+# ---------------------------------------------------------------------------
+def _golden_e4m3(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "e4m3_cases.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            y, code, val = line.split()
+            rows.append((float(y), int(code, 16), float(val)))
+    return rows
+
+
+def test_e4m3_golden_cases(golden_dir):
+    """Hand-derived cases: ties to even code, saturation at 448, subnormals,
+    the sign bit.  Catches ties-away rounding or a wrong maximum."""
+    rows = _golden_e4m3(golden_dir)
+    y = np.array([r[0] for r in rows], dtype=np.float32)
+    codes = orc.e4m3_encode(y)
+    for (yy, c, val), got in zip(rows, codes):
+        assert got == c, (yy, hex(c), hex(got))
+        dec = orc.e4m3_decode(np.array([got], np.uint8))[0]
+        assert dec == val and np.signbit(dec) == np.signbit(val), (yy, dec, val)
+
+
+def _grid_f64():
+    """E4M3FN non-negative finite values from the format definition."""
+    vals = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        vals.append((m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def _numpy_bruteforce(y):
+    grid = _grid_f64()
+    a = np.minimum(np.abs(y.astype(np.float64)), 448.0)
+    d = np.abs(a[:, None] - grid[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among equally near codes prefer the even one
+    even = cand & ((np.arange(127) & 1) == 0)[None, :]
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def _e4m3_probe_values():
+    grid = _grid_f64()
+    mids = (grid[1:] + grid[:-1]) / 2
+    pts = np.concatenate([grid, mids, [464.0, 470.0, 2 ** -10, 1e-30, 0.0]]).astype(np.float32)
+    nb = [pts]
+    for k in (1, 2, 3):
+        nb.append(np.nextafter(pts, np.float32(np.inf)))
+        nb.append(np.nextafter(pts, np.float32(0)))
+        pts = nb[-2]
+    rng = np.random.default_rng(7)
+    rnd = (np.exp2(rng.uniform(-14, np.log2(460), 200_000))).astype(np.float32)
+    allv = np.concatenate(nb + [rnd])
+    return np.concatenate([allv, -allv])
+
+
+def test_e4m3_bisection_matches_bruteforce():
+    """The oracle's bisection equals an exhaustive nearest search (written
+    here independently in numpy) at every grid point, every midpoint, their
+    fp32 neighbours, and 400k random values."""
+    y = _e4m3_probe_values()
+    np.testing.assert_array_equal(orc.e4m3_encode(y), _numpy_bruteforce(y))
+
+
+def test_e4m3_c_bruteforce_subset():
+    y = _e4m3_probe_values()[::97]
+    np.testing.assert_array_equal(orc.e4m3_encode(y), orc.e4m3_encode_bruteforce(y))
+
+
+def test_e4m3_matches_torch_cast():
+    """torch's float8_e4m3fn cast (round to nearest even) agrees wherever it
+    is finite (|y| <= 464)."""
+    y = _e4m3_probe_values()
+    y = y[np.abs(y) <= 464]
+    t = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(orc.e4m3_encode(y), t)
+
+
+# ---------------------------------------------------------------------------
+# Tile QDQ
+# ---------------------------------------------------------------------------
+def test_qdq_zero_tile():
+    x = np.zeros((1, 64, 32), np.float32)
+    out, sc, codes = orc.qdq_states(x)
+    assert np.all(out == 0) and sc[0, 0] == 1.0 and np.all(codes == 0)
+
+
+def test_qdq_scale_is_amax_over_448_per_tile():
+    """One fp32 scale per 64 value rows x all key columns, amax/448 (fp32
+    division).  Catches a per-tensor scale, a per-row scale, or 240."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((3, 128, 64)).astype(np.float32)
+    x[1, 64:] *= 1000.0
+    out, sc, codes = orc.qdq_states(x)
+    for s in range(3):
+        for j in range(2):
+            tile = x[s, 64 * j:64 * (j + 1)]
+            amax = np.float32(np.abs(tile).max())
+            assert sc[s, j] == np.float32(amax / np.float32(448.0))
+            # the largest element lands exactly on the largest code
+            i = np.unravel_index(np.abs(tile).argmax(), tile.shape)
+            assert codes[s, 64 * j + i[0], i[1]] & 0x7F == 0x7E
+
+
+def test_qdq_already_e4m3_tile_is_unchanged():
+    """A tile X = C * 2^e with every C on the E4M3 grid and max |C| = 448 is
+    returned bitwise unchanged (scale 2^e)."""
+    rng = np.random.default_rng(2)
+    grid = _grid_f64()
+    C = rng.choice(grid, size=(2, 64, 128)) * rng.choice([-1.0, 1.0], size=(2, 64, 128))
+    C[:, 0, 0] = 448.0
+    for e in (-20, -3, 0, 5):
+        X = (C * 2.0 ** e).astype(np.float32)
+        out, sc, _ = orc.qdq_states(X)
+        assert np.all(sc == np.float32(2.0 ** e))
+        np.testing.assert_array_equal(out.view(np.uint32), X.view(np.uint32))
+
+
+def test_qdq_idempotent_codes():
+    """QDQ(QDQ(x)) keeps the same codes and its values move by at most one
+    fp32 ulp (only the rounding of code * scale can differ)."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((4, 64, 128)) * rng.uniform(0.01, 100, (4, 1, 1))).astype(np.float32)
+    y, s1, c1 = orc.qdq_states(x)
+    z, s2, c2 = orc.qdq_states(y)
+    np.testing.assert_array_equal(c1, c2)
+    ulp = np.spacing(np.abs(y).astype(np.float32))
+    assert np.all(np.abs(z - y) <= ulp)
+
+
+def test_qdq_power_of_two_and_sign():
+    """QDQ(2^e x) = 2^e QDQ(x) and QDQ(-x) = -QDQ(x), bitwise."""
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((2, 64, 64)).astype(np.float32)
+    y, _, _ = orc.qdq_states(x)
+    y8, _, _ = orc.qdq_states(x * np.float32(8.0))
+    yn, _, _ = orc.qdq_states(-x)
+    np.testing.assert_array_equal(y8, y * np.float32(8.0))
+    np.testing.assert_array_equal(yn, -y)
+
+
+def test_qdq_relative_error_bound():
+    """Every element moves by at most half an E4M3 step of its binade times
+    the scale (relative 2^-4 for normals, absolute 2^-10 * scale below)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((8, 64, 128)).astype(np.float32)
+    y, sc, _ = orc.qdq_states(x)
+    s = np.repeat(sc, 64, axis=1)[..., None]
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(np.abs(y - x) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# Recurrence
+# ---------------------------------------------------------------------------
+def test_recurrence_hand_worked_two_tokens(golden_dir):
+    """Hand-worked two-token examples (scalar and per-key-channel gate).
+    Catches a transposed state, a wrong sign in the delta correction, decay
+    after instead of before the correction, or the output taken before the
+    update."""
+    with open(os.path.join(golden_dir, "gdn_two_token.json")) as f:
+        gold = json.load(f)
+    for key in ("scalar", "per_channel"):
+        c = gold[key]
+        a = np.array(c["a"], dtype=np.float64)
+        r = orc.gdn_sequence(np.array(c["q"]), np.array(c["k"]), np.array(c["v"]),
+                             np.array(c["beta"]), np.log(a), flags=0)
+        np.testing.assert_allclose(r["o"], np.array(c["o"]), rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(r["S"], np.array(c["S"]), rtol=1e-14, atol=1e-14)
+
+
+def _seq(L, dk, dv, per_channel=False, seed=0, g_scale=0.1, io=gi.F32):
+    w = gi.make_packed([L], 1, dk, dv, io_dtype=io, per_channel=per_channel,
+                       g_scale=g_scale, seed=seed)
+    g = w.f64("g")[:, 0]
+    return (w.f64("q")[:, 0], w.f64("k")[:, 0], w.f64("v")[:, 0], w.f64("beta")[:, 0], g)
+
+
+def test_one_token_closed_form():
+    """From the zero state, o_1 = beta (k.q) v and S_1 = beta v k^T."""
+    q, k, v, b, g = _seq(1, 64, 64, seed=11)
+    r = orc.gdn_sequence(q, k, v, b, g, flags=0)
+    np.testing.assert_allclose(r["o"][0], b[0] * (k[0] @ q[0]) * v[0], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(r["S"], b[0] * np.outer(v[0], k[0]), rtol=1e-13, atol=1e-15)
+
+
+def test_one_chunk_qdq_only_touches_final_state():
+    """Within one chunk (L <= 64) the outputs are the same with QDQ on or
+    off, and the final state with QDQ is QDQ of the final state without."""
+    q, k, v, b, g = _seq(50, 64, 128, seed=12)
+    off = orc.gdn_sequence(q, k, v, b, g, flags=0)
+    on = orc.gdn_sequence(q, k, v, b, g, flags=orc.QDQ_CHUNK)
+    np.testing.assert_array_equal(off["o"], on["o"])
+    want, _, _ = orc.qdq_states(off["S"].astype(np.float32))
+    np.testing.assert_array_equal(on["S"], want.astype(np.float64))
+
+
+def test_beta_zero_keeps_zero_state():
+    q, k, v, b, g = _seq(130, 64, 64, seed=13)
+    r = orc.gdn_sequence(q, k, v, np.zeros_like(b), g)
+    assert np.all(r["o"] == 0) and np.all(r["S"] == 0)
+
+
+def test_full_forgetting_gate():
+    """a_t = 0 (g = -inf): each token sees only itself, o_t = beta_t (k_t.q_t) v_t."""
+    q, k, v, b, g = _seq(70, 64, 64, seed=14)
+    r = orc.gdn_sequence(q, k, v, b, np.full_like(g, -np.inf), flags=0)
+    want = (b * np.einsum("tc,tc->t", k, q))[:, None] * v
+    np.testing.assert_allclose(r["o"], want, rtol=1e-13, atol=1e-15)
+
+
+def test_delta_rule_overwrite():
+    """beta = 1, a = 1, unit basis keys: S k_t = v_t after the write, so with
+    q_t = k_t the output is v_t (the delta rule replaces the value stored
+    under a key).  Catches a missing delta correction (o would accumulate)."""
+    rng = np.random.default_rng(15)
+    L, d = 40, 64
+    idx = rng.integers(0, d, L)
+    k = np.eye(d)[idx]
+    v = rng.standard_normal((L, d))
+    r = orc.gdn_sequence(k, k, v, np.ones(L), np.zeros(L), flags=0)
+    # exact in real arithmetic; old + (new - old) rounds by at most an ulp
+    np.testing.assert_allclose(r["o"], v, rtol=0, atol=4 * np.spacing(np.abs(v).max()))
+
+
+def test_orthogonal_keys_sum():
+    """Distinct basis keys, a = 1: S_{t-1} k_t = 0, so S_L = sum beta v k^T."""
+    rng = np.random.default_rng(16)
+    L, d = 64, 64
+    k = np.eye(d)[rng.permutation(d)[:L]]
+    v = rng.standard_normal((L, d))
+    b = rng.uniform(0.1, 0.9, L)
+    r = orc.gdn_sequence(rng.standard_normal((L, d)), k, v, b, np.zeros(L), flags=0)
+    np.testing.assert_allclose(r["S"], (b[:, None] * v).T @ k, rtol=1e-15, atol=1e-15)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunked_form_equals_recurrence_qdq_off(per_channel, chunk):
+    """The chunk-parallel form (exact solve, WY/UT W and U) is an identity of
+    the recurrence: agreement to fp64 rounding, ragged last chunk included."""
+    q, k, v, b, g = _seq(203, 64, 64, per_channel=per_channel, seed=17,
+                         g_scale=0.05 if per_channel else 0.1)
+    rec = orc.gdn_sequence(q, k, v, b, g, flags=0)
+    chk = gdn_chunked(q, k, v, b, g, chunk=chunk, qdq=False)
+    for key in ("o", "S"):
+        rel = np.linalg.norm(chk[key] - rec[key]) / np.linalg.norm(rec[key])
+        assert rel < 1e-12, (key, rel)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_chunked_form_equals_recurrence_qdq_on(per_channel):
+    """With state QDQ at every 64-token boundary (and at t = L) both forms
+    place the QDQ at the same points: outputs and final state agree."""
+    q, k, v, b, g = _seq(203, 64, 128, per_channel=per_channel, seed=18,
+                         g_scale=0.05 if per_channel else 0.1)
+    rec = orc.gdn_sequence(q, k, v, b, g, flags=orc.QDQ_CHUNK)
+    chk = gdn_chunked(q, k, v, b, g, chunk=64, qdq=True)
+    for key in ("o", "S"):
+        rel = np.linalg.norm(chk[key] - rec[key]) / np.linalg.norm(rec[key])
+        assert rel < 1e-10, (key, rel)
+    # and QDQ really happened: off differs
+    off = orc.gdn_sequence(q, k, v, b, g, flags=0)
+    assert np.linalg.norm(off["o"] - rec["o"]) / np.linalg.norm(rec["o"]) > 1e-4
+
+
+def test_power_of_two_and_sign_invariance_with_qdq():
+    """S is linear in v and QDQ commutes with power-of-two scaling and
+    negation, so o(2^e v) = 2^e o(v) and o(-v) = -o(v) bitwise."""
+    q, k, v, b, g = _seq(150, 64, 64, seed=19)
+    r = orc.gdn_sequence(q, k, v, b, g)
+    r4 = orc.gdn_sequence(q, k, 4.0 * v, b, g)
+    rn = orc.gdn_sequence(q, k, -v, b, g)
+    np.testing.assert_array_equal(r4["o"], 4.0 * r["o"])
+    np.testing.assert_array_equal(rn["o"], -r["o"])
+
+
+def test_handoff_and_per_write_qdq_composition():
+    """Write QDQ with a prefix P < L equals: prefix without internal QDQ,
+    QDQ at the handoff, then one recurrent step per token, each quantizing
+    the state it stores, each output taken before that QDQ."""
+    q, k, v, b, g = _seq(100, 64, 64, seed=20)
+    P = 70
+    full = orc.gdn_sequence(q, k, v, b, g, prefix_len=P, flags=orc.QDQ_WRITE)
+    pre = orc.gdn_sequence(q[:P], k[:P], v[:P], b[:P], g[:P], flags=0)
+    S, _, _ = orc.qdq_states(pre["S"].astype(np.float32))
+    S = S.astype(np.float64)
+    np.testing.assert_array_equal(full["o"][:P], pre["o"])
+    for t in range(P, 100):
+        step = orc.gdn_sequence(q[t:t + 1], k[t:t + 1], v[t:t + 1], b[t:t + 1], g[t:t + 1],
+                                prefix_len=0, flags=orc.QDQ_WRITE, S0=S)
+        np.testing.assert_array_equal(full["o"][t], step["o"][0])
+        S = step["S"]
+    np.testing.assert_array_equal(full["S"], S)
+
+
+def test_split_resume_matches_single_call():
+    """Running [0, P) then [P, L) from the returned state (P a multiple of 64,
+    boundary QDQ on) equals one call over [0, L)."""
+    q, k, v, b, g = _seq(300, 64, 64, seed=21)
+    whole = orc.gdn_sequence(q, k, v, b, g, flags=orc.QDQ_CHUNK)
+    a = orc.gdn_sequence(q[:128], k[:128], v[:128], b[:128], g[:128], flags=orc.QDQ_CHUNK)
+    c = orc.gdn_sequence(q[128:], k[128:], v[128:], b[128:], g[128:], flags=orc.QDQ_CHUNK,
+                         S0=a["S"])
+    np.testing.assert_array_equal(whole["o"], np.concatenate([a["o"], c["o"]]))
+    np.testing.assert_array_equal(whole["S"], c["S"])
+
+
+def test_boundary_record():
+    """Recorded boundaries: one per 64 tokens plus the ragged end; post is the
+    QDQ of pre; the final post is the returned state."""
+    q, k, v, b, g = _seq(200, 64, 64, seed=22)
+    r = orc.gdn_sequence(q, k, v, b, g, flags=orc.QDQ_CHUNK, record=True)
+    assert r["n_bounds"] == 4
+    for i in range(4):
+        want, sc, _ = orc.qdq_states(r["bound_pre"][i].astype(np.float32))
+        np.testing.assert_array_equal(r["bound_post"][i], want.astype(np.float64))
+        np.testing.assert_array_equal(r["scales"][i], sc)
+    np.testing.assert_array_equal(r["bound_post"][-1], r["S"])
+
+
+def test_packed_matches_per_sequence():
+    """Packed varlen with padding: each sequence's rows equal a standalone
+    run; padding rows are zero."""
+    w = gi.make_packed([70, 5, 130], 2, 64, 64, io_dtype=gi.F32, pads=[3, 0, 10], seed=23)
+    res = orc.gdn_packed(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("beta"), w.f64("g"),
+                         w.cu_seqlens, seq_lens=w.seq_lens)
+    cu = w.cu_seqlens
+    for n in range(3):
+        for h in range(2):
+            s, L = cu[n], w.seq_lens[n]
+            r = orc.gdn_sequence(w.f64("q")[s:s + L, h], w.f64("k")[s:s + L, h],
+                                 w.f64("v")[s:s + L, h], w.f64("beta")[s:s + L, h],
+                                 w.f64("g")[s:s + L, h])
+            np.testing.assert_array_equal(res["o"][s:s + L, h], r["o"])
+            np.testing.assert_array_equal(res["S"][n, h], r["S"])
+            assert np.all(res["o"][s + L:cu[n + 1], h] == 0)
