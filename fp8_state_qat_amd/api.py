@@ -1,0 +1,111 @@
+"""torch-facing binding of the C ABI: argument marshalling only.
+
+Every function takes device tensors (torch is used for device memory and the
+current stream), turns them into pointers and sizes, and calls one entry
+point of libgdn.so on torch's current stream.  All arithmetic runs in the
+HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import GDN_BF16, GDN_F32, GDN_QDQ_CHUNK, GDN_QDQ_WRITE, GdnDebug, GdnShape
+
+_DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
+              initial_state=None, qdq_flags=GDN_QDQ_CHUNK | GDN_QDQ_WRITE, o_dtype=None,
+              out=None, final_state=None, debug=None):
+    """gdn_chunk_fwd.  q, k: [T, H, dk]; v: [T, H, dv] (fp32 or bf16); beta:
+    [T, H] fp32; g: [T, H] or [T, H, dk] fp32; cu_seqlens: [N+1] int32.
+    debug: optional dict with device tensors bound_offsets, bound_pre,
+    bound_post, scales.  Returns (o, final_state)."""
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if q.dtype != k.dtype or v.dtype != k.dtype or k.dtype not in _DT:
+        raise ValueError("q, k, v must share one dtype: float32 or bfloat16")
+    o_dtype = k.dtype if o_dtype is None else o_dtype
+    for name, t, dt in (("q", q, None), ("k", k, None), ("v", v, None), ("beta", beta, torch.float32),
+                        ("g", g, torch.float32), ("cu_seqlens", cu_seqlens, torch.int32),
+                        ("seq_lens", seq_lens, torch.int32), ("prefix_lens", prefix_lens, torch.int32),
+                        ("initial_state", initial_state, torch.float32)):
+        _dev(t, name, dt)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=o_dtype, device=k.device)
+    if final_state is None:
+        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=k.device)
+    _dev(out, "out", o_dtype)
+    _dev(final_state, "final_state", torch.float32)
+    shape = GdnShape(N, H, dk, dv, T, _DT[k.dtype], _DT[o_dtype], 1 if g.dim() == 3 else 0,
+                     int(qdq_flags))
+    dbg = None
+    if debug is not None:
+        dbg = GdnDebug(*(_ptr(debug.get(key)) for key in ("bound_offsets", "bound_pre",
+                                                          "bound_post", "scales")))
+    st = _lib.lib().gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                  _ptr(g), _ptr(cu_seqlens), _ptr(seq_lens), _ptr(prefix_lens),
+                                  _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                  ctypes.byref(dbg) if dbg is not None else None, _stream())
+    _lib.check(st)
+    return out, final_state
+
+
+def state_qdq(x, out=None, scales=None, want_scales=True):
+    """gdn_state_qdq on x [..., dv, dk] fp32.  Returns (out, scales [..., dv/64])."""
+    _dev(x, "x", torch.float32)
+    dv, dk = x.shape[-2], x.shape[-1]
+    n = x.numel() // (dv * dk) if x.numel() else 0
+    if out is None:
+        out = torch.empty_like(x)
+    if scales is None and want_scales:
+        scales = torch.empty(x.shape[:-2] + (dv // 64,), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    st = _lib.lib().gdn_state_qdq(_ptr(x), _ptr(out), _ptr(scales), n, dv, dk, _stream())
+    _lib.check(st)
+    return out, scales
+
+
+def decode_step(q, k, v, beta, g, state, *, qdq=True, o=None, o_dtype=None, state_pre=None,
+                scales=None):
+    """gdn_decode_step.  q, k: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; g: [N, H]
+    or [N, H, dk]; state [N, H, dv, dk] fp32 updated in place.  Returns o."""
+    N, H, dk = k.shape
+    dv = v.shape[2]
+    o_dtype = k.dtype if o_dtype is None else o_dtype
+    for name, t, dt in (("q", q, None), ("k", k, None), ("v", v, None), ("beta", beta, torch.float32),
+                        ("g", g, torch.float32), ("state", state, torch.float32),
+                        ("state_pre", state_pre, torch.float32), ("scales", scales, torch.float32)):
+        _dev(t, name, dt)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=o_dtype, device=k.device)
+    shape = GdnShape(N, H, dk, dv, N, _DT[k.dtype], _DT[o_dtype], 1 if g.dim() == 3 else 0,
+                     GDN_QDQ_WRITE if qdq else 0)
+    st = _lib.lib().gdn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                    _ptr(g), _ptr(state), _ptr(o), _ptr(state_pre), _ptr(scales),
+                                    _stream())
+    _lib.check(st)
+    return o

@@ -1,0 +1,157 @@
+// gdn_abi.hip -- the C ABI declared in include/gdn.h: host-side argument
+// checks (run before any launch, never touching device memory), a per-device
+// gfx950 capability cache, and dispatch to the launch functions.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "gdn.h"
+#include "gdn_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status_t fail(gdn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+gdn_status_t check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(GDN_ERR_DEVICE, "no current HIP device");
+  if (dev >= kMaxDevices) return fail(GDN_ERR_DEVICE, "device index %d out of range", dev);
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(GDN_ERR_DEVICE, "hipGetDeviceProperties failed on device %d", dev);
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(GDN_ERR_DEVICE, "device %d is not gfx950 (MI355X)", dev);
+  return GDN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+gdn_status_t check_shape(const gdn_shape_t* s, bool decode) {
+  if (s == nullptr) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
+  if (s->n_seqs < 1) return fail(GDN_ERR_INVALID_ARG, "n_seqs must be >= 1 (got %d)", s->n_seqs);
+  if (s->n_heads < 1) return fail(GDN_ERR_INVALID_ARG, "n_heads must be >= 1 (got %d)", s->n_heads);
+  if (s->dk < 1 || s->dv < 1) return fail(GDN_ERR_INVALID_ARG, "dk, dv must be positive");
+  if (s->dv % 64 != 0) return fail(GDN_ERR_INVALID_ARG, "dv must be a multiple of 64 (got %d)", s->dv);
+  if (s->dk != 64 && s->dk != 128) return fail(GDN_ERR_UNSUPPORTED, "dk must be 64 or 128 (got %d)", s->dk);
+  if (s->dv > 256) return fail(GDN_ERR_UNSUPPORTED, "dv above 256 is not supported (got %d)", s->dv);
+  if (s->total_tokens < 0) return fail(GDN_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if ((s->io_dtype != GDN_F32 && s->io_dtype != GDN_BF16) ||
+      (s->o_dtype != GDN_F32 && s->o_dtype != GDN_BF16))
+    return fail(GDN_ERR_INVALID_ARG, "io_dtype and o_dtype must be GDN_F32 or GDN_BF16");
+  if (s->gate_per_channel != 0 && s->gate_per_channel != 1)
+    return fail(GDN_ERR_INVALID_ARG, "gate_per_channel must be 0 or 1");
+  if (s->qdq_flags & ~(GDN_QDQ_CHUNK | GDN_QDQ_WRITE))
+    return fail(GDN_ERR_INVALID_ARG, "unknown qdq_flags bits 0x%x", s->qdq_flags);
+  const int64_t blocks = (int64_t)s->n_seqs * s->n_heads * (s->dv / 64);
+  if (blocks >= (int64_t)1 << 31) return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, head, tile) units");
+  if (decode && s->total_tokens != s->n_seqs)
+    return fail(GDN_ERR_INVALID_ARG, "decode: total_tokens must equal n_seqs");
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status_t status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_DEVICE: return "GDN_ERR_DEVICE";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char* gdn_last_error(void) { return g_err; }
+
+gdn_status_t gdn_state_qdq(const float* in, float* out, float* scales, int64_t n_states,
+                           int32_t dv, int32_t dk, void* stream) {
+  g_err[0] = 0;
+  if (n_states < 0) return fail(GDN_ERR_INVALID_ARG, "n_states must be >= 0");
+  if (dv < 64 || dv % 64 != 0) return fail(GDN_ERR_INVALID_ARG, "dv must be a positive multiple of 64");
+  if (dk < 4 || dk % 4 != 0) return fail(GDN_ERR_INVALID_ARG, "dk must be a positive multiple of 4");
+  if (dk > 256) return fail(GDN_ERR_UNSUPPORTED, "dk above 256 is not supported");
+  const int64_t tiles = n_states * (dv / 64);
+  if (tiles >= (int64_t)1 << 31) return fail(GDN_ERR_UNSUPPORTED, "too many tiles");
+  if (n_states > 0) {
+    if (in == nullptr || out == nullptr) return fail(GDN_ERR_INVALID_ARG, "in/out is NULL");
+    if (!aligned(in, 16) || !aligned(out, 16)) return fail(GDN_ERR_INVALID_ARG, "in/out must be 16-byte aligned");
+  }
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  hipError_t e = gdn::launch_state_qdq(in, out, scales, tiles, dk, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void* k,
+                             const void* v, const float* beta, const float* g, float* state,
+                             void* o, float* state_pre, float* scales, void* stream) {
+  g_err[0] = 0;
+  gdn_status_t st = check_shape(shape, true);
+  if (st != GDN_OK) return st;
+  if (!q || !k || !v || !beta || !g || !state || !o)
+    return fail(GDN_ERR_INVALID_ARG, "q, k, v, beta, g, state and o must be non-NULL");
+  const uintptr_t ea = shape->io_dtype == GDN_BF16 ? 8 : 16;
+  if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, 4) || !aligned(state, 16) ||
+      (state_pre && !aligned(state_pre, 16)) || !aligned(beta, 4) || !aligned(g, 4) ||
+      !aligned(o, shape->o_dtype == GDN_BF16 ? 2 : 4))
+    return fail(GDN_ERR_INVALID_ARG, "misaligned buffer");
+  st = check_device();
+  if (st != GDN_OK) return st;
+  hipError_t e = gdn::launch_decode_step(*shape, q, k, v, beta, g, state, o, state_pre, scales,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, const int32_t* cu_seqlens,
+                           const int32_t* seq_lens, const int32_t* prefix_lens,
+                           const float* initial_state, void* o, float* final_state,
+                           const gdn_debug_t* debug, void* stream) {
+  g_err[0] = 0;
+  gdn_status_t st = check_shape(shape, false);
+  if (st != GDN_OK) return st;
+  if (!cu_seqlens || !final_state) return fail(GDN_ERR_INVALID_ARG, "cu_seqlens and final_state must be non-NULL");
+  if (shape->total_tokens > 0 && (!q || !k || !v || !beta || !g || !o))
+    return fail(GDN_ERR_INVALID_ARG, "q, k, v, beta, g and o must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(final_state, 16) || (initial_state && !aligned(initial_state, 16)) ||
+      !aligned(beta, 4) || !aligned(g, 4) || !aligned(cu_seqlens, 4))
+    return fail(GDN_ERR_INVALID_ARG, "misaligned buffer (q, k, v, o and states need 16 bytes)");
+  if (debug && (debug->bound_pre || debug->bound_post || debug->scales) && !debug->bound_offsets)
+    return fail(GDN_ERR_INVALID_ARG, "debug record needs bound_offsets");
+  if (shape->io_dtype == GDN_F32 && shape->dk != 64)
+    return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs are supported with dk = 64 only");
+  if (shape->io_dtype == GDN_F32 && shape->gate_per_channel)
+    return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs with a per-key-channel gate are not supported");
+  st = check_device();
+  if (st != GDN_OK) return st;
+  hipError_t e = gdn::launch_chunk_fwd(*shape, q, k, v, beta, g, cu_seqlens, seq_lens, prefix_lens,
+                                       initial_state, o, final_state, debug, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(GDN_ERR_UNSUPPORTED, "configuration not supported");
+  if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+}  // extern "C"

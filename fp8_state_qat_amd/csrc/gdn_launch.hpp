@@ -1,0 +1,25 @@
+// gdn_launch.hpp -- internal launch functions behind the C ABI (gdn_abi.hip).
+// Arguments arrive already validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+hipError_t launch_state_qdq(const float* in, float* out, float* scales, int64_t n_tiles, int dk,
+                            hipStream_t stream);
+
+hipError_t launch_decode_step(const gdn_shape_t& s, const void* q, const void* k, const void* v,
+                              const float* beta, const float* g, float* state, void* o,
+                              float* state_pre, float* scales, hipStream_t stream);
+
+hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, const void* v,
+                            const float* beta, const float* g, const int32_t* cu_seqlens,
+                            const int32_t* seq_lens, const int32_t* prefix_lens,
+                            const float* initial_state, void* o, float* final_state,
+                            const gdn_debug_t* debug, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,64 @@
+// gdn_qdq.hip -- standalone per-tile state QDQ (fake quantize-dequantize of
+// fp32 states to FP8-E4M3 with one scalar scale per tile of 64 value rows x
+// all key columns; Model-Optimizer #2497 "What does this PR do?").
+//
+// One workgroup of 256 threads per tile.  The tile (64 * dk fp32, 32 KiB at
+// dk = 128) is read once into registers with coalesced 16-byte loads, its
+// amax reduced in a fixed tree, then quantized and written back.  Memory
+// bound: 8 bytes of HBM traffic per state element.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+template <int V4>  // float4 per thread = 64 * dk / 4 / 256 = dk / 16
+__global__ __launch_bounds__(kThreads) void state_qdq_kernel(const float* in,
+                                                            float* out, float* __restrict__ scales,
+                                                            int dk) {
+  __shared__ float red[4];
+  const int64_t tile = blockIdx.x;
+  const int n4 = 16 * dk;  // float4 per tile
+  const float4* src = reinterpret_cast<const float4*>(in) + tile * n4;
+  float4* dst = reinterpret_cast<float4*>(out) + tile * n4;
+  float4 x[V4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    int idx = threadIdx.x + kThreads * j;
+    if (idx < n4) {
+      x[j] = src[idx];
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[j].x), fabsf(x[j].y)),
+                               fmaxf(fabsf(x[j].z), fabsf(x[j].w))));
+    }
+  }
+  amax = block_max(amax, red);
+  const float s = qdq_scale(amax);
+#pragma unroll
+  for (int j = 0; j < V4; ++j) {
+    int idx = threadIdx.x + kThreads * j;
+    if (idx < n4) {
+      float4 y;
+      y.x = qdq_value(x[j].x, s);
+      y.y = qdq_value(x[j].y, s);
+      y.z = qdq_value(x[j].z, s);
+      y.w = qdq_value(x[j].w, s);
+      dst[idx] = y;
+    }
+  }
+  if (scales != nullptr && threadIdx.x == 0) scales[tile] = s;
+}
+
+hipError_t launch_state_qdq(const float* in, float* out, float* scales, int64_t n_tiles, int dk,
+                            hipStream_t stream) {
+  if (n_tiles == 0) return hipSuccess;
+  dim3 grid((unsigned)n_tiles), block(kThreads);
+  if (dk <= 64)
+    hipLaunchKernelGGL(state_qdq_kernel<4>, grid, block, 0, stream, in, out, scales, dk);
+  else if (dk <= 128)
+    hipLaunchKernelGGL(state_qdq_kernel<8>, grid, block, 0, stream, in, out, scales, dk);
+  else
+    hipLaunchKernelGGL(state_qdq_kernel<16>, grid, block, 0, stream, in, out, scales, dk);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -179,3 +179,18 @@ def decode_tokens(n_seqs, H, dk, dv, steps, *, io_dtype=BF16, per_channel=False,
                         v=_round_io(v, io_dtype), beta=beta.astype(np.float32),
                         g=g.astype(np.float32)))
     return out
+
+
+def to_torch(a, device):
+    """numpy input array -> torch tensor on device (uint16 bf16 bits become
+    torch.bfloat16 without any rounding)."""
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def device_tensors(w: Workload, device="cuda"):
+    """All inputs of a workload as device tensors (dict)."""
+    return {name: to_torch(getattr(w, name), device)
+            for name in ("q", "k", "v", "beta", "g", "cu_seqlens", "seq_lens", "prefix_lens")}

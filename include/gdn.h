@@ -1,0 +1,158 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule library with dynamic
+ * per-tile FP8-E4M3 fake quantize-dequantize (QDQ) of the recurrent state.
+ *
+ * The method (the pages: NVIDIA Model-Optimizer pull requests #2497 "GDN
+ * state/W QAT foundation", #2519 "Torch GDN/KDA decode QAT", #2506 "KDA
+ * prefill numerical emulation"):
+ *   - Gated delta rule, per sequence n and head h, state S (dv x dk, row =
+ *     value channel, column = key channel), token t:
+ *         S <- S * a_t        (a_t = exp(g_t); or S * diag(exp(g_t)) for a
+ *                              per-key-channel gate, #2506 "per-key-channel
+ *                              retention")
+ *         u  = beta_t (v_t - S k_t);   S <- S + u k_t^T;   o_t = S q_t
+ *   - Computed chunk-parallel in 64-token chunks (#2497 "What does this PR
+ *     do?": fused path with chunk size 64) with WY/UT-transformed W and U and
+ *     an exact triangular solve (#2506: "the exact solve remains the default").
+ *   - State QDQ (#2497 "What does this PR do?"): at every chunk boundary, for
+ *     every tile of 64 value rows x all dk key columns of every (sequence,
+ *     head), scale s = amax / 448 (zero guard: s = 1 when amax / 448 is not
+ *     positive), S <- RNE_E4M3(S / s) * s.  The state stays fp32.
+ *   - Prefill -> decode handoff (#2519 "What does this PR do?", step 3): QDQ
+ *     at the handoff and after every later recurrent write; each output is
+ *     taken from the updated working state before that QDQ.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers on the current HIP device unless
+ *     stated otherwise.  The caller owns every buffer; the library allocates
+ *     nothing and keeps no state beyond a per-device capability cache.
+ *   - `stream` is a hipStream_t passed as void*.  Work is enqueued
+ *     asynchronously on it; no entry point synchronizes the host.
+ *   - Arguments are checked on the host before anything is launched.  A
+ *     failed check returns GDN_ERR_INVALID_ARG or GDN_ERR_UNSUPPORTED and
+ *     launches nothing; gdn_last_error() then describes the failure.  The
+ *     contents of device index arrays (cu_seqlens, lengths) are
+ *     preconditions and are not read on the host.
+ *   - Non-finite inputs are outside the contract.
+ *   - Calls are reentrant; calls that write the same buffers race.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned buffer, bad flag */
+    GDN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head size, dtype combo) */
+    GDN_ERR_DEVICE = 3         /* no gfx950 device current, or a HIP launch failed */
+} gdn_status_t;
+
+typedef enum {
+    GDN_F32 = 0,
+    GDN_BF16 = 1
+} gdn_dtype_t;
+
+/* qdq_flags bits */
+#define GDN_QDQ_CHUNK 1u   /* QDQ after every 64-token chunk of the chunked prefix and at its end (t = P) */
+#define GDN_QDQ_WRITE 2u   /* QDQ at the handoff t = P and after every recurrent write t > P */
+
+typedef struct {
+    int32_t n_seqs;            /* N >= 1 */
+    int32_t n_heads;           /* H >= 1 */
+    int32_t dk;                /* key head size: 64 or 128 */
+    int32_t dv;                /* value head size: a multiple of 64, at most 256 */
+    int64_t total_tokens;      /* rows of the packed q/k/v/o buffers (decode: must equal n_seqs) */
+    int32_t io_dtype;          /* gdn_dtype_t of q, k, v */
+    int32_t o_dtype;           /* gdn_dtype_t of o */
+    int32_t gate_per_channel;  /* 0: g is [T, H]; 1: g is [T, H, dk] (per-key-channel gate) */
+    uint32_t qdq_flags;        /* GDN_QDQ_* bits */
+} gdn_shape_t;
+
+/* Optional per-boundary record of the chunked prefix, for parity checks.
+ * Boundary b of sequence n is b = bound_offsets[n] + i for its i-th chunk
+ * end (i = 0 .. ceil(P_n / 64) - 1).  All pointers nullable. */
+typedef struct {
+    const int32_t* bound_offsets;  /* [N + 1] device; prefix sums of ceil(P_n / 64) */
+    float* bound_pre;              /* [n_bounds, H, dv, dk] state after the chunk, before QDQ */
+    float* bound_post;             /* [n_bounds, H, dv, dk] state after QDQ (= pre when none) */
+    float* scales;                 /* [n_bounds, H, dv / 64] QDQ scales (1 when none) */
+} gdn_debug_t;
+
+/*
+ * gdn_chunk_fwd -- chunked gated delta rule forward over packed sequences.
+ *
+ *   q, k  [total_tokens, H, dk]   io_dtype, row-major (16-byte aligned)
+ *   v     [total_tokens, H, dv]   io_dtype
+ *   beta  [total_tokens, H]       fp32
+ *   g     [total_tokens, H] or [total_tokens, H, dk]   fp32 natural-log gate (<= 0 expected)
+ *   cu_seqlens  [N + 1] int32: storage segment of sequence n is rows
+ *               [cu_seqlens[n], cu_seqlens[n+1]); cu_seqlens[N] <= total_tokens.
+ *   seq_lens    [N] int32 valid length L_n <= segment length; NULL: the segment length.
+ *               Rows of a segment past L_n are padding: they never touch the state
+ *               and their o rows are written as 0.
+ *   prefix_lens [N] int32 chunked-prefix length P_n <= L_n; NULL: P_n = L_n.  Tokens
+ *               P_n < t <= L_n run as recurrent writes (#2519 prefix/suffix split).
+ *   initial_state [N, H, dv, dk] fp32 or NULL (zero).  Used as given (not quantized).
+ *   o      [total_tokens, H, dv]  o_dtype (output)
+ *   final_state [N, H, dv, dk] fp32 (output), may alias initial_state.
+ *   debug  NULL or a per-boundary record (see gdn_debug_t).
+ *
+ * QDQ placement for token t of a sequence (1-based): after token t when
+ * (GDN_QDQ_CHUNK and t <= P and (t % 64 == 0 or t == P)) or
+ * (GDN_QDQ_WRITE and t >= max(P, 1)); chunks start at each sequence's first
+ * valid token.
+ */
+gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape,
+                           const void* q, const void* k, const void* v,
+                           const float* beta, const float* g,
+                           const int32_t* cu_seqlens, const int32_t* seq_lens,
+                           const int32_t* prefix_lens,
+                           const float* initial_state,
+                           void* o, float* final_state,
+                           const gdn_debug_t* debug, void* stream);
+
+/*
+ * gdn_state_qdq -- standalone per-tile state QDQ (#2497: one scalar scale per
+ * full-key x 64-value-column tile; #2497 "fp8_scalar_qdq" applies a scale per
+ * tile).
+ *   in, out  [n_states, dv, dk] fp32 (out may alias in); dv % 64 == 0,
+ *            dk % 4 == 0, 4 <= dk <= 256, 16-byte aligned.
+ *   scales   [n_states, dv / 64] fp32 output, or NULL.
+ */
+gdn_status_t gdn_state_qdq(const float* in, float* out, float* scales,
+                           int64_t n_states, int32_t dv, int32_t dk, void* stream);
+
+/*
+ * gdn_decode_step -- one recurrent token per sequence against a stored state
+ * (#2519 step 3: read the stored state, output from the updated working
+ * state, QDQ before storing when GDN_QDQ_WRITE is set).
+ *   shape->total_tokens must equal shape->n_seqs; GDN_QDQ_CHUNK is ignored.
+ *   q, k  [N, H, dk] io_dtype;  v [N, H, dv] io_dtype
+ *   beta  [N, H] fp32;  g [N, H] or [N, H, dk] fp32
+ *   state [N, H, dv, dk] fp32, read and written in place
+ *   o     [N, H, dv] o_dtype
+ *   state_pre  [N, H, dv, dk] fp32 or NULL: the updated state before QDQ (parity record)
+ *   scales     [N, H, dv / 64] fp32 or NULL: QDQ scales (1 when no QDQ)
+ */
+gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
+                             const void* q, const void* k, const void* v,
+                             const float* beta, const float* g,
+                             float* state, void* o,
+                             float* state_pre, float* scales, void* stream);
+
+/* Static description of a status code. */
+const char* gdn_status_string(gdn_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,136 @@
+"""Shared plumbing for the GPU parity tests: run the HIP path through the C
+ABI on seeded inputs, run the oracle on the same inputs, compare."""
+from __future__ import annotations
+
+import numpy as np
+
+from fp8_state_qat_amd import inputs as gi
+from oracle import oracle as orc
+
+CHUNK = 64
+
+
+def rel_l2(x, ref):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
+
+
+def np64(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def n_bounds(prefix_lens):
+    return [(int(p) + CHUNK - 1) // CHUNK for p in prefix_lens]
+
+
+def run_chunk_gpu(w: gi.Workload, flags, *, o_dtype=None, record=False, initial_state=None,
+                  use_prefix=True, use_seq_lens=True):
+    """Run gdn_chunk_fwd on workload w; returns numpy dict (o, S and, when
+    record, bound_pre/bound_post/scales [nb_total, H, dv(/64), dk])."""
+    import torch
+    from fp8_state_qat_amd import api
+    d = gi.device_tensors(w)
+    H, dk, dv = w.n_heads, w.dk, w.dv
+    dbg = None
+    nb = n_bounds(w.prefix_lens)
+    offs = np.zeros(len(nb) + 1, np.int32)
+    offs[1:] = np.cumsum(nb)
+    if record:
+        tot = int(offs[-1])
+        dbg = dict(bound_offsets=torch.from_numpy(offs).cuda(),
+                   bound_pre=torch.full((tot, H, dv, dk), np.nan, device="cuda"),
+                   bound_post=torch.full((tot, H, dv, dk), np.nan, device="cuda"),
+                   scales=torch.full((tot, H, dv // 64), np.nan, device="cuda"))
+    init = None if initial_state is None else torch.from_numpy(
+        np.ascontiguousarray(initial_state, np.float32)).cuda()
+    o_dt = None if o_dtype is None else {"f32": torch.float32, "bf16": torch.bfloat16}[o_dtype]
+    o, S = api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                         seq_lens=d["seq_lens"] if use_seq_lens else None,
+                         prefix_lens=d["prefix_lens"] if use_prefix else None,
+                         initial_state=init, qdq_flags=flags, o_dtype=o_dt, debug=dbg)
+    torch.cuda.synchronize()
+    res = {"o": np64(o), "S": S.cpu().numpy(), "offsets": offs}
+    if record:
+        for key in ("bound_pre", "bound_post", "scales"):
+            res[key] = dbg[key].cpu().numpy()
+    return res
+
+
+def run_chunk_oracle(w: gi.Workload, flags, *, pairs=None, threads=8, initial_state=None,
+                     record=False):
+    return orc.gdn_packed(w.f64("q"), w.f64("k"), w.f64("v"), w.f64("beta"), w.f64("g"),
+                          w.cu_seqlens, seq_lens=w.seq_lens, prefix_lens=w.prefix_lens,
+                          flags=flags, S0=None if initial_state is None else
+                          np.asarray(initial_state, np.float64),
+                          pairs=pairs, threads=threads, record=record)
+
+
+def midpoint_distance(y):
+    """Distance of code-domain values y = x / s to the nearest E4M3 rounding
+    midpoint, relative to the tile's range (|x - x_mid| / amax = |y - mid| /
+    448), in fp64.  The tile's amax is the unit in which fp32 arithmetic
+    error of a state element scales, so "within 1e-6 relative of a
+    midpoint" is read against it."""
+    grid = orc.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (grid[1:] + grid[:-1]) / 2
+    a = np.abs(np.asarray(y, np.float64)).ravel()
+    i = np.clip(np.searchsorted(mids, a), 1, len(mids) - 1)
+    d = np.minimum(np.abs(a - mids[i - 1]), np.abs(a - mids[i]))
+    return d / 448.0
+
+
+def teacher_forced(w: gi.Workload, gpu, flags, pairs, *, initial_state=None):
+    """G2: for every chunk of every (n, h) in pairs, restart the oracle from
+    the GPU's post-QDQ boundary state and run that one chunk.  Returns the
+    rel-L2 of o and of the pre-QDQ states over all those chunks (o_rel,
+    pre_rel), the worst single chunk (o_rel_max, pre_rel_max) and the code
+    mismatch counts."""
+    q, k, v, b, g = (w.f64(x) for x in ("q", "k", "v", "beta", "g"))
+    cu, offs = w.cu_seqlens, gpu["offsets"]
+    out = dict(o_rel=0.0, pre_rel=0.0, o_rel_max=0.0, pre_rel_max=0.0, gpu_code_mismatch=0,
+               oracle_code_mismatch=0, oracle_mismatch_far=0, codes=0, scale_mismatch=0)
+    acc = np.zeros(4)   # sum |o err|^2, |o ref|^2, |pre err|^2, |pre ref|^2
+    for (n, h) in pairs:
+        P = int(w.prefix_lens[n])
+        s0 = int(cu[n])
+        for c in range((P + CHUNK - 1) // CHUNK):
+            bidx = int(offs[n]) + c
+            t0, t1 = c * CHUNK, min(P, (c + 1) * CHUNK)
+            if c == 0:
+                S0 = None if initial_state is None else np.asarray(initial_state[n, h], np.float64)
+            else:
+                S0 = gpu["bound_post"][bidx - 1, h].astype(np.float64)
+            sl = slice(s0 + t0, s0 + t1)
+            gg = g[sl, h] if g.ndim == 2 else g[sl, h, :]
+            # this chunk alone: its end is a boundary; CHUNK QDQ there iff the
+            # full run quantizes after this chunk
+            last = (c == (P + CHUNK - 1) // CHUNK - 1)
+            qdq_here = bool(flags & orc.QDQ_CHUNK) or (bool(flags & orc.QDQ_WRITE) and last)
+            r = orc.gdn_sequence(q[sl, h], k[sl, h], v[sl, h], b[sl, h], gg,
+                                 flags=orc.QDQ_CHUNK if qdq_here else 0, S0=S0, record=True)
+            pre_gpu = gpu["bound_pre"][bidx, h]
+            out["o_rel_max"] = max(out["o_rel_max"], rel_l2(gpu["o"][sl, h], r["o"]))
+            out["pre_rel_max"] = max(out["pre_rel_max"], rel_l2(pre_gpu, r["bound_pre"][0]))
+            acc += [np.sum((gpu["o"][sl, h] - r["o"]) ** 2), np.sum(r["o"] ** 2),
+                    np.sum((pre_gpu - r["bound_pre"][0]) ** 2), np.sum(r["bound_pre"][0] ** 2)]
+            if qdq_here:
+                want, sc, codes_gpu_pre = orc.qdq_states(pre_gpu.astype(np.float32))
+                out["gpu_code_mismatch"] += int(np.sum(want.view(np.uint32) !=
+                                                       gpu["bound_post"][bidx, h].view(np.uint32)))
+                out["scale_mismatch"] += int(np.sum(sc != gpu["scales"][bidx, h]))
+                # the oracle's own decision on its own pre-QDQ state
+                _, sc_o, codes_orc = orc.qdq_states(r["bound_pre"][0].astype(np.float32))
+                mism = codes_orc != codes_gpu_pre
+                out["codes"] += codes_orc.size
+                out["oracle_code_mismatch"] += int(mism.sum())
+                if mism.any():
+                    scale = np.repeat(sc_o, 64, axis=0)[:, None] * np.ones_like(pre_gpu)
+                    y = r["bound_pre"][0] / scale.astype(np.float64)
+                    far = midpoint_distance(y[mism]) > 1e-6
+                    out["oracle_mismatch_far"] += int(far.sum())
+    out["o_rel"] = float(np.sqrt(acc[0] / max(acc[1], 1e-300)))
+    out["pre_rel"] = float(np.sqrt(acc[2] / max(acc[3], 1e-300)))
+    return out

@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+that include/gdn.h declares, and rejects bad arguments on the host before
+touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from fp8_state_qat_amd import _lib
+from fp8_state_qat_amd._lib import GdnDebug, GdnShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HAS_GPU = torch.cuda.is_available()
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert _lib.status_string(0) == "GDN_OK"
+    assert _lib.status_string(1) == "GDN_ERR_INVALID_ARG"
+    assert _lib.status_string(2) == "GDN_ERR_UNSUPPORTED"
+    assert _lib.status_string(3) == "GDN_ERR_DEVICE"
+
+
+FAKE = 0x10000  # 64 KiB-aligned stand-in address; never dereferenced on the host
+
+
+def _shape(**kw):
+    d = dict(n_seqs=2, n_heads=4, dk=128, dv=128, total_tokens=100, io_dtype=1, o_dtype=1,
+             gate_per_channel=0, qdq_flags=3)
+    d.update(kw)
+    return GdnShape(**d)
+
+
+def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None):
+    p = ctypes.c_void_p
+    return _lib.lib().gdn_chunk_fwd(ctypes.byref(shape) if shape is not None else None,
+                                    p(q), p(FAKE), p(FAKE), p(beta), p(FAKE), p(cu), None, None,
+                                    None, p(FAKE), p(fin), dbg, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_seqs=0), 1), (dict(n_heads=0), 1), (dict(dv=96), 1), (dict(dk=96), 2),
+    (dict(dk=32), 2), (dict(dv=512), 2), (dict(total_tokens=-1), 1), (dict(io_dtype=7), 1),
+    (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=4), 1),
+    (dict(io_dtype=0, dk=128), 2), (dict(io_dtype=0, dk=64, dv=64, gate_per_channel=1), 2),
+])
+def test_chunk_fwd_rejects_bad_shape(kw, status):
+    assert _chunk(_shape(**kw)) == status
+    assert _lib.last_error()
+
+
+def test_chunk_fwd_rejects_null_and_misaligned():
+    assert _chunk(None) == 1
+    assert _chunk(_shape(), q=0) == 1
+    assert _chunk(_shape(), cu=0) == 1
+    assert _chunk(_shape(), fin=0) == 1
+    assert _chunk(_shape(), q=FAKE + 8) == 1
+    assert _chunk(_shape(), beta=FAKE + 2) == 1
+    dbg = GdnDebug(None, ctypes.c_void_p(FAKE), None, None)   # record without offsets
+    assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
+
+
+def test_state_qdq_rejects_bad_args():
+    L = _lib.lib()
+    p = ctypes.c_void_p
+    assert L.gdn_state_qdq(p(FAKE), p(FAKE), None, -1, 64, 128, None) == 1
+    assert L.gdn_state_qdq(p(FAKE), p(FAKE), None, 4, 96, 128, None) == 1
+    assert L.gdn_state_qdq(p(FAKE), p(FAKE), None, 4, 64, 6, None) == 1
+    assert L.gdn_state_qdq(p(FAKE), p(FAKE), None, 4, 64, 512, None) == 2
+    assert L.gdn_state_qdq(None, p(FAKE), None, 4, 64, 128, None) == 1
+    assert L.gdn_state_qdq(p(FAKE + 4), p(FAKE), None, 4, 64, 128, None) == 1
+
+
+def test_decode_rejects_bad_args():
+    L = _lib.lib()
+    p = ctypes.c_void_p
+    s = _shape(total_tokens=3)     # decode needs total_tokens == n_seqs
+    args = [p(FAKE)] * 7 + [None, None, None]
+    assert L.gdn_decode_step(ctypes.byref(s), *args) == 1
+    s = _shape(total_tokens=2)
+    bad = [p(FAKE)] * 5 + [None, p(FAKE), None, None, None]   # state NULL
+    assert L.gdn_decode_step(ctypes.byref(s), *bad) == 1
+
+
+@pytest.mark.skipif(HAS_GPU, reason="would launch with stand-in pointers on a GPU")
+def test_valid_call_without_gpu_reports_device_error():
+    assert _chunk(_shape()) == 3
+    assert "device" in _lib.last_error().lower()
