@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step = one gdn_chunk_fwd call over the GDN prefill workload (B=4,
+T=4096, H=16, dk=dv=128, bf16 q/k/v and o, fp32 state, FP8-E4M3 state QDQ
+at every 64-token boundary and at the end): staging, gates, K K^T, the exact
+solve, W and U, U', O, the state update and the boundary QDQ, all in one
+kernel launch.  Inputs are resident in HBM before the timed region.
+
+Also reported: the prefill->decode handoff workload (256 sequences, H=32,
+d=128: 2048-token chunked prefix with QDQ, then 512 single-token decode steps
+each writing the state through per-tile QDQ) as decode-step HBM GB/s, and the
+CPU oracle's throughput on a bounded sample of the prefill workload.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2516.6 # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "GDN chunked-prefill tokens/s + MFMA %peak; decode step HBM GB/s, 1×MI355X"
+
+
+def flops_per_token_head(C, dk, dv):
+    """Algorithmic flops of the chunked forward per token and head (dense
+    64x64 tiles): K K^T, W, Q K^T (2C dk each), U, P U' (2C dv each), W S^T,
+    Q S^T, U'^T K (2 dk dv each) and the solve (C^2 / 3)."""
+    return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3
+
+
+def prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes, gate_floats=1):
+    """Algorithmic HBM bytes of one prefill launch: q, k, v read once, beta
+    and g read once, o written once, the final state written once."""
+    per = io_bytes * (2 * dk + dv) + 4 * (1 + gate_floats) + o_bytes * dv
+    return T_heads * per + n_states * dv * dk * 4
+
+
+def decode_bytes(n_heads_seqs, dk, dv, io_bytes, o_bytes):
+    """Per decode step: the fp32 state read and written once, q, k, v read,
+    beta and g read, o written."""
+    return n_heads_seqs * (2 * 4 * dv * dk + io_bytes * (2 * dk + dv) + 8 + o_bytes * dv)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(fn, steps, warmup):
+    """Warm up, then time exactly `steps` calls between synchronizations with
+    HIP events on torch's current stream (the stream the library launches
+    on).  Returns (total ms, per-call ms list)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]), per
+
+
+def cpu_baseline(w, flags, n_pairs, threads):
+    from oracle import oracle as orc
+    pairs = [(n, h) for n in range(w.n_seqs) for h in range(w.n_heads)][:n_pairs]
+    q, k, v, b, g = (w.f64(x) for x in ("q", "k", "v", "beta", "g"))
+    t0 = time.perf_counter()
+    orc.gdn_packed(q, k, v, b, g, w.cu_seqlens, seq_lens=w.seq_lens, prefix_lens=w.prefix_lens,
+                   flags=flags, pairs=pairs, threads=threads)
+    dt = time.perf_counter() - t0
+    token_heads = sum(int(w.seq_lens[n]) for n, _ in pairs)
+    return {"value": token_heads / w.n_heads / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(pairs)} (sequence, head) pairs x {int(w.seq_lens[0])} tokens of the "
+                      f"prefill workload, QDQ on, fp64 recurrence; token-heads/s divided by "
+                      f"H={w.n_heads}; {dt:.1f} s wall on {threads} threads"}
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM traffic per launch from a committed rocprofv3 PMC summary, if the
+    kernel source has not changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", f"{kernel_key}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=32)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also launch one plain device copy of this many MiB (PMC calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the path shards by "
+                                   "(sequence, head) with no exchange, and multi-GPU runs are "
+                                   "not part of it", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from fp8_state_qat_amd import api, inputs as gi
+    from fp8_state_qat_amd._lib import GDN_QDQ_CHUNK, GDN_QDQ_WRITE
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flags = GDN_QDQ_CHUNK | GDN_QDQ_WRITE
+
+    # ---------------- prefill workload (headline) ----------------
+    w = gi.gdn_prefill()
+    d = gi.device_tensors(w, dev)
+    B, T, H, dk, dv = w.n_seqs, int(w.seq_lens[0]), w.n_heads, w.dk, w.dv
+    o = torch.empty((w.total_tokens, H, dv), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+
+    def step():
+        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=flags,
+                      out=o, final_state=fin)
+
+    total_ms, per = time_launches(step, args.steps, args.warmup)
+    ms_step = total_ms / args.steps
+    kern_ms = float(np.mean(per))
+    tokens = B * T
+    token_heads = tokens * H
+    fl = flops_per_token_head(64, dk, dv) * token_heads
+    by = prefill_bytes(token_heads, B * H, dk, dv, 2, 2)
+    src = source_hash([os.path.join(ROOT, "fp8_state_qat_amd", "csrc", f)
+                       for f in ("gdn_chunk.hip", "gdn_device.hpp")])
+    traffic = load_traffic("chunk_fwd_gdn_prefill", src)
+    hbm_gbs = by / (kern_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "chunk_fwd_kernel<128, bf16>",
+                "algorithmic_bytes_per_launch": by, "avg_launch_ms": round(kern_ms, 5)}
+    tflops = fl / (kern_ms * 1e-3) / 1e12
+    mfma = {"achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": fl,
+            "flops_per_token_head": flops_per_token_head(64, dk, dv)}
+
+    # QDQ off, same workload (reported)
+    def step_off():
+        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=0,
+                      out=o, final_state=fin)
+    off_ms, _ = time_launches(step_off, args.steps, args.warmup)
+
+    out = {"metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "GDN chunked prefill, B=4 T=4096 H=16 dk=dv=128, bf16 q/k/v "
+                                  "and o, fp32 state, chunk 64, FP8-E4M3 state QDQ at every "
+                                  "boundary (tiles 128x64 per head)",
+                      "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv,
+                      "qdq_flags": flags},
+           "roofline": roofline, "mfma": mfma,
+           "qdq_off": {"ms_per_step": round(off_ms / args.steps, 5),
+                       "tokens_per_s": round(tokens / (off_ms / args.steps * 1e-3), 1)}}
+
+    # ---------------- prefill -> decode handoff workload ----------------
+    if not args.no_decode:
+        del d
+        torch.cuda.empty_cache()
+        N4, H4, P4, steps4 = 256, 32, 2048, 512
+        pd = gi.device_packed([P4] * N4, H4, 128, 128, seed=4, device=dev)
+        o4 = torch.empty((N4 * P4, H4, 128), dtype=torch.bfloat16, device=dev)
+        state = torch.empty((N4, H4, 128, 128), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        api.chunk_fwd(pd["q"], pd["k"], pd["v"], pd["beta"], pd["g"], pd["cu_seqlens"],
+                      qdq_flags=flags, out=o4, final_state=state)
+        torch.cuda.synchronize()
+        pre_ms = (time.perf_counter() - t0) * 1e3
+        del pd, o4
+        torch.cuda.empty_cache()
+        tok = gi.device_decode_tokens(N4, H4, 128, 128, steps4, seed=5, device=dev)
+        od = torch.empty((N4, H4, 128), dtype=torch.bfloat16, device=dev)
+        it = {"i": 0}
+
+        def dstep():
+            i = it["i"] % steps4
+            api.decode_step(tok["q"][i], tok["k"][i], tok["v"][i], tok["beta"][i], tok["g"][i],
+                            state, qdq=True, o=od)
+            it["i"] += 1
+
+        dwarm = 8
+        dtot, dper = time_launches(dstep, steps4 - dwarm, dwarm)
+        dms = float(np.mean(dper))
+        dby = decode_bytes(N4 * H4, 128, 128, 2, 2)
+        out["decode"] = {"workload": "256 sequences, H=32, dk=dv=128, bf16 q/k/v/o, fp32 state; "
+                                     "2048-token chunked prefix with QDQ, then 512 decode steps "
+                                     "with per-write QDQ",
+                         "prefill_ms": round(pre_ms, 3),
+                         "prefill_tokens_per_s": round(N4 * P4 / (pre_ms * 1e-3), 1),
+                         "decode_steps_timed": steps4 - dwarm,
+                         "ms_per_step": round(dms, 5),
+                         "tokens_per_s": round(N4 / (dms * 1e-3), 1),
+                         "roofline": {"bound": "hbm", "achieved": round(dby / (dms * 1e-3) / 1e9, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(dby / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "algorithmic_bytes_per_launch": dby}}
+        del tok, state
+        torch.cuda.empty_cache()
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n * 4
+
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        out["cpu_baseline"] = cpu_baseline(w, flags, args.cpu_pairs, threads)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,12 +12,14 @@
 //
 // Per chunk of n <= 64 tokens (rows past n are zero-filled, beta = g = 0, so
 // they drop out of every product), with gamma = in-chunk cumulative log-gate:
-//   a1  stage q, k (row-major and transposed), v (transposed), beta, g -> LDS
-//   a2  gamma, exp(gamma), exp(gamma_C - gamma)            (wave 0, scan)
+//   a1  stage q, k (row-major and transposed), v (transposed) -> LDS; the
+//       next chunk's q, k, v, beta, g are already in flight to registers
+//   a2  gamma (wave scan), exp(gamma), exp(gamma_C - gamma)
 //   a3  A[r][s] = beta_r exp(gamma_r - gamma_s) k_r.k_s   (s < r)      MFMA
 //       P[r][s] = exp(gamma_r - gamma_s) q_r.k_s          (s <= r)     MFMA
-//   a4  X = (I + A)^-1 by blocked forward substitution in fp32 (16 x 16
-//       diagonal blocks, then off-diagonal blocks level by level);
+//   a4  X = (I + A)^-1 by blocked forward substitution in fp32: the four
+//       16 x 16 diagonal blocks column by column, then the off-diagonal
+//       blocks level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj;
 //       T = X diag(beta), T' = T diag(exp(gamma))
 //   a5  W = T' K  (computed as W^T = K^T T'^T so it lands row-major in LDS),
 //       U = T V                                                        MFMA
@@ -28,6 +30,10 @@
 //       S <- RNE_E4M3(S/s) s
 // then the recurrent suffix (tokens P_n < t <= L_n, QDQ after every write)
 // and the final state store.
+//
+// With one wave per SIMD nothing hides latency but the wave's own
+// instruction stream, so every phase issues all of its fragment loads before
+// its MFMAs and keeps several independent accumulators in flight.
 //
 // Precision (bf16 inputs, fp32 accumulate): q, k, v enter the MFMAs exactly.
 // T, T', P and U' are fed as hi + lo bf16 pairs (their rounding would cost
@@ -53,43 +59,34 @@ struct EngBF16 {
   static __device__ __forceinline__ Fr load(const E* row, int kb, int gq) {
     const uint2 a = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * gq);
     const uint2 b = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * gq);
-    const uint4 u = make_uint4(a.x, a.y, b.x, b.y);
-    return __builtin_bit_cast(Fr, u);
+    return __builtin_bit_cast(Fr, make_uint4(a.x, a.y, b.x, b.y));
   }
   static __device__ __forceinline__ void mma(f32x4& c, const Fr& a, const Fr& b) { mma_bf16(c, a, b); }
   static __device__ __forceinline__ Fr round(const float (&x)[8]) {
-    uint16_t h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) h[j] = float_to_bf16_bits(x[j]);
-    return __builtin_bit_cast(Fr, h);
+    return __builtin_bit_cast(Fr, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                             pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
   }
   static __device__ __forceinline__ void split(const float (&x)[8], Fr& hi, Fr& lo) {
-    uint16_t h[8], l[8];
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h[j] = float_to_bf16_bits(x[j]);
-      l[j] = float_to_bf16_bits(x[j] - bf16_bits_to_float(h[j]));
-    }
-    hi = __builtin_bit_cast(Fr, h);
-    lo = __builtin_bit_cast(Fr, l);
+    for (int j = 0; j < 4; ++j) split_bf16x2(x[2 * j], x[2 * j + 1], h[j], l[j]);
+    hi = __builtin_bit_cast(Fr, make_uint4(h[0], h[1], h[2], h[3]));
+    lo = __builtin_bit_cast(Fr, make_uint4(l[0], l[1], l[2], l[3]));
   }
-  static __device__ __forceinline__ E cvt(float x) { return float_to_bf16_bits(x); }
   static __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
-    uint2 u;
-    u.x = (uint32_t)float_to_bf16_bits(a) | ((uint32_t)float_to_bf16_bits(b) << 16);
-    u.y = (uint32_t)float_to_bf16_bits(c) | ((uint32_t)float_to_bf16_bits(d) << 16);
-    *reinterpret_cast<uint2*>(p) = u;
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
   }
   // hi and lo parts of four consecutive values
   static __device__ __forceinline__ void store4_split(E* ph, E* pl, const float (&x)[4]) {
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h[j] = float_to_bf16_bits(x[j]);
-      l[j] = float_to_bf16_bits(x[j] - bf16_bits_to_float(h[j]));
-    }
-    *reinterpret_cast<uint2*>(ph) = __builtin_bit_cast(uint2, h);
-    *reinterpret_cast<uint2*>(pl) = __builtin_bit_cast(uint2, l);
+    uint32_t h0, l0, h1, l1;
+    split_bf16x2(x[0], x[1], h0, l0);
+    split_bf16x2(x[2], x[3], h1, l1);
+    *reinterpret_cast<uint2*>(ph) = make_uint2(h0, h1);
+    *reinterpret_cast<uint2*>(pl) = make_uint2(l0, l1);
+  }
+  // two rows, same column: one 4-byte LDS write of (row r, row r+1)
+  static __device__ __forceinline__ void store_pair(E* p, E a, E b) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)a | ((uint32_t)b << 16);
   }
 };
 
@@ -117,13 +114,15 @@ struct EngF32 {
     hi = round(x);
     (void)lo;
   }
-  static __device__ __forceinline__ E cvt(float x) { return x; }
   static __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
   }
   static __device__ __forceinline__ void store4_split(E* ph, E* pl, const float (&x)[4]) {
     (void)pl;
     *reinterpret_cast<float4*>(ph) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+  static __device__ __forceinline__ void store_pair(E* p, E a, E b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
   }
 };
 
@@ -151,12 +150,14 @@ struct Smem {
   static constexpr size_t oT = oXW + szXW;              // T hi [, T lo]
   static constexpr size_t oTg = oT + kSplitN * szM;     // T' hi [, lo]
   static constexpr size_t oP = oTg + kSplitN * szM;     // P hi [, lo]
-  static constexpr size_t oVec = oP + kSplitN * szM;    // gamma, e^gamma, e^(gC-gamma), beta
+  static constexpr size_t oVec = oP + kSplitN * szM;    // gamma*log2e, e^gamma, e^(gC-gamma), beta
   static constexpr size_t oRed = oVec + 4 * 64 * sizeof(float);
   static constexpr size_t bytes = oRed + 16 * sizeof(float);
-  // solve scratch (3 x 16 x 16 fp32) lives in the T area before T is written
-  static constexpr size_t oR = oT;
-  static_assert(3 * 256 * sizeof(float) <= kSplitN * szM, "solve scratch does not fit");
+  // solve scratch lives in the T / T' area before T is written:
+  // X^T (fp32 [64][L64]) and R^T (3 x 16 x 16 fp32)
+  static constexpr size_t oXT = oT;
+  static constexpr size_t oRT = oT + szF;
+  static_assert(szF + 3 * 256 * sizeof(float) <= 2 * kSplitN * szM, "solve scratch does not fit");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -181,6 +182,24 @@ struct ChunkArgs {
   unsigned flags;
 };
 
+__device__ __forceinline__ float dot4(const float4 a, const float4 b, float acc) {
+  acc = fmaf(a.x, b.x, acc);
+  acc = fmaf(a.y, b.y, acc);
+  acc = fmaf(a.z, b.z, acc);
+  return fmaf(a.w, b.w, acc);
+}
+
+// 16-element dot product of two fp32 LDS rows (4 partial sums).
+__device__ __forceinline__ float dot16(const float* a, const float* b) {
+  const float4* a4 = reinterpret_cast<const float4*>(a);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  const float4 a0 = a4[0], a1 = a4[1], a2 = a4[2], a3 = a4[3];
+  const float4 b0 = b4[0], b1 = b4[1], b2 = b4[2], b3 = b4[3];
+  return (dot4(a0, b0, 0.f) + dot4(a1, b1, 0.f)) + (dot4(a2, b2, 0.f) + dot4(a3, b3, 0.f));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
 template <int DK, class Eng, typename TIO, typename TO>
 __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
   using S_ = Smem<DK, Eng>;
@@ -204,12 +223,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
   E* sTgl = sTgh + 64 * L64;
   E* sPh = reinterpret_cast<E*>(smem + S_::oP);
   E* sPl = sPh + 64 * L64;
-  float* sGam = reinterpret_cast<float*>(smem + S_::oVec);
-  float* sEg = sGam + 64;
+  float* sXT = reinterpret_cast<float*>(smem + S_::oXT);
+  float* sRT = reinterpret_cast<float*>(smem + S_::oRT);
+  float* sG2 = reinterpret_cast<float*>(smem + S_::oVec);  // gamma * log2(e)
+  float* sEg = sG2 + 64;
   float* sEgc = sEg + 64;
   float* sBeta = sEgc + 64;
   float* sRed = reinterpret_cast<float*>(smem + S_::oRed);
-  float* sR = reinterpret_cast<float*>(smem + S_::oR);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;        // wave
@@ -219,8 +239,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
 
   const int H = args.H, dv = args.dv;
   const int tiles = dv / kTileRows;
-  const int vt = blockIdx.x % tiles;
-  const int nh = blockIdx.x / tiles;
+  // Block -> (n*H + h, vt).  Workgroups are dispatched to the 8 XCDs round
+  // robin; when heads come in groups of 8, the value tiles of one head get
+  // block ids 8 apart, i.e. the same XCD, so their q/k reads share an L2.
+  int nh, vt;
+  {
+    const int b = blockIdx.x, G = gridDim.x;
+    if (tiles > 1 && G % (8 * tiles) == 0) {
+      const int slot = b >> 3;
+      vt = slot % tiles;
+      nh = (slot / tiles) * 8 + (b & 7);
+    } else {
+      vt = b % tiles;
+      nh = b / tiles;
+    }
+  }
   const int h = nh % H;
   const int n = nh / H;
 
@@ -258,179 +291,231 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
   const int n_chunks = (P + kChunk - 1) / kChunk;
   const int bound0 = args.bound_offsets ? args.bound_offsets[n] : 0;
 
+  // ---- staging geometry: 16-byte segments, two adjacent rows per thread
+  constexpr int EPS = 16 / (int)sizeof(TIO);   // elements per segment
+  constexpr int SPR = DK / EPS;                // segments per q/k row
+  constexpr int NPK = 64 * SPR / kThreads / 2; // row pairs per thread (q/k)
+  constexpr int VSPR = kTileRows / EPS;        // segments per v row
+  constexpr int NPV = 64 * VSPR / kThreads / 2;
+  static_assert(NPK >= 1 && NPV >= 1, "staging geometry");
+  uint4 pk[NPK][2], pq[NPK][2], pv[NPV][2];
+  float pg = 0.f, pb = 0.f;
+  auto fetch = [&](int c) {
+    const int t0 = seg0 + c * kChunk;
+    const int nv = min(kChunk, P - c * kChunk);
+#pragma unroll
+    for (int j = 0; j < NPK; ++j) {
+      const int rp = tid / SPR + (kThreads / SPR) * j, c0 = (tid % SPR) * EPS;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * rp + e;
+        pk[j][e] = make_uint4(0u, 0u, 0u, 0u);
+        pq[j][e] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < nv) {
+          const int64_t off = (int64_t)(t0 + r) * qk_row + (int64_t)h * DK + c0;
+          pk[j][e] = *reinterpret_cast<const uint4*>(gk_ + off);
+          pq[j][e] = *reinterpret_cast<const uint4*>(gq_ + off);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+      const int rp = tid / VSPR + (kThreads / VSPR) * j, c0 = (tid % VSPR) * EPS;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * rp + e;
+        pv[j][e] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < nv)
+          pv[j][e] = *reinterpret_cast<const uint4*>(gv_ + (int64_t)(t0 + r) * v_row +
+                                                       (int64_t)h * dv + kTileRows * vt + c0);
+      }
+    }
+    if (w == 0) {
+      pg = 0.f;
+      pb = 0.f;
+      if (lane < nv) {
+        pg = args.g[(int64_t)(t0 + lane) * H + h];
+        pb = args.beta[(int64_t)(t0 + lane) * H + h];
+      }
+    }
+  };
+  if (n_chunks > 0) fetch(0);
+
   for (int c = 0; c < n_chunks; ++c) {
     const int t0 = seg0 + c * kChunk;
     const int nv = min(kChunk, P - c * kChunk);  // valid tokens in this chunk
 
-    // ---------------- a1: stage the chunk ----------------
-    {
-      constexpr int EPS = 16 / sizeof(TIO);           // elements per 16-byte segment
-      constexpr int SPR = DK / EPS;                   // segments per q/k row
-      constexpr int NSEG = 64 * SPR / kThreads;       // per thread
+    // ---------------- a1: staged registers -> LDS; a2: gates ----------------
 #pragma unroll
-      for (int j = 0; j < NSEG; ++j) {
-        const int seg = tid + kThreads * j;
-        const int r = seg / SPR, c0 = (seg % SPR) * EPS;
-        uint4 kraw = make_uint4(0u, 0u, 0u, 0u), qraw = make_uint4(0u, 0u, 0u, 0u);
-        if (r < nv) {
-          const int64_t off = (int64_t)(t0 + r) * qk_row + (int64_t)h * DK + c0;
-          kraw = *reinterpret_cast<const uint4*>(gk_ + off);
-          qraw = *reinterpret_cast<const uint4*>(gq_ + off);
-        }
-        // row-major copies (LDS element type == I/O element type here)
-        *reinterpret_cast<uint4*>(sK + r * LDK + c0) = kraw;
-        *reinterpret_cast<uint4*>(sQ + r * LDK + c0) = qraw;
-        TIO kv[EPS];
-        __builtin_memcpy(kv, &kraw, 16);
+    for (int j = 0; j < NPK; ++j) {
+      const int rp = tid / SPR + (kThreads / SPR) * j, c0 = (tid % SPR) * EPS;
+      *reinterpret_cast<uint4*>(sK + (2 * rp) * LDK + c0) = pk[j][0];
+      *reinterpret_cast<uint4*>(sK + (2 * rp + 1) * LDK + c0) = pk[j][1];
+      *reinterpret_cast<uint4*>(sQ + (2 * rp) * LDK + c0) = pq[j][0];
+      *reinterpret_cast<uint4*>(sQ + (2 * rp + 1) * LDK + c0) = pq[j][1];
+      E k0[EPS], k1[EPS];
+      __builtin_memcpy(k0, &pk[j][0], 16);
+      __builtin_memcpy(k1, &pk[j][1], 16);
 #pragma unroll
-        for (int e = 0; e < EPS; ++e) sKT[(c0 + e) * L64 + r] = kv[e];
-      }
-      constexpr int VSPR = 64 / EPS;
-      constexpr int VNSEG = 64 * VSPR / kThreads;
-#pragma unroll
-      for (int j = 0; j < VNSEG; ++j) {
-        const int seg = tid + kThreads * j;
-        const int r = seg / VSPR, c0 = (seg % VSPR) * EPS;
-        uint4 vraw = make_uint4(0u, 0u, 0u, 0u);
-        if (r < nv) {
-          const int64_t off = (int64_t)(t0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + c0;
-          vraw = *reinterpret_cast<const uint4*>(gv_ + off);
-        }
-        TIO vv[EPS];
-        __builtin_memcpy(vv, &vraw, 16);
-#pragma unroll
-        for (int e = 0; e < EPS; ++e) sVT[(c0 + e) * L64 + r] = vv[e];
-      }
-      // ---------------- a2: gates (wave 0, lane = token) ----------------
-      if (w == 0) {
-        float gv = 0.f, bv = 0.f;
-        if (lane < nv) {
-          gv = args.g[(int64_t)(t0 + lane) * H + h];
-          bv = args.beta[(int64_t)(t0 + lane) * H + h];
-        }
-        float x = gv;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(x, off, 64);
-          if (lane >= off) x += y;
-        }
-        const float gC = __shfl(x, 63, 64);
-        sGam[lane] = x;
-        sEg[lane] = expf(x);
-        sEgc[lane] = expf(gC - x);
-        sBeta[lane] = bv;
-        if (lane == 0) sRed[4] = expf(gC);
-      }
+      for (int e = 0; e < EPS; ++e) Eng::store_pair(sKT + (c0 + e) * L64 + 2 * rp, k0[e], k1[e]);
     }
+#pragma unroll
+    for (int j = 0; j < NPV; ++j) {
+      const int rp = tid / VSPR + (kThreads / VSPR) * j, c0 = (tid % VSPR) * EPS;
+      E v0[EPS], v1[EPS];
+      __builtin_memcpy(v0, &pv[j][0], 16);
+      __builtin_memcpy(v1, &pv[j][1], 16);
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) Eng::store_pair(sVT + (c0 + e) * L64 + 2 * rp, v0[e], v1[e]);
+    }
+    if (w == 0) {
+      float x = pg;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      const float gC = __shfl(x, 63, 64);
+      sG2[lane] = x * kLog2e;
+      sEg[lane] = __builtin_amdgcn_exp2f(x * kLog2e);
+      sEgc[lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
+      sBeta[lane] = pb;
+      if (lane == 0) sRed[4] = __builtin_amdgcn_exp2f(gC * kLog2e);
+    }
+    if (c + 1 < n_chunks) fetch(c + 1);   // lands in registers while this chunk computes
     __syncthreads();
 
     // ---------------- a3: A (strict lower) and P (lower incl. diagonal) ----------------
-    // Job list: 10 lower tiles of A, 10 lower tiles of P, 2 zero tiles of P.
-    for (int job = w; job < 22; job += 4) {
-      int si, ri, kind;  // kind 0: A, 1: P, 2: P zero tile
-      if (job < 20) {
-        const int jj = job % 10;
-        kind = job / 10;
-        ri = (jj < 1) ? 0 : (jj < 3) ? 1 : (jj < 6) ? 2 : 3;
-        si = jj - (ri * (ri + 1)) / 2;
-      } else {
-        kind = 2;
-        si = (job == 20) ? 1 : 3;
-        ri = si - 1;
-      }
-      if (kind == 2) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        Eng::store4_split(sPh + (16 * ri + ln) * L64 + 16 * si + 4 * gq,
-                          sPl + (16 * ri + ln) * L64 + 16 * si + 4 * gq, z);
-        continue;
-      }
-      // C[s][r] = sum_d K[s][d] * (K or Q)[r][d]
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const E* arow = sK + (16 * si + ln) * LDK;
-      const E* brow = (kind == 0 ? sK : sQ) + (16 * ri + ln) * LDK;
+    // Waves 0, 1 compute A, waves 2, 3 compute P; each takes the row blocks
+    // {0, 3} or {1, 2} (five lower 16x16 tiles either way).
+    {
+      const bool isP = (w >> 1) != 0;
+      const int ra = (w & 1) ? 1 : 0, rb = (w & 1) ? 2 : 3;
+      const E* bsrc = isP ? sQ : sK;
+      Fr bfa[NKB], bfb[NKB], af[4][NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) Eng::mma(acc, Eng::load(arow, kb, gq), Eng::load(brow, kb, gq));
-      const int r = 16 * ri + ln;
-      const float gr = sGam[r];
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = 16 * si + 4 * gq + i;
-        const bool keep = (kind == 0) ? (s < r) : (s <= r);
-        x[i] = keep ? expf(gr - sGam[s]) * acc[i] : 0.f;
+      for (int kb = 0; kb < NKB; ++kb) {
+        bfa[kb] = Eng::load(bsrc + (16 * ra + ln) * LDK, kb, gq);
+        bfb[kb] = Eng::load(bsrc + (16 * rb + ln) * LDK, kb, gq);
       }
-      if (kind == 0) {
+#pragma unroll
+      for (int si = 0; si < 4; ++si)
+        if (si <= rb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) af[si][kb] = Eng::load(sK + (16 * si + ln) * LDK, kb, gq);
+      f32x4 acc[2][4];
+#pragma unroll
+      for (int si = 0; si < 4; ++si) {
+        acc[0][si] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[1][si] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int si = 0; si < 4; ++si) {
+          if (si <= ra) Eng::mma(acc[0][si], af[si][kb], bfa[kb]);
+          if (si <= rb) Eng::mma(acc[1][si], af[si][kb], bfb[kb]);
+        }
+      // acc[x][si][i] = C[s][r], s = 16 si + 4 gq + i, r = 16 ri + ln
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int ri = x ? rb : ra;
+        const int r = 16 * ri + ln;
+        const float g2r = sG2[r];
         const float br = sBeta[r];
-        *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) =
-            make_float4(br * x[0], br * x[1], br * x[2], br * x[3]);
-      } else {
-        Eng::store4_split(sPh + r * L64 + 16 * si + 4 * gq, sPl + r * L64 + 16 * si + 4 * gq, x);
+#pragma unroll
+        for (int si = 0; si < 4; ++si) {
+          float v[4];
+          if (si <= ri) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int s = 16 * si + 4 * gq + i;
+              const bool keep = isP ? (s <= r) : (s < r);
+              v[i] = keep ? __builtin_amdgcn_exp2f(g2r - sG2[s]) * acc[x][si][i] : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = 0.f;
+          }
+          if (isP) {
+            Eng::store4_split(sPh + r * L64 + 16 * si + 4 * gq, sPl + r * L64 + 16 * si + 4 * gq, v);
+          } else if (si <= ri) {
+            *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) =
+                make_float4(br * v[0], br * v[1], br * v[2], br * v[3]);
+          }
+        }
       }
     }
     __syncthreads();
 
     // ---------------- a4: X = (I + A)^-1, blocked, fp32 ----------------
     if (w == 0) {
-      // diagonal blocks: lane = (block bi, column cc); forward substitution down the column
+      // diagonal block bi, column cc: x[r] = delta(r, cc) - sum_{s<r} A[r][s] x[s],
+      // evaluated column-oriented (after x[s] is final, update every later row)
       const int bi = lane >> 4, cc = lane & 15;
-      float xcol[16];
+      const float* Ab = sA + 16 * bi * L64 + 16 * bi;
+      float a[16][16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == cc) ? 1.f : 0.f;
-        const float* arow = sA + (16 * bi + r) * L64 + 16 * bi;
+      for (int r = 1; r < 16; ++r)
 #pragma unroll
-        for (int s = 0; s < r; ++s) acc -= arow[s] * xcol[s];
-        xcol[r] = acc;
-      }
+        for (int q4 = 0; q4 * 4 < r; ++q4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(Ab + r * L64 + 4 * q4);
+          a[r][4 * q4] = v4.x; a[r][4 * q4 + 1] = v4.y; a[r][4 * q4 + 2] = v4.z; a[r][4 * q4 + 3] = v4.w;
+        }
+      float xc[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sX[(16 * bi + r) * L64 + 16 * bi + cc] = xcol[r];
+      for (int r = 0; r < 16; ++r) xc[r] = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < 16; ++s)
+#pragma unroll
+        for (int r = s + 1; r < 16; ++r) xc[r] = fmaf(-a[r][s], xc[s], xc[r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sX[(16 * bi + r) * L64 + 16 * bi + cc] = xc[r];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(sXT + (16 * bi + cc) * L64 + 16 * bi + 4 * q4) =
+            make_float4(xc[4 * q4], xc[4 * q4 + 1], xc[4 * q4 + 2], xc[4 * q4 + 3]);
     }
     __syncthreads();
     {
       const int r = tid >> 4, cc = tid & 15;
 #pragma unroll
       for (int d = 1; d < 4; ++d) {
-        // R_ij = sum_{k=j}^{i-1} A_ik X_kj  for blocks (i, j) = (d + b, b)
+        // R_ij = sum_{k=j}^{i-1} A_ik X_kj for blocks (i, j) = (d + b, b); stored transposed
 #pragma unroll
         for (int b = 0; b + d < 4; ++b) {
           const int i = d + b, j = b;
           float acc = 0.f;
-          for (int kk = j; kk < i; ++kk) {
-            const float* arow = sA + (16 * i + r) * L64 + 16 * kk;
-            const float* xcol = sX + (16 * kk) * L64 + 16 * j + cc;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) acc += arow[s] * xcol[s * L64];
-          }
-          sR[b * 256 + r * 16 + cc] = acc;
+          for (int kk = j; kk < i; ++kk)
+            acc += dot16(sA + (16 * i + r) * L64 + 16 * kk, sXT + (16 * j + cc) * L64 + 16 * kk);
+          sRT[b * 256 + cc * 16 + r] = acc;
         }
         __syncthreads();
         // X_ij = -X_ii R_ij
 #pragma unroll
         for (int b = 0; b + d < 4; ++b) {
           const int i = d + b, j = b;
-          const float* xrow = sX + (16 * i + r) * L64 + 16 * i;
-          float acc = 0.f;
-#pragma unroll
-          for (int s = 0; s < 16; ++s) acc += xrow[s] * sR[b * 256 + s * 16 + cc];
-          sX[(16 * i + r) * L64 + 16 * j + cc] = -acc;
+          const float xv = -dot16(sX + (16 * i + r) * L64 + 16 * i, sRT + b * 256 + cc * 16);
+          sX[(16 * i + r) * L64 + 16 * j + cc] = xv;
+          sXT[(16 * j + cc) * L64 + 16 * i + r] = xv;
         }
         __syncthreads();
       }
     }
     // T = X diag(beta), T' = T diag(e^gamma); zero above the block diagonal.
     {
-      const int r = tid >> 2, q4 = (tid & 3) * 16;
+      const int r = tid >> 2, q16 = (tid & 3) * 16;
+      const bool below = (q16 >> 4) <= (r >> 4);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int s0 = q4 + 4 * u;
-        float tv[4], tg[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = s0 + e;
-          const float xv = ((s >> 4) <= (r >> 4)) ? sX[r * L64 + s] : 0.f;
-          tv[e] = xv * sBeta[s];
-          tg[e] = tv[e] * sEg[s];
-        }
+        const int s0 = q16 + 4 * u;
+        float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (below) x4 = *reinterpret_cast<const float4*>(sX + r * L64 + s0);
+        const float4 b4 = *reinterpret_cast<const float4*>(sBeta + s0);
+        const float4 e4 = *reinterpret_cast<const float4*>(sEg + s0);
+        const float tv[4] = {x4.x * b4.x, x4.y * b4.y, x4.z * b4.z, x4.w * b4.w};
+        const float tg[4] = {tv[0] * e4.x, tv[1] * e4.y, tv[2] * e4.z, tv[3] * e4.w};
         Eng::store4_split(sTh + r * L64 + s0, sTl + r * L64 + s0, tv);
         Eng::store4_split(sTgh + r * L64 + s0, sTgl + r * L64 + s0, tg);
       }
@@ -438,44 +523,53 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
     __syncthreads();
 
     // ---------------- a5: W^T = K^T T'^T (-> sW row-major), U = T V ----------------
-    {
-      constexpr int DPW = NT / 4;  // dk tiles of W^T per wave
-#pragma unroll
-      for (int dd = 0; dd < DPW; ++dd) {
-        const int di = DPW * w + dd;
-        const E* arow = sKT + (16 * di + ln) * L64;
-        Fr a0 = Eng::load(arow, 0, gq);
-        Fr a1 = Eng::load(arow, 1, gq);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const E* bh = sTgh + (16 * ti + ln) * L64;
-          Eng::mma(acc, a0, Eng::load(bh, 0, gq));
-          if constexpr (Eng::kSplit) Eng::mma(acc, a0, Eng::load(sTgl + (16 * ti + ln) * L64, 0, gq));
-          if (ti >= 2) {
-            Eng::mma(acc, a1, Eng::load(bh, 1, gq));
-            if constexpr (Eng::kSplit) Eng::mma(acc, a1, Eng::load(sTgl + (16 * ti + ln) * L64, 1, gq));
-          }
-          // acc[i] = W^T[16di + 4gq + i][16ti + ln] = W[16ti + ln][16di + 4gq + i]
-          Eng::store4(sW + (16 * ti + ln) * LDK + 16 * di + 4 * gq, acc[0], acc[1], acc[2], acc[3]);
-        }
-      }
-    }
     f32x4 uacc[4];
     {
-      const E* brow = sVT + (16 * w + ln) * L64;
-      const Fr b0 = Eng::load(brow, 0, gq);
-      const Fr b1 = Eng::load(brow, 1, gq);
+      constexpr int DPW = NT / 4;  // dk tiles of W^T per wave
+      Fr ka[DPW][2], tgh[6], tgl[6], th[6], tl[6], vb[2];
+      // (ti, kb) pairs of the lower-triangular T: (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        uacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Eng::mma(uacc[ti], Eng::load(sTh + (16 * ti + ln) * L64, 0, gq), b0);
-        if constexpr (Eng::kSplit) Eng::mma(uacc[ti], Eng::load(sTl + (16 * ti + ln) * L64, 0, gq), b0);
-        if (ti >= 2) {
-          Eng::mma(uacc[ti], Eng::load(sTh + (16 * ti + ln) * L64, 1, gq), b1);
-          if constexpr (Eng::kSplit) Eng::mma(uacc[ti], Eng::load(sTl + (16 * ti + ln) * L64, 1, gq), b1);
+      for (int p = 0; p < 6; ++p) {
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        tgh[p] = Eng::load(sTgh + (16 * ti + ln) * L64, kb, gq);
+        th[p] = Eng::load(sTh + (16 * ti + ln) * L64, kb, gq);
+        if constexpr (Eng::kSplit) {
+          tgl[p] = Eng::load(sTgl + (16 * ti + ln) * L64, kb, gq);
+          tl[p] = Eng::load(sTl + (16 * ti + ln) * L64, kb, gq);
         }
       }
+#pragma unroll
+      for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ka[dd][kb] = Eng::load(sKT + (16 * (DPW * w + dd) + ln) * L64, kb, gq);
+      vb[0] = Eng::load(sVT + (16 * w + ln) * L64, 0, gq);
+      vb[1] = Eng::load(sVT + (16 * w + ln) * L64, 1, gq);
+
+      f32x4 wacc[DPW][4];
+#pragma unroll
+      for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) wacc[dd][ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) uacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+#pragma unroll
+        for (int dd = 0; dd < DPW; ++dd) {
+          Eng::mma(wacc[dd][ti], ka[dd][kb], tgh[p]);
+          if constexpr (Eng::kSplit) Eng::mma(wacc[dd][ti], ka[dd][kb], tgl[p]);
+        }
+        Eng::mma(uacc[ti], th[p], vb[kb]);
+        if constexpr (Eng::kSplit) Eng::mma(uacc[ti], tl[p], vb[kb]);
+      }
+      // wacc[dd][ti][i] = W^T[16di + 4gq + i][16ti + ln] = W[16ti + ln][16di + 4gq + i]
+#pragma unroll
+      for (int dd = 0; dd < DPW; ++dd)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+          Eng::store4(sW + (16 * ti + ln) * LDK + 16 * (DPW * w + dd) + 4 * gq, wacc[dd][ti][0],
+                      wacc[dd][ti][1], wacc[dd][ti][2], wacc[dd][ti][3]);
     }
     __syncthreads();  // sW complete
 
@@ -488,68 +582,131 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
       wacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
       oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float sv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = st[2 * kb][i];
-        sv[4 + i] = st[2 * kb + 1][i];
-      }
-      Fr bh, bl;
-      if (use_codes) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] *= inv_s;  // the codes, exact in bf16
-        bh = Eng::round(sv);
-      } else {
-        Eng::split(sv, bh, bl);
-      }
+    {
+      Fr aw[2][4], aq[2][4];
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const Fr aw = Eng::load(sW + (16 * ti + ln) * LDK, kb, gq);
-        const Fr aq = Eng::load(sQ + (16 * ti + ln) * LDK, kb, gq);
-        Eng::mma(wacc[ti], aw, bh);
-        Eng::mma(oacc[ti], aq, bh);
+        aw[0][ti] = Eng::load(sW + (16 * ti + ln) * LDK, 0, gq);
+        aq[0][ti] = Eng::load(sQ + (16 * ti + ln) * LDK, 0, gq);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int cur = kb & 1;
+        if (kb + 1 < NKB) {
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) {
+            aw[cur ^ 1][ti] = Eng::load(sW + (16 * ti + ln) * LDK, kb + 1, gq);
+            aq[cur ^ 1][ti] = Eng::load(sQ + (16 * ti + ln) * LDK, kb + 1, gq);
+          }
+        }
+        float sv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = st[2 * kb][i];
+          sv[4 + i] = st[2 * kb + 1][i];
+        }
+        Fr bh, bl;
+        if (use_codes) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sv[j] *= inv_s;  // the codes, exact in bf16
+          bh = Eng::round(sv);
+        } else {
+          Eng::split(sv, bh, bl);
+        }
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          Eng::mma(wacc[ti], aw[cur][ti], bh);
+          Eng::mma(oacc[ti], aq[cur][ti], bh);
+        }
         if constexpr (Eng::kSplit) {
           if (!use_codes) {
-            Eng::mma(wacc[ti], aw, bl);
-            Eng::mma(oacc[ti], aq, bl);
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+              Eng::mma(wacc[ti], aw[cur][ti], bl);
+              Eng::mma(oacc[ti], aq[cur][ti], bl);
+            }
           }
         }
       }
     }
+    // P fragments for the intra-chunk product (issued before the VALU work below)
+    Fr ph[6], pl[6];
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+      ph[p] = Eng::load(sPh + (16 * ti + ln) * L64, kb, gq);
+      if constexpr (Eng::kSplit) pl[p] = Eng::load(sPl + (16 * ti + ln) * L64, kb, gq);
+    }
     const float sc = use_codes ? s_cur : 1.0f;
     // U' = U - W S^T (fp32), rows 16ti + 4gq + i, column vcol
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int ti = 0; ti < 4; ++ti) {
+      const float4 eg = *reinterpret_cast<const float4*>(sEg + 16 * ti + 4 * gq);
+      const float egv[4] = {eg.x, eg.y, eg.z, eg.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uacc[ti][i] = uacc[ti][i] - sc * wacc[ti][i];
-        oacc[ti][i] = sEg[16 * ti + 4 * gq + i] * (sc * oacc[ti][i]);
+        uacc[ti][i] = fmaf(-sc, wacc[ti][i], uacc[ti][i]);
+        oacc[ti][i] = egv[i] * (sc * oacc[ti][i]);
       }
+    }
 
     // ---------------- a7 (intra-chunk part): O += P U' ----------------
+    {
+      Fr uh[2], ul[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float uv[8];
+      for (int kb = 0; kb < 2; ++kb) {
+        float uv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uv[i] = uacc[2 * kb][i];
-        uv[4 + i] = uacc[2 * kb + 1][i];
+        for (int i = 0; i < 4; ++i) {
+          uv[i] = uacc[2 * kb][i];
+          uv[4 + i] = uacc[2 * kb + 1][i];
+        }
+        Eng::split(uv, uh[kb], ul[kb]);
       }
-      Fr bh, bl;
-      Eng::split(uv, bh, bl);
 #pragma unroll
-      for (int ti = 2 * kb; ti < 4; ++ti) {
-        const Fr ah = Eng::load(sPh + (16 * ti + ln) * L64, kb, gq);
-        Eng::mma(oacc[ti], ah, bh);
+      for (int p = 0; p < 6; ++p) {
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        Eng::mma(oacc[ti], ph[p], uh[kb]);
         if constexpr (Eng::kSplit) {
-          const Fr al = Eng::load(sPl + (16 * ti + ln) * L64, kb, gq);
-          Eng::mma(oacc[ti], ah, bl);
-          Eng::mma(oacc[ti], al, bh);
+          Eng::mma(oacc[ti], ph[p], ul[kb]);
+          Eng::mma(oacc[ti], pl[p], uh[kb]);
         }
       }
     }
+
+    // ---------------- a8: S^T <- e^gC S^T + K^T diag(e^(gC - gamma)) U' ----------------
+    {
+      Fr ka[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        ka[t][0] = Eng::load(sKT + (16 * t + ln) * L64, 0, gq);
+        ka[t][1] = Eng::load(sKT + (16 * t + ln) * L64, 1, gq);
+      }
+      Fr bh[2], bl[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float4 e0 = *reinterpret_cast<const float4*>(sEgc + 32 * kb + 4 * gq);
+        const float4 e1 = *reinterpret_cast<const float4*>(sEgc + 32 * kb + 16 + 4 * gq);
+        const float uv[8] = {e0.x * uacc[2 * kb][0], e0.y * uacc[2 * kb][1], e0.z * uacc[2 * kb][2],
+                             e0.w * uacc[2 * kb][3], e1.x * uacc[2 * kb + 1][0],
+                             e1.y * uacc[2 * kb + 1][1], e1.z * uacc[2 * kb + 1][2],
+                             e1.w * uacc[2 * kb + 1][3]};
+        Eng::split(uv, bh[kb], bl[kb]);
+      }
+      const float aC = sRed[4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[t][i] *= aC;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          Eng::mma(st[t], ka[t][kb], bh[kb]);
+          if constexpr (Eng::kSplit) Eng::mma(st[t], ka[t][kb], bl[kb]);
+        }
+    }
+
     // store o rows (valid tokens only)
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
@@ -558,32 +715,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
         const int r = 16 * ti + 4 * gq + i;
         if (r < nv) io<TO>::st(go_ + (int64_t)(t0 + r) * v_row + (int64_t)h * dv + vcol0, oacc[ti][i]);
       }
-
-    // ---------------- a8: S^T <- e^gC S^T + K^T diag(e^(gC - gamma)) U' ----------------
-    {
-      const float aC = sRed[4];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[t][i] *= aC;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float uv[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uv[i] = sEgc[32 * kb + 4 * gq + i] * uacc[2 * kb][i];
-          uv[4 + i] = sEgc[32 * kb + 16 + 4 * gq + i] * uacc[2 * kb + 1][i];
-        }
-        Fr bh, bl;
-        Eng::split(uv, bh, bl);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const Fr a = Eng::load(sKT + (16 * t + ln) * L64, kb, gq);
-          Eng::mma(st[t], a, bh);
-          if constexpr (Eng::kSplit) Eng::mma(st[t], a, bl);
-        }
-      }
-    }
 
     // ---------------- a9: boundary QDQ ----------------
     const bool last = (c == n_chunks - 1);
@@ -604,13 +735,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
         for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t][i]));
       amax = block_max(amax, sRed);  // also orders this chunk's LDS reads before the next chunk's writes
       s_new = qdq_scale(amax);
+      const float r = 1.0f / s_new;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[t][i] = qdq_value(st[t][i], s_new);
+      for (int t = 0; t < NT; ++t) qdq4(st[t], s_new, r);
       coded = true;
       s_cur = s_new;
-      inv_s = 1.0f / s_new;
+      inv_s = r;
     } else {
       coded = false;
       __syncthreads();
@@ -629,7 +759,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
     float* sq = sA;          // q_t, k_t: DK each; v_t: 64
     float* sk = sA + 256;
     float* sv = sA + 512;
-    float* sg = sA + 640;    // g_t (scalar) / DK values; beta at sg[DK]
+    float* sg = sA + 640;    // g_t at sg[0], beta_t at sg[DK]
     for (int t = P; t < L; ++t) {
       const int64_t row = seg0 + t;
       if (tid < DK) {
@@ -674,10 +804,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
           for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t2][i]));
         amax = block_max(amax, sRed);
         const float s = qdq_scale(amax);
+        const float r = 1.0f / s;
 #pragma unroll
-        for (int t2 = 0; t2 < NT; ++t2)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st[t2][i] = qdq_value(st[t2][i], s);
+        for (int t2 = 0; t2 < NT; ++t2) qdq4(st[t2], s, r);
       } else {
         __syncthreads();
       }
@@ -697,7 +826,7 @@ template <int DK, class Eng, typename TIO, typename TO>
 static hipError_t launch_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
   auto kern = chunk_fwd_kernel<DK, Eng, TIO, TO>;
   constexpr size_t lds = Smem<DK, Eng>::bytes;
-  static bool attr_set = false;  // per process; the attribute is per function
+  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -99,13 +99,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   if (do_qdq) {
     amax = block_max(amax, red);
     s = qdq_scale(amax);
+    const float r = 1.0f / s;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      x[p].x = qdq_value(x[p].x, s);
-      x[p].y = qdq_value(x[p].y, s);
-      x[p].z = qdq_value(x[p].z, s);
-      x[p].w = qdq_value(x[p].w, s);
-    }
+    for (int p = 0; p < NP; ++p) qdq4(x[p], s, r);
   }
 #pragma unroll
   for (int p = 0; p < NP; ++p) S[t + kThreads * p] = x[p];

@@ -9,42 +9,60 @@
 namespace gdn {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
 constexpr int kChunk = 64;     // tokens per chunk
 constexpr int kTileRows = 64;  // value rows per QDQ tile
 constexpr int kThreads = 256;  // 4 waves of 64
 
 // ---------------------------------------------------------------------------
-// OCP E4M3FN rounding in the value domain.  Returns the E4M3 value nearest to
-// y (ties to the even code), saturating at +-448.  Normals (|y| >= 2^-6) keep
-// 3 mantissa bits: add half an E4M3 ulp minus one plus the kept LSB, then
-// clear the 20 dropped bits (round to nearest even on the bit pattern).
-// Below 2^-6 the grid is the multiples of 2^-9: y * 2^9 is exact, rintf
-// rounds to nearest even.  NaN propagates.
+// State QDQ arithmetic, IEEE fp32 throughout:
+//   s = amax / 448 (IEEE division; 1 when not positive, the zero guard)
+//   y = x / s      (IEEE division, computed as below)
+//   c = E4M3FN value nearest to y, ties to even (hardware conversion)
+//   x <- c * s     (sign of x kept for zeros)
+//
+// x / s is evaluated from r = RN(1 / s) (one IEEE division per tile): q = x r
+// is within about 1.5 ulp of x / s, and each step q <- q + r (x - s q), with
+// the remainder x - s q exact in an fma, is Markstein's correction; after two
+// steps q is the correctly rounded quotient (results in the fp32 subnormal
+// range, which all map to code 0, excepted).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float e4m3_rne(float y) {
-  float a = fabsf(y);
-  float r;
-  if (a >= 0.015625f) {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    b &= 0xFFF00000u;
-    r = fminf(__uint_as_float(b), 448.0f);
-  } else {
-    r = rintf(a * 512.0f) * 0.001953125f;
-  }
-  return copysignf(r, y);
-}
-
-// QDQ scale of a tile: amax / 448 as an IEEE division, 1 when not positive.
 __device__ __forceinline__ float qdq_scale(float amax) {
   float s = amax / 448.0f;
   return (s > 0.0f) ? s : 1.0f;
 }
 
-// x -> RNE_E4M3(x / s) * s, both operations IEEE fp32.
-__device__ __forceinline__ float qdq_value(float x, float s) { return e4m3_rne(x / s) * s; }
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  float q = x * r;
+  float e = fmaf(-s, q, x);
+  q = fmaf(e, r, q);
+  e = fmaf(-s, q, x);
+  return fmaf(e, r, q);
+}
+
+// QDQ of two values with scale s and r = RN(1 / s).  gfx950's
+// v_cvt_pk_fp8_f32 rounds to the nearest OCP E4M3FN value (ties to even).
+__device__ __forceinline__ void qdq2(float& x0, float& x1, float s, float r) {
+  const float y0 = div_rn(x0, s, r), y1 = div_rn(x1, s, r);
+  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  x0 = copysignf(__builtin_amdgcn_cvt_f32_fp8(p, 0) * s, x0);
+  x1 = copysignf(__builtin_amdgcn_cvt_f32_fp8(p, 1) * s, x1);
+}
+
+__device__ __forceinline__ void qdq4(float4& v, float s, float r) {
+  qdq2(v.x, v.y, s, r);
+  qdq2(v.z, v.w, s, r);
+}
+
+__device__ __forceinline__ void qdq4(f32x4& v, float s, float r) {
+  float a = v[0], b = v[1], c = v[2], d = v[3];
+  qdq2(a, b, s, r);
+  qdq2(c, d, s, r);
+  v = f32x4{a, b, c, d};
+}
 
 // ---------------------------------------------------------------------------
 // Reductions in a fixed order (the same tree on every call).
@@ -79,11 +97,18 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-__device__ __forceinline__ __bf16 to_bf16(float x) {
-  return __builtin_bit_cast(__bf16, float_to_bf16_bits(x));
+// Two values -> two bf16 (round to nearest even, one v_cvt_pk_bf16_f32),
+// first value in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
-__device__ __forceinline__ float from_bf16(__bf16 x) {
-  return bf16_bits_to_float(__builtin_bit_cast(uint16_t, x));
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+// hi + lo split of two values: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
 }
 
 // Element loads/stores by I/O type.

@@ -33,16 +33,13 @@ __global__ __launch_bounds__(kThreads) void state_qdq_kernel(const float* in,
   }
   amax = block_max(amax, red);
   const float s = qdq_scale(amax);
+  const float r = 1.0f / s;
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
     int idx = threadIdx.x + kThreads * j;
     if (idx < n4) {
-      float4 y;
-      y.x = qdq_value(x[j].x, s);
-      y.y = qdq_value(x[j].y, s);
-      y.z = qdq_value(x[j].z, s);
-      y.w = qdq_value(x[j].w, s);
-      dst[idx] = y;
+      qdq4(x[j], s, r);
+      dst[idx] = x[j];
     }
   }
   if (scales != nullptr && threadIdx.x == 0) scales[tile] = s;

@@ -194,3 +194,57 @@ def device_tensors(w: Workload, device="cuda"):
     """All inputs of a workload as device tensors (dict)."""
     return {name: to_torch(getattr(w, name), device)
             for name in ("q", "k", "v", "beta", "g", "cu_seqlens", "seq_lens", "prefix_lens")}
+
+
+def device_packed(seq_lens, n_heads, dk, dv, *, io_dtype=BF16, per_channel=False, g_scale=0.1,
+                  seed=0, device="cuda"):
+    """Same distributions as make_packed, drawn on the device with torch's
+    seeded Philox generator (for workloads too large to draw on the host).
+    Transforms run in fp32 on the device, then round to the I/O dtype.
+    Returns a dict of device tensors (q, k, v, beta, g, cu_seqlens)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    lens = torch.as_tensor(np.asarray(seq_lens, np.int64))
+    T = int(lens.sum())
+    H = n_heads
+    dt = torch.bfloat16 if io_dtype == BF16 else torch.float32
+
+    def unit(d):
+        x = torch.randn((T, H, d), generator=gen, device=device, dtype=torch.float32)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(dt)
+
+    q = unit(dk)
+    k = unit(dk)
+    v = torch.randn((T, H, dv), generator=gen, device=device, dtype=torch.float32).to(dt)
+    beta = torch.sigmoid(torch.randn((T, H), generator=gen, device=device))
+    gshape = (T, H, dk) if per_channel else (T, H)
+    g = -torch.nn.functional.softplus(torch.randn(gshape, generator=gen, device=device)) * g_scale
+    cu = torch.zeros(lens.numel() + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    return dict(q=q, k=k, v=v, beta=beta.contiguous(), g=g.contiguous(), cu_seqlens=cu.to(device))
+
+
+def device_decode_tokens(n_seqs, n_heads, dk, dv, steps, *, io_dtype=BF16, per_channel=False,
+                         g_scale=0.1, seed=1, device="cuda"):
+    """Decode tokens for `steps` steps drawn on the device: dict of tensors
+    with a leading step axis (q, k [steps, N, H, dk], v, beta, g)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = torch.bfloat16 if io_dtype == BF16 else torch.float32
+    shp = (steps, n_seqs, n_heads)
+
+    def unit(d):
+        x = torch.randn(shp + (d,), generator=gen, device=device)
+        x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x.to(dt)
+
+    q = unit(dk)
+    k = unit(dk)
+    v = torch.randn(shp + (dv,), generator=gen, device=device).to(dt)
+    beta = torch.sigmoid(torch.randn(shp, generator=gen, device=device))
+    g = -torch.nn.functional.softplus(
+        torch.randn(shp + ((dk,) if per_channel else ()), generator=gen, device=device)) * g_scale
+    return dict(q=q, k=k, v=v, beta=beta, g=g)

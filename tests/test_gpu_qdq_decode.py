@@ -35,6 +35,33 @@ def test_state_qdq_bit_exact(dv, dk):
     np.testing.assert_array_equal(scales.cpu().numpy(), sc)
 
 
+def test_state_qdq_many_scales_bit_exact():
+    """4096 tiles, each with its own scale (random amax mantissa and
+    exponent) and elements with random fp32 bit patterns below amax: the
+    device QDQ (quotient by reciprocal plus correction steps, hardware E4M3
+    rounding) equals the oracle's IEEE x / s decision bit for bit."""
+    rng = np.random.default_rng(123)
+    n = 4096
+    amax = (rng.uniform(1.0, 2.0, n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
+    mant = rng.integers(0, 1 << 23, size=(n, 64 * 128), dtype=np.uint32)
+    expo = rng.integers(0, 40, size=(n, 64 * 128), dtype=np.uint32)
+    top = amax.view(np.uint32) >> 23
+    e = np.clip(top[:, None].astype(np.int64) - expo.astype(np.int64), 1, 254).astype(np.uint32)
+    x = ((e << 23) | mant).view(np.float32)
+    x = np.where(np.abs(x) > amax[:, None], amax[:, None], x)
+    sign = rng.integers(0, 2, size=x.shape).astype(bool)
+    x = np.where(sign, -x, x).astype(np.float32)
+    x[:, 0] = amax
+    x = x.reshape(n, 64, 128)
+    want, sc, _ = orc.qdq_states(x)
+    out, scales = api.state_qdq(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bad = np.flatnonzero(got.view(np.uint32).ravel() != want.view(np.uint32).ravel())
+    assert bad.size == 0, (bad.size, x.ravel()[bad[:4]], got.ravel()[bad[:4]], want.ravel()[bad[:4]])
+    np.testing.assert_array_equal(scales.cpu().numpy().ravel(), sc.ravel())
+
+
 def test_state_qdq_in_place_and_already_e4m3():
     rng = np.random.default_rng(1)
     grid = orc.e4m3_decode(np.arange(127, dtype=np.uint8))
