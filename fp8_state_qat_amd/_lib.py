@@ -21,8 +21,8 @@ GDN_BF16 = 1
 GDN_QDQ_CHUNK = 1
 GDN_QDQ_WRITE = 2
 
-EXPORTS = ("gdn_chunk_fwd", "gdn_state_qdq", "gdn_decode_step", "gdn_status_string",
-           "gdn_last_error")
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_state_qdq", "gdn_decode_step",
+           "gdn_status_string", "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
@@ -69,8 +69,10 @@ def lib():
             "g.build()'` (or python fp8_state_qat_amd/build.py)")
     L = ctypes.CDLL(LIB_PATH)
     L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                _vp, _vp, _vp, ctypes.POINTER(GdnDebug), _vp]
+                                _vp, _vp, _vp, _vp, ctypes.c_size_t, ctypes.POINTER(GdnDebug), _vp]
     L.gdn_chunk_fwd.restype = ctypes.c_int
+    L.gdn_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
+    L.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_state_qdq.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
     L.gdn_state_qdq.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -36,13 +36,28 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _shape(N, H, dk, dv, T, io_dt, o_dt, per_channel, flags):
+    return GdnShape(N, H, dk, dv, T, _DT[io_dt], _DT[o_dt], 1 if per_channel else 0, int(flags))
+
+
+def chunk_workspace_bytes(N, H, dk, dv, T, io_dtype=torch.bfloat16):
+    """Device workspace gdn_chunk_fwd needs for this shape (bytes)."""
+    shape = _shape(N, H, dk, dv, T, io_dtype, io_dtype, False, 0)
+    n = _lib.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        _lib.check(_lib.GDN_ERR_INVALID_ARG)
+    return n
+
+
 def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
               initial_state=None, qdq_flags=GDN_QDQ_CHUNK | GDN_QDQ_WRITE, o_dtype=None,
-              out=None, final_state=None, debug=None):
+              out=None, final_state=None, workspace=None, debug=None):
     """gdn_chunk_fwd.  q, k: [T, H, dk]; v: [T, H, dv] (fp32 or bf16); beta:
     [T, H] fp32; g: [T, H] or [T, H, dk] fp32; cu_seqlens: [N+1] int32.
-    debug: optional dict with device tensors bound_offsets, bound_pre,
-    bound_post, scales.  Returns (o, final_state)."""
+    workspace: optional uint8 device tensor of chunk_workspace_bytes(...)
+    bytes (allocated here when None).  debug: optional dict with device
+    tensors bound_offsets, bound_pre, bound_post, scales.  Returns (o,
+    final_state)."""
     T, H, dk = k.shape
     dv = v.shape[2]
     N = cu_seqlens.numel() - 1
@@ -60,8 +75,13 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
         final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=k.device)
     _dev(out, "out", o_dtype)
     _dev(final_state, "final_state", torch.float32)
-    shape = GdnShape(N, H, dk, dv, T, _DT[k.dtype], _DT[o_dtype], 1 if g.dim() == 3 else 0,
-                     int(qdq_flags))
+    shape = _shape(N, H, dk, dv, T, k.dtype, o_dtype, g.dim() == 3, qdq_flags)
+    ws_bytes = _lib.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape))
+    if ws_bytes == 0:
+        _lib.check(_lib.GDN_ERR_INVALID_ARG)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
+    _dev(workspace, "workspace", torch.uint8)
     dbg = None
     if debug is not None:
         dbg = GdnDebug(*(_ptr(debug.get(key)) for key in ("bound_offsets", "bound_pre",
@@ -69,6 +89,7 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     st = _lib.lib().gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                   _ptr(g), _ptr(cu_seqlens), _ptr(seq_lens), _ptr(prefix_lens),
                                   _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                  _ptr(workspace), workspace.numel(),
                                   ctypes.byref(dbg) if dbg is not None else None, _stream())
     _lib.check(st)
     return out, final_state

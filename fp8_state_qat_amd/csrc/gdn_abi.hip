@@ -124,14 +124,26 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void
   return GDN_OK;
 }
 
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape) {
+  g_err[0] = 0;
+  if (check_shape(shape, false) != GDN_OK) return 0;
+  return gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
+}
+
 gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
                            const float* beta, const float* g, const int32_t* cu_seqlens,
                            const int32_t* seq_lens, const int32_t* prefix_lens,
                            const float* initial_state, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes,
                            const gdn_debug_t* debug, void* stream) {
   g_err[0] = 0;
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
+  const size_t need = gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (!cu_seqlens || !final_state) return fail(GDN_ERR_INVALID_ARG, "cu_seqlens and final_state must be non-NULL");
   if (shape->total_tokens > 0 && (!q || !k || !v || !beta || !g || !o))
     return fail(GDN_ERR_INVALID_ARG, "q, k, v, beta, g and o must be non-NULL");
@@ -148,7 +160,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   st = check_device();
   if (st != GDN_OK) return st;
   hipError_t e = gdn::launch_chunk_fwd(*shape, q, k, v, beta, g, cu_seqlens, seq_lens, prefix_lens,
-                                       initial_state, o, final_state, debug, (hipStream_t)stream);
+                                       initial_state, o, final_state, workspace, debug,
+                                       (hipStream_t)stream);
   if (e == hipErrorNotSupported) return fail(GDN_ERR_UNSUPPORTED, "configuration not supported");
   if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return GDN_OK;

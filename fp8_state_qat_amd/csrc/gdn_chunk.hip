@@ -1,47 +1,43 @@
-// gdn_chunk.hip -- fused chunked gated delta rule forward with per-boundary
-// FP8-E4M3 state QDQ (Model-Optimizer #2497 "What does this PR do?": 64-token
-// chunks, WY-transformed W, dynamic per-tile state QDQ at every boundary;
-// #2506: exact triangular solve).
+// gdn_chunk.hip -- sequential part of the chunked gated delta rule forward
+// with per-boundary FP8-E4M3 state QDQ (Model-Optimizer #2497 "What does this
+// PR do?": 64-token chunks, WY-transformed W, dynamic per-tile state QDQ at
+// every boundary; #2519: QDQ at the handoff and after every later recurrent
+// write).
 //
 // Work unit: one workgroup (4 waves) per (sequence n, head h, 64-column value
 // tile vt).  It walks its sequence chunk by chunk and keeps its slice of the
-// state, S^T (dk x 64), in registers for the whole sequence: wave w owns value
-// columns 16w..16w+15 of the tile, i.e. dk/16 accumulator tiles.  The 64 x dk
-// state tile is exactly one QDQ tile, so the QDQ amax needs no exchange with
-// other workgroups.
+// state in registers for the whole sequence: wave w owns value columns
+// 16w..16w+15 of the tile, i.e. dk/16 16x16 accumulator tiles of S^T.  The
+// 64 x dk state tile is exactly one QDQ tile, so the QDQ amax needs no
+// exchange with other workgroups.  T = (I + A)^-1 diag(beta) of every chunk
+// comes from the prep kernel (gdn_prep.hip) through the workspace.
 //
-// Per chunk of n <= 64 tokens (rows past n are zero-filled, beta = g = 0, so
-// they drop out of every product), with gamma = in-chunk cumulative log-gate:
-//   a1  stage q, k (row-major and transposed), v (transposed) -> LDS; the
-//       next chunk's q, k, v, beta, g are already in flight to registers
-//   a2  gamma (wave scan), exp(gamma), exp(gamma_C - gamma)
-//   a3  A[r][s] = beta_r exp(gamma_r - gamma_s) k_r.k_s   (s < r)      MFMA
-//       P[r][s] = exp(gamma_r - gamma_s) q_r.k_s          (s <= r)     MFMA
-//   a4  X = (I + A)^-1 by blocked forward substitution in fp32: the four
-//       16 x 16 diagonal blocks column by column, then the off-diagonal
-//       blocks level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj;
-//       T = X diag(beta), T' = T diag(exp(gamma))
-//   a5  W = T' K  (computed as W^T = K^T T'^T so it lands row-major in LDS),
+// Per chunk of n <= 64 tokens (rows past n are zero, beta = g = 0, so they
+// drop out of every product), gamma = in-chunk cumulative log-gate:
+//   a1  stage q, k (row-major and transposed), v (transposed) and T -> LDS;
+//       gamma (wave scan), exp(gamma), exp(gamma_C - gamma).  The next
+//       chunk's inputs are already in flight to registers.
+//   a3  P[r][s] = exp(gamma_r - gamma_s) q_r . k_s  (s <= r)          MFMA
+//   a5  W = T (exp(gamma) * K)  (as W^T = (exp(gamma) * K)^T T^T),
 //       U = T V                                                        MFMA
 //   a6  U' = U - W S^T                                                 MFMA
-//   a7  O  = diag(exp(gamma)) Q S^T + P U'                             MFMA
+//   a7  O^T = diag-scaled S Q^T + U'^T P^T   (o lands 4 values per lane)
 //   a8  S^T <- exp(gamma_C) S^T + K^T diag(exp(gamma_C - gamma)) U'    MFMA
 //   a9  QDQ: amax over the 64 x dk tile (wave + LDS tree), s = amax/448,
 //       S <- RNE_E4M3(S/s) s
 // then the recurrent suffix (tokens P_n < t <= L_n, QDQ after every write)
 // and the final state store.
 //
-// With one wave per SIMD nothing hides latency but the wave's own
-// instruction stream, so every phase issues all of its fragment loads before
-// its MFMAs and keeps several independent accumulators in flight.
+// The state fragment built once per k-block serves as the B operand of
+// W S^T and as the A operand of S Q^T: an accumulator tile already holds, in
+// every lane, the eight k-slots a fragment needs (see gdn_device.hpp).
 //
-// Precision (bf16 inputs, fp32 accumulate): q, k, v enter the MFMAs exactly.
-// T, T', P and U' are fed as hi + lo bf16 pairs (their rounding would cost
-// about 1.6e-3 relative each in o); W enters as one bf16.  After a QDQ the
-// state is code * s with the code exactly representable in bf16, so S^T is
-// fed as the codes and the product is scaled by s afterwards; otherwise
-// (QDQ off, supplied initial state) S^T is fed as a hi + lo pair.  fp32 inputs
-// use the fp32 MFMA throughout.
+// Precision (bf16 inputs, fp32 accumulate): q, k, v enter the MFMAs exactly;
+// T, P and U' as hi + lo bf16 pairs; exp(gamma) * K and W as one bf16 each.
+// After a QDQ the state is code * s with the code exactly representable in
+// bf16, so it is fed as the codes and the products are scaled by s; otherwise
+// (QDQ off, supplied initial state) as a hi + lo pair.  fp32 inputs use the
+// fp32 MFMA throughout.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -73,10 +69,16 @@ struct EngBF16 {
     hi = __builtin_bit_cast(Fr, make_uint4(h[0], h[1], h[2], h[3]));
     lo = __builtin_bit_cast(Fr, make_uint4(l[0], l[1], l[2], l[3]));
   }
+  // fragment with every element j multiplied by f[j] (one rounding)
+  static __device__ __forceinline__ Fr scale(const Fr& x, const float (&f)[8]) {
+    const uint4 u = __builtin_bit_cast(uint4, x);
+    const float v[8] = {bf16_lo(u.x) * f[0], bf16_hi(u.x) * f[1], bf16_lo(u.y) * f[2], bf16_hi(u.y) * f[3],
+                        bf16_lo(u.z) * f[4], bf16_hi(u.z) * f[5], bf16_lo(u.w) * f[6], bf16_hi(u.w) * f[7]};
+    return round(v);
+  }
   static __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
     *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
   }
-  // hi and lo parts of four consecutive values
   static __device__ __forceinline__ void store4_split(E* ph, E* pl, const float (&x)[4]) {
     uint32_t h0, l0, h1, l1;
     split_bf16x2(x[0], x[1], h0, l0);
@@ -114,6 +116,12 @@ struct EngF32 {
     hi = round(x);
     (void)lo;
   }
+  static __device__ __forceinline__ Fr scale(const Fr& x, const float (&f)[8]) {
+    Fr r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.v[j] = x.v[j] * f[j];
+    return r;
+  }
   static __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
   }
@@ -126,38 +134,28 @@ struct EngF32 {
   }
 };
 
-// LDS layout of the chunk kernel (bytes).  Row strides are padded so that
-// the 16 rows read by one fragment load fall in different banks; [64][dk]
+// LDS layout of the sequential kernel (bytes).  Row strides are padded so
+// that the 16 rows read by one fragment load fall in different banks; [64][dk]
 // rows stay 16-byte aligned for the staging stores.
 template <int DK, class Eng>
 struct Smem {
   using E = typename Eng::E;
-  static constexpr int LDK = DK + 16 / (int)sizeof(E);  // stride of [64][DK] buffers (E), 16-byte rows
-  static constexpr int L64 = 64 + 4;                     // stride of [*][64] buffers (E or fp32)
+  static constexpr int LDK = DK + 16 / (int)sizeof(E);  // stride of [64][DK] buffers (E)
+  static constexpr int L64 = 64 + 4;                     // stride of [*][64] buffers (E)
   static constexpr int kSplitN = Eng::kSplit ? 2 : 1;
   static constexpr size_t szK = 64 * LDK * sizeof(E);
   static constexpr size_t szKT = DK * L64 * sizeof(E);
-  static constexpr size_t szVT = 64 * L64 * sizeof(E);
-  static constexpr size_t szF = 64 * L64 * sizeof(float);
-  static constexpr size_t szXW = (szF > szK) ? szF : szK;
   static constexpr size_t szM = 64 * L64 * sizeof(E);  // one 64x64 operand matrix
   static constexpr size_t oK = 0;
   static constexpr size_t oKT = oK + szK;
   static constexpr size_t oQ = oKT + szKT;
   static constexpr size_t oVT = oQ + szK;
-  static constexpr size_t oA = oVT + szVT;
-  static constexpr size_t oXW = oA + szF;               // X (fp32, solve) aliased with W (E)
-  static constexpr size_t oT = oXW + szXW;              // T hi [, T lo]
-  static constexpr size_t oTg = oT + kSplitN * szM;     // T' hi [, lo]
-  static constexpr size_t oP = oTg + kSplitN * szM;     // P hi [, lo]
-  static constexpr size_t oVec = oP + kSplitN * szM;    // gamma*log2e, e^gamma, e^(gC-gamma), beta
+  static constexpr size_t oT = oVT + szM;               // T hi [, T lo]
+  static constexpr size_t oP = oT + kSplitN * szM;      // P hi [, P lo]
+  static constexpr size_t oW = oP + kSplitN * szM;      // W [64][DK]
+  static constexpr size_t oVec = oW + szK;              // gamma*log2e, e^gamma, e^(gC-gamma), beta
   static constexpr size_t oRed = oVec + 4 * 64 * sizeof(float);
   static constexpr size_t bytes = oRed + 16 * sizeof(float);
-  // solve scratch lives in the T / T' area before T is written:
-  // X^T (fp32 [64][L64]) and R^T (3 x 16 x 16 fp32)
-  static constexpr size_t oXT = oT;
-  static constexpr size_t oRT = oT + szF;
-  static_assert(szF + 3 * 256 * sizeof(float) <= 2 * kSplitN * szM, "solve scratch does not fit");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -170,6 +168,8 @@ struct ChunkArgs {
   const int32_t* cu_seqlens;
   const int32_t* seq_lens;
   const int32_t* prefix_lens;
+  const int32_t* chunk_offs;  // prefix sums of ceil(P_n / 64) (prep kernel)
+  const void* T;              // 16 KiB record per (chunk, head) (prep kernel)
   const float* init;
   void* o;
   float* fin;
@@ -181,22 +181,6 @@ struct ChunkArgs {
   int dv;
   unsigned flags;
 };
-
-__device__ __forceinline__ float dot4(const float4 a, const float4 b, float acc) {
-  acc = fmaf(a.x, b.x, acc);
-  acc = fmaf(a.y, b.y, acc);
-  acc = fmaf(a.z, b.z, acc);
-  return fmaf(a.w, b.w, acc);
-}
-
-// 16-element dot product of two fp32 LDS rows (4 partial sums).
-__device__ __forceinline__ float dot16(const float* a, const float* b) {
-  const float4* a4 = reinterpret_cast<const float4*>(a);
-  const float4* b4 = reinterpret_cast<const float4*>(b);
-  const float4 a0 = a4[0], a1 = a4[1], a2 = a4[2], a3 = a4[3];
-  const float4 b0 = b4[0], b1 = b4[1], b2 = b4[2], b3 = b4[3];
-  return (dot4(a0, b0, 0.f) + dot4(a1, b1, 0.f)) + (dot4(a2, b2, 0.f) + dot4(a3, b3, 0.f));
-}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -214,17 +198,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
   E* sKT = reinterpret_cast<E*>(smem + S_::oKT);
   E* sQ = reinterpret_cast<E*>(smem + S_::oQ);
   E* sVT = reinterpret_cast<E*>(smem + S_::oVT);
-  float* sA = reinterpret_cast<float*>(smem + S_::oA);
-  float* sX = reinterpret_cast<float*>(smem + S_::oXW);
-  E* sW = reinterpret_cast<E*>(smem + S_::oXW);
   E* sTh = reinterpret_cast<E*>(smem + S_::oT);
   E* sTl = sTh + 64 * L64;
-  E* sTgh = reinterpret_cast<E*>(smem + S_::oTg);
-  E* sTgl = sTgh + 64 * L64;
   E* sPh = reinterpret_cast<E*>(smem + S_::oP);
   E* sPl = sPh + 64 * L64;
-  float* sXT = reinterpret_cast<float*>(smem + S_::oXT);
-  float* sRT = reinterpret_cast<float*>(smem + S_::oRT);
+  E* sW = reinterpret_cast<E*>(smem + S_::oW);
   float* sG2 = reinterpret_cast<float*>(smem + S_::oVec);  // gamma * log2(e)
   float* sEg = sG2 + 64;
   float* sEgc = sEg + 64;
@@ -290,6 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
 
   const int n_chunks = (P + kChunk - 1) / kChunk;
   const int bound0 = args.bound_offsets ? args.bound_offsets[n] : 0;
+  const int chunk0 = args.chunk_offs[n];
 
   // ---- staging geometry: 16-byte segments, two adjacent rows per thread
   constexpr int EPS = 16 / (int)sizeof(TIO);   // elements per segment
@@ -297,45 +276,61 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
   constexpr int NPK = 64 * SPR / kThreads / 2; // row pairs per thread (q/k)
   constexpr int VSPR = kTileRows / EPS;        // segments per v row
   constexpr int NPV = 64 * VSPR / kThreads / 2;
-  static_assert(NPK >= 1 && NPV >= 1, "staging geometry");
-  uint4 pk[NPK][2], pq[NPK][2], pv[NPV][2];
+  constexpr int NTS = 16384 / 16 / kThreads;   // 16-byte pieces of a T record per thread
+  static_assert(NPK >= 1 && NPV >= 1 && NTS == 4, "staging geometry");
+  // per-thread global offsets (elements) of chunk 0; chunk c adds c * 64 rows
+  int64_t kq_off[NPK][2], v_off[NPV][2];
+  int kq_row[NPK][2], v_row_i[NPV][2];
+#pragma unroll
+  for (int j = 0; j < NPK; ++j)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * (tid / SPR + (kThreads / SPR) * j) + e;
+      kq_row[j][e] = r;
+      kq_off[j][e] = (int64_t)(seg0 + r) * qk_row + (int64_t)h * DK + (tid % SPR) * EPS;
+    }
+#pragma unroll
+  for (int j = 0; j < NPV; ++j)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = 2 * (tid / VSPR + (kThreads / VSPR) * j) + e;
+      v_row_i[j][e] = r;
+      v_off[j][e] = (int64_t)(seg0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + (tid % VSPR) * EPS;
+    }
+  const uint4* Trec = reinterpret_cast<const uint4*>(args.T);
+  uint4 pk[NPK][2], pq[NPK][2], pv[NPV][2], pt[NTS];
   float pg = 0.f, pb = 0.f;
   auto fetch = [&](int c) {
-    const int t0 = seg0 + c * kChunk;
     const int nv = min(kChunk, P - c * kChunk);
+    const int64_t dqk = (int64_t)c * kChunk * qk_row, dvv = (int64_t)c * kChunk * v_row;
 #pragma unroll
-    for (int j = 0; j < NPK; ++j) {
-      const int rp = tid / SPR + (kThreads / SPR) * j, c0 = (tid % SPR) * EPS;
+    for (int j = 0; j < NPK; ++j)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int r = 2 * rp + e;
         pk[j][e] = make_uint4(0u, 0u, 0u, 0u);
         pq[j][e] = make_uint4(0u, 0u, 0u, 0u);
-        if (r < nv) {
-          const int64_t off = (int64_t)(t0 + r) * qk_row + (int64_t)h * DK + c0;
-          pk[j][e] = *reinterpret_cast<const uint4*>(gk_ + off);
-          pq[j][e] = *reinterpret_cast<const uint4*>(gq_ + off);
+        if (kq_row[j][e] < nv) {
+          pk[j][e] = *reinterpret_cast<const uint4*>(gk_ + kq_off[j][e] + dqk);
+          pq[j][e] = *reinterpret_cast<const uint4*>(gq_ + kq_off[j][e] + dqk);
         }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      const int rp = tid / VSPR + (kThreads / VSPR) * j, c0 = (tid % VSPR) * EPS;
+    for (int j = 0; j < NPV; ++j)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int r = 2 * rp + e;
         pv[j][e] = make_uint4(0u, 0u, 0u, 0u);
-        if (r < nv)
-          pv[j][e] = *reinterpret_cast<const uint4*>(gv_ + (int64_t)(t0 + r) * v_row +
-                                                       (int64_t)h * dv + kTileRows * vt + c0);
+        if (v_row_i[j][e] < nv) pv[j][e] = *reinterpret_cast<const uint4*>(gv_ + v_off[j][e] + dvv);
       }
-    }
+    const uint4* rec = Trec + ((int64_t)(chunk0 + c) * H + h) * (16384 / 16);
+#pragma unroll
+    for (int j = 0; j < NTS; ++j) pt[j] = rec[tid + kThreads * j];
     if (w == 0) {
       pg = 0.f;
       pb = 0.f;
       if (lane < nv) {
-        pg = args.g[(int64_t)(t0 + lane) * H + h];
-        pb = args.beta[(int64_t)(t0 + lane) * H + h];
+        const int64_t gi = (int64_t)(seg0 + c * kChunk + lane) * H + h;
+        pg = args.g[gi];
+        pb = args.beta[gi];
       }
     }
   };
@@ -345,28 +340,42 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
     const int t0 = seg0 + c * kChunk;
     const int nv = min(kChunk, P - c * kChunk);  // valid tokens in this chunk
 
-    // ---------------- a1: staged registers -> LDS; a2: gates ----------------
+    // ---------------- a1: staged registers -> LDS; gates ----------------
 #pragma unroll
     for (int j = 0; j < NPK; ++j) {
-      const int rp = tid / SPR + (kThreads / SPR) * j, c0 = (tid % SPR) * EPS;
-      *reinterpret_cast<uint4*>(sK + (2 * rp) * LDK + c0) = pk[j][0];
-      *reinterpret_cast<uint4*>(sK + (2 * rp + 1) * LDK + c0) = pk[j][1];
-      *reinterpret_cast<uint4*>(sQ + (2 * rp) * LDK + c0) = pq[j][0];
-      *reinterpret_cast<uint4*>(sQ + (2 * rp + 1) * LDK + c0) = pq[j][1];
+      const int r0 = kq_row[j][0], c0 = (tid % SPR) * EPS;
+      *reinterpret_cast<uint4*>(sK + r0 * LDK + c0) = pk[j][0];
+      *reinterpret_cast<uint4*>(sK + (r0 + 1) * LDK + c0) = pk[j][1];
+      *reinterpret_cast<uint4*>(sQ + r0 * LDK + c0) = pq[j][0];
+      *reinterpret_cast<uint4*>(sQ + (r0 + 1) * LDK + c0) = pq[j][1];
       E k0[EPS], k1[EPS];
       __builtin_memcpy(k0, &pk[j][0], 16);
       __builtin_memcpy(k1, &pk[j][1], 16);
 #pragma unroll
-      for (int e = 0; e < EPS; ++e) Eng::store_pair(sKT + (c0 + e) * L64 + 2 * rp, k0[e], k1[e]);
+      for (int e = 0; e < EPS; ++e) Eng::store_pair(sKT + (c0 + e) * L64 + r0, k0[e], k1[e]);
     }
 #pragma unroll
     for (int j = 0; j < NPV; ++j) {
-      const int rp = tid / VSPR + (kThreads / VSPR) * j, c0 = (tid % VSPR) * EPS;
+      const int r0 = v_row_i[j][0], c0 = (tid % VSPR) * EPS;
       E v0[EPS], v1[EPS];
       __builtin_memcpy(v0, &pv[j][0], 16);
       __builtin_memcpy(v1, &pv[j][1], 16);
 #pragma unroll
-      for (int e = 0; e < EPS; ++e) Eng::store_pair(sVT + (c0 + e) * L64 + 2 * rp, v0[e], v1[e]);
+      for (int e = 0; e < EPS; ++e) Eng::store_pair(sVT + (c0 + e) * L64 + r0, v0[e], v1[e]);
+    }
+    // T record: bf16 = hi plane then lo plane ([64][64] each); fp32 = one plane
+#pragma unroll
+    for (int j = 0; j < NTS; ++j) {
+      const int idx = tid + kThreads * j;            // 16-byte piece
+      if constexpr (Eng::kSplit) {
+        const int plane = idx >> 9, rr = (idx >> 3) & 63, cc = (idx & 7) * 8;
+        E* dst = (plane ? sTl : sTh) + rr * L64 + cc;
+        reinterpret_cast<uint2*>(dst)[0] = make_uint2(pt[j].x, pt[j].y);
+        reinterpret_cast<uint2*>(dst)[1] = make_uint2(pt[j].z, pt[j].w);
+      } else {
+        const int rr = idx >> 4, cc = (idx & 15) * 4;
+        *reinterpret_cast<uint4*>(sTh + rr * L64 + cc) = pt[j];
+      }
     }
     if (w == 0) {
       float x = pg;
@@ -385,166 +394,69 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
     if (c + 1 < n_chunks) fetch(c + 1);   // lands in registers while this chunk computes
     __syncthreads();
 
-    // ---------------- a3: A (strict lower) and P (lower incl. diagonal) ----------------
-    // Waves 0, 1 compute A, waves 2, 3 compute P; each takes the row blocks
-    // {0, 3} or {1, 2} (five lower 16x16 tiles either way).
-    {
-      const bool isP = (w >> 1) != 0;
-      const int ra = (w & 1) ? 1 : 0, rb = (w & 1) ? 2 : 3;
-      const E* bsrc = isP ? sQ : sK;
-      Fr bfa[NKB], bfb[NKB], af[4][NKB];
+    // ---------------- a3: P = decay * Q K^T (lower incl. diagonal) ----------------
+    // 10 lower tiles + 2 zero tiles read by the triangular products; 3 per wave
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        bfa[kb] = Eng::load(bsrc + (16 * ra + ln) * LDK, kb, gq);
-        bfb[kb] = Eng::load(bsrc + (16 * rb + ln) * LDK, kb, gq);
+    for (int jj = 0; jj < 3; ++jj) {
+      const int job = w + 4 * jj;
+      int ri, si;
+      if (job < 10) {
+        ri = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
+        si = job - (ri * (ri + 1)) / 2;
+      } else {
+        si = (job == 10) ? 1 : 3;
+        ri = si - 1;
       }
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (job < 10) {
+        // C[s][r] = sum_d K[s][d] Q[r][d]
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        Fr af[NKB], bf[NKB];
 #pragma unroll
-      for (int si = 0; si < 4; ++si)
-        if (si <= rb)
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) af[si][kb] = Eng::load(sK + (16 * si + ln) * LDK, kb, gq);
-      f32x4 acc[2][4];
-#pragma unroll
-      for (int si = 0; si < 4; ++si) {
-        acc[0][si] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[1][si] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int si = 0; si < 4; ++si) {
-          if (si <= ra) Eng::mma(acc[0][si], af[si][kb], bfa[kb]);
-          if (si <= rb) Eng::mma(acc[1][si], af[si][kb], bfb[kb]);
+        for (int kb = 0; kb < NKB; ++kb) {
+          af[kb] = Eng::load(sK + (16 * si + ln) * LDK, kb, gq);
+          bf[kb] = Eng::load(sQ + (16 * ri + ln) * LDK, kb, gq);
         }
-      // acc[x][si][i] = C[s][r], s = 16 si + 4 gq + i, r = 16 ri + ln
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int ri = x ? rb : ra;
+        for (int kb = 0; kb < NKB; ++kb) Eng::mma(acc, af[kb], bf[kb]);
         const int r = 16 * ri + ln;
         const float g2r = sG2[r];
-        const float br = sBeta[r];
+        const float4 g2s = *reinterpret_cast<const float4*>(sG2 + 16 * si + 4 * gq);
+        const float gs[4] = {g2s.x, g2s.y, g2s.z, g2s.w};
 #pragma unroll
-        for (int si = 0; si < 4; ++si) {
-          float v[4];
-          if (si <= ri) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int s = 16 * si + 4 * gq + i;
-              const bool keep = isP ? (s <= r) : (s < r);
-              v[i] = keep ? __builtin_amdgcn_exp2f(g2r - sG2[s]) * acc[x][si][i] : 0.f;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = 0.f;
-          }
-          if (isP) {
-            Eng::store4_split(sPh + r * L64 + 16 * si + 4 * gq, sPl + r * L64 + 16 * si + 4 * gq, v);
-          } else if (si <= ri) {
-            *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) =
-                make_float4(br * v[0], br * v[1], br * v[2], br * v[3]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * si + 4 * gq + i;
+          x[i] = (s <= r) ? __builtin_amdgcn_exp2f(g2r - gs[i]) * acc[i] : 0.f;
         }
       }
+      const int r = 16 * ri + ln;
+      Eng::store4_split(sPh + r * L64 + 16 * si + 4 * gq, sPl + r * L64 + 16 * si + 4 * gq, x);
     }
-    __syncthreads();
 
-    // ---------------- a4: X = (I + A)^-1, blocked, fp32 ----------------
-    if (w == 0) {
-      // diagonal block bi, column cc: x[r] = delta(r, cc) - sum_{s<r} A[r][s] x[s],
-      // evaluated column-oriented (after x[s] is final, update every later row)
-      const int bi = lane >> 4, cc = lane & 15;
-      const float* Ab = sA + 16 * bi * L64 + 16 * bi;
-      float a[16][16];
-#pragma unroll
-      for (int r = 1; r < 16; ++r)
-#pragma unroll
-        for (int q4 = 0; q4 * 4 < r; ++q4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(Ab + r * L64 + 4 * q4);
-          a[r][4 * q4] = v4.x; a[r][4 * q4 + 1] = v4.y; a[r][4 * q4 + 2] = v4.z; a[r][4 * q4 + 3] = v4.w;
-        }
-      float xc[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xc[r] = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-#pragma unroll
-        for (int r = s + 1; r < 16; ++r) xc[r] = fmaf(-a[r][s], xc[s], xc[r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sX[(16 * bi + r) * L64 + 16 * bi + cc] = xc[r];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<float4*>(sXT + (16 * bi + cc) * L64 + 16 * bi + 4 * q4) =
-            make_float4(xc[4 * q4], xc[4 * q4 + 1], xc[4 * q4 + 2], xc[4 * q4 + 3]);
-    }
-    __syncthreads();
-    {
-      const int r = tid >> 4, cc = tid & 15;
-#pragma unroll
-      for (int d = 1; d < 4; ++d) {
-        // R_ij = sum_{k=j}^{i-1} A_ik X_kj for blocks (i, j) = (d + b, b); stored transposed
-#pragma unroll
-        for (int b = 0; b + d < 4; ++b) {
-          const int i = d + b, j = b;
-          float acc = 0.f;
-#pragma unroll
-          for (int kk = j; kk < i; ++kk)
-            acc += dot16(sA + (16 * i + r) * L64 + 16 * kk, sXT + (16 * j + cc) * L64 + 16 * kk);
-          sRT[b * 256 + cc * 16 + r] = acc;
-        }
-        __syncthreads();
-        // X_ij = -X_ii R_ij
-#pragma unroll
-        for (int b = 0; b + d < 4; ++b) {
-          const int i = d + b, j = b;
-          const float xv = -dot16(sX + (16 * i + r) * L64 + 16 * i, sRT + b * 256 + cc * 16);
-          sX[(16 * i + r) * L64 + 16 * j + cc] = xv;
-          sXT[(16 * j + cc) * L64 + 16 * i + r] = xv;
-        }
-        __syncthreads();
-      }
-    }
-    // T = X diag(beta), T' = T diag(e^gamma); zero above the block diagonal.
-    {
-      const int r = tid >> 2, q16 = (tid & 3) * 16;
-      const bool below = (q16 >> 4) <= (r >> 4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s0 = q16 + 4 * u;
-        float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (below) x4 = *reinterpret_cast<const float4*>(sX + r * L64 + s0);
-        const float4 b4 = *reinterpret_cast<const float4*>(sBeta + s0);
-        const float4 e4 = *reinterpret_cast<const float4*>(sEg + s0);
-        const float tv[4] = {x4.x * b4.x, x4.y * b4.y, x4.z * b4.z, x4.w * b4.w};
-        const float tg[4] = {tv[0] * e4.x, tv[1] * e4.y, tv[2] * e4.z, tv[3] * e4.w};
-        Eng::store4_split(sTh + r * L64 + s0, sTl + r * L64 + s0, tv);
-        Eng::store4_split(sTgh + r * L64 + s0, sTgl + r * L64 + s0, tg);
-      }
-    }
-    __syncthreads();
-
-    // ---------------- a5: W^T = K^T T'^T (-> sW row-major), U = T V ----------------
+    // ---------------- a5: W^T = (e^gamma K)^T T^T (-> sW row-major), U = T V ----------------
     f32x4 uacc[4];
     {
       constexpr int DPW = NT / 4;  // dk tiles of W^T per wave
-      Fr ka[DPW][2], tgh[6], tgl[6], th[6], tl[6], vb[2];
       // (ti, kb) pairs of the lower-triangular T: (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
+      Fr th[6], tl[6];
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        tgh[p] = Eng::load(sTgh + (16 * ti + ln) * L64, kb, gq);
         th[p] = Eng::load(sTh + (16 * ti + ln) * L64, kb, gq);
-        if constexpr (Eng::kSplit) {
-          tgl[p] = Eng::load(sTgl + (16 * ti + ln) * L64, kb, gq);
-          tl[p] = Eng::load(sTl + (16 * ti + ln) * L64, kb, gq);
-        }
+        if constexpr (Eng::kSplit) tl[p] = Eng::load(sTl + (16 * ti + ln) * L64, kb, gq);
       }
+      Fr ka[DPW][2];
 #pragma unroll
-      for (int dd = 0; dd < DPW; ++dd)
+      for (int kb = 0; kb < 2; ++kb) {
+        const float4 e0 = *reinterpret_cast<const float4*>(sEg + 32 * kb + 4 * gq);
+        const float4 e1 = *reinterpret_cast<const float4*>(sEg + 32 * kb + 16 + 4 * gq);
+        const float ef[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ka[dd][kb] = Eng::load(sKT + (16 * (DPW * w + dd) + ln) * L64, kb, gq);
-      vb[0] = Eng::load(sVT + (16 * w + ln) * L64, 0, gq);
-      vb[1] = Eng::load(sVT + (16 * w + ln) * L64, 1, gq);
-
+        for (int dd = 0; dd < DPW; ++dd)
+          ka[dd][kb] = Eng::scale(Eng::load(sKT + (16 * (DPW * w + dd) + ln) * L64, kb, gq), ef);
+      }
+      const Fr vb0 = Eng::load(sVT + (16 * w + ln) * L64, 0, gq);
+      const Fr vb1 = Eng::load(sVT + (16 * w + ln) * L64, 1, gq);
       f32x4 wacc[DPW][4];
 #pragma unroll
       for (int dd = 0; dd < DPW; ++dd)
@@ -557,11 +469,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
 #pragma unroll
         for (int dd = 0; dd < DPW; ++dd) {
-          Eng::mma(wacc[dd][ti], ka[dd][kb], tgh[p]);
-          if constexpr (Eng::kSplit) Eng::mma(wacc[dd][ti], ka[dd][kb], tgl[p]);
+          Eng::mma(wacc[dd][ti], ka[dd][kb], th[p]);
+          if constexpr (Eng::kSplit) Eng::mma(wacc[dd][ti], ka[dd][kb], tl[p]);
         }
-        Eng::mma(uacc[ti], th[p], vb[kb]);
-        if constexpr (Eng::kSplit) Eng::mma(uacc[ti], tl[p], vb[kb]);
+        Eng::mma(uacc[ti], th[p], kb ? vb1 : vb0);
+        if constexpr (Eng::kSplit) Eng::mma(uacc[ti], tl[p], kb ? vb1 : vb0);
       }
       // wacc[dd][ti][i] = W^T[16di + 4gq + i][16ti + ln] = W[16ti + ln][16di + 4gq + i]
 #pragma unroll
@@ -571,86 +483,67 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
           Eng::store4(sW + (16 * ti + ln) * LDK + 16 * (DPW * w + dd) + 4 * gq, wacc[dd][ti][0],
                       wacc[dd][ti][1], wacc[dd][ti][2], wacc[dd][ti][3]);
     }
-    __syncthreads();  // sW complete
+    __syncthreads();  // sP, sW complete
 
-    // ---------------- a6 + a7 (inter-chunk part): W S^T and Q S^T ----------------
-    // After a QDQ (bf16 engine) feed the codes, exact in bf16, and scale by s.
+    // ---------------- a6 + a7 (inter part): U' = U - W S^T ; O^T = S Q^T ----------------
+    // After a QDQ (bf16 engine) the state fragment holds the codes, exact in
+    // bf16, and the products are scaled by s.
     const bool use_codes = Eng::kSplit && coded;
-    f32x4 wacc[4], oacc[4];
+    f32x4 wacc[4], oacc[4];   // wacc: [tok][vcol] tiles ; oacc: O^T [vcol 16w+4gq+i][tok 16ti+ln]
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       wacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
       oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    {
-      Fr aw[2][4], aq[2][4];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      Fr aw[4], bq[4];
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        aw[0][ti] = Eng::load(sW + (16 * ti + ln) * LDK, 0, gq);
-        aq[0][ti] = Eng::load(sQ + (16 * ti + ln) * LDK, 0, gq);
+        aw[ti] = Eng::load(sW + (16 * ti + ln) * LDK, kb, gq);
+        bq[ti] = Eng::load(sQ + (16 * ti + ln) * LDK, kb, gq);
+      }
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = st[2 * kb][i];
+        sv[4 + i] = st[2 * kb + 1][i];
+      }
+      Fr sh, sl;
+      if (use_codes) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] *= inv_s;
+        sh = Eng::round(sv);
+      } else {
+        Eng::split(sv, sh, sl);
       }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < NKB) {
+      for (int ti = 0; ti < 4; ++ti) {
+        Eng::mma(wacc[ti], aw[ti], sh);   // W S^T     : A = W rows, B = state
+        Eng::mma(oacc[ti], sh, bq[ti]);   // (S Q^T)   : A = state,  B = Q rows
+      }
+      if constexpr (Eng::kSplit) {
+        if (!use_codes) {
 #pragma unroll
           for (int ti = 0; ti < 4; ++ti) {
-            aw[cur ^ 1][ti] = Eng::load(sW + (16 * ti + ln) * LDK, kb + 1, gq);
-            aq[cur ^ 1][ti] = Eng::load(sQ + (16 * ti + ln) * LDK, kb + 1, gq);
-          }
-        }
-        float sv[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = st[2 * kb][i];
-          sv[4 + i] = st[2 * kb + 1][i];
-        }
-        Fr bh, bl;
-        if (use_codes) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) sv[j] *= inv_s;  // the codes, exact in bf16
-          bh = Eng::round(sv);
-        } else {
-          Eng::split(sv, bh, bl);
-        }
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          Eng::mma(wacc[ti], aw[cur][ti], bh);
-          Eng::mma(oacc[ti], aq[cur][ti], bh);
-        }
-        if constexpr (Eng::kSplit) {
-          if (!use_codes) {
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-              Eng::mma(wacc[ti], aw[cur][ti], bl);
-              Eng::mma(oacc[ti], aq[cur][ti], bl);
-            }
+            Eng::mma(wacc[ti], aw[ti], sl);
+            Eng::mma(oacc[ti], sl, bq[ti]);
           }
         }
       }
     }
-    // P fragments for the intra-chunk product (issued before the VALU work below)
-    Fr ph[6], pl[6];
-#pragma unroll
-    for (int p = 0; p < 6; ++p) {
-      const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-      ph[p] = Eng::load(sPh + (16 * ti + ln) * L64, kb, gq);
-      if constexpr (Eng::kSplit) pl[p] = Eng::load(sPl + (16 * ti + ln) * L64, kb, gq);
-    }
     const float sc = use_codes ? s_cur : 1.0f;
-    // U' = U - W S^T (fp32), rows 16ti + 4gq + i, column vcol
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-      const float4 eg = *reinterpret_cast<const float4*>(sEg + 16 * ti + 4 * gq);
-      const float egv[4] = {eg.x, eg.y, eg.z, eg.w};
+      const float egt = sc * sEg[16 * ti + ln];   // column tok = 16ti + ln of O^T
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uacc[ti][i] = fmaf(-sc, wacc[ti][i], uacc[ti][i]);
-        oacc[ti][i] = egv[i] * (sc * oacc[ti][i]);
+        oacc[ti][i] *= egt;
       }
     }
 
-    // ---------------- a7 (intra-chunk part): O += P U' ----------------
+    // ---------------- a7 (intra part): O^T += U'^T P^T ----------------
     {
       Fr uh[2], ul[2];
 #pragma unroll
@@ -666,22 +559,32 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        Eng::mma(oacc[ti], ph[p], uh[kb]);
+        const Fr ph = Eng::load(sPh + (16 * ti + ln) * L64, kb, gq);
+        Eng::mma(oacc[ti], uh[kb], ph);
         if constexpr (Eng::kSplit) {
-          Eng::mma(oacc[ti], ph[p], ul[kb]);
-          Eng::mma(oacc[ti], pl[p], uh[kb]);
+          const Fr pl = Eng::load(sPl + (16 * ti + ln) * L64, kb, gq);
+          Eng::mma(oacc[ti], ul[kb], ph);
+          Eng::mma(oacc[ti], uh[kb], pl);
+        }
+      }
+    }
+    // o rows: lane holds o[tok = 16ti + ln][16w + 4gq .. +3] of this tile
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      const int tok = 16 * ti + ln;
+      if (tok < nv) {
+        TO* dst = go_ + (int64_t)(t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + 16 * w + 4 * gq;
+        if constexpr (sizeof(TO) == 2) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(oacc[ti][0], oacc[ti][1]),
+                                                      pack_bf16x2(oacc[ti][2], oacc[ti][3]));
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(oacc[ti][0], oacc[ti][1], oacc[ti][2], oacc[ti][3]);
         }
       }
     }
 
     // ---------------- a8: S^T <- e^gC S^T + K^T diag(e^(gC - gamma)) U' ----------------
     {
-      Fr ka[NT][2];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        ka[t][0] = Eng::load(sKT + (16 * t + ln) * L64, 0, gq);
-        ka[t][1] = Eng::load(sKT + (16 * t + ln) * L64, 1, gq);
-      }
       Fr bh[2], bl[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -699,22 +602,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[t][i] *= aC;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          Eng::mma(st[t], ka[t][kb], bh[kb]);
-          if constexpr (Eng::kSplit) Eng::mma(st[t], ka[t][kb], bl[kb]);
+      for (int t = 0; t < NT; ++t) {
+        const Fr a0 = Eng::load(sKT + (16 * t + ln) * L64, 0, gq);
+        const Fr a1 = Eng::load(sKT + (16 * t + ln) * L64, 1, gq);
+        Eng::mma(st[t], a0, bh[0]);
+        Eng::mma(st[t], a1, bh[1]);
+        if constexpr (Eng::kSplit) {
+          Eng::mma(st[t], a0, bl[0]);
+          Eng::mma(st[t], a1, bl[1]);
         }
-    }
-
-    // store o rows (valid tokens only)
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * ti + 4 * gq + i;
-        if (r < nv) io<TO>::st(go_ + (int64_t)(t0 + r) * v_row + (int64_t)h * dv + vcol0, oacc[ti][i]);
       }
+    }
 
     // ---------------- a9: boundary QDQ ----------------
     const bool last = (c == n_chunks - 1);
@@ -756,10 +654,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
 
   // ---------------- a10: recurrent suffix, tokens P < t <= L ----------------
   if (P < L) {
-    float* sq = sA;          // q_t, k_t: DK each; v_t: 64
-    float* sk = sA + 256;
-    float* sv = sA + 512;
-    float* sg = sA + 640;    // g_t at sg[0], beta_t at sg[DK]
+    float* sq = reinterpret_cast<float*>(smem + S_::oW);  // q_t, k_t: DK each; v_t: 64
+    float* sk = sq + 256;
+    float* sv = sq + 512;
+    float* sg = sq + 640;    // g_t at sg[0], beta_t at sg[DK]
     for (int t = P; t < L; ++t) {
       const int64_t row = seg0 + t;
       if (tid < DK) {
@@ -841,11 +739,16 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             const float* beta, const float* g, const int32_t* cu_seqlens,
                             const int32_t* seq_lens, const int32_t* prefix_lens,
                             const float* initial_state, void* o, float* final_state,
-                            const gdn_debug_t* debug, hipStream_t stream) {
+                            void* workspace, const gdn_debug_t* debug, hipStream_t stream) {
   if (s.gate_per_channel) return hipErrorNotSupported;
   ChunkArgs a;
+  const int32_t* offs = nullptr;
+  void* T = nullptr;
+  hipError_t e = launch_prep(s, k, beta, g, cu_seqlens, seq_lens, prefix_lens, workspace, &offs, &T, stream);
+  if (e != hipSuccess) return e;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
   a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens; a.prefix_lens = prefix_lens;
+  a.chunk_offs = offs; a.T = T;
   a.init = initial_state; a.o = o; a.fin = final_state;
   a.bound_offsets = debug ? debug->bound_offsets : nullptr;
   a.bound_pre = debug ? debug->bound_pre : nullptr;

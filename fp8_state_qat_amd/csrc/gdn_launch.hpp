@@ -20,6 +20,16 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             const float* beta, const float* g, const int32_t* cu_seqlens,
                             const int32_t* seq_lens, const int32_t* prefix_lens,
                             const float* initial_state, void* o, float* final_state,
-                            const gdn_debug_t* debug, hipStream_t stream);
+                            void* workspace, const gdn_debug_t* debug, hipStream_t stream);
+
+// Bytes of the chunk workspace: chunk offsets [N + 1] (padded to 256 bytes)
+// and one 16 KiB T record per (chunk, head) for the worst-case chunk count
+// ceil(total_tokens / 64) + N.
+size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens);
+
+hipError_t launch_prep(const gdn_shape_t& s, const void* k, const float* beta, const float* g,
+                       const int32_t* cu_seqlens, const int32_t* seq_lens,
+                       const int32_t* prefix_lens, void* workspace, const int32_t** offs_out,
+                       void** T_out, hipStream_t stream);
 
 }  // namespace gdn

@@ -1,0 +1,307 @@
+// gdn_prep.hip -- the state-independent part of the chunked gated delta rule
+// (Model-Optimizer #2497: 64-token chunks with WY/UT-transformed W and U;
+// #2506: the exact triangular solve), for every (chunk, head) in parallel.
+//
+// Per chunk of n <= 64 tokens of sequence n, head h (rows past n are zero):
+//     gamma_r = sum_{s<=r} g_s                                (in-chunk scan)
+//     A[r][s] = beta_r exp(gamma_r - gamma_s) k_r . k_s       (s < r)
+//     T       = (I + A)^-1 diag(beta)                         (exact solve)
+// T is written to the workspace for the sequential kernel, which forms
+// W = T (exp(gamma) * K) and U = T V from it.
+//
+// The solve is blocked on 16 x 16 blocks in fp32: the four diagonal blocks
+// by forward substitution (one lane per column), then the off-diagonal
+// blocks level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
+//
+// Workspace layout: int32 chunk offsets [N + 1] (prefix sums of
+// ceil(P_n / 64)), padded to 256 bytes, then one 16 KiB record per (chunk,
+// head): bf16 inputs store T as hi = bf16(T) and lo = bf16(T - hi), two
+// [64][64] bf16 planes; fp32 inputs store T as [64][64] fp32.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// chunk offsets: offs[n] = sum_{m < n} ceil(P_m / 64), one workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void chunk_offsets_kernel(const int32_t* __restrict__ cu,
+                                                                 const int32_t* __restrict__ seq_lens,
+                                                                 const int32_t* __restrict__ prefix_lens,
+                                                                 int N, int32_t* __restrict__ offs) {
+  __shared__ int32_t part[kThreads];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += kThreads) {
+    const int n = base + threadIdx.x;
+    int32_t cnt = 0;
+    if (n < N) {
+      const int32_t L = seq_lens ? seq_lens[n] : (cu[n + 1] - cu[n]);
+      const int32_t P = prefix_lens ? prefix_lens[n] : L;
+      cnt = (P + kChunk - 1) / kChunk;
+    }
+    part[threadIdx.x] = cnt;
+    __syncthreads();
+    // inclusive Hillis-Steele scan over the tile
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int32_t v = (threadIdx.x >= off) ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (n < N) offs[n] = carry + part[threadIdx.x] - cnt;
+    __syncthreads();
+    if (threadIdx.x == kThreads - 1) carry += part[kThreads - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) offs[N] = carry;
+}
+
+struct PrepArgs {
+  const void* k;
+  const float* beta;
+  const float* g;
+  const int32_t* cu_seqlens;
+  const int32_t* seq_lens;
+  const int32_t* prefix_lens;
+  const int32_t* offs;
+  void* T;        // records of 16 KiB
+  int N;
+  int H;
+};
+
+__device__ __forceinline__ float dot4p(const float4 a, const float4 b) {
+  return fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, a.w * b.w)));
+}
+__device__ __forceinline__ float dot16p(const float* a, const float* b) {
+  const float4* a4 = reinterpret_cast<const float4*>(a);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  return (dot4p(a4[0], b4[0]) + dot4p(a4[1], b4[1])) + (dot4p(a4[2], b4[2]) + dot4p(a4[3], b4[3]));
+}
+
+// One workgroup (4 waves) per (chunk, head).  TIO: uint16_t (bf16) or float.
+template <int DK, typename TIO>
+__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
+  constexpr bool kBF = sizeof(TIO) == 2;
+  constexpr int L64 = 64 + 4;
+  constexpr int LDK = DK + 16 / (int)sizeof(TIO);  // K row stride (elements), 16-byte rows
+  constexpr int NKB = DK / 32;
+  __shared__ __align__(16) TIO sK[64 * LDK];
+  __shared__ __align__(16) float sA[64 * L64];
+  __shared__ __align__(16) float sX[64 * L64];
+  __shared__ __align__(16) float sXT[64 * L64];
+  __shared__ __align__(16) float sRT[3 * 256];
+  __shared__ float sG2[64], sBeta[64];
+
+  const int H = a.H;
+  const int j = blockIdx.x / H, h = blockIdx.x % H;
+  const int total = a.offs[a.N];
+  if (j >= total) return;  // grid is sized for the worst case
+  // sequence of chunk j: last n with offs[n] <= j
+  int lo = 0, hi = a.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.offs[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  const int n = lo, c = j - a.offs[n];
+  const int seg0 = a.cu_seqlens[n];
+  const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
+  const int P = a.prefix_lens ? a.prefix_lens[n] : L;
+  const int t0 = seg0 + c * kChunk;
+  const int nv = min(kChunk, P - c * kChunk);
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
+
+  // ---- stage K (rows past nv are zero), gates
+  {
+    constexpr int EPS = 16 / (int)sizeof(TIO);
+    constexpr int SPR = DK / EPS;
+    const TIO* gk = reinterpret_cast<const TIO*>(a.k);
+#pragma unroll
+    for (int jj = 0; jj < 64 * SPR / kThreads; ++jj) {
+      const int seg = tid + kThreads * jj;
+      const int r = seg / SPR, c0 = (seg % SPR) * EPS;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < nv) v = *reinterpret_cast<const uint4*>(gk + ((int64_t)(t0 + r) * H + h) * DK + c0);
+      *reinterpret_cast<uint4*>(sK + r * LDK + c0) = v;
+    }
+    if (w == 0) {
+      float gv = 0.f, bv = 0.f;
+      if (lane < nv) {
+        gv = a.g[(int64_t)(t0 + lane) * H + h];
+        bv = a.beta[(int64_t)(t0 + lane) * H + h];
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(gv, off, 64);
+        if (lane >= off) gv += y;
+      }
+      sG2[lane] = gv * 1.4426950408889634f;
+      sBeta[lane] = bv;
+    }
+  }
+  __syncthreads();
+
+  // ---- A = beta_r exp(gamma_r - gamma_s) K K^T, strictly lower; 10 tiles over 4 waves
+  for (int job = w; job < 10; job += 4) {
+    const int ri = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
+    const int si = job - (ri * (ri + 1)) / 2;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const TIO* arow = sK + (16 * si + ln) * LDK;
+    const TIO* brow = sK + (16 * ri + ln) * LDK;
+    if constexpr (kBF) {
+      bf16x8 af[NKB], bf[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint2 a0 = *reinterpret_cast<const uint2*>(arow + 32 * kb + 4 * gq);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(arow + 32 * kb + 16 + 4 * gq);
+        const uint2 b0 = *reinterpret_cast<const uint2*>(brow + 32 * kb + 4 * gq);
+        const uint2 b1 = *reinterpret_cast<const uint2*>(brow + 32 * kb + 16 + 4 * gq);
+        af[kb] = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        bf[kb] = __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y));
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) mma_bf16(acc, af[kb], bf[kb]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float av[8], bv[8];
+        const float4 a0 = *reinterpret_cast<const float4*>(arow + 32 * kb + 4 * gq);
+        const float4 a1 = *reinterpret_cast<const float4*>(arow + 32 * kb + 16 + 4 * gq);
+        const float4 b0 = *reinterpret_cast<const float4*>(brow + 32 * kb + 4 * gq);
+        const float4 b1 = *reinterpret_cast<const float4*>(brow + 32 * kb + 16 + 4 * gq);
+        av[0] = a0.x; av[1] = a0.y; av[2] = a0.z; av[3] = a0.w; av[4] = a1.x; av[5] = a1.y; av[6] = a1.z; av[7] = a1.w;
+        bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w; bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
+        mma_f32(acc, av, bv);
+      }
+    }
+    // acc[i] = k_s . k_r with s = 16 si + 4 gq + i, r = 16 ri + ln
+    const int r = 16 * ri + ln;
+    const float g2r = sG2[r], br = sBeta[r];
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 16 * si + 4 * gq + i;
+      v[i] = (s < r) ? br * __builtin_amdgcn_exp2f(g2r - sG2[s]) * acc[i] : 0.f;
+    }
+    *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __syncthreads();
+
+  // ---- diagonal blocks of X = (I + A)^-1: lane = (block, column), column-oriented
+  if (w == 0) {
+    const int bi = lane >> 4, cc = lane & 15;
+    const float* Ab = sA + 16 * bi * L64 + 16 * bi;
+    float am[16][16];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+      for (int q4 = 0; q4 * 4 < r; ++q4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(Ab + r * L64 + 4 * q4);
+        am[r][4 * q4] = v4.x; am[r][4 * q4 + 1] = v4.y; am[r][4 * q4 + 2] = v4.z; am[r][4 * q4 + 3] = v4.w;
+      }
+    float xc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xc[r] = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int r = s + 1; r < 16; ++r) xc[r] = fmaf(-am[r][s], xc[s], xc[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sX[(16 * bi + r) * L64 + 16 * bi + cc] = xc[r];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<float4*>(sXT + (16 * bi + cc) * L64 + 16 * bi + 4 * q4) =
+          make_float4(xc[4 * q4], xc[4 * q4 + 1], xc[4 * q4 + 2], xc[4 * q4 + 3]);
+  }
+  __syncthreads();
+  // ---- off-diagonal blocks, level by level
+  {
+    const int r = tid >> 4, cc = tid & 15;
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+#pragma unroll
+      for (int b = 0; b + d < 4; ++b) {
+        const int i = d + b, jb = b;
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = jb; kk < i; ++kk)
+          acc += dot16p(sA + (16 * i + r) * L64 + 16 * kk, sXT + (16 * jb + cc) * L64 + 16 * kk);
+        sRT[b * 256 + cc * 16 + r] = acc;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b + d < 4; ++b) {
+        const int i = d + b, jb = b;
+        const float xv = -dot16p(sX + (16 * i + r) * L64 + 16 * i, sRT + b * 256 + cc * 16);
+        sX[(16 * i + r) * L64 + 16 * jb + cc] = xv;
+        sXT[(16 * jb + cc) * L64 + 16 * i + r] = xv;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- T = X diag(beta), zero above the block diagonal -> workspace record
+  {
+    const int r = tid >> 2, q16 = (tid & 3) * 16;
+    const bool below = (q16 >> 4) <= (r >> 4);
+    const int64_t rec = ((int64_t)j * H + h) * 4096;  // elements of 4 bytes
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s0 = q16 + 4 * u;
+      float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (below) x4 = *reinterpret_cast<const float4*>(sX + r * L64 + s0);
+      const float4 b4 = *reinterpret_cast<const float4*>(sBeta + s0);
+      const float t0v = x4.x * b4.x, t1v = x4.y * b4.y, t2v = x4.z * b4.z, t3v = x4.w * b4.w;
+      if constexpr (kBF) {
+        uint32_t h0, l0, h1, l1;
+        split_bf16x2(t0v, t1v, h0, l0);
+        split_bf16x2(t2v, t3v, h1, l1);
+        uint16_t* Th = reinterpret_cast<uint16_t*>(a.T) + rec * 2;  // 2 planes of 4096 bf16
+        *reinterpret_cast<uint2*>(Th + r * 64 + s0) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(Th + 4096 + r * 64 + s0) = make_uint2(l0, l1);
+      } else {
+        float* Tf = reinterpret_cast<float*>(a.T) + rec;
+        *reinterpret_cast<float4*>(Tf + r * 64 + s0) = make_float4(t0v, t1v, t2v, t3v);
+      }
+    }
+  }
+}
+
+size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens) {
+  const int64_t max_chunks = (total_tokens + kChunk - 1) / kChunk + n_seqs;
+  const size_t offs = ((size_t)(n_seqs + 1) * 4 + 255) / 256 * 256;
+  return offs + (size_t)max_chunks * n_heads * 16384;
+}
+
+hipError_t launch_prep(const gdn_shape_t& s, const void* k, const float* beta, const float* g,
+                       const int32_t* cu_seqlens, const int32_t* seq_lens,
+                       const int32_t* prefix_lens, void* workspace, const int32_t** offs_out,
+                       void** T_out, hipStream_t stream) {
+  int32_t* offs = reinterpret_cast<int32_t*>(workspace);
+  const size_t offs_bytes = ((size_t)(s.n_seqs + 1) * 4 + 255) / 256 * 256;
+  void* T = reinterpret_cast<char*>(workspace) + offs_bytes;
+  *offs_out = offs;
+  *T_out = T;
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(kThreads), 0, stream, cu_seqlens, seq_lens,
+                     prefix_lens, s.n_seqs, offs);
+  const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
+  const int64_t blocks = max_chunks * s.n_heads;
+  if (blocks == 0) return hipGetLastError();
+  PrepArgs a;
+  a.k = k; a.beta = beta; a.g = g; a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens;
+  a.prefix_lens = prefix_lens; a.offs = offs; a.T = T; a.N = s.n_seqs; a.H = s.n_heads;
+  if (s.io_dtype == GDN_BF16) {
+    if (s.dk == 128)
+      hipLaunchKernelGGL((chunk_prep_kernel<128, uint16_t>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<64, uint16_t>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  } else {
+    if (s.dk != 64) return hipErrorNotSupported;  // fp32 inputs: dk = 64 only
+    hipLaunchKernelGGL((chunk_prep_kernel<64, float>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -39,6 +39,7 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -100,6 +101,10 @@ typedef struct {
  *   initial_state [N, H, dv, dk] fp32 or NULL (zero).  Used as given (not quantized).
  *   o      [total_tokens, H, dv]  o_dtype (output)
  *   final_state [N, H, dv, dk] fp32 (output), may alias initial_state.
+ *   workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes(shape)
+ *               bytes, 256-byte aligned, owned by the caller; its contents on entry
+ *               are ignored and on return are unspecified.  Two calls that share a
+ *               workspace must not overlap in time.
  *   debug  NULL or a per-boundary record (see gdn_debug_t).
  *
  * QDQ placement for token t of a sequence (1-based): after token t when
@@ -114,7 +119,17 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape,
                            const int32_t* prefix_lens,
                            const float* initial_state,
                            void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes,
                            const gdn_debug_t* debug, void* stream);
+
+/*
+ * gdn_chunk_fwd_workspace_bytes -- bytes of device workspace gdn_chunk_fwd
+ * needs for this shape: the per-chunk solve T = (I + A)^-1 diag(beta) of
+ * every (chunk, head) (16 KiB each, for the worst-case chunk count
+ * ceil(total_tokens / 64) + n_seqs) plus the chunk offsets.  Returns 0 for an
+ * invalid shape (gdn_last_error() says why).
+ */
+size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape);
 
 /*
  * gdn_state_qdq -- standalone per-tile state QDQ (#2497: one scalar scale per

@@ -49,11 +49,17 @@ def _shape(**kw):
     return GdnShape(**d)
 
 
-def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None):
+def _ws(shape):
+    return _lib.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape))
+
+
+def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None, ws=FAKE, ws_bytes=None):
     p = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = _ws(shape) if shape is not None else 0
     return _lib.lib().gdn_chunk_fwd(ctypes.byref(shape) if shape is not None else None,
                                     p(q), p(FAKE), p(FAKE), p(beta), p(FAKE), p(cu), None, None,
-                                    None, p(FAKE), p(fin), dbg, None)
+                                    None, p(FAKE), p(fin), p(ws), ws_bytes, dbg, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -76,6 +82,18 @@ def test_chunk_fwd_rejects_null_and_misaligned():
     assert _chunk(_shape(), beta=FAKE + 2) == 1
     dbg = GdnDebug(None, ctypes.c_void_p(FAKE), None, None)   # record without offsets
     assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
+
+
+def test_workspace_size_and_checks():
+    """Workspace: worst-case chunk count ceil(T/64) + N records of 16 KiB per
+    head plus the chunk offsets; too small, NULL or misaligned is rejected."""
+    s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
+    n = _ws(s)
+    assert n == 256 + (3 + 3) * 2 * 16384
+    assert _ws(_shape(dv=96)) == 0 and _lib.last_error()
+    assert _chunk(s, ws_bytes=n - 1) == 1
+    assert _chunk(s, ws=0) == 1
+    assert _chunk(s, ws=FAKE + 64) == 1
 
 
 def test_state_qdq_rejects_bad_args():
