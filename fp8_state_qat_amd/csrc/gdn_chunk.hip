@@ -300,6 +300,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
   const uint4* Trec = reinterpret_cast<const uint4*>(args.T);
   uint4 pk[NPK][2], pq[NPK][2], pv[NPV][2], pt[NTS];
   float pg = 0.f, pb = 0.f;
+  // Loads are unconditional (rows past the chunk's valid count are clamped to
+  // its last valid row) so they stay in flight; the zero mask is applied when
+  // the data is written to LDS.
   auto fetch = [&](int c) {
     const int nv = min(kChunk, P - c * kChunk);
     const int64_t dqk = (int64_t)c * kChunk * qk_row, dvv = (int64_t)c * kChunk * v_row;
@@ -307,31 +310,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
     for (int j = 0; j < NPK; ++j)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        pk[j][e] = make_uint4(0u, 0u, 0u, 0u);
-        pq[j][e] = make_uint4(0u, 0u, 0u, 0u);
-        if (kq_row[j][e] < nv) {
-          pk[j][e] = *reinterpret_cast<const uint4*>(gk_ + kq_off[j][e] + dqk);
-          pq[j][e] = *reinterpret_cast<const uint4*>(gq_ + kq_off[j][e] + dqk);
-        }
+        const int64_t clamp = (int64_t)(min(kq_row[j][e], nv - 1) - kq_row[j][e]) * qk_row;
+        pk[j][e] = *reinterpret_cast<const uint4*>(gk_ + kq_off[j][e] + dqk + clamp);
+        pq[j][e] = *reinterpret_cast<const uint4*>(gq_ + kq_off[j][e] + dqk + clamp);
       }
 #pragma unroll
     for (int j = 0; j < NPV; ++j)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        pv[j][e] = make_uint4(0u, 0u, 0u, 0u);
-        if (v_row_i[j][e] < nv) pv[j][e] = *reinterpret_cast<const uint4*>(gv_ + v_off[j][e] + dvv);
+        const int64_t clamp = (int64_t)(min(v_row_i[j][e], nv - 1) - v_row_i[j][e]) * v_row;
+        pv[j][e] = *reinterpret_cast<const uint4*>(gv_ + v_off[j][e] + dvv + clamp);
       }
     const uint4* rec = Trec + ((int64_t)(chunk0 + c) * H + h) * (16384 / 16);
 #pragma unroll
     for (int j = 0; j < NTS; ++j) pt[j] = rec[tid + kThreads * j];
     if (w == 0) {
-      pg = 0.f;
-      pb = 0.f;
-      if (lane < nv) {
-        const int64_t gi = (int64_t)(seg0 + c * kChunk + lane) * H + h;
-        pg = args.g[gi];
-        pb = args.beta[gi];
-      }
+      const int64_t gi = (int64_t)(seg0 + c * kChunk + min(lane, nv - 1)) * H + h;
+      pg = args.g[gi];
+      pb = args.beta[gi];
     }
   };
   if (n_chunks > 0) fetch(0);
@@ -341,6 +337,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
     const int nv = min(kChunk, P - c * kChunk);  // valid tokens in this chunk
 
     // ---------------- a1: staged registers -> LDS; gates ----------------
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < NPK; ++j)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (kq_row[j][e] >= nv) { pk[j][e] = zero4; pq[j][e] = zero4; }
+#pragma unroll
+    for (int j = 0; j < NPV; ++j)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (v_row_i[j][e] >= nv) pv[j][e] = zero4;
+    if (lane >= nv) { pg = 0.f; pb = 0.f; }
 #pragma unroll
     for (int j = 0; j < NPK; ++j) {
       const int r0 = kq_row[j][0], c0 = (tid % SPR) * EPS;
