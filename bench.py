@@ -3,14 +3,17 @@
 
 One step = one gdn_chunk_fwd call over the GDN prefill workload (B=4,
 T=4096, H=16, dk=dv=128, bf16 q/k/v and o, fp32 state, FP8-E4M3 state QDQ
-at every 64-token boundary and at the end): staging, gates, K K^T, the exact
-solve, W and U, U', O, the state update and the boundary QDQ, all in one
-kernel launch.  Inputs are resident in HBM before the timed region.
+at every 64-token boundary and at the end): a parallel prep kernel (gates,
+K K^T, the exact solve per chunk) and the sequential state kernel (W and U,
+U', O, the state update and the boundary QDQ).  Inputs are resident in HBM
+before the timed region.  The roofline object covers the sequential state
+kernel, timed with HIP events recorded around it by the library.
 
 Also reported: the prefill->decode handoff workload (256 sequences, H=32,
 d=128: 2048-token chunked prefix with QDQ, then 512 single-token decode steps
 each writing the state through per-tile QDQ) as decode-step HBM GB/s, and the
-CPU oracle's throughput on a bounded sample of the prefill workload.
+CPU oracle's throughput on the prefill workload (all 64 (sequence, head) pairs
+by default).
 
 Prints one JSON line.
 """
@@ -40,11 +43,23 @@ def flops_per_token_head(C, dk, dv):
     return 2 * C * (3 * dk + 2 * dv) + 6 * dk * dv + C * C / 3
 
 
+def state_kernel_flops_per_token_head(C, dk, dv):
+    """The part of flops_per_token_head done by the sequential state kernel:
+    everything but K K^T and the solve, which the parallel prep kernel does."""
+    return flops_per_token_head(C, dk, dv) - 2 * C * dk - C * C / 3
+
+
 def prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes, gate_floats=1):
-    """Algorithmic HBM bytes of one prefill launch: q, k, v read once, beta
+    """Algorithmic HBM bytes of one prefill call: q, k, v read once, beta
     and g read once, o written once, the final state written once."""
     per = io_bytes * (2 * dk + dv) + 4 * (1 + gate_floats) + o_bytes * dv
     return T_heads * per + n_states * dv * dk * 4
+
+
+def state_kernel_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes, o_bytes):
+    """Algorithmic HBM bytes of the sequential state kernel: the prefill bytes
+    plus one read of the per-chunk solve (16 KiB per chunk and head)."""
+    return prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes) + n_chunk_heads * 16384
 
 
 def decode_bytes(n_heads_seqs, dk, dv, io_bytes, o_bytes):
@@ -79,20 +94,24 @@ def time_launches(fn, steps, warmup):
     return evs[0].elapsed_time(evs[-1]), per
 
 
-def cpu_baseline(w, flags, n_pairs, threads):
+def cpu_baseline(w, flags, n_pairs, threads, repeats):
+    """The oracle (plain fp64 recurrence with QDQ) over `n_pairs` (sequence,
+    head) pairs of the prefill workload, run `repeats` times."""
     from oracle import oracle as orc
     pairs = [(n, h) for n in range(w.n_seqs) for h in range(w.n_heads)][:n_pairs]
     q, k, v, b, g = (w.f64(x) for x in ("q", "k", "v", "beta", "g"))
     t0 = time.perf_counter()
-    orc.gdn_packed(q, k, v, b, g, w.cu_seqlens, seq_lens=w.seq_lens, prefix_lens=w.prefix_lens,
-                   flags=flags, pairs=pairs, threads=threads)
+    for _ in range(repeats):
+        orc.gdn_packed(q, k, v, b, g, w.cu_seqlens, seq_lens=w.seq_lens,
+                       prefix_lens=w.prefix_lens, flags=flags, pairs=pairs, threads=threads)
     dt = time.perf_counter() - t0
-    token_heads = sum(int(w.seq_lens[n]) for n, _ in pairs)
+    token_heads = repeats * sum(int(w.seq_lens[n]) for n, _ in pairs)
     return {"value": token_heads / w.n_heads / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(pairs)} (sequence, head) pairs x {int(w.seq_lens[0])} tokens of the "
-                      f"prefill workload, QDQ on, fp64 recurrence; token-heads/s divided by "
-                      f"H={w.n_heads}; {dt:.1f} s wall on {threads} threads"}
+            "sample": f"{len(pairs)} of {w.n_seqs * w.n_heads} (sequence, head) pairs x "
+                      f"{int(w.seq_lens[0])} tokens of the prefill workload, run {repeats} times, "
+                      f"QDQ on, fp64 recurrence; token-heads/s divided by H={w.n_heads}; "
+                      f"{dt:.1f} s wall on {threads} threads"}
 
 
 def load_traffic(kernel_key, src_hash):
@@ -115,7 +134,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-pairs", type=int, default=32)
+    ap.add_argument("--cpu-pairs", type=int, default=64,
+                    help="(sequence, head) pairs the oracle runs (64 = the whole workload)")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
@@ -140,28 +161,48 @@ def main():
     o = torch.empty((w.total_tokens, H, dv), dtype=torch.bfloat16, device=dev)
     fin = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
 
-    def step():
-        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=flags,
-                      out=o, final_state=fin)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps + args.warmup)]
+    it = {"i": 0}
 
+    def step():
+        e0, e1 = ev[it["i"]]
+        it["i"] += 1
+        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=flags,
+                      out=o, final_state=fin, debug={"kernel_start": e0, "kernel_end": e1})
+
+    for e0, e1 in ev:  # create the HIP events outside the timed region
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
     total_ms, per = time_launches(step, args.steps, args.warmup)
     ms_step = total_ms / args.steps
-    kern_ms = float(np.mean(per))
+    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev[args.warmup:]]))
     tokens = B * T
     token_heads = tokens * H
-    fl = flops_per_token_head(64, dk, dv) * token_heads
-    by = prefill_bytes(token_heads, B * H, dk, dv, 2, 2)
+    n_chunk_heads = B * H * ((T + 63) // 64)
+    fl_all = flops_per_token_head(64, dk, dv) * token_heads
+    fl = state_kernel_flops_per_token_head(64, dk, dv) * token_heads
+    by = state_kernel_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2, 2)
     src = source_hash([os.path.join(ROOT, "fp8_state_qat_amd", "csrc", f)
                        for f in ("gdn_chunk.hip", "gdn_device.hpp")])
     traffic = load_traffic("chunk_fwd_gdn_prefill", src)
-    hbm_gbs = by / (kern_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "chunk_fwd_kernel<128, bf16>",
-                "algorithmic_bytes_per_launch": by, "avg_launch_ms": round(kern_ms, 5)}
     tflops = fl / (kern_ms * 1e-3) / 1e12
-    mfma = {"achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": fl,
+    hbm_gbs = by / (kern_ms * 1e-3) / 1e9
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "chunk_fwd_kernel<128, EngBF16, bf16, bf16>",
+                "algorithmic_flops_per_launch": fl,
+                "flops_per_token_head": state_kernel_flops_per_token_head(64, dk, dv),
+                "avg_launch_ms": round(kern_ms, 5),
+                "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_launch": by}}
+    step_tflops = fl_all / (ms_step * 1e-3) / 1e12
+    mfma = {"scope": "whole step (prep + state kernels)", "achieved": round(step_tflops, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(step_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_step": fl_all,
             "flops_per_token_head": flops_per_token_head(64, dk, dv)}
 
     # QDQ off, same workload (reported)
@@ -213,6 +254,8 @@ def main():
         dtot, dper = time_launches(dstep, steps4 - dwarm, dwarm)
         dms = float(np.mean(dper))
         dby = decode_bytes(N4 * H4, 128, 128, 2, 2)
+        dsrc = source_hash([os.path.join(ROOT, "fp8_state_qat_amd", "csrc", f)
+                            for f in ("gdn_decode.hip", "gdn_device.hpp")])
         out["decode"] = {"workload": "256 sequences, H=32, dk=dv=128, bf16 q/k/v/o, fp32 state; "
                                      "2048-token chunked prefix with QDQ, then 512 decode steps "
                                      "with per-write QDQ",
@@ -224,7 +267,9 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": round(dby / (dms * 1e-3) / 1e9, 1),
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": round(dby / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                      "algorithmic_bytes_per_launch": dby}}
+                                      "algorithmic_bytes_per_launch": dby,
+                                      "traffic": load_traffic("decode_step_handoff", dsrc),
+                                      "kernel": "decode_step_kernel<128, bf16, bf16>"}}
         del tok, state
         torch.cuda.empty_cache()
 
@@ -239,7 +284,7 @@ def main():
 
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
-        out["cpu_baseline"] = cpu_baseline(w, flags, args.cpu_pairs, threads)
+        out["cpu_baseline"] = cpu_baseline(w, flags, args.cpu_pairs, threads, args.cpu_repeats)
 
     print(json.dumps(out), flush=True)
 

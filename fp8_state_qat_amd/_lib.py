@@ -45,6 +45,8 @@ class GdnDebug(ctypes.Structure):
         ("bound_pre", ctypes.c_void_p),
         ("bound_post", ctypes.c_void_p),
         ("scales", ctypes.c_void_p),
+        ("kernel_start", ctypes.c_void_p),
+        ("kernel_end", ctypes.c_void_p),
     ]
 
 

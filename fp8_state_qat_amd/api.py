@@ -56,8 +56,9 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     [T, H] fp32; g: [T, H] or [T, H, dk] fp32; cu_seqlens: [N+1] int32.
     workspace: optional uint8 device tensor of chunk_workspace_bytes(...)
     bytes (allocated here when None).  debug: optional dict with device
-    tensors bound_offsets, bound_pre, bound_post, scales.  Returns (o,
-    final_state)."""
+    tensors bound_offsets, bound_pre, bound_post, scales and/or
+    torch.cuda.Event objects kernel_start, kernel_end (recorded around the
+    sequential state kernel).  Returns (o, final_state)."""
     T, H, dk = k.shape
     dv = v.shape[2]
     N = cu_seqlens.numel() - 1
@@ -84,8 +85,14 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     _dev(workspace, "workspace", torch.uint8)
     dbg = None
     if debug is not None:
+        evs = []
+        for key in ("kernel_start", "kernel_end"):
+            ev = debug.get(key)
+            if ev is not None and not ev.cuda_event:
+                ev.record()  # torch creates its HIP event on first record
+            evs.append(None if ev is None else ctypes.c_void_p(ev.cuda_event))
         dbg = GdnDebug(*(_ptr(debug.get(key)) for key in ("bound_offsets", "bound_pre",
-                                                          "bound_post", "scales")))
+                                                          "bound_post", "scales")), *evs)
     st = _lib.lib().gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                   _ptr(g), _ptr(cu_seqlens), _ptr(seq_lens), _ptr(prefix_lens),
                                   _ptr(initial_state), _ptr(out), _ptr(final_state),

@@ -764,17 +764,26 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   a.bound_scales = debug ? debug->scales : nullptr;
   a.H = s.n_heads; a.dv = s.dv; a.flags = s.qdq_flags;
   const bool ob = s.o_dtype == GDN_BF16;
+  if (debug && debug->kernel_start) {
+    e = hipEventRecord((hipEvent_t)debug->kernel_start, stream);
+    if (e != hipSuccess) return e;
+  }
   if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)
-      return ob ? launch_typed<128, EngBF16, uint16_t, uint16_t>(s, a, stream)
-                : launch_typed<128, EngBF16, uint16_t, float>(s, a, stream);
-    return ob ? launch_typed<64, EngBF16, uint16_t, uint16_t>(s, a, stream)
-              : launch_typed<64, EngBF16, uint16_t, float>(s, a, stream);
+      e = ob ? launch_typed<128, EngBF16, uint16_t, uint16_t>(s, a, stream)
+             : launch_typed<128, EngBF16, uint16_t, float>(s, a, stream);
+    else
+      e = ob ? launch_typed<64, EngBF16, uint16_t, uint16_t>(s, a, stream)
+             : launch_typed<64, EngBF16, uint16_t, float>(s, a, stream);
+  } else if (s.dk == 64) {
+    e = ob ? launch_typed<64, EngF32, float, uint16_t>(s, a, stream)
+           : launch_typed<64, EngF32, float, float>(s, a, stream);
+  } else {
+    return hipErrorNotSupported;
   }
-  if (s.dk == 64)
-    return ob ? launch_typed<64, EngF32, float, uint16_t>(s, a, stream)
-              : launch_typed<64, EngF32, float, float>(s, a, stream);
-  return hipErrorNotSupported;
+  if (e == hipSuccess && debug && debug->kernel_end)
+    e = hipEventRecord((hipEvent_t)debug->kernel_end, stream);
+  return e;
 }
 
 }  // namespace gdn

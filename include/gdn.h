@@ -74,14 +74,18 @@ typedef struct {
     uint32_t qdq_flags;        /* GDN_QDQ_* bits */
 } gdn_shape_t;
 
-/* Optional per-boundary record of the chunked prefix, for parity checks.
- * Boundary b of sequence n is b = bound_offsets[n] + i for its i-th chunk
- * end (i = 0 .. ceil(P_n / 64) - 1).  All pointers nullable. */
+/* Optional per-boundary record of the chunked prefix, for parity checks, and
+ * a timing hook.  Boundary b of sequence n is b = bound_offsets[n] + i for its
+ * i-th chunk end (i = 0 .. ceil(P_n / 64) - 1).  All pointers nullable; the
+ * record needs bound_offsets when any of its three arrays is set. */
 typedef struct {
     const int32_t* bound_offsets;  /* [N + 1] device; prefix sums of ceil(P_n / 64) */
     float* bound_pre;              /* [n_bounds, H, dv, dk] state after the chunk, before QDQ */
     float* bound_post;             /* [n_bounds, H, dv, dk] state after QDQ (= pre when none) */
     float* scales;                 /* [n_bounds, H, dv / 64] QDQ scales (1 when none) */
+    void* kernel_start;            /* hipEvent_t or NULL: recorded on the stream just before */
+    void* kernel_end;              /* and just after the sequential state kernel (timing hook; */
+                                   /* the parallel per-chunk solve runs before kernel_start) */
 } gdn_debug_t;
 
 /*
