@@ -1,62 +1,84 @@
 // gdn_chunk.hip -- sequential part of the chunked gated delta rule forward
 // with per-boundary FP8-E4M3 state QDQ (Model-Optimizer #2497 "What does this
-// PR do?": 64-token chunks, WY-transformed W, dynamic per-tile state QDQ at
-// every boundary; #2519: QDQ at the handoff and after every later recurrent
-// write).
+// PR do?": 64-token chunks, WY/UT-transformed operands, dynamic per-tile state
+// QDQ at every boundary; #2519: QDQ at the handoff and after every later
+// recurrent write).
 //
-// Work unit: one workgroup (4 waves) per (sequence n, head h, 64-column value
+// Work unit: one workgroup of 8 waves per (sequence n, head h, 64-column value
 // tile vt).  It walks its sequence chunk by chunk and keeps its slice of the
-// state in registers for the whole sequence: wave w owns value columns
-// 16w..16w+15 of the tile, i.e. dk/16 16x16 accumulator tiles of S^T.  The
-// 64 x dk state tile is exactly one QDQ tile, so the QDQ amax needs no
-// exchange with other workgroups.  T = (I + A)^-1 diag(beta) of every chunk
-// comes from the prep kernel (gdn_prep.hip) through the workspace.
+// state in registers for the whole sequence.  The 64 x dk state tile is
+// exactly one QDQ tile, so the QDQ amax needs no exchange with other
+// workgroups.  T = (I + A)^-1 diag(beta) of every chunk comes from the prep
+// kernel (gdn_prep.hip) through the workspace.
 //
-// Per chunk of n <= 64 tokens (rows past n are zero, beta = g = 0, so they
-// drop out of every product), gamma = in-chunk cumulative log-gate:
-//   a1  stage q, k (row-major and transposed), v (transposed) and T -> LDS;
-//       gamma (wave scan), exp(gamma), exp(gamma_C - gamma).  The next
-//       chunk's inputs are already in flight to registers.
-//   a3  P[r][s] = exp(gamma_r - gamma_s) q_r . k_s  (s <= r)          MFMA
-//   a5  W = T (exp(gamma) * K)  (as W^T = (exp(gamma) * K)^T T^T),
-//       U = T V                                                        MFMA
-//   a6  U' = U - W S^T                                                 MFMA
-//   a7  O^T = diag-scaled S Q^T + U'^T P^T   (o lands 4 values per lane)
-//   a8  S^T <- exp(gamma_C) S^T + K^T diag(exp(gamma_C - gamma)) U'    MFMA
-//   a9  QDQ: amax over the 64 x dk tile (wave + LDS tree), s = amax/448,
-//       S <- RNE_E4M3(S/s) s
-// then the recurrent suffix (tokens P_n < t <= L_n, QDQ after every write)
-// and the final state store.
+// Waves 0..3 ("chain" waves) carry the state: chain wave c owns value columns
+// 16c..16c+15 of the tile, i.e. dk/16 16x16 accumulator tiles of S^T, and
+// runs everything that depends on the state.  Waves 4..7 ("helper" waves)
+// stage the next chunk into LDS, form P and produce the outputs, so each SIMD
+// runs one wave of each kind and the two overlap.  With gamma the in-chunk
+// cumulative log-gate and s the scale of the state entering the chunk (1
+// when it is not coded), one chunk of n <= 64 tokens (rows past n are zero)
+// goes through three phases separated by workgroup barriers:
 //
-// The state fragment built once per k-block serves as the B operand of
-// W S^T and as the A operand of S Q^T: an accumulator tile already holds, in
-// every lane, the eight k-slots a fragment needs (see gdn_device.hpp).
+//   1a  chain : X = V - s exp(gamma) * (K S^T), U' = T X            (MFMA)
+//       helper: P[r][s] = exp(gamma_r - gamma_s) q_r . k_s (s <= r)  (MFMA)
+//   1b  chain : S^T <- exp(gamma_C) S^T + K^T diag(exp(gamma_C - gamma)) U'
+//               and the tile amax
+//       helper: O = s exp(gamma) * (Q S^T) + P U', stored to o
+//   2   chain : QDQ: s = amax / 448, S <- RNE_E4M3(S / s) s
+//       helper: the next chunk's q, k, v, T and gates registers -> LDS,
+//               gate scan, and the global loads of the chunk after it
+//
+// U' = T X is U - W S^T with U = T V and W = T (exp(gamma) * K) regrouped, so
+// W is never formed.  Then the recurrent suffix (tokens P_n < t <= L_n, QDQ
+// after every write) and the final state store.
+//
+// LDS operands are kept in MFMA fragment order ("dumps"): fragment f of a
+// buffer is 64 lanes x 8 elements, lane-major, laid out exactly as the lanes
+// consume it (see the conventions in gdn_device.hpp), so every operand read
+// is one lane-linear load without bank conflicts.
 //
 // Precision (bf16 inputs, fp32 accumulate): q, k, v enter the MFMAs exactly;
-// T, P and U' as hi + lo bf16 pairs; exp(gamma) * K and W as one bf16 each.
-// After a QDQ the state is code * s with the code exactly representable in
-// bf16, so it is fed as the codes and the products are scaled by s; otherwise
-// (QDQ off, supplied initial state) as a hi + lo pair.  fp32 inputs use the
-// fp32 MFMA throughout.
+// T, P, X, U' and exp(gamma_C - gamma) U' as hi + lo bf16 pairs.  After a QDQ
+// the state is code * s with the code exactly representable in bf16, so it is
+// fed as the codes and the products are scaled by s; otherwise (QDQ off, a
+// supplied initial state) as a hi + lo pair.  fp32 inputs use the fp32 MFMA
+// throughout.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
+constexpr int kChunkWaves = 8;
+constexpr int kChunkThreads = 64 * kChunkWaves;
+constexpr int kHelperThreads = 256;  // waves 4..7
+constexpr float kLog2e = 1.4426950408889634f;
+
 struct Frag8 {
   float v[8];
 };
 
-// bf16 engine: LDS operands are bf16 bit patterns.
+// Direct global -> LDS copy: lane l of the wave writes the 16 (or 4) bytes at
+// src to dst + 16 l (4 l); dst must be the same in every lane.
+__device__ __forceinline__ void lds_load16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+// Wait until this wave's outstanding vector memory operations (including
+// direct LDS loads) have completed.
+__device__ __forceinline__ void wait_vmem() { wait_vmem(); }
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// bf16 engine: LDS operands are bf16 bit patterns, fragments 8 x bf16.
 struct EngBF16 {
   using E = uint16_t;
   using Fr = bf16x8;
   static constexpr bool kSplit = true;
-  static __device__ __forceinline__ Fr load(const E* row, int kb, int gq) {
-    const uint2 a = *reinterpret_cast<const uint2*>(row + 32 * kb + 4 * gq);
-    const uint2 b = *reinterpret_cast<const uint2*>(row + 32 * kb + 16 + 4 * gq);
-    return __builtin_bit_cast(Fr, make_uint4(a.x, a.y, b.x, b.y));
-  }
+  static constexpr int kPlanes = 2;  // hi and lo planes of split operands
+  static __device__ __forceinline__ Fr ld(const E* p) { return *reinterpret_cast<const Fr*>(p); }
+  static __device__ __forceinline__ void st(E* p, const Fr& f) { *reinterpret_cast<Fr*>(p) = f; }
   static __device__ __forceinline__ void mma(f32x4& c, const Fr& a, const Fr& b) { mma_bf16(c, a, b); }
   static __device__ __forceinline__ Fr round(const float (&x)[8]) {
     return __builtin_bit_cast(Fr, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
@@ -69,41 +91,46 @@ struct EngBF16 {
     hi = __builtin_bit_cast(Fr, make_uint4(h[0], h[1], h[2], h[3]));
     lo = __builtin_bit_cast(Fr, make_uint4(l[0], l[1], l[2], l[3]));
   }
-  // fragment with every element j multiplied by f[j] (one rounding)
-  static __device__ __forceinline__ Fr scale(const Fr& x, const float (&f)[8]) {
-    const uint4 u = __builtin_bit_cast(uint4, x);
-    const float v[8] = {bf16_lo(u.x) * f[0], bf16_hi(u.x) * f[1], bf16_lo(u.y) * f[2], bf16_hi(u.y) * f[3],
-                        bf16_lo(u.z) * f[4], bf16_hi(u.z) * f[5], bf16_lo(u.w) * f[6], bf16_hi(u.w) * f[7]};
-    return round(v);
+  // fragment from two 4-element pieces (k slots 0..3 and 4..7)
+  static __device__ __forceinline__ Fr ld2(const E* a, const E* b) {
+    const uint2 u = *reinterpret_cast<const uint2*>(a);
+    const uint2 v = *reinterpret_cast<const uint2*>(b);
+    return __builtin_bit_cast(Fr, make_uint4(u.x, u.y, v.x, v.y));
   }
-  static __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+  static __device__ __forceinline__ Fr pack8(const E (&x)[8]) {
+    return __builtin_bit_cast(Fr, make_uint4((uint32_t)x[0] | ((uint32_t)x[1] << 16),
+                                             (uint32_t)x[2] | ((uint32_t)x[3] << 16),
+                                             (uint32_t)x[4] | ((uint32_t)x[5] << 16),
+                                             (uint32_t)x[6] | ((uint32_t)x[7] << 16)));
   }
-  static __device__ __forceinline__ void store4_split(E* ph, E* pl, const float (&x)[4]) {
+  static __device__ __forceinline__ float to_f(E x) { return bf16_bits_to_float(x); }
+  // four values -> hi at ph, lo at pl
+  static __device__ __forceinline__ void st4_split(E* ph, E* pl, const float (&x)[4]) {
     uint32_t h0, l0, h1, l1;
     split_bf16x2(x[0], x[1], h0, l0);
     split_bf16x2(x[2], x[3], h1, l1);
     *reinterpret_cast<uint2*>(ph) = make_uint2(h0, h1);
     *reinterpret_cast<uint2*>(pl) = make_uint2(l0, l1);
   }
-  // two rows, same column: one 4-byte LDS write of (row r, row r+1)
-  static __device__ __forceinline__ void store_pair(E* p, E a, E b) {
-    *reinterpret_cast<uint32_t*>(p) = (uint32_t)a | ((uint32_t)b << 16);
-  }
 };
 
-// fp32 engine: LDS operands are fp32, products use the fp32 MFMA.
+// fp32 engine: LDS operands are fp32, fragments 8 x fp32, products on the fp32 MFMA.
 struct EngF32 {
   using E = float;
   using Fr = Frag8;
   static constexpr bool kSplit = false;
-  static __device__ __forceinline__ Fr load(const E* row, int kb, int gq) {
-    const float4 a = *reinterpret_cast<const float4*>(row + 32 * kb + 4 * gq);
-    const float4 b = *reinterpret_cast<const float4*>(row + 32 * kb + 16 + 4 * gq);
+  static constexpr int kPlanes = 1;
+  static __device__ __forceinline__ Fr ld(const E* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
     Fr f;
     f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
     return f;
+  }
+  static __device__ __forceinline__ void st(E* p, const Fr& f) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
   }
   static __device__ __forceinline__ void mma(f32x4& c, const Fr& a, const Fr& b) { mma_f32(c, a.v, b.v); }
   static __device__ __forceinline__ Fr round(const float (&x)[8]) {
@@ -116,47 +143,58 @@ struct EngF32 {
     hi = round(x);
     (void)lo;
   }
-  static __device__ __forceinline__ Fr scale(const Fr& x, const float (&f)[8]) {
-    Fr r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r.v[j] = x.v[j] * f[j];
-    return r;
+  static __device__ __forceinline__ Fr ld2(const E* a, const E* b) {
+    const float4 u = *reinterpret_cast<const float4*>(a);
+    const float4 v = *reinterpret_cast<const float4*>(b);
+    Fr f;
+    f.v[0] = u.x; f.v[1] = u.y; f.v[2] = u.z; f.v[3] = u.w;
+    f.v[4] = v.x; f.v[5] = v.y; f.v[6] = v.z; f.v[7] = v.w;
+    return f;
   }
-  static __device__ __forceinline__ void store4(E* p, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-  }
-  static __device__ __forceinline__ void store4_split(E* ph, E* pl, const float (&x)[4]) {
+  static __device__ __forceinline__ Fr pack8(const E (&x)[8]) { return round(x); }
+  static __device__ __forceinline__ float to_f(E x) { return x; }
+  static __device__ __forceinline__ void st4_split(E* ph, E* pl, const float (&x)[4]) {
     (void)pl;
     *reinterpret_cast<float4*>(ph) = make_float4(x[0], x[1], x[2], x[3]);
   }
-  static __device__ __forceinline__ void store_pair(E* p, E a, E b) {
-    *reinterpret_cast<float2*>(p) = make_float2(a, b);
-  }
 };
 
-// LDS layout of the sequential kernel (bytes).  Row strides are padded so
-// that the 16 rows read by one fragment load fall in different banks; [64][dk]
-// rows stay 16-byte aligned for the staging stores.
+// LDS layout of the sequential kernel (bytes).  F = one fragment dump.
+//   K   [64][DK + 16 bytes]  the chunk's k rows, row-major, rows padded by 16
+//                  bytes, filled by direct global->LDS loads; A of K S^T, A of P
+//   Q   2 x [64][DK + 16 bytes]  the same for q, double-buffered by chunk
+//                  parity; B of P, B of S Q^T
+//   KT  [dt][kb]   dump: A of the state update (row = key)     2 NT fragments
+//   V   [64][64 + 16 bytes]  the tile's v rows
+//   T   [plane][p] 6 fragments per plane (the prep kernel's record, copied as is)
+//   P   [plane][p] 6 fragments per plane, same pairs as T
+//   XU  [c][plane*2 + kb]     U' as the A operand of U'^T P^T, per chain wave
+//   XS  [c][plane*NKB + kb]   the state as the A operand of S Q^T, per chain wave
+//   G   [64]       the chunk's log-gates
+//   vec gamma*log2(e), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
+//   red the four chain waves' amax
 template <int DK, class Eng>
-struct Smem {
+struct Lds {
   using E = typename Eng::E;
-  static constexpr int LDK = DK + 16 / (int)sizeof(E);  // stride of [64][DK] buffers (E)
-  static constexpr int L64 = 64 + 4;                     // stride of [*][64] buffers (E)
-  static constexpr int kSplitN = Eng::kSplit ? 2 : 1;
-  static constexpr size_t szK = 64 * LDK * sizeof(E);
-  static constexpr size_t szKT = DK * L64 * sizeof(E);
-  static constexpr size_t szM = 64 * L64 * sizeof(E);  // one 64x64 operand matrix
+  static constexpr int NKB = DK / 32, NT = DK / 16, NP = Eng::kPlanes;
+  static constexpr size_t F = 64 * 8 * sizeof(E);
+  static constexpr size_t RK = DK * sizeof(E) + 16;  // padded q/k row (bytes)
+  static constexpr size_t RV = 64 * sizeof(E) + 16;  // padded v row (bytes)
   static constexpr size_t oK = 0;
-  static constexpr size_t oKT = oK + szK;
-  static constexpr size_t oQ = oKT + szKT;
-  static constexpr size_t oVT = oQ + szK;
-  static constexpr size_t oT = oVT + szM;               // T hi [, T lo]
-  static constexpr size_t oP = oT + kSplitN * szM;      // P hi [, P lo]
-  static constexpr size_t oW = oP + kSplitN * szM;      // W [64][DK]
-  static constexpr size_t oVec = oW + szK;              // gamma*log2e, e^gamma, e^(gC-gamma), beta
-  static constexpr size_t oRed = oVec + 4 * 64 * sizeof(float);
-  static constexpr size_t bytes = oRed + 16 * sizeof(float);
+  static constexpr size_t oQ = oK + 64 * RK;
+  static constexpr size_t oKT = oQ + 2 * 64 * RK;
+  static constexpr size_t oV = oKT + 2 * NT * F;
+  static constexpr size_t oT = oV + 64 * RV;
+  static constexpr size_t oP = oT + 6 * NP * F;
+  static constexpr size_t oXU = oP + 6 * NP * F;
+  static constexpr size_t oXS = oXU + 4 * 2 * NP * F;
+  static constexpr size_t oG = oXS + 4 * NKB * NP * F;
+  static constexpr size_t oVec = oG + 64 * sizeof(float);
+  static constexpr size_t oRed = oVec + (3 * 64 + 8) * sizeof(float);
+  static constexpr size_t bytes = oRed + 8 * sizeof(float);
+  static_assert(6 * NP * F == kTRecBytes, "T record and its LDS copy differ");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
+  static_assert(oK + (2 * DK + 64 + 8) * sizeof(float) <= oQ, "suffix buffers do not fit");
 };
 
 struct ChunkArgs {
@@ -169,7 +207,7 @@ struct ChunkArgs {
   const int32_t* seq_lens;
   const int32_t* prefix_lens;
   const int32_t* chunk_offs;  // prefix sums of ceil(P_n / 64) (prep kernel)
-  const void* T;              // 16 KiB record per (chunk, head) (prep kernel)
+  const void* T;              // one T record per (chunk, head) (prep kernel)
   const float* init;
   void* o;
   float* fin;
@@ -182,51 +220,54 @@ struct ChunkArgs {
   unsigned flags;
 };
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 template <int DK, class Eng, typename TIO, typename TO>
-__global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
-  using S_ = Smem<DK, Eng>;
+__global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
+  using Ls = Lds<DK, Eng>;
   using E = typename Eng::E;
   using Fr = typename Eng::Fr;
-  constexpr int LDK = S_::LDK;
-  constexpr int L64 = S_::L64;
-  constexpr int NT = DK / 16;   // state accumulator tiles per wave
+  constexpr int NT = DK / 16;   // state accumulator tiles per chain wave
   constexpr int NKB = DK / 32;  // k-blocks over dk
+  constexpr int NP = Eng::kPlanes;
+  constexpr bool kSplit = Eng::kSplit;
   extern __shared__ __align__(16) char smem[];
-  E* sK = reinterpret_cast<E*>(smem + S_::oK);
-  E* sKT = reinterpret_cast<E*>(smem + S_::oKT);
-  E* sQ = reinterpret_cast<E*>(smem + S_::oQ);
-  E* sVT = reinterpret_cast<E*>(smem + S_::oVT);
-  E* sTh = reinterpret_cast<E*>(smem + S_::oT);
-  E* sTl = sTh + 64 * L64;
-  E* sPh = reinterpret_cast<E*>(smem + S_::oP);
-  E* sPl = sPh + 64 * L64;
-  E* sW = reinterpret_cast<E*>(smem + S_::oW);
-  float* sG2 = reinterpret_cast<float*>(smem + S_::oVec);  // gamma * log2(e)
-  float* sEg = sG2 + 64;
-  float* sEgc = sEg + 64;
-  float* sBeta = sEgc + 64;
-  float* sRed = reinterpret_cast<float*>(smem + S_::oRed);
+  E* sK = reinterpret_cast<E*>(smem + Ls::oK);
+  E* sQ = reinterpret_cast<E*>(smem + Ls::oQ);
+  E* sKT = reinterpret_cast<E*>(smem + Ls::oKT);
+  E* sV = reinterpret_cast<E*>(smem + Ls::oV);
+  E* sT = reinterpret_cast<E*>(smem + Ls::oT);
+  E* sP = reinterpret_cast<E*>(smem + Ls::oP);
+  E* sXU = reinterpret_cast<E*>(smem + Ls::oXU);
+  E* sXS = reinterpret_cast<E*>(smem + Ls::oXS);
+  float* sG = reinterpret_cast<float*>(smem + Ls::oG);      // raw log-gates of the staged chunk
+  float* sG2 = reinterpret_cast<float*>(smem + Ls::oVec);  // gamma * log2(e)
+  float* sEg = sG2 + 64;                                    // exp(gamma)
+  float* sEgc = sEg + 64;                                   // exp(gamma_C - gamma)
+  float* sMisc = sEgc + 64;  // [0] exp(gamma_C) of the staged chunk, [1] scale of the state entering it
+  float* sRed = reinterpret_cast<float*>(smem + Ls::oRed);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;        // wave
   const int lane = tid & 63;
   const int gq = lane >> 4;      // lane group (k-slots / accumulator rows 4gq..4gq+3)
   const int ln = lane & 15;      // accumulator column / fragment row
+  const bool chain = w < 4;
+  const int c4 = w & 3;          // value block (16 columns) this wave serves
+  const int hw = uniform(w) - 4;    // helper wave index (waves 4..7)
+  // fragment f of an LDS dump, this lane's slot
+  auto slot = [lane](E* base, int f) { return base + (f * 64 + lane) * 8; };
 
   const int H = args.H, dv = args.dv;
   const int tiles = dv / kTileRows;
   // Block -> (n*H + h, vt).  Workgroups are dispatched to the 8 XCDs round
   // robin; when heads come in groups of 8, the value tiles of one head get
-  // block ids 8 apart, i.e. the same XCD, so their q/k reads share an L2.
+  // block ids 8 apart, i.e. the same XCD, so their q/k/T reads share an L2.
   int nh, vt;
   {
     const int b = blockIdx.x, G = gridDim.x;
     if (tiles > 1 && G % (8 * tiles) == 0) {
-      const int slot = b >> 3;
-      vt = slot % tiles;
-      nh = (slot / tiles) * 8 + (b & 7);
+      const int slot8 = b >> 3;
+      vt = slot8 % tiles;
+      nh = (slot8 / tiles) * 8 + (b & 7);
     } else {
       vt = b % tiles;
       nh = b / tiles;
@@ -247,146 +288,102 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
   TO* go_ = reinterpret_cast<TO*>(args.o);
   const int64_t qk_row = (int64_t)H * DK;   // token stride of q, k
   const int64_t v_row = (int64_t)H * dv;    // token stride of v, o
-  const int vcol0 = kTileRows * vt + 16 * w + ln;  // this lane's value column (in dv)
-
-  // ---- state: st[t][i] = S^T[16t + 4gq + i][vcol] = S[vcol][16t + 4gq + i]
-  f32x4 st[NT];
+  const int vcol0 = kTileRows * vt + 16 * c4 + ln;  // chain lane's value column (in dv)
   const int64_t state_base = ((int64_t)nh * dv + vcol0) * DK;  // row vcol0 of S
-  if (args.init != nullptr) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float4 x = *reinterpret_cast<const float4*>(args.init + state_base + 16 * t + 4 * gq);
-      st[t] = f32x4{x.x, x.y, x.z, x.w};
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bool coded = false;   // state is code * s_cur with codes on the E4M3 grid
-  float s_cur = 1.0f;
-  float inv_s = 1.0f;
 
   const int n_chunks = (P + kChunk - 1) / kChunk;
   const int bound0 = args.bound_offsets ? args.bound_offsets[n] : 0;
   const int chunk0 = args.chunk_offs[n];
 
-  // ---- staging geometry: 16-byte segments, two adjacent rows per thread
-  constexpr int EPS = 16 / (int)sizeof(TIO);   // elements per segment
-  constexpr int SPR = DK / EPS;                // segments per q/k row
-  constexpr int NPK = 64 * SPR / kThreads / 2; // row pairs per thread (q/k)
-  constexpr int VSPR = kTileRows / EPS;        // segments per v row
-  constexpr int NPV = 64 * VSPR / kThreads / 2;
-  constexpr int NTS = 16384 / 16 / kThreads;   // 16-byte pieces of a T record per thread
-  static_assert(NPK >= 1 && NPV >= 1 && NTS == 4, "staging geometry");
-  // per-thread global offsets (elements) of chunk 0; chunk c adds c * 64 rows
-  int64_t kq_off[NPK][2], v_off[NPV][2];
-  int kq_row[NPK][2], v_row_i[NPV][2];
+  // ---- chain-wave state: st[t][i] = S^T[16t + 4gq + i][vcol0] = S[vcol0][16t + 4gq + i]
+  f32x4 st[NT];
+  Fr sh[NKB];            // after a chunk QDQ: the codes as the MFMA operand (bf16 engine)
+  float s_cur = 1.0f;    // scale of the coded state
+  f32x4 uacc[4];         // U'[16tt + 4gq + i][vcol0], phase 1a -> 1b
+
+  // uncoded state -> operand fragments: hi + lo (bf16 engine) / exact fp32
+  auto state_frags = [&](Fr (&hi)[NKB], Fr (&lo)[NKB]) {
 #pragma unroll
-  for (int j = 0; j < NPK; ++j)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int r = 2 * (tid / SPR + (kThreads / SPR) * j) + e;
-      kq_row[j][e] = r;
-      kq_off[j][e] = (int64_t)(seg0 + r) * qk_row + (int64_t)h * DK + (tid % SPR) * EPS;
-    }
-#pragma unroll
-  for (int j = 0; j < NPV; ++j)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int r = 2 * (tid / VSPR + (kThreads / VSPR) * j) + e;
-      v_row_i[j][e] = r;
-      v_off[j][e] = (int64_t)(seg0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + (tid % VSPR) * EPS;
-    }
-  const uint4* Trec = reinterpret_cast<const uint4*>(args.T);
-  uint4 pk[NPK][2], pq[NPK][2], pv[NPV][2], pt[NTS];
-  float pg = 0.f, pb = 0.f;
-  // Loads are unconditional (rows past the chunk's valid count are clamped to
-  // its last valid row) so they stay in flight; the zero mask is applied when
-  // the data is written to LDS.
-  auto fetch = [&](int c) {
-    const int nv = min(kChunk, P - c * kChunk);
-    const int64_t dqk = (int64_t)c * kChunk * qk_row, dvv = (int64_t)c * kChunk * v_row;
-#pragma unroll
-    for (int j = 0; j < NPK; ++j)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t clamp = (int64_t)(min(kq_row[j][e], nv - 1) - kq_row[j][e]) * qk_row;
-        pk[j][e] = *reinterpret_cast<const uint4*>(gk_ + kq_off[j][e] + dqk + clamp);
-        pq[j][e] = *reinterpret_cast<const uint4*>(gq_ + kq_off[j][e] + dqk + clamp);
-      }
-#pragma unroll
-    for (int j = 0; j < NPV; ++j)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t clamp = (int64_t)(min(v_row_i[j][e], nv - 1) - v_row_i[j][e]) * v_row;
-        pv[j][e] = *reinterpret_cast<const uint4*>(gv_ + v_off[j][e] + dvv + clamp);
-      }
-    const uint4* rec = Trec + ((int64_t)(chunk0 + c) * H + h) * (16384 / 16);
-#pragma unroll
-    for (int j = 0; j < NTS; ++j) pt[j] = rec[tid + kThreads * j];
-    if (w == 0) {
-      const int64_t gi = (int64_t)(seg0 + c * kChunk + min(lane, nv - 1)) * H + h;
-      pg = args.g[gi];
-      pb = args.beta[gi];
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float x[8] = {st[2 * kb][0], st[2 * kb][1], st[2 * kb][2], st[2 * kb][3],
+                          st[2 * kb + 1][0], st[2 * kb + 1][1], st[2 * kb + 1][2], st[2 * kb + 1][3]};
+      Eng::split(x, hi[kb], lo[kb]);
     }
   };
-  if (n_chunks > 0) fetch(0);
-
-  for (int c = 0; c < n_chunks; ++c) {
-    const int t0 = seg0 + c * kChunk;
-    const int nv = min(kChunk, P - c * kChunk);  // valid tokens in this chunk
-
-    // ---------------- a1: staged registers -> LDS; gates ----------------
-    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  // the state fragments for the helper wave's S Q^T (lo only when split)
+  auto write_xs = [&](const Fr (&hi)[NKB], const Fr (&lo)[NKB], bool two) {
 #pragma unroll
-    for (int j = 0; j < NPK; ++j)
+    for (int kb = 0; kb < NKB; ++kb) Eng::st(slot(sXS, c4 * NP * NKB + kb), hi[kb]);
+    if constexpr (kSplit) {
+      if (two) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        if (kq_row[j][e] >= nv) { pk[j][e] = zero4; pq[j][e] = zero4; }
-#pragma unroll
-    for (int j = 0; j < NPV; ++j)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        if (v_row_i[j][e] >= nv) pv[j][e] = zero4;
-    if (lane >= nv) { pg = 0.f; pb = 0.f; }
-#pragma unroll
-    for (int j = 0; j < NPK; ++j) {
-      const int r0 = kq_row[j][0], c0 = (tid % SPR) * EPS;
-      *reinterpret_cast<uint4*>(sK + r0 * LDK + c0) = pk[j][0];
-      *reinterpret_cast<uint4*>(sK + (r0 + 1) * LDK + c0) = pk[j][1];
-      *reinterpret_cast<uint4*>(sQ + r0 * LDK + c0) = pq[j][0];
-      *reinterpret_cast<uint4*>(sQ + (r0 + 1) * LDK + c0) = pq[j][1];
-      E k0[EPS], k1[EPS];
-      __builtin_memcpy(k0, &pk[j][0], 16);
-      __builtin_memcpy(k1, &pk[j][1], 16);
-#pragma unroll
-      for (int e = 0; e < EPS; ++e) Eng::store_pair(sKT + (c0 + e) * L64 + r0, k0[e], k1[e]);
-    }
-#pragma unroll
-    for (int j = 0; j < NPV; ++j) {
-      const int r0 = v_row_i[j][0], c0 = (tid % VSPR) * EPS;
-      E v0[EPS], v1[EPS];
-      __builtin_memcpy(v0, &pv[j][0], 16);
-      __builtin_memcpy(v1, &pv[j][1], 16);
-#pragma unroll
-      for (int e = 0; e < EPS; ++e) Eng::store_pair(sVT + (c0 + e) * L64 + r0, v0[e], v1[e]);
-    }
-    // T record: bf16 = hi plane then lo plane ([64][64] each); fp32 = one plane
-#pragma unroll
-    for (int j = 0; j < NTS; ++j) {
-      const int idx = tid + kThreads * j;            // 16-byte piece
-      if constexpr (Eng::kSplit) {
-        const int plane = idx >> 9, rr = (idx >> 3) & 63, cc = (idx & 7) * 8;
-        E* dst = (plane ? sTl : sTh) + rr * L64 + cc;
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(pt[j].x, pt[j].y);
-        reinterpret_cast<uint2*>(dst)[1] = make_uint2(pt[j].z, pt[j].w);
-      } else {
-        const int rr = idx >> 4, cc = (idx & 15) * 4;
-        *reinterpret_cast<uint4*>(sTh + rr * L64 + cc) = pt[j];
+        for (int kb = 0; kb < NKB; ++kb) Eng::st(slot(sXS, c4 * NP * NKB + NKB + kb), lo[kb]);
       }
     }
-    if (w == 0) {
-      float x = pg;
+  };
+
+  // ---- raw row buffers: rows of 16-byte pieces padded by one piece, so the
+  // 16 rows one fragment load touches fall in different banks
+  constexpr int EPP = 16 / (int)sizeof(E);  // elements per piece
+  constexpr int PPR = DK / EPP;             // pieces per q/k row
+  constexpr int PPV = kTileRows / EPP;      // pieces per v row
+  constexpr int RSK = (PPR + 1) * EPP;      // q/k row stride (elements)
+  constexpr int RSV = (PPV + 1) * EPP;      // v row stride (elements)
+  static_assert(sizeof(TIO) == sizeof(E), "LDS element type is the input type");
+  // A/B fragment of row r (k-block kb) from a raw q/k buffer
+  auto rowfrag = [&](const E* base, int r, int kb) {
+    const E* p = base + r * RSK + 32 * kb + 4 * gq;
+    return Eng::ld2(p, p + 16);
+  };
+
+  // Helper waves: direct global -> LDS loads of chunk cc (k, q, v rows, the T
+  // record, the log-gates).  One instruction writes 64 consecutive 16-byte LDS
+  // pieces, i.e. whole padded rows (the pad piece gets a copy of the row's last
+  // piece).  Rows past the chunk's valid count load its last valid row: they
+  // meet zero rows and columns of T, or outputs that are not stored, so they
+  // need no zeroing.
+  auto load_rows = [&](const TIO* src, int64_t stride, E* dst, int ppr, int nv) {
+    const int rpi = 64 / (ppr + 1);                 // rows per instruction
+    const int rr = lane / (ppr + 1), pc = lane % (ppr + 1);
+    const int64_t lane_off = (int64_t)min(pc, ppr - 1) * EPP;
+    for (int i = hw; i * rpi < 64; i += 4) {
+      const int r = i * rpi + rr;
+      if (rr < rpi && r < 64)
+        lds_load16(src + (int64_t)min(r, nv - 1) * stride + lane_off, dst + i * rpi * (ppr + 1) * EPP);
+    }
+  };
+  auto issue = [&](int cc) {
+    const int nv = min(kChunk, P - cc * kChunk);
+    const int64_t row0 = seg0 + cc * kChunk;
+    load_rows(gk_ + row0 * qk_row + (int64_t)h * DK, qk_row, sK, PPR, nv);
+    load_rows(gq_ + row0 * qk_row + (int64_t)h * DK, qk_row, sQ + (cc & 1) * (64 * RSK), PPR, nv);
+    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, v_row, sV, PPV, nv);
+    const char* rec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
+#pragma unroll
+    for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
+      const int idx = hw * (kTRecBytes / 1024 / 4) + ii;
+      lds_load16(rec + (idx * 64 + lane) * 16, reinterpret_cast<char*>(sT) + idx * 1024);
+    }
+    if (hw == 0) lds_load4(args.g + (row0 + min(lane, nv - 1)) * H + h, sG);
+  };
+  // Helper waves, after every helper's loads have landed: the K^T dump
+  // (fragment f = 2 dt + kb, lane l holds K[32 kb + kperm(l/16, j)][16 dt + l%16])
+  // and the gate scan.
+  auto transform = [&](int cc) {
+    const int nv = min(kChunk, P - cc * kChunk);
+#pragma unroll
+    for (int m = 0; m < NT / 2; ++m) {
+      const int f = hw + 4 * m, dt = f >> 1, kb = f & 1;
+      E x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
+        x[j] = sK[r * RSK + 16 * dt + ln];
+      }
+      Eng::st(slot(sKT, f), Eng::pack8(x));
+    }
+    if (hw == 0) {
+      float x = (lane < nv) ? sG[lane] : 0.f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -396,342 +393,382 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_fwd_kernel(ChunkArgs args) 
       sG2[lane] = x * kLog2e;
       sEg[lane] = __builtin_amdgcn_exp2f(x * kLog2e);
       sEgc[lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
-      sBeta[lane] = pb;
-      if (lane == 0) sRed[4] = __builtin_amdgcn_exp2f(gC * kLog2e);
+      if (lane == 0) sMisc[0] = __builtin_amdgcn_exp2f(gC * kLog2e);
     }
-    if (c + 1 < n_chunks) fetch(c + 1);   // lands in registers while this chunk computes
+  };
+
+  // ---------------- prologue ----------------
+  if (chain) {
+    if (args.init != nullptr) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float4 x = *reinterpret_cast<const float4*>(args.init + state_base + 16 * t + 4 * gq);
+        st[t] = f32x4{x.x, x.y, x.z, x.w};
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    Fr hi[NKB], lo[NKB];
+    state_frags(hi, lo);
+    write_xs(hi, lo, true);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];
+  } else if (n_chunks > 0) {
+    issue(0);
+    wait_vmem();
+  }
+  __syncthreads();
+  if (!chain && n_chunks > 0) transform(0);
+  __syncthreads();
+
+  for (int c = 0; c < n_chunks; ++c) {
+    const int t0 = seg0 + c * kChunk;
+    const int nv = min(kChunk, P - c * kChunk);  // valid tokens in this chunk
+    // the state entering this chunk is code * s_cur (bf16 engine, after a chunk QDQ)
+    const bool coded_in = kSplit && c > 0 && (flags & GDN_QDQ_CHUNK);
+    const bool two = kSplit && !coded_in;  // state operand as hi + lo
+    const bool last = (c == n_chunks - 1);
+    const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
+    const E* sQc = sQ + (c & 1) * (64 * (DK + 16 / (int)sizeof(E)));  // this chunk's q rows
+
+    // ======== phase 1a ========
+    if (chain) {
+      // K S^T: A = K rows (tokens), B = the state
+      const float sc = coded_in ? s_cur : 1.0f;
+      f32x4 acc[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (two) {  // uncoded state: hi + lo from the fp32 state
+        Fr hi[NKB], lo[NKB];
+        state_frags(hi, lo);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const Fr a = rowfrag(sK, 16 * tt + ln, kb);
+            Eng::mma(acc[tt], a, hi[kb]);
+            Eng::mma(acc[tt], a, lo[kb]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], rowfrag(sK, 16 * tt + ln, kb), sh[kb]);
+      }
+      // X[t][v] = V[t][v] - s exp(gamma_t) (K S^T)[t][v], t = 16tt + 4gq + i
+      Fr xh[2], xl[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float x8[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int tt = 2 * kb + hh;
+          const float4 e4 = *reinterpret_cast<const float4*>(sEg + 16 * tt + 4 * gq);
+          float vv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vv[i] = Eng::to_f(sV[(16 * tt + 4 * gq + i) * RSV + 16 * c4 + ln]);
+          x8[4 * hh + 0] = fmaf(-sc * e4.x, acc[tt][0], vv[0]);
+          x8[4 * hh + 1] = fmaf(-sc * e4.y, acc[tt][1], vv[1]);
+          x8[4 * hh + 2] = fmaf(-sc * e4.z, acc[tt][2], vv[2]);
+          x8[4 * hh + 3] = fmaf(-sc * e4.w, acc[tt][3], vv[3]);
+        }
+        Eng::split(x8, xh[kb], xl[kb]);
+      }
+      // U' = T X over the lower-triangular T pairs (ti, kb): (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) uacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        const Fr tf = Eng::ld(slot(sT, p));
+        Eng::mma(uacc[ti], tf, xh[kb]);
+        if constexpr (kSplit) {
+          const Fr tl = Eng::ld(slot(sT, 6 + p));
+          Eng::mma(uacc[ti], tf, xl[kb]);
+          Eng::mma(uacc[ti], tl, xh[kb]);
+        }
+      }
+      // U' as the A operand of U'^T P^T, for the helper wave
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float u8[8] = {uacc[2 * kb][0], uacc[2 * kb][1], uacc[2 * kb][2], uacc[2 * kb][3],
+                             uacc[2 * kb + 1][0], uacc[2 * kb + 1][1], uacc[2 * kb + 1][2],
+                             uacc[2 * kb + 1][3]};
+        Fr uh, ul;
+        Eng::split(u8, uh, ul);
+        Eng::st(slot(sXU, c4 * 2 * NP + kb), uh);
+        if constexpr (kSplit) Eng::st(slot(sXU, c4 * 2 * NP + 2 + kb), ul);
+      }
+    } else {
+      // P tiles: C[s][t] = k_s . q_t -> P[t][s] (s <= t), 10 lower tiles + 2
+      // zero tiles that complete the fragment pairs; 3 per helper wave
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj) {
+        const int job = hw + 4 * jj;
+        int ti, si;
+        if (job < 10) {
+          ti = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
+          si = job - (ti * (ti + 1)) / 2;
+        } else {
+          si = (job == 10) ? 1 : 3;
+          ti = si - 1;
+        }
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (job < 10) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            Eng::mma(acc, rowfrag(sK, 16 * si + ln, kb), rowfrag(sQc, 16 * ti + ln, kb));
+          const int t = 16 * ti + ln;
+          const float g2t = sG2[t];
+          const float4 g2s = *reinterpret_cast<const float4*>(sG2 + 16 * si + 4 * gq);
+          const float gs[4] = {g2s.x, g2s.y, g2s.z, g2s.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            x[i] = (16 * si + 4 * gq + i <= t) ? __builtin_amdgcn_exp2f(g2t - gs[i]) * acc[i] : 0.f;
+        }
+        const int pr = (si >= 2) ? ti + 2 : ti, jb = (si & 1) * 4;
+        Eng::st4_split(slot(sP, pr) + jb, slot(sP, 6 + pr) + jb, x);
+      }
+    }
     __syncthreads();
 
-    // ---------------- a3: P = decay * Q K^T (lower incl. diagonal) ----------------
-    // 10 lower tiles + 2 zero tiles read by the triangular products; 3 per wave
-#pragma unroll
-    for (int jj = 0; jj < 3; ++jj) {
-      const int job = w + 4 * jj;
-      int ri, si;
-      if (job < 10) {
-        ri = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
-        si = job - (ri * (ri + 1)) / 2;
-      } else {
-        si = (job == 10) ? 1 : 3;
-        ri = si - 1;
-      }
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-      if (job < 10) {
-        // C[s][r] = sum_d K[s][d] Q[r][d]
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        Fr af[NKB], bf[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          af[kb] = Eng::load(sK + (16 * si + ln) * LDK, kb, gq);
-          bf[kb] = Eng::load(sQ + (16 * ri + ln) * LDK, kb, gq);
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) Eng::mma(acc, af[kb], bf[kb]);
-        const int r = 16 * ri + ln;
-        const float g2r = sG2[r];
-        const float4 g2s = *reinterpret_cast<const float4*>(sG2 + 16 * si + 4 * gq);
-        const float gs[4] = {g2s.x, g2s.y, g2s.z, g2s.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * si + 4 * gq + i;
-          x[i] = (s <= r) ? __builtin_amdgcn_exp2f(g2r - gs[i]) * acc[i] : 0.f;
-        }
-      }
-      const int r = 16 * ri + ln;
-      Eng::store4_split(sPh + r * L64 + 16 * si + 4 * gq, sPl + r * L64 + 16 * si + 4 * gq, x);
-    }
-
-    // ---------------- a5: W^T = (e^gamma K)^T T^T (-> sW row-major), U = T V ----------------
-    f32x4 uacc[4];
-    {
-      constexpr int DPW = NT / 4;  // dk tiles of W^T per wave
-      // (ti, kb) pairs of the lower-triangular T: (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
-      Fr th[6], tl[6];
-#pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        th[p] = Eng::load(sTh + (16 * ti + ln) * L64, kb, gq);
-        if constexpr (Eng::kSplit) tl[p] = Eng::load(sTl + (16 * ti + ln) * L64, kb, gq);
-      }
-      Fr ka[DPW][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const float4 e0 = *reinterpret_cast<const float4*>(sEg + 32 * kb + 4 * gq);
-        const float4 e1 = *reinterpret_cast<const float4*>(sEg + 32 * kb + 16 + 4 * gq);
-        const float ef[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-#pragma unroll
-        for (int dd = 0; dd < DPW; ++dd)
-          ka[dd][kb] = Eng::scale(Eng::load(sKT + (16 * (DPW * w + dd) + ln) * L64, kb, gq), ef);
-      }
-      const Fr vb0 = Eng::load(sVT + (16 * w + ln) * L64, 0, gq);
-      const Fr vb1 = Eng::load(sVT + (16 * w + ln) * L64, 1, gq);
-      f32x4 wacc[DPW][4];
-#pragma unroll
-      for (int dd = 0; dd < DPW; ++dd)
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) wacc[dd][ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) uacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-#pragma unroll
-        for (int dd = 0; dd < DPW; ++dd) {
-          Eng::mma(wacc[dd][ti], ka[dd][kb], th[p]);
-          if constexpr (Eng::kSplit) Eng::mma(wacc[dd][ti], ka[dd][kb], tl[p]);
-        }
-        Eng::mma(uacc[ti], th[p], kb ? vb1 : vb0);
-        if constexpr (Eng::kSplit) Eng::mma(uacc[ti], tl[p], kb ? vb1 : vb0);
-      }
-      // wacc[dd][ti][i] = W^T[16di + 4gq + i][16ti + ln] = W[16ti + ln][16di + 4gq + i]
-#pragma unroll
-      for (int dd = 0; dd < DPW; ++dd)
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-          Eng::store4(sW + (16 * ti + ln) * LDK + 16 * (DPW * w + dd) + 4 * gq, wacc[dd][ti][0],
-                      wacc[dd][ti][1], wacc[dd][ti][2], wacc[dd][ti][3]);
-    }
-    __syncthreads();  // sP, sW complete
-
-    // ---------------- a6 + a7 (inter part): U' = U - W S^T ; O^T = S Q^T ----------------
-    // After a QDQ (bf16 engine) the state fragment holds the codes, exact in
-    // bf16, and the products are scaled by s.
-    const bool use_codes = Eng::kSplit && coded;
-    f32x4 wacc[4], oacc[4];   // wacc: [tok][vcol] tiles ; oacc: O^T [vcol 16w+4gq+i][tok 16ti+ln]
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      wacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-      oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      Fr aw[4], bq[4];
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        aw[ti] = Eng::load(sW + (16 * ti + ln) * LDK, kb, gq);
-        bq[ti] = Eng::load(sQ + (16 * ti + ln) * LDK, kb, gq);
-      }
-      float sv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = st[2 * kb][i];
-        sv[4 + i] = st[2 * kb + 1][i];
-      }
-      Fr sh, sl;
-      if (use_codes) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] *= inv_s;
-        sh = Eng::round(sv);
-      } else {
-        Eng::split(sv, sh, sl);
-      }
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        Eng::mma(wacc[ti], aw[ti], sh);   // W S^T     : A = W rows, B = state
-        Eng::mma(oacc[ti], sh, bq[ti]);   // (S Q^T)   : A = state,  B = Q rows
-      }
-      if constexpr (Eng::kSplit) {
-        if (!use_codes) {
-#pragma unroll
-          for (int ti = 0; ti < 4; ++ti) {
-            Eng::mma(wacc[ti], aw[ti], sl);
-            Eng::mma(oacc[ti], sl, bq[ti]);
-          }
-        }
-      }
-    }
-    const float sc = use_codes ? s_cur : 1.0f;
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const float egt = sc * sEg[16 * ti + ln];   // column tok = 16ti + ln of O^T
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uacc[ti][i] = fmaf(-sc, wacc[ti][i], uacc[ti][i]);
-        oacc[ti][i] *= egt;
-      }
-    }
-
-    // ---------------- a7 (intra part): O^T += U'^T P^T ----------------
-    {
-      Fr uh[2], ul[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float uv[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uv[i] = uacc[2 * kb][i];
-          uv[4 + i] = uacc[2 * kb + 1][i];
-        }
-        Eng::split(uv, uh[kb], ul[kb]);
-      }
-#pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        const Fr ph = Eng::load(sPh + (16 * ti + ln) * L64, kb, gq);
-        Eng::mma(oacc[ti], uh[kb], ph);
-        if constexpr (Eng::kSplit) {
-          const Fr pl = Eng::load(sPl + (16 * ti + ln) * L64, kb, gq);
-          Eng::mma(oacc[ti], ul[kb], ph);
-          Eng::mma(oacc[ti], uh[kb], pl);
-        }
-      }
-    }
-    // o rows: lane holds o[tok = 16ti + ln][16w + 4gq .. +3] of this tile
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const int tok = 16 * ti + ln;
-      if (tok < nv) {
-        TO* dst = go_ + (int64_t)(t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + 16 * w + 4 * gq;
-        if constexpr (sizeof(TO) == 2) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(oacc[ti][0], oacc[ti][1]),
-                                                      pack_bf16x2(oacc[ti][2], oacc[ti][3]));
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(oacc[ti][0], oacc[ti][1], oacc[ti][2], oacc[ti][3]);
-        }
-      }
-    }
-
-    // ---------------- a8: S^T <- e^gC S^T + K^T diag(e^(gC - gamma)) U' ----------------
-    {
+    // ======== phase 1b ========
+    if (chain) {
+      // S^T <- exp(gamma_C) S^T + K^T (exp(gamma_C - gamma) * U')
       Fr bh[2], bl[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const float4 e0 = *reinterpret_cast<const float4*>(sEgc + 32 * kb + 4 * gq);
         const float4 e1 = *reinterpret_cast<const float4*>(sEgc + 32 * kb + 16 + 4 * gq);
-        const float uv[8] = {e0.x * uacc[2 * kb][0], e0.y * uacc[2 * kb][1], e0.z * uacc[2 * kb][2],
+        const float u8[8] = {e0.x * uacc[2 * kb][0], e0.y * uacc[2 * kb][1], e0.z * uacc[2 * kb][2],
                              e0.w * uacc[2 * kb][3], e1.x * uacc[2 * kb + 1][0],
                              e1.y * uacc[2 * kb + 1][1], e1.z * uacc[2 * kb + 1][2],
                              e1.w * uacc[2 * kb + 1][3]};
-        Eng::split(uv, bh[kb], bl[kb]);
+        Eng::split(u8, bh[kb], bl[kb]);
       }
-      const float aC = sRed[4];
+      const float aC = sMisc[0];
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[t][i] *= aC;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const Fr a0 = Eng::load(sKT + (16 * t + ln) * L64, 0, gq);
-        const Fr a1 = Eng::load(sKT + (16 * t + ln) * L64, 1, gq);
+        const Fr a0 = Eng::ld(slot(sKT, 2 * t));
+        const Fr a1 = Eng::ld(slot(sKT, 2 * t + 1));
         Eng::mma(st[t], a0, bh[0]);
         Eng::mma(st[t], a1, bh[1]);
-        if constexpr (Eng::kSplit) {
+        if constexpr (kSplit) {
           Eng::mma(st[t], a0, bl[0]);
           Eng::mma(st[t], a1, bl[1]);
         }
       }
-    }
-
-    // ---------------- a9: boundary QDQ ----------------
-    const bool last = (c == n_chunks - 1);
-    const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
-    const int bidx = bound0 + c;
-    if (args.bound_pre) {
+      if (args.bound_pre) {
+        const int bidx = bound0 + c;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        *reinterpret_cast<float4*>(args.bound_pre + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
-                                   16 * t + 4 * gq) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
-    }
-    float s_new = 1.0f;
-    if (do_qdq) {
-      float amax = 0.f;
+        for (int t = 0; t < NT; ++t)
+          *reinterpret_cast<float4*>(args.bound_pre + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
+                                     16 * t + 4 * gq) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+      }
+      if (do_qdq) {
+        float amax = 0.f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t][i]));
-      amax = block_max(amax, sRed);  // also orders this chunk's LDS reads before the next chunk's writes
-      s_new = qdq_scale(amax);
-      const float r = 1.0f / s_new;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) qdq4(st[t], s_new, r);
-      coded = true;
-      s_cur = s_new;
-      inv_s = r;
+          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t][i]));
+        amax = wave_max(amax);
+        if (lane == 0) sRed[c4] = amax;
+      }
     } else {
-      coded = false;
-      __syncthreads();
-    }
-    if (args.bound_post) {
+      // the next chunk's loads fly while the output is formed
+      if (c + 1 < n_chunks) issue(c + 1);
+      // O^T[v][t] = s exp(gamma_t) (S Q^T)[v][t] + (U'^T P^T)[v][t], v in block c4
+      const float sc = coded_in ? sMisc[1] : 1.0f;
+      f32x4 oacc[4];
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
-                                   16 * t + 4 * gq) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+      for (int ti = 0; ti < 4; ++ti) oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const Fr sa = Eng::ld(slot(sXS, c4 * NP * NKB + kb));
+        Fr sb;
+        if (two) sb = Eng::ld(slot(sXS, c4 * NP * NKB + NKB + kb));
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          const Fr bq = rowfrag(sQc, 16 * ti + ln, kb);
+          Eng::mma(oacc[ti], sa, bq);
+          if (two) Eng::mma(oacc[ti], sb, bq);
+        }
+      }
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        const float egt = sc * sEg[16 * ti + ln];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[ti][i] *= egt;
+      }
+      Fr uh[2], ul[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uh[kb] = Eng::ld(slot(sXU, c4 * 2 * NP + kb));
+        if constexpr (kSplit) ul[kb] = Eng::ld(slot(sXU, c4 * 2 * NP + 2 + kb));
+      }
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        const Fr ph = Eng::ld(slot(sP, p));
+        Eng::mma(oacc[ti], uh[kb], ph);
+        if constexpr (kSplit) {
+          const Fr pl = Eng::ld(slot(sP, 6 + p));
+          Eng::mma(oacc[ti], ul[kb], ph);
+          Eng::mma(oacc[ti], uh[kb], pl);
+        }
+      }
+      // lane holds o[tok = 16ti + ln][16c4 + 4gq .. +3] of this tile
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        const int tok = 16 * ti + ln;
+        if (tok < nv) {
+          TO* dst = go_ + (int64_t)(t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + 16 * c4 + 4 * gq;
+          if constexpr (sizeof(TO) == 2) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(oacc[ti][0], oacc[ti][1]),
+                                                        pack_bf16x2(oacc[ti][2], oacc[ti][3]));
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(oacc[ti][0], oacc[ti][1], oacc[ti][2], oacc[ti][3]);
+          }
+        }
+      }
+      wait_vmem();  // this wave's loads are in LDS before the barrier
     }
-    if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
+    __syncthreads();
+
+    // ======== phase 2 ========
+    if (chain) {
+      float s_new = 1.0f;
+      if (do_qdq) {
+        const float amax = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
+        s_new = qdq_scale(amax);
+        const float r = 1.0f / s_new;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          float c0[4], c1[4];
+          qdq4c(st[2 * kb], c0, s_new, r);
+          qdq4c(st[2 * kb + 1], c1, s_new, r);
+          if constexpr (kSplit) {
+            const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
+          }
+        }
+        s_cur = s_new;
+      }
+      if (!last) {
+        if (kSplit && do_qdq) {
+          write_xs(sh, sh, false);
+        } else {
+          Fr hi[NKB], lo[NKB];
+          state_frags(hi, lo);
+          write_xs(hi, lo, true);
+          if constexpr (!kSplit) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];  // fp32 engine: the exact state
+          }
+        }
+        if (c4 == 0 && lane == 0) sMisc[1] = s_new;
+      }
+      const int bidx = bound0 + c;
+      if (args.bound_post) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
+                                     16 * t + 4 * gq) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+      }
+      if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
+    } else if (c + 1 < n_chunks) {
+      transform(c + 1);
+    }
+    __syncthreads();
   }
 
-  // ---------------- a10: recurrent suffix, tokens P < t <= L ----------------
+  // ---------------- recurrent suffix, tokens P < t <= L ----------------
   if (P < L) {
-    float* sq = reinterpret_cast<float*>(smem + S_::oW);  // q_t, k_t: DK each; v_t: 64
-    float* sk = sq + 256;
-    float* sv = sq + 512;
-    float* sg = sq + 640;    // g_t at sg[0], beta_t at sg[DK]
+    float* sq = reinterpret_cast<float*>(smem + Ls::oK);  // q_t, k_t: DK each; v_t: 64; g_t, beta_t
+    float* sk = sq + DK;
+    float* sv = sk + DK;
+    float* sgb = sv + 64;
     for (int t = P; t < L; ++t) {
       const int64_t row = seg0 + t;
-      if (tid < DK) {
-        sq[tid] = io<TIO>::ld(gq_ + row * qk_row + (int64_t)h * DK + tid);
-        sk[tid] = io<TIO>::ld(gk_ + row * qk_row + (int64_t)h * DK + tid);
-      }
-      if (tid < 64) sv[tid] = io<TIO>::ld(gv_ + row * v_row + (int64_t)h * dv + kTileRows * vt + tid);
-      if (tid == 0) {
-        sg[0] = args.g[row * H + h];
-        sg[DK] = args.beta[row * H + h];
+      if (!chain) {
+        const int th = tid - (kChunkThreads - kHelperThreads);
+        if (th < DK) {
+          sq[th] = io<TIO>::ld(gq_ + row * qk_row + (int64_t)h * DK + th);
+          sk[th] = io<TIO>::ld(gk_ + row * qk_row + (int64_t)h * DK + th);
+        }
+        if (th < 64) sv[th] = io<TIO>::ld(gv_ + row * v_row + (int64_t)h * dv + kTileRows * vt + th);
+        if (th == 0) {
+          sgb[0] = args.g[row * H + h];
+          sgb[1] = args.beta[row * H + h];
+        }
       }
       __syncthreads();
-      const float a = expf(sg[0]);
-      const float b = sg[DK];
-      float y = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < NT; ++t2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          st[t2][i] *= a;
-          y += st[t2][i] * sk[16 * t2 + 4 * gq + i];
-        }
-      y += __shfl_xor(y, 16, 64);
-      y += __shfl_xor(y, 32, 64);
-      const float u = b * (sv[16 * w + ln] - y);
-      float z = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < NT; ++t2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          st[t2][i] += u * sk[16 * t2 + 4 * gq + i];
-          z += st[t2][i] * sq[16 * t2 + 4 * gq + i];
-        }
-      z += __shfl_xor(z, 16, 64);
-      z += __shfl_xor(z, 32, 64);
-      if (gq == 0) io<TO>::st(go_ + row * v_row + (int64_t)h * dv + vcol0, z);
-      if (flags & GDN_QDQ_WRITE) {
-        float amax = 0.f;
+      if (chain) {
+        const float a = expf(sgb[0]);
+        const float b = sgb[1];
+        float y = 0.f;
 #pragma unroll
         for (int t2 = 0; t2 < NT; ++t2)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t2][i]));
-        amax = block_max(amax, sRed);
-        const float s = qdq_scale(amax);
+          for (int i = 0; i < 4; ++i) {
+            st[t2][i] *= a;
+            y += st[t2][i] * sk[16 * t2 + 4 * gq + i];
+          }
+        y += __shfl_xor(y, 16, 64);
+        y += __shfl_xor(y, 32, 64);
+        const float u = b * (sv[16 * c4 + ln] - y);
+        float z = 0.f;
+#pragma unroll
+        for (int t2 = 0; t2 < NT; ++t2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            st[t2][i] += u * sk[16 * t2 + 4 * gq + i];
+            z += st[t2][i] * sq[16 * t2 + 4 * gq + i];
+          }
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        if (gq == 0) io<TO>::st(go_ + row * v_row + (int64_t)h * dv + vcol0, z);
+        if (flags & GDN_QDQ_WRITE) {
+          float amax = 0.f;
+#pragma unroll
+          for (int t2 = 0; t2 < NT; ++t2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t2][i]));
+          amax = wave_max(amax);
+          if (lane == 0) sRed[c4] = amax;
+        }
+      }
+      __syncthreads();
+      if (chain && (flags & GDN_QDQ_WRITE)) {
+        const float s = qdq_scale(fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3])));
         const float r = 1.0f / s;
 #pragma unroll
         for (int t2 = 0; t2 < NT; ++t2) qdq4(st[t2], s, r);
-      } else {
-        __syncthreads();
       }
     }
   }
 
-  // ---------------- a11: final state, zero padding rows of o ----------------
+  // ---------------- final state, zero padding rows of o ----------------
+  if (chain) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    *reinterpret_cast<float4*>(args.fin + state_base + 16 * t + 4 * gq) =
-        make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
-  for (int r = L + (tid >> 6); r < seg1 - seg0; r += 4)
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<float4*>(args.fin + state_base + 16 * t + 4 * gq) =
+          make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+  }
+  for (int r = L + w; r < seg1 - seg0; r += kChunkWaves)
     io<TO>::st(go_ + (int64_t)(seg0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + lane, 0.f);
 }
 
 template <int DK, class Eng, typename TIO, typename TO>
 static hipError_t launch_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
   auto kern = chunk_fwd_kernel<DK, Eng, TIO, TO>;
-  constexpr size_t lds = Smem<DK, Eng>::bytes;
+  constexpr size_t lds = Lds<DK, Eng>::bytes;
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -739,7 +776,7 @@ static hipError_t launch_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStre
     attr_set = true;
   }
   const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kChunkThreads), lds, stream, a);
   return hipGetLastError();
 }
 

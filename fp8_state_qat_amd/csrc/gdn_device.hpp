@@ -43,13 +43,21 @@ __device__ __forceinline__ float div_rn(float x, float s, float r) {
   return fmaf(e, r, q);
 }
 
-// QDQ of two values with scale s and r = RN(1 / s).  gfx950's
-// v_cvt_pk_fp8_f32 rounds to the nearest OCP E4M3FN value (ties to even).
-__device__ __forceinline__ void qdq2(float& x0, float& x1, float s, float r) {
+// QDQ of two values with scale s and r = RN(1 / s); c0, c1 receive the E4M3
+// values (the codes as floats).  gfx950's v_cvt_pk_fp8_f32 rounds to the
+// nearest OCP E4M3FN value (ties to even).
+__device__ __forceinline__ void qdq2c(float& x0, float& x1, float s, float r, float& c0, float& c1) {
   const float y0 = div_rn(x0, s, r), y1 = div_rn(x1, s, r);
   const int p = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-  x0 = copysignf(__builtin_amdgcn_cvt_f32_fp8(p, 0) * s, x0);
-  x1 = copysignf(__builtin_amdgcn_cvt_f32_fp8(p, 1) * s, x1);
+  c0 = __builtin_amdgcn_cvt_f32_fp8(p, 0);
+  c1 = __builtin_amdgcn_cvt_f32_fp8(p, 1);
+  x0 = copysignf(c0 * s, x0);
+  x1 = copysignf(c1 * s, x1);
+}
+
+__device__ __forceinline__ void qdq2(float& x0, float& x1, float s, float r) {
+  float c0, c1;
+  qdq2c(x0, x1, s, r, c0, c1);
 }
 
 __device__ __forceinline__ void qdq4(float4& v, float s, float r) {
@@ -61,6 +69,13 @@ __device__ __forceinline__ void qdq4(f32x4& v, float s, float r) {
   float a = v[0], b = v[1], c = v[2], d = v[3];
   qdq2(a, b, s, r);
   qdq2(c, d, s, r);
+  v = f32x4{a, b, c, d};
+}
+
+__device__ __forceinline__ void qdq4c(f32x4& v, float (&cv)[4], float s, float r) {
+  float a = v[0], b = v[1], c = v[2], d = v[3];
+  qdq2c(a, b, s, r, cv[0], cv[1]);
+  qdq2c(c, d, s, r, cv[2], cv[3]);
   v = f32x4{a, b, c, d};
 }
 

@@ -22,8 +22,12 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             const float* initial_state, void* o, float* final_state,
                             void* workspace, const gdn_debug_t* debug, hipStream_t stream);
 
+// One T record per (chunk, head): T = (I + A)^-1 diag(beta) in MFMA
+// A-fragment order (see gdn_prep.hip), 12 KiB for both engines.
+constexpr int kTRecBytes = 12288;
+
 // Bytes of the chunk workspace: chunk offsets [N + 1] (padded to 256 bytes)
-// and one 16 KiB T record per (chunk, head) for the worst-case chunk count
+// and one T record per (chunk, head) for the worst-case chunk count
 // ceil(total_tokens / 64) + N.
 size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens);
 

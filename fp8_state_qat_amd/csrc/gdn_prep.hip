@@ -7,16 +7,22 @@
 //     A[r][s] = beta_r exp(gamma_r - gamma_s) k_r . k_s       (s < r)
 //     T       = (I + A)^-1 diag(beta)                         (exact solve)
 // T is written to the workspace for the sequential kernel, which forms
-// W = T (exp(gamma) * K) and U = T V from it.
+// U' = T (V - exp(gamma) * K S^T) from it.
 //
 // The solve is blocked on 16 x 16 blocks in fp32: the four diagonal blocks
 // by forward substitution (one lane per column), then the off-diagonal
 // blocks level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
 //
 // Workspace layout: int32 chunk offsets [N + 1] (prefix sums of
-// ceil(P_n / 64)), padded to 256 bytes, then one 16 KiB record per (chunk,
-// head): bf16 inputs store T as hi = bf16(T) and lo = bf16(T - hi), two
-// [64][64] bf16 planes; fp32 inputs store T as [64][64] fp32.
+// ceil(P_n / 64)), padded to 256 bytes, then one 12 KiB record per (chunk,
+// head) holding the six nonzero 16 x 32 A-operand fragments of the block
+// lower-triangular T, pair p = (ti, kb) in (0,0) (1,0) (2,0) (3,0) (2,1)
+// (3,1): lane l of fragment p holds T[16 ti + l % 16][32 kb + kperm(l / 16, j)]
+// for j = 0..7 (kperm as in gdn_device.hpp), fragments stored one after the
+// other, lane-major.  bf16 inputs store hi = bf16(T) (six fragments) then
+// lo = bf16(T - hi) (six more); fp32 inputs store T in fp32.  The sequential
+// kernel copies the record into LDS unchanged and reads each fragment with
+// one lane-linear load.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -66,7 +72,7 @@ struct PrepArgs {
   const int32_t* seq_lens;
   const int32_t* prefix_lens;
   const int32_t* offs;
-  void* T;        // records of 16 KiB
+  void* T;        // one record of kTRecBytes per (chunk, head)
   int N;
   int H;
 };
@@ -243,28 +249,34 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
   }
 
   // ---- T = X diag(beta), zero above the block diagonal -> workspace record
-  {
-    const int r = tid >> 2, q16 = (tid & 3) * 16;
-    const bool below = (q16 >> 4) <= (r >> 4);
-    const int64_t rec = ((int64_t)j * H + h) * 4096;  // elements of 4 bytes
+  for (int slot = tid; slot < 6 * 64; slot += kThreads) {
+    const int p = slot >> 6, l = slot & 63, g4 = l >> 4;
+    const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+    const int r = 16 * ti + (l & 15);
+    float t8[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s0 = q16 + 4 * u;
+    for (int half = 0; half < 2; ++half) {
+      const int s0 = 32 * kb + 16 * half + 4 * g4;
       float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (below) x4 = *reinterpret_cast<const float4*>(sX + r * L64 + s0);
+      if ((s0 >> 4) <= ti) x4 = *reinterpret_cast<const float4*>(sX + r * L64 + s0);
       const float4 b4 = *reinterpret_cast<const float4*>(sBeta + s0);
-      const float t0v = x4.x * b4.x, t1v = x4.y * b4.y, t2v = x4.z * b4.z, t3v = x4.w * b4.w;
-      if constexpr (kBF) {
-        uint32_t h0, l0, h1, l1;
-        split_bf16x2(t0v, t1v, h0, l0);
-        split_bf16x2(t2v, t3v, h1, l1);
-        uint16_t* Th = reinterpret_cast<uint16_t*>(a.T) + rec * 2;  // 2 planes of 4096 bf16
-        *reinterpret_cast<uint2*>(Th + r * 64 + s0) = make_uint2(h0, h1);
-        *reinterpret_cast<uint2*>(Th + 4096 + r * 64 + s0) = make_uint2(l0, l1);
-      } else {
-        float* Tf = reinterpret_cast<float*>(a.T) + rec;
-        *reinterpret_cast<float4*>(Tf + r * 64 + s0) = make_float4(t0v, t1v, t2v, t3v);
-      }
+      t8[4 * half] = x4.x * b4.x;
+      t8[4 * half + 1] = x4.y * b4.y;
+      t8[4 * half + 2] = x4.z * b4.z;
+      t8[4 * half + 3] = x4.w * b4.w;
+    }
+    char* rec = reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes;
+    if constexpr (kBF) {
+      uint32_t hv[4], lv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], lv[q]);
+      uint4* dst = reinterpret_cast<uint4*>(rec);
+      dst[p * 64 + l] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      dst[(6 + p) * 64 + l] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+    } else {
+      float4* dst = reinterpret_cast<float4*>(rec) + 2 * (p * 64 + l);
+      dst[0] = make_float4(t8[0], t8[1], t8[2], t8[3]);
+      dst[1] = make_float4(t8[4], t8[5], t8[6], t8[7]);
     }
   }
 }
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
 size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens) {
   const int64_t max_chunks = (total_tokens + kChunk - 1) / kChunk + n_seqs;
   const size_t offs = ((size_t)(n_seqs + 1) * 4 + 255) / 256 * 256;
-  return offs + (size_t)max_chunks * n_heads * 16384;
+  return offs + (size_t)max_chunks * n_heads * kTRecBytes;
 }
 
 hipError_t launch_prep(const gdn_shape_t& s, const void* k, const float* beta, const float* g,

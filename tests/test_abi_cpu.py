@@ -89,7 +89,7 @@ def test_workspace_size_and_checks():
     head plus the chunk offsets; too small, NULL or misaligned is rejected."""
     s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
     n = _ws(s)
-    assert n == 256 + (3 + 3) * 2 * 16384
+    assert n == 256 + (3 + 3) * 2 * 12288
     assert _ws(_shape(dv=96)) == 0 and _lib.last_error()
     assert _chunk(s, ws_bytes=n - 1) == 1
     assert _chunk(s, ws=0) == 1
