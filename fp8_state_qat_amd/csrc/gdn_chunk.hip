@@ -68,7 +68,7 @@ __device__ __forceinline__ void lds_load4(const void* src, void* dst) {
 }
 // Wait until this wave's outstanding vector memory operations (including
 // direct LDS loads) have completed.
-__device__ __forceinline__ void wait_vmem() { wait_vmem(); }
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // bf16 engine: LDS operands are bf16 bit patterns, fragments 8 x bf16.
@@ -159,13 +159,29 @@ struct EngF32 {
   }
 };
 
-// LDS layout of the sequential kernel (bytes).  F = one fragment dump.
-//   K   [64][DK + 16 bytes]  the chunk's k rows, row-major, rows padded by 16
-//                  bytes, filled by direct global->LDS loads; A of K S^T, A of P
-//   Q   2 x [64][DK + 16 bytes]  the same for q, double-buffered by chunk
-//                  parity; B of P, B of S Q^T
-//   KT  [dt][kb]   dump: A of the state update (row = key)     2 NT fragments
-//   V   [64][64 + 16 bytes]  the tile's v rows
+// Key-channel order of the state.  The chain waves hold S^T in accumulator
+// tiles whose rows are "state rows" sr = 16 t + 4 (l/16) + i; state row sr
+// carries key channel
+//     dkmap(sr) = 32 (sr / 32) + 8 ((sr % 16) / 4) + 4 ((sr / 16) % 2) + sr % 4.
+// With this relabelling the eight k-slots kperm(gq, 0..7) of k-block kb,
+// state rows 32 kb + kperm(gq, j), are the key channels 32 kb + 8 gq + j: a K
+// or Q fragment lane holds 8 consecutive channels of one row, 16 contiguous
+// bytes of the input, so the fragment dumps below are filled by direct
+// 16-byte global->LDS loads.  Contractions over the key axis (K S^T, S Q^T,
+// Q K^T) only need both operands in the same order; the relabelling is undone
+// where the state meets memory.
+__host__ __device__ constexpr int dkmap(int sr) {
+  return 32 * (sr / 32) + 8 * ((sr % 16) / 4) + 4 * ((sr / 16) % 2) + sr % 4;
+}
+
+// LDS layout of the sequential kernel (bytes).  F = one fragment dump (64
+// lanes x 8 elements, lane-major).
+//   K   [tt][kb]   dump: lane l holds k[16tt + l%16][32kb + 8(l/16) .. +7];
+//                  A of K S^T, A of P                          4 NKB fragments
+//   Q   2 x [tt][kb]  the same for q, double-buffered by chunk parity; B of
+//                  P, B of S Q^T
+//   KT  [dt][kb]   dump: A of the state update (row = state row) 2 NT
+//   V   [64][64 + 16 bytes]  the tile's v rows, row-major, padded rows
 //   T   [plane][p] 6 fragments per plane (the prep kernel's record, copied as is)
 //   P   [plane][p] 6 fragments per plane, same pairs as T
 //   XU  [c][plane*2 + kb]     U' as the A operand of U'^T P^T, per chain wave
@@ -178,11 +194,10 @@ struct Lds {
   using E = typename Eng::E;
   static constexpr int NKB = DK / 32, NT = DK / 16, NP = Eng::kPlanes;
   static constexpr size_t F = 64 * 8 * sizeof(E);
-  static constexpr size_t RK = DK * sizeof(E) + 16;  // padded q/k row (bytes)
   static constexpr size_t RV = 64 * sizeof(E) + 16;  // padded v row (bytes)
   static constexpr size_t oK = 0;
-  static constexpr size_t oQ = oK + 64 * RK;
-  static constexpr size_t oKT = oQ + 2 * 64 * RK;
+  static constexpr size_t oQ = oK + 4 * NKB * F;
+  static constexpr size_t oKT = oQ + 2 * 4 * NKB * F;
   static constexpr size_t oV = oKT + 2 * NT * F;
   static constexpr size_t oT = oV + 64 * RV;
   static constexpr size_t oP = oT + 6 * NP * F;
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   const int bound0 = args.bound_offsets ? args.bound_offsets[n] : 0;
   const int chunk0 = args.chunk_offs[n];
 
-  // ---- chain-wave state: st[t][i] = S^T[16t + 4gq + i][vcol0] = S[vcol0][16t + 4gq + i]
+  // ---- chain-wave state: st[t][i] = S[vcol0][dkmap(16t + 4gq + i)]
   f32x4 st[NT];
   Fr sh[NKB];            // after a chunk QDQ: the codes as the MFMA operand (bf16 engine)
   float s_cur = 1.0f;    // scale of the coded state
@@ -322,28 +337,28 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     }
   };
 
-  // ---- raw row buffers: rows of 16-byte pieces padded by one piece, so the
-  // 16 rows one fragment load touches fall in different banks
-  constexpr int EPP = 16 / (int)sizeof(E);  // elements per piece
-  constexpr int PPR = DK / EPP;             // pieces per q/k row
+  constexpr int EPP = 16 / (int)sizeof(E);  // elements per 16-byte piece
   constexpr int PPV = kTileRows / EPP;      // pieces per v row
-  constexpr int RSK = (PPR + 1) * EPP;      // q/k row stride (elements)
-  constexpr int RSV = (PPV + 1) * EPP;      // v row stride (elements)
+  constexpr int RSV = (PPV + 1) * EPP;      // padded v row stride (elements)
   static_assert(sizeof(TIO) == sizeof(E), "LDS element type is the input type");
-  // A/B fragment of row r (k-block kb) from a raw q/k buffer
-  auto rowfrag = [&](const E* base, int r, int kb) {
-    const E* p = base + r * RSK + 32 * kb + 4 * gq;
-    return Eng::ld2(p, p + 16);
-  };
 
-  // Helper waves: direct global -> LDS loads of chunk cc (k, q, v rows, the T
-  // record, the log-gates).  One instruction writes 64 consecutive 16-byte LDS
-  // pieces, i.e. whole padded rows (the pad piece gets a copy of the row's last
-  // piece).  Rows past the chunk's valid count load its last valid row: they
-  // meet zero rows and columns of T, or outputs that are not stored, so they
-  // need no zeroing.
-  auto load_rows = [&](const TIO* src, int64_t stride, E* dst, int ppr, int nv) {
-    const int rpi = 64 / (ppr + 1);                 // rows per instruction
+  // Helper waves: direct global -> LDS loads of chunk cc (k and q dumps, v
+  // rows, the T record, the log-gates).  One instruction writes 64
+  // consecutive 16-byte LDS pieces.  Rows past the chunk's valid count load
+  // its last valid row: they meet zero rows and columns of T, or outputs that
+  // are not stored, so they need no zeroing.
+  auto load_dump = [&](const TIO* src, E* dst, int nv) {  // src: the chunk's row 0, the head's column 0
+    constexpr int UPS = (int)sizeof(E) / 2;              // 16-byte pieces per lane slot
+    for (int i = hw; i < 4 * NKB * UPS; i += 4) {
+      const int u = i * 64 + lane, sl = u / UPS, part = u % UPS;
+      const int f = sl >> 6, l2 = sl & 63;
+      const int r = 16 * (f / NKB) + (l2 & 15);
+      const int d = 32 * (f % NKB) + 8 * (l2 >> 4) + part * EPP;
+      lds_load16(src + (int64_t)min(r, nv - 1) * qk_row + d, reinterpret_cast<char*>(dst) + i * 1024);
+    }
+  };
+  auto load_rows = [&](const TIO* src, int64_t stride, E* dst, int ppr, int nv) {  // padded rows
+    const int rpi = 64 / (ppr + 1);  // rows per instruction
     const int rr = lane / (ppr + 1), pc = lane % (ppr + 1);
     const int64_t lane_off = (int64_t)min(pc, ppr - 1) * EPP;
     for (int i = hw; i * rpi < 64; i += 4) {
@@ -355,8 +370,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   auto issue = [&](int cc) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
-    load_rows(gk_ + row0 * qk_row + (int64_t)h * DK, qk_row, sK, PPR, nv);
-    load_rows(gq_ + row0 * qk_row + (int64_t)h * DK, qk_row, sQ + (cc & 1) * (64 * RSK), PPR, nv);
+    load_dump(gk_ + row0 * qk_row + (int64_t)h * DK, sK, nv);
+    load_dump(gq_ + row0 * qk_row + (int64_t)h * DK, sQ + (cc & 1) * (64 * DK), nv);
     load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, v_row, sV, PPV, nv);
     const char* rec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
 #pragma unroll
@@ -367,18 +382,20 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     if (hw == 0) lds_load4(args.g + (row0 + min(lane, nv - 1)) * H + h, sG);
   };
   // Helper waves, after every helper's loads have landed: the K^T dump
-  // (fragment f = 2 dt + kb, lane l holds K[32 kb + kperm(l/16, j)][16 dt + l%16])
+  // (fragment f = 2 dt + kb, lane l holds k[32 kb + kperm(l/16, j)][dkmap(16 dt + l%16)])
   // and the gate scan.
   auto transform = [&](int cc) {
     const int nv = min(kChunk, P - cc * kChunk);
 #pragma unroll
     for (int m = 0; m < NT / 2; ++m) {
       const int f = hw + 4 * m, dt = f >> 1, kb = f & 1;
+      const int d = dkmap(16 * dt + ln);  // key channel of this lane's state row
+      const E* col = sK + (((d >> 5) * 64 + ((d & 31) >> 3) * 16) * 8 + (d & 7));
       E x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int r = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
-        x[j] = sK[r * RSK + 16 * dt + ln];
+        const int t = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
+        x[j] = col[((t >> 4) * NKB * 64 + (t & 15)) * 8];
       }
       Eng::st(slot(sKT, f), Eng::pack8(x));
     }
@@ -402,7 +419,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     if (args.init != nullptr) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float4 x = *reinterpret_cast<const float4*>(args.init + state_base + 16 * t + 4 * gq);
+        const float4 x = *reinterpret_cast<const float4*>(args.init + state_base + dkmap(16 * t + 4 * gq));
         st[t] = f32x4{x.x, x.y, x.z, x.w};
       }
     } else {
@@ -430,7 +447,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const bool two = kSplit && !coded_in;  // state operand as hi + lo
     const bool last = (c == n_chunks - 1);
     const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
-    const E* sQc = sQ + (c & 1) * (64 * (DK + 16 / (int)sizeof(E)));  // this chunk's q rows
+    E* sQc = sQ + (c & 1) * (64 * DK);  // this chunk's q dump
 
     // ======== phase 1a ========
     if (chain) {
@@ -446,7 +463,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            const Fr a = rowfrag(sK, 16 * tt + ln, kb);
+            const Fr a = Eng::ld(slot(sK, tt * NKB + kb));
             Eng::mma(acc[tt], a, hi[kb]);
             Eng::mma(acc[tt], a, lo[kb]);
           }
@@ -454,7 +471,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], rowfrag(sK, 16 * tt + ln, kb), sh[kb]);
+          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], Eng::ld(slot(sK, tt * NKB + kb)), sh[kb]);
       }
       // X[t][v] = V[t][v] - s exp(gamma_t) (K S^T)[t][v], t = 16tt + 4gq + i
       Fr xh[2], xl[2];
@@ -519,7 +536,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            Eng::mma(acc, rowfrag(sK, 16 * si + ln, kb), rowfrag(sQc, 16 * ti + ln, kb));
+            Eng::mma(acc, Eng::ld(slot(sK, si * NKB + kb)), Eng::ld(slot(sQc, ti * NKB + kb)));
           const int t = 16 * ti + ln;
           const float g2t = sG2[t];
           const float4 g2s = *reinterpret_cast<const float4*>(sG2 + 16 * si + 4 * gq);
@@ -569,7 +586,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           *reinterpret_cast<float4*>(args.bound_pre + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
-                                     16 * t + 4 * gq) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+                                     dkmap(16 * t + 4 * gq)) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
       }
       if (do_qdq) {
         float amax = 0.f;
@@ -595,7 +612,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if (two) sb = Eng::ld(slot(sXS, c4 * NP * NKB + NKB + kb));
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-          const Fr bq = rowfrag(sQc, 16 * ti + ln, kb);
+          const Fr bq = Eng::ld(slot(sQc, ti * NKB + kb));
           Eng::mma(oacc[ti], sa, bq);
           if (two) Eng::mma(oacc[ti], sb, bq);
         }
@@ -679,7 +696,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
-                                     16 * t + 4 * gq) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+                                     dkmap(16 * t + 4 * gq)) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
       }
       if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
     } else if (c + 1 < n_chunks) {
@@ -718,7 +735,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             st[t2][i] *= a;
-            y += st[t2][i] * sk[16 * t2 + 4 * gq + i];
+            y += st[t2][i] * sk[dkmap(16 * t2 + 4 * gq + i)];
           }
         y += __shfl_xor(y, 16, 64);
         y += __shfl_xor(y, 32, 64);
@@ -728,8 +745,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int t2 = 0; t2 < NT; ++t2)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            st[t2][i] += u * sk[16 * t2 + 4 * gq + i];
-            z += st[t2][i] * sq[16 * t2 + 4 * gq + i];
+            st[t2][i] += u * sk[dkmap(16 * t2 + 4 * gq + i)];
+            z += st[t2][i] * sq[dkmap(16 * t2 + 4 * gq + i)];
           }
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
@@ -758,7 +775,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   if (chain) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<float4*>(args.fin + state_base + 16 * t + 4 * gq) =
+      *reinterpret_cast<float4*>(args.fin + state_base + dkmap(16 * t + 4 * gq)) =
           make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
   }
   for (int r = L + w; r < seg1 - seg0; r += kChunkWaves)
