@@ -70,13 +70,29 @@ __device__ __forceinline__ void lds_load4(const void* src, void* dst) {
 // direct LDS loads) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// gfx950 LDS transpose read of 16-bit data: inside each group of 16 lanes,
+// lane i receives, in its slot k (k = 0..3), element i % 4 of the 8 bytes
+// addressed by lane 4k + i / 4 of the same group.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) char*)p));
+  return __builtin_bit_cast(uint2, r);
+}
+// Slot of lane l inside a k/q fragment dump: each block of 16 lanes is
+// rotated by 4 per block so that the transpose reads of the state update hit
+// different banks.
+__device__ __forceinline__ int rot_slot(int l) { return (l & 48) | ((l + ((l >> 4) << 2)) & 15); }
+__device__ __forceinline__ int rot_lane(int p) { return (p & 48) | ((p - ((p >> 4) << 2)) & 15); }
 
 // bf16 engine: LDS operands are bf16 bit patterns, fragments 8 x bf16.
 struct EngBF16 {
   using E = uint16_t;
   using Fr = bf16x8;
   static constexpr bool kSplit = true;
-  static constexpr int kPlanes = 2;  // hi and lo planes of split operands
+  static constexpr int kPlanes = 2;     // hi and lo planes of split operands
+  static constexpr bool kTrRead = true; // K^T fragments by LDS transpose reads
   static __device__ __forceinline__ Fr ld(const E* p) { return *reinterpret_cast<const Fr*>(p); }
   static __device__ __forceinline__ void st(E* p, const Fr& f) { *reinterpret_cast<Fr*>(p) = f; }
   static __device__ __forceinline__ void mma(f32x4& c, const Fr& a, const Fr& b) { mma_bf16(c, a, b); }
@@ -120,6 +136,7 @@ struct EngF32 {
   using Fr = Frag8;
   static constexpr bool kSplit = false;
   static constexpr int kPlanes = 1;
+  static constexpr bool kTrRead = false; // K^T fragments from a gathered dump
   static __device__ __forceinline__ Fr ld(const E* p) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
     const float4 b = reinterpret_cast<const float4*>(p)[1];
@@ -176,11 +193,13 @@ __host__ __device__ constexpr int dkmap(int sr) {
 
 // LDS layout of the sequential kernel (bytes).  F = one fragment dump (64
 // lanes x 8 elements, lane-major).
-//   K   [tt][kb]   dump: lane l holds k[16tt + l%16][32kb + 8(l/16) .. +7];
-//                  A of K S^T, A of P                          4 NKB fragments
+//   K   [tt][kb]   dump: lane l holds k[16tt + l%16][32kb + 8(l/16) .. +7]
+//                  in slot rot_slot(l); A of K S^T, A of P     4 NKB fragments
 //   Q   2 x [tt][kb]  the same for q, double-buffered by chunk parity; B of
 //                  P, B of S Q^T
-//   KT  [dt][kb]   dump: A of the state update (row = state row) 2 NT
+//   KT  [dt][kb]   dump: A of the state update (row = state row), 2 NT
+//                  fragments (fp32 engine; the bf16 engine reads these
+//                  fragments from K with transpose reads)
 //   V   [64][64 + 16 bytes]  the tile's v rows, row-major, padded rows
 //   T   [plane][p] 6 fragments per plane (the prep kernel's record, copied as is)
 //   P   [plane][p] 6 fragments per plane, same pairs as T
@@ -198,7 +217,7 @@ struct Lds {
   static constexpr size_t oK = 0;
   static constexpr size_t oQ = oK + 4 * NKB * F;
   static constexpr size_t oKT = oQ + 2 * 4 * NKB * F;
-  static constexpr size_t oV = oKT + 2 * NT * F;
+  static constexpr size_t oV = oKT + (Eng::kTrRead ? 0 : 2 * NT * F);
   static constexpr size_t oT = oV + 64 * RV;
   static constexpr size_t oP = oT + 6 * NP * F;
   static constexpr size_t oXU = oP + 6 * NP * F;
@@ -270,6 +289,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   const int hw = uniform(w) - 4;    // helper wave index (waves 4..7)
   // fragment f of an LDS dump, this lane's slot
   auto slot = [lane](E* base, int f) { return base + (f * 64 + lane) * 8; };
+  const int qs = rot_slot(lane);
+  auto qslot = [qs](E* base, int f) { return base + (f * 64 + qs) * 8; };  // k/q dumps
+  // element offset of k[t][d] in a k/q dump
+  auto kpos = [](int t, int d) {
+    return (((t >> 4) * (DK / 32) + (d >> 5)) * 64 + rot_slot(((d & 31) >> 3) * 16 + (t & 15))) * 8 + (d & 7);
+  };
 
   const int H = args.H, dv = args.dv;
   const int tiles = dv / kTileRows;
@@ -342,62 +367,67 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   constexpr int RSV = (PPV + 1) * EPP;      // padded v row stride (elements)
   static_assert(sizeof(TIO) == sizeof(E), "LDS element type is the input type");
 
-  // Helper waves: direct global -> LDS loads of chunk cc (k and q dumps, v
-  // rows, the T record, the log-gates).  One instruction writes 64
+  // Direct global -> LDS loads of chunk cc (k and q dumps, v rows, the T
+  // record, the log-gates).  One instruction writes 64
   // consecutive 16-byte LDS pieces.  Rows past the chunk's valid count load
   // its last valid row: they meet zero rows and columns of T, or outputs that
   // are not stored, so they need no zeroing.
-  auto load_dump = [&](const TIO* src, E* dst, int nv) {  // src: the chunk's row 0, the head's column 0
-    constexpr int UPS = (int)sizeof(E) / 2;              // 16-byte pieces per lane slot
-    for (int i = hw; i < 4 * NKB * UPS; i += 4) {
+  auto load_dump = [&](const TIO* src, E* dst, int nv, int wi) {  // src: the chunk's row 0, the head's column 0
+    constexpr int UPS = (int)sizeof(E) / 2;                      // 16-byte pieces per lane slot
+    for (int i = wi; i < 4 * NKB * UPS; i += 4) {
       const int u = i * 64 + lane, sl = u / UPS, part = u % UPS;
-      const int f = sl >> 6, l2 = sl & 63;
+      const int f = sl >> 6, l2 = rot_lane(sl & 63);
       const int r = 16 * (f / NKB) + (l2 & 15);
       const int d = 32 * (f % NKB) + 8 * (l2 >> 4) + part * EPP;
       lds_load16(src + (int64_t)min(r, nv - 1) * qk_row + d, reinterpret_cast<char*>(dst) + i * 1024);
     }
   };
-  auto load_rows = [&](const TIO* src, int64_t stride, E* dst, int ppr, int nv) {  // padded rows
+  auto load_rows = [&](const TIO* src, int64_t stride, E* dst, int ppr, int nv, int wi) {  // padded rows
     const int rpi = 64 / (ppr + 1);  // rows per instruction
     const int rr = lane / (ppr + 1), pc = lane % (ppr + 1);
     const int64_t lane_off = (int64_t)min(pc, ppr - 1) * EPP;
-    for (int i = hw; i * rpi < 64; i += 4) {
+    for (int i = wi; i * rpi < 64; i += 4) {
       const int r = i * rpi + rr;
       if (rr < rpi && r < 64)
         lds_load16(src + (int64_t)min(r, nv - 1) * stride + lane_off, dst + i * rpi * (ppr + 1) * EPP);
     }
   };
-  auto issue = [&](int cc) {
+  // Chain waves (after their phase-1b work) load k, v, T and the gates of
+  // chunk cc; helper waves load q.  wi / nw: this wave's index among the
+  // waves that share a buffer.
+  auto issue_kvtg = [&](int cc) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
-    load_dump(gk_ + row0 * qk_row + (int64_t)h * DK, sK, nv);
-    load_dump(gq_ + row0 * qk_row + (int64_t)h * DK, sQ + (cc & 1) * (64 * DK), nv);
-    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, v_row, sV, PPV, nv);
+    load_dump(gk_ + row0 * qk_row + (int64_t)h * DK, sK, nv, c4);
+    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, v_row, sV, PPV, nv, c4);
     const char* rec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
 #pragma unroll
     for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
-      const int idx = hw * (kTRecBytes / 1024 / 4) + ii;
+      const int idx = c4 * (kTRecBytes / 1024 / 4) + ii;
       lds_load16(rec + (idx * 64 + lane) * 16, reinterpret_cast<char*>(sT) + idx * 1024);
     }
-    if (hw == 0) lds_load4(args.g + (row0 + min(lane, nv - 1)) * H + h, sG);
+    if (c4 == 0) lds_load4(args.g + (row0 + min(lane, nv - 1)) * H + h, sG);
   };
-  // Helper waves, after every helper's loads have landed: the K^T dump
-  // (fragment f = 2 dt + kb, lane l holds k[32 kb + kperm(l/16, j)][dkmap(16 dt + l%16)])
-  // and the gate scan.
+  auto issue_q = [&](int cc) {
+    const int nv = min(kChunk, P - cc * kChunk);
+    const int64_t row0 = seg0 + cc * kChunk;
+    load_dump(gq_ + row0 * qk_row + (int64_t)h * DK, sQ + (cc & 1) * (64 * DK), nv, hw);
+  };
+  // Helper waves, after every wave's loads have landed: the gate scan and,
+  // for the fp32 engine, the K^T dump (fragment f = 2 dt + kb, lane l holds
+  // k[32 kb + kperm(l/16, j)][dkmap(16 dt + l%16)]).
   auto transform = [&](int cc) {
     const int nv = min(kChunk, P - cc * kChunk);
+    if constexpr (!Eng::kTrRead) {
 #pragma unroll
-    for (int m = 0; m < NT / 2; ++m) {
-      const int f = hw + 4 * m, dt = f >> 1, kb = f & 1;
-      const int d = dkmap(16 * dt + ln);  // key channel of this lane's state row
-      const E* col = sK + (((d >> 5) * 64 + ((d & 31) >> 3) * 16) * 8 + (d & 7));
-      E x[8];
+      for (int m = 0; m < NT / 2; ++m) {
+        const int f = hw + 4 * m, dt = f >> 1, kb = f & 1;
+        const int d = dkmap(16 * dt + ln);  // key channel of this lane's state row
+        E x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
-        x[j] = col[((t >> 4) * NKB * 64 + (t & 15)) * 8];
+        for (int j = 0; j < 8; ++j) x[j] = sK[kpos(32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4)), d)];
+        Eng::st(slot(sKT, f), Eng::pack8(x));
       }
-      Eng::st(slot(sKT, f), Eng::pack8(x));
     }
     if (hw == 0) {
       float x = (lane < nv) ? sG[lane] : 0.f;
@@ -431,8 +461,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     write_xs(hi, lo, true);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];
-  } else if (n_chunks > 0) {
-    issue(0);
+  }
+  if (n_chunks > 0) {
+    if (chain) issue_kvtg(0); else issue_q(0);
     wait_vmem();
   }
   __syncthreads();
@@ -463,7 +494,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            const Fr a = Eng::ld(slot(sK, tt * NKB + kb));
+            const Fr a = Eng::ld(qslot(sK, tt * NKB + kb));
             Eng::mma(acc[tt], a, hi[kb]);
             Eng::mma(acc[tt], a, lo[kb]);
           }
@@ -471,7 +502,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], Eng::ld(slot(sK, tt * NKB + kb)), sh[kb]);
+          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], Eng::ld(qslot(sK, tt * NKB + kb)), sh[kb]);
       }
       // X[t][v] = V[t][v] - s exp(gamma_t) (K S^T)[t][v], t = 16tt + 4gq + i
       Fr xh[2], xl[2];
@@ -536,7 +567,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            Eng::mma(acc, Eng::ld(slot(sK, si * NKB + kb)), Eng::ld(slot(sQc, ti * NKB + kb)));
+            Eng::mma(acc, Eng::ld(qslot(sK, si * NKB + kb)), Eng::ld(qslot(sQc, ti * NKB + kb)));
           const int t = 16 * ti + ln;
           const float g2t = sG2[t];
           const float4 g2s = *reinterpret_cast<const float4*>(sG2 + 16 * si + 4 * gq);
@@ -572,8 +603,19 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int i = 0; i < 4; ++i) st[t][i] *= aC;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const Fr a0 = Eng::ld(slot(sKT, 2 * t));
-        const Fr a1 = Eng::ld(slot(sKT, 2 * t + 1));
+        Fr a0, a1;
+        if constexpr (Eng::kTrRead) {
+          // lane (gq, l) of each 16-lane group points at k[32kb + 16h + 4gq + l/4][dkmap(16t + 4(l%4)) .. +3]
+          const int d = dkmap(16 * t + 4 * (ln & 3));
+          const int t0 = 4 * gq + (ln >> 2);
+          const uint2 x0 = lds_read_tr16(sK + kpos(t0, d)), x1 = lds_read_tr16(sK + kpos(t0 + 16, d));
+          const uint2 y0 = lds_read_tr16(sK + kpos(t0 + 32, d)), y1 = lds_read_tr16(sK + kpos(t0 + 48, d));
+          a0 = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
+          a1 = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
+        } else {
+          a0 = Eng::ld(slot(sKT, 2 * t));
+          a1 = Eng::ld(slot(sKT, 2 * t + 1));
+        }
         Eng::mma(st[t], a0, bh[0]);
         Eng::mma(st[t], a1, bh[1]);
         if constexpr (kSplit) {
@@ -594,12 +636,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t][i]));
-        amax = wave_max(amax);
+        amax = wave_max_dpp(amax);
         if (lane == 0) sRed[c4] = amax;
       }
+      // the next chunk's k, v, T and gates: their buffers were last read in phase 1a
+      if (c + 1 < n_chunks) issue_kvtg(c + 1);
+      wait_vmem();  // this wave's loads are in LDS before the barrier
     } else {
-      // the next chunk's loads fly while the output is formed
-      if (c + 1 < n_chunks) issue(c + 1);
+      // the next chunk's q (other buffer) flies while the output is formed
+      if (c + 1 < n_chunks) issue_q(c + 1);
       // O^T[v][t] = s exp(gamma_t) (S Q^T)[v][t] + (U'^T P^T)[v][t], v in block c4
       const float sc = coded_in ? sMisc[1] : 1.0f;
       f32x4 oacc[4];
@@ -612,7 +657,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if (two) sb = Eng::ld(slot(sXS, c4 * NP * NKB + NKB + kb));
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-          const Fr bq = Eng::ld(slot(sQc, ti * NKB + kb));
+          const Fr bq = Eng::ld(qslot(sQc, ti * NKB + kb));
           Eng::mma(oacc[ti], sa, bq);
           if (two) Eng::mma(oacc[ti], sb, bq);
         }
@@ -757,7 +802,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           for (int t2 = 0; t2 < NT; ++t2)
 #pragma unroll
             for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t2][i]));
-          amax = wave_max(amax);
+          amax = wave_max_dpp(amax);
           if (lane == 0) sRed[c4] = amax;
         }
       }

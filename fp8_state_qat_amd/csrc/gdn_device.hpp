@@ -88,6 +88,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max over the 64 lanes of a wave with DPP lane moves inside each row of 16
+// lanes (quad swaps, then half-row and row mirrors) and the four row results
+// read back as scalars.  Every lane returns the same value.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int m = __builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(m));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_max<0x141>(v);  // row_half_mirror
+  v = dpp_max<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Max over the 256 threads of a block; red must hold 4 floats of LDS.  All
 // threads return the same value.  Contains two barriers.
 __device__ __forceinline__ float block_max(float v, float* red) {
