@@ -58,17 +58,34 @@ struct Frag8 {
   float v[8];
 };
 
-// Direct global -> LDS copy: lane l of the wave writes the 16 (or 4) bytes at
-// src to dst + 16 l (4 l); dst must be the same in every lane.
+// Direct global -> LDS copy: lane l of the wave writes the 16 bytes at src to
+// dst + 16 l; dst must be the same in every lane.  Issued from inline
+// assembly so that the compiler does not hold later LDS accesses of the wave
+// behind it: the kernel orders these copies itself, with wait_vmem() before
+// the barrier that publishes them.  M0 (the LDS base of the copy) is restored.
 __device__ __forceinline__ void lds_load16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
 }
 // Wait until this wave's outstanding vector memory operations (including
 // direct LDS loads) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier that orders LDS accesses only: it does not wait for the
+// wave's direct LDS loads or global memory operations in flight.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 // gfx950 LDS transpose read of 16-bit data: inside each group of 16 lanes,
 // lane i receives, in its slot k (k = 0..3), element i % 4 of the 8 bytes
@@ -193,8 +210,9 @@ __host__ __device__ constexpr int dkmap(int sr) {
 
 // LDS layout of the sequential kernel (bytes).  F = one fragment dump (64
 // lanes x 8 elements, lane-major).
-//   K   [tt][kb]   dump: lane l holds k[16tt + l%16][32kb + 8(l/16) .. +7]
-//                  in slot rot_slot(l); A of K S^T, A of P     4 NKB fragments
+//   K   2 x [tt][kb]  dump, double-buffered by chunk parity: lane l holds
+//                  k[16tt + l%16][32kb + 8(l/16) .. +7] in slot rot_slot(l);
+//                  A of K S^T, A of P, K^T by transpose reads   4 NKB fragments
 //   Q   2 x [tt][kb]  the same for q, double-buffered by chunk parity; B of
 //                  P, B of S Q^T
 //   KT  [dt][kb]   dump: A of the state update (row = state row), 2 NT
@@ -205,7 +223,6 @@ __host__ __device__ constexpr int dkmap(int sr) {
 //   P   [plane][p] 6 fragments per plane, same pairs as T
 //   XU  [c][plane*2 + kb]     U' as the A operand of U'^T P^T, per chain wave
 //   XS  [c][plane*NKB + kb]   the state as the A operand of S Q^T, per chain wave
-//   G   [64]       the chunk's log-gates
 //   vec gamma*log2(e), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
 //   red the four chain waves' amax
 template <int DK, class Eng>
@@ -213,17 +230,16 @@ struct Lds {
   using E = typename Eng::E;
   static constexpr int NKB = DK / 32, NT = DK / 16, NP = Eng::kPlanes;
   static constexpr size_t F = 64 * 8 * sizeof(E);
-  static constexpr size_t RV = 64 * sizeof(E) + 16;  // padded v row (bytes)
-  static constexpr size_t oK = 0;
-  static constexpr size_t oQ = oK + 4 * NKB * F;
+  static constexpr size_t RV = 64 * sizeof(E) + 16;    // padded v row (bytes)
+  static constexpr size_t oK = 0;                      // 2 buffers by chunk parity
+  static constexpr size_t oQ = oK + 2 * 4 * NKB * F;   // 2 buffers by chunk parity
   static constexpr size_t oKT = oQ + 2 * 4 * NKB * F;
   static constexpr size_t oV = oKT + (Eng::kTrRead ? 0 : 2 * NT * F);
   static constexpr size_t oT = oV + 64 * RV;
   static constexpr size_t oP = oT + 6 * NP * F;
   static constexpr size_t oXU = oP + 6 * NP * F;
   static constexpr size_t oXS = oXU + 4 * 2 * NP * F;
-  static constexpr size_t oG = oXS + 4 * NKB * NP * F;
-  static constexpr size_t oVec = oG + 64 * sizeof(float);
+  static constexpr size_t oVec = oXS + 4 * NKB * NP * F;
   static constexpr size_t oRed = oVec + (3 * 64 + 8) * sizeof(float);
   static constexpr size_t bytes = oRed + 8 * sizeof(float);
   static_assert(6 * NP * F == kTRecBytes, "T record and its LDS copy differ");
@@ -272,11 +288,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   E* sP = reinterpret_cast<E*>(smem + Ls::oP);
   E* sXU = reinterpret_cast<E*>(smem + Ls::oXU);
   E* sXS = reinterpret_cast<E*>(smem + Ls::oXS);
-  float* sG = reinterpret_cast<float*>(smem + Ls::oG);      // raw log-gates of the staged chunk
   float* sG2 = reinterpret_cast<float*>(smem + Ls::oVec);  // gamma * log2(e)
-  float* sEg = sG2 + 64;                                    // exp(gamma)
-  float* sEgc = sEg + 64;                                   // exp(gamma_C - gamma)
-  float* sMisc = sEgc + 64;  // [0] exp(gamma_C) of the staged chunk, [1] scale of the state entering it
   float* sRed = reinterpret_cast<float*>(smem + Ls::oRed);
 
   const int tid = threadIdx.x;
@@ -351,13 +363,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     }
   };
   // the state fragments for the helper wave's S Q^T (lo only when split)
-  auto write_xs = [&](const Fr (&hi)[NKB], const Fr (&lo)[NKB], bool two) {
+  auto write_xs = [&](E* xsb, const Fr (&hi)[NKB], const Fr (&lo)[NKB], bool two) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) Eng::st(slot(sXS, c4 * NP * NKB + kb), hi[kb]);
+    for (int kb = 0; kb < NKB; ++kb) Eng::st(slot(xsb, c4 * NP * NKB + kb), hi[kb]);
     if constexpr (kSplit) {
       if (two) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) Eng::st(slot(sXS, c4 * NP * NKB + NKB + kb), lo[kb]);
+        for (int kb = 0; kb < NKB; ++kb) Eng::st(slot(xsb, c4 * NP * NKB + NKB + kb), lo[kb]);
       }
     }
   };
@@ -392,32 +404,50 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         lds_load16(src + (int64_t)min(r, nv - 1) * stride + lane_off, dst + i * rpi * (ppr + 1) * EPP);
     }
   };
-  // Chain waves (after their phase-1b work) load k, v, T and the gates of
-  // chunk cc; helper waves load q.  wi / nw: this wave's index among the
-  // waves that share a buffer.
-  auto issue_kvtg = [&](int cc) {
+  // Loads of chunk cc, by buffer lifetime: k and q have two buffers (chunk
+  // parity) and are issued one chunk ahead at the start of phase 1a; v and
+  // T (one buffer each) at the start of phase 1b, once phase 1a has read
+  // them.  Chain waves load k, v and T, helper waves q; helper wave 0 fetches
+  // the log-gates into a register.
+  auto issue_k = [&](int cc, E* kdst) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
-    load_dump(gk_ + row0 * qk_row + (int64_t)h * DK, sK, nv, c4);
-    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, v_row, sV, PPV, nv, c4);
+    load_dump(gk_ + row0 * qk_row + (int64_t)h * DK, kdst, nv, c4);
+  };
+  auto issue_v = [&](int cc, E* vdst, E* tdst) {
+    const int nv = min(kChunk, P - cc * kChunk);
+    const int64_t row0 = seg0 + cc * kChunk;
+    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, v_row, vdst, PPV, nv, c4);
     const char* rec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
 #pragma unroll
     for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
       const int idx = c4 * (kTRecBytes / 1024 / 4) + ii;
-      lds_load16(rec + (idx * 64 + lane) * 16, reinterpret_cast<char*>(sT) + idx * 1024);
+      lds_load16(rec + (idx * 64 + lane) * 16, reinterpret_cast<char*>(tdst) + idx * 1024);
     }
-    if (c4 == 0) lds_load4(args.g + (row0 + min(lane, nv - 1)) * H + h, sG);
   };
-  auto issue_q = [&](int cc) {
+  auto issue_q = [&](int cc, E* qdst) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
-    load_dump(gq_ + row0 * qk_row + (int64_t)h * DK, sQ + (cc & 1) * (64 * DK), nv, hw);
+    load_dump(gq_ + row0 * qk_row + (int64_t)h * DK, qdst, nv, hw);
   };
-  // Helper waves, after every wave's loads have landed: the gate scan and,
-  // for the fp32 engine, the K^T dump (fragment f = 2 dt + kb, lane l holds
-  // k[32 kb + kperm(l/16, j)][dkmap(16 dt + l%16)]).
-  auto transform = [&](int cc) {
+  float pg = 0.f;  // helper wave 0: log-gate of token `lane` of the next chunk
+  auto fetch_g = [&](int cc) {
     const int nv = min(kChunk, P - cc * kChunk);
+    pg = args.g[(int64_t)(seg0 + cc * kChunk + min(lane, nv - 1)) * H + h];
+  };
+  // Helper wave 0: gates of chunk cc from pg (tokens past its end count 0).
+  auto scan = [&](int cc, float* vecb) {
+    const int nv = min(kChunk, P - cc * kChunk);
+    const float x = wave_prefix_sum((lane < nv) ? pg : 0.f);
+    const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    vecb[lane] = x * kLog2e;
+    vecb[64 + lane] = __builtin_amdgcn_exp2f(x * kLog2e);
+    vecb[128 + lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
+    if (lane == 0) vecb[192] = __builtin_amdgcn_exp2f(gC * kLog2e);
+  };
+  // fp32 engine, helper waves, phase 1a: the K^T dump of the current chunk
+  // (fragment f = 2 dt + kb, lane l holds k[32 kb + kperm(l/16, j)][dkmap(16 dt + l%16)]).
+  auto transform = [&](const E* kd, E* ktd) {
     if constexpr (!Eng::kTrRead) {
 #pragma unroll
       for (int m = 0; m < NT / 2; ++m) {
@@ -425,22 +455,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         const int d = dkmap(16 * dt + ln);  // key channel of this lane's state row
         E x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = sK[kpos(32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4)), d)];
-        Eng::st(slot(sKT, f), Eng::pack8(x));
+        for (int j = 0; j < 8; ++j) x[j] = kd[kpos(32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4)), d)];
+        Eng::st(slot(ktd, f), Eng::pack8(x));
       }
-    }
-    if (hw == 0) {
-      float x = (lane < nv) ? sG[lane] : 0.f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-      }
-      const float gC = __shfl(x, 63, 64);
-      sG2[lane] = x * kLog2e;
-      sEg[lane] = __builtin_amdgcn_exp2f(x * kLog2e);
-      sEgc[lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
-      if (lane == 0) sMisc[0] = __builtin_amdgcn_exp2f(gC * kLog2e);
     }
   };
 
@@ -458,19 +475,34 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     }
     Fr hi[NKB], lo[NKB];
     state_frags(hi, lo);
-    write_xs(hi, lo, true);
+    write_xs(sXS, hi, lo, true);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];
   }
   if (n_chunks > 0) {
-    if (chain) issue_kvtg(0); else issue_q(0);
+    if (chain) {
+      issue_k(0, sK);
+      issue_v(0, sV, sT);
+    } else {
+      issue_q(0, sQ);
+      if (hw == 0) fetch_g(0);
+    }
     wait_vmem();
+    if (hw == 0) scan(0, sG2);
   }
-  __syncthreads();
-  if (!chain && n_chunks > 0) transform(0);
-  __syncthreads();
+  barrier_lds();
 
-  for (int c = 0; c < n_chunks; ++c) {
+  // One chunk.  Every LDS buffer it touches arrives as a __restrict__
+  // pointer, so the compiler can tell the buffers apart and does not hold LDS
+  // reads behind the direct loads in flight into other buffers.
+  auto step = [&](const int c, E* __restrict__ kc, E* __restrict__ kn, E* __restrict__ qc,
+                  E* __restrict__ qn, E* __restrict__ tb, E* __restrict__ vb, E* __restrict__ pb,
+                  E* __restrict__ xu, E* __restrict__ xs, E* __restrict__ kt, float* __restrict__ vec,
+                  float* __restrict__ red) {
+    float* gg2 = vec;         // gamma * log2(e)
+    float* geg = vec + 64;    // exp(gamma)
+    float* gegc = vec + 128;  // exp(gamma_C - gamma)
+    float* gmisc = vec + 192; // [0] exp(gamma_C), [1] scale of the state entering the chunk
     const int t0 = seg0 + c * kChunk;
     const int nv = min(kChunk, P - c * kChunk);  // valid tokens in this chunk
     // the state entering this chunk is code * s_cur (bf16 engine, after a chunk QDQ)
@@ -478,10 +510,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const bool two = kSplit && !coded_in;  // state operand as hi + lo
     const bool last = (c == n_chunks - 1);
     const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
-    E* sQc = sQ + (c & 1) * (64 * DK);  // this chunk's q dump
 
     // ======== phase 1a ========
     if (chain) {
+      if (c + 1 < n_chunks) issue_k(c + 1, kn);  // the other k buffer
       // K S^T: A = K rows (tokens), B = the state
       const float sc = coded_in ? s_cur : 1.0f;
       f32x4 acc[4];
@@ -494,7 +526,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            const Fr a = Eng::ld(qslot(sK, tt * NKB + kb));
+            const Fr a = Eng::ld(qslot(kc, tt * NKB + kb));
             Eng::mma(acc[tt], a, hi[kb]);
             Eng::mma(acc[tt], a, lo[kb]);
           }
@@ -502,7 +534,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], Eng::ld(qslot(sK, tt * NKB + kb)), sh[kb]);
+          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], Eng::ld(qslot(kc, tt * NKB + kb)), sh[kb]);
       }
       // X[t][v] = V[t][v] - s exp(gamma_t) (K S^T)[t][v], t = 16tt + 4gq + i
       Fr xh[2], xl[2];
@@ -512,10 +544,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int tt = 2 * kb + hh;
-          const float4 e4 = *reinterpret_cast<const float4*>(sEg + 16 * tt + 4 * gq);
+          const float4 e4 = *reinterpret_cast<const float4*>(geg + 16 * tt + 4 * gq);
           float vv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vv[i] = Eng::to_f(sV[(16 * tt + 4 * gq + i) * RSV + 16 * c4 + ln]);
+          for (int i = 0; i < 4; ++i) vv[i] = Eng::to_f(vb[(16 * tt + 4 * gq + i) * RSV + 16 * c4 + ln]);
           x8[4 * hh + 0] = fmaf(-sc * e4.x, acc[tt][0], vv[0]);
           x8[4 * hh + 1] = fmaf(-sc * e4.y, acc[tt][1], vv[1]);
           x8[4 * hh + 2] = fmaf(-sc * e4.z, acc[tt][2], vv[2]);
@@ -529,10 +561,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        const Fr tf = Eng::ld(slot(sT, p));
+        const Fr tf = Eng::ld(slot(tb, p));
         Eng::mma(uacc[ti], tf, xh[kb]);
         if constexpr (kSplit) {
-          const Fr tl = Eng::ld(slot(sT, 6 + p));
+          const Fr tl = Eng::ld(slot(tb, 6 + p));
           Eng::mma(uacc[ti], tf, xl[kb]);
           Eng::mma(uacc[ti], tl, xh[kb]);
         }
@@ -545,10 +577,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
                              uacc[2 * kb + 1][3]};
         Fr uh, ul;
         Eng::split(u8, uh, ul);
-        Eng::st(slot(sXU, c4 * 2 * NP + kb), uh);
-        if constexpr (kSplit) Eng::st(slot(sXU, c4 * 2 * NP + 2 + kb), ul);
+        Eng::st(slot(xu, c4 * 2 * NP + kb), uh);
+        if constexpr (kSplit) Eng::st(slot(xu, c4 * 2 * NP + 2 + kb), ul);
       }
     } else {
+      if (c + 1 < n_chunks) {
+        issue_q(c + 1, qn);  // the other q buffer
+        if (hw == 0) fetch_g(c + 1);
+      }
+      transform(kc, kt);
       // P tiles: C[s][t] = k_s . q_t -> P[t][s] (s <= t), 10 lower tiles + 2
       // zero tiles that complete the fragment pairs; 3 per helper wave
 #pragma unroll
@@ -567,36 +604,38 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            Eng::mma(acc, Eng::ld(qslot(sK, si * NKB + kb)), Eng::ld(qslot(sQc, ti * NKB + kb)));
+            Eng::mma(acc, Eng::ld(qslot(kc, si * NKB + kb)), Eng::ld(qslot(qc, ti * NKB + kb)));
           const int t = 16 * ti + ln;
-          const float g2t = sG2[t];
-          const float4 g2s = *reinterpret_cast<const float4*>(sG2 + 16 * si + 4 * gq);
+          const float g2t = gg2[t];
+          const float4 g2s = *reinterpret_cast<const float4*>(gg2 + 16 * si + 4 * gq);
           const float gs[4] = {g2s.x, g2s.y, g2s.z, g2s.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             x[i] = (16 * si + 4 * gq + i <= t) ? __builtin_amdgcn_exp2f(g2t - gs[i]) * acc[i] : 0.f;
         }
         const int pr = (si >= 2) ? ti + 2 : ti, jb = (si & 1) * 4;
-        Eng::st4_split(slot(sP, pr) + jb, slot(sP, 6 + pr) + jb, x);
+        Eng::st4_split(slot(pb, pr) + jb, slot(pb, 6 + pr) + jb, x);
       }
     }
-    __syncthreads();
+    barrier_lds();
 
     // ======== phase 1b ========
+    f32x4 oacc[4];  // helper waves: O^T of this chunk, phase 1b -> 2
     if (chain) {
+      if (c + 1 < n_chunks) issue_v(c + 1, vb, tb);  // v and T were last read in phase 1a
       // S^T <- exp(gamma_C) S^T + K^T (exp(gamma_C - gamma) * U')
       Fr bh[2], bl[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float4 e0 = *reinterpret_cast<const float4*>(sEgc + 32 * kb + 4 * gq);
-        const float4 e1 = *reinterpret_cast<const float4*>(sEgc + 32 * kb + 16 + 4 * gq);
+        const float4 e0 = *reinterpret_cast<const float4*>(gegc + 32 * kb + 4 * gq);
+        const float4 e1 = *reinterpret_cast<const float4*>(gegc + 32 * kb + 16 + 4 * gq);
         const float u8[8] = {e0.x * uacc[2 * kb][0], e0.y * uacc[2 * kb][1], e0.z * uacc[2 * kb][2],
                              e0.w * uacc[2 * kb][3], e1.x * uacc[2 * kb + 1][0],
                              e1.y * uacc[2 * kb + 1][1], e1.z * uacc[2 * kb + 1][2],
                              e1.w * uacc[2 * kb + 1][3]};
         Eng::split(u8, bh[kb], bl[kb]);
       }
-      const float aC = sMisc[0];
+      const float aC = gmisc[0];
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -608,13 +647,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           // lane (gq, l) of each 16-lane group points at k[32kb + 16h + 4gq + l/4][dkmap(16t + 4(l%4)) .. +3]
           const int d = dkmap(16 * t + 4 * (ln & 3));
           const int t0 = 4 * gq + (ln >> 2);
-          const uint2 x0 = lds_read_tr16(sK + kpos(t0, d)), x1 = lds_read_tr16(sK + kpos(t0 + 16, d));
-          const uint2 y0 = lds_read_tr16(sK + kpos(t0 + 32, d)), y1 = lds_read_tr16(sK + kpos(t0 + 48, d));
+          const uint2 x0 = lds_read_tr16(kc + kpos(t0, d)), x1 = lds_read_tr16(kc + kpos(t0 + 16, d));
+          const uint2 y0 = lds_read_tr16(kc + kpos(t0 + 32, d)), y1 = lds_read_tr16(kc + kpos(t0 + 48, d));
           a0 = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
           a1 = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
         } else {
-          a0 = Eng::ld(slot(sKT, 2 * t));
-          a1 = Eng::ld(slot(sKT, 2 * t + 1));
+          a0 = Eng::ld(slot(kt, 2 * t));
+          a1 = Eng::ld(slot(kt, 2 * t + 1));
         }
         Eng::mma(st[t], a0, bh[0]);
         Eng::mma(st[t], a1, bh[1]);
@@ -637,50 +676,91 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
           for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t][i]));
         amax = wave_max_dpp(amax);
-        if (lane == 0) sRed[c4] = amax;
+        if (lane == 0) red[c4] = amax;
       }
-      // the next chunk's k, v, T and gates: their buffers were last read in phase 1a
-      if (c + 1 < n_chunks) issue_kvtg(c + 1);
-      wait_vmem();  // this wave's loads are in LDS before the barrier
     } else {
-      // the next chunk's q (other buffer) flies while the output is formed
-      if (c + 1 < n_chunks) issue_q(c + 1);
-      // O^T[v][t] = s exp(gamma_t) (S Q^T)[v][t] + (U'^T P^T)[v][t], v in block c4
-      const float sc = coded_in ? sMisc[1] : 1.0f;
-      f32x4 oacc[4];
+      // O^T[v][t] = s exp(gamma_t) (S Q^T)[v][t] + (U'^T P^T)[v][t], v in block c4;
+      // the first term here, the second in phase 2
+      const float sc = coded_in ? gmisc[1] : 1.0f;
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const Fr sa = Eng::ld(slot(sXS, c4 * NP * NKB + kb));
+        const Fr sa = Eng::ld(slot(xs, c4 * NP * NKB + kb));
         Fr sb;
-        if (two) sb = Eng::ld(slot(sXS, c4 * NP * NKB + NKB + kb));
+        if (two) sb = Eng::ld(slot(xs, c4 * NP * NKB + NKB + kb));
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-          const Fr bq = Eng::ld(qslot(sQc, ti * NKB + kb));
+          const Fr bq = Eng::ld(qslot(qc, ti * NKB + kb));
           Eng::mma(oacc[ti], sa, bq);
           if (two) Eng::mma(oacc[ti], sb, bq);
         }
       }
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const float egt = sc * sEg[16 * ti + ln];
+        const float egt = sc * geg[16 * ti + ln];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[ti][i] *= egt;
       }
+    }
+    barrier_lds();
+
+    // ======== phase 2 ========
+    if (chain) {
+      float s_new = 1.0f;
+      if (do_qdq) {
+        const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        s_new = qdq_scale(amax);
+        const float r = 1.0f / s_new;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          float c0[4], c1[4];
+          qdq4c(st[2 * kb], c0, s_new, r);
+          qdq4c(st[2 * kb + 1], c1, s_new, r);
+          if constexpr (kSplit) {
+            const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
+          }
+        }
+        s_cur = s_new;
+      }
+      if (!last) {
+        if (kSplit && do_qdq) {
+          write_xs(xs, sh, sh, false);
+        } else {
+          Fr hi[NKB], lo[NKB];
+          state_frags(hi, lo);
+          write_xs(xs, hi, lo, true);
+          if constexpr (!kSplit) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];  // fp32 engine: the exact state
+          }
+        }
+        if (c4 == 0 && lane == 0) gmisc[1] = s_new;
+      }
+      const int bidx = bound0 + c;
+      if (args.bound_post) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
+                                     dkmap(16 * t + 4 * gq)) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+      }
+      if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
+      wait_vmem();  // this wave's loads are in LDS before the barrier
+    } else {
       Fr uh[2], ul[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        uh[kb] = Eng::ld(slot(sXU, c4 * 2 * NP + kb));
-        if constexpr (kSplit) ul[kb] = Eng::ld(slot(sXU, c4 * 2 * NP + 2 + kb));
+        uh[kb] = Eng::ld(slot(xu, c4 * 2 * NP + kb));
+        if constexpr (kSplit) ul[kb] = Eng::ld(slot(xu, c4 * 2 * NP + 2 + kb));
       }
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        const Fr ph = Eng::ld(slot(sP, p));
+        const Fr ph = Eng::ld(slot(pb, p));
         Eng::mma(oacc[ti], uh[kb], ph);
         if constexpr (kSplit) {
-          const Fr pl = Eng::ld(slot(sP, 6 + p));
+          const Fr pl = Eng::ld(slot(pb, 6 + p));
           Eng::mma(oacc[ti], ul[kb], ph);
           Eng::mma(oacc[ti], uh[kb], pl);
         }
@@ -699,55 +779,19 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           }
         }
       }
+      if (c + 1 < n_chunks && hw == 0) scan(c + 1, vec);  // gates of the next chunk
       wait_vmem();  // this wave's loads are in LDS before the barrier
     }
-    __syncthreads();
-
-    // ======== phase 2 ========
-    if (chain) {
-      float s_new = 1.0f;
-      if (do_qdq) {
-        const float amax = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
-        s_new = qdq_scale(amax);
-        const float r = 1.0f / s_new;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          float c0[4], c1[4];
-          qdq4c(st[2 * kb], c0, s_new, r);
-          qdq4c(st[2 * kb + 1], c1, s_new, r);
-          if constexpr (kSplit) {
-            const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-            sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
-          }
-        }
-        s_cur = s_new;
-      }
-      if (!last) {
-        if (kSplit && do_qdq) {
-          write_xs(sh, sh, false);
-        } else {
-          Fr hi[NKB], lo[NKB];
-          state_frags(hi, lo);
-          write_xs(hi, lo, true);
-          if constexpr (!kSplit) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];  // fp32 engine: the exact state
-          }
-        }
-        if (c4 == 0 && lane == 0) sMisc[1] = s_new;
-      }
-      const int bidx = bound0 + c;
-      if (args.bound_post) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
-                                     dkmap(16 * t + 4 * gq)) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
-      }
-      if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
-    } else if (c + 1 < n_chunks) {
-      transform(c + 1);
-    }
-    __syncthreads();
+    barrier_lds();
+  };
+  for (int c = 0; c < n_chunks; ++c) {
+    const bool odd = c & 1;
+    E* k0 = sK;
+    E* k1 = sK + 64 * DK;
+    E* q0 = sQ;
+    E* q1 = sQ + 64 * DK;
+    step(c, odd ? k1 : k0, odd ? k0 : k1, odd ? q1 : q0, odd ? q0 : q1, sT, sV, sP, sXU, sXS,
+         Eng::kTrRead ? nullptr : sKT, sG2, sRed);
   }
 
   // ---------------- recurrent suffix, tokens P < t <= L ----------------

@@ -108,6 +108,24 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each
+// row of 16 lanes with DPP row shifts, then the running row totals carried
+// into the later rows with the row broadcasts.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int m = __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false);
+  return v + __int_as_float(m);
+}
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Max over the 256 threads of a block; red must hold 4 floats of LDS.  All
 // threads return the same value.  Contains two barriers.
 __device__ __forceinline__ float block_max(float v, float* red) {
