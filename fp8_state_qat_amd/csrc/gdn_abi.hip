@@ -62,6 +62,9 @@ gdn_status_t check_shape(const gdn_shape_t* s, bool decode) {
     return fail(GDN_ERR_INVALID_ARG, "unknown qdq_flags bits 0x%x", s->qdq_flags);
   const int64_t blocks = (int64_t)s->n_seqs * s->n_heads * (s->dv / 64);
   if (blocks >= (int64_t)1 << 31) return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, head, tile) units");
+  // the chunk kernel addresses one 64-token chunk of a head with 32-bit byte offsets
+  if ((int64_t)64 * s->n_heads * (s->dk > s->dv ? s->dk : s->dv) * 4 >= (int64_t)1 << 31)
+    return fail(GDN_ERR_UNSUPPORTED, "n_heads too large (64 * n_heads * max(dk, dv) * 4 bytes must be < 2^31)");
   if (decode && s->total_tokens != s->n_seqs)
     return fail(GDN_ERR_INVALID_ARG, "decode: total_tokens must equal n_seqs");
   return GDN_OK;

@@ -58,22 +58,27 @@ struct Frag8 {
   float v[8];
 };
 
-// Direct global -> LDS copy: lane l of the wave writes the 16 bytes at src to
+// Direct global -> LDS copy: lane l of the wave writes the 16 bytes at
+// base + off (base the same in every lane, off this lane's byte offset) to
 // dst + 16 l; dst must be the same in every lane.  Issued from inline
 // assembly so that the compiler does not hold later LDS accesses of the wave
 // behind it: the kernel orders these copies itself, with wait_vmem() before
 // the barrier that publishes them.  M0 (the LDS base of the copy) is restored.
-__device__ __forceinline__ void lds_load16(const void* src, void* dst) {
+__device__ __forceinline__ void lds_load16(const void* base, uint32_t off, void* dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+  // readfirstlane returns int: widen each half through uint32_t (no sign extension)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds)
+      : "v"(off), "s"(sb), "s"(lds)
       : "memory");
 }
 // Wait until this wave's outstanding vector memory operations (including
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   const int gq = lane >> 4;      // lane group (k-slots / accumulator rows 4gq..4gq+3)
   const int ln = lane & 15;      // accumulator column / fragment row
   const bool chain = w < 4;
-  const int c4 = w & 3;          // value block (16 columns) this wave serves
+  const int c4 = uniform(w) & 3; // value block (16 columns) this wave serves
   const int hw = uniform(w) - 4;    // helper wave index (waves 4..7)
   // fragment f of an LDS dump, this lane's slot
   auto slot = [lane](E* base, int f) { return base + (f * 64 + lane) * 8; };
@@ -386,22 +391,31 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   // are not stored, so they need no zeroing.
   auto load_dump = [&](const TIO* src, E* dst, int nv, int wi) {  // src: the chunk's row 0, the head's column 0
     constexpr int UPS = (int)sizeof(E) / 2;                      // 16-byte pieces per lane slot
-    for (int i = wi; i < 4 * NKB * UPS; i += 4) {
+    constexpr int NI = 4 * NKB * UPS;                            // instructions (multiple of 4)
+    static_assert(NI % 4 == 0, "dump load geometry");
+#pragma unroll
+    for (int ii = 0; ii < NI / 4; ++ii) {
+      const int i = wi + 4 * ii;
       const int u = i * 64 + lane, sl = u / UPS, part = u % UPS;
       const int f = sl >> 6, l2 = rot_lane(sl & 63);
       const int r = 16 * (f / NKB) + (l2 & 15);
       const int d = 32 * (f % NKB) + 8 * (l2 >> 4) + part * EPP;
-      lds_load16(src + (int64_t)min(r, nv - 1) * qk_row + d, reinterpret_cast<char*>(dst) + i * 1024);
+      lds_load16(src, (uint32_t)((min(r, nv - 1) * (int)qk_row + d) * (int)sizeof(E)),
+                 reinterpret_cast<char*>(dst) + i * 1024);
     }
   };
-  auto load_rows = [&](const TIO* src, int64_t stride, E* dst, int ppr, int nv, int wi) {  // padded rows
-    const int rpi = 64 / (ppr + 1);  // rows per instruction
-    const int rr = lane / (ppr + 1), pc = lane % (ppr + 1);
-    const int64_t lane_off = (int64_t)min(pc, ppr - 1) * EPP;
-    for (int i = wi; i * rpi < 64; i += 4) {
-      const int r = i * rpi + rr;
-      if (rr < rpi && r < 64)
-        lds_load16(src + (int64_t)min(r, nv - 1) * stride + lane_off, dst + i * rpi * (ppr + 1) * EPP);
+  auto load_rows = [&](const TIO* src, int stride, E* dst, int nv, int wi) {  // padded v rows
+    constexpr int RPI = 64 / (PPV + 1);           // rows per instruction
+    constexpr int NI = (64 + RPI - 1) / RPI;      // instructions
+    const int rr = lane / (PPV + 1), pc = lane % (PPV + 1);
+    const int lane_off = min(pc, PPV - 1) * EPP;
+#pragma unroll
+    for (int ii = 0; ii < (NI + 3) / 4; ++ii) {
+      const int i = wi + 4 * ii;
+      const int r = i * RPI + rr;
+      if (i < NI && rr < RPI && r < 64)
+        lds_load16(src, (uint32_t)((min(r, nv - 1) * stride + lane_off) * (int)sizeof(E)),
+                   dst + i * RPI * (PPV + 1) * EPP);
     }
   };
   // Loads of chunk cc, by buffer lifetime: k and q have two buffers (chunk
@@ -417,12 +431,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   auto issue_v = [&](int cc, E* vdst, E* tdst) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
-    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, v_row, vdst, PPV, nv, c4);
+    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, (int)v_row, vdst, nv, c4);
     const char* rec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
 #pragma unroll
     for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
       const int idx = c4 * (kTRecBytes / 1024 / 4) + ii;
-      lds_load16(rec + (idx * 64 + lane) * 16, reinterpret_cast<char*>(tdst) + idx * 1024);
+      lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), reinterpret_cast<char*>(tdst) + idx * 1024);
     }
   };
   auto issue_q = [&](int cc, E* qdst) {
