@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+T_RECORD_BYTES = 12288         # per (chunk, head): T = (I + A)^-1 diag(beta), hi + lo bf16 planes
 BF16_MFMA_PEAK_TFLOPS = 2516.6 # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "GDN chunked-prefill tokens/s + MFMA %peak; decode step HBM GB/s, 1×MI355X"
 
@@ -58,8 +59,8 @@ def prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes, gate_floats=1):
 
 def state_kernel_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes, o_bytes):
     """Algorithmic HBM bytes of the sequential state kernel: the prefill bytes
-    plus one read of the per-chunk solve (16 KiB per chunk and head)."""
-    return prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes) + n_chunk_heads * 16384
+    plus one read of the per-chunk solve (12 KiB per chunk and head)."""
+    return prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes) + n_chunk_heads * T_RECORD_BYTES
 
 
 def decode_bytes(n_heads_seqs, dk, dv, io_bytes, o_bytes):
