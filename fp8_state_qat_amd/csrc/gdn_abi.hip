@@ -130,7 +130,8 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape) {
   g_err[0] = 0;
   if (check_shape(shape, false) != GDN_OK) return 0;
-  return gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
+  return gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens,
+                                   shape->gate_per_channel != 0);
 }
 
 gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
@@ -142,7 +143,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   g_err[0] = 0;
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
-  const size_t need = gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
+  const size_t need = gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens,
+                                                shape->gate_per_channel != 0);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL");
@@ -158,8 +160,6 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
     return fail(GDN_ERR_INVALID_ARG, "debug record needs bound_offsets");
   if (shape->io_dtype == GDN_F32 && shape->dk != 64)
     return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs are supported with dk = 64 only");
-  if (shape->io_dtype == GDN_F32 && shape->gate_per_channel)
-    return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs with a per-key-channel gate are not supported");
   st = check_device();
   if (st != GDN_OK) return st;
   hipError_t e = gdn::launch_chunk_fwd(*shape, q, k, v, beta, g, cu_seqlens, seq_lens, prefix_lens,

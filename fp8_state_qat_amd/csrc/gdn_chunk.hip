@@ -44,174 +44,13 @@
 // fed as the codes and the products are scaled by s; otherwise (QDQ off, a
 // supplied initial state) as a hi + lo pair.  fp32 inputs use the fp32 MFMA
 // throughout.
-#include "gdn_device.hpp"
-#include "gdn_launch.hpp"
+#include "gdn_chunk_common.hpp"
 
 namespace gdn {
 
 constexpr int kChunkWaves = 8;
 constexpr int kChunkThreads = 64 * kChunkWaves;
 constexpr int kHelperThreads = 256;  // waves 4..7
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct Frag8 {
-  float v[8];
-};
-
-// Direct global -> LDS copy: lane l of the wave writes the 16 bytes at
-// base + off (base the same in every lane, off this lane's byte offset) to
-// dst + 16 l; dst must be the same in every lane.  Issued from inline
-// assembly so that the compiler does not hold later LDS accesses of the wave
-// behind it: the kernel orders these copies itself, with wait_vmem() before
-// the barrier that publishes them.  M0 (the LDS base of the copy) is restored.
-__device__ __forceinline__ void lds_load16(const void* base, uint32_t off, void* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
-  // readfirstlane returns int: widen each half through uint32_t (no sign extension)
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(sb), "s"(lds)
-      : "memory");
-}
-// Wait until this wave's outstanding vector memory operations (including
-// direct LDS loads) have completed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Workgroup barrier that orders LDS accesses only: it does not wait for the
-// wave's direct LDS loads or global memory operations in flight.
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-// gfx950 LDS transpose read of 16-bit data: inside each group of 16 lanes,
-// lane i receives, in its slot k (k = 0..3), element i % 4 of the 8 bytes
-// addressed by lane 4k + i / 4 of the same group.
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16*)((__attribute__((address_space(3))) char*)p));
-  return __builtin_bit_cast(uint2, r);
-}
-// Slot of lane l inside a k/q fragment dump: each block of 16 lanes is
-// rotated by 4 per block so that the transpose reads of the state update hit
-// different banks.
-__device__ __forceinline__ int rot_slot(int l) { return (l & 48) | ((l + ((l >> 4) << 2)) & 15); }
-__device__ __forceinline__ int rot_lane(int p) { return (p & 48) | ((p - ((p >> 4) << 2)) & 15); }
-
-// bf16 engine: LDS operands are bf16 bit patterns, fragments 8 x bf16.
-struct EngBF16 {
-  using E = uint16_t;
-  using Fr = bf16x8;
-  static constexpr bool kSplit = true;
-  static constexpr int kPlanes = 2;     // hi and lo planes of split operands
-  static constexpr bool kTrRead = true; // K^T fragments by LDS transpose reads
-  static __device__ __forceinline__ Fr ld(const E* p) { return *reinterpret_cast<const Fr*>(p); }
-  static __device__ __forceinline__ void st(E* p, const Fr& f) { *reinterpret_cast<Fr*>(p) = f; }
-  static __device__ __forceinline__ void mma(f32x4& c, const Fr& a, const Fr& b) { mma_bf16(c, a, b); }
-  static __device__ __forceinline__ Fr round(const float (&x)[8]) {
-    return __builtin_bit_cast(Fr, make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                             pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
-  }
-  static __device__ __forceinline__ void split(const float (&x)[8], Fr& hi, Fr& lo) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) split_bf16x2(x[2 * j], x[2 * j + 1], h[j], l[j]);
-    hi = __builtin_bit_cast(Fr, make_uint4(h[0], h[1], h[2], h[3]));
-    lo = __builtin_bit_cast(Fr, make_uint4(l[0], l[1], l[2], l[3]));
-  }
-  // fragment from two 4-element pieces (k slots 0..3 and 4..7)
-  static __device__ __forceinline__ Fr ld2(const E* a, const E* b) {
-    const uint2 u = *reinterpret_cast<const uint2*>(a);
-    const uint2 v = *reinterpret_cast<const uint2*>(b);
-    return __builtin_bit_cast(Fr, make_uint4(u.x, u.y, v.x, v.y));
-  }
-  static __device__ __forceinline__ Fr pack8(const E (&x)[8]) {
-    return __builtin_bit_cast(Fr, make_uint4((uint32_t)x[0] | ((uint32_t)x[1] << 16),
-                                             (uint32_t)x[2] | ((uint32_t)x[3] << 16),
-                                             (uint32_t)x[4] | ((uint32_t)x[5] << 16),
-                                             (uint32_t)x[6] | ((uint32_t)x[7] << 16)));
-  }
-  static __device__ __forceinline__ float to_f(E x) { return bf16_bits_to_float(x); }
-  // four values -> hi at ph, lo at pl
-  static __device__ __forceinline__ void st4_split(E* ph, E* pl, const float (&x)[4]) {
-    uint32_t h0, l0, h1, l1;
-    split_bf16x2(x[0], x[1], h0, l0);
-    split_bf16x2(x[2], x[3], h1, l1);
-    *reinterpret_cast<uint2*>(ph) = make_uint2(h0, h1);
-    *reinterpret_cast<uint2*>(pl) = make_uint2(l0, l1);
-  }
-};
-
-// fp32 engine: LDS operands are fp32, fragments 8 x fp32, products on the fp32 MFMA.
-struct EngF32 {
-  using E = float;
-  using Fr = Frag8;
-  static constexpr bool kSplit = false;
-  static constexpr int kPlanes = 1;
-  static constexpr bool kTrRead = false; // K^T fragments from a gathered dump
-  static __device__ __forceinline__ Fr ld(const E* p) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    Fr f;
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-  }
-  static __device__ __forceinline__ void st(E* p, const Fr& f) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(f.v[0], f.v[1], f.v[2], f.v[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(f.v[4], f.v[5], f.v[6], f.v[7]);
-  }
-  static __device__ __forceinline__ void mma(f32x4& c, const Fr& a, const Fr& b) { mma_f32(c, a.v, b.v); }
-  static __device__ __forceinline__ Fr round(const float (&x)[8]) {
-    Fr f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f.v[j] = x[j];
-    return f;
-  }
-  static __device__ __forceinline__ void split(const float (&x)[8], Fr& hi, Fr& lo) {
-    hi = round(x);
-    (void)lo;
-  }
-  static __device__ __forceinline__ Fr ld2(const E* a, const E* b) {
-    const float4 u = *reinterpret_cast<const float4*>(a);
-    const float4 v = *reinterpret_cast<const float4*>(b);
-    Fr f;
-    f.v[0] = u.x; f.v[1] = u.y; f.v[2] = u.z; f.v[3] = u.w;
-    f.v[4] = v.x; f.v[5] = v.y; f.v[6] = v.z; f.v[7] = v.w;
-    return f;
-  }
-  static __device__ __forceinline__ Fr pack8(const E (&x)[8]) { return round(x); }
-  static __device__ __forceinline__ float to_f(E x) { return x; }
-  static __device__ __forceinline__ void st4_split(E* ph, E* pl, const float (&x)[4]) {
-    (void)pl;
-    *reinterpret_cast<float4*>(ph) = make_float4(x[0], x[1], x[2], x[3]);
-  }
-};
-
-// Key-channel order of the state.  The chain waves hold S^T in accumulator
-// tiles whose rows are "state rows" sr = 16 t + 4 (l/16) + i; state row sr
-// carries key channel
-//     dkmap(sr) = 32 (sr / 32) + 8 ((sr % 16) / 4) + 4 ((sr / 16) % 2) + sr % 4.
-// With this relabelling the eight k-slots kperm(gq, 0..7) of k-block kb,
-// state rows 32 kb + kperm(gq, j), are the key channels 32 kb + 8 gq + j: a K
-// or Q fragment lane holds 8 consecutive channels of one row, 16 contiguous
-// bytes of the input, so the fragment dumps below are filled by direct
-// 16-byte global->LDS loads.  Contractions over the key axis (K S^T, S Q^T,
-// Q K^T) only need both operands in the same order; the relabelling is undone
-// where the state meets memory.
-__host__ __device__ constexpr int dkmap(int sr) {
-  return 32 * (sr / 32) + 8 * ((sr % 16) / 4) + 4 * ((sr / 16) % 2) + sr % 4;
-}
 
 // LDS layout of the sequential kernel (bytes).  F = one fragment dump (64
 // lanes x 8 elements, lane-major).
@@ -252,28 +91,6 @@ struct Lds {
   static_assert(oK + (2 * DK + 64 + 8) * sizeof(float) <= oQ, "suffix buffers do not fit");
 };
 
-struct ChunkArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* beta;
-  const float* g;
-  const int32_t* cu_seqlens;
-  const int32_t* seq_lens;
-  const int32_t* prefix_lens;
-  const int32_t* chunk_offs;  // prefix sums of ceil(P_n / 64) (prep kernel)
-  const void* T;              // one T record per (chunk, head) (prep kernel)
-  const float* init;
-  void* o;
-  float* fin;
-  const int32_t* bound_offsets;
-  float* bound_pre;
-  float* bound_post;
-  float* bound_scales;
-  int H;
-  int dv;
-  unsigned flags;
-};
 
 template <int DK, class Eng, typename TIO, typename TO>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
@@ -905,15 +722,16 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             const int32_t* seq_lens, const int32_t* prefix_lens,
                             const float* initial_state, void* o, float* final_state,
                             void* workspace, const gdn_debug_t* debug, hipStream_t stream) {
-  if (s.gate_per_channel) return hipErrorNotSupported;
   ChunkArgs a;
   const int32_t* offs = nullptr;
   void* T = nullptr;
-  hipError_t e = launch_prep(s, k, beta, g, cu_seqlens, seq_lens, prefix_lens, workspace, &offs, &T, stream);
+  void* Prec = nullptr;
+  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, workspace, &offs, &T,
+                             &Prec, stream);
   if (e != hipSuccess) return e;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
   a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens; a.prefix_lens = prefix_lens;
-  a.chunk_offs = offs; a.T = T;
+  a.chunk_offs = offs; a.T = T; a.Prec = Prec;
   a.init = initial_state; a.o = o; a.fin = final_state;
   a.bound_offsets = debug ? debug->bound_offsets : nullptr;
   a.bound_pre = debug ? debug->bound_pre : nullptr;
@@ -925,7 +743,9 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
     e = hipEventRecord((hipEvent_t)debug->kernel_start, stream);
     if (e != hipSuccess) return e;
   }
-  if (s.io_dtype == GDN_BF16) {
+  if (s.gate_per_channel) {
+    e = launch_kda_state(s, a, stream);
+  } else if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)
       e = ob ? launch_typed<128, EngBF16, uint16_t, uint16_t>(s, a, stream)
              : launch_typed<128, EngBF16, uint16_t, float>(s, a, stream);

@@ -23,17 +23,18 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             void* workspace, const gdn_debug_t* debug, hipStream_t stream);
 
 // One T record per (chunk, head): T = (I + A)^-1 diag(beta) in MFMA
-// A-fragment order (see gdn_prep.hip), 12 KiB for both engines.
+// A-fragment order (see gdn_prep.hip), 12 KiB for both engines.  The
+// per-key-channel gate adds one P record of the same layout.
 constexpr int kTRecBytes = 12288;
 
 // Bytes of the chunk workspace: chunk offsets [N + 1] (padded to 256 bytes)
-// and one T record per (chunk, head) for the worst-case chunk count
-// ceil(total_tokens / 64) + N.
-size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens);
+// and one T record (two records -- T, then P -- with a per-key-channel gate)
+// per (chunk, head) for the worst-case chunk count ceil(total_tokens / 64) + N.
+size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens, bool per_channel);
 
-hipError_t launch_prep(const gdn_shape_t& s, const void* k, const float* beta, const float* g,
-                       const int32_t* cu_seqlens, const int32_t* seq_lens,
+hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
+                       const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
                        const int32_t* prefix_lens, void* workspace, const int32_t** offs_out,
-                       void** T_out, hipStream_t stream);
+                       void** T_out, void** P_out, hipStream_t stream);
 
 }  // namespace gdn

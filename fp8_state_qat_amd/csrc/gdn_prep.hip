@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void chunk_offsets_kernel(const int32_t* 
 }
 
 struct PrepArgs {
+  const void* q;  // per-key-channel gate only
   const void* k;
   const float* beta;
   const float* g;
@@ -73,6 +74,7 @@ struct PrepArgs {
   const int32_t* prefix_lens;
   const int32_t* offs;
   void* T;        // one record of kTRecBytes per (chunk, head)
+  void* P;        // per-key-channel gate: one P record per (chunk, head)
   int N;
   int H;
 };
@@ -86,11 +88,117 @@ __device__ __forceinline__ float dot16p(const float* a, const float* b) {
   return (dot4p(a4[0], b4[0]) + dot4p(a4[1], b4[1])) + (dot4p(a4[2], b4[2]) + dot4p(a4[3], b4[3]));
 }
 
+// Row stride (floats) of the 64 x 64 fp32 LDS matrices of the prep kernels.
+constexpr int kL64 = 64 + 4;
+
+// X = (I + A)^-1 for the strictly lower A in sA (only the block-lower 16 x 16
+// blocks are read), 256 threads: the four diagonal blocks by forward
+// substitution (one lane per column), then the off-diagonal blocks level by
+// level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.  sX receives X row-major
+// (block-lower part; the diagonal blocks carry zeros above their diagonal),
+// sXT its transpose; sRT is scratch.  Contains barriers.
+__device__ __forceinline__ void solve_unit_lower(const float* sA, float* sX, float* sXT, float* sRT) {
+  constexpr int L64 = kL64;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // ---- diagonal blocks of X = (I + A)^-1: lane = (block, column), column-oriented
+  if (w == 0) {
+    const int bi = lane >> 4, cc = lane & 15;
+    const float* Ab = sA + 16 * bi * L64 + 16 * bi;
+    float am[16][16];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+      for (int q4 = 0; q4 * 4 < r; ++q4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(Ab + r * L64 + 4 * q4);
+        am[r][4 * q4] = v4.x; am[r][4 * q4 + 1] = v4.y; am[r][4 * q4 + 2] = v4.z; am[r][4 * q4 + 3] = v4.w;
+      }
+    float xc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xc[r] = (r == cc) ? 1.f : 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int r = s + 1; r < 16; ++r) xc[r] = fmaf(-am[r][s], xc[s], xc[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sX[(16 * bi + r) * L64 + 16 * bi + cc] = xc[r];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<float4*>(sXT + (16 * bi + cc) * L64 + 16 * bi + 4 * q4) =
+          make_float4(xc[4 * q4], xc[4 * q4 + 1], xc[4 * q4 + 2], xc[4 * q4 + 3]);
+  }
+  __syncthreads();
+  // ---- off-diagonal blocks, level by level
+  {
+    const int r = tid >> 4, cc = tid & 15;
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+#pragma unroll
+      for (int b = 0; b + d < 4; ++b) {
+        const int i = d + b, jb = b;
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = jb; kk < i; ++kk)
+          acc += dot16p(sA + (16 * i + r) * L64 + 16 * kk, sXT + (16 * jb + cc) * L64 + 16 * kk);
+        sRT[b * 256 + cc * 16 + r] = acc;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b + d < 4; ++b) {
+        const int i = d + b, jb = b;
+        const float xv = -dot16p(sX + (16 * i + r) * L64 + 16 * i, sRT + b * 256 + cc * 16);
+        sX[(16 * i + r) * L64 + 16 * jb + cc] = xv;
+        sXT[(16 * jb + cc) * L64 + 16 * i + r] = xv;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Writes the block-lower part of the 64 x 64 matrix M (row-major, stride
+// kL64, zeros above the diagonal of its diagonal blocks), times diag(colscale)
+// when colscale is not null, as one record in MFMA fragment order (the record
+// layout described at the top of this file), 256 threads.
+template <bool kBF>
+__device__ __forceinline__ void store_record(const float* M, const float* colscale, char* rec) {
+  constexpr int L64 = kL64;
+  const int tid = threadIdx.x;
+  for (int slot = tid; slot < 6 * 64; slot += kThreads) {
+    const int p = slot >> 6, l = slot & 63, g4 = l >> 4;
+    const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+    const int r = 16 * ti + (l & 15);
+    float t8[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int s0 = 32 * kb + 16 * half + 4 * g4;
+      float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if ((s0 >> 4) <= ti) x4 = *reinterpret_cast<const float4*>(M + r * L64 + s0);
+      const float4 b4 = colscale ? *reinterpret_cast<const float4*>(colscale + s0)
+                                 : make_float4(1.f, 1.f, 1.f, 1.f);
+      t8[4 * half] = x4.x * b4.x;
+      t8[4 * half + 1] = x4.y * b4.y;
+      t8[4 * half + 2] = x4.z * b4.z;
+      t8[4 * half + 3] = x4.w * b4.w;
+    }
+    if constexpr (kBF) {
+      uint32_t hv[4], lv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], lv[q]);
+      uint4* dst = reinterpret_cast<uint4*>(rec);
+      dst[p * 64 + l] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      dst[(6 + p) * 64 + l] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+    } else {
+      float4* dst = reinterpret_cast<float4*>(rec) + 2 * (p * 64 + l);
+      dst[0] = make_float4(t8[0], t8[1], t8[2], t8[3]);
+      dst[1] = make_float4(t8[4], t8[5], t8[6], t8[7]);
+    }
+  }
+}
+
 // One workgroup (4 waves) per (chunk, head).  TIO: uint16_t (bf16) or float.
 template <int DK, typename TIO>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
   constexpr bool kBF = sizeof(TIO) == 2;
-  constexpr int L64 = 64 + 4;
+  constexpr int L64 = kL64;
   constexpr int LDK = DK + 16 / (int)sizeof(TIO);  // K row stride (elements), 16-byte rows
   constexpr int NKB = DK / 32;
   __shared__ __align__(16) TIO sK[64 * LDK];
@@ -195,123 +303,265 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // ---- diagonal blocks of X = (I + A)^-1: lane = (block, column), column-oriented
-  if (w == 0) {
-    const int bi = lane >> 4, cc = lane & 15;
-    const float* Ab = sA + 16 * bi * L64 + 16 * bi;
-    float am[16][16];
-#pragma unroll
-    for (int r = 1; r < 16; ++r)
-#pragma unroll
-      for (int q4 = 0; q4 * 4 < r; ++q4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(Ab + r * L64 + 4 * q4);
-        am[r][4 * q4] = v4.x; am[r][4 * q4 + 1] = v4.y; am[r][4 * q4 + 2] = v4.z; am[r][4 * q4 + 3] = v4.w;
+  solve_unit_lower(sA, sX, sXT, sRT);
+  store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes);
+}
+
+
+// ---------------------------------------------------------------------------
+// Per-key-channel gate (#2506 "What does this PR do?": per-key-channel
+// retention, pairwise exponentials from prefix differences).  g is
+// [T, H, dk], gamma_r in R^dk, and per chunk
+//     A[r][s] = beta_r sum_c k_rc k_sc exp(gamma_rc - gamma_sc)      (s < r)
+//     P[r][s] = sum_c q_rc k_sc exp(gamma_rc - gamma_sc)             (s <= r)
+//     T       = (I + A)^-1 diag(beta)
+// No exp(-gamma) is formed on its own (it overflows).  For 16-token blocks
+// R > S the last token m of block S is a reference point:
+// exp(gamma_r - gamma_s) = exp(gamma_r - gamma_m) exp(gamma_m - gamma_s), both
+// factors <= 1 for non-positive gates, so those blocks are fp32 MFMA products
+// of pre-scaled operands.  The four diagonal 16 x 16 blocks are summed
+// channel by channel with the exponential of each difference.  T and P are
+// written as two records per (chunk, head) in the layout above.
+// ---------------------------------------------------------------------------
+template <int DK, typename TIO>
+struct KdaPrepLds {
+  static constexpr int LX = DK + 16 / (int)sizeof(TIO);  // k, q row stride (elements)
+  static constexpr int LG = DK + 4;                      // gamma row stride (floats)
+  static constexpr size_t oK = 0;
+  static constexpr size_t oQ = oK + 64 * LX * sizeof(TIO);
+  static constexpr size_t oG = oQ + 64 * LX * sizeof(TIO);
+  static constexpr size_t oA = oG + 64 * LG * sizeof(float);
+  static constexpr size_t oP = oA + 64 * kL64 * sizeof(float);
+  static constexpr size_t oRT = oP + 64 * kL64 * sizeof(float);
+  static constexpr size_t oTot = oRT + 3 * 256 * sizeof(float);
+  static constexpr size_t oBeta = oTot + kThreads * sizeof(float);
+  static constexpr size_t bytes = oBeta + 64 * sizeof(float);
+  // once A and P are formed, the solve's X overlays k and q, X^T overlays gamma
+  static constexpr size_t oX = oK, oXT = oG;
+  static_assert(64 * kL64 * sizeof(float) <= oG - oK, "X does not fit over k and q");
+  static_assert(64 * kL64 * sizeof(float) <= oA - oG, "X^T does not fit over gamma");
+};
+
+template <typename TIO>
+__device__ __forceinline__ void load4f(const TIO* p, float (&x)[4]) {
+  if constexpr (sizeof(TIO) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+}
+
+template <int DK, typename TIO>
+__global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
+  using Ls = KdaPrepLds<DK, TIO>;
+  constexpr bool kBF = sizeof(TIO) == 2;
+  constexpr int LX = Ls::LX, LG = Ls::LG, L64 = kL64, NKB = DK / 32;
+  extern __shared__ __align__(16) char smem[];
+  TIO* sK = reinterpret_cast<TIO*>(smem + Ls::oK);
+  TIO* sQ = reinterpret_cast<TIO*>(smem + Ls::oQ);
+  float* sG = reinterpret_cast<float*>(smem + Ls::oG);    // gamma * log2(e)
+  float* sA = reinterpret_cast<float*>(smem + Ls::oA);
+  float* sP = reinterpret_cast<float*>(smem + Ls::oP);
+  float* sRT = reinterpret_cast<float*>(smem + Ls::oRT);
+  float* sTot = reinterpret_cast<float*>(smem + Ls::oTot);
+  float* sBeta = reinterpret_cast<float*>(smem + Ls::oBeta);
+  float* sX = reinterpret_cast<float*>(smem + Ls::oX);
+  float* sXT = reinterpret_cast<float*>(smem + Ls::oXT);
+
+  const int H = a.H;
+  const int j = blockIdx.x / H, h = blockIdx.x % H;
+  const int total = a.offs[a.N];
+  if (j >= total) return;  // grid is sized for the worst case
+  int lo = 0, hi = a.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.offs[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  const int n = lo, c = j - a.offs[n];
+  const int seg0 = a.cu_seqlens[n];
+  const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
+  const int P = a.prefix_lens ? a.prefix_lens[n] : L;
+  const int t0 = seg0 + c * kChunk;
+  const int nv = min(kChunk, P - c * kChunk);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
+
+  // ---- stage k and q (rows past nv are zero), beta, and the per-channel gate prefix
+  {
+    constexpr int EPS = 16 / (int)sizeof(TIO);
+    constexpr int SPR = DK / EPS;
+    const TIO* gk = reinterpret_cast<const TIO*>(a.k);
+    const TIO* gqv = reinterpret_cast<const TIO*>(a.q);
+    for (int seg = tid; seg < 64 * SPR; seg += kThreads) {
+      const int r = seg / SPR, c0 = (seg % SPR) * EPS;
+      uint4 kv = make_uint4(0u, 0u, 0u, 0u), qv = make_uint4(0u, 0u, 0u, 0u);
+      if (r < nv) {
+        const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c0;
+        kv = *reinterpret_cast<const uint4*>(gk + off);
+        qv = *reinterpret_cast<const uint4*>(gqv + off);
       }
-    float xc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xc[r] = (r == cc) ? 1.f : 0.f;
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-#pragma unroll
-      for (int r = s + 1; r < 16; ++r) xc[r] = fmaf(-am[r][s], xc[s], xc[r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sX[(16 * bi + r) * L64 + 16 * bi + cc] = xc[r];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<float4*>(sXT + (16 * bi + cc) * L64 + 16 * bi + 4 * q4) =
-          make_float4(xc[4 * q4], xc[4 * q4 + 1], xc[4 * q4 + 2], xc[4 * q4 + 3]);
+      *reinterpret_cast<uint4*>(sK + r * LX + c0) = kv;
+      *reinterpret_cast<uint4*>(sQ + r * LX + c0) = qv;
+    }
+    if (tid < 64) sBeta[tid] = (tid < nv) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;
+  }
+  constexpr int NPART = kThreads / DK, TPP = 64 / NPART;  // token parts of the per-channel scan
+  {
+    const int d = tid % DK, part = tid / DK;
+    float run = 0.f;
+    for (int r = part * TPP; r < (part + 1) * TPP; ++r) {
+      run += (r < nv) ? a.g[((int64_t)(t0 + r) * H + h) * DK + d] : 0.f;
+      sG[r * LG + d] = run;
+    }
+    sTot[tid] = run;
   }
   __syncthreads();
-  // ---- off-diagonal blocks, level by level
   {
-    const int r = tid >> 4, cc = tid & 15;
+    const int d = tid % DK, part = tid / DK;
+    float off = 0.f;
+    for (int pp = 0; pp < part; ++pp) off += sTot[pp * DK + d];
+    for (int r = part * TPP; r < (part + 1) * TPP; ++r) sG[r * LG + d] = (sG[r * LG + d] + off) * 1.4426950408889634f;
+  }
+  __syncthreads();
+
+  // ---- blocks R > S, pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): C[s][r] with
+  // A = k_s exp(gamma_m - gamma_s), B = x_r exp(gamma_r - gamma_m), m = 16 S + 15
+  for (int pr = w; pr < 6; pr += 4) {
+    const int R = (pr < 1) ? 1 : (pr < 3) ? 2 : 3;
+    const int S = pr - (R * (R - 1)) / 2;
+    const int m = 16 * S + 15;
+    const int s = 16 * S + ln, r = 16 * R + ln;
+    f32x4 ca = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
+    for (int kb = 0; kb < NKB; ++kb) {
+      float av[8], bk[8], bq[8];
 #pragma unroll
-      for (int b = 0; b + d < 4; ++b) {
-        const int i = d + b, jb = b;
-        float acc = 0.f;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c0 = 32 * kb + 16 * hh + 4 * gq;  // channels kperm(gq, 4 hh .. 4 hh + 3)
+        const float4 gs4 = *reinterpret_cast<const float4*>(sG + s * LG + c0);
+        const float4 gm4 = *reinterpret_cast<const float4*>(sG + m * LG + c0);
+        const float4 gr4 = *reinterpret_cast<const float4*>(sG + r * LG + c0);
+        const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+        const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
+        const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+        float ks[4], kr[4], qr[4];
+        load4f(sK + s * LX + c0, ks);
+        load4f(sK + r * LX + c0, kr);
+        load4f(sQ + r * LX + c0, qr);
 #pragma unroll
-        for (int kk = jb; kk < i; ++kk)
-          acc += dot16p(sA + (16 * i + r) * L64 + 16 * kk, sXT + (16 * jb + cc) * L64 + 16 * kk);
-        sRT[b * 256 + cc * 16 + r] = acc;
+        for (int i = 0; i < 4; ++i) {
+          av[4 * hh + i] = ks[i] * __builtin_amdgcn_exp2f(gm[i] - gs[i]);
+          const float f = __builtin_amdgcn_exp2f(gr[i] - gm[i]);
+          bk[4 * hh + i] = kr[i] * f;
+          bq[4 * hh + i] = qr[i] * f;
+        }
       }
-      __syncthreads();
-#pragma unroll
-      for (int b = 0; b + d < 4; ++b) {
-        const int i = d + b, jb = b;
-        const float xv = -dot16p(sX + (16 * i + r) * L64 + 16 * i, sRT + b * 256 + cc * 16);
-        sX[(16 * i + r) * L64 + 16 * jb + cc] = xv;
-        sXT[(16 * jb + cc) * L64 + 16 * i + r] = xv;
-      }
-      __syncthreads();
+      mma_f32(ca, av, bk);
+      mma_f32(cp, av, bq);
     }
+    // lane holds C[16 S + 4 gq + i][16 R + ln]
+    const float br = sBeta[r];
+    *reinterpret_cast<float4*>(sA + r * L64 + 16 * S + 4 * gq) =
+        make_float4(br * ca[0], br * ca[1], br * ca[2], br * ca[3]);
+    *reinterpret_cast<float4*>(sP + r * L64 + 16 * S + 4 * gq) = make_float4(cp[0], cp[1], cp[2], cp[3]);
   }
 
-  // ---- T = X diag(beta), zero above the block diagonal -> workspace record
-  for (int slot = tid; slot < 6 * 64; slot += kThreads) {
-    const int p = slot >> 6, l = slot & 63, g4 = l >> 4;
-    const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-    const int r = 16 * ti + (l & 15);
-    float t8[8];
+  // ---- diagonal blocks: pairs s <= r inside each 16-token block, channel by channel
+  for (int pi = tid; pi < 4 * 136; pi += kThreads) {
+    const int b = pi / 136, idx = pi - 136 * b;
+    int rl = 0;
+    while ((rl + 1) * (rl + 2) / 2 <= idx) ++rl;  // idx = rl (rl + 1) / 2 + sl
+    const int sl = idx - rl * (rl + 1) / 2;
+    const int r = 16 * b + rl, s = 16 * b + sl;
+    float sa[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < DK; c0 += 4) {
+      float kr[4], qr[4], ks[4];
+      load4f(sK + r * LX + c0, kr);
+      load4f(sQ + r * LX + c0, qr);
+      load4f(sK + s * LX + c0, ks);
+      const float4 gr4 = *reinterpret_cast<const float4*>(sG + r * LG + c0);
+      const float4 gs4 = *reinterpret_cast<const float4*>(sG + s * LG + c0);
+      const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+      const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int s0 = 32 * kb + 16 * half + 4 * g4;
-      float4 x4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if ((s0 >> 4) <= ti) x4 = *reinterpret_cast<const float4*>(sX + r * L64 + s0);
-      const float4 b4 = *reinterpret_cast<const float4*>(sBeta + s0);
-      t8[4 * half] = x4.x * b4.x;
-      t8[4 * half + 1] = x4.y * b4.y;
-      t8[4 * half + 2] = x4.z * b4.z;
-      t8[4 * half + 3] = x4.w * b4.w;
+      for (int i = 0; i < 4; ++i) {
+        const float ke = ks[i] * __builtin_amdgcn_exp2f(gr[i] - gs[i]);
+        sa[i] = fmaf(kr[i], ke, sa[i]);
+        sp[i] = fmaf(qr[i], ke, sp[i]);
+      }
     }
-    char* rec = reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes;
-    if constexpr (kBF) {
-      uint32_t hv[4], lv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) split_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], lv[q]);
-      uint4* dst = reinterpret_cast<uint4*>(rec);
-      dst[p * 64 + l] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-      dst[(6 + p) * 64 + l] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
-    } else {
-      float4* dst = reinterpret_cast<float4*>(rec) + 2 * (p * 64 + l);
-      dst[0] = make_float4(t8[0], t8[1], t8[2], t8[3]);
-      dst[1] = make_float4(t8[4], t8[5], t8[6], t8[7]);
+    const float av = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+    const float pv = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    sP[r * L64 + s] = pv;
+    if (sl < rl) {
+      sA[r * L64 + s] = sBeta[r] * av;
+      sP[s * L64 + r] = 0.f;  // above the diagonal
     }
   }
+  __syncthreads();
+
+  const int64_t rec = ((int64_t)j * H + h) * kTRecBytes;
+  store_record<kBF>(sP, nullptr, reinterpret_cast<char*>(a.P) + rec);
+  solve_unit_lower(sA, sX, sXT, sRT);
+  store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + rec);
 }
 
-size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens) {
+size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens, bool per_channel) {
   const int64_t max_chunks = (total_tokens + kChunk - 1) / kChunk + n_seqs;
   const size_t offs = ((size_t)(n_seqs + 1) * 4 + 255) / 256 * 256;
-  return offs + (size_t)max_chunks * n_heads * kTRecBytes;
+  return offs + (size_t)max_chunks * n_heads * kTRecBytes * (per_channel ? 2 : 1);
 }
 
-hipError_t launch_prep(const gdn_shape_t& s, const void* k, const float* beta, const float* g,
-                       const int32_t* cu_seqlens, const int32_t* seq_lens,
+template <int DK, typename TIO>
+static hipError_t launch_kda_prep(dim3 grid, const PrepArgs& a, hipStream_t stream) {
+  auto kern = kda_prep_kernel<DK, TIO>;
+  constexpr size_t lds = KdaPrepLds<DK, TIO>::bytes;
+  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
+                       const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
                        const int32_t* prefix_lens, void* workspace, const int32_t** offs_out,
-                       void** T_out, hipStream_t stream) {
+                       void** T_out, void** P_out, hipStream_t stream) {
   int32_t* offs = reinterpret_cast<int32_t*>(workspace);
   const size_t offs_bytes = ((size_t)(s.n_seqs + 1) * 4 + 255) / 256 * 256;
-  void* T = reinterpret_cast<char*>(workspace) + offs_bytes;
-  *offs_out = offs;
-  *T_out = T;
-  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(kThreads), 0, stream, cu_seqlens, seq_lens,
-                     prefix_lens, s.n_seqs, offs);
   const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
   const int64_t blocks = max_chunks * s.n_heads;
+  void* T = reinterpret_cast<char*>(workspace) + offs_bytes;
+  void* Prec = s.gate_per_channel ? reinterpret_cast<char*>(T) + (size_t)blocks * kTRecBytes : nullptr;
+  *offs_out = offs;
+  *T_out = T;
+  *P_out = Prec;
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(kThreads), 0, stream, cu_seqlens, seq_lens,
+                     prefix_lens, s.n_seqs, offs);
   if (blocks == 0) return hipGetLastError();
   PrepArgs a;
-  a.k = k; a.beta = beta; a.g = g; a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens;
-  a.prefix_lens = prefix_lens; a.offs = offs; a.T = T; a.N = s.n_seqs; a.H = s.n_heads;
+  a.q = q; a.k = k; a.beta = beta; a.g = g; a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens;
+  a.prefix_lens = prefix_lens; a.offs = offs; a.T = T; a.P = Prec; a.N = s.n_seqs; a.H = s.n_heads;
+  const dim3 grid((unsigned)blocks);
+  if (s.gate_per_channel) {
+    if (s.io_dtype == GDN_BF16)
+      return s.dk == 128 ? launch_kda_prep<128, uint16_t>(grid, a, stream)
+                         : launch_kda_prep<64, uint16_t>(grid, a, stream);
+    if (s.dk != 64) return hipErrorNotSupported;  // fp32 inputs: dk = 64 only
+    return launch_kda_prep<64, float>(grid, a, stream);
+  }
   if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)
-      hipLaunchKernelGGL((chunk_prep_kernel<128, uint16_t>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((chunk_prep_kernel<128, uint16_t>), grid, dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((chunk_prep_kernel<64, uint16_t>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((chunk_prep_kernel<64, uint16_t>), grid, dim3(kThreads), 0, stream, a);
   } else {
     if (s.dk != 64) return hipErrorNotSupported;  // fp32 inputs: dk = 64 only
-    hipLaunchKernelGGL((chunk_prep_kernel<64, float>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((chunk_prep_kernel<64, float>), grid, dim3(kThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

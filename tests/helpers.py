@@ -134,3 +134,75 @@ def teacher_forced(w: gi.Workload, gpu, flags, pairs, *, initial_state=None):
     out["o_rel"] = float(np.sqrt(acc[0] / max(acc[1], 1e-300)))
     out["pre_rel"] = float(np.sqrt(acc[2] / max(acc[3], 1e-300)))
     return out
+
+
+# G1 / G2 gates (rel-L2 over valid rows)
+TOL = {gi.F32: 1e-5, gi.BF16: 2e-3}
+
+
+def valid_rows(w):
+    m = np.zeros(w.total_tokens, bool)
+    for n in range(w.n_seqs):
+        m[w.cu_seqlens[n]:w.cu_seqlens[n] + w.seq_lens[n]] = True
+    return m
+
+
+def check_g1(w, gpu, ref, tol):
+    m = valid_rows(w)
+    o_rel = rel_l2(gpu["o"][m], ref["o"][m])
+    s_rel = rel_l2(gpu["S"], ref["S"])
+    print(f"G1 o_rel={o_rel:.3e} S_rel={s_rel:.3e} tol={tol}", flush=True)
+    assert o_rel <= tol and s_rel <= tol
+    # padding rows are zero
+    assert np.all(gpu["o"][~m] == 0)
+
+
+def check_g2(w, gpu, flags, tol, initial_state=None):
+    pairs = [(n, h) for n in range(w.n_seqs) for h in range(w.n_heads)]
+    r = teacher_forced(w, gpu, flags, pairs, initial_state=initial_state)
+    print("G2", r, flush=True)
+    assert r["o_rel"] <= tol and r["pre_rel"] <= tol
+    assert r["gpu_code_mismatch"] == 0 and r["scale_mismatch"] == 0
+    if r["codes"]:
+        assert r["oracle_code_mismatch"] <= 1e-4 * r["codes"] or w.io_dtype == gi.BF16
+        if w.io_dtype == gi.F32:
+            assert r["oracle_mismatch_far"] == 0
+    return r
+
+
+def check_prefix_suffix(w, gpu, flags, tol):
+    """Prefix P_n then recurrent suffix up to L_n.  The chunked prefix is
+    checked teacher-forced per boundary (G2, when it quantizes).  The suffix
+    restarts the oracle from the GPU's handoff state (its last boundary
+    record, or the zero state when P_n = 0) and runs tokens P_n .. L_n - 1
+    free: within tol when the suffix does not quantize; with a per-write QDQ
+    an fp32-versus-fp64 difference of ~1e-7 flips a code now and then
+    (~3e-6 per element decision, within 1e-6 of a midpoint), which moves
+    later outputs by ~1e-4, so those runs are held to 1e-3 and the exact
+    per-write QDQ rule is pinned by the decode-step tests instead."""
+    pairs = [(n, h) for n in range(w.n_seqs) for h in range(w.n_heads)]
+    if flags:
+        r = teacher_forced(w, gpu, flags, [p for p in pairs if int(w.prefix_lens[p[0]]) > 0])
+        print("G2 prefix", r, flush=True)
+        assert r["o_rel"] <= tol and r["pre_rel"] <= tol
+        assert r["gpu_code_mismatch"] == 0 and r["scale_mismatch"] == 0
+    q, k, v, b, g = (w.f64(x) for x in ("q", "k", "v", "beta", "g"))
+    acc = np.zeros(4)
+    for (n, h) in pairs:
+        P, L, s0 = int(w.prefix_lens[n]), int(w.seq_lens[n]), int(w.cu_seqlens[n])
+        if L == P:
+            continue
+        S0 = None
+        if P > 0:
+            S0 = gpu["bound_post"][int(gpu["offsets"][n]) + (P + CHUNK - 1) // CHUNK - 1, h].astype(np.float64)
+        sl = slice(s0 + P, s0 + L)
+        gg = g[sl, h] if g.ndim == 2 else g[sl, h, :]
+        r = orc.gdn_sequence(q[sl, h], k[sl, h], v[sl, h], b[sl, h], gg, prefix_len=0,
+                             flags=orc.QDQ_WRITE if flags & orc.QDQ_WRITE else 0, S0=S0)
+        acc += [np.sum((gpu["o"][sl, h] - r["o"]) ** 2), np.sum(r["o"] ** 2),
+                np.sum((gpu["S"][n, h] - r["S"]) ** 2), np.sum(r["S"] ** 2)]
+    o_rel = float(np.sqrt(acc[0] / max(acc[1], 1e-300)))
+    s_rel = float(np.sqrt(acc[2] / max(acc[3], 1e-300)))
+    bound = tol if not (flags & orc.QDQ_WRITE) else 1e-3
+    print(f"suffix from the handoff state: o_rel={o_rel:.3e} S_rel={s_rel:.3e} bound={bound}", flush=True)
+    assert o_rel <= bound and s_rel <= bound

@@ -66,7 +66,7 @@ def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None, ws=FAKE, ws_by
     (dict(n_seqs=0), 1), (dict(n_heads=0), 1), (dict(dv=96), 1), (dict(dk=96), 2),
     (dict(dk=32), 2), (dict(dv=512), 2), (dict(total_tokens=-1), 1), (dict(io_dtype=7), 1),
     (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=4), 1),
-    (dict(io_dtype=0, dk=128), 2), (dict(io_dtype=0, dk=64, dv=64, gate_per_channel=1), 2),
+    (dict(io_dtype=0, dk=128), 2), (dict(io_dtype=0, dk=128, gate_per_channel=1), 2),
 ])
 def test_chunk_fwd_rejects_bad_shape(kw, status):
     assert _chunk(_shape(**kw)) == status
@@ -85,11 +85,14 @@ def test_chunk_fwd_rejects_null_and_misaligned():
 
 
 def test_workspace_size_and_checks():
-    """Workspace: worst-case chunk count ceil(T/64) + N records of 16 KiB per
-    head plus the chunk offsets; too small, NULL or misaligned is rejected."""
+    """Workspace: worst-case chunk count ceil(T/64) + N records of 12 KiB per
+    head (two records, T and P, with a per-key-channel gate) plus the chunk
+    offsets; too small, NULL or misaligned is rejected."""
     s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
     n = _ws(s)
     assert n == 256 + (3 + 3) * 2 * 12288
+    assert _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, gate_per_channel=1)) == \
+        256 + (3 + 3) * 2 * 2 * 12288
     assert _ws(_shape(dv=96)) == 0 and _lib.last_error()
     assert _chunk(s, ws_bytes=n - 1) == 1
     assert _chunk(s, ws=0) == 1

@@ -18,42 +18,10 @@ import pytest
 from fp8_state_qat_amd import inputs as gi
 from oracle import oracle as orc
 
-from helpers import rel_l2, run_chunk_gpu, run_chunk_oracle, teacher_forced
+from helpers import TOL, check_prefix_suffix, rel_l2, run_chunk_gpu, run_chunk_oracle, teacher_forced
+from helpers import check_g1 as _check_g1, check_g2 as _check_g2
 
 pytestmark = pytest.mark.gpu
-
-TOL = {gi.F32: 1e-5, gi.BF16: 2e-3}
-
-
-def _valid_rows(w):
-    m = np.zeros(w.total_tokens, bool)
-    for n in range(w.n_seqs):
-        m[w.cu_seqlens[n]:w.cu_seqlens[n] + w.seq_lens[n]] = True
-    return m
-
-
-def _check_g1(w, gpu, ref, tol):
-    m = _valid_rows(w)
-    o_rel = rel_l2(gpu["o"][m], ref["o"][m])
-    s_rel = rel_l2(gpu["S"], ref["S"])
-    print(f"G1 o_rel={o_rel:.3e} S_rel={s_rel:.3e} tol={tol}", flush=True)
-    assert o_rel <= tol and s_rel <= tol
-    # padding rows are zero
-    assert np.all(gpu["o"][~m] == 0)
-
-
-def _check_g2(w, gpu, flags, tol, initial_state=None):
-    pairs = [(n, h) for n in range(w.n_seqs) for h in range(w.n_heads)]
-    r = teacher_forced(w, gpu, flags, pairs, initial_state=initial_state)
-    print("G2", r, flush=True)
-    assert r["o_rel"] <= tol and r["pre_rel"] <= tol
-    assert r["gpu_code_mismatch"] == 0 and r["scale_mismatch"] == 0
-    if r["codes"]:
-        assert r["oracle_code_mismatch"] <= 1e-4 * r["codes"] or w.io_dtype == gi.BF16
-        if w.io_dtype == gi.F32:
-            assert r["oracle_mismatch_far"] == 0
-    return r
-
 
 # ---------------------------------------------------------------------------
 def test_tiny_fp32_qdq_on():
@@ -110,10 +78,7 @@ def test_prefix_suffix_fp32(flags):
     w = gi.make_packed([150, 70, 9], 2, 64, 64, io_dtype=gi.F32, seed=7 + flags,
                        prefix_lens=[128, 33, 0])
     gpu = run_chunk_gpu(w, flags, record=True)
-    ref = run_chunk_oracle(w, flags)
-    o_rel, s_rel = rel_l2(gpu["o"], ref["o"]), rel_l2(gpu["S"], ref["S"])
-    print(f"flags={flags} o_rel={o_rel:.3e} S_rel={s_rel:.3e}", flush=True)
-    assert o_rel <= 1e-5 and s_rel <= 1e-5
+    check_prefix_suffix(w, gpu, flags, TOL[gi.F32])
 
 
 def test_prefix_suffix_bf16_no_suffix_qdq():
