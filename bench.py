@@ -9,7 +9,8 @@ U', O, the state update and the boundary QDQ).  Inputs are resident in HBM
 before the timed region.  The roofline object covers the sequential state
 kernel, timed with HIP events recorded around it by the library.
 
-Also reported: the prefill->decode handoff workload (256 sequences, H=32,
+Also reported: the same prefill with a per-key-channel gate (KDA-style g
+[T, H, dk]) as tokens/s and its state kernel's time; the prefill->decode handoff workload (256 sequences, H=32,
 d=128: 2048-token chunked prefix with QDQ, then 512 single-token decode steps
 each writing the state through per-tile QDQ) as decode-step HBM GB/s, and the
 CPU oracle's throughput on the prefill workload (all 64 (sequence, head) pairs
@@ -135,6 +136,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-kda", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=64,
                     help="(sequence, head) pairs the oracle runs (64 = the whole workload)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
@@ -186,7 +188,7 @@ def main():
     fl = state_kernel_flops_per_token_head(64, dk, dv) * token_heads
     by = state_kernel_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2, 2)
     src = source_hash([os.path.join(ROOT, "fp8_state_qat_amd", "csrc", f)
-                       for f in ("gdn_chunk.hip", "gdn_device.hpp")])
+                       for f in ("gdn_chunk.hip", "gdn_chunk_common.hpp", "gdn_device.hpp")])
     traffic = load_traffic("chunk_fwd_gdn_prefill", src)
     tflops = fl / (kern_ms * 1e-3) / 1e12
     hbm_gbs = by / (kern_ms * 1e-3) / 1e9
@@ -224,6 +226,44 @@ def main():
            "roofline": roofline, "mfma": mfma,
            "qdq_off": {"ms_per_step": round(off_ms / args.steps, 5),
                        "tokens_per_s": round(tokens / (off_ms / args.steps * 1e-3), 1)}}
+
+    # ---------------- per-key-channel gate (KDA) prefill, same shape (reported) ----------------
+    if not args.no_kda:
+        wk = gi.kda_prefill()
+        dk_ = gi.device_tensors(wk, dev)
+        evk = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps + args.warmup)]
+        itk = {"i": 0}
+
+        def kstep():
+            e0, e1 = evk[itk["i"]]
+            itk["i"] += 1
+            api.chunk_fwd(dk_["q"], dk_["k"], dk_["v"], dk_["beta"], dk_["g"], dk_["cu_seqlens"],
+                          qdq_flags=flags, out=o, final_state=fin,
+                          debug={"kernel_start": e0, "kernel_end": e1})
+
+        for e0, e1 in evk:
+            e0.record()
+            e1.record()
+        torch.cuda.synchronize()
+        ktot, _ = time_launches(kstep, args.steps, args.warmup)
+        kms = ktot / args.steps
+        kkern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evk[args.warmup:]]))
+        kfl = state_kernel_flops_per_token_head(64, dk, dv) * token_heads
+        kby = (prefill_bytes(token_heads, B * H, dk, dv, 2, 2, gate_floats=dk)
+               + n_chunk_heads * 2 * T_RECORD_BYTES)
+        out["kda"] = {"workload": "per-key-channel gate prefill, B=4 T=4096 H=16 dk=dv=128, bf16 "
+                                  "q/k/v and o, fp32 g [T, H, dk] and state, FP8-E4M3 state QDQ "
+                                  "at every boundary",
+                      "ms_per_step": round(kms, 5), "tokens_per_s": round(tokens / (kms * 1e-3), 1),
+                      "state_kernel": {"kernel": "kda_fwd_kernel<128, EngBF16, bf16, bf16>",
+                                       "avg_launch_ms": round(kkern, 5),
+                                       "mfma_tflops": round(kfl / (kkern * 1e-3) / 1e12, 2),
+                                       "mfma_frac": round(kfl / (kkern * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                       "hbm_gbs": round(kby / (kkern * 1e-3) / 1e9, 1),
+                                       "algorithmic_bytes_per_launch": kby}}
+        del dk_
+        torch.cuda.empty_cache()
 
     # ---------------- prefill -> decode handoff workload ----------------
     if not args.no_decode:

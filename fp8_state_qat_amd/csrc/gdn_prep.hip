@@ -315,13 +315,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
 //     A[r][s] = beta_r sum_c k_rc k_sc exp(gamma_rc - gamma_sc)      (s < r)
 //     P[r][s] = sum_c q_rc k_sc exp(gamma_rc - gamma_sc)             (s <= r)
 //     T       = (I + A)^-1 diag(beta)
-// No exp(-gamma) is formed on its own (it overflows).  For 16-token blocks
-// R > S the last token m of block S is a reference point:
-// exp(gamma_r - gamma_s) = exp(gamma_r - gamma_m) exp(gamma_m - gamma_s), both
-// factors <= 1 for non-positive gates, so those blocks are fp32 MFMA products
-// of pre-scaled operands.  The four diagonal 16 x 16 blocks are summed
-// channel by channel with the exponential of each difference.  T and P are
-// written as two records per (chunk, head) in the layout above.
+// No exp(-gamma) is formed on its own (it overflows).  Each 16 x 16 tile
+// (R, S) is an fp32 MFMA product of operands scaled to a reference token m
+// of block R: exp(gamma_r - gamma_s) = exp(gamma_r - gamma_m)
+// exp(gamma_m - gamma_s), both factors <= 1 for non-positive gates when S < R;
+// on the diagonal tiles the factors stay within a guard band or the tile is
+// summed channel by channel from the differences.  T and P are written as
+// two records per (chunk, head) in the layout above.
 // ---------------------------------------------------------------------------
 template <int DK, typename TIO>
 struct KdaPrepLds {
@@ -393,7 +393,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
     constexpr int SPR = DK / EPS;
     const TIO* gk = reinterpret_cast<const TIO*>(a.k);
     const TIO* gqv = reinterpret_cast<const TIO*>(a.q);
-    for (int seg = tid; seg < 64 * SPR; seg += kThreads) {
+    static_assert(64 * SPR % kThreads == 0, "staging geometry");
+#pragma unroll
+    for (int jj = 0; jj < 64 * SPR / kThreads; ++jj) {
+      const int seg = tid + kThreads * jj;
       const int r = seg / SPR, c0 = (seg % SPR) * EPS;
       uint4 kv = make_uint4(0u, 0u, 0u, 0u), qv = make_uint4(0u, 0u, 0u, 0u);
       if (r < nv) {
@@ -409,10 +412,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   constexpr int NPART = kThreads / DK, TPP = 64 / NPART;  // token parts of the per-channel scan
   {
     const int d = tid % DK, part = tid / DK;
+    float gv[TPP];  // all loads in flight before the scan
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+      const int r = part * TPP + i;
+      gv[i] = (r < nv) ? a.g[((int64_t)(t0 + r) * H + h) * DK + d] : 0.f;
+    }
     float run = 0.f;
-    for (int r = part * TPP; r < (part + 1) * TPP; ++r) {
-      run += (r < nv) ? a.g[((int64_t)(t0 + r) * H + h) * DK + d] : 0.f;
-      sG[r * LG + d] = run;
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+      run += gv[i];
+      sG[(part * TPP + i) * LG + d] = run;
     }
     sTot[tid] = run;
   }
@@ -421,18 +431,29 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
     const int d = tid % DK, part = tid / DK;
     float off = 0.f;
     for (int pp = 0; pp < part; ++pp) off += sTot[pp * DK + d];
-    for (int r = part * TPP; r < (part + 1) * TPP; ++r) sG[r * LG + d] = (sG[r * LG + d] + off) * 1.4426950408889634f;
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+      const int r = part * TPP + i;
+      sG[r * LG + d] = (sG[r * LG + d] + off) * 1.4426950408889634f;
+    }
   }
   __syncthreads();
 
-  // ---- blocks R > S, pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): C[s][r] with
-  // A = k_s exp(gamma_m - gamma_s), B = x_r exp(gamma_r - gamma_m), m = 16 S + 15
-  for (int pr = w; pr < 6; pr += 4) {
-    const int R = (pr < 1) ? 1 : (pr < 3) ? 2 : 3;
-    const int S = pr - (R * (R - 1)) / 2;
-    const int m = 16 * S + 15;
-    const int s = 16 * S + ln, r = 16 * R + ln;
+  // ---- the ten 16 x 16 tiles (R, S), S <= R, one job each: C[s][r] with
+  // A = k_s exp(gamma_m - gamma_s), B = x_r exp(gamma_r - gamma_m) (x = k for
+  // A, q for P), m = 16 R the first token of block R.  For S < R both factors
+  // are <= 1.  On the diagonal tile the first factor is >= 1: it is used only
+  // when every |gamma_t - gamma_m| of the block stays under 2^kGuard in
+  // magnitude (no overflow, no underflow), else that tile is summed channel
+  // by channel with the exponential of each difference.
+  constexpr float kGuard = 100.f;  // log2 units
+  for (int job = w; job < 10; job += 4) {
+    const int R = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
+    const int S = job - (R * (R + 1)) / 2;
+    const int m = 16 * R;
+    const int s = 16 * S + ln, r = 16 * R + ln;  // A-operand row s, B-operand column r of this lane
     f32x4 ca = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
+    float span = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float av[8], bk[8], bq[8];
@@ -451,8 +472,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
         load4f(sQ + r * LX + c0, qr);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          av[4 * hh + i] = ks[i] * __builtin_amdgcn_exp2f(gm[i] - gs[i]);
-          const float f = __builtin_amdgcn_exp2f(gr[i] - gm[i]);
+          span = fmaxf(span, fmaxf(fabsf(gm[i] - gs[i]), fabsf(gr[i] - gm[i])));
+          av[4 * hh + i] = ks[i] * __builtin_amdgcn_exp2f(fminf(gm[i] - gs[i], kGuard));
+          const float f = __builtin_amdgcn_exp2f(fminf(gr[i] - gm[i], kGuard));
           bk[4 * hh + i] = kr[i] * f;
           bq[4 * hh + i] = qr[i] * f;
         }
@@ -460,43 +482,48 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
       mma_f32(ca, av, bk);
       mma_f32(cp, av, bq);
     }
-    // lane holds C[16 S + 4 gq + i][16 R + ln]
-    const float br = sBeta[r];
-    *reinterpret_cast<float4*>(sA + r * L64 + 16 * S + 4 * gq) =
-        make_float4(br * ca[0], br * ca[1], br * ca[2], br * ca[3]);
-    *reinterpret_cast<float4*>(sP + r * L64 + 16 * S + 4 * gq) = make_float4(cp[0], cp[1], cp[2], cp[3]);
-  }
-
-  // ---- diagonal blocks: pairs s <= r inside each 16-token block, channel by channel
-  for (int pi = tid; pi < 4 * 136; pi += kThreads) {
-    const int b = pi / 136, idx = pi - 136 * b;
-    int rl = 0;
-    while ((rl + 1) * (rl + 2) / 2 <= idx) ++rl;  // idx = rl (rl + 1) / 2 + sl
-    const int sl = idx - rl * (rl + 1) / 2;
-    const int r = 16 * b + rl, s = 16 * b + sl;
-    float sa[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < DK; c0 += 4) {
-      float kr[4], qr[4], ks[4];
-      load4f(sK + r * LX + c0, kr);
-      load4f(sQ + r * LX + c0, qr);
-      load4f(sK + s * LX + c0, ks);
-      const float4 gr4 = *reinterpret_cast<const float4*>(sG + r * LG + c0);
-      const float4 gs4 = *reinterpret_cast<const float4*>(sG + s * LG + c0);
-      const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
-      const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+    const bool exact = (S < R) || wave_max_dpp(span) < kGuard;
+    if (exact) {
+      // lane holds C[16 S + 4 gq + i][16 R + ln]; zero at and above the diagonal (A), above it (P)
+      const float br = sBeta[r];
+      float va[4], vp[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ke = ks[i] * __builtin_amdgcn_exp2f(gr[i] - gs[i]);
-        sa[i] = fmaf(kr[i], ke, sa[i]);
-        sp[i] = fmaf(qr[i], ke, sp[i]);
+        const int sc = 16 * S + 4 * gq + i;
+        va[i] = (sc < r) ? br * ca[i] : 0.f;
+        vp[i] = (sc <= r) ? cp[i] : 0.f;
       }
-    }
-    const float av = (sa[0] + sa[1]) + (sa[2] + sa[3]);
-    const float pv = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-    sP[r * L64 + s] = pv;
-    if (sl < rl) {
-      sA[r * L64 + s] = sBeta[r] * av;
-      sP[s * L64 + r] = 0.f;  // above the diagonal
+      *reinterpret_cast<float4*>(sA + r * L64 + 16 * S + 4 * gq) = make_float4(va[0], va[1], va[2], va[3]);
+      *reinterpret_cast<float4*>(sP + r * L64 + 16 * S + 4 * gq) = make_float4(vp[0], vp[1], vp[2], vp[3]);
+    } else {
+      // diagonal tile with a large in-block decay: pairs s <= r, channel by channel
+      for (int pi = lane; pi < 256; pi += 64) {
+        const int rl = pi >> 4, sl = pi & 15;
+        const int rr = 16 * R + rl, ss = 16 * R + sl;
+        float sa[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
+        if (sl <= rl) {
+          for (int c0 = 0; c0 < DK; c0 += 4) {
+            float kr[4], qr[4], ks[4];
+            load4f(sK + rr * LX + c0, kr);
+            load4f(sQ + rr * LX + c0, qr);
+            load4f(sK + ss * LX + c0, ks);
+            const float4 gr4 = *reinterpret_cast<const float4*>(sG + rr * LG + c0);
+            const float4 gs4 = *reinterpret_cast<const float4*>(sG + ss * LG + c0);
+            const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+            const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float ke = ks[i] * __builtin_amdgcn_exp2f(gr[i] - gs[i]);
+              sa[i] = fmaf(kr[i], ke, sa[i]);
+              sp[i] = fmaf(qr[i], ke, sp[i]);
+            }
+          }
+        }
+        const float av = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+        const float pv = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+        sA[rr * L64 + ss] = (sl < rl) ? sBeta[rr] * av : 0.f;
+        sP[rr * L64 + ss] = (sl <= rl) ? pv : 0.f;
+      }
     }
   }
   __syncthreads();

@@ -70,6 +70,19 @@ def test_kda_strong_gates_fp32():
     check_g1(w, gpu, run_chunk_oracle(w, 0), TOL[gi.F32])
 
 
+def test_kda_in_block_decay_beyond_guard_fp32():
+    """Gates of ~-6 per token: the decay across one 16-token block passes the
+    prep kernel's guard band, so its diagonal tiles take the per-channel path
+    (exponentials of differences only) while the off-diagonal tiles stay on
+    the scaled-operand MFMA path."""
+    w = _kda([192, 77], 2, 64, 64, gi.F32, seed=71, g_scale=8.0)
+    gpu = run_chunk_gpu(w, 0)
+    assert np.all(np.isfinite(gpu["o"])) and np.all(np.isfinite(gpu["S"]))
+    check_g1(w, gpu, run_chunk_oracle(w, 0), TOL[gi.F32])
+    wb = _kda([192, 77], 2, 128, 128, gi.BF16, seed=73, g_scale=8.0)
+    check_g1(wb, run_chunk_gpu(wb, 0, o_dtype="f32"), run_chunk_oracle(wb, 0), TOL[gi.BF16])
+
+
 def test_kda_varlen_padding_is_isolated():
     w = _kda([70, 0, 5, 130, 64], 2, 128, 128, gi.BF16, seed=53, pads=[3, 4, 0, 61, 1],
              pad_fill=np.nan)
