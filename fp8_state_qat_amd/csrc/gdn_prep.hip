@@ -11,7 +11,8 @@
 //
 // The solve is blocked on 16 x 16 blocks in fp32: the four diagonal blocks
 // by forward substitution (one lane per column), then the off-diagonal
-// blocks level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.
+// blocks level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, on the fp32
+// MFMA.
 //
 // Workspace layout: int32 chunk offsets [N + 1] (prefix sums of
 // ceil(P_n / 64)), padded to 256 bytes, then one 12 KiB record per (chunk,
@@ -79,78 +80,64 @@ struct PrepArgs {
   int H;
 };
 
-__device__ __forceinline__ float dot4p(const float4 a, const float4 b) {
-  return fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, a.w * b.w)));
-}
-__device__ __forceinline__ float dot16p(const float* a, const float* b) {
-  const float4* a4 = reinterpret_cast<const float4*>(a);
-  const float4* b4 = reinterpret_cast<const float4*>(b);
-  return (dot4p(a4[0], b4[0]) + dot4p(a4[1], b4[1])) + (dot4p(a4[2], b4[2]) + dot4p(a4[3], b4[3]));
-}
-
 // Row stride (floats) of the 64 x 64 fp32 LDS matrices of the prep kernels.
 constexpr int kL64 = 64 + 4;
 
 // X = (I + A)^-1 for the strictly lower A in sA (only the block-lower 16 x 16
-// blocks are read), 256 threads: the four diagonal blocks by forward
-// substitution (one lane per column), then the off-diagonal blocks level by
-// level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj.  sX receives X row-major
-// (block-lower part; the diagonal blocks carry zeros above their diagonal),
-// sXT its transpose; sRT is scratch.  Contains barriers.
-__device__ __forceinline__ void solve_unit_lower(const float* sA, float* sX, float* sXT, float* sRT) {
+// blocks are read), 256 threads.  sX receives X row-major (block-lower part;
+// the diagonal blocks carry zeros above their diagonal).  Contains barriers.
+//   diagonal blocks: forward substitution, wave 0, one lane per (block, column)
+//   X_ij (i > j), level by level (i - j = 1, 2, 3), one wave per block:
+//       X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj
+//   on the fp32 MFMA (16x16x4).  Instruction q of a 16-deep product takes
+//   k = 4 (l / 16) + q from lane l, so the accumulator of the sum (lane l
+//   holds rows 4 (l / 16) .. + 3 of column l % 16) is the B operand of the
+//   product with X_ii as it stands.
+__device__ __forceinline__ void solve_unit_lower(const float* sA, float* sX) {
   constexpr int L64 = kL64;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // ---- diagonal blocks of X = (I + A)^-1: lane = (block, column), column-oriented
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
   if (w == 0) {
-    const int bi = lane >> 4, cc = lane & 15;
+    const int bi = gq, cc = ln;
     const float* Ab = sA + 16 * bi * L64 + 16 * bi;
-    float am[16][16];
-#pragma unroll
-    for (int r = 1; r < 16; ++r)
-#pragma unroll
-      for (int q4 = 0; q4 * 4 < r; ++q4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(Ab + r * L64 + 4 * q4);
-        am[r][4 * q4] = v4.x; am[r][4 * q4 + 1] = v4.y; am[r][4 * q4 + 2] = v4.z; am[r][4 * q4 + 3] = v4.w;
-      }
     float xc[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xc[r] = (r == cc) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
+      for (int q4 = 0; q4 * 4 < r; ++q4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(Ab + r * L64 + 4 * q4);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-      for (int r = s + 1; r < 16; ++r) xc[r] = fmaf(-am[r][s], xc[s], xc[r]);
+        for (int i = 0; i < 4; ++i)
+          if (4 * q4 + i < r) acc = fmaf(-av[i], xc[4 * q4 + i], acc);
+      }
+      xc[r] = acc;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) sX[(16 * bi + r) * L64 + 16 * bi + cc] = xc[r];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<float4*>(sXT + (16 * bi + cc) * L64 + 16 * bi + 4 * q4) =
-          make_float4(xc[4 * q4], xc[4 * q4 + 1], xc[4 * q4 + 2], xc[4 * q4 + 3]);
   }
   __syncthreads();
-  // ---- off-diagonal blocks, level by level
-  {
-    const int r = tid >> 4, cc = tid & 15;
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
+  for (int d = 1; d < 4; ++d) {
+    if (w + d < 4) {
+      const int i = w + d, j = w;
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b + d < 4; ++b) {
-        const int i = d + b, jb = b;
-        float acc = 0.f;
+      for (int kb = j; kb < i; ++kb)
 #pragma unroll
-        for (int kk = jb; kk < i; ++kk)
-          acc += dot16p(sA + (16 * i + r) * L64 + 16 * kk, sXT + (16 * jb + cc) * L64 + 16 * kk);
-        sRT[b * 256 + cc * 16 + r] = acc;
-      }
-      __syncthreads();
+        for (int q = 0; q < 4; ++q) {
+          const float av = sA[(16 * i + ln) * L64 + 16 * kb + 4 * gq + q];
+          const float bv = sX[(16 * kb + 4 * gq + q) * L64 + 16 * j + ln];
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, y, 0, 0, 0);
+        }
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b + d < 4; ++b) {
-        const int i = d + b, jb = b;
-        const float xv = -dot16p(sX + (16 * i + r) * L64 + 16 * i, sRT + b * 256 + cc * 16);
-        sX[(16 * i + r) * L64 + 16 * jb + cc] = xv;
-        sXT[(16 * jb + cc) * L64 + 16 * i + r] = xv;
-      }
-      __syncthreads();
+      for (int q = 0; q < 4; ++q)
+        x = __builtin_amdgcn_mfma_f32_16x16x4f32(sX[(16 * i + ln) * L64 + 16 * i + 4 * gq + q], y[q], x, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sX[(16 * i + 4 * gq + r) * L64 + 16 * j + ln] = -x[r];
     }
+    __syncthreads();
   }
 }
 
@@ -196,17 +183,17 @@ __device__ __forceinline__ void store_record(const float* M, const float* colsca
 
 // One workgroup (4 waves) per (chunk, head).  TIO: uint16_t (bf16) or float.
 template <int DK, typename TIO>
-__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
   constexpr bool kBF = sizeof(TIO) == 2;
   constexpr int L64 = kL64;
   constexpr int LDK = DK + 16 / (int)sizeof(TIO);  // K row stride (elements), 16-byte rows
   constexpr int NKB = DK / 32;
-  __shared__ __align__(16) TIO sK[64 * LDK];
+  constexpr int KX = (64 * LDK * (int)sizeof(TIO) > 64 * L64 * 4) ? 64 * LDK * (int)sizeof(TIO) : 64 * L64 * 4;
+  __shared__ __align__(16) char sKX[KX];  // K, then (once A is formed) the solve's X
   __shared__ __align__(16) float sA[64 * L64];
-  __shared__ __align__(16) float sX[64 * L64];
-  __shared__ __align__(16) float sXT[64 * L64];
-  __shared__ __align__(16) float sRT[3 * 256];
   __shared__ float sG2[64], sBeta[64];
+  TIO* sK = reinterpret_cast<TIO*>(sKX);
+  float* sX = reinterpret_cast<float*>(sKX);
 
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
@@ -303,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  solve_unit_lower(sA, sX, sXT, sRT);
+  solve_unit_lower(sA, sX);
   store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes);
 }
 
@@ -332,14 +319,12 @@ struct KdaPrepLds {
   static constexpr size_t oG = oQ + 64 * LX * sizeof(TIO);
   static constexpr size_t oA = oG + 64 * LG * sizeof(float);
   static constexpr size_t oP = oA + 64 * kL64 * sizeof(float);
-  static constexpr size_t oRT = oP + 64 * kL64 * sizeof(float);
-  static constexpr size_t oTot = oRT + 3 * 256 * sizeof(float);
+  static constexpr size_t oTot = oP + 64 * kL64 * sizeof(float);
   static constexpr size_t oBeta = oTot + kThreads * sizeof(float);
   static constexpr size_t bytes = oBeta + 64 * sizeof(float);
-  // once A and P are formed, the solve's X overlays k and q, X^T overlays gamma
-  static constexpr size_t oX = oK, oXT = oG;
+  // once A and P are formed, the solve's X overlays k and q
+  static constexpr size_t oX = oK;
   static_assert(64 * kL64 * sizeof(float) <= oG - oK, "X does not fit over k and q");
-  static_assert(64 * kL64 * sizeof(float) <= oA - oG, "X^T does not fit over gamma");
 };
 
 template <typename TIO>
@@ -364,11 +349,9 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   float* sG = reinterpret_cast<float*>(smem + Ls::oG);    // gamma * log2(e)
   float* sA = reinterpret_cast<float*>(smem + Ls::oA);
   float* sP = reinterpret_cast<float*>(smem + Ls::oP);
-  float* sRT = reinterpret_cast<float*>(smem + Ls::oRT);
   float* sTot = reinterpret_cast<float*>(smem + Ls::oTot);
   float* sBeta = reinterpret_cast<float*>(smem + Ls::oBeta);
   float* sX = reinterpret_cast<float*>(smem + Ls::oX);
-  float* sXT = reinterpret_cast<float*>(smem + Ls::oXT);
 
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
@@ -530,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
 
   const int64_t rec = ((int64_t)j * H + h) * kTRecBytes;
   store_record<kBF>(sP, nullptr, reinterpret_cast<char*>(a.P) + rec);
-  solve_unit_lower(sA, sX, sXT, sRT);
+  solve_unit_lower(sA, sX);
   store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + rec);
 }
 
