@@ -130,8 +130,7 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape) {
   g_err[0] = 0;
   if (check_shape(shape, false) != GDN_OK) return 0;
-  return gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens,
-                                   shape->gate_per_channel != 0);
+  return gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
 }
 
 gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
@@ -143,8 +142,7 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   g_err[0] = 0;
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
-  const size_t need = gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens,
-                                                shape->gate_per_channel != 0);
+  const size_t need = gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL");

@@ -8,26 +8,29 @@
 // tile vt).  It walks its sequence chunk by chunk and keeps its slice of the
 // state in registers for the whole sequence.  The 64 x dk state tile is
 // exactly one QDQ tile, so the QDQ amax needs no exchange with other
-// workgroups.  T = (I + A)^-1 diag(beta) of every chunk comes from the prep
-// kernel (gdn_prep.hip) through the workspace.
+// workgroups.  T and P of every chunk come from the prep kernel
+// (gdn_prep.hip) through the workspace.
 //
 // Waves 0..3 ("chain" waves) carry the state: chain wave c owns value columns
 // 16c..16c+15 of the tile, i.e. dk/16 16x16 accumulator tiles of S^T, and
 // runs everything that depends on the state.  Waves 4..7 ("helper" waves)
-// stage the next chunk into LDS, form P and produce the outputs, so each SIMD
-// runs one wave of each kind and the two overlap.  With gamma the in-chunk
-// cumulative log-gate and s the scale of the state entering the chunk (1
-// when it is not coded), one chunk of n <= 64 tokens (rows past n are zero)
-// goes through three phases separated by workgroup barriers:
+// produce the outputs and stage the next chunk, so each SIMD runs one wave of
+// each kind and the two overlap.  With gamma the in-chunk cumulative log-gate
+// and s the scale of the state entering the chunk (1 when it is not coded),
+// one chunk of n <= 64 tokens (rows past n are zero) goes through three
+// phases separated by workgroup barriers:
 //
 //   1a  chain : X = V - s exp(gamma) * (K S^T), U' = T X            (MFMA)
-//       helper: P[r][s] = exp(gamma_r - gamma_s) q_r . k_s (s <= r)  (MFMA)
+//       helper: s exp(gamma) * (Q S^T), from the state the chain left in LDS
 //   1b  chain : S^T <- exp(gamma_C) S^T + K^T diag(exp(gamma_C - gamma)) U'
 //               and the tile amax
-//       helper: O = s exp(gamma) * (Q S^T) + P U', stored to o
+//       helper: O += P U', stored to o
 //   2   chain : QDQ: s = amax / 448, S <- RNE_E4M3(S / s) s
-//       helper: the next chunk's q, k, v, T and gates registers -> LDS,
-//               gate scan, and the global loads of the chunk after it
+//       helper: the gate scan of the next chunk
+// T = (I + A)^-1 diag(beta) and P[r][s] = exp(gamma_r - gamma_s) q_r . k_s
+// (s <= r) come from the prep kernel as records; the next chunk's k and q
+// (double-buffered), v, T and P arrive by direct global->LDS loads issued as
+// soon as their buffers are free.
 //
 // U' = T X is U - W S^T with U = T V and W = T (exp(gamma) * K) regrouped, so
 // W is never formed.  Then the recurrent suffix (tokens P_n < t <= L_n, QDQ
@@ -64,10 +67,10 @@ constexpr int kHelperThreads = 256;  // waves 4..7
 //                  fragments from K with transpose reads)
 //   V   [64][64 + 16 bytes]  the tile's v rows, row-major, padded rows
 //   T   [plane][p] 6 fragments per plane (the prep kernel's record, copied as is)
-//   P   [plane][p] 6 fragments per plane, same pairs as T
+//   P   [plane][p] the prep kernel's P record, same layout
 //   XU  [c][plane*2 + kb]     U' as the A operand of U'^T P^T, per chain wave
 //   XS  [c][plane*NKB + kb]   the state as the A operand of S Q^T, per chain wave
-//   vec gamma*log2(e), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
+//   vec (unused), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
 //   red the four chain waves' amax
 template <int DK, class Eng>
 struct Lds {
@@ -261,6 +264,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const int64_t row0 = seg0 + cc * kChunk;
     load_dump(gq_ + row0 * qk_row + (int64_t)h * DK, qdst, nv, hw);
   };
+  auto issue_p = [&](int cc, E* pdst) {  // the P record of chunk cc
+    const char* rec = reinterpret_cast<const char*>(args.Prec) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
+#pragma unroll
+    for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
+      const int idx = hw * (kTRecBytes / 1024 / 4) + ii;
+      lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), reinterpret_cast<char*>(pdst) + idx * 1024);
+    }
+  };
   float pg = 0.f;  // helper wave 0: log-gate of token `lane` of the next chunk
   auto fetch_g = [&](int cc) {
     const int nv = min(kChunk, P - cc * kChunk);
@@ -271,7 +282,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const int nv = min(kChunk, P - cc * kChunk);
     const float x = wave_prefix_sum((lane < nv) ? pg : 0.f);
     const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-    vecb[lane] = x * kLog2e;
     vecb[64 + lane] = __builtin_amdgcn_exp2f(x * kLog2e);
     vecb[128 + lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
     if (lane == 0) vecb[192] = __builtin_amdgcn_exp2f(gC * kLog2e);
@@ -316,6 +326,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       issue_v(0, sV, sT);
     } else {
       issue_q(0, sQ);
+      issue_p(0, sP);
       if (hw == 0) fetch_g(0);
     }
     wait_vmem();
@@ -330,7 +341,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
                   E* __restrict__ qn, E* __restrict__ tb, E* __restrict__ vb, E* __restrict__ pb,
                   E* __restrict__ xu, E* __restrict__ xs, E* __restrict__ kt, float* __restrict__ vec,
                   float* __restrict__ red) {
-    float* gg2 = vec;         // gamma * log2(e)
     float* geg = vec + 64;    // exp(gamma)
     float* gegc = vec + 128;  // exp(gamma_C - gamma)
     float* gmisc = vec + 192; // [0] exp(gamma_C), [1] scale of the state entering the chunk
@@ -342,6 +352,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const bool last = (c == n_chunks - 1);
     const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
 
+    f32x4 oacc[4];  // helper waves: O^T of this chunk, phase 1a -> 1b
     // ======== phase 1a ========
     if (chain) {
       if (c + 1 < n_chunks) issue_k(c + 1, kn);  // the other k buffer
@@ -417,41 +428,33 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if (hw == 0) fetch_g(c + 1);
       }
       transform(kc, kt);
-      // P tiles: C[s][t] = k_s . q_t -> P[t][s] (s <= t), 10 lower tiles + 2
-      // zero tiles that complete the fragment pairs; 3 per helper wave
+      // O^T[v][t] = s exp(gamma_t) (S Q^T)[v][t] + (U'^T P^T)[v][t], v in block c4;
+      // the first term here (XS holds the state entering the chunk), the second in phase 1b
+      const float sc = coded_in ? gmisc[1] : 1.0f;
 #pragma unroll
-      for (int jj = 0; jj < 3; ++jj) {
-        const int job = hw + 4 * jj;
-        int ti, si;
-        if (job < 10) {
-          ti = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
-          si = job - (ti * (ti + 1)) / 2;
-        } else {
-          si = (job == 10) ? 1 : 3;
-          ti = si - 1;
+      for (int ti = 0; ti < 4; ++ti) oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const Fr sa = Eng::ld(slot(xs, c4 * NP * NKB + kb));
+        Fr sb;
+        if (two) sb = Eng::ld(slot(xs, c4 * NP * NKB + NKB + kb));
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          const Fr bq = Eng::ld(qslot(qc, ti * NKB + kb));
+          Eng::mma(oacc[ti], sa, bq);
+          if (two) Eng::mma(oacc[ti], sb, bq);
         }
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (job < 10) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-            Eng::mma(acc, Eng::ld(qslot(kc, si * NKB + kb)), Eng::ld(qslot(qc, ti * NKB + kb)));
-          const int t = 16 * ti + ln;
-          const float g2t = gg2[t];
-          const float4 g2s = *reinterpret_cast<const float4*>(gg2 + 16 * si + 4 * gq);
-          const float gs[4] = {g2s.x, g2s.y, g2s.z, g2s.w};
+      for (int ti = 0; ti < 4; ++ti) {
+        const float egt = sc * geg[16 * ti + ln];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            x[i] = (16 * si + 4 * gq + i <= t) ? __builtin_amdgcn_exp2f(g2t - gs[i]) * acc[i] : 0.f;
-        }
-        const int pr = (si >= 2) ? ti + 2 : ti, jb = (si & 1) * 4;
-        Eng::st4_split(slot(pb, pr) + jb, slot(pb, 6 + pr) + jb, x);
+        for (int i = 0; i < 4; ++i) oacc[ti][i] *= egt;
       }
     }
     barrier_lds();
 
     // ======== phase 1b ========
-    f32x4 oacc[4];  // helper waves: O^T of this chunk, phase 1b -> 2
     if (chain) {
       if (c + 1 < n_chunks) issue_v(c + 1, vb, tb);  // v and T were last read in phase 1a
       // S^T <- exp(gamma_C) S^T + K^T (exp(gamma_C - gamma) * U')
@@ -510,29 +513,38 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if (lane == 0) red[c4] = amax;
       }
     } else {
-      // O^T[v][t] = s exp(gamma_t) (S Q^T)[v][t] + (U'^T P^T)[v][t], v in block c4;
-      // the first term here, the second in phase 2
-      const float sc = coded_in ? gmisc[1] : 1.0f;
+      Fr uh[2], ul[2];
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb) {
+        uh[kb] = Eng::ld(slot(xu, c4 * 2 * NP + kb));
+        if constexpr (kSplit) ul[kb] = Eng::ld(slot(xu, c4 * 2 * NP + 2 + kb));
+      }
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const Fr sa = Eng::ld(slot(xs, c4 * NP * NKB + kb));
-        Fr sb;
-        if (two) sb = Eng::ld(slot(xs, c4 * NP * NKB + NKB + kb));
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const Fr bq = Eng::ld(qslot(qc, ti * NKB + kb));
-          Eng::mma(oacc[ti], sa, bq);
-          if (two) Eng::mma(oacc[ti], sb, bq);
+      for (int p = 0; p < 6; ++p) {
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        const Fr ph = Eng::ld(slot(pb, p));
+        Eng::mma(oacc[ti], uh[kb], ph);
+        if constexpr (kSplit) {
+          const Fr pl = Eng::ld(slot(pb, 6 + p));
+          Eng::mma(oacc[ti], ul[kb], ph);
+          Eng::mma(oacc[ti], uh[kb], pl);
         }
       }
+      // lane holds o[tok = 16ti + ln][16c4 + 4gq .. +3] of this tile
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const float egt = sc * geg[16 * ti + ln];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[ti][i] *= egt;
+        const int tok = 16 * ti + ln;
+        if (tok < nv) {
+          TO* dst = go_ + (int64_t)(t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + 16 * c4 + 4 * gq;
+          if constexpr (sizeof(TO) == 2) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(oacc[ti][0], oacc[ti][1]),
+                                                        pack_bf16x2(oacc[ti][2], oacc[ti][3]));
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(oacc[ti][0], oacc[ti][1], oacc[ti][2], oacc[ti][3]);
+          }
+        }
       }
+      if (c + 1 < n_chunks) issue_p(c + 1, pb);  // P of this chunk has been read
     }
     barrier_lds();
 
@@ -579,37 +591,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
       wait_vmem();  // this wave's loads are in LDS before the barrier
     } else {
-      Fr uh[2], ul[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        uh[kb] = Eng::ld(slot(xu, c4 * 2 * NP + kb));
-        if constexpr (kSplit) ul[kb] = Eng::ld(slot(xu, c4 * 2 * NP + 2 + kb));
-      }
-#pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        const Fr ph = Eng::ld(slot(pb, p));
-        Eng::mma(oacc[ti], uh[kb], ph);
-        if constexpr (kSplit) {
-          const Fr pl = Eng::ld(slot(pb, 6 + p));
-          Eng::mma(oacc[ti], ul[kb], ph);
-          Eng::mma(oacc[ti], uh[kb], pl);
-        }
-      }
-      // lane holds o[tok = 16ti + ln][16c4 + 4gq .. +3] of this tile
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        const int tok = 16 * ti + ln;
-        if (tok < nv) {
-          TO* dst = go_ + (int64_t)(t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + 16 * c4 + 4 * gq;
-          if constexpr (sizeof(TO) == 2) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(oacc[ti][0], oacc[ti][1]),
-                                                        pack_bf16x2(oacc[ti][2], oacc[ti][3]));
-          } else {
-            *reinterpret_cast<float4*>(dst) = make_float4(oacc[ti][0], oacc[ti][1], oacc[ti][2], oacc[ti][3]);
-          }
-        }
-      }
       if (c + 1 < n_chunks && hw == 0) scan(c + 1, vec);  // gates of the next chunk
       wait_vmem();  // this wave's loads are in LDS before the barrier
     }

@@ -22,15 +22,15 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             const float* initial_state, void* o, float* final_state,
                             void* workspace, const gdn_debug_t* debug, hipStream_t stream);
 
-// One T record per (chunk, head): T = (I + A)^-1 diag(beta) in MFMA
-// A-fragment order (see gdn_prep.hip), 12 KiB for both engines.  The
-// per-key-channel gate adds one P record of the same layout.
+// Two records per (chunk, head): T = (I + A)^-1 diag(beta) and the decayed,
+// masked P = Q K^T, each in MFMA fragment order (see gdn_prep.hip), 12 KiB
+// for both engines.
 constexpr int kTRecBytes = 12288;
 
-// Bytes of the chunk workspace: chunk offsets [N + 1] (padded to 256 bytes)
-// and one T record (two records -- T, then P -- with a per-key-channel gate)
-// per (chunk, head) for the worst-case chunk count ceil(total_tokens / 64) + N.
-size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens, bool per_channel);
+// Bytes of the chunk workspace: chunk offsets [N + 1] (padded to 256 bytes),
+// then the T records and the P records for the worst-case chunk count
+// ceil(total_tokens / 64) + N.
+size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens);
 
 hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                        const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,

@@ -6,8 +6,9 @@
 //     gamma_r = sum_{s<=r} g_s                                (in-chunk scan)
 //     A[r][s] = beta_r exp(gamma_r - gamma_s) k_r . k_s       (s < r)
 //     T       = (I + A)^-1 diag(beta)                         (exact solve)
-// T is written to the workspace for the sequential kernel, which forms
-// U' = T (V - exp(gamma) * K S^T) from it.
+//     P[t][s] = exp(gamma_t - gamma_s) q_t . k_s              (s <= t)
+// T and P are written to the workspace for the sequential kernel, which forms
+// U' = T (V - exp(gamma) * K S^T) and O = exp(gamma) * Q S^T + P U' from them.
 //
 // The solve is blocked on 16 x 16 blocks in fp32: the four diagonal blocks
 // by forward substitution (one lane per column), then the off-diagonal
@@ -15,15 +16,17 @@
 // MFMA.
 //
 // Workspace layout: int32 chunk offsets [N + 1] (prefix sums of
-// ceil(P_n / 64)), padded to 256 bytes, then one 12 KiB record per (chunk,
-// head) holding the six nonzero 16 x 32 A-operand fragments of the block
-// lower-triangular T, pair p = (ti, kb) in (0,0) (1,0) (2,0) (3,0) (2,1)
-// (3,1): lane l of fragment p holds T[16 ti + l % 16][32 kb + kperm(l / 16, j)]
-// for j = 0..7 (kperm as in gdn_device.hpp), fragments stored one after the
-// other, lane-major.  bf16 inputs store hi = bf16(T) (six fragments) then
-// lo = bf16(T - hi) (six more); fp32 inputs store T in fp32.  The sequential
-// kernel copies the record into LDS unchanged and reads each fragment with
-// one lane-linear load.
+// ceil(P_n / 64)), padded to 256 bytes, then one 12 KiB T record per (chunk,
+// head), then one P record per (chunk, head) of the same layout.  A record
+// holds the six nonzero 16 x 32 fragments of a block lower-triangular 64 x 64
+// matrix M, pair p = (ti, kb) in (0,0) (1,0) (2,0) (3,0) (2,1) (3,1): lane l
+// of fragment p holds M[16 ti + l % 16][32 kb + kperm(l / 16, j)] for
+// j = 0..7 (kperm as in gdn_device.hpp), fragments stored one after the
+// other, lane-major.  bf16 inputs store hi = bf16(M) (six fragments) then
+// lo = bf16(M - hi) (six more); fp32 inputs store M in fp32.  The sequential
+// kernels copy a record into LDS unchanged and read each fragment with one
+// lane-linear load (T as the A operand of T X, P as the B operand of
+// U'^T P^T).
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -189,7 +192,8 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
   constexpr int LDK = DK + 16 / (int)sizeof(TIO);  // K row stride (elements), 16-byte rows
   constexpr int NKB = DK / 32;
   constexpr int KX = (64 * LDK * (int)sizeof(TIO) > 64 * L64 * 4) ? 64 * LDK * (int)sizeof(TIO) : 64 * L64 * 4;
-  __shared__ __align__(16) char sKX[KX];  // K, then (once A is formed) the solve's X
+  __shared__ __align__(16) char sKX[KX];  // K, then (once A and P are formed) the solve's X
+  __shared__ __align__(16) TIO sQ[64 * LDK];
   __shared__ __align__(16) float sA[64 * L64];
   __shared__ float sG2[64], sBeta[64];
   TIO* sK = reinterpret_cast<TIO*>(sKX);
@@ -214,18 +218,24 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
 
-  // ---- stage K (rows past nv are zero), gates
+  // ---- stage K and Q (rows past nv are zero), gates
   {
     constexpr int EPS = 16 / (int)sizeof(TIO);
     constexpr int SPR = DK / EPS;
     const TIO* gk = reinterpret_cast<const TIO*>(a.k);
+    const TIO* gqv = reinterpret_cast<const TIO*>(a.q);
 #pragma unroll
     for (int jj = 0; jj < 64 * SPR / kThreads; ++jj) {
       const int seg = tid + kThreads * jj;
       const int r = seg / SPR, c0 = (seg % SPR) * EPS;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nv) v = *reinterpret_cast<const uint4*>(gk + ((int64_t)(t0 + r) * H + h) * DK + c0);
-      *reinterpret_cast<uint4*>(sK + r * LDK + c0) = v;
+      uint4 kv = make_uint4(0u, 0u, 0u, 0u), qv = make_uint4(0u, 0u, 0u, 0u);
+      if (r < nv) {
+        const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c0;
+        kv = *reinterpret_cast<const uint4*>(gk + off);
+        qv = *reinterpret_cast<const uint4*>(gqv + off);
+      }
+      *reinterpret_cast<uint4*>(sK + r * LDK + c0) = kv;
+      *reinterpret_cast<uint4*>(sQ + r * LDK + c0) = qv;
     }
     if (w == 0) {
       float gv = 0.f, bv = 0.f;
@@ -244,13 +254,9 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // ---- A = beta_r exp(gamma_r - gamma_s) K K^T, strictly lower; 10 tiles over 4 waves
-  for (int job = w; job < 10; job += 4) {
-    const int ri = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
-    const int si = job - (ri * (ri + 1)) / 2;
+  // C[s][t] = x_s . y_t for one 16 x 16 tile (rows 16 si.., 16 ti..): lane holds s = 16 si + 4 gq + i, t = 16 ti + ln
+  auto tile = [&](const TIO* arow, const TIO* brow) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const TIO* arow = sK + (16 * si + ln) * LDK;
-    const TIO* brow = sK + (16 * ri + ln) * LDK;
     if constexpr (kBF) {
       bf16x8 af[NKB], bf[NKB];
 #pragma unroll
@@ -277,16 +283,53 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
         mma_f32(acc, av, bv);
       }
     }
-    // acc[i] = k_s . k_r with s = 16 si + 4 gq + i, r = 16 ri + ln
-    const int r = 16 * ri + ln;
-    const float g2r = sG2[r], br = sBeta[r];
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = 16 * si + 4 * gq + i;
-      v[i] = (s < r) ? br * __builtin_amdgcn_exp2f(g2r - sG2[s]) * acc[i] : 0.f;
+    return acc;
+  };
+  // ---- ten tile jobs (ri, si), si <= ri, at most 3 per wave: with C_A = K K^T
+  // and C_P = K Q^T on the tile (one shared A operand, the k rows of block si)
+  //   A[r][s] = beta_r exp(gamma_r - gamma_s) C_A[s][r]    (s < r)   -> sA
+  //   P[r][s] = exp(gamma_r - gamma_s) C_P[s][r]           (s <= r)  -> the P record
+  // plus the two zero P tiles (0,1) and (2,3) that complete fragment pairs.
+  char* prec = reinterpret_cast<char*>(a.P) + ((int64_t)j * H + h) * kTRecBytes;
+  auto put_p = [&](int ri, int si, const float (&v)[4]) {
+    // record slot: pair pr = (ri, si / 2), lane l, elements 4 (si % 2) .. + 3
+    const int pr = (si >= 2) ? ri + 2 : ri, jb = (si & 1) * 4;
+    if constexpr (kBF) {
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(v[0], v[1], h0, l0);
+      split_bf16x2(v[2], v[3], h1, l1);
+      *reinterpret_cast<uint2*>(prec + (pr * 64 + lane) * 16 + jb * 2) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(prec + ((6 + pr) * 64 + lane) * 16 + jb * 2) = make_uint2(l0, l1);
+    } else {
+      *reinterpret_cast<float4*>(prec + (pr * 64 + lane) * 32 + jb * 4) = make_float4(v[0], v[1], v[2], v[3]);
     }
-    *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) = make_float4(v[0], v[1], v[2], v[3]);
+  };
+#pragma unroll
+  for (int jj = 0; jj < 3; ++jj) {
+    const int job = w + 4 * jj;
+    if (job < 10) {
+      const int ri = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
+      const int si = job - (ri * (ri + 1)) / 2;
+      const int r = 16 * ri + ln;
+      const TIO* arow = sK + (16 * si + ln) * LDK;
+      const f32x4 ca = tile(arow, sK + r * LDK);
+      const f32x4 cp = tile(arow, sQ + r * LDK);
+      const float g2r = sG2[r], br = sBeta[r];
+      float va[4], vp[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * si + 4 * gq + i;
+        const float e = (s <= r) ? __builtin_amdgcn_exp2f(g2r - sG2[s]) : 0.f;
+        va[i] = (s < r) ? br * e * ca[i] : 0.f;
+        vp[i] = e * cp[i];
+      }
+      *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) = make_float4(va[0], va[1], va[2], va[3]);
+      put_p(ri, si, vp);
+    } else if (job < 12) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      const int si = (job == 10) ? 1 : 3;
+      put_p(si - 1, si, z);
+    }
   }
   __syncthreads();
 
@@ -517,10 +560,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + rec);
 }
 
-size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens, bool per_channel) {
+size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens) {
   const int64_t max_chunks = (total_tokens + kChunk - 1) / kChunk + n_seqs;
   const size_t offs = ((size_t)(n_seqs + 1) * 4 + 255) / 256 * 256;
-  return offs + (size_t)max_chunks * n_heads * kTRecBytes * (per_channel ? 2 : 1);
+  return offs + (size_t)max_chunks * n_heads * kTRecBytes * 2;
 }
 
 template <int DK, typename TIO>
@@ -546,7 +589,7 @@ hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const
   const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
   const int64_t blocks = max_chunks * s.n_heads;
   void* T = reinterpret_cast<char*>(workspace) + offs_bytes;
-  void* Prec = s.gate_per_channel ? reinterpret_cast<char*>(T) + (size_t)blocks * kTRecBytes : nullptr;
+  void* Prec = reinterpret_cast<char*>(T) + (size_t)blocks * kTRecBytes;
   *offs_out = offs;
   *T_out = T;
   *P_out = Prec;

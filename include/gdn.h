@@ -128,10 +128,10 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape,
 
 /*
  * gdn_chunk_fwd_workspace_bytes -- bytes of device workspace gdn_chunk_fwd
- * needs for this shape: the per-chunk solve T = (I + A)^-1 diag(beta) of
- * every (chunk, head) (12 KiB each, for the worst-case chunk count
- * ceil(total_tokens / 64) + n_seqs) plus the chunk offsets.  Returns 0 for an
- * invalid shape (gdn_last_error() says why).
+ * needs for this shape: the per-chunk solve T = (I + A)^-1 diag(beta) and the
+ * decayed, masked P = Q K^T of every (chunk, head) (12 KiB each, for the
+ * worst-case chunk count ceil(total_tokens / 64) + n_seqs) plus the chunk
+ * offsets.  Returns 0 for an invalid shape (gdn_last_error() says why).
  */
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape);
 

@@ -85,14 +85,13 @@ def test_chunk_fwd_rejects_null_and_misaligned():
 
 
 def test_workspace_size_and_checks():
-    """Workspace: worst-case chunk count ceil(T/64) + N records of 12 KiB per
-    head (two records, T and P, with a per-key-channel gate) plus the chunk
-    offsets; too small, NULL or misaligned is rejected."""
+    """Workspace: for the worst-case chunk count ceil(T/64) + N, two records
+    of 12 KiB (T and P) per chunk and head, plus the chunk offsets; too
+    small, NULL or misaligned is rejected."""
     s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
     n = _ws(s)
-    assert n == 256 + (3 + 3) * 2 * 12288
-    assert _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, gate_per_channel=1)) == \
-        256 + (3 + 3) * 2 * 2 * 12288
+    assert n == 256 + (3 + 3) * 2 * 2 * 12288
+    assert _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, gate_per_channel=1)) == n
     assert _ws(_shape(dv=96)) == 0 and _lib.last_error()
     assert _chunk(s, ws_bytes=n - 1) == 1
     assert _chunk(s, ws=0) == 1
