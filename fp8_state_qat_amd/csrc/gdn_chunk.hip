@@ -116,6 +116,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   float* sG2 = reinterpret_cast<float*>(smem + Ls::oVec);  // gamma * log2(e)
   float* sRed = reinterpret_cast<float*>(smem + Ls::oRed);
 
+  const uint32_t lds0 = lds_base_u32(smem);
+  auto lds_of = [&](const void* p) { return lds0 + (uint32_t)(reinterpret_cast<const char*>(p) - smem); };
   const int tid = threadIdx.x;
   const int w = tid >> 6;        // wave
   const int lane = tid & 63;
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       const int r = 16 * (f / NKB) + (l2 & 15);
       const int d = 32 * (f % NKB) + 8 * (l2 >> 4) + part * EPP;
       lds_load16(src, (uint32_t)((min(r, nv - 1) * (int)qk_row + d) * (int)sizeof(E)),
-                 reinterpret_cast<char*>(dst) + i * 1024);
+                 lds_of(dst) + i * 1024);
     }
   };
   auto load_rows = [&](const TIO* src, int stride, E* dst, int nv, int wi) {  // padded v rows
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       const int r = i * RPI + rr;
       if (i < NI && rr < RPI && r < 64)
         lds_load16(src, (uint32_t)((min(r, nv - 1) * stride + lane_off) * (int)sizeof(E)),
-                   dst + i * RPI * (PPV + 1) * EPP);
+                   lds_of(dst) + i * RPI * (PPV + 1) * EPP * (int)sizeof(E));
     }
   };
   // Loads of chunk cc, by buffer lifetime: k and q have two buffers (chunk
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
     for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
       const int idx = c4 * (kTRecBytes / 1024 / 4) + ii;
-      lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), reinterpret_cast<char*>(tdst) + idx * 1024);
+      lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(tdst) + idx * 1024);
     }
   };
   auto issue_q = [&](int cc, E* qdst) {
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
     for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
       const int idx = hw * (kTRecBytes / 1024 / 4) + ii;
-      lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), reinterpret_cast<char*>(pdst) + idx * 1024);
+      lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(pdst) + idx * 1024);
     }
   };
   float pg = 0.f;  // helper wave 0: log-gate of token `lane` of the next chunk

@@ -18,12 +18,13 @@ struct Frag8 {
 
 // Direct global -> LDS copy: lane l of the wave writes the 16 bytes at
 // base + off (base the same in every lane, off this lane's byte offset) to
-// dst + 16 l; dst must be the same in every lane.  Issued from inline
-// assembly so that the compiler does not hold later LDS accesses of the wave
-// behind it: the kernel orders these copies itself, with wait_vmem() before
-// the barrier that publishes them.  M0 (the LDS base of the copy) is restored.
-__device__ __forceinline__ void lds_load16(const void* base, uint32_t off, void* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+// LDS byte address lds + 16 l; lds must be the same in every lane.  Issued
+// from inline assembly so that the compiler does not hold later LDS accesses
+// of the wave behind it: the kernel orders these copies itself, with
+// wait_vmem() before the barrier that publishes them.  M0 (the LDS base of
+// the copy) is restored.
+__device__ __forceinline__ void lds_load16(const void* base, uint32_t off, uint32_t lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
   // readfirstlane returns int: widen each half through uint32_t (no sign extension)
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)base);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)base >> 32));
@@ -36,8 +37,15 @@ __device__ __forceinline__ void lds_load16(const void* base, uint32_t off, void*
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(off), "s"(sb), "s"(lds)
+      : "v"(off), "s"(sb), "s"(m)
       : "memory");
+}
+// LDS byte address of a pointer into the dynamic LDS block that starts at
+// smem, from the block's own address (one cast per kernel, the rest is
+// uniform integer arithmetic).
+__device__ __forceinline__ uint32_t lds_base_u32(const char* smem) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)smem);
 }
 // Wait until this wave's outstanding vector memory operations (including
 // direct LDS loads) have completed.

@@ -106,6 +106,8 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   float* sEC = reinterpret_cast<float*>(smem + Ls::oEC);
   float* sRed = reinterpret_cast<float*>(smem + Ls::oRed);
 
+  const uint32_t lds0 = lds_base_u32(smem);
+  auto lds_of = [&](const void* p) { return lds0 + (uint32_t)(reinterpret_cast<const char*>(p) - smem); };
   const int tid = threadIdx.x;
   const int w = uniform(tid >> 6);  // wave = value block of 16 rows
   const int lane = tid & 63;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
         const int r = i * RPI + rr;
         if (i < NI && rr < RPI && r < 64)
           lds_load16(src, (uint32_t)((min(r, nv - 1) * (int)v_row + lane_off) * (int)sizeof(E)),
-                     sV + i * RPI * (PPV + 1) * EPP);
+                     lds_of(sV) + i * RPI * (PPV + 1) * EPP * (int)sizeof(E));
       }
     }
     const int64_t rec = ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
@@ -307,8 +309,8 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
 #pragma unroll
     for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
       const int idx = w * (kTRecBytes / 1024 / 4) + ii;
-      lds_load16(trec, (uint32_t)((idx * 64 + lane) * 16), reinterpret_cast<char*>(sT) + idx * 1024);
-      lds_load16(prec, (uint32_t)((idx * 64 + lane) * 16), reinterpret_cast<char*>(sP) + idx * 1024);
+      lds_load16(trec, (uint32_t)((idx * 64 + lane) * 16), lds_of(sT) + idx * 1024);
+      lds_load16(prec, (uint32_t)((idx * 64 + lane) * 16), lds_of(sP) + idx * 1024);
     }
   };
 
