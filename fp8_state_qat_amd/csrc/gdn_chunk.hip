@@ -245,19 +245,19 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   // T (one buffer each) at the start of phase 1b, once phase 1a has read
   // them.  Chain waves load k, v and T, helper waves q; helper wave 0 fetches
   // the log-gates into a register.
-  auto issue_k = [&](int cc, E* kdst) {
+  auto issue_k = [&](int cc, E* kdst, int wi) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
-    load_dump(gk_ + row0 * qk_row + (int64_t)h * DK, kdst, nv, c4);
+    load_dump(gk_ + row0 * qk_row + (int64_t)h * DK, kdst, nv, wi);
   };
-  auto issue_v = [&](int cc, E* vdst, E* tdst) {
+  auto issue_v = [&](int cc, E* vdst, E* tdst, int wi) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
-    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, (int)v_row, vdst, nv, c4);
+    load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, (int)v_row, vdst, nv, wi);
     const char* rec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
 #pragma unroll
     for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
-      const int idx = c4 * (kTRecBytes / 1024 / 4) + ii;
+      const int idx = wi * (kTRecBytes / 1024 / 4) + ii;
       lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(tdst) + idx * 1024);
     }
   };
@@ -324,11 +324,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   }
   if (n_chunks > 0) {
     if (chain) {
-      issue_k(0, sK);
-      issue_v(0, sV, sT);
+      issue_k(0, sK, c4);
+      issue_v(0, sV, sT, c4);
     } else {
       issue_q(0, sQ);
       issue_p(0, sP);
+      if (n_chunks > 1) issue_k(1, sK + 64 * DK, hw);
       if (hw == 0) fetch_g(0);
     }
     wait_vmem();
@@ -357,7 +358,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     f32x4 oacc[4];  // helper waves: O^T of this chunk, phase 1a -> 1b
     // ======== phase 1a ========
     if (chain) {
-      if (c + 1 < n_chunks) issue_k(c + 1, kn);  // the other k buffer
       // K S^T: A = K rows (tokens), B = the state
       const float sc = coded_in ? s_cur : 1.0f;
       f32x4 acc[4];
@@ -458,7 +458,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 
     // ======== phase 1b ========
     if (chain) {
-      if (c + 1 < n_chunks) issue_v(c + 1, vb, tb);  // v and T were last read in phase 1a
       // S^T <- exp(gamma_C) S^T + K^T (exp(gamma_C - gamma) * U')
       Fr bh[2], bl[2];
 #pragma unroll
@@ -546,7 +545,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           }
         }
       }
-      if (c + 1 < n_chunks) issue_p(c + 1, pb);  // P of this chunk has been read
+      if (c + 1 < n_chunks) {
+        issue_p(c + 1, pb);      // P of this chunk has been read
+        issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
+      }
     }
     barrier_lds();
 
@@ -591,10 +593,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
                                      dkmap(16 * t + 4 * gq)) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
       }
       if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
-      wait_vmem();  // this wave's loads are in LDS before the barrier
     } else {
       if (c + 1 < n_chunks && hw == 0) scan(c + 1, vec);  // gates of the next chunk
-      wait_vmem();  // this wave's loads are in LDS before the barrier
+      wait_vmem();  // this wave's loads (k of the next chunk included) are in LDS before the barrier
+      if (c + 2 < n_chunks) issue_k(c + 2, kc, hw);  // k of this chunk has been read
     }
     barrier_lds();
   };
