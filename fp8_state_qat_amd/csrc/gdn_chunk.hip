@@ -178,6 +178,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   f32x4 st[NT];
   Fr sh[NKB];            // after a chunk QDQ: the codes as the MFMA operand (bf16 engine)
   float s_cur = 1.0f;    // scale of the coded state
+  bool st_coded = false; // bf16 engine after a chunk QDQ: st holds the E4M3 codes, the state is st * s_cur
   f32x4 uacc[4];         // U'[16tt + 4gq + i][vcol0], phase 1a -> 1b
 
   // uncoded state -> operand fragments: hi + lo (bf16 engine) / exact fp32
@@ -470,11 +471,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
                              e1.w * uacc[2 * kb + 1][3]};
         Eng::split(u8, bh[kb], bl[kb]);
       }
-      const float aC = gmisc[0];
+      const float aC = st_coded ? gmisc[0] * s_cur : gmisc[0];  // decay, and the scale of a coded state
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[t][i] *= aC;
+      st_coded = false;
+      // all K^T fragments first, so that the transpose reads overlap
+      Fr ka0[NT], ka1[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         Fr a0, a1;
@@ -490,6 +494,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           a0 = Eng::ld(slot(kt, 2 * t));
           a1 = Eng::ld(slot(kt, 2 * t + 1));
         }
+        ka0[t] = a0;
+        ka1[t] = a1;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const Fr a0 = ka0[t], a1 = ka1[t];
         Eng::mma(st[t], a0, bh[0]);
         Eng::mma(st[t], a1, bh[1]);
         if constexpr (kSplit) {
@@ -562,14 +572,21 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           float c0[4], c1[4];
-          qdq4c(st[2 * kb], c0, s_new, r);
-          qdq4c(st[2 * kb + 1], c1, s_new, r);
           if constexpr (kSplit) {
+            // keep the codes; the scale is folded into the next decay multiply
+            e4m3_codes4(st[2 * kb], s_new, r, c0);
+            e4m3_codes4(st[2 * kb + 1], s_new, r, c1);
+            st[2 * kb] = f32x4{c0[0], c0[1], c0[2], c0[3]};
+            st[2 * kb + 1] = f32x4{c1[0], c1[1], c1[2], c1[3]};
             const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
             sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
+          } else {
+            qdq4c(st[2 * kb], c0, s_new, r);
+            qdq4c(st[2 * kb + 1], c1, s_new, r);
           }
         }
         s_cur = s_new;
+        st_coded = kSplit;
       }
       if (!last) {
         if (kSplit && do_qdq) {
@@ -587,10 +604,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       }
       const int bidx = bound0 + c;
       if (args.bound_post) {
+        const float f = st_coded ? s_cur : 1.0f;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
-                                     dkmap(16 * t + 4 * gq)) = make_float4(st[t][0], st[t][1], st[t][2], st[t][3]);
+                                     dkmap(16 * t + 4 * gq)) = make_float4(st[t][0] * f, st[t][1] * f,
+                                                                           st[t][2] * f, st[t][3] * f);
       }
       if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
     } else {
@@ -608,6 +627,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     E* q1 = sQ + 64 * DK;
     step(c, odd ? k1 : k0, odd ? k0 : k1, odd ? q1 : q0, odd ? q0 : q1, sT, sV, sP, sXU, sXS,
          Eng::kTrRead ? nullptr : sKT, sG2, sRed);
+  }
+
+  if (st_coded) {  // back to the state values: code * s
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[t][i] *= s_cur;
+    st_coded = false;
   }
 
   // ---------------- recurrent suffix, tokens P < t <= L ----------------

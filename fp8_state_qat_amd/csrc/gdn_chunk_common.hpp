@@ -40,6 +40,22 @@ __device__ __forceinline__ void lds_load16(const void* base, uint32_t off, uint3
       : "v"(off), "s"(sb), "s"(m)
       : "memory");
 }
+// E4M3 codes of four state values at scale s (r = RN(1 / s)), as floats:
+// the correctly rounded quotient x / s (div_rn) converted to the nearest
+// OCP E4M3FN value, ties to even, by v_cvt_pk_fp8_f32, and back two at a
+// time.  The conversion keeps the sign of values that round to zero (-0),
+// so code * s has the sign of x without a copysign.
+__device__ __forceinline__ void e4m3_codes4(const f32x4& x, float s, float r, float (&c)[4]) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn(x[0], s, r), div_rn(x[1], s, r), 0, false);
+  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn(x[2], s, r), div_rn(x[3], s, r), lo, true);
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(p, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(p, true);
+  c[0] = a[0];
+  c[1] = a[1];
+  c[2] = b[0];
+  c[3] = b[1];
+}
+
 // LDS byte address of a pointer into the dynamic LDS block that starts at
 // smem, from the block's own address (one cast per kernel, the rest is
 // uniform integer arithmetic).
