@@ -27,8 +27,7 @@
 // kernels copy a record into LDS unchanged and read each fragment with one
 // lane-linear load (T as the A operand of T X, P as the B operand of
 // U'^T P^T).
-#include "gdn_device.hpp"
-#include "gdn_launch.hpp"
+#include "gdn_chunk_common.hpp"
 
 namespace gdn {
 
@@ -189,15 +188,25 @@ template <int DK, typename TIO>
 __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
   constexpr bool kBF = sizeof(TIO) == 2;
   constexpr int L64 = kL64;
-  constexpr int LDK = DK + 16 / (int)sizeof(TIO);  // K row stride (elements), 16-byte rows
   constexpr int NKB = DK / 32;
-  constexpr int KX = (64 * LDK * (int)sizeof(TIO) > 64 * L64 * 4) ? 64 * LDK * (int)sizeof(TIO) : 64 * L64 * 4;
-  __shared__ __align__(16) char sKX[KX];  // K, then (once A and P are formed) the solve's X
-  __shared__ __align__(16) TIO sQ[64 * LDK];
+  // k and q rows unpadded, 16-byte pieces XOR-swizzled by row (piece p of row r
+  // at slot p ^ (r % PPR)), so that direct loads fill them 1 KiB at a time and
+  // the fragment reads of 16 rows at one column hit different banks
+  constexpr int RB = DK * (int)sizeof(TIO);  // bytes per row
+  constexpr int PPR = RB / 16;               // pieces per row
+  constexpr int KQ = 2 * 64 * RB;
+  constexpr int KX = (KQ > 64 * L64 * 4) ? KQ : 64 * L64 * 4;
+  __shared__ __align__(16) char sKX[KX];  // k, q, then (once A and P are formed) the solve's X
   __shared__ __align__(16) float sA[64 * L64];
   __shared__ float sG2[64], sBeta[64];
-  TIO* sK = reinterpret_cast<TIO*>(sKX);
+  const char* sK = sKX;
+  const char* sQ = sKX + 64 * RB;
   float* sX = reinterpret_cast<float*>(sKX);
+  // byte address of element c of row r in the k or q block
+  auto kq_at = [](int r, int c) {
+    const int p = c * (int)sizeof(TIO) / 16, within = c * (int)sizeof(TIO) % 16;
+    return r * RB + ((p ^ (r & (PPR - 1))) * 16) + within;
+  };
 
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
@@ -218,24 +227,22 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
 
-  // ---- stage K and Q (rows past nv are zero), gates
+  // ---- stage K and Q by direct loads (rows past nv repeat the last valid row:
+  // beta is zero there, which zeroes those rows of A and columns of T, and P
+  // rows past nv only reach outputs that are not stored), gates
   {
-    constexpr int EPS = 16 / (int)sizeof(TIO);
-    constexpr int SPR = DK / EPS;
-    const TIO* gk = reinterpret_cast<const TIO*>(a.k);
-    const TIO* gqv = reinterpret_cast<const TIO*>(a.q);
+    const uint32_t lds0 = lds_base_u32(sKX);
+    const TIO* gk = reinterpret_cast<const TIO*>(a.k) + ((int64_t)t0 * H + h) * DK;
+    const TIO* gqv = reinterpret_cast<const TIO*>(a.q) + ((int64_t)t0 * H + h) * DK;
+    constexpr int NI = 64 * RB / 1024;  // instructions per block
+    static_assert(NI % 4 == 0, "staging geometry");
 #pragma unroll
-    for (int jj = 0; jj < 64 * SPR / kThreads; ++jj) {
-      const int seg = tid + kThreads * jj;
-      const int r = seg / SPR, c0 = (seg % SPR) * EPS;
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u), qv = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nv) {
-        const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c0;
-        kv = *reinterpret_cast<const uint4*>(gk + off);
-        qv = *reinterpret_cast<const uint4*>(gqv + off);
-      }
-      *reinterpret_cast<uint4*>(sK + r * LDK + c0) = kv;
-      *reinterpret_cast<uint4*>(sQ + r * LDK + c0) = qv;
+    for (int ii = 0; ii < NI / 4; ++ii) {
+      const int i = uniform(w) + 4 * ii;
+      const int u = i * 64 + lane, r = u / PPR, p = (u % PPR) ^ (r & (PPR - 1));
+      const uint32_t off = (uint32_t)((min(r, nv - 1) * H * DK) * (int)sizeof(TIO) + p * 16);
+      lds_load16(gk, off, lds0 + i * 1024);
+      lds_load16(gqv, off, lds0 + 64 * RB + i * 1024);
     }
     if (w == 0) {
       float gv = 0.f, bv = 0.f;
@@ -251,20 +258,21 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
       sG2[lane] = gv * 1.4426950408889634f;
       sBeta[lane] = bv;
     }
+    wait_vmem();
   }
   __syncthreads();
 
-  // C[s][t] = x_s . y_t for one 16 x 16 tile (rows 16 si.., 16 ti..): lane holds s = 16 si + 4 gq + i, t = 16 ti + ln
-  auto tile = [&](const TIO* arow, const TIO* brow) {
+  // C[s][t] = x_s . y_t for one 16 x 16 tile (rows sr of x, tr of y): lane holds s = 16 si + 4 gq + i, t = 16 ti + ln
+  auto tile = [&](const char* xb, int sr, const char* yb, int tr) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBF) {
       bf16x8 af[NKB], bf[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const uint2 a0 = *reinterpret_cast<const uint2*>(arow + 32 * kb + 4 * gq);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(arow + 32 * kb + 16 + 4 * gq);
-        const uint2 b0 = *reinterpret_cast<const uint2*>(brow + 32 * kb + 4 * gq);
-        const uint2 b1 = *reinterpret_cast<const uint2*>(brow + 32 * kb + 16 + 4 * gq);
+        const uint2 a0 = *reinterpret_cast<const uint2*>(xb + kq_at(sr, 32 * kb + 4 * gq));
+        const uint2 a1 = *reinterpret_cast<const uint2*>(xb + kq_at(sr, 32 * kb + 16 + 4 * gq));
+        const uint2 b0 = *reinterpret_cast<const uint2*>(yb + kq_at(tr, 32 * kb + 4 * gq));
+        const uint2 b1 = *reinterpret_cast<const uint2*>(yb + kq_at(tr, 32 * kb + 16 + 4 * gq));
         af[kb] = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
         bf[kb] = __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y));
       }
@@ -274,10 +282,10 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float av[8], bv[8];
-        const float4 a0 = *reinterpret_cast<const float4*>(arow + 32 * kb + 4 * gq);
-        const float4 a1 = *reinterpret_cast<const float4*>(arow + 32 * kb + 16 + 4 * gq);
-        const float4 b0 = *reinterpret_cast<const float4*>(brow + 32 * kb + 4 * gq);
-        const float4 b1 = *reinterpret_cast<const float4*>(brow + 32 * kb + 16 + 4 * gq);
+        const float4 a0 = *reinterpret_cast<const float4*>(xb + kq_at(sr, 32 * kb + 4 * gq));
+        const float4 a1 = *reinterpret_cast<const float4*>(xb + kq_at(sr, 32 * kb + 16 + 4 * gq));
+        const float4 b0 = *reinterpret_cast<const float4*>(yb + kq_at(tr, 32 * kb + 4 * gq));
+        const float4 b1 = *reinterpret_cast<const float4*>(yb + kq_at(tr, 32 * kb + 16 + 4 * gq));
         av[0] = a0.x; av[1] = a0.y; av[2] = a0.z; av[3] = a0.w; av[4] = a1.x; av[5] = a1.y; av[6] = a1.z; av[7] = a1.w;
         bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w; bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
         mma_f32(acc, av, bv);
@@ -311,9 +319,8 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
       const int ri = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
       const int si = job - (ri * (ri + 1)) / 2;
       const int r = 16 * ri + ln;
-      const TIO* arow = sK + (16 * si + ln) * LDK;
-      const f32x4 ca = tile(arow, sK + r * LDK);
-      const f32x4 cp = tile(arow, sQ + r * LDK);
+      const f32x4 ca = tile(sK, 16 * si + ln, sK, r);
+      const f32x4 cp = tile(sK, 16 * si + ln, sQ, r);
       const float g2r = sG2[r], br = sBeta[r];
       float va[4], vp[4];
 #pragma unroll
