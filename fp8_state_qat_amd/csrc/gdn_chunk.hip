@@ -60,14 +60,14 @@ constexpr int kHelperThreads = 256;  // waves 4..7
 //   K   2 x [tt][kb]  dump, double-buffered by chunk parity: lane l holds
 //                  k[16tt + l%16][32kb + 8(l/16) .. +7] in slot rot_slot(l);
 //                  A of K S^T, A of P, K^T by transpose reads   4 NKB fragments
-//   Q   2 x [tt][kb]  the same for q, double-buffered by chunk parity; B of
-//                  P, B of S Q^T
+//   Q   [tt][kb]   the same for q (read in phase 1a only); B of S Q^T
 //   KT  [dt][kb]   dump: A of the state update (row = state row), 2 NT
 //                  fragments (fp32 engine; the bf16 engine reads these
 //                  fragments from K with transpose reads)
 //   V   [64][64 + 16 bytes]  the tile's v rows, row-major, padded rows
 //   T   [plane][p] 6 fragments per plane (the prep kernel's record, copied as is)
-//   P   [plane][p] the prep kernel's P record, same layout
+//   P   2 x [plane][p]  the prep kernel's P record, same layout, double-buffered
+//                  by chunk parity
 //   XU  [c][plane*2 + kb]     U' as the A operand of U'^T P^T, per chain wave
 //   XS  [c][plane*NKB + kb]   the state as the A operand of S Q^T, per chain wave
 //   vec (unused), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
@@ -80,11 +80,11 @@ struct Lds {
   static constexpr size_t RV = 64 * sizeof(E) + 16;    // padded v row (bytes)
   static constexpr size_t oK = 0;                      // 2 buffers by chunk parity
   static constexpr size_t oQ = oK + 2 * 4 * NKB * F;   // 2 buffers by chunk parity
-  static constexpr size_t oKT = oQ + 2 * 4 * NKB * F;
+  static constexpr size_t oKT = oQ + 4 * NKB * F;
   static constexpr size_t oV = oKT + (Eng::kTrRead ? 0 : 2 * NT * F);
   static constexpr size_t oT = oV + 64 * RV;
   static constexpr size_t oP = oT + 6 * NP * F;
-  static constexpr size_t oXU = oP + 6 * NP * F;
+  static constexpr size_t oXU = oP + 2 * 6 * NP * F;  // 2 buffers by chunk parity
   static constexpr size_t oXS = oXU + 4 * 2 * NP * F;
   static constexpr size_t oVec = oXS + 4 * NKB * NP * F;
   static constexpr size_t oRed = oVec + (3 * 64 + 8) * sizeof(float);
@@ -341,9 +341,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   // One chunk.  Every LDS buffer it touches arrives as a __restrict__
   // pointer, so the compiler can tell the buffers apart and does not hold LDS
   // reads behind the direct loads in flight into other buffers.
-  auto step = [&](const int c, E* __restrict__ kc, E* __restrict__ kn, E* __restrict__ qc,
-                  E* __restrict__ qn, E* __restrict__ tb, E* __restrict__ vb, E* __restrict__ pb,
-                  E* __restrict__ xu, E* __restrict__ xs, E* __restrict__ kt, float* __restrict__ vec,
+  auto step = [&](const int c, E* __restrict__ kc, E* __restrict__ qc, E* __restrict__ tb,
+                  E* __restrict__ vb, E* __restrict__ pb, E* __restrict__ pn, E* __restrict__ xu,
+                  E* __restrict__ xs, E* __restrict__ kt, float* __restrict__ vec,
                   float* __restrict__ red) {
     float* geg = vec + 64;    // exp(gamma)
     float* gegc = vec + 128;  // exp(gamma_C - gamma)
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       }
     } else {
       if (c + 1 < n_chunks) {
-        issue_q(c + 1, qn);  // the other q buffer
+        issue_p(c + 1, pn);  // the other P buffer
         if (hw == 0) fetch_g(c + 1);
       }
       transform(kc, kt);
@@ -524,6 +524,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if (lane == 0) red[c4] = amax;
       }
     } else {
+      if (c + 1 < n_chunks) {
+        issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
+        issue_q(c + 1, qc);          // and q
+      }
       Fr uh[2], ul[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -554,10 +558,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
             *reinterpret_cast<float4*>(dst) = make_float4(oacc[ti][0], oacc[ti][1], oacc[ti][2], oacc[ti][3]);
           }
         }
-      }
-      if (c + 1 < n_chunks) {
-        issue_p(c + 1, pb);      // P of this chunk has been read
-        issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
       }
     }
     barrier_lds();
@@ -623,9 +623,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const bool odd = c & 1;
     E* k0 = sK;
     E* k1 = sK + 64 * DK;
-    E* q0 = sQ;
-    E* q1 = sQ + 64 * DK;
-    step(c, odd ? k1 : k0, odd ? k0 : k1, odd ? q1 : q0, odd ? q0 : q1, sT, sV, sP, sXU, sXS,
+    E* p0 = sP;
+    E* p1 = sP + 6 * NP * 64 * 8;
+    step(c, odd ? k1 : k0, sQ, sT, sV, odd ? p1 : p0, odd ? p0 : p1, sXU, sXS,
          Eng::kTrRead ? nullptr : sKT, sG2, sRed);
   }
 
