@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-T_RECORD_BYTES = 12288         # per (chunk, head): T = (I + A)^-1 diag(beta), hi + lo bf16 planes
+T_RECORD_BYTES = 12288         # per (chunk, head) and record: T = (I + A)^-1 diag(beta), and P; hi + lo bf16 planes
 BF16_MFMA_PEAK_TFLOPS = 2516.6 # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "GDN chunked-prefill tokens/s + MFMA %peak; decode step HBM GB/s, 1×MI355X"
 
@@ -60,8 +60,9 @@ def prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes, gate_floats=1):
 
 def state_kernel_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes, o_bytes):
     """Algorithmic HBM bytes of the sequential state kernel: the prefill bytes
-    plus one read of the per-chunk solve (12 KiB per chunk and head)."""
-    return prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes) + n_chunk_heads * T_RECORD_BYTES
+    plus one read of the two per-chunk records the prep kernel writes (T and
+    P, 12 KiB each per chunk and head)."""
+    return prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes) + n_chunk_heads * 2 * T_RECORD_BYTES
 
 
 def decode_bytes(n_heads_seqs, dk, dv, io_bytes, o_bytes):
@@ -251,7 +252,7 @@ def main():
         kkern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evk[args.warmup:]]))
         kfl = state_kernel_flops_per_token_head(64, dk, dv) * token_heads
         kby = (prefill_bytes(token_heads, B * H, dk, dv, 2, 2, gate_floats=dk)
-               + n_chunk_heads * 2 * T_RECORD_BYTES)
+               + n_chunk_heads * 2 * T_RECORD_BYTES)  # T and P records
         out["kda"] = {"workload": "per-key-channel gate prefill, B=4 T=4096 H=16 dk=dv=128, bf16 "
                                   "q/k/v and o, fp32 g [T, H, dk] and state, FP8-E4M3 state QDQ "
                                   "at every boundary",
