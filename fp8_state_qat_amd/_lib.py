@@ -21,6 +21,10 @@ GDN_BF16 = 1
 GDN_QDQ_CHUNK = 1
 GDN_QDQ_WRITE = 2
 
+GDN_SCHEDULE_AUTO = 0
+GDN_SCHEDULE_SPLIT = 1
+GDN_SCHEDULE_FUSED = 2
+
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_state_qdq", "gdn_decode_step",
            "gdn_status_string", "gdn_last_error")
 
@@ -47,6 +51,7 @@ class GdnDebug(ctypes.Structure):
         ("scales", ctypes.c_void_p),
         ("kernel_start", ctypes.c_void_p),
         ("kernel_end", ctypes.c_void_p),
+        ("schedule", ctypes.c_int32),
     ]
 
 

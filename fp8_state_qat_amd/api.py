@@ -56,9 +56,11 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     [T, H] fp32; g: [T, H] or [T, H, dk] fp32; cu_seqlens: [N+1] int32.
     workspace: optional uint8 device tensor of chunk_workspace_bytes(...)
     bytes (allocated here when None).  debug: optional dict with device
-    tensors bound_offsets, bound_pre, bound_post, scales and/or
-    torch.cuda.Event objects kernel_start, kernel_end (recorded around the
-    sequential state kernel).  Returns (o, final_state)."""
+    tensors bound_offsets, bound_pre, bound_post, scales, torch.cuda.Event
+    objects kernel_start, kernel_end (recorded around the sequential state
+    kernel) and/or schedule (GDN_SCHEDULE_AUTO, _SPLIT or _FUSED: the
+    per-chunk solve as its own kernel or inside the state kernel's launch).
+    Returns (o, final_state)."""
     T, H, dk = k.shape
     dv = v.shape[2]
     N = cu_seqlens.numel() - 1
@@ -92,7 +94,8 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
                 ev.record()  # torch creates its HIP event on first record
             evs.append(None if ev is None else ctypes.c_void_p(ev.cuda_event))
         dbg = GdnDebug(*(_ptr(debug.get(key)) for key in ("bound_offsets", "bound_pre",
-                                                          "bound_post", "scales")), *evs)
+                                                          "bound_post", "scales")), *evs,
+                       int(debug.get("schedule", _lib.GDN_SCHEDULE_AUTO)))
     st = _lib.lib().gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                   _ptr(g), _ptr(cu_seqlens), _ptr(seq_lens), _ptr(prefix_lens),
                                   _ptr(initial_state), _ptr(out), _ptr(final_state),

@@ -47,7 +47,7 @@
 // fed as the codes and the products are scaled by s; otherwise (QDQ off, a
 // supplied initial state) as a hi + lo pair.  fp32 inputs use the fp32 MFMA
 // throughout.
-#include "gdn_chunk_common.hpp"
+#include "gdn_prep_item.hpp"
 
 namespace gdn {
 
@@ -95,7 +95,82 @@ struct Lds {
 };
 
 
-template <int DK, class Eng, typename TIO, typename TO>
+// XCD (accelerator complex die) that runs the calling wave: hardware
+// register XCC_ID, bits 3:0.  The dispatcher hands workgroup b of a launch
+// to XCD b % 8; each XCD has its own L2.
+__device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u; }
+
+// Ready flag of a (chunk, head) record pair: bit 0 set once the records are
+// complete, bits 4:1 the producer's XCD, bit 8 set when the producer also
+// wrote its L2 back to memory (device-scope release).
+constexpr unsigned kReadyReleased = 1u << 8;
+
+// Fused launch, workgroups 0 .. n_prep - 1: the T and P records of every
+// (chunk, head), two at a time (waves 0..3 and waves 4..7 each take one item).
+// Producer p serves the (sequence, head) pairs nh with nh % 8 == p % 8, in
+// chunk-major order: the R = n_prep / 8 producers of a class take its items
+// m = r, r + R, r + 2R, ... (r = p / 8), item m being chunk m / M of the
+// class's (m % M)-th pair, M the pairs in the class.  n_prep is a multiple
+// of 8 and the state part maps nh to blocks on XCD nh % 8, so producer and
+// consumers of a record share one L2: the record stores complete in that L2
+// (every wave waits for its stores, then the workgroup barrier), then the
+// flag is stored at device scope, past the L1.  A producer that finds itself
+// off its XCD writes its L2 back first and says so in the flag, and a
+// consumer on another XCD then invalidates its caches before reading
+// (device-scope release and acquire).  Producers never wait, so the
+// consumers' waits end once every producer has been dispatched; producers
+// have the lower workgroup ids.
+template <int DK, typename TIO>
+__device__ __forceinline__ void produce_records(const ChunkArgs& args, char* smem) {
+  using IL = PrepItemLds<DK, TIO>;
+  const int half = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  char* lds = smem + half * IL::bytes;
+  PrepArgs a;
+  a.q = args.q; a.k = args.k; a.beta = args.beta; a.g = args.g; a.cu_seqlens = args.cu_seqlens;
+  a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
+  a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
+  const int H = args.H, NH = args.N * args.H;
+  const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
+  const unsigned xcd = xcd_id();
+  const bool home = xcd == (unsigned)x;
+  const int M = NH > x ? (NH - x + 7) >> 3 : 0;
+  const int64_t total = (int64_t)args.chunk_offs[args.N + 1] * M;
+  for (int64_t m0 = r; m0 < total; m0 += 2 * R) {
+    const int64_t m = m0 + (int64_t)half * R;
+    bool active = m < total;
+    int j = 0, h = 0, t0 = 0, nv = 0;
+    if (active) {
+      const int c = (int)(m / M), nh = x + 8 * (int)(m % M);
+      const int n = nh / H;
+      h = nh % H;
+      const int seg0 = args.cu_seqlens[n];
+      const int L = args.seq_lens ? args.seq_lens[n] : (args.cu_seqlens[n + 1] - seg0);
+      const int P = args.prefix_lens ? args.prefix_lens[n] : L;
+      active = c * kChunk < P;
+      if (active) {
+        j = args.chunk_offs[n] + c;
+        t0 = seg0 + c * kChunk;
+        nv = min(kChunk, P - c * kChunk);
+      }
+    }
+    prep_item<DK, TIO>(a, j, h, t0, nv, lds, tid, active);
+    wait_vmem();      // this wave's record stores are complete
+    __syncthreads();  // ... in every wave of the item; the LDS blocks are free again
+    if (active && tid == 0) {
+      unsigned flag = 1u | (xcd << 1);
+      if (!home) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        flag |= kReadyReleased;
+      }
+      __hip_atomic_store(args.ready + ((int64_t)j * H + h), flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Spin limit of a consumer's wait for a ready flag (about 0.1 s of s_sleep 4).
+constexpr int kReadySpinLimit = 1 << 20;
+
+template <int DK, class Eng, typename TIO, typename TO, bool kFused>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
   using Ls = Lds<DK, Eng>;
   using E = typename Eng::E;
@@ -105,6 +180,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   constexpr int NP = Eng::kPlanes;
   constexpr bool kSplit = Eng::kSplit;
   extern __shared__ __align__(16) char smem[];
+  if constexpr (kFused) {
+    if ((int)blockIdx.x < args.n_prep) {
+      produce_records<DK, TIO>(args, smem);
+      return;
+    }
+  }
   E* sK = reinterpret_cast<E*>(smem + Ls::oK);
   E* sQ = reinterpret_cast<E*>(smem + Ls::oQ);
   E* sKT = reinterpret_cast<E*>(smem + Ls::oKT);
@@ -142,7 +223,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   // block ids 8 apart, i.e. the same XCD, so their q/k/T reads share an L2.
   int nh, vt;
   {
-    const int b = blockIdx.x, G = gridDim.x;
+    const int b = (int)blockIdx.x - (kFused ? args.n_prep : 0);
+    const int G = (int)gridDim.x - (kFused ? args.n_prep : 0);
     if (tiles > 1 && G % (8 * tiles) == 0) {
       const int slot8 = b >> 3;
       vt = slot8 % tiles;
@@ -305,7 +387,53 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     }
   };
 
+  // Fused launch: the records of chunk cc come from a producer workgroup
+  // through ready flag (chunk, head).  Helper wave 1 waits for it (bounded
+  // spin); the barriers that follow order every wave's record loads after
+  // that.  A producer on this XCD completed the records in the shared L2;
+  // one on another XCD must have released them device-wide, and then this
+  // wave invalidates its caches (device-scope acquire).  A wait that runs
+  // out, or a record that cannot be trusted, sets the decay multiplier
+  // misc[2] to NaN, so the state and every later output show it.
+  unsigned pend = 0u;     // helper wave 1: a ready flag read ahead (used after a wait_vmem)
+  bool poisoned = false;
+  auto ready_ptr = [&](int cc) { return args.ready + ((int64_t)(chunk0 + cc) * H + h); };
+  auto load_ready = [&](int cc) { return __hip_atomic_load(ready_ptr(cc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto read_ready = [&](int cc) { return (unsigned)__builtin_amdgcn_readfirstlane((int)load_ready(cc)); };
+  const unsigned xcd_self = kFused ? xcd_id() : 0u;
+  auto poison = [&](float* vecb) {
+    poisoned = true;
+    if (lane == 0) vecb[194] = __builtin_nanf("");
+  };
+  auto await_ready = [&](int cc, unsigned v0, float* vecb) {
+    unsigned v = (unsigned)__builtin_amdgcn_readfirstlane((int)v0);
+    for (int spin = 0; v == 0u && !poisoned; ++spin) {
+      if (spin >= kReadySpinLimit) {
+        poison(vecb);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+      v = read_ready(cc);
+    }
+    if (v != 0u && ((v >> 1) & 15u) != xcd_self) {
+      if (v & kReadyReleased) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        wait_vmem();
+      } else {
+        poison(vecb);
+      }
+    }
+  };
+
   // ---------------- prologue ----------------
+  if constexpr (kFused) {
+    if (hw == 1 && n_chunks > 0) {
+      if (lane == 0) sG2[194] = 1.0f;
+      await_ready(0, read_ready(0), sG2);
+      if (n_chunks > 1) await_ready(1, read_ready(1), sG2);
+    }
+    barrier_lds();
+  }
   if (chain) {
     if (args.init != nullptr) {
 #pragma unroll
@@ -471,7 +599,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
                              e1.w * uacc[2 * kb + 1][3]};
         Eng::split(u8, bh[kb], bl[kb]);
       }
-      const float aC = st_coded ? gmisc[0] * s_cur : gmisc[0];  // decay, and the scale of a coded state
+      float aC = st_coded ? gmisc[0] * s_cur : gmisc[0];  // decay, and the scale of a coded state
+      if constexpr (kFused) aC *= gmisc[2];  // NaN after a failed wait for a ready flag
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -527,6 +656,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       if (c + 1 < n_chunks) {
         issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
         issue_q(c + 1, qc);          // and q
+      }
+      if constexpr (kFused) {
+        if (hw == 1 && c + 2 < n_chunks) pend = load_ready(c + 2);  // checked in phase 2
       }
       Fr uh[2], ul[2];
 #pragma unroll
@@ -615,6 +747,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     } else {
       if (c + 1 < n_chunks && hw == 0) scan(c + 1, vec);  // gates of the next chunk
       wait_vmem();  // this wave's loads (k of the next chunk included) are in LDS before the barrier
+      if constexpr (kFused) {
+        if (hw == 1 && c + 2 < n_chunks) await_ready(c + 2, pend, vec);  // P and T of chunk c + 2 load in the next step
+      }
       if (c + 2 < n_chunks) issue_k(c + 2, kc, hw);  // k of this chunk has been read
     }
     barrier_lds();
@@ -714,19 +849,58 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     io<TO>::st(go_ + (int64_t)(seg0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + lane, 0.f);
 }
 
-template <int DK, class Eng, typename TIO, typename TO>
+template <int DK, class Eng, typename TIO, typename TO, bool kFused>
 static hipError_t launch_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  auto kern = chunk_fwd_kernel<DK, Eng, TIO, TO>;
-  constexpr size_t lds = Lds<DK, Eng>::bytes;
+  auto kern = chunk_fwd_kernel<DK, Eng, TIO, TO, kFused>;
+  constexpr size_t item_lds = 2 * (size_t)PrepItemLds<DK, TIO>::bytes;  // a producer's two items
+  constexpr size_t lds = (kFused && item_lds > Lds<DK, Eng>::bytes) ? item_lds : Lds<DK, Eng>::bytes;
+  static_assert(lds <= 160 * 1024, "LDS budget exceeded");
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
+  const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows) + (kFused ? a.n_prep : 0);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kChunkThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+template <int DK, class Eng, typename TIO, typename TO>
+static hipError_t launch_sched(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
+  return a.n_prep > 0 ? launch_typed<DK, Eng, TIO, TO, true>(s, a, stream)
+                      : launch_typed<DK, Eng, TIO, TO, false>(s, a, stream);
+}
+
+// Compute units of the current device (0 when it cannot be read).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+// Fused launch or two kernels.  The state part runs one workgroup per (n, h,
+// value tile) for the whole sequence; when those fill at most half of the
+// compute units, the idle ones produce the T and P records in the same launch
+// (producer workgroups first) instead of a prep kernel that runs before it.
+// Each workgroup of the launch takes a whole compute unit (its LDS), so all
+// producers and consumers are resident together.
+static int producer_workgroups(const gdn_shape_t& s, const gdn_debug_t* debug) {
+  const int sched = debug ? debug->schedule : GDN_SCHEDULE_AUTO;
+  if (s.gate_per_channel || sched == GDN_SCHEDULE_SPLIT) return 0;
+  const int64_t tiles = s.dv / kTileRows;
+  const int64_t n_state = (int64_t)s.n_seqs * s.n_heads * tiles;
+  // every value tile of a (sequence, head) pair on XCD nh % 8 (block mapping of the state part)
+  if (tiles > 1 && ((int64_t)s.n_seqs * s.n_heads) % 8 != 0) return 0;
+  const int n_cu = device_cu_count();
+  if (n_cu < 16 || n_state + 8 > n_cu) return 0;
+  if (sched != GDN_SCHEDULE_FUSED && 2 * n_state > n_cu) return 0;
+  return (int)((n_cu - n_state) / 8 * 8);
 }
 
 hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, const void* v,
@@ -735,21 +909,20 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             const float* initial_state, void* o, float* final_state,
                             void* workspace, const gdn_debug_t* debug, hipStream_t stream) {
   ChunkArgs a;
-  const int32_t* offs = nullptr;
-  void* T = nullptr;
-  void* Prec = nullptr;
-  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, workspace, &offs, &T,
-                             &Prec, stream);
+  const PrepLayout L = prep_layout(s, workspace);
+  const int n_prep = producer_workgroups(s, debug);
+  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, L, n_prep == 0, stream);
   if (e != hipSuccess) return e;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
   a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens; a.prefix_lens = prefix_lens;
-  a.chunk_offs = offs; a.T = T; a.Prec = Prec;
+  a.chunk_offs = L.offs; a.T = L.T; a.Prec = L.P;
   a.init = initial_state; a.o = o; a.fin = final_state;
   a.bound_offsets = debug ? debug->bound_offsets : nullptr;
   a.bound_pre = debug ? debug->bound_pre : nullptr;
   a.bound_post = debug ? debug->bound_post : nullptr;
   a.bound_scales = debug ? debug->scales : nullptr;
   a.H = s.n_heads; a.dv = s.dv; a.flags = s.qdq_flags;
+  a.N = s.n_seqs; a.ready = L.ready; a.n_prep = n_prep;
   const bool ob = s.o_dtype == GDN_BF16;
   if (debug && debug->kernel_start) {
     e = hipEventRecord((hipEvent_t)debug->kernel_start, stream);
@@ -759,14 +932,14 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
     e = launch_kda_state(s, a, stream);
   } else if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)
-      e = ob ? launch_typed<128, EngBF16, uint16_t, uint16_t>(s, a, stream)
-             : launch_typed<128, EngBF16, uint16_t, float>(s, a, stream);
+      e = ob ? launch_sched<128, EngBF16, uint16_t, uint16_t>(s, a, stream)
+             : launch_sched<128, EngBF16, uint16_t, float>(s, a, stream);
     else
-      e = ob ? launch_typed<64, EngBF16, uint16_t, uint16_t>(s, a, stream)
-             : launch_typed<64, EngBF16, uint16_t, float>(s, a, stream);
+      e = ob ? launch_sched<64, EngBF16, uint16_t, uint16_t>(s, a, stream)
+             : launch_sched<64, EngBF16, uint16_t, float>(s, a, stream);
   } else if (s.dk == 64) {
-    e = ob ? launch_typed<64, EngF32, float, uint16_t>(s, a, stream)
-           : launch_typed<64, EngF32, float, float>(s, a, stream);
+    e = ob ? launch_sched<64, EngF32, float, uint16_t>(s, a, stream)
+           : launch_sched<64, EngF32, float, float>(s, a, stream);
   } else {
     return hipErrorNotSupported;
   }

@@ -205,8 +205,8 @@ struct ChunkArgs {
   const int32_t* seq_lens;
   const int32_t* prefix_lens;
   const int32_t* chunk_offs;  // prefix sums of ceil(P_n / 64) (prep kernel)
-  const void* T;              // one T record per (chunk, head) (prep kernel)
-  const void* Prec;           // per-key-channel gate: one P record per (chunk, head)
+  const void* T;              // one T record per (chunk, head) (prep kernel or producer workgroups)
+  const void* Prec;           // one P record per (chunk, head), the same way
   const float* init;
   void* o;
   float* fin;
@@ -217,6 +217,9 @@ struct ChunkArgs {
   int H;
   int dv;
   unsigned flags;
+  int N;               // sequences
+  unsigned* ready;     // fused launch: one ready flag per (chunk, head), cleared before the launch
+  int n_prep;          // fused launch: workgroups 0 .. n_prep - 1 produce the T and P records
 };
 
 // The sequential kernel for a per-key-channel gate (gdn_kda.hip); the prep

@@ -27,14 +27,26 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
 // for both engines.
 constexpr int kTRecBytes = 12288;
 
-// Bytes of the chunk workspace: chunk offsets [N + 1] (padded to 256 bytes),
-// then the T records and the P records for the worst-case chunk count
-// ceil(total_tokens / 64) + N.
+// The chunk workspace: int32 chunk offsets [N + 1] and the largest chunk
+// count of a sequence (padded to 256 bytes), one uint32 ready flag per
+// (chunk, head) (padded to 256 bytes), then the T records and the P records,
+// all sized for the worst-case chunk count ceil(total_tokens / 64) + N.
+struct PrepLayout {
+  int32_t* offs;
+  unsigned* ready;
+  void* T;
+  void* P;
+  int64_t items;  // (chunk, head) slots
+  size_t bytes;   // total workspace bytes
+};
+PrepLayout prep_layout(const gdn_shape_t& s, void* workspace);
 size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens);
 
+// Chunk offsets, then (records true) the T and P records of every (chunk,
+// head); with records false the ready flags are cleared instead, for a fused
+// launch that produces the records itself.
 hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                        const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
-                       const int32_t* prefix_lens, void* workspace, const int32_t** offs_out,
-                       void** T_out, void** P_out, hipStream_t stream);
+                       const int32_t* prefix_lens, const PrepLayout& L, bool records, hipStream_t stream);
 
 }  // namespace gdn

@@ -85,8 +85,22 @@ typedef struct {
     float* scales;                 /* [n_bounds, H, dv / 64] QDQ scales (1 when none) */
     void* kernel_start;            /* hipEvent_t or NULL: recorded on the stream just before */
     void* kernel_end;              /* and just after the sequential state kernel (timing hook; */
-                                   /* the parallel per-chunk solve runs before kernel_start) */
+                                   /* a separate per-chunk solve kernel runs before kernel_start, */
+                                   /* a fused one inside the bracket) */
+    int32_t schedule;              /* GDN_SCHEDULE_*: how the per-chunk solve is scheduled */
 } gdn_debug_t;
+
+/* gdn_debug_t.schedule.  The per-chunk solve (T and P records of every chunk
+ * and head) either runs as its own kernel before the sequential state kernel
+ * (SPLIT) or inside the same launch, on compute units the state kernel leaves
+ * idle, handing each record over through a ready flag (FUSED).  AUTO (also
+ * when debug is NULL) fuses when the state kernel's workgroups fill at most
+ * half of the compute units; FUSED fuses whenever at least 8 compute units
+ * stay free.  Both give bit-identical results.  The per-key-channel gate
+ * always runs SPLIT. */
+#define GDN_SCHEDULE_AUTO 0
+#define GDN_SCHEDULE_SPLIT 1
+#define GDN_SCHEDULE_FUSED 2
 
 /*
  * gdn_chunk_fwd -- chunked gated delta rule forward over packed sequences.

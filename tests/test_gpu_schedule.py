@@ -1,0 +1,95 @@
+"""The two schedules of the per-chunk solve give bit-identical results:
+SPLIT runs it as its own kernel before the sequential state kernel, FUSED
+inside the state kernel's launch on compute units the state workgroups leave
+idle, each (chunk, head) record handed over through a ready flag.  The
+parity tests of the other files run with the automatic choice (fused for
+every workload whose state workgroups fill at most half of the GPU), so this
+equality carries their oracle comparisons over to the split schedule, and
+back for the workloads that split automatically."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_state_qat_amd import api
+from fp8_state_qat_amd import inputs as gi
+from fp8_state_qat_amd._lib import GDN_SCHEDULE_AUTO, GDN_SCHEDULE_FUSED, GDN_SCHEDULE_SPLIT
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(d, flags, sched, *, o_dtype=None, seq_lens=None, prefix_lens=None, workspace=None):
+    o, S = api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                         seq_lens=seq_lens, prefix_lens=prefix_lens, qdq_flags=flags,
+                         o_dtype=o_dtype, workspace=workspace, debug={"schedule": sched})
+    torch.cuda.synchronize()
+    return o.clone(), S.clone()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+def _same(a, b, what):
+    for x, y, name in ((a[0], b[0], "o"), (a[1], b[1], "S")):
+        diff = int((_bits(x) != _bits(y)).sum())
+        print(f"{what} {name}: {diff} differing elements of {x.numel()}", flush=True)
+        assert diff == 0
+
+
+@pytest.mark.parametrize("flags", [0, 3])
+def test_full_prefill_fused_equals_split(flags):
+    """B=4, T=4096, H=16, d=128, bf16: 128 state workgroups, fused by default."""
+    d = gi.device_packed([4096] * 4, 16, 128, 128, seed=11)
+    split = _run(d, flags, GDN_SCHEDULE_SPLIT, o_dtype=torch.bfloat16)
+    auto = _run(d, flags, GDN_SCHEDULE_AUTO, o_dtype=torch.bfloat16)
+    assert torch.isfinite(auto[1]).all()
+    _same(split, auto, f"full prefill flags={flags}")
+
+
+@pytest.mark.parametrize("io,d", [(gi.F32, 64), (gi.BF16, 64), (gi.BF16, 128)])
+def test_ragged_prefix_fused_equals_split(io, d):
+    """Ragged lengths (empty, one token, chunk multiples and tails), padding
+    rows and chunked prefixes shorter than the sequences."""
+    w = gi.make_packed([300, 0, 1, 64, 129, 77], 3, d, d, io_dtype=io, seed=5 + d,
+                       pads=[2, 0, 5, 0, 63, 1], prefix_lens=[256, 0, 1, 64, 100, 0])
+    dt = gi.device_tensors(w)
+    for flags in (0, 1, 2, 3):
+        a = _run(dt, flags, GDN_SCHEDULE_SPLIT, o_dtype=torch.float32, seq_lens=dt["seq_lens"],
+                 prefix_lens=dt["prefix_lens"])
+        b = _run(dt, flags, GDN_SCHEDULE_FUSED, o_dtype=torch.float32, seq_lens=dt["seq_lens"],
+                 prefix_lens=dt["prefix_lens"])
+        _same(a, b, f"ragged {io} d={d} flags={flags}")
+
+
+def test_forced_fusion_where_auto_splits():
+    """192 state workgroups (more than half of the GPU): automatic splits,
+    FUSED still fuses with the 64 compute units left; same bits."""
+    d = gi.device_packed([1024, 700, 1024, 333], 24, 128, 128, seed=13)
+    a = _run(d, 3, GDN_SCHEDULE_AUTO, o_dtype=torch.bfloat16)
+    b = _run(d, 3, GDN_SCHEDULE_FUSED, o_dtype=torch.bfloat16)
+    _same(a, b, "192 state workgroups")
+
+
+def test_workspace_reuse_and_garbage():
+    """Ready flags are cleared on every call: a workspace full of nonzero
+    bytes, and one reused right after another fused call on other inputs,
+    give the bits of a fresh split run."""
+    d1 = gi.device_packed([2048, 1500], 8, 128, 128, seed=17)
+    d2 = gi.device_packed([2048, 1500], 8, 128, 128, seed=19)
+    ref = _run(d2, 3, GDN_SCHEDULE_SPLIT, o_dtype=torch.bfloat16)
+    n = api.chunk_workspace_bytes(2, 8, 128, 128, 3548)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    _same(ref, _run(d2, 3, GDN_SCHEDULE_FUSED, o_dtype=torch.bfloat16, workspace=ws), "garbage workspace")
+    _run(d1, 3, GDN_SCHEDULE_FUSED, o_dtype=torch.bfloat16, workspace=ws)
+    _same(ref, _run(d2, 3, GDN_SCHEDULE_FUSED, o_dtype=torch.bfloat16, workspace=ws), "reused workspace")
+    # every (chunk, head) of the call was produced and flagged: bit 0 ready,
+    # bits 4:1 the producer's XCD, bit 8 a device-wide release (producer off
+    # its XCD, expected never)
+    hdr = ((2 + 2) * 4 + 255) // 256 * 256   # chunk offsets and the largest chunk count
+    n_items = (32 + 24) * 8                    # (chunk, head) pairs of the call
+    flags = ws[hdr:hdr + 4 * n_items].view(torch.int32).cpu().numpy()
+    assert np.all(flags & 1 == 1) and np.all(flags >> 9 == 0)
+    nh = np.concatenate([np.repeat(0, 32), np.repeat(1, 24)])[:, None] * 8 + np.arange(8)[None, :]
+    home = ((flags.reshape(56, 8) >> 1) & 15) == nh % 8
+    print(f"producers on the XCD of their consumers: {int(home.sum())} of {home.size}; "
+          f"released device-wide: {int((flags >> 8 & 1).sum())}", flush=True)
