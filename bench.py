@@ -3,11 +3,14 @@
 
 One step = one gdn_chunk_fwd call over the GDN prefill workload (B=4,
 T=4096, H=16, dk=dv=128, bf16 q/k/v and o, fp32 state, FP8-E4M3 state QDQ
-at every 64-token boundary and at the end): a parallel prep kernel (gates,
-K K^T, the exact solve per chunk) and the sequential state kernel (W and U,
-U', O, the state update and the boundary QDQ).  Inputs are resident in HBM
-before the timed region.  The roofline object covers the sequential state
-kernel, timed with HIP events recorded around it by the library.
+at every 64-token boundary and at the end): a small chunk-offsets kernel,
+then one launch in which 128 producer workgroups form the per-chunk records
+(gates, K K^T, the exact solve, P) while the 128 state workgroups run the
+sequential part (U', O, the state update and the boundary QDQ) and consume
+them.  Inputs are resident in HBM before the timed region.  The roofline
+object covers that launch, timed with HIP events recorded around it by the
+library; the split schedule (prep kernel, then the state kernel alone) is
+timed too and reported beside it.
 
 Also reported: the same prefill with a per-key-channel gate (KDA-style g
 [T, H, dk]) as tokens/s and its state kernel's time; the prefill->decode handoff workload (256 sequences, H=32,
@@ -58,7 +61,7 @@ def prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes, gate_floats=1):
     return T_heads * per + n_states * dv * dk * 4
 
 
-def state_kernel_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes, o_bytes):
+def split_state_kernel_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes, o_bytes):
     """Algorithmic HBM bytes of the sequential state kernel: the prefill bytes
     plus one read of the two per-chunk records the prep kernel writes (T and
     P, 12 KiB each per chunk and head)."""
@@ -152,7 +155,7 @@ def main():
 
     import torch
     from fp8_state_qat_amd import api, inputs as gi
-    from fp8_state_qat_amd._lib import GDN_QDQ_CHUNK, GDN_QDQ_WRITE
+    from fp8_state_qat_amd._lib import GDN_QDQ_CHUNK, GDN_QDQ_WRITE, GDN_SCHEDULE_SPLIT
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -187,17 +190,21 @@ def main():
     n_chunk_heads = B * H * ((T + 63) // 64)
     fl_all = flops_per_token_head(64, dk, dv) * token_heads
     fl = state_kernel_flops_per_token_head(64, dk, dv) * token_heads
-    by = state_kernel_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2, 2)
+    # the fused launch does every flop of the step and moves the prefill's bytes
+    # (the records stay inside it: written and read back through the L2)
+    by = prefill_bytes(token_heads, B * H, dk, dv, 2, 2)
     src = source_hash([os.path.join(ROOT, "fp8_state_qat_amd", "csrc", f)
-                       for f in ("gdn_chunk.hip", "gdn_chunk_common.hpp", "gdn_device.hpp")])
+                       for f in ("gdn_chunk.hip", "gdn_chunk_common.hpp", "gdn_device.hpp",
+                                 "gdn_prep_item.hpp")])
     traffic = load_traffic("chunk_fwd_gdn_prefill", src)
-    tflops = fl / (kern_ms * 1e-3) / 1e12
+    tflops = fl_all / (kern_ms * 1e-3) / 1e12
     hbm_gbs = by / (kern_ms * 1e-3) / 1e9
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": "chunk_fwd_kernel<128, EngBF16, bf16, bf16>",
-                "algorithmic_flops_per_launch": fl,
-                "flops_per_token_head": state_kernel_flops_per_token_head(64, dk, dv),
+                "traffic": traffic,
+                "kernel": "chunk_fwd_kernel<128, EngBF16, bf16, bf16, fused> (128 producer + 128 state workgroups)",
+                "algorithmic_flops_per_launch": fl_all,
+                "flops_per_token_head": flops_per_token_head(64, dk, dv),
                 "avg_launch_ms": round(kern_ms, 5),
                 "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
@@ -215,6 +222,26 @@ def main():
                       out=o, final_state=fin)
     off_ms, _ = time_launches(step_off, args.steps, args.warmup)
 
+    # split schedule, same workload (reported): prep kernel, then the state kernel alone
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps + args.warmup)]
+    its = {"i": 0}
+
+    def step_split():
+        e0, e1 = evs[its["i"]]
+        its["i"] += 1
+        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=flags,
+                      out=o, final_state=fin,
+                      debug={"kernel_start": e0, "kernel_end": e1, "schedule": GDN_SCHEDULE_SPLIT})
+
+    for e0, e1 in evs:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    split_ms, _ = time_launches(step_split, args.steps, args.warmup)
+    split_kern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[args.warmup:]]))
+    split_by = split_state_kernel_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2, 2)
+
     out = {"metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -226,7 +253,14 @@ def main():
                       "qdq_flags": flags},
            "roofline": roofline, "mfma": mfma,
            "qdq_off": {"ms_per_step": round(off_ms / args.steps, 5),
-                       "tokens_per_s": round(tokens / (off_ms / args.steps * 1e-3), 1)}}
+                       "tokens_per_s": round(tokens / (off_ms / args.steps * 1e-3), 1)},
+           "split_schedule": {"ms_per_step": round(split_ms / args.steps, 5),
+                              "tokens_per_s": round(tokens / (split_ms / args.steps * 1e-3), 1),
+                              "state_kernel": "chunk_fwd_kernel<128, EngBF16, bf16, bf16>",
+                              "state_kernel_avg_launch_ms": round(split_kern, 5),
+                              "state_kernel_mfma_tflops": round(fl / (split_kern * 1e-3) / 1e12, 2),
+                              "state_kernel_hbm_gbs": round(split_by / (split_kern * 1e-3) / 1e9, 1),
+                              "state_kernel_algorithmic_bytes": split_by}}
 
     # ---------------- per-key-channel gate (KDA) prefill, same shape (reported) ----------------
     if not args.no_kda:
