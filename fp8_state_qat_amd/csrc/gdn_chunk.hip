@@ -123,7 +123,7 @@ constexpr unsigned kReadyReleased = 1u << 8;
 template <int DK, typename TIO>
 __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* smem) {
   using IL = PrepItemLds<DK, TIO>;
-  const int half = threadIdx.x >> 8, tid = threadIdx.x & 255;
+  const int half = uniform((int)threadIdx.x >> 8), tid = threadIdx.x & 255;  // half: wave-uniform
   char* lds = smem + half * IL::bytes;
   PrepArgs a;
   a.q = args.q; a.k = args.k; a.beta = args.beta; a.g = args.g; a.cu_seqlens = args.cu_seqlens;
@@ -153,7 +153,11 @@ __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* sme
         nv = min(kChunk, P - c * kChunk);
       }
     }
-    prep_item<DK, TIO>(a, j, h, t0, nv, lds, tid, active);
+    // a fresh copy of the lane index per item keeps the compiler from holding
+    // the item's lane-dependent LDS addresses live across the whole loop
+    int tid_i = tid;
+    asm volatile("" : "+v"(tid_i));
+    prep_item<DK, TIO>(a, j, h, t0, nv, lds, tid_i, active);
     wait_vmem();      // this wave's record stores are complete
     __syncthreads();  // ... in every wave of the item; the LDS blocks are free again
     if (active && tid == 0) {
@@ -519,8 +523,19 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           const int tt = 2 * kb + hh;
           const float4 e4 = *reinterpret_cast<const float4*>(geg + 16 * tt + 4 * gq);
           float vv[4];
+          if constexpr (Eng::kTrRead) {
+            // one transpose read: lane 4k + j of each 16-lane group points at row
+            // 16tt + 4gq + k, columns 16c4 + 4j .. + 3, so lane ln receives column
+            // 16c4 + ln of rows 16tt + 4gq + 0..3
+            const uint2 r = lds_read_tr16(vb + (16 * tt + 4 * gq + (ln >> 2)) * RSV + 16 * c4 + 4 * (ln & 3));
+            vv[0] = __uint_as_float(r.x << 16);
+            vv[1] = __uint_as_float(r.x & 0xffff0000u);
+            vv[2] = __uint_as_float(r.y << 16);
+            vv[3] = __uint_as_float(r.y & 0xffff0000u);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vv[i] = Eng::to_f(vb[(16 * tt + 4 * gq + i) * RSV + 16 * c4 + ln]);
+            for (int i = 0; i < 4; ++i) vv[i] = Eng::to_f(vb[(16 * tt + 4 * gq + i) * RSV + 16 * c4 + ln]);
+          }
           x8[4 * hh + 0] = fmaf(-sc * e4.x, acc[tt][0], vv[0]);
           x8[4 * hh + 1] = fmaf(-sc * e4.y, acc[tt][1], vv[1]);
           x8[4 * hh + 2] = fmaf(-sc * e4.z, acc[tt][2], vv[2]);
@@ -653,10 +668,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if (lane == 0) red[c4] = amax;
       }
     } else {
-      if (c + 1 < n_chunks) {
-        issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
-        issue_q(c + 1, qc);          // and q
-      }
+      if (c + 1 < n_chunks) issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
       if constexpr (kFused) {
         if (hw == 1 && c + 2 < n_chunks) pend = load_ready(c + 2);  // checked in phase 2
       }
@@ -666,15 +678,22 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         uh[kb] = Eng::ld(slot(xu, c4 * 2 * NP + kb));
         if constexpr (kSplit) ul[kb] = Eng::ld(slot(xu, c4 * 2 * NP + 2 + kb));
       }
+      // the P fragments in registers before q is issued: a wave waits at each
+      // direct load until the load unit takes it, so the reads go out first
+      Fr phs[6], pls[6];
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        phs[p] = Eng::ld(slot(pb, p));
+        if constexpr (kSplit) pls[p] = Eng::ld(slot(pb, 6 + p));
+      }
+      if (c + 1 < n_chunks) issue_q(c + 1, qc);  // q was last read in phase 1a
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        const Fr ph = Eng::ld(slot(pb, p));
-        Eng::mma(oacc[ti], uh[kb], ph);
+        Eng::mma(oacc[ti], uh[kb], phs[p]);
         if constexpr (kSplit) {
-          const Fr pl = Eng::ld(slot(pb, 6 + p));
-          Eng::mma(oacc[ti], ul[kb], ph);
-          Eng::mma(oacc[ti], uh[kb], pl);
+          Eng::mma(oacc[ti], ul[kb], phs[p]);
+          Eng::mma(oacc[ti], uh[kb], pls[p]);
         }
       }
       // lane holds o[tok = 16ti + ln][16c4 + 4gq .. +3] of this tile

@@ -29,8 +29,9 @@ constexpr int kTRecBytes = 12288;
 
 // The chunk workspace: int32 chunk offsets [N + 1] and the largest chunk
 // count of a sequence (padded to 256 bytes), one uint32 ready flag per
-// (chunk, head) (padded to 256 bytes), then the T records and the P records,
-// all sized for the worst-case chunk count ceil(total_tokens / 64) + N.
+// (chunk, head) (padded to 256 bytes; used by the fused launch), then the T
+// records and the P records, all sized for the worst-case chunk count
+// ceil(total_tokens / 64) + N.
 struct PrepLayout {
   int32_t* offs;
   unsigned* ready;
