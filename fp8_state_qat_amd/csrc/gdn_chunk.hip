@@ -79,7 +79,7 @@ struct Lds {
   static constexpr size_t F = 64 * 8 * sizeof(E);
   static constexpr size_t RV = 64 * sizeof(E) + 16;    // padded v row (bytes)
   static constexpr size_t oK = 0;                      // 2 buffers by chunk parity
-  static constexpr size_t oQ = oK + 2 * 4 * NKB * F;   // 2 buffers by chunk parity
+  static constexpr size_t oQ = oK + 2 * 4 * NKB * F;
   static constexpr size_t oKT = oQ + 4 * NKB * F;
   static constexpr size_t oV = oKT + (Eng::kTrRead ? 0 : 2 * NT * F);
   static constexpr size_t oT = oV + 64 * RV;
@@ -327,11 +327,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
                    lds_of(dst) + i * RPI * (PPV + 1) * EPP * (int)sizeof(E));
     }
   };
-  // Loads of chunk cc, by buffer lifetime: k and q have two buffers (chunk
-  // parity) and are issued one chunk ahead at the start of phase 1a; v and
-  // T (one buffer each) at the start of phase 1b, once phase 1a has read
-  // them.  Chain waves load k, v and T, helper waves q; helper wave 0 fetches
-  // the log-gates into a register.
+  // Loads of chunk cc, by buffer lifetime: k and P have two buffers (chunk
+  // parity); P of the next chunk is issued at the start of phase 1a, k two
+  // chunks ahead in phase 2 once the update has read it; v, T and q (one
+  // buffer each) in phase 1b, once phase 1a has read them.  In the loop the
+  // helper waves issue all of them; helper wave 0 fetches the log-gates into
+  // a register.
   auto issue_k = [&](int cc, E* kdst, int wi) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
@@ -496,6 +497,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       f32x4 acc[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // the operand reads of a product all issued before its first MFMA, so
+      // that they overlap one another instead of each waiting for the last
+      Fr kf[4 * NKB];
+#pragma unroll
+      for (int f = 0; f < 4 * NKB; ++f) kf[f] = Eng::ld(qslot(kc, f));  // f = tt * NKB + kb
       if (two) {  // uncoded state: hi + lo from the fp32 state
         Fr hi[NKB], lo[NKB];
         state_frags(hi, lo);
@@ -503,15 +509,20 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            const Fr a = Eng::ld(qslot(kc, tt * NKB + kb));
-            Eng::mma(acc[tt], a, hi[kb]);
-            Eng::mma(acc[tt], a, lo[kb]);
+            Eng::mma(acc[tt], kf[tt * NKB + kb], hi[kb]);
+            Eng::mma(acc[tt], kf[tt * NKB + kb], lo[kb]);
           }
       } else {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], Eng::ld(qslot(kc, tt * NKB + kb)), sh[kb]);
+          for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], kf[tt * NKB + kb], sh[kb]);
+      }
+      Fr tf[6], tl[6];
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        tf[p] = Eng::ld(slot(tb, p));
+        if constexpr (kSplit) tl[p] = Eng::ld(slot(tb, 6 + p));
       }
       // X[t][v] = V[t][v] - s exp(gamma_t) (K S^T)[t][v], t = 16tt + 4gq + i
       Fr xh[2], xl[2];
@@ -549,12 +560,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        const Fr tf = Eng::ld(slot(tb, p));
-        Eng::mma(uacc[ti], tf, xh[kb]);
+        Eng::mma(uacc[ti], tf[p], xh[kb]);
         if constexpr (kSplit) {
-          const Fr tl = Eng::ld(slot(tb, 6 + p));
-          Eng::mma(uacc[ti], tf, xl[kb]);
-          Eng::mma(uacc[ti], tl, xh[kb]);
+          Eng::mma(uacc[ti], tf[p], xl[kb]);
+          Eng::mma(uacc[ti], tl[p], xh[kb]);
         }
       }
       // U' as the A operand of U'^T P^T, for the helper wave
@@ -579,16 +588,21 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       const float sc = coded_in ? gmisc[1] : 1.0f;
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Fr qf[4 * NKB], sa[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const Fr sa = Eng::ld(slot(xs, c4 * NP * NKB + kb));
-        Fr sb;
-        if (two) sb = Eng::ld(slot(xs, c4 * NP * NKB + NKB + kb));
+      for (int kb = 0; kb < NKB; ++kb) sa[kb] = Eng::ld(slot(xs, c4 * NP * NKB + kb));
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const Fr bq = Eng::ld(qslot(qc, ti * NKB + kb));
-          Eng::mma(oacc[ti], sa, bq);
-          if (two) Eng::mma(oacc[ti], sb, bq);
+      for (int f = 0; f < 4 * NKB; ++f) qf[f] = Eng::ld(qslot(qc, f));  // f = ti * NKB + kb
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) Eng::mma(oacc[ti], sa[kb], qf[ti * NKB + kb]);
+      if (two) {  // the lo plane of an uncoded state
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const Fr sb = Eng::ld(slot(xs, c4 * NP * NKB + NKB + kb));
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) Eng::mma(oacc[ti], sb, qf[ti * NKB + kb]);
         }
       }
 #pragma unroll
