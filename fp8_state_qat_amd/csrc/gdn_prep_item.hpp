@@ -246,50 +246,58 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t
     }
     return acc;
   };
-  // ---- ten tile jobs (ri, si), si <= ri, at most 3 per wave: with C_A = K K^T
-  // and C_P = K Q^T on the tile (one shared A operand, the k rows of block si)
+  // ---- six strip jobs, one per record pair p = (ri, kb) in the record order
+  // (0,0) (1,0) (2,0) (3,0) (2,1) (3,1): the tiles si = 2kb and 2kb + 1 of row
+  // block ri (a tile with si > ri is zero).  With C_A = K K^T and C_P = K Q^T
+  // on a tile (one shared A operand, the k rows of block si)
   //   A[r][s] = beta_r exp(gamma_r - gamma_s) C_A[s][r]    (s < r)   -> sA
   //   P[r][s] = exp(gamma_r - gamma_s) C_P[s][r]           (s <= r)  -> the P record
-  // plus the two zero P tiles (0,1) and (2,3) that complete fragment pairs.
+  // A lane holds P[r][s] for one row r and the four s of each tile that its
+  // record slot takes (k-slots kperm(l / 16, 0..3) and 4..7), so it writes
+  // whole 16-byte slots and every store instruction whole cache lines.
+  // Waves: 0 takes pairs 0 and 5, 1 pairs 1 and 4, 2 pair 2, 3 pair 3 (three
+  // nonzero tiles at most per wave).
   char* prec = reinterpret_cast<char*>(a.P) + ((int64_t)j * H + h) * kTRecBytes;
-  auto put_p = [&](int ri, int si, const float (&v)[4]) {
-    // record slot: pair pr = (ri, si / 2), lane l, elements 4 (si % 2) .. + 3
-    const int pr = (si >= 2) ? ri + 2 : ri, jb = (si & 1) * 4;
-    if constexpr (kBF) {
-      uint32_t h0, l0, h1, l1;
-      split_bf16x2(v[0], v[1], h0, l0);
-      split_bf16x2(v[2], v[3], h1, l1);
-      *reinterpret_cast<uint2*>(prec + (pr * 64 + lane) * 16 + jb * 2) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(prec + ((6 + pr) * 64 + lane) * 16 + jb * 2) = make_uint2(l0, l1);
-    } else {
-      *reinterpret_cast<float4*>(prec + (pr * 64 + lane) * 32 + jb * 4) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-  };
   if (active) {
 #pragma unroll
-    for (int jj = 0; jj < 3; ++jj) {
-      const int job = w + 4 * jj;
-      if (job < 10) {
-        const int ri = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
-        const int si = job - (ri * (ri + 1)) / 2;
+    for (int jj = 0; jj < 2; ++jj) {
+      const int pr = (jj == 0) ? w : (w == 0 ? 5 : w == 1 ? 4 : -1);
+      if (pr >= 0) {
+        const int ri = pr < 4 ? pr : pr - 2, kb = pr < 4 ? 0 : 1;
         const int r = 16 * ri + ln;
-        const f32x4 ca = tile(sK, 16 * si + ln, sK, r);
-        const f32x4 cp = tile(sK, 16 * si + ln, sQ, r);
         const float g2r = sG2[r], br = sBeta[r];
-        float va[4], vp[4];
+        float vp8[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * si + 4 * gq + i;
-          const float e = (s <= r) ? __builtin_amdgcn_exp2f(g2r - sG2[s]) : 0.f;
-          va[i] = (s < r) ? br * e * ca[i] : 0.f;
-          vp[i] = e * cp[i];
+        for (int hh = 0; hh < 2; ++hh) {
+          const int si = 2 * kb + hh;
+          if (si <= ri) {
+            const f32x4 ca = tile(sK, 16 * si + ln, sK, r);
+            const f32x4 cp = tile(sK, 16 * si + ln, sQ, r);
+            float va[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int s = 16 * si + 4 * gq + i;
+              const float e = (s <= r) ? __builtin_amdgcn_exp2f(g2r - sG2[s]) : 0.f;
+              va[i] = (s < r) ? br * e * ca[i] : 0.f;
+              vp8[4 * hh + i] = e * cp[i];
+            }
+            *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) = make_float4(va[0], va[1], va[2], va[3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vp8[4 * hh + i] = 0.f;
+          }
         }
-        *reinterpret_cast<float4*>(sA + r * L64 + 16 * si + 4 * gq) = make_float4(va[0], va[1], va[2], va[3]);
-        put_p(ri, si, vp);
-      } else if (job < 12) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        const int si = (job == 10) ? 1 : 3;
-        put_p(si - 1, si, z);
+        if constexpr (kBF) {
+          uint32_t hv[4], lv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) split_bf16x2(vp8[2 * q], vp8[2 * q + 1], hv[q], lv[q]);
+          *reinterpret_cast<uint4*>(prec + (pr * 64 + lane) * 16) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+          *reinterpret_cast<uint4*>(prec + ((6 + pr) * 64 + lane) * 16) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+        } else {
+          float4* dst = reinterpret_cast<float4*>(prec + (pr * 64 + lane) * 32);
+          dst[0] = make_float4(vp8[0], vp8[1], vp8[2], vp8[3]);
+          dst[1] = make_float4(vp8[4], vp8[5], vp8[6], vp8[7]);
+        }
       }
     }
   }
