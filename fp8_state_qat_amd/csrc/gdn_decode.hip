@@ -14,7 +14,9 @@
 // workgroup (256 threads) per tile.  Thread t owns the float4 column group
 // c4 = t % (dk/4) and rows t / (dk/4) + p * (256 / (dk/4)); every load and
 // store instruction of the block covers 4 KiB of contiguous state.  Row dot
-// products are reduced over the dk/4 lanes of a row with a fixed xor tree.
+// products are reduced over the dk/4 lanes of a row by DPP lane moves (a
+// fixed order); the tile's 64 outputs go through LDS and leave as one
+// contiguous store.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -30,6 +32,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   constexpr int RPP = kThreads / F; // rows covered by one pass of the block
   constexpr int NP = kTileRows / RPP;
   __shared__ float red[4];
+  __shared__ float s_o[kTileRows];
 
   const int tiles = dv / kTileRows;
   const int vt = blockIdx.x % tiles;
@@ -58,9 +61,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   const float b = beta[nh];
 
   // k . q over all dk columns (same fixed tree in every row group)
-  float kq = kc[0] * qc[0] + kc[1] * qc[1] + kc[2] * qc[2] + kc[3] * qc[3];
-#pragma unroll
-  for (int off = F / 2; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+  const float kq = group_sum<F>(kc[0] * qc[0] + kc[1] * qc[1] + kc[2] * qc[2] + kc[3] * qc[3]);
 
   const int64_t tile_base = (nh * dv + (int64_t)kTileRows * vt) * DK;  // float offset
   float4* S = reinterpret_cast<float4*>(state + tile_base);
@@ -73,17 +74,12 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   for (int p = 0; p < NP; ++p) {
     const int row = rr + RPP * p;
     float sd0 = x[p].x * dec[0], sd1 = x[p].y * dec[1], sd2 = x[p].z * dec[2], sd3 = x[p].w * dec[3];
-    float y = sd0 * kc[0] + sd1 * kc[1] + sd2 * kc[2] + sd3 * kc[3];
-    float z = sd0 * qc[0] + sd1 * qc[1] + sd2 * qc[2] + sd3 * qc[3];
-#pragma unroll
-    for (int off = F / 2; off >= 1; off >>= 1) {
-      y += __shfl_xor(y, off, 64);
-      z += __shfl_xor(z, off, 64);
-    }
+    const float y = group_sum<F>(sd0 * kc[0] + sd1 * kc[1] + sd2 * kc[2] + sd3 * kc[3]);
+    const float z = group_sum<F>(sd0 * qc[0] + sd1 * qc[1] + sd2 * qc[2] + sd3 * qc[3]);
     const float vr = io<TIO>::ld(v + nh * dv + kTileRows * vt + row);
     const float u = b * (vr - y);
     const float orow = z + kq * u;
-    if (c4 == 0) io<TO>::st(o + nh * dv + kTileRows * vt + row, orow);
+    if (c4 == 0) s_o[row] = orow;
     x[p].x = sd0 + u * kc[0];
     x[p].y = sd1 + u * kc[1];
     x[p].z = sd2 + u * kc[2];
@@ -97,14 +93,17 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   }
   float s = 1.0f;
   if (do_qdq) {
-    amax = block_max(amax, red);
+    amax = block_max(amax, red);  // its barriers also publish s_o
     s = qdq_scale(amax);
     const float r = 1.0f / s;
 #pragma unroll
     for (int p = 0; p < NP; ++p) qdq4(x[p], s, r);
+  } else {
+    __syncthreads();  // s_o
   }
 #pragma unroll
   for (int p = 0; p < NP; ++p) S[t + kThreads * p] = x[p];
+  if (t < kTileRows) io<TO>::st(o + nh * dv + kTileRows * vt + t, s_o[t]);
   if (scales != nullptr && t == 0) scales[nh * tiles + vt] = s;
 }
 

@@ -126,10 +126,26 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v;
 }
 
+// Sum over each group of F consecutive lanes (F = 16 or 32, groups aligned),
+// every lane of a group receiving it: quad swaps and rotations by 4 and 8
+// inside each row of 16 lanes (DPP), then for F = 32 a swizzle that swaps
+// the two rows of each 32-lane half.  The order of the additions is fixed.
+template <int F>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(F == 16 || F == 32, "group of 16 or 32 lanes");
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_add<0x124, 0xF>(v);  // row_ror:4
+  v = dpp_add<0x128, 0xF>(v);  // row_ror:8
+  if constexpr (F == 32)       // bit-mode swizzle: and 0x1f, or 0, xor 0x10
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  return v;
+}
+
 // Max over the 256 threads of a block; red must hold 4 floats of LDS.  All
 // threads return the same value.  Contains two barriers.
 __device__ __forceinline__ float block_max(float v, float* red) {
-  v = wave_max(v);
+  v = wave_max_dpp(v);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
