@@ -95,15 +95,6 @@ struct Lds {
 };
 
 
-// XCD (accelerator complex die) that runs the calling wave: hardware
-// register XCC_ID, bits 3:0.  The dispatcher hands workgroup b of a launch
-// to XCD b % 8; each XCD has its own L2.
-__device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u; }
-
-// Ready flag of a (chunk, head) record pair: bit 0 set once the records are
-// complete, bits 4:1 the producer's XCD, bit 8 set when the producer also
-// wrote its L2 back to memory (device-scope release).
-constexpr unsigned kReadyReleased = 1u << 8;
 
 // Fused launch, workgroups 0 .. n_prep - 1: the T and P records of every
 // (chunk, head), two at a time (waves 0..3 and waves 4..7 each take one item).
@@ -171,8 +162,6 @@ __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* sme
   }
 }
 
-// Spin limit of a consumer's wait for a ready flag (about 0.1 s of s_sleep 4).
-constexpr int kReadySpinLimit = 1 << 20;
 
 template <int DK, class Eng, typename TIO, typename TO, bool kFused>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
@@ -411,24 +400,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     if (lane == 0) vecb[194] = __builtin_nanf("");
   };
   auto await_ready = [&](int cc, unsigned v0, float* vecb) {
-    unsigned v = (unsigned)__builtin_amdgcn_readfirstlane((int)v0);
-    for (int spin = 0; v == 0u && !poisoned; ++spin) {
-      if (spin >= kReadySpinLimit) {
-        poison(vecb);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(4);
-      v = read_ready(cc);
-    }
-    if (v != 0u && ((v >> 1) & 15u) != xcd_self) {
-      if (v & kReadyReleased) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        wait_vmem();
-      } else {
-        poison(vecb);
-      }
-    }
+    if (!poisoned && !await_ready_flag(ready_ptr(cc), v0, xcd_self)) poison(vecb);
   };
+
 
   // ---------------- prologue ----------------
   if constexpr (kFused) {
@@ -925,7 +899,7 @@ static int device_cu_count() {
 // producers and consumers are resident together.
 static int producer_workgroups(const gdn_shape_t& s, const gdn_debug_t* debug) {
   const int sched = debug ? debug->schedule : GDN_SCHEDULE_AUTO;
-  if (s.gate_per_channel || sched == GDN_SCHEDULE_SPLIT) return 0;
+  if (sched == GDN_SCHEDULE_SPLIT) return 0;
   const int64_t tiles = s.dv / kTileRows;
   const int64_t n_state = (int64_t)s.n_seqs * s.n_heads * tiles;
   // every value tile of a (sequence, head) pair on XCD nh % 8 (block mapping of the state part)

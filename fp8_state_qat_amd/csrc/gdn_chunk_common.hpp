@@ -222,6 +222,43 @@ struct ChunkArgs {
   int n_prep;          // fused launch: workgroups 0 .. n_prep - 1 produce the T and P records
 };
 
+// XCD (accelerator complex die) that runs the calling wave: hardware
+// register XCC_ID, bits 3:0.  The dispatcher hands workgroup b of a launch
+// to XCD b % 8; each XCD has its own L2.
+__device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u; }
+
+// Ready flag of a (chunk, head) record pair: bit 0 set once the records are
+// complete, bits 4:1 the producer's XCD, bit 8 set when the producer also
+// wrote its L2 back to memory (device-scope release).
+constexpr unsigned kReadyReleased = 1u << 8;
+
+// Spin limit of a consumer's wait for a ready flag (about 0.1 s of s_sleep 4).
+constexpr int kReadySpinLimit = 1 << 20;
+
+// Consumer side of the fused launch: wait (bounded) for the ready flag at
+// flag, whose first reading is v0, then make the record readable.  A record
+// written on this XCD sits in the shared L2 and is read through an L1 that
+// never held it in this launch; one written on another XCD needs the
+// producer's device-scope release, and then this wave invalidates its caches
+// (device-scope acquire).  Returns false when the wait runs out or the
+// record cannot be trusted.  The caller's barriers order the other waves'
+// record loads after it.
+__device__ __forceinline__ bool await_ready_flag(const unsigned* flag, unsigned v0, unsigned xcd_self) {
+  unsigned v = (unsigned)__builtin_amdgcn_readfirstlane((int)v0);
+  for (int spin = 0; v == 0u; ++spin) {
+    if (spin >= kReadySpinLimit) return false;
+    __builtin_amdgcn_s_sleep(4);
+    v = (unsigned)__builtin_amdgcn_readfirstlane(
+        (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+  if (((v >> 1) & 15u) != xcd_self) {
+    if (!(v & kReadyReleased)) return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    wait_vmem();
+  }
+  return true;
+}
+
 // The sequential kernel for a per-key-channel gate (gdn_kda.hip); the prep
 // kernel has filled a.T and a.Prec.
 hipError_t launch_kda_state(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream);

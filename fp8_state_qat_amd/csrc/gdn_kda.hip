@@ -30,7 +30,7 @@
 // arrive by direct global->LDS loads issued one chunk ahead.  Then the
 // recurrent suffix (tokens P_n < t <= L_n, QDQ after every write) and the
 // final state store.
-#include "gdn_chunk_common.hpp"
+#include "gdn_prep_item.hpp"
 
 namespace gdn {
 
@@ -87,7 +87,50 @@ struct KdaLds {
   static_assert((3 * DK + 64 + 8) * sizeof(float) <= oV, "suffix buffers do not fit");
 };
 
-template <int DK, class Eng, typename TIO, typename TO>
+// Fused launch, workgroups 0 .. n_prep - 1: the T and P records of every
+// (chunk, head) for a per-key-channel gate, one item at a time, published
+// through the ready flags exactly as the scalar-gate producers do (same
+// item order and XCD assignment, same flag bits; see gdn_chunk.hip).
+template <int DK, typename TIO>
+__device__ __forceinline__ void produce_kda_records(const ChunkArgs& args, char* smem) {
+  PrepArgs a;
+  a.q = args.q; a.k = args.k; a.beta = args.beta; a.g = args.g; a.cu_seqlens = args.cu_seqlens;
+  a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
+  a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
+  const int tid = threadIdx.x;
+  const int H = args.H, NH = args.N * args.H;
+  const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
+  const unsigned xcd = xcd_id();
+  const bool home = xcd == (unsigned)x;
+  const int M = NH > x ? (NH - x + 7) >> 3 : 0;
+  const int64_t total = (int64_t)args.chunk_offs[args.N + 1] * M;
+  for (int64_t m = r; m < total; m += R) {
+    const int c = (int)(m / M), nh = x + 8 * (int)(m % M);
+    const int n = nh / H, h = nh % H;
+    const int seg0 = args.cu_seqlens[n];
+    const int L = args.seq_lens ? args.seq_lens[n] : (args.cu_seqlens[n + 1] - seg0);
+    const int P = args.prefix_lens ? args.prefix_lens[n] : L;
+    if (c * kChunk >= P) continue;  // the same for the whole workgroup
+    const int j = args.chunk_offs[n] + c;
+    // a fresh copy of the lane index per item keeps the compiler from holding
+    // the item's lane-dependent LDS addresses live across the whole loop
+    int tid_i = tid;
+    asm volatile("" : "+v"(tid_i));
+    kda_prep_item<DK, TIO>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, tid_i);
+    wait_vmem();      // this wave's record stores are complete
+    __syncthreads();  // ... in every wave; the LDS is free again
+    if (tid == 0) {
+      unsigned flag = 1u | (xcd << 1);
+      if (!home) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        flag |= kReadyReleased;
+      }
+      __hip_atomic_store(args.ready + ((int64_t)j * H + h), flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int DK, class Eng, typename TIO, typename TO, bool kFused>
 __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args) {
   using Ls = KdaLds<DK, Eng>;
   using E = typename Eng::E;
@@ -97,6 +140,12 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   constexpr bool kSplit = Eng::kSplit;
   constexpr int PLANE = 4 * NKB * 64 * 8;  // elements of one operand plane
   extern __shared__ __align__(16) char smem[];
+  if constexpr (kFused) {
+    if ((int)blockIdx.x < args.n_prep) {
+      produce_kda_records<DK, TIO>(args, smem);
+      return;
+    }
+  }
   E* sKa = reinterpret_cast<E*>(smem + Ls::oKa);
   E* sQa = reinterpret_cast<E*>(smem + Ls::oQa);
   E* sKc = reinterpret_cast<E*>(smem + Ls::oKc);
@@ -124,7 +173,8 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   const int tiles = dv / kTileRows;
   int nh, vt;  // value tiles of one head on one XCD when heads come in groups of 8
   {
-    const int b = blockIdx.x, G = gridDim.x;
+    const int b = (int)blockIdx.x - (kFused ? args.n_prep : 0);
+    const int G = (int)gridDim.x - (kFused ? args.n_prep : 0);
     if (tiles > 1 && G % (8 * tiles) == 0) {
       const int slot8 = b >> 3;
       vt = slot8 % tiles;
@@ -479,6 +529,15 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
 
   // ---- QDQ of the tile once the four amax are in LDS
   auto qdq_step = [&](int c) {
+    if constexpr (kFused) {  // NaN after a failed wait for a ready flag
+      const float pz = sRed[4];
+      if (pz != 1.0f) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[t][i] *= pz;
+      }
+    }
     const bool last = (c == n_chunks - 1);
     const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
     float s_new = 1.0f;
@@ -508,7 +567,30 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
   };
 
+  // Fused launch: T and P of chunk cc come from a producer workgroup through
+  // ready flag (chunk, head); wave 0 waits for it (await_ready_flag) before
+  // the barrier that precedes their loads.  A failed wait sets red[4] to NaN,
+  // which the next QDQ step multiplies into the state.
+  unsigned pend = 0u;
+  const unsigned xcd_self = kFused ? xcd_id() : 0u;
+  auto ready_ptr = [&](int cc) { return args.ready + ((int64_t)(chunk0 + cc) * H + h); };
+  auto load_ready = [&](int cc) { return __hip_atomic_load(ready_ptr(cc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  bool poisoned = false;
+  auto await_ready = [&](int cc, unsigned v0) {
+    if (!poisoned && !await_ready_flag(ready_ptr(cc), v0, xcd_self)) {
+      poisoned = true;
+      if (lane == 0) sRed[4] = __builtin_nanf("");
+    }
+  };
+
   // ---------------- prologue ----------------
+  if constexpr (kFused) {
+    if (w == 0) {
+      if (lane == 0) sRed[4] = 1.0f;
+      if (n_chunks > 0) await_ready(0, load_ready(0));
+    }
+    barrier_lds();
+  }
   if (n_chunks > 0) {
     fetch(0);
     issue_vtp(0);
@@ -532,7 +614,13 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   for (int c = 0; c < n_chunks; ++c) {
     wait_vmem();  // this wave's direct loads are in LDS before the barrier
     barrier_lds();
+    if constexpr (kFused) {
+      if (w == 0 && c + 1 < n_chunks) pend = load_ready(c + 1);  // examined after phase B
+    }
     phase_b(c);
+    if constexpr (kFused) {
+      if (w == 0 && c + 1 < n_chunks) await_ready(c + 1, pend);  // T and P of chunk c + 1 load after the barrier
+    }
     barrier_lds();
     if (c + 1 < n_chunks) {
       build(c + 1);
@@ -611,33 +699,41 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     io<TO>::st(go_ + (int64_t)(seg0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + lane, 0.f);
 }
 
-template <int DK, class Eng, typename TIO, typename TO>
+template <int DK, class Eng, typename TIO, typename TO, bool kFused>
 static hipError_t launch_kda_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  auto kern = kda_fwd_kernel<DK, Eng, TIO, TO>;
-  constexpr size_t lds = KdaLds<DK, Eng>::bytes;
+  auto kern = kda_fwd_kernel<DK, Eng, TIO, TO, kFused>;
+  constexpr size_t prep_lds = KdaPrepLds<DK, TIO>::bytes;  // a producer's item
+  constexpr size_t lds = (kFused && prep_lds > KdaLds<DK, Eng>::bytes) ? prep_lds : KdaLds<DK, Eng>::bytes;
+  static_assert(lds <= 160 * 1024, "LDS budget exceeded");
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
+  const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows) + (kFused ? a.n_prep : 0);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kKdaThreads), lds, stream, a);
   return hipGetLastError();
+}
+
+template <int DK, class Eng, typename TIO, typename TO>
+static hipError_t launch_kda_sched(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
+  return a.n_prep > 0 ? launch_kda_typed<DK, Eng, TIO, TO, true>(s, a, stream)
+                      : launch_kda_typed<DK, Eng, TIO, TO, false>(s, a, stream);
 }
 
 hipError_t launch_kda_state(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
   const bool ob = s.o_dtype == GDN_BF16;
   if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)
-      return ob ? launch_kda_typed<128, EngBF16, uint16_t, uint16_t>(s, a, stream)
-                : launch_kda_typed<128, EngBF16, uint16_t, float>(s, a, stream);
-    return ob ? launch_kda_typed<64, EngBF16, uint16_t, uint16_t>(s, a, stream)
-              : launch_kda_typed<64, EngBF16, uint16_t, float>(s, a, stream);
+      return ob ? launch_kda_sched<128, EngBF16, uint16_t, uint16_t>(s, a, stream)
+                : launch_kda_sched<128, EngBF16, uint16_t, float>(s, a, stream);
+    return ob ? launch_kda_sched<64, EngBF16, uint16_t, uint16_t>(s, a, stream)
+              : launch_kda_sched<64, EngBF16, uint16_t, float>(s, a, stream);
   }
   if (s.dk != 64) return hipErrorNotSupported;
-  return ob ? launch_kda_typed<64, EngF32, float, uint16_t>(s, a, stream)
-            : launch_kda_typed<64, EngF32, float, float>(s, a, stream);
+  return ob ? launch_kda_sched<64, EngF32, float, uint16_t>(s, a, stream)
+            : launch_kda_sched<64, EngF32, float, float>(s, a, stream);
 }
 
 }  // namespace gdn

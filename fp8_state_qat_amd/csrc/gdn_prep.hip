@@ -123,52 +123,12 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
 // two records per (chunk, head) in the layout above.
 // ---------------------------------------------------------------------------
 template <int DK, typename TIO>
-struct KdaPrepLds {
-  static constexpr int LX = DK + 16 / (int)sizeof(TIO);  // k, q row stride (elements)
-  static constexpr int LG = DK + 4;                      // gamma row stride (floats)
-  static constexpr size_t oK = 0;
-  static constexpr size_t oQ = oK + 64 * LX * sizeof(TIO);
-  static constexpr size_t oG = oQ + 64 * LX * sizeof(TIO);
-  static constexpr size_t oA = oG + 64 * LG * sizeof(float);
-  static constexpr size_t oP = oA + 64 * kL64 * sizeof(float);
-  static constexpr size_t oTot = oP + 64 * kL64 * sizeof(float);
-  static constexpr size_t oBeta = oTot + kThreads * sizeof(float);
-  static constexpr size_t bytes = oBeta + 64 * sizeof(float);
-  // once A and P are formed, the solve's X overlays k and q
-  static constexpr size_t oX = oK;
-  static_assert(64 * kL64 * sizeof(float) <= oG - oK, "X does not fit over k and q");
-};
-
-template <typename TIO>
-__device__ __forceinline__ void load4f(const TIO* p, float (&x)[4]) {
-  if constexpr (sizeof(TIO) == 2) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-  } else {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-  }
-}
-
-template <int DK, typename TIO>
 __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
-  using Ls = KdaPrepLds<DK, TIO>;
-  constexpr bool kBF = sizeof(TIO) == 2;
-  constexpr int LX = Ls::LX, LG = Ls::LG, L64 = kL64, NKB = DK / 32;
   extern __shared__ __align__(16) char smem[];
-  TIO* sK = reinterpret_cast<TIO*>(smem + Ls::oK);
-  TIO* sQ = reinterpret_cast<TIO*>(smem + Ls::oQ);
-  float* sG = reinterpret_cast<float*>(smem + Ls::oG);    // gamma * log2(e)
-  float* sA = reinterpret_cast<float*>(smem + Ls::oA);
-  float* sP = reinterpret_cast<float*>(smem + Ls::oP);
-  float* sTot = reinterpret_cast<float*>(smem + Ls::oTot);
-  float* sBeta = reinterpret_cast<float*>(smem + Ls::oBeta);
-  float* sX = reinterpret_cast<float*>(smem + Ls::oX);
-
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
   const int total = a.offs[a.N];
-  if (j >= total) return;  // grid is sized for the worst case
+  if (j >= total) return;
   int lo = 0, hi = a.N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -178,155 +138,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   const int seg0 = a.cu_seqlens[n];
   const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
   const int P = a.prefix_lens ? a.prefix_lens[n] : L;
-  const int t0 = seg0 + c * kChunk;
-  const int nv = min(kChunk, P - c * kChunk);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
-
-  // ---- stage k and q (rows past nv are zero), beta, and the per-channel gate prefix
-  {
-    constexpr int EPS = 16 / (int)sizeof(TIO);
-    constexpr int SPR = DK / EPS;
-    const TIO* gk = reinterpret_cast<const TIO*>(a.k);
-    const TIO* gqv = reinterpret_cast<const TIO*>(a.q);
-    static_assert(64 * SPR % kThreads == 0, "staging geometry");
-#pragma unroll
-    for (int jj = 0; jj < 64 * SPR / kThreads; ++jj) {
-      const int seg = tid + kThreads * jj;
-      const int r = seg / SPR, c0 = (seg % SPR) * EPS;
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u), qv = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nv) {
-        const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c0;
-        kv = *reinterpret_cast<const uint4*>(gk + off);
-        qv = *reinterpret_cast<const uint4*>(gqv + off);
-      }
-      *reinterpret_cast<uint4*>(sK + r * LX + c0) = kv;
-      *reinterpret_cast<uint4*>(sQ + r * LX + c0) = qv;
-    }
-    if (tid < 64) sBeta[tid] = (tid < nv) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;
-  }
-  constexpr int NPART = kThreads / DK, TPP = 64 / NPART;  // token parts of the per-channel scan
-  {
-    const int d = tid % DK, part = tid / DK;
-    float gv[TPP];  // all loads in flight before the scan
-#pragma unroll
-    for (int i = 0; i < TPP; ++i) {
-      const int r = part * TPP + i;
-      gv[i] = (r < nv) ? a.g[((int64_t)(t0 + r) * H + h) * DK + d] : 0.f;
-    }
-    float run = 0.f;
-#pragma unroll
-    for (int i = 0; i < TPP; ++i) {
-      run += gv[i];
-      sG[(part * TPP + i) * LG + d] = run;
-    }
-    sTot[tid] = run;
-  }
-  __syncthreads();
-  {
-    const int d = tid % DK, part = tid / DK;
-    float off = 0.f;
-    for (int pp = 0; pp < part; ++pp) off += sTot[pp * DK + d];
-#pragma unroll
-    for (int i = 0; i < TPP; ++i) {
-      const int r = part * TPP + i;
-      sG[r * LG + d] = (sG[r * LG + d] + off) * 1.4426950408889634f;
-    }
-  }
-  __syncthreads();
-
-  // ---- the ten 16 x 16 tiles (R, S), S <= R, one job each: C[s][r] with
-  // A = k_s exp(gamma_m - gamma_s), B = x_r exp(gamma_r - gamma_m) (x = k for
-  // A, q for P), m = 16 R the first token of block R.  For S < R both factors
-  // are <= 1.  On the diagonal tile the first factor is >= 1: it is used only
-  // when every |gamma_t - gamma_m| of the block stays under 2^kGuard in
-  // magnitude (no overflow, no underflow), else that tile is summed channel
-  // by channel with the exponential of each difference.
-  constexpr float kGuard = 100.f;  // log2 units
-  for (int job = w; job < 10; job += 4) {
-    const int R = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
-    const int S = job - (R * (R + 1)) / 2;
-    const int m = 16 * R;
-    const int s = 16 * S + ln, r = 16 * R + ln;  // A-operand row s, B-operand column r of this lane
-    f32x4 ca = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
-    float span = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float av[8], bk[8], bq[8];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int c0 = 32 * kb + 16 * hh + 4 * gq;  // channels kperm(gq, 4 hh .. 4 hh + 3)
-        const float4 gs4 = *reinterpret_cast<const float4*>(sG + s * LG + c0);
-        const float4 gm4 = *reinterpret_cast<const float4*>(sG + m * LG + c0);
-        const float4 gr4 = *reinterpret_cast<const float4*>(sG + r * LG + c0);
-        const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-        const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
-        const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
-        float ks[4], kr[4], qr[4];
-        load4f(sK + s * LX + c0, ks);
-        load4f(sK + r * LX + c0, kr);
-        load4f(sQ + r * LX + c0, qr);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          span = fmaxf(span, fmaxf(fabsf(gm[i] - gs[i]), fabsf(gr[i] - gm[i])));
-          av[4 * hh + i] = ks[i] * __builtin_amdgcn_exp2f(fminf(gm[i] - gs[i], kGuard));
-          const float f = __builtin_amdgcn_exp2f(fminf(gr[i] - gm[i], kGuard));
-          bk[4 * hh + i] = kr[i] * f;
-          bq[4 * hh + i] = qr[i] * f;
-        }
-      }
-      mma_f32(ca, av, bk);
-      mma_f32(cp, av, bq);
-    }
-    const bool exact = (S < R) || wave_max_dpp(span) < kGuard;
-    if (exact) {
-      // lane holds C[16 S + 4 gq + i][16 R + ln]; zero at and above the diagonal (A), above it (P)
-      const float br = sBeta[r];
-      float va[4], vp[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sc = 16 * S + 4 * gq + i;
-        va[i] = (sc < r) ? br * ca[i] : 0.f;
-        vp[i] = (sc <= r) ? cp[i] : 0.f;
-      }
-      *reinterpret_cast<float4*>(sA + r * L64 + 16 * S + 4 * gq) = make_float4(va[0], va[1], va[2], va[3]);
-      *reinterpret_cast<float4*>(sP + r * L64 + 16 * S + 4 * gq) = make_float4(vp[0], vp[1], vp[2], vp[3]);
-    } else {
-      // diagonal tile with a large in-block decay: pairs s <= r, channel by channel
-      for (int pi = lane; pi < 256; pi += 64) {
-        const int rl = pi >> 4, sl = pi & 15;
-        const int rr = 16 * R + rl, ss = 16 * R + sl;
-        float sa[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
-        if (sl <= rl) {
-          for (int c0 = 0; c0 < DK; c0 += 4) {
-            float kr[4], qr[4], ks[4];
-            load4f(sK + rr * LX + c0, kr);
-            load4f(sQ + rr * LX + c0, qr);
-            load4f(sK + ss * LX + c0, ks);
-            const float4 gr4 = *reinterpret_cast<const float4*>(sG + rr * LG + c0);
-            const float4 gs4 = *reinterpret_cast<const float4*>(sG + ss * LG + c0);
-            const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
-            const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float ke = ks[i] * __builtin_amdgcn_exp2f(gr[i] - gs[i]);
-              sa[i] = fmaf(kr[i], ke, sa[i]);
-              sp[i] = fmaf(qr[i], ke, sp[i]);
-            }
-          }
-        }
-        const float av = (sa[0] + sa[1]) + (sa[2] + sa[3]);
-        const float pv = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-        sA[rr * L64 + ss] = (sl < rl) ? sBeta[rr] * av : 0.f;
-        sP[rr * L64 + ss] = (sl <= rl) ? pv : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-
-  const int64_t rec = ((int64_t)j * H + h) * kTRecBytes;
-  store_record<kBF>(sP, nullptr, reinterpret_cast<char*>(a.P) + rec, threadIdx.x);
-  solve_unit_lower(sA, sX, threadIdx.x);
-  store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + rec, threadIdx.x);
+  kda_prep_item<DK, TIO>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, threadIdx.x);
 }
 
 PrepLayout prep_layout(const gdn_shape_t& s, void* workspace) {

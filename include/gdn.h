@@ -96,8 +96,7 @@ typedef struct {
  * idle, handing each record over through a ready flag (FUSED).  AUTO (also
  * when debug is NULL) fuses when the state kernel's workgroups fill at most
  * half of the compute units; FUSED fuses whenever at least 8 compute units
- * stay free.  Both give bit-identical results.  The per-key-channel gate
- * always runs SPLIT. */
+ * stay free.  Both give bit-identical results, for either gate. */
 #define GDN_SCHEDULE_AUTO 0
 #define GDN_SCHEDULE_SPLIT 1
 #define GDN_SCHEDULE_FUSED 2

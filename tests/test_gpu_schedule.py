@@ -1,4 +1,5 @@
-"""The two schedules of the per-chunk solve give bit-identical results:
+"""The two schedules of the per-chunk solve give bit-identical results, for
+the scalar gate and for a per-key-channel gate:
 SPLIT runs it as its own kernel before the sequential state kernel, FUSED
 inside the state kernel's launch on compute units the state workgroups leave
 idle, each (chunk, head) record handed over through a ready flag.  The
@@ -93,3 +94,27 @@ def test_workspace_reuse_and_garbage():
     home = ((flags.reshape(56, 8) >> 1) & 15) == nh % 8
     print(f"producers on the XCD of their consumers: {int(home.sum())} of {home.size}; "
           f"released device-wide: {int((flags >> 8 & 1).sum())}", flush=True)
+
+
+@pytest.mark.parametrize("flags", [0, 3])
+def test_kda_full_prefill_fused_equals_split(flags):
+    """Per-key-channel gate, B=4, T=4096, H=16, d=128, bf16: the per-channel
+    prep items run on the producer workgroups of the fused launch."""
+    d = gi.device_packed([4096] * 4, 16, 128, 128, per_channel=True, g_scale=0.05, seed=23)
+    split = _run(d, flags, GDN_SCHEDULE_SPLIT, o_dtype=torch.bfloat16)
+    auto = _run(d, flags, GDN_SCHEDULE_AUTO, o_dtype=torch.bfloat16)
+    assert torch.isfinite(auto[1]).all()
+    _same(split, auto, f"KDA full prefill flags={flags}")
+
+
+@pytest.mark.parametrize("io,d", [(gi.F32, 64), (gi.BF16, 128)])
+def test_kda_ragged_prefix_fused_equals_split(io, d):
+    w = gi.make_packed([300, 0, 1, 64, 129, 77], 3, d, d, io_dtype=io, per_channel=True, g_scale=0.05,
+                       seed=29 + d, pads=[2, 0, 5, 0, 63, 1], prefix_lens=[256, 0, 1, 64, 100, 0])
+    dt = gi.device_tensors(w)
+    for flags in (0, 3):
+        a = _run(dt, flags, GDN_SCHEDULE_SPLIT, o_dtype=torch.float32, seq_lens=dt["seq_lens"],
+                 prefix_lens=dt["prefix_lens"])
+        b = _run(dt, flags, GDN_SCHEDULE_FUSED, o_dtype=torch.float32, seq_lens=dt["seq_lens"],
+                 prefix_lens=dt["prefix_lens"])
+        _same(a, b, f"KDA ragged {io} d={d} flags={flags}")
