@@ -8,8 +8,9 @@
 // tile vt).  It walks its sequence chunk by chunk and keeps its slice of the
 // state in registers for the whole sequence.  The 64 x dk state tile is
 // exactly one QDQ tile, so the QDQ amax needs no exchange with other
-// workgroups.  T and P of every chunk come from the prep kernel
-// (gdn_prep.hip) through the workspace.
+// workgroups.  T and P of every chunk come through the workspace, from the
+// prep kernel (gdn_prep.hip) or, in the fused launch, from producer
+// workgroups of this same launch (produce_records below).
 //
 // Waves 0..3 ("chain" waves) carry the state: chain wave c owns value columns
 // 16c..16c+15 of the tile, i.e. dk/16 16x16 accumulator tiles of S^T, and
@@ -28,9 +29,9 @@
 //   2   chain : QDQ: s = amax / 448, S <- RNE_E4M3(S / s) s
 //       helper: the gate scan of the next chunk
 // T = (I + A)^-1 diag(beta) and P[r][s] = exp(gamma_r - gamma_s) q_r . k_s
-// (s <= r) come from the prep kernel as records; the next chunk's k and q
-// (double-buffered), v, T and P arrive by direct global->LDS loads issued as
-// soon as their buffers are free.
+// (s <= r) arrive as records; the next chunk's k (two chunks ahead), q, v, T
+// and P arrive by direct global->LDS loads issued as soon as their buffers
+// are free.
 //
 // U' = T X is U - W S^T with U = T V and W = T (exp(gamma) * K) regrouped, so
 // W is never formed.  Then the recurrent suffix (tokens P_n < t <= L_n, QDQ

@@ -8,8 +8,8 @@
 // gamma_C its value at the chunk's last token, one chunk of n <= 64 tokens
 // (rows past n are zero) does ("o" is the elementwise product)
 //     X  = V - s (K o exp(gamma)) S^T
-//     U' = T X                                  (T from the prep kernel)
-//     O  = s (Q o exp(gamma)) S^T + P U'        (P from the prep kernel)
+//     U' = T X                                  (T: the per-chunk record)
+//     O  = s (Q o exp(gamma)) S^T + P U'        (P: the per-chunk record)
 //     S <- S diag(exp(gamma_C)) + U'^T (K o exp(gamma_C - gamma))
 // where s is the scale of the coded state entering the chunk (1 when it is
 // not coded).  Every exponential has a non-positive argument for
@@ -27,7 +27,9 @@
 //   QDQ    per wave, once the four waves' amax are in LDS
 // with two workgroup barriers.  The raw k, q, g of the next chunk are loaded
 // into registers while the current chunk runs; v and the T and P records
-// arrive by direct global->LDS loads issued one chunk ahead.  Then the
+// arrive by direct global->LDS loads issued one chunk ahead.  The records
+// come from kda_prep_kernel or, in the fused launch, from producer
+// workgroups of this same launch (produce_kda_records).  Then the
 // recurrent suffix (tokens P_n < t <= L_n, QDQ after every write) and the
 // final state store.
 #include "gdn_prep_item.hpp"
