@@ -24,6 +24,7 @@ GDN_QDQ_WRITE = 2
 GDN_SCHEDULE_AUTO = 0
 GDN_SCHEDULE_SPLIT = 1
 GDN_SCHEDULE_FUSED = 2
+GDN_SCHEDULE_FUSED_NO_PRODUCERS = 3   # test hook: every wait for a ready flag runs out
 
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_state_qdq", "gdn_decode_step",
            "gdn_status_string", "gdn_last_error")

@@ -59,7 +59,8 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     tensors bound_offsets, bound_pre, bound_post, scales, torch.cuda.Event
     objects kernel_start, kernel_end (recorded around the sequential state
     kernel) and/or schedule (GDN_SCHEDULE_AUTO, _SPLIT or _FUSED: the
-    per-chunk solve as its own kernel or inside the state kernel's launch).
+    per-chunk solve as its own kernel or inside the state kernel's launch;
+    _FUSED_NO_PRODUCERS, a test hook whose bounded waits all run out).
     Returns (o, final_state)."""
     T, H, dk = k.shape
     dv = v.shape[2]

@@ -156,8 +156,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
     return fail(GDN_ERR_INVALID_ARG, "misaligned buffer (q, k, v, o and states need 16 bytes)");
   if (debug && (debug->bound_pre || debug->bound_post || debug->scales) && !debug->bound_offsets)
     return fail(GDN_ERR_INVALID_ARG, "debug record needs bound_offsets");
-  if (debug && (debug->schedule < GDN_SCHEDULE_AUTO || debug->schedule > GDN_SCHEDULE_FUSED))
-    return fail(GDN_ERR_INVALID_ARG, "debug schedule must be GDN_SCHEDULE_AUTO, _SPLIT or _FUSED");
+  if (debug && (debug->schedule < GDN_SCHEDULE_AUTO || debug->schedule > GDN_SCHEDULE_FUSED_NO_PRODUCERS))
+    return fail(GDN_ERR_INVALID_ARG, "debug schedule must be GDN_SCHEDULE_AUTO, _SPLIT, _FUSED or _FUSED_NO_PRODUCERS");
   if (shape->io_dtype == GDN_F32 && shape->dk != 64)
     return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs are supported with dk = 64 only");
   st = check_device();

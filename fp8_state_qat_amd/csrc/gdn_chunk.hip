@@ -876,8 +876,8 @@ static hipError_t launch_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStre
 
 template <int DK, class Eng, typename TIO, typename TO>
 static hipError_t launch_sched(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  return a.n_prep > 0 ? launch_typed<DK, Eng, TIO, TO, true>(s, a, stream)
-                      : launch_typed<DK, Eng, TIO, TO, false>(s, a, stream);
+  return a.fused ? launch_typed<DK, Eng, TIO, TO, true>(s, a, stream)
+                 : launch_typed<DK, Eng, TIO, TO, false>(s, a, stream);
 }
 
 // Compute units of the current device (0 when it cannot be read).
@@ -900,7 +900,7 @@ static int device_cu_count() {
 // producers and consumers are resident together.
 static int producer_workgroups(const gdn_shape_t& s, const gdn_debug_t* debug) {
   const int sched = debug ? debug->schedule : GDN_SCHEDULE_AUTO;
-  if (sched == GDN_SCHEDULE_SPLIT) return 0;
+  if (sched == GDN_SCHEDULE_SPLIT || sched == GDN_SCHEDULE_FUSED_NO_PRODUCERS) return 0;
   const int64_t tiles = s.dv / kTileRows;
   const int64_t n_state = (int64_t)s.n_seqs * s.n_heads * tiles;
   // every value tile of a (sequence, head) pair on XCD nh % 8 (block mapping of the state part)
@@ -919,7 +919,10 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   ChunkArgs a;
   const PrepLayout L = prep_layout(s, workspace);
   const int n_prep = producer_workgroups(s, debug);
-  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, L, n_prep == 0, stream);
+  // test hook: the fused instantiation without its producers (every wait for a ready flag runs out)
+  const bool no_producers = debug && debug->schedule == GDN_SCHEDULE_FUSED_NO_PRODUCERS;
+  const bool fused = n_prep > 0 || no_producers;
+  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, L, !fused, stream);
   if (e != hipSuccess) return e;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
   a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens; a.prefix_lens = prefix_lens;
@@ -930,7 +933,7 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   a.bound_post = debug ? debug->bound_post : nullptr;
   a.bound_scales = debug ? debug->scales : nullptr;
   a.H = s.n_heads; a.dv = s.dv; a.flags = s.qdq_flags;
-  a.N = s.n_seqs; a.ready = L.ready; a.n_prep = n_prep;
+  a.N = s.n_seqs; a.ready = L.ready; a.n_prep = n_prep; a.fused = fused ? 1 : 0;
   const bool ob = s.o_dtype == GDN_BF16;
   if (debug && debug->kernel_start) {
     e = hipEventRecord((hipEvent_t)debug->kernel_start, stream);

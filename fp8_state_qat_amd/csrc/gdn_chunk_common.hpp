@@ -218,6 +218,7 @@ struct ChunkArgs {
   int dv;
   unsigned flags;
   int N;               // sequences
+  int fused;           // the fused instantiation runs (its waits on the ready flags included)
   unsigned* ready;     // fused launch: one ready flag per (chunk, head), cleared before the launch
   int n_prep;          // fused launch: workgroups 0 .. n_prep - 1 produce the T and P records
 };
@@ -232,8 +233,9 @@ __device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg(
 // wrote its L2 back to memory (device-scope release).
 constexpr unsigned kReadyReleased = 1u << 8;
 
-// Spin limit of a consumer's wait for a ready flag (about 0.1 s of s_sleep 4).
-constexpr int kReadySpinLimit = 1 << 20;
+// Bound of a consumer's wait for one ready flag: 200 ms of the 100 MHz
+// real-time clock.
+constexpr uint64_t kReadyWaitTicks = 20000000;
 
 // Consumer side of the fused launch: wait (bounded) for the ready flag at
 // flag, whose first reading is v0, then make the record readable.  A record
@@ -245,11 +247,14 @@ constexpr int kReadySpinLimit = 1 << 20;
 // record loads after it.
 __device__ __forceinline__ bool await_ready_flag(const unsigned* flag, unsigned v0, unsigned xcd_self) {
   unsigned v = (unsigned)__builtin_amdgcn_readfirstlane((int)v0);
-  for (int spin = 0; v == 0u; ++spin) {
-    if (spin >= kReadySpinLimit) return false;
-    __builtin_amdgcn_s_sleep(4);
-    v = (unsigned)__builtin_amdgcn_readfirstlane(
-        (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (v == 0u) {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kReadyWaitTicks;
+    do {
+      if (__builtin_amdgcn_s_memrealtime() > t_end) return false;
+      __builtin_amdgcn_s_sleep(4);
+      v = (unsigned)__builtin_amdgcn_readfirstlane(
+          (int)__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    } while (v == 0u);
   }
   if (((v >> 1) & 15u) != xcd_self) {
     if (!(v & kReadyReleased)) return false;

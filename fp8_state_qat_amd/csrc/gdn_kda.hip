@@ -720,8 +720,8 @@ static hipError_t launch_kda_typed(const gdn_shape_t& s, const ChunkArgs& a, hip
 
 template <int DK, class Eng, typename TIO, typename TO>
 static hipError_t launch_kda_sched(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  return a.n_prep > 0 ? launch_kda_typed<DK, Eng, TIO, TO, true>(s, a, stream)
-                      : launch_kda_typed<DK, Eng, TIO, TO, false>(s, a, stream);
+  return a.fused ? launch_kda_typed<DK, Eng, TIO, TO, true>(s, a, stream)
+                 : launch_kda_typed<DK, Eng, TIO, TO, false>(s, a, stream);
 }
 
 hipError_t launch_kda_state(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {

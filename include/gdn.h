@@ -100,6 +100,11 @@ typedef struct {
 #define GDN_SCHEDULE_AUTO 0
 #define GDN_SCHEDULE_SPLIT 1
 #define GDN_SCHEDULE_FUSED 2
+/* Test hook for the failure path of the fused launch: the state workgroups
+ * run without their producers, so every wait for a record runs out (200 ms of
+ * the device's real-time clock per workgroup) and the launch still ends; the
+ * state and the outputs after the first chunk come out NaN.  Not for use. */
+#define GDN_SCHEDULE_FUSED_NO_PRODUCERS 3
 
 /*
  * gdn_chunk_fwd -- chunked gated delta rule forward over packed sequences.

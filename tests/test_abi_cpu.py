@@ -82,9 +82,10 @@ def test_chunk_fwd_rejects_null_and_misaligned():
     assert _chunk(_shape(), beta=FAKE + 2) == 1
     dbg = GdnDebug(None, ctypes.c_void_p(FAKE), None, None)   # record without offsets
     assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
-    dbg = GdnDebug(None, None, None, None, None, None, 3)     # unknown schedule
-    assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
-    assert "schedule" in _lib.last_error()
+    for bad in (-1, 4):                                        # unknown schedules
+        dbg = GdnDebug(None, None, None, None, None, None, bad)
+        assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
+        assert "schedule" in _lib.last_error()
 
 
 def test_workspace_size_and_checks():

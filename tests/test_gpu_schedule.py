@@ -7,13 +7,16 @@ parity tests of the other files run with the automatic choice (fused for
 every workload whose state workgroups fill at most half of the GPU), so this
 equality carries their oracle comparisons over to the split schedule, and
 back for the workloads that split automatically."""
+import time
+
 import numpy as np
 import pytest
 import torch
 
 from fp8_state_qat_amd import api
 from fp8_state_qat_amd import inputs as gi
-from fp8_state_qat_amd._lib import GDN_SCHEDULE_AUTO, GDN_SCHEDULE_FUSED, GDN_SCHEDULE_SPLIT
+from fp8_state_qat_amd._lib import (GDN_SCHEDULE_AUTO, GDN_SCHEDULE_FUSED, GDN_SCHEDULE_FUSED_NO_PRODUCERS,
+                                    GDN_SCHEDULE_SPLIT)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,3 +121,28 @@ def test_kda_ragged_prefix_fused_equals_split(io, d):
         b = _run(dt, flags, GDN_SCHEDULE_FUSED, o_dtype=torch.float32, seq_lens=dt["seq_lens"],
                  prefix_lens=dt["prefix_lens"])
         _same(a, b, f"KDA ragged {io} d={d} flags={flags}")
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_fused_wait_runs_out_and_poisons(per_channel):
+    """Failure path of the handoff, forced from the host: the fused launch
+    with no producer workgroups, so no ready flag is ever set.  Each state
+    workgroup's wait is bounded by the device's real-time clock (200 ms);
+    when it runs out the workgroup carries on with NaN in its decay, so the
+    launch ends and the final state of every (sequence, head) with a chunk
+    is NaN instead of a silently wrong value.  A normal call afterwards is
+    unaffected."""
+    kw = dict(per_channel=True, g_scale=0.05) if per_channel else {}
+    d = gi.device_packed([200, 64, 130], 2, 64, 64, seed=31, **kw)
+    t0 = time.perf_counter()
+    o, S = _run(d, 3, GDN_SCHEDULE_FUSED_NO_PRODUCERS, o_dtype=torch.float32)
+    dt = time.perf_counter() - t0
+    print(f"per_channel={per_channel}: call with no producers took {dt:.3f} s; "
+          f"NaN state elements {int(torch.isnan(S).sum())} of {S.numel()}", flush=True)
+    assert torch.isnan(S).all()
+    assert torch.isnan(o).any()
+    assert dt < 30.0
+    a = _run(d, 3, GDN_SCHEDULE_SPLIT, o_dtype=torch.float32)
+    b = _run(d, 3, GDN_SCHEDULE_FUSED, o_dtype=torch.float32)
+    assert torch.isfinite(a[1]).all() and torch.isfinite(a[0]).all()
+    _same(a, b, f"after the failed waits, per_channel={per_channel}")
