@@ -154,6 +154,20 @@ void orc_qdq_tile_f32(const float* x, int64_t n, float* out, float* scale, uint8
     if (scale) *scale = s;
 }
 
+/* QDQ of n_rows rows of row_len fp32 values, each row one group with its
+ * own scale: the per-(token, head) grouping of the W quantizer (#2497 page,
+ * Usage: the W quantizer keeps axes (0, 1, 2) of W [batch, token, head, key],
+ * so its amax runs over the key axis alone).  scales: [n_rows] or NULL. */
+void orc_qdq_rows_f32(const float* x, int64_t n_rows, int row_len,
+                      float* out, float* scales, uint8_t* codes)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t off = r * row_len;
+        orc_qdq_tile_f32(x + off, row_len, out + off, scales ? scales + r : NULL,
+                         codes ? codes + off : NULL);
+    }
+}
+
 /* QDQ of n_states states of dv x dk fp32 values, one tile per 64 rows
  * (rows = value channels).  scales: [n_states][dv/64] or NULL. */
 void orc_qdq_states_f32(const float* x, int64_t n_states, int dv, int dk,

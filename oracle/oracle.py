@@ -46,6 +46,8 @@ def _load():
     lib.orc_e4m3_encode_array.restype = None
     lib.orc_qdq_tile_f32.argtypes = [_fp, ctypes.c_int64, _fp, _fp, _u8p]
     lib.orc_qdq_tile_f32.restype = None
+    lib.orc_qdq_rows_f32.argtypes = [_fp, ctypes.c_int64, ctypes.c_int, _fp, _fp, _u8p]
+    lib.orc_qdq_rows_f32.restype = None
     lib.orc_qdq_states_f32.argtypes = [_fp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                        _fp, _fp, _u8p]
     lib.orc_qdq_states_f32.restype = None
@@ -106,6 +108,23 @@ def qdq_states(x):
     codes = np.empty(x.shape, dtype=np.uint8)
     lib.orc_qdq_states_f32(_ptr(x, _fp), n, dv, dk, _ptr(out, _fp), _ptr(scales, _fp),
                            _ptr(codes, _u8p))
+    return out, scales, codes
+
+
+def qdq_rows(x):
+    """QDQ of fp32 rows [..., n]: every row (last axis) is one group with its
+    own scale amax / 448 (zero guard), the grouping of the W quantizer.
+
+    Returns (out fp32 same shape, scales [...] fp32, codes uint8)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.shape[-1]
+    rows = x.size // n if n else 0
+    out = np.empty_like(x)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    if rows:
+        lib.orc_qdq_rows_f32(_ptr(x, _fp), rows, n, _ptr(out, _fp), _ptr(scales, _fp), _ptr(codes, _u8p))
     return out, scales, codes
 
 

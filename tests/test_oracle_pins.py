@@ -359,3 +359,122 @@ def test_packed_matches_per_sequence():
             np.testing.assert_array_equal(res["o"][s:s + L, h], r["o"])
             np.testing.assert_array_equal(res["S"][n, h], r["S"])
             assert np.all(res["o"][s + L:cu[n + 1], h] == 0)
+
+
+# ---------------------------------------------------------------------------
+# W QDQ (chunked form only; #2497 page: independent dynamic FP8 fake QDQ of
+# the WY-transformed W, grouping per token and head over the key axis)
+# ---------------------------------------------------------------------------
+from oracle.chunked import chunk_step, qdq_w  # noqa: E402
+
+
+def test_w_rows_grouping_and_error_bound():
+    """Each row of W is its own group: a row quantized inside a tile where
+    it is alone (the state QDQ's grouping, pinned above) gives the same bits;
+    every element is within half an E4M3 step of its row's scale, the row
+    maximum survives, a zero row stays zero with scale 1.  Catches a
+    per-column or per-matrix grouping (small rows would flush to zero) and a
+    wrong largest code."""
+    rng = np.random.default_rng(31)
+    W = rng.standard_normal((9, 128)) * (10.0 ** rng.uniform(-6, 3, 9))[:, None]
+    W[4] = 0.0
+    Wq, sc = qdq_w(W)
+    W32 = W.astype(np.float32)
+    for r in range(9):
+        tile = np.zeros((64, 128), np.float32)
+        tile[0] = W32[r]
+        alone, s_alone, _ = orc.qdq_states(tile)
+        np.testing.assert_array_equal(Wq[r].astype(np.float32), alone[0])
+        assert sc[r] == s_alone[0]
+        amax = np.abs(W32[r]).max()
+        if amax == 0:
+            assert sc[r] == 1.0 and np.all(Wq[r] == 0)
+            continue
+        assert np.all(np.abs(Wq[r] - W32[r]) <= 2.0 ** -4 * amax * (1 + 1e-6))
+        i = np.abs(W32[r]).argmax()
+        assert abs(abs(Wq[r, i]) - amax) <= 2.0 ** -22 * amax
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_w_qdq_has_no_effect_from_zero_state(per_channel):
+    """W only enters U' through W S^T: from the zero state one chunk gives the
+    same outputs and state with W QDQ on or off (bitwise), and from a nonzero
+    state it changes them.  Catches QDQ'd W leaking into U = T V or the
+    state update."""
+    q, k, v, b, g = _seq(64, 64, 64, per_channel=per_channel, seed=32,
+                         g_scale=0.05 if per_channel else 0.1)
+    z = np.zeros((64, 64))
+    on = chunk_step(q, k, v, b, g, z, w_qdq=True)
+    off = chunk_step(q, k, v, b, g, z, w_qdq=False)
+    np.testing.assert_array_equal(on["o"], off["o"])
+    np.testing.assert_array_equal(on["S"], off["S"])
+    assert np.linalg.norm(on["Wq"] - on["W"]) > 0
+    S = np.random.default_rng(33).standard_normal((64, 64))
+    on = chunk_step(q, k, v, b, g, S, w_qdq=True)
+    off = chunk_step(q, k, v, b, g, S, w_qdq=False)
+    assert np.linalg.norm(on["o"] - off["o"]) > 1e-6 * np.linalg.norm(off["o"])
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_w_qdq_one_token_chunks_token_form(per_channel):
+    """With one-token chunks, T = beta and W = beta (k * exp(g)): the chunked
+    form with W QDQ is the token recurrence in which the term beta a S k of the
+    delta correction uses the row-quantized beta (a * k) -- written out here
+    token by token, with no solve and no WY algebra.  Catches a W without its
+    gate factor or beta, or quantized along the wrong axis."""
+    L, d = 40, 64
+    q, k, v, b, g = _seq(L, d, d, per_channel=per_channel, seed=34,
+                         g_scale=0.05 if per_channel else 0.1)
+    g = g * 3.0  # gate factors far from 1
+    chk = gdn_chunked(q, k, v, b, g, chunk=1, qdq=False, w_qdq=True)
+    S = np.zeros((d, d))
+    o = np.zeros((L, d))
+    for t in range(L):
+        a = np.exp(g[t])                       # scalar or [dk]
+        w, _ = qdq_w((b[t] * (a * k[t]))[None, :])
+        u = b[t] * v[t] - S @ w[0]
+        o[t] = S @ (a * q[t]) + (q[t] @ k[t]) * u
+        S = S * a + np.outer(u, k[t])
+    np.testing.assert_allclose(chk["o"], o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(chk["S"], S, rtol=1e-12, atol=1e-14)
+
+
+def test_w_qdq_power_of_two_and_sign_invariance():
+    """W does not depend on v, so with W QDQ and state QDQ on, o(4 v) = 4 o(v)
+    and o(-v) = -o(v) bitwise over several chunks."""
+    q, k, v, b, g = _seq(150, 64, 64, seed=35)
+    r = gdn_chunked(q, k, v, b, g, w_qdq=True)
+    r4 = gdn_chunked(q, k, 4.0 * v, b, g, w_qdq=True)
+    rn = gdn_chunked(q, k, -v, b, g, w_qdq=True)
+    np.testing.assert_array_equal(r4["o"], 4.0 * r["o"])
+    np.testing.assert_array_equal(rn["o"], -r["o"])
+
+
+def test_w_qdq_record():
+    """Per-chunk record: Wq is the row QDQ of W, rows past a chunk's end are
+    zero, the boundary states follow the QDQ flags."""
+    q, k, v, b, g = _seq(150, 64, 64, seed=36)
+    r = gdn_chunked(q, k, v, b, g, w_qdq=True, record=True)
+    assert r["W"].shape == (3, 64, 64)
+    for i, n in enumerate((64, 64, 22)):
+        want, sc = qdq_w(r["W"][i, :n])
+        np.testing.assert_array_equal(r["Wq"][i, :n], want)
+        np.testing.assert_array_equal(r["w_scales"][i, :n], sc)
+        assert np.all(r["W"][i, n:] == 0) and np.all(r["Wq"][i, n:] == 0)
+        post, _, _ = orc.qdq_states(r["bound_pre"][i].astype(np.float32))
+        np.testing.assert_array_equal(r["bound_post"][i], post.astype(np.float64))
+    np.testing.assert_array_equal(r["bound_post"][-1], r["S"])
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_chunked_prefix_and_suffix_equal_recurrence(flags):
+    """Chunked prefix of P tokens, then token-by-token writes: with W QDQ off
+    the chunked oracle places every QDQ where the recurrence does (chunk
+    boundaries, the handoff t = P, each later write)."""
+    q, k, v, b, g = _seq(230, 64, 64, seed=37)
+    for P in (0, 1, 64, 100, 230):
+        rec = orc.gdn_sequence(q, k, v, b, g, prefix_len=P, flags=flags)
+        chk = gdn_chunked(q, k, v, b, g, prefix_len=P, flags=flags)
+        for key in ("o", "S"):
+            rel = np.linalg.norm(chk[key] - rec[key]) / np.linalg.norm(rec[key])
+            assert rel < 1e-10, (P, key, rel)
