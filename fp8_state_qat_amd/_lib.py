@@ -20,6 +20,7 @@ GDN_BF16 = 1
 
 GDN_QDQ_CHUNK = 1
 GDN_QDQ_WRITE = 2
+GDN_QDQ_W = 4        # W QDQ in every chunk of the chunked prefix (scalar gate)
 
 GDN_SCHEDULE_AUTO = 0
 GDN_SCHEDULE_SPLIT = 1
@@ -53,6 +54,8 @@ class GdnDebug(ctypes.Structure):
         ("kernel_start", ctypes.c_void_p),
         ("kernel_end", ctypes.c_void_p),
         ("schedule", ctypes.c_int32),
+        ("w_pre", ctypes.c_void_p),
+        ("w_post", ctypes.c_void_p),
     ]
 
 

@@ -40,9 +40,9 @@ def _shape(N, H, dk, dv, T, io_dt, o_dt, per_channel, flags):
     return GdnShape(N, H, dk, dv, T, _DT[io_dt], _DT[o_dt], 1 if per_channel else 0, int(flags))
 
 
-def chunk_workspace_bytes(N, H, dk, dv, T, io_dtype=torch.bfloat16):
+def chunk_workspace_bytes(N, H, dk, dv, T, io_dtype=torch.bfloat16, qdq_flags=0):
     """Device workspace gdn_chunk_fwd needs for this shape (bytes)."""
-    shape = _shape(N, H, dk, dv, T, io_dtype, io_dtype, False, 0)
+    shape = _shape(N, H, dk, dv, T, io_dtype, io_dtype, False, qdq_flags)
     n = _lib.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape))
     if n == 0:
         _lib.check(_lib.GDN_ERR_INVALID_ARG)
@@ -56,7 +56,9 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     [T, H] fp32; g: [T, H] or [T, H, dk] fp32; cu_seqlens: [N+1] int32.
     workspace: optional uint8 device tensor of chunk_workspace_bytes(...)
     bytes (allocated here when None).  debug: optional dict with device
-    tensors bound_offsets, bound_pre, bound_post, scales, torch.cuda.Event
+    tensors bound_offsets, bound_pre, bound_post, scales, w_pre, w_post
+    ([n_bounds, H, 64, dk] fp32, W of each chunk before and after its QDQ,
+    with GDN_QDQ_W in qdq_flags), torch.cuda.Event
     objects kernel_start, kernel_end (recorded around the sequential state
     kernel) and/or schedule (GDN_SCHEDULE_AUTO, _SPLIT or _FUSED: the
     per-chunk solve as its own kernel or inside the state kernel's launch;
@@ -96,7 +98,8 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
             evs.append(None if ev is None else ctypes.c_void_p(ev.cuda_event))
         dbg = GdnDebug(*(_ptr(debug.get(key)) for key in ("bound_offsets", "bound_pre",
                                                           "bound_post", "scales")), *evs,
-                       int(debug.get("schedule", _lib.GDN_SCHEDULE_AUTO)))
+                       int(debug.get("schedule", _lib.GDN_SCHEDULE_AUTO)),
+                       _ptr(debug.get("w_pre")), _ptr(debug.get("w_post")))
     st = _lib.lib().gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                   _ptr(g), _ptr(cu_seqlens), _ptr(seq_lens), _ptr(prefix_lens),
                                   _ptr(initial_state), _ptr(out), _ptr(final_state),

@@ -58,7 +58,7 @@ gdn_status_t check_shape(const gdn_shape_t* s, bool decode) {
     return fail(GDN_ERR_INVALID_ARG, "io_dtype and o_dtype must be GDN_F32 or GDN_BF16");
   if (s->gate_per_channel != 0 && s->gate_per_channel != 1)
     return fail(GDN_ERR_INVALID_ARG, "gate_per_channel must be 0 or 1");
-  if (s->qdq_flags & ~(GDN_QDQ_CHUNK | GDN_QDQ_WRITE))
+  if (s->qdq_flags & ~(GDN_QDQ_CHUNK | GDN_QDQ_WRITE | GDN_QDQ_W))
     return fail(GDN_ERR_INVALID_ARG, "unknown qdq_flags bits 0x%x", s->qdq_flags);
   const int64_t blocks = (int64_t)s->n_seqs * s->n_heads * (s->dv / 64);
   if (blocks >= (int64_t)1 << 31) return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, head, tile) units");
@@ -130,7 +130,7 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape) {
   g_err[0] = 0;
   if (check_shape(shape, false) != GDN_OK) return 0;
-  return gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
+  return gdn::prep_workspace_bytes(*shape);
 }
 
 gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
@@ -142,7 +142,9 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   g_err[0] = 0;
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
-  const size_t need = gdn::prep_workspace_bytes(shape->n_seqs, shape->n_heads, shape->total_tokens);
+  if ((shape->qdq_flags & GDN_QDQ_W) && shape->gate_per_channel)
+    return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_W is supported with the scalar gate only");
+  const size_t need = gdn::prep_workspace_bytes(*shape);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL");
@@ -154,7 +156,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
       !aligned(final_state, 16) || (initial_state && !aligned(initial_state, 16)) ||
       !aligned(beta, 4) || !aligned(g, 4) || !aligned(cu_seqlens, 4))
     return fail(GDN_ERR_INVALID_ARG, "misaligned buffer (q, k, v, o and states need 16 bytes)");
-  if (debug && (debug->bound_pre || debug->bound_post || debug->scales) && !debug->bound_offsets)
+  if (debug && (debug->bound_pre || debug->bound_post || debug->scales || debug->w_pre || debug->w_post) &&
+      !debug->bound_offsets)
     return fail(GDN_ERR_INVALID_ARG, "debug record needs bound_offsets");
   if (debug && (debug->schedule < GDN_SCHEDULE_AUTO || debug->schedule > GDN_SCHEDULE_FUSED_NO_PRODUCERS))
     return fail(GDN_ERR_INVALID_ARG, "debug schedule must be GDN_SCHEDULE_AUTO, _SPLIT, _FUSED or _FUSED_NO_PRODUCERS");

@@ -34,8 +34,12 @@
 // are free.
 //
 // U' = T X is U - W S^T with U = T V and W = T (exp(gamma) * K) regrouped, so
-// W is never formed.  Then the recurrent suffix (tokens P_n < t <= L_n, QDQ
-// after every write) and the final state store.
+// W is never formed.  With W QDQ (kW) W is formed by the producers, row-
+// quantized (#2497: dynamic FP8 QDQ of the WY-transformed W, one scale per
+// token and head) and arrives as its E4M3 codes and row scales w_s, so
+//   1a  chain : U' = T V - s w_s * (W_codes S^T)
+// in place of the line above, the rest unchanged.  Then the recurrent suffix
+// (tokens P_n < t <= L_n, QDQ after every write) and the final state store.
 //
 // LDS operands are kept in MFMA fragment order ("dumps"): fragment f of a
 // buffer is 64 lanes x 8 elements, lane-major, laid out exactly as the lanes
@@ -73,7 +77,9 @@ constexpr int kHelperThreads = 256;  // waves 4..7
 //   XS  [c][plane*NKB + kb]   the state as the A operand of S Q^T, per chain wave
 //   vec (unused), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
 //   red the four chain waves' amax
-template <int DK, class Eng>
+//   W   (kW only) the W record of the chunk as is: 4 NKB bf16 fragments of
+//       codes (A of W S^T, both engines), then the 64 row scales
+template <int DK, class Eng, bool kW = false>
 struct Lds {
   using E = typename Eng::E;
   static constexpr int NKB = DK / 32, NT = DK / 16, NP = Eng::kPlanes;
@@ -89,8 +95,10 @@ struct Lds {
   static constexpr size_t oXS = oXU + 4 * 2 * NP * F;
   static constexpr size_t oVec = oXS + 4 * NKB * NP * F;
   static constexpr size_t oRed = oVec + (3 * 64 + 8) * sizeof(float);
-  static constexpr size_t bytes = oRed + 8 * sizeof(float);
+  static constexpr size_t oW = oRed + 8 * sizeof(float);
+  static constexpr size_t bytes = oW + (kW ? (size_t)w_rec_bytes(DK) : 0);
   static_assert(6 * NP * F == kTRecBytes, "T record and its LDS copy differ");
+  static_assert(oW % 16 == 0, "direct loads need 16-byte aligned LDS");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
   static_assert(oK + (2 * DK + 64 + 8) * sizeof(float) <= oQ, "suffix buffers do not fit");
 };
@@ -112,15 +120,16 @@ struct Lds {
 // (device-scope release and acquire).  Producers never wait, so the
 // consumers' waits end once every producer has been dispatched; producers
 // have the lower workgroup ids.
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool kW>
 __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* smem) {
-  using IL = PrepItemLds<DK, TIO>;
+  using IL = PrepItemLds<DK, TIO, kW>;
   const int half = uniform((int)threadIdx.x >> 8), tid = threadIdx.x & 255;  // half: wave-uniform
   char* lds = smem + half * IL::bytes;
   PrepArgs a;
   a.q = args.q; a.k = args.k; a.beta = args.beta; a.g = args.g; a.cu_seqlens = args.cu_seqlens;
   a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
   a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
+  a.W = const_cast<void*>(args.Wrec); a.w_pre = args.w_pre; a.w_post = args.w_post;
   const int H = args.H, NH = args.N * args.H;
   const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
   const unsigned xcd = xcd_id();
@@ -149,7 +158,7 @@ __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* sme
     // the item's lane-dependent LDS addresses live across the whole loop
     int tid_i = tid;
     asm volatile("" : "+v"(tid_i));
-    prep_item<DK, TIO>(a, j, h, t0, nv, lds, tid_i, active);
+    prep_item<DK, TIO, kW>(a, j, h, t0, nv, lds, tid_i, active);
     wait_vmem();      // this wave's record stores are complete
     __syncthreads();  // ... in every wave of the item; the LDS blocks are free again
     if (active && tid == 0) {
@@ -164,9 +173,27 @@ __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* sme
 }
 
 
-template <int DK, class Eng, typename TIO, typename TO, bool kFused>
+// A fragment of bf16 values (the W codes) as the engine's operand.
+template <class Eng>
+__device__ __forceinline__ typename Eng::Fr ld_bf16_frag(const uint16_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  if constexpr (Eng::kSplit) {
+    return __builtin_bit_cast(typename Eng::Fr, u);
+  } else {
+    typename Eng::Fr f;
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f.v[2 * q] = __uint_as_float(w4[q] << 16);
+      f.v[2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
+    }
+    return f;
+  }
+}
+
+template <int DK, class Eng, typename TIO, typename TO, bool kFused, bool kW>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
-  using Ls = Lds<DK, Eng>;
+  using Ls = Lds<DK, Eng, kW>;
   using E = typename Eng::E;
   using Fr = typename Eng::Fr;
   constexpr int NT = DK / 16;   // state accumulator tiles per chain wave
@@ -176,7 +203,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   extern __shared__ __align__(16) char smem[];
   if constexpr (kFused) {
     if ((int)blockIdx.x < args.n_prep) {
-      produce_records<DK, TIO>(args, smem);
+      produce_records<DK, TIO, kW>(args, smem);
       return;
     }
   }
@@ -190,6 +217,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   E* sXS = reinterpret_cast<E*>(smem + Ls::oXS);
   float* sG2 = reinterpret_cast<float*>(smem + Ls::oVec);  // gamma * log2(e)
   float* sRed = reinterpret_cast<float*>(smem + Ls::oRed);
+  uint16_t* sW = reinterpret_cast<uint16_t*>(smem + Ls::oW);  // kW only
 
   const uint32_t lds0 = lds_base_u32(smem);
   auto lds_of = [&](const void* p) { return lds0 + (uint32_t)(reinterpret_cast<const char*>(p) - smem); };
@@ -339,6 +367,15 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(tdst) + idx * 1024);
     }
   };
+  auto issue_w = [&](int cc, uint16_t* wdst, int wi) {  // the W record of chunk cc (kW)
+    constexpr int NI = w_rec_bytes(DK) / 1024;
+    const char* rec = reinterpret_cast<const char*>(args.Wrec) + ((int64_t)(chunk0 + cc) * H + h) * w_rec_bytes(DK);
+#pragma unroll
+    for (int ii = 0; ii < (NI + 3) / 4; ++ii) {
+      const int idx = wi + 4 * ii;
+      if (idx < NI) lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(wdst) + idx * 1024);
+    }
+  };
   auto issue_q = [&](int cc, E* qdst) {
     const int nv = min(kChunk, P - cc * kChunk);
     const int64_t row0 = seg0 + cc * kChunk;
@@ -435,6 +472,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     if (chain) {
       issue_k(0, sK, c4);
       issue_v(0, sV, sT, c4);
+      if constexpr (kW) issue_w(0, sW, c4);
     } else {
       issue_q(0, sQ);
       issue_p(0, sP);
@@ -452,7 +490,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   auto step = [&](const int c, E* __restrict__ kc, E* __restrict__ qc, E* __restrict__ tb,
                   E* __restrict__ vb, E* __restrict__ pb, E* __restrict__ pn, E* __restrict__ xu,
                   E* __restrict__ xs, E* __restrict__ kt, float* __restrict__ vec,
-                  float* __restrict__ red) {
+                  float* __restrict__ red, uint16_t* __restrict__ wb) {
     float* geg = vec + 64;    // exp(gamma)
     float* gegc = vec + 128;  // exp(gamma_C - gamma)
     float* gmisc = vec + 192; // [0] exp(gamma_C), [1] scale of the state entering the chunk
@@ -474,9 +512,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
       // the operand reads of a product all issued before its first MFMA, so
       // that they overlap one another instead of each waiting for the last
-      Fr kf[4 * NKB];
+      Fr kf[4 * NKB];  // K rows, or with kW the W codes
+      if constexpr (kW) {
 #pragma unroll
-      for (int f = 0; f < 4 * NKB; ++f) kf[f] = Eng::ld(qslot(kc, f));  // f = tt * NKB + kb
+        for (int f = 0; f < 4 * NKB; ++f) kf[f] = ld_bf16_frag<Eng>(wb + (f * 64 + lane) * 8);
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4 * NKB; ++f) kf[f] = Eng::ld(qslot(kc, f));  // f = tt * NKB + kb
+      }
       if (two) {  // uncoded state: hi + lo from the fp32 state
         Fr hi[NKB], lo[NKB];
         state_frags(hi, lo);
@@ -499,6 +542,43 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         tf[p] = Eng::ld(slot(tb, p));
         if constexpr (kSplit) tl[p] = Eng::ld(slot(tb, 6 + p));
       }
+      if constexpr (kW) {
+        // U' = T V - s w_s[t] (W S^T)[t][v]: V enters exactly, as the B
+        // operand (element j = V[32kb + kperm(gq, j)][16c4 + ln])
+        Fr vf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (Eng::kTrRead) {
+            const uint2 r0 = lds_read_tr16(vb + (32 * kb + 4 * gq + (ln >> 2)) * RSV + 16 * c4 + 4 * (ln & 3));
+            const uint2 r1 = lds_read_tr16(vb + (32 * kb + 16 + 4 * gq + (ln >> 2)) * RSV + 16 * c4 + 4 * (ln & 3));
+            vf[kb] = __builtin_bit_cast(Fr, make_uint4(r0.x, r0.y, r1.x, r1.y));
+          } else {
+            float v8[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v8[4 * hh + i] = Eng::to_f(vb[(32 * kb + 16 * hh + 4 * gq + i) * RSV + 16 * c4 + ln]);
+            vf[kb] = Eng::round(v8);
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) uacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+          const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+          Eng::mma(uacc[ti], tf[p], vf[kb]);
+          if constexpr (kSplit) Eng::mma(uacc[ti], tl[p], vf[kb]);
+        }
+        const float* wsc = reinterpret_cast<const float*>(wb + 4 * NKB * 512);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const float4 w4 = *reinterpret_cast<const float4*>(wsc + 16 * tt + 4 * gq);
+          uacc[tt][0] = fmaf(-sc * w4.x, acc[tt][0], uacc[tt][0]);
+          uacc[tt][1] = fmaf(-sc * w4.y, acc[tt][1], uacc[tt][1]);
+          uacc[tt][2] = fmaf(-sc * w4.z, acc[tt][2], uacc[tt][2]);
+          uacc[tt][3] = fmaf(-sc * w4.w, acc[tt][3], uacc[tt][3]);
+        }
+      } else {
       // X[t][v] = V[t][v] - s exp(gamma_t) (K S^T)[t][v], t = 16tt + 4gq + i
       Fr xh[2], xl[2];
 #pragma unroll
@@ -541,6 +621,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           Eng::mma(uacc[ti], tl[p], xh[kb]);
         }
       }
+      }  // kW
       // U' as the A operand of U'^T P^T, for the helper wave
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -657,7 +738,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if (lane == 0) red[c4] = amax;
       }
     } else {
-      if (c + 1 < n_chunks) issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
+      if (c + 1 < n_chunks) {
+        issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
+        if constexpr (kW) issue_w(c + 1, wb, hw);  // and W
+      }
       if constexpr (kFused) {
         if (hw == 1 && c + 2 < n_chunks) pend = load_ready(c + 2);  // checked in phase 2
       }
@@ -769,7 +853,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     E* p0 = sP;
     E* p1 = sP + 6 * NP * 64 * 8;
     step(c, odd ? k1 : k0, sQ, sT, sV, odd ? p1 : p0, odd ? p0 : p1, sXU, sXS,
-         Eng::kTrRead ? nullptr : sKT, sG2, sRed);
+         Eng::kTrRead ? nullptr : sKT, sG2, sRed, sW);
   }
 
   if (st_coded) {  // back to the state values: code * s
@@ -857,11 +941,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     io<TO>::st(go_ + (int64_t)(seg0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + lane, 0.f);
 }
 
-template <int DK, class Eng, typename TIO, typename TO, bool kFused>
+template <int DK, class Eng, typename TIO, typename TO, bool kFused, bool kW>
 static hipError_t launch_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  auto kern = chunk_fwd_kernel<DK, Eng, TIO, TO, kFused>;
-  constexpr size_t item_lds = 2 * (size_t)PrepItemLds<DK, TIO>::bytes;  // a producer's two items
-  constexpr size_t lds = (kFused && item_lds > Lds<DK, Eng>::bytes) ? item_lds : Lds<DK, Eng>::bytes;
+  auto kern = chunk_fwd_kernel<DK, Eng, TIO, TO, kFused, kW>;
+  constexpr size_t item_lds = 2 * (size_t)PrepItemLds<DK, TIO, kW>::bytes;  // a producer's two items
+  constexpr size_t state_lds = Lds<DK, Eng, kW>::bytes;
+  constexpr size_t lds = (kFused && item_lds > state_lds) ? item_lds : state_lds;
   static_assert(lds <= 160 * 1024, "LDS budget exceeded");
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
@@ -876,8 +961,11 @@ static hipError_t launch_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStre
 
 template <int DK, class Eng, typename TIO, typename TO>
 static hipError_t launch_sched(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  return a.fused ? launch_typed<DK, Eng, TIO, TO, true>(s, a, stream)
-                 : launch_typed<DK, Eng, TIO, TO, false>(s, a, stream);
+  if (a.Wrec != nullptr)
+    return a.fused ? launch_typed<DK, Eng, TIO, TO, true, true>(s, a, stream)
+                   : launch_typed<DK, Eng, TIO, TO, false, true>(s, a, stream);
+  return a.fused ? launch_typed<DK, Eng, TIO, TO, true, false>(s, a, stream)
+                 : launch_typed<DK, Eng, TIO, TO, false, false>(s, a, stream);
 }
 
 // Compute units of the current device (0 when it cannot be read).
@@ -922,11 +1010,14 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   // test hook: the fused instantiation without its producers (every wait for a ready flag runs out)
   const bool no_producers = debug && debug->schedule == GDN_SCHEDULE_FUSED_NO_PRODUCERS;
   const bool fused = n_prep > 0 || no_producers;
-  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, L, !fused, stream);
+  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, L, !fused,
+                             debug ? debug->w_pre : nullptr, debug ? debug->w_post : nullptr, stream);
   if (e != hipSuccess) return e;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
   a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens; a.prefix_lens = prefix_lens;
-  a.chunk_offs = L.offs; a.T = L.T; a.Prec = L.P;
+  a.chunk_offs = L.offs; a.T = L.T; a.Prec = L.P; a.Wrec = L.W;
+  a.w_pre = debug ? debug->w_pre : nullptr;
+  a.w_post = debug ? debug->w_post : nullptr;
   a.init = initial_state; a.o = o; a.fin = final_state;
   a.bound_offsets = debug ? debug->bound_offsets : nullptr;
   a.bound_pre = debug ? debug->bound_pre : nullptr;

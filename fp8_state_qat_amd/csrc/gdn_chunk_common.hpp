@@ -207,6 +207,9 @@ struct ChunkArgs {
   const int32_t* chunk_offs;  // prefix sums of ceil(P_n / 64) (prep kernel)
   const void* T;              // one T record per (chunk, head) (prep kernel or producer workgroups)
   const void* Prec;           // one P record per (chunk, head), the same way
+  const void* Wrec;           // W QDQ: one W record per (chunk, head), the same way
+  float* w_pre;               // optional debug record of W (producer workgroups)
+  float* w_post;
   const float* init;
   void* o;
   float* fin;

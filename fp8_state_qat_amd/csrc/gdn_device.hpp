@@ -96,6 +96,13 @@ __device__ __forceinline__ float dpp_max(float v) {
   const int m = __builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false);
   return fmaxf(v, __int_as_float(m));
 }
+// Max over each row of 16 lanes; every lane of the row receives it.
+__device__ __forceinline__ float row16_max_dpp(float v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_max<0x141>(v);  // row_half_mirror
+  return dpp_max<0x140>(v);  // row_mirror
+}
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]
   v = dpp_max<0x4E>(v);   // quad_perm [2, 3, 0, 1]

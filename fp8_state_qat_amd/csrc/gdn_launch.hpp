@@ -27,27 +27,38 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
 // for both engines.
 constexpr int kTRecBytes = 12288;
 
+// With W QDQ, a third record per (chunk, head): the E4M3 codes of the
+// row-quantized W = T (K * exp(gamma)) as bf16 values (exact), in the
+// fragment order of the sequential kernel's k dump without its rotation
+// (fragment f = tt * dk / 32 + kb, lane l holds W[16 tt + l % 16][32 kb +
+// 8 (l / 16) .. + 7]), then one 1 KiB block whose first 64 floats are the
+// row scales.
+constexpr int w_rec_bytes(int dk) { return dk * 128 + 1024; }
+
 // The chunk workspace: int32 chunk offsets [N + 1] and the largest chunk
 // count of a sequence (padded to 256 bytes), one uint32 ready flag per
 // (chunk, head) (padded to 256 bytes; used by the fused launch), then the T
-// records and the P records, all sized for the worst-case chunk count
-// ceil(total_tokens / 64) + N.
+// records, the P records and, with W QDQ, the W records, all sized for the
+// worst-case chunk count ceil(total_tokens / 64) + N.
 struct PrepLayout {
   int32_t* offs;
   unsigned* ready;
   void* T;
   void* P;
+  void* W;        // null without W QDQ
   int64_t items;  // (chunk, head) slots
   size_t bytes;   // total workspace bytes
 };
 PrepLayout prep_layout(const gdn_shape_t& s, void* workspace);
-size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens);
+size_t prep_workspace_bytes(const gdn_shape_t& s);
 
-// Chunk offsets, then (records true) the T and P records of every (chunk,
-// head); with records false the ready flags are cleared instead, for a fused
-// launch that produces the records itself.
+// Chunk offsets, then (records true) the T and P (and W) records of every
+// (chunk, head); with records false the ready flags are cleared instead, for
+// a fused launch that produces the records itself.  w_pre / w_post: the
+// optional W record of the debug struct (null when absent).
 hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                        const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
-                       const int32_t* prefix_lens, const PrepLayout& L, bool records, hipStream_t stream);
+                       const int32_t* prefix_lens, const PrepLayout& L, bool records, float* w_pre,
+                       float* w_post, hipStream_t stream);
 
 }  // namespace gdn

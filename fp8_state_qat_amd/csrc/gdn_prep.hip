@@ -15,7 +15,8 @@
 // ceil(P_n / 64)) and the largest chunk count of a sequence, padded to 256
 // bytes; one uint32 ready flag per (chunk, head) (used by the fused launch of
 // the scalar-gate kernel), padded to 256 bytes; then one 12 KiB T record per
-// (chunk, head), then one P record per (chunk, head) of the same layout.  A
+// (chunk, head), then one P record per (chunk, head) of the same layout, then
+// with W QDQ one W record per (chunk, head) (layout in gdn_launch.hpp).  A
 // record holds the six nonzero 16 x 32 fragments of a block lower-triangular
 // 64 x 64 matrix M, pair p = (ti, kb) in (0,0) (1,0) (2,0) (3,0) (2,1) (3,1):
 // lane l of fragment p holds M[16 ti + l % 16][32 kb + kperm(l / 16, j)] for
@@ -86,9 +87,10 @@ __global__ __launch_bounds__(kThreads) void chunk_offsets_kernel(const int32_t* 
 }
 
 // One workgroup (4 waves) per (chunk, head).  TIO: uint16_t (bf16) or float.
-template <int DK, typename TIO>
-__global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
-  __shared__ __align__(16) char lds[PrepItemLds<DK, TIO>::bytes];
+// kW: W QDQ, the W record too (its LDS block is dynamic: over 64 KiB).
+template <int DK, typename TIO, bool kW>
+__global__ __launch_bounds__(kThreads, kW ? 2 : 3) void chunk_prep_kernel(PrepArgs a) {
+  extern __shared__ __align__(16) char lds[];
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
   const int total = a.offs[a.N];
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_prep_kernel(PrepArgs a) {
   const int seg0 = a.cu_seqlens[n];
   const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
   const int P = a.prefix_lens ? a.prefix_lens[n] : L;
-  prep_item<DK, TIO>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), lds, threadIdx.x, true);
+  prep_item<DK, TIO, kW>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), lds, threadIdx.x, true);
 }
 
 
@@ -150,23 +152,33 @@ PrepLayout prep_layout(const gdn_shape_t& s, void* workspace) {
   const size_t ready_bytes = ((size_t)L.items * 4 + 255) / 256 * 256;
   L.offs = nullptr;
   L.ready = nullptr;
-  L.T = L.P = nullptr;
+  L.T = L.P = L.W = nullptr;
+  const size_t w_bytes = (s.qdq_flags & GDN_QDQ_W) ? (size_t)L.items * w_rec_bytes(s.dk) : 0;
   if (w != nullptr) {
     L.offs = reinterpret_cast<int32_t*>(w);
     L.ready = reinterpret_cast<unsigned*>(w + offs_bytes);
     L.T = w + offs_bytes + ready_bytes;
     L.P = w + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes;
+    if (w_bytes) L.W = w + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2;
   }
-  L.bytes = offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2;
+  L.bytes = offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2 + w_bytes;
   return L;
 }
 
-size_t prep_workspace_bytes(int64_t n_seqs, int64_t n_heads, int64_t total_tokens) {
-  gdn_shape_t s{};
-  s.n_seqs = (int32_t)n_seqs;
-  s.n_heads = (int32_t)n_heads;
-  s.total_tokens = total_tokens;
-  return prep_layout(s, nullptr).bytes;
+size_t prep_workspace_bytes(const gdn_shape_t& s) { return prep_layout(s, nullptr).bytes; }
+
+template <int DK, typename TIO, bool kW>
+static hipError_t launch_chunk_prep(dim3 grid, const PrepArgs& a, hipStream_t stream) {
+  auto kern = chunk_prep_kernel<DK, TIO, kW>;
+  constexpr size_t lds = PrepItemLds<DK, TIO, kW>::bytes;
+  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
 }
 
 template <int DK, typename TIO>
@@ -185,7 +197,8 @@ static hipError_t launch_kda_prep(dim3 grid, const PrepArgs& a, hipStream_t stre
 
 hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                        const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
-                       const int32_t* prefix_lens, const PrepLayout& L, bool records, hipStream_t stream) {
+                       const int32_t* prefix_lens, const PrepLayout& L, bool records, float* w_pre,
+                       float* w_post, hipStream_t stream) {
   // with records false the fused launch produces them and needs cleared ready flags
   const int64_t zero_blocks = records ? 1 : std::min<int64_t>(64, std::max<int64_t>(1, (L.items + 4095) / 4096));
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3((unsigned)zero_blocks), dim3(kThreads), 0, stream, cu_seqlens,
@@ -194,7 +207,9 @@ hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const
   PrepArgs a;
   a.q = q; a.k = k; a.beta = beta; a.g = g; a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens;
   a.prefix_lens = prefix_lens; a.offs = L.offs; a.T = L.T; a.P = L.P; a.N = s.n_seqs; a.H = s.n_heads;
+  a.W = L.W; a.w_pre = w_pre; a.w_post = w_post;
   const dim3 grid((unsigned)L.items);
+  const bool wq = L.W != nullptr;
   if (s.gate_per_channel) {
     if (s.io_dtype == GDN_BF16)
       return s.dk == 128 ? launch_kda_prep<128, uint16_t>(grid, a, stream)
@@ -204,14 +219,14 @@ hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const
   }
   if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)
-      hipLaunchKernelGGL((chunk_prep_kernel<128, uint16_t>), grid, dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((chunk_prep_kernel<64, uint16_t>), grid, dim3(kThreads), 0, stream, a);
-  } else {
-    if (s.dk != 64) return hipErrorNotSupported;  // fp32 inputs: dk = 64 only
-    hipLaunchKernelGGL((chunk_prep_kernel<64, float>), grid, dim3(kThreads), 0, stream, a);
+      return wq ? launch_chunk_prep<128, uint16_t, true>(grid, a, stream)
+                : launch_chunk_prep<128, uint16_t, false>(grid, a, stream);
+    return wq ? launch_chunk_prep<64, uint16_t, true>(grid, a, stream)
+              : launch_chunk_prep<64, uint16_t, false>(grid, a, stream);
   }
-  return hipGetLastError();
+  if (s.dk != 64) return hipErrorNotSupported;  // fp32 inputs: dk = 64 only
+  return wq ? launch_chunk_prep<64, float, true>(grid, a, stream)
+            : launch_chunk_prep<64, float, false>(grid, a, stream);
 }
 
 }  // namespace gdn

@@ -11,7 +11,11 @@
 //     T       = (I + A)^-1 diag(beta)                         (exact solve)
 //     P[t][s] = exp(gamma_t - gamma_s) q_t . k_s              (s <= t)
 // T and P go to the workspace as records in MFMA fragment order (layout at
-// the top of gdn_prep.hip).
+// the top of gdn_prep.hip).  With W QDQ (#2497: independent dynamic FP8 QDQ
+// of the WY-transformed W, one scale per token and head) also
+//     W       = T (K * exp(gamma)),   W <- RNE_E4M3(W / s_r) s_r per row r,
+//     s_r     = max_c |W[r][c]| / 448 (1 when that is not positive)
+// as a third record (codes and row scales, layout in gdn_launch.hpp).
 #pragma once
 
 #include "gdn_chunk_common.hpp"
@@ -29,6 +33,9 @@ struct PrepArgs {
   const int32_t* offs;
   void* T;        // one record of kTRecBytes per (chunk, head)
   void* P;        // one P record per (chunk, head)
+  void* W;        // W QDQ: one W record (w_rec_bytes(dk)) per (chunk, head)
+  float* w_pre;   // optional debug record of W before / after its QDQ,
+  float* w_post;  // [chunk, head, 64, dk]
   int N;
   int H;
 };
@@ -139,18 +146,21 @@ __device__ __forceinline__ void store_record(const float* M, const float* colsca
 // XOR-swizzled by row (piece p of row r at slot p ^ (r % PPR)), so that
 // direct loads fill them 1 KiB at a time and the fragment reads of 16 rows at
 // one column hit different banks; once A and P are formed the solve's X
-// overlays them.  Then A, the scaled log-gates and beta.
-template <int DK, typename TIO>
+// overlays them (with W QDQ, whose product still reads K, X has a block of
+// its own at the end).  Then A, the scaled log-gates and beta.
+template <int DK, typename TIO, bool kW = false>
 struct PrepItemLds {
   static constexpr int RB = DK * (int)sizeof(TIO);  // bytes per k or q row
   static constexpr int PPR = RB / 16;               // pieces per row
   static constexpr int KQ = 2 * 64 * RB;
-  static constexpr int KX = (KQ > 64 * kL64 * 4) ? KQ : 64 * kL64 * 4;
+  static constexpr int KX = (KQ > 64 * kL64 * 4 || kW) ? KQ : 64 * kL64 * 4;
   static constexpr int oA = KX;
   static constexpr int oG2 = oA + 64 * kL64 * 4;
   static constexpr int oBeta = oG2 + 64 * 4;
-  static constexpr int bytes = oBeta + 64 * 4;
+  static constexpr int oX = kW ? oBeta + 64 * 4 : 0;
+  static constexpr int bytes = oBeta + 64 * 4 + (kW ? 64 * kL64 * 4 : 0);
   static_assert(bytes % 16 == 0, "item LDS blocks stay 16-byte aligned");
+  static_assert(!kW || 64 * DK * 2 <= 64 * RB, "W codes are staged over the k rows");
 };
 
 // The records of chunk j (tokens t0 .. t0 + nv - 1 of the packed inputs), head
@@ -158,17 +168,17 @@ struct PrepItemLds {
 // (PrepItemLds bytes, 16-byte aligned).  Contains workgroup barriers; with
 // active false the waves only take part in them.  On return this wave's
 // record stores may still be in flight.
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool kW = false>
 __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t0, int nv, char* lds,
                                           int tid, bool active) {
-  using IL = PrepItemLds<DK, TIO>;
+  using IL = PrepItemLds<DK, TIO, kW>;
   constexpr bool kBF = sizeof(TIO) == 2;
   constexpr int L64 = kL64;
   constexpr int NKB = DK / 32;
   constexpr int RB = IL::RB, PPR = IL::PPR;
   const char* sK = lds;
   const char* sQ = lds + 64 * RB;
-  float* sX = reinterpret_cast<float*>(lds);
+  float* sX = reinterpret_cast<float*>(lds + IL::oX);
   float* sA = reinterpret_cast<float*>(lds + IL::oA);
   float* sG2 = reinterpret_cast<float*>(lds + IL::oG2);
   float* sBeta = reinterpret_cast<float*>(lds + IL::oBeta);
@@ -305,6 +315,128 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t
 
   solve_unit_lower(sA, sX, tid, active);
   if (active) store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes, tid);
+
+  if constexpr (kW) {
+    // ---- W = X diag(beta exp(gamma)) K on the MFMA: wave w forms rows
+    // 16w .. 16w + 15 (lane holds W[16w + 4gq + i][16ct + ln]), so every row
+    // lies in one wave.  A = X' rows (k = tokens s, only the block-lower
+    // part: s / 16 <= w), B = K with k = tokens (bf16: two transpose reads
+    // per fragment; fp32: one read per element).
+    constexpr int NT = DK / 16;
+    f32x4 wacc[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) wacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active) {
+      const int wr = 16 * w + ln;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (2 * kb > w) break;  // wave-uniform: the block-upper part of X is zero
+        float xa[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int s = 32 * kb + (jj < 4 ? 4 * gq + jj : 16 + 4 * gq + (jj - 4));
+          xa[jj] = ((s >> 4) <= w) ? sX[wr * L64 + s] * sBeta[s] * __builtin_amdgcn_exp2f(sG2[s]) : 0.f;
+        }
+        if constexpr (kBF) {
+          // X' as three bf16 planes (24 significant bits): W keeps fp32
+          // accuracy, so its codes differ from the oracle's only at midpoints
+          uint32_t hv[4], mv[4], lv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            hv[q] = pack_bf16x2(xa[2 * q], xa[2 * q + 1]);
+            split_bf16x2(xa[2 * q] - bf16_lo(hv[q]), xa[2 * q + 1] - bf16_hi(hv[q]), mv[q], lv[q]);
+          }
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+          const bf16x8 am = __builtin_bit_cast(bf16x8, make_uint4(mv[0], mv[1], mv[2], mv[3]));
+          const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
+          // lane 4kk + qq of a 16-lane group points at K[s0 + kk][16ct + 4qq .. + 3], so
+          // lane ln receives K[s0 + 0..3][16ct + ln]
+          const int kk = ln >> 2, qq = ln & 3;
+          const int s0 = 32 * kb + 4 * gq, s1 = s0 + 16;
+          bf16x8 bfr[NT];
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            const uint2 b0 = lds_read_tr16(sK + kq_at(s0 + kk, 16 * ct + 4 * qq));
+            const uint2 b1 = lds_read_tr16(sK + kq_at(s1 + kk, 16 * ct + 4 * qq));
+            bfr[ct] = __builtin_bit_cast(bf16x8, make_uint4(b0.x, b0.y, b1.x, b1.y));
+          }
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            mma_bf16(wacc[ct], ah, bfr[ct]);
+            mma_bf16(wacc[ct], am, bfr[ct]);
+            mma_bf16(wacc[ct], al, bfr[ct]);
+          }
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) {
+            float bv[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const int s = 32 * kb + (jj < 4 ? 4 * gq + jj : 16 + 4 * gq + (jj - 4));
+              bv[jj] = *reinterpret_cast<const float*>(sK + kq_at(s, 16 * ct + ln));
+            }
+            mma_f32(wacc[ct], xa, bv);
+          }
+        }
+      }
+    }
+    // row scales (a row is one lane row of 16 across the NT tiles) and codes
+    float sc[4], rc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) m = fmaxf(m, fabsf(wacc[ct][i]));
+      sc[i] = qdq_scale(row16_max_dpp(m));
+      rc[i] = 1.0f / sc[i];
+    }
+    float cw[NT][4];
+#pragma unroll
+    for (int ct = 0; ct < NT; ct += 2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn(wacc[ct][i], sc[i], rc[i]),
+                                                      div_rn(wacc[ct + 1][i], sc[i], rc[i]), 0, false);
+        cw[ct][i] = __builtin_amdgcn_cvt_f32_fp8(p, 0);
+        cw[ct + 1][i] = __builtin_amdgcn_cvt_f32_fp8(p, 1);
+      }
+    if (active && (a.w_pre != nullptr || a.w_post != nullptr)) {
+      const int64_t base = ((int64_t)j * H + h) * 64 * DK;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = (16 * w + 4 * gq + i) * DK + 16 * ct + ln;
+          if (a.w_pre) a.w_pre[base + e] = wacc[ct][i];
+          if (a.w_post) a.w_post[base + e] = cw[ct][i] * sc[i];
+        }
+    }
+    __syncthreads();  // every wave is done with K and X
+    // codes as bf16 (exact) row-major over the k rows, row scales over the q rows
+    uint16_t* stage = reinterpret_cast<uint16_t*>(lds);
+    float* ssc = reinterpret_cast<float*>(lds + 64 * RB);
+    if (active) {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stage[(16 * w + 4 * gq + i) * DK + 16 * ct + ln] = float_to_bf16_bits(cw[ct][i]);
+      if (ln == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ssc[16 * w + 4 * gq + i] = sc[i];
+      }
+    }
+    __syncthreads();
+    if (active) {
+      char* wrec = reinterpret_cast<char*>(a.W) + ((int64_t)j * H + h) * w_rec_bytes(DK);
+      constexpr int NF = 4 * NKB;  // fragments: f = tt * NKB + kb
+      for (int slot = tid; slot < NF * 64; slot += kThreads) {
+        const int f = slot >> 6, l = slot & 63;
+        const int r = 16 * (f / NKB) + (l & 15), c0 = 32 * (f % NKB) + 8 * (l >> 4);
+        *reinterpret_cast<uint4*>(wrec + slot * 16) = *reinterpret_cast<const uint4*>(stage + r * DK + c0);
+      }
+      if (tid < 64) reinterpret_cast<float*>(wrec + NF * 1024)[tid] = ssc[tid];
+    }
+  }
 }
 
 template <int DK, typename TIO>

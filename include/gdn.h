@@ -21,6 +21,13 @@
  *   - Prefill -> decode handoff (#2519 "What does this PR do?", step 3): QDQ
  *     at the handoff and after every later recurrent write; each output is
  *     taken from the updated working state before that QDQ.
+ *   - Optional W QDQ (#2497 "What does this PR do?": independent dynamic FP8
+ *     fake QDQ of the WY-transformed W; Usage: grouping per token and head):
+ *     per chunk W = T (K * exp(gamma)) with T = (I + A)^-1 diag(beta) and
+ *     gamma the in-chunk cumulative log-gate; every row of W (one token of
+ *     one head, all dk keys) gets its own scale amax / 448 (same zero guard)
+ *     and W <- RNE_E4M3(W / s) * s before the pseudo-values
+ *     U' = T V - W S^T use it.
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers on the current HIP device unless
@@ -61,6 +68,8 @@ typedef enum {
 /* qdq_flags bits */
 #define GDN_QDQ_CHUNK 1u   /* QDQ after every 64-token chunk of the chunked prefix and at its end (t = P) */
 #define GDN_QDQ_WRITE 2u   /* QDQ at the handoff t = P and after every recurrent write t > P */
+#define GDN_QDQ_W 4u       /* W QDQ in every chunk of the chunked prefix (scalar gate only; */
+                           /* gdn_decode_step and the recurrent suffix have no W and ignore it) */
 
 typedef struct {
     int32_t n_seqs;            /* N >= 1 */
@@ -77,7 +86,7 @@ typedef struct {
 /* Optional per-boundary record of the chunked prefix, for parity checks, and
  * a timing hook.  Boundary b of sequence n is b = bound_offsets[n] + i for its
  * i-th chunk end (i = 0 .. ceil(P_n / 64) - 1).  All pointers nullable; the
- * record needs bound_offsets when any of its three arrays is set. */
+ * record needs bound_offsets when any of its five arrays is set. */
 typedef struct {
     const int32_t* bound_offsets;  /* [N + 1] device; prefix sums of ceil(P_n / 64) */
     float* bound_pre;              /* [n_bounds, H, dv, dk] state after the chunk, before QDQ */
@@ -88,6 +97,9 @@ typedef struct {
                                    /* a separate per-chunk solve kernel runs before kernel_start, */
                                    /* a fused one inside the bracket) */
     int32_t schedule;              /* GDN_SCHEDULE_*: how the per-chunk solve is scheduled */
+    float* w_pre;                  /* [n_bounds, H, 64, dk] W of chunk b before its QDQ (GDN_QDQ_W) */
+    float* w_post;                 /* [n_bounds, H, 64, dk] W after QDQ; rows past the chunk's */
+                                   /* end are 0.  Both written only with GDN_QDQ_W. */
 } gdn_debug_t;
 
 /* gdn_debug_t.schedule.  The per-chunk solve (T and P records of every chunk
@@ -148,8 +160,10 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape,
  * gdn_chunk_fwd_workspace_bytes -- bytes of device workspace gdn_chunk_fwd
  * needs for this shape: the per-chunk solve T = (I + A)^-1 diag(beta) and the
  * decayed, masked P = Q K^T of every (chunk, head) (12 KiB each, for the
- * worst-case chunk count ceil(total_tokens / 64) + n_seqs) plus the chunk
- * offsets.  Returns 0 for an invalid shape (gdn_last_error() says why).
+ * worst-case chunk count ceil(total_tokens / 64) + n_seqs), with GDN_QDQ_W
+ * the quantized W of every (chunk, head) (dk * 128 + 1024 bytes each), plus
+ * the chunk offsets and one ready flag per (chunk, head).  Returns 0 for an
+ * invalid shape (gdn_last_error() says why).
  */
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape);
 

@@ -65,7 +65,7 @@ def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None, ws=FAKE, ws_by
 @pytest.mark.parametrize("kw,status", [
     (dict(n_seqs=0), 1), (dict(n_heads=0), 1), (dict(dv=96), 1), (dict(dk=96), 2),
     (dict(dk=32), 2), (dict(dv=512), 2), (dict(total_tokens=-1), 1), (dict(io_dtype=7), 1),
-    (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=4), 1),
+    (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=8), 1),
     (dict(io_dtype=0, dk=128), 2), (dict(io_dtype=0, dk=128, gate_per_channel=1), 2),
 ])
 def test_chunk_fwd_rejects_bad_shape(kw, status):
@@ -103,6 +103,21 @@ def test_workspace_size_and_checks():
     assert _chunk(s, ws_bytes=n - 1) == 1
     assert _chunk(s, ws=0) == 1
     assert _chunk(s, ws=FAKE + 64) == 1
+
+
+def test_w_qdq_flag():
+    """GDN_QDQ_W adds one W record per chunk and head (the codes of 64 rows x
+    dk as bf16 and a 1 KiB block for the row scales); it is rejected with a
+    per-key-channel gate, and unknown flag bits stay rejected."""
+    base = _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130))
+    for dk in (64, 128):
+        w = _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, dk=dk, qdq_flags=3 | _lib.GDN_QDQ_W))
+        assert w == base + (3 + 3) * 2 * (dk * 128 + 1024)
+    assert _chunk(_shape(gate_per_channel=1, qdq_flags=_lib.GDN_QDQ_W)) == 2
+    assert "scalar gate" in _lib.last_error()
+    assert _chunk(_shape(qdq_flags=8)) == 1
+    dbg = GdnDebug(None, None, None, None, None, None, 0, ctypes.c_void_p(FAKE), None)  # W record without offsets
+    assert _chunk(_shape(qdq_flags=7), dbg=ctypes.byref(dbg)) == 1
 
 
 def test_state_qdq_rejects_bad_args():
