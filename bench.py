@@ -12,7 +12,8 @@ object covers that launch, timed with HIP events recorded around it by the
 library; the split schedule (prep kernel, then the state kernel alone) is
 timed too and reported beside it.
 
-Also reported: the same prefill with a per-key-channel gate (KDA-style g
+Also reported: the same prefill with W QDQ on top (each row of the
+WY-transformed W quantized to FP8 E4M3 before W S^T); the same prefill with a per-key-channel gate (KDA-style g
 [T, H, dk]) as tokens/s and its state kernel's time; the prefill->decode handoff workload (256 sequences, H=32,
 d=128: 2048-token chunked prefix with QDQ, then 512 single-token decode steps
 each writing the state through per-tile QDQ) as decode-step HBM GB/s, and the
@@ -155,7 +156,7 @@ def main():
 
     import torch
     from fp8_state_qat_amd import api, inputs as gi
-    from fp8_state_qat_amd._lib import GDN_QDQ_CHUNK, GDN_QDQ_WRITE, GDN_SCHEDULE_SPLIT
+    from fp8_state_qat_amd._lib import GDN_QDQ_CHUNK, GDN_QDQ_W, GDN_QDQ_WRITE, GDN_SCHEDULE_SPLIT
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -242,6 +243,26 @@ def main():
     split_kern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[args.warmup:]]))
     split_by = split_state_kernel_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2, 2)
 
+    # W QDQ on top, same workload (reported): W formed and row-quantized by the producers
+    evw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps + args.warmup)]
+    itw = {"i": 0}
+
+    def step_w():
+        e0, e1 = evw[itw["i"]]
+        itw["i"] += 1
+        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"],
+                      qdq_flags=flags | GDN_QDQ_W, out=o, final_state=fin,
+                      debug={"kernel_start": e0, "kernel_end": e1})
+
+    for e0, e1 in evw:
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    w_ms, _ = time_launches(step_w, args.steps, args.warmup)
+    w_kern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evw[args.warmup:]]))
+    w_tflops = fl_all / (w_kern * 1e-3) / 1e12
+
     out = {"metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -260,7 +281,14 @@ def main():
                               "state_kernel_avg_launch_ms": round(split_kern, 5),
                               "state_kernel_mfma_tflops": round(fl / (split_kern * 1e-3) / 1e12, 2),
                               "state_kernel_hbm_gbs": round(split_by / (split_kern * 1e-3) / 1e9, 1),
-                              "state_kernel_algorithmic_bytes": split_by}}
+                              "state_kernel_algorithmic_bytes": split_by},
+           "w_qdq": {"qdq_flags": flags | GDN_QDQ_W,
+                     "ms_per_step": round(w_ms / args.steps, 5),
+                     "tokens_per_s": round(tokens / (w_ms / args.steps * 1e-3), 1),
+                     "kernel": "chunk_fwd_kernel<128, EngBF16, bf16, bf16, fused, W QDQ>",
+                     "avg_launch_ms": round(w_kern, 5),
+                     "mfma_tflops": round(w_tflops, 2),
+                     "mfma_frac": round(w_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}}
 
     # ---------------- per-key-channel gate (KDA) prefill, same shape (reported) ----------------
     if not args.no_kda:
