@@ -42,6 +42,14 @@
  *    A token that satisfies both is quantized once.  A supplied initial state
  *    is used as given.
  *
+ *  - INT8 block-32 state QDQ (#2519 page: dynamic INT8 state recipes, one of
+ *    them with 32-element blocks; the page gives no formula, so what follows
+ *    is this oracle's reading): with ORC_QDQ_INT8 every QDQ of the state
+ *    quantizes each block of 32 consecutive key columns of a state row on
+ *    its own: s = amax / 127 (IEEE fp32; s = 1 when that is not positive),
+ *    code = x / s (IEEE fp32 division) rounded half to even, clamped to
+ *    [-127, 127], stored value code * s in fp32.
+ *
  * Build: gcc -O2 -std=c99 -fPIC -shared -ffp-contract=off (no fast-math), so
  * float expressions are evaluated in IEEE binary32 and double ones in binary64.
  */
@@ -52,6 +60,8 @@
 
 #define ORC_QDQ_CHUNK 1u
 #define ORC_QDQ_WRITE 2u
+#define ORC_QDQ_INT8 8u
+#define ORC_INT8_BLOCK 32
 #define ORC_CHUNK 64
 #define ORC_TILE_ROWS 64
 
@@ -168,6 +178,44 @@ void orc_qdq_rows_f32(const float* x, int64_t n_rows, int row_len,
     }
 }
 
+/* Round half to even of an fp32 value to an integral value (|y| < 2^22),
+ * from the definition: the nearer integer, the even one on a tie. */
+static float round_half_even(float y)
+{
+    float f = floorf(y);
+    float d = y - f;                 /* exact: y and f share the binade's ulp */
+    if (d > 0.5f) return f + 1.0f;
+    if (d < 0.5f) return f;
+    return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+}
+
+/* INT8 QDQ of n_blocks blocks of `block` consecutive fp32 values, each block
+ * one group (reading above).  out may alias x; scales [n_blocks] and codes
+ * may be NULL. */
+void orc_qdq_int8_blocks_f32(const float* x, int64_t n_blocks, int block, float* out,
+                             float* scales, int8_t* codes)
+{
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        const float* xb = x + b * block;
+        float* ob = out + b * block;
+        float amax = 0.0f;
+        for (int i = 0; i < block; ++i) {
+            float ax = fabsf(xb[i]);
+            if (ax > amax) amax = ax;
+        }
+        float s = amax / 127.0f;
+        if (!(s > 0.0f)) s = 1.0f;
+        for (int i = 0; i < block; ++i) {
+            float c = round_half_even(xb[i] / s);
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+            if (codes) codes[b * block + i] = (int8_t)c;
+            ob[i] = c * s;
+        }
+        if (scales) scales[b] = s;
+    }
+}
+
 /* QDQ of n_states states of dv x dk fp32 values, one tile per 64 rows
  * (rows = value channels).  scales: [n_states][dv/64] or NULL. */
 void orc_qdq_states_f32(const float* x, int64_t n_states, int dv, int dk,
@@ -214,6 +262,7 @@ int orc_gdn_sequence(int L, int P, int dk, int dv, int per_channel, unsigned fla
 {
     if (L < 0 || P < 0 || P > L || dk <= 0 || dv <= 0) return -1;
     if (flags && dv % ORC_TILE_ROWS) return -1;     /* QDQ tiles are 64 value rows */
+    if ((flags & ORC_QDQ_INT8) && dk % ORC_INT8_BLOCK) return -1;
     int64_t n = (int64_t)dv * dk;
     int tiles = dv / ORC_TILE_ROWS > 0 ? dv / ORC_TILE_ROWS : 1;
     double* S = (double*)malloc(sizeof(double) * (size_t)n);
@@ -261,8 +310,16 @@ int orc_gdn_sequence(int L, int P, int dk, int dv, int per_channel, unsigned fla
                      ((flags & ORC_QDQ_WRITE) && t >= (P > 1 ? P : 1));
         if (is_bound && nb < max_bounds && bound_pre)
             memcpy(bound_pre + (int64_t)nb * n, S, sizeof(double) * (size_t)n);
-        if (do_qdq) qdq_state_f64(S, dv, dk, tmp, sc);
-        else for (int j = 0; j < tiles; ++j) sc[j] = 1.0f;
+        if (do_qdq && (flags & ORC_QDQ_INT8)) {
+            for (int64_t i = 0; i < n; ++i) tmp[i] = (float)S[i];
+            orc_qdq_int8_blocks_f32(tmp, n / ORC_INT8_BLOCK, ORC_INT8_BLOCK, tmp, NULL, NULL);
+            for (int64_t i = 0; i < n; ++i) S[i] = (double)tmp[i];
+            for (int j = 0; j < tiles; ++j) sc[j] = 1.0f;    /* the record's scales are the FP8 codec's */
+        } else if (do_qdq) {
+            qdq_state_f64(S, dv, dk, tmp, sc);
+        } else {
+            for (int j = 0; j < tiles; ++j) sc[j] = 1.0f;
+        }
         if (is_bound && nb < max_bounds) {
             if (bound_post) memcpy(bound_post + (int64_t)nb * n, S, sizeof(double) * (size_t)n);
             if (bound_scales) memcpy(bound_scales + (int64_t)nb * tiles, sc, sizeof(float) * (size_t)tiles);

@@ -16,6 +16,8 @@ import numpy as np
 
 QDQ_CHUNK = 1
 QDQ_WRITE = 2
+QDQ_INT8 = 8          # INT8 block-32 codec for every state QDQ of a sequence
+INT8_BLOCK = 32
 CHUNK = 64
 TILE_ROWS = 64
 
@@ -46,6 +48,9 @@ def _load():
     lib.orc_e4m3_encode_array.restype = None
     lib.orc_qdq_tile_f32.argtypes = [_fp, ctypes.c_int64, _fp, _fp, _u8p]
     lib.orc_qdq_tile_f32.restype = None
+    lib.orc_qdq_int8_blocks_f32.argtypes = [_fp, ctypes.c_int64, ctypes.c_int, _fp, _fp,
+                                            ctypes.POINTER(ctypes.c_int8)]
+    lib.orc_qdq_int8_blocks_f32.restype = None
     lib.orc_qdq_rows_f32.argtypes = [_fp, ctypes.c_int64, ctypes.c_int, _fp, _fp, _u8p]
     lib.orc_qdq_rows_f32.restype = None
     lib.orc_qdq_states_f32.argtypes = [_fp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
@@ -125,6 +130,25 @@ def qdq_rows(x):
     codes = np.empty(x.shape, dtype=np.uint8)
     if rows:
         lib.orc_qdq_rows_f32(_ptr(x, _fp), rows, n, _ptr(out, _fp), _ptr(scales, _fp), _ptr(codes, _u8p))
+    return out, scales, codes
+
+
+def qdq_int8_blocks(x, block=INT8_BLOCK):
+    """INT8 QDQ of fp32 values [..., n] (n a multiple of block): every block
+    of `block` consecutive values along the last axis is one group with
+    scale amax / 127 (zero guard), codes rounded half to even.
+
+    Returns (out fp32 same shape, scales [..., n / block] fp32, codes int8)."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape[-1] % block == 0
+    nb = x.size // block
+    out = np.empty_like(x)
+    scales = np.empty(x.shape[:-1] + (x.shape[-1] // block,), dtype=np.float32)
+    codes = np.empty(x.shape, dtype=np.int8)
+    if nb:
+        lib.orc_qdq_int8_blocks_f32(_ptr(x, _fp), nb, block, _ptr(out, _fp), _ptr(scales, _fp),
+                                    codes.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)))
     return out, scales, codes
 
 

@@ -478,3 +478,93 @@ def test_chunked_prefix_and_suffix_equal_recurrence(flags):
         for key in ("o", "S"):
             rel = np.linalg.norm(chk[key] - rec[key]) / np.linalg.norm(rec[key])
             assert rel < 1e-10, (P, key, rel)
+
+
+# ---------------------------------------------------------------------------
+# INT8 block-32 state QDQ (#2519 page: dynamic INT8 state recipes with
+# 32-element blocks; the formula is the oracle's reading: signed symmetric,
+# scale amax / 127 per block of 32 key columns, round half to even)
+# ---------------------------------------------------------------------------
+def test_int8_hand_cases():
+    """Scale 1 (block amax 127): ties go to the even integer in both signs,
+    everything else to the nearest; -0.5 gives a zero code."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, :10] = [127, 2.5, -2.5, 3.5, 0.5, 1.5, 126.5, -0.5, 0.49999997, -1.5000001]
+    out, sc, codes = orc.qdq_int8_blocks(x)
+    assert sc[0, 0] == 1.0
+    assert list(codes[0, :10]) == [127, 2, -2, 4, 0, 2, 126, 0, 0, -2]
+    np.testing.assert_array_equal(out[0, :10], codes[0, :10].astype(np.float32))
+
+
+def test_int8_rounding_against_brute_force():
+    """Codes at scale 1 against a nearest-integer search over every code in
+    [-127, 127] with ties to the even one; values drawn at and around every
+    half-integer.  Catches ties-away rounding or truncation."""
+    rng = np.random.default_rng(61)
+    halves = np.arange(-127, 127) + 0.5
+    y = np.concatenate([halves, np.nextafter(halves, 0, dtype=np.float64),
+                        np.nextafter(halves, 200, dtype=np.float64), rng.uniform(-127, 127, 4000)])
+    y = y.astype(np.float32)
+    n = (y.size + 30) // 31 * 31
+    y = np.pad(y, (0, n - y.size))
+    blocks = np.zeros((n // 31, 32), np.float32)
+    blocks[:, 0] = 127.0                       # fixes the scale at 1
+    blocks[:, 1:] = y.reshape(-1, 31)
+    _, sc, codes = orc.qdq_int8_blocks(blocks)
+    assert np.all(sc == 1.0)
+    cand = np.arange(-127, 128, dtype=np.float64)
+    d = np.abs(blocks[:, 1:, None].astype(np.float64) - cand[None, None, :])
+    best = d.min(axis=2, keepdims=True)
+    tie_even = np.where(d == best, np.where(cand % 2 == 0, 0, 1), 2)   # prefer the even one on a tie
+    want = cand[np.argmin(tie_even, axis=2)]
+    np.testing.assert_array_equal(codes[:, 1:].astype(np.float64), want)
+
+
+def test_int8_blocks_grouping_and_bounds():
+    """Each run of 32 consecutive key columns is its own group: a block
+    quantized alone gives the same bits; every element is within half a step
+    of its block's scale; the block maximum maps to +-127; a zero block stays
+    zero with scale 1.  Catches a per-row or per-tile grouping."""
+    rng = np.random.default_rng(62)
+    S = (rng.standard_normal((64, 128)) * (10.0 ** rng.uniform(-5, 3, (64, 4))).repeat(32, axis=1))
+    S = S.astype(np.float32)
+    S[3, 32:64] = 0.0
+    out, sc, codes = orc.qdq_int8_blocks(S)
+    assert sc.shape == (64, 4)
+    for r in (0, 3, 17, 63):
+        for b in range(4):
+            blk = S[r, 32 * b:32 * b + 32]
+            o1, s1, c1 = orc.qdq_int8_blocks(blk[None, :])
+            np.testing.assert_array_equal(o1[0], out[r, 32 * b:32 * b + 32])
+            assert s1[0, 0] == sc[r, b]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert sc[r, b] == 1.0 and np.all(out[r, 32 * b:32 * b + 32] == 0)
+                continue
+            assert np.all(np.abs(out[r, 32 * b:32 * b + 32] - blk) <= 0.5 * sc[r, b] * (1 + 1e-6))
+            assert np.abs(c1[0]).max() == 127
+
+
+def test_int8_decode_one_token_closed_form():
+    """From the zero state one token with a per-write INT8 QDQ: the output is
+    taken before the QDQ (o_1 = beta (k.q) v) and the stored state is the
+    INT8 QDQ of beta v k^T."""
+    q, k, v, b, g = _seq(1, 128, 64, seed=63)
+    r = orc.gdn_sequence(q, k, v, b, g, prefix_len=0, flags=orc.QDQ_WRITE | orc.QDQ_INT8)
+    np.testing.assert_allclose(r["o"][0], b[0] * (k[0] @ q[0]) * v[0], rtol=1e-13, atol=1e-15)
+    want, _, _ = orc.qdq_int8_blocks((b[0] * np.outer(v[0], k[0])).astype(np.float32))
+    np.testing.assert_array_equal(r["S"], want.astype(np.float64))
+    fp8 = orc.gdn_sequence(q, k, v, b, g, prefix_len=0, flags=orc.QDQ_WRITE)
+    assert not np.array_equal(fp8["S"], r["S"])
+
+
+def test_int8_power_of_two_and_sign_invariance():
+    """INT8 QDQ commutes with power-of-two scaling and negation, so over a
+    run of per-write QDQs o(4 v) = 4 o(v) and o(-v) = -o(v) bitwise."""
+    q, k, v, b, g = _seq(40, 64, 64, seed=64)
+    f = orc.QDQ_WRITE | orc.QDQ_INT8
+    r = orc.gdn_sequence(q, k, v, b, g, prefix_len=0, flags=f)
+    r4 = orc.gdn_sequence(q, k, 4.0 * v, b, g, prefix_len=0, flags=f)
+    rn = orc.gdn_sequence(q, k, -v, b, g, prefix_len=0, flags=f)
+    np.testing.assert_array_equal(r4["o"], 4.0 * r["o"])
+    np.testing.assert_array_equal(rn["o"], -r["o"])
