@@ -179,14 +179,17 @@ void orc_qdq_rows_f32(const float* x, int64_t n_rows, int row_len,
 }
 
 /* Round half to even of an fp32 value to an integral value (|y| < 2^22),
- * from the definition: the nearer integer, the even one on a tie. */
+ * from the definition: the nearer integer, the even one on a tie; a zero
+ * result keeps the operand's sign (IEEE 754 roundToIntegralTiesToEven). */
 static float round_half_even(float y)
 {
     float f = floorf(y);
     float d = y - f;                 /* exact: y and f share the binade's ulp */
-    if (d > 0.5f) return f + 1.0f;
-    if (d < 0.5f) return f;
-    return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+    float r;
+    if (d > 0.5f) r = f + 1.0f;
+    else if (d < 0.5f) r = f;
+    else r = (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+    return copysignf(r, y);
 }
 
 /* INT8 QDQ of n_blocks blocks of `block` consecutive fp32 values, each block

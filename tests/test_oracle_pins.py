@@ -494,6 +494,8 @@ def test_int8_hand_cases():
     assert sc[0, 0] == 1.0
     assert list(codes[0, :10]) == [127, 2, -2, 4, 0, 2, 126, 0, 0, -2]
     np.testing.assert_array_equal(out[0, :10], codes[0, :10].astype(np.float32))
+    # a value that rounds to zero keeps its sign, as IEEE rounding to integral does
+    assert np.signbit(out[0, 7]) and not np.signbit(out[0, 4])
 
 
 def test_int8_rounding_against_brute_force():
