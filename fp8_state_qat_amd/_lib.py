@@ -21,14 +21,15 @@ GDN_BF16 = 1
 GDN_QDQ_CHUNK = 1
 GDN_QDQ_WRITE = 2
 GDN_QDQ_W = 4        # W QDQ in every chunk of the chunked prefix (scalar gate)
+GDN_QDQ_INT8 = 8     # decode step: INT8 block-32 per-write QDQ instead of FP8 per tile
 
 GDN_SCHEDULE_AUTO = 0
 GDN_SCHEDULE_SPLIT = 1
 GDN_SCHEDULE_FUSED = 2
 GDN_SCHEDULE_FUSED_NO_PRODUCERS = 3   # test hook: every wait for a ready flag runs out
 
-EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_state_qdq", "gdn_decode_step",
-           "gdn_status_string", "gdn_last_error")
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_state_qdq", "gdn_state_qdq_int8",
+           "gdn_decode_step", "gdn_status_string", "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
@@ -86,6 +87,8 @@ def lib():
     L.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_state_qdq.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
     L.gdn_state_qdq.restype = ctypes.c_int
+    L.gdn_state_qdq_int8.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
+    L.gdn_state_qdq_int8.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp]
     L.gdn_decode_step.restype = ctypes.c_int

@@ -124,10 +124,28 @@ def state_qdq(x, out=None, scales=None, want_scales=True):
     return out, scales
 
 
+def state_qdq_int8(x, out=None, scales=None, want_scales=True):
+    """gdn_state_qdq_int8 on x [..., dv, dk] fp32 (blocks of 32 key columns).
+    Returns (out, scales [..., dv, dk/32])."""
+    _dev(x, "x", torch.float32)
+    dv, dk = x.shape[-2], x.shape[-1]
+    n = x.numel() // (dv * dk) if x.numel() else 0
+    if out is None:
+        out = torch.empty_like(x)
+    if scales is None and want_scales:
+        scales = torch.empty(x.shape[:-1] + (dk // 32,), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    st = _lib.lib().gdn_state_qdq_int8(_ptr(x), _ptr(out), _ptr(scales), n, dv, dk, _stream())
+    _lib.check(st)
+    return out, scales
+
+
 def decode_step(q, k, v, beta, g, state, *, qdq=True, o=None, o_dtype=None, state_pre=None,
-                scales=None):
+                scales=None, int8=False):
     """gdn_decode_step.  q, k: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; g: [N, H]
-    or [N, H, dk]; state [N, H, dv, dk] fp32 updated in place.  Returns o."""
+    or [N, H, dk]; state [N, H, dv, dk] fp32 updated in place.  int8: the
+    per-write QDQ is INT8 block-32 (scales [N, H, dv, dk/32]) instead of FP8
+    per tile.  Returns o."""
     N, H, dk = k.shape
     dv = v.shape[2]
     o_dtype = k.dtype if o_dtype is None else o_dtype
@@ -138,7 +156,7 @@ def decode_step(q, k, v, beta, g, state, *, qdq=True, o=None, o_dtype=None, stat
     if o is None:
         o = torch.empty((N, H, dv), dtype=o_dtype, device=k.device)
     shape = GdnShape(N, H, dk, dv, N, _DT[k.dtype], _DT[o_dtype], 1 if g.dim() == 3 else 0,
-                     GDN_QDQ_WRITE if qdq else 0)
+                     (GDN_QDQ_WRITE if qdq else 0) | (_lib.GDN_QDQ_INT8 if int8 else 0))
     st = _lib.lib().gdn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                     _ptr(g), _ptr(state), _ptr(o), _ptr(state_pre), _ptr(scales),
                                     _stream())

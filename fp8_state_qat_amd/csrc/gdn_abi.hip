@@ -58,7 +58,7 @@ gdn_status_t check_shape(const gdn_shape_t* s, bool decode) {
     return fail(GDN_ERR_INVALID_ARG, "io_dtype and o_dtype must be GDN_F32 or GDN_BF16");
   if (s->gate_per_channel != 0 && s->gate_per_channel != 1)
     return fail(GDN_ERR_INVALID_ARG, "gate_per_channel must be 0 or 1");
-  if (s->qdq_flags & ~(GDN_QDQ_CHUNK | GDN_QDQ_WRITE | GDN_QDQ_W))
+  if (s->qdq_flags & ~(GDN_QDQ_CHUNK | GDN_QDQ_WRITE | GDN_QDQ_W | GDN_QDQ_INT8))
     return fail(GDN_ERR_INVALID_ARG, "unknown qdq_flags bits 0x%x", s->qdq_flags);
   const int64_t blocks = (int64_t)s->n_seqs * s->n_heads * (s->dv / 64);
   if (blocks >= (int64_t)1 << 31) return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, head, tile) units");
@@ -106,6 +106,26 @@ gdn_status_t gdn_state_qdq(const float* in, float* out, float* scales, int64_t n
   return GDN_OK;
 }
 
+gdn_status_t gdn_state_qdq_int8(const float* in, float* out, float* scales, int64_t n_states,
+                                int32_t dv, int32_t dk, void* stream) {
+  g_err[0] = 0;
+  if (n_states < 0) return fail(GDN_ERR_INVALID_ARG, "n_states must be >= 0");
+  if (dv < 64 || dv % 64 != 0) return fail(GDN_ERR_INVALID_ARG, "dv must be a positive multiple of 64");
+  if (dk < 32 || dk % 32 != 0) return fail(GDN_ERR_INVALID_ARG, "dk must be a positive multiple of 32");
+  if (dk > 256) return fail(GDN_ERR_UNSUPPORTED, "dk above 256 is not supported");
+  const int64_t n_values = n_states * dv * dk;
+  if (n_values / 4 / 256 >= (int64_t)1 << 31) return fail(GDN_ERR_UNSUPPORTED, "too many values");
+  if (n_states > 0) {
+    if (in == nullptr || out == nullptr) return fail(GDN_ERR_INVALID_ARG, "in/out is NULL");
+    if (!aligned(in, 16) || !aligned(out, 16)) return fail(GDN_ERR_INVALID_ARG, "in/out must be 16-byte aligned");
+  }
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  hipError_t e = gdn::launch_state_qdq_int8(in, out, scales, n_values, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
 gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void* k,
                              const void* v, const float* beta, const float* g, float* state,
                              void* o, float* state_pre, float* scales, void* stream) {
@@ -142,6 +162,8 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   g_err[0] = 0;
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
+  if (shape->qdq_flags & GDN_QDQ_INT8)
+    return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_INT8 is a decode-step codec (gdn_decode_step, gdn_state_qdq_int8)");
   if ((shape->qdq_flags & GDN_QDQ_W) && shape->gate_per_channel)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_W is supported with the scalar gate only");
   const size_t need = gdn::prep_workspace_bytes(*shape);

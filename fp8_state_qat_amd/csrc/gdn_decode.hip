@@ -17,12 +17,18 @@
 // products are reduced over the dk/4 lanes of a row by DPP lane moves (a
 // fixed order); the tile's 64 outputs go through LDS and leave as one
 // contiguous store.
+//
+// kInt8: the per-write QDQ is INT8 with one scale per block of 32
+// consecutive key columns of a state row (#2519: dynamic INT8 state recipes
+// with 32-element blocks; scale amax / 127, round half to even): a block is
+// the float4s of 8 adjacent lanes, so its amax is three DPP steps and the
+// tile needs no workgroup reduction.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
-template <int DK, typename TIO, typename TO, bool PC>
+template <int DK, typename TIO, typename TO, bool PC, bool kInt8>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ g, float* __restrict__ state,
@@ -92,7 +98,18 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     for (int p = 0; p < NP; ++p) P[t + kThreads * p] = x[p];
   }
   float s = 1.0f;
-  if (do_qdq) {
+  if (kInt8 && do_qdq) {
+    static_assert(DK % 32 == 0, "INT8 blocks of 32 key columns");
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float bm = lane8_max_dpp(fmaxf(fmaxf(fabsf(x[p].x), fabsf(x[p].y)), fmaxf(fabsf(x[p].z), fabsf(x[p].w))));
+      const float sb = int8_scale(bm);
+      qdq_int8_4(x[p], sb, 1.0f / sb);
+      if (scales != nullptr && (c4 & 7) == 0)
+        scales[(nh * dv + kTileRows * vt + rr + RPP * p) * (DK / 32) + (c4 >> 3)] = sb;
+    }
+    __syncthreads();  // s_o
+  } else if (do_qdq) {
     amax = block_max(amax, red);  // its barriers also publish s_o
     s = qdq_scale(amax);
     const float r = 1.0f / s;
@@ -104,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 #pragma unroll
   for (int p = 0; p < NP; ++p) S[t + kThreads * p] = x[p];
   if (t < kTileRows) io<TO>::st(o + nh * dv + kTileRows * vt + t, s_o[t]);
-  if (scales != nullptr && t == 0) scales[nh * tiles + vt] = s;
+  if (!kInt8 && scales != nullptr && t == 0) scales[nh * tiles + vt] = s;
 }
 
 template <int DK, typename TIO, typename TO>
@@ -113,14 +130,18 @@ static void launch_dk_io_o(const gdn_shape_t& s, const void* q, const void* k, c
                            float* state_pre, float* scales, hipStream_t stream) {
   const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
   const int qdq = (s.qdq_flags & GDN_QDQ_WRITE) ? 1 : 0;
-  if (s.gate_per_channel)
-    hipLaunchKernelGGL((decode_step_kernel<DK, TIO, TO, true>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, (const TIO*)q, (const TIO*)k, (const TIO*)v,
-                       beta, g, state, (TO*)o, state_pre, scales, s.dv, qdq);
-  else
-    hipLaunchKernelGGL((decode_step_kernel<DK, TIO, TO, false>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, (const TIO*)q, (const TIO*)k, (const TIO*)v,
-                       beta, g, state, (TO*)o, state_pre, scales, s.dv, qdq);
+  const bool i8 = (s.qdq_flags & GDN_QDQ_INT8) != 0;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, (const TIO*)q, (const TIO*)k,
+                       (const TIO*)v, beta, g, state, (TO*)o, state_pre, scales, s.dv, qdq);
+  };
+  if (s.gate_per_channel) {
+    if (i8) go(decode_step_kernel<DK, TIO, TO, true, true>);
+    else go(decode_step_kernel<DK, TIO, TO, true, false>);
+  } else {
+    if (i8) go(decode_step_kernel<DK, TIO, TO, false, true>);
+    else go(decode_step_kernel<DK, TIO, TO, false, false>);
+  }
 }
 
 template <int DK>

@@ -96,6 +96,31 @@ __device__ __forceinline__ float dpp_max(float v) {
   const int m = __builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false);
   return fmaxf(v, __int_as_float(m));
 }
+// Max over each aligned group of 8 lanes; every lane of the group receives it.
+__device__ __forceinline__ float lane8_max_dpp(float v) {
+  v = dpp_max<0xB1>(v);      // quad_perm [1, 0, 3, 2]
+  v = dpp_max<0x4E>(v);      // quad_perm [2, 3, 0, 1]
+  return dpp_max<0x141>(v);  // row_half_mirror
+}
+
+// INT8 block QDQ of four values of one block with scale s and r = RN(1 / s):
+// code = x / s (correctly rounded) rounded half to even (v_rndne_f32),
+// clamped to [-127, 127], value = code * s.
+__device__ __forceinline__ float int8_scale(float amax) {
+  float s = amax / 127.0f;
+  return (s > 0.0f) ? s : 1.0f;
+}
+__device__ __forceinline__ float qdq_int8_1(float x, float s, float r) {
+  const float c = fminf(fmaxf(__builtin_rintf(div_rn(x, s, r)), -127.0f), 127.0f);
+  return c * s;
+}
+__device__ __forceinline__ void qdq_int8_4(float4& v, float s, float r) {
+  v.x = qdq_int8_1(v.x, s, r);
+  v.y = qdq_int8_1(v.y, s, r);
+  v.z = qdq_int8_1(v.z, s, r);
+  v.w = qdq_int8_1(v.w, s, r);
+}
+
 // Max over each row of 16 lanes; every lane of the row receives it.
 __device__ __forceinline__ float row16_max_dpp(float v) {
   v = dpp_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]

@@ -12,6 +12,10 @@ namespace gdn {
 hipError_t launch_state_qdq(const float* in, float* out, float* scales, int64_t n_tiles, int dk,
                             hipStream_t stream);
 
+// n_values a multiple of 64 * 32 (whole 64-row tiles of 32-column blocks).
+hipError_t launch_state_qdq_int8(const float* in, float* out, float* scales, int64_t n_values,
+                                 hipStream_t stream);
+
 hipError_t launch_decode_step(const gdn_shape_t& s, const void* q, const void* k, const void* v,
                               const float* beta, const float* g, float* state, void* o,
                               float* state_pre, float* scales, hipStream_t stream);

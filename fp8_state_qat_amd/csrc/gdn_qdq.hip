@@ -45,6 +45,30 @@ __global__ __launch_bounds__(kThreads) void state_qdq_kernel(const float* in,
   if (scales != nullptr && threadIdx.x == 0) scales[tile] = s;
 }
 
+// INT8 block QDQ of n4 float4 (blocks of 32 consecutive values = the
+// float4s of 8 adjacent lanes; #2519 dynamic INT8 state recipes with
+// 32-element blocks: scale amax / 127, round half to even).  One float4 per
+// thread.
+__global__ __launch_bounds__(kThreads) void state_qdq_int8_kernel(const float* in, float* out,
+                                                                 float* __restrict__ scales, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // n4 is a multiple of 8 and of the block
+  float4 x = reinterpret_cast<const float4*>(in)[i];
+  const float s = int8_scale(lane8_max_dpp(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)))));
+  qdq_int8_4(x, s, 1.0f / s);
+  reinterpret_cast<float4*>(out)[i] = x;
+  if (scales != nullptr && (threadIdx.x & 7) == 0) scales[i >> 3] = s;
+}
+
+hipError_t launch_state_qdq_int8(const float* in, float* out, float* scales, int64_t n_values,
+                                 hipStream_t stream) {
+  const int64_t n4 = n_values / 4;
+  if (n4 == 0) return hipSuccess;
+  // every float4 of the grid exists: n_values is a multiple of 64 * 32 (dv % 64, dk % 32)
+  hipLaunchKernelGGL(state_qdq_int8_kernel, dim3((unsigned)(n4 / kThreads)), dim3(kThreads), 0, stream, in, out,
+                     scales, n4);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_qdq(const float* in, float* out, float* scales, int64_t n_tiles, int dk,
                             hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;

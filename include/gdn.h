@@ -70,6 +70,8 @@ typedef enum {
 #define GDN_QDQ_WRITE 2u   /* QDQ at the handoff t = P and after every recurrent write t > P */
 #define GDN_QDQ_W 4u       /* W QDQ in every chunk of the chunked prefix (scalar gate only; */
                            /* gdn_decode_step and the recurrent suffix have no W and ignore it) */
+#define GDN_QDQ_INT8 8u    /* gdn_decode_step only: each per-write QDQ is INT8 block-32 */
+                           /* (see gdn_state_qdq_int8) instead of FP8 per tile */
 
 typedef struct {
     int32_t n_seqs;            /* N >= 1 */
@@ -179,6 +181,21 @@ gdn_status_t gdn_state_qdq(const float* in, float* out, float* scales,
                            int64_t n_states, int32_t dv, int32_t dk, void* stream);
 
 /*
+ * gdn_state_qdq_int8 -- standalone INT8 block-32 state QDQ (#2519 "What does
+ * this PR do?" and its recipe list: dynamic INT8 state quantization with
+ * 32-element blocks).  The page gives no formula; the library's reading:
+ * every block of 32 consecutive key columns of a state row is one group,
+ * scale s = amax / 127 (s = 1 when that is not positive), code = x / s
+ * (IEEE fp32 division) rounded half to even and clamped to [-127, 127],
+ * stored value code * s (fp32).
+ *   in, out  [n_states, dv, dk] fp32 (out may alias in); dv % 64 == 0,
+ *            dk % 32 == 0, 32 <= dk <= 256, 16-byte aligned.
+ *   scales   [n_states, dv, dk / 32] fp32 output, or NULL.
+ */
+gdn_status_t gdn_state_qdq_int8(const float* in, float* out, float* scales,
+                                int64_t n_states, int32_t dv, int32_t dk, void* stream);
+
+/*
  * gdn_decode_step -- one recurrent token per sequence against a stored state
  * (#2519 step 3: read the stored state, output from the updated working
  * state, QDQ before storing when GDN_QDQ_WRITE is set).
@@ -188,7 +205,8 @@ gdn_status_t gdn_state_qdq(const float* in, float* out, float* scales,
  *   state [N, H, dv, dk] fp32, read and written in place
  *   o     [N, H, dv] o_dtype
  *   state_pre  [N, H, dv, dk] fp32 or NULL: the updated state before QDQ (parity record)
- *   scales     [N, H, dv / 64] fp32 or NULL: QDQ scales (1 when no QDQ)
+ *   scales     [N, H, dv / 64] fp32 or NULL: QDQ scales (1 when no QDQ); with
+ *              GDN_QDQ_INT8 and GDN_QDQ_WRITE [N, H, dv, dk / 32], one per block
  */
 gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
                              const void* q, const void* k, const void* v,

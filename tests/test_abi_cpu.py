@@ -65,7 +65,7 @@ def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None, ws=FAKE, ws_by
 @pytest.mark.parametrize("kw,status", [
     (dict(n_seqs=0), 1), (dict(n_heads=0), 1), (dict(dv=96), 1), (dict(dk=96), 2),
     (dict(dk=32), 2), (dict(dv=512), 2), (dict(total_tokens=-1), 1), (dict(io_dtype=7), 1),
-    (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=8), 1),
+    (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=16), 1), (dict(qdq_flags=8 | 3), 2),
     (dict(io_dtype=0, dk=128), 2), (dict(io_dtype=0, dk=128, gate_per_channel=1), 2),
 ])
 def test_chunk_fwd_rejects_bad_shape(kw, status):
@@ -115,7 +115,7 @@ def test_w_qdq_flag():
         assert w == base + (3 + 3) * 2 * (dk * 128 + 1024)
     assert _chunk(_shape(gate_per_channel=1, qdq_flags=_lib.GDN_QDQ_W)) == 2
     assert "scalar gate" in _lib.last_error()
-    assert _chunk(_shape(qdq_flags=8)) == 1
+    assert _chunk(_shape(qdq_flags=16)) == 1
     dbg = GdnDebug(None, None, None, None, None, None, 0, ctypes.c_void_p(FAKE), None)  # W record without offsets
     assert _chunk(_shape(qdq_flags=7), dbg=ctypes.byref(dbg)) == 1
 
@@ -129,6 +129,18 @@ def test_state_qdq_rejects_bad_args():
     assert L.gdn_state_qdq(p(FAKE), p(FAKE), None, 4, 64, 512, None) == 2
     assert L.gdn_state_qdq(None, p(FAKE), None, 4, 64, 128, None) == 1
     assert L.gdn_state_qdq(p(FAKE + 4), p(FAKE), None, 4, 64, 128, None) == 1
+
+
+def test_state_qdq_int8_rejects_bad_args():
+    L = _lib.lib()
+    p = ctypes.c_void_p
+    assert L.gdn_state_qdq_int8(p(FAKE), p(FAKE), None, -1, 64, 128, None) == 1
+    assert L.gdn_state_qdq_int8(p(FAKE), p(FAKE), None, 4, 96, 128, None) == 1
+    assert L.gdn_state_qdq_int8(p(FAKE), p(FAKE), None, 4, 64, 48, None) == 1
+    assert L.gdn_state_qdq_int8(p(FAKE), p(FAKE), None, 4, 64, 512, None) == 2
+    assert L.gdn_state_qdq_int8(None, p(FAKE), None, 4, 64, 128, None) == 1
+    assert L.gdn_state_qdq_int8(p(FAKE + 4), p(FAKE), None, 4, 64, 128, None) == 1
+    assert L.gdn_state_qdq_int8(None, None, None, 0, 64, 128, None) in (0, 3)  # nothing to do
 
 
 def test_decode_rejects_bad_args():
