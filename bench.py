@@ -16,7 +16,8 @@ Also reported: the same prefill with W QDQ on top (each row of the
 WY-transformed W quantized to FP8 E4M3 before W S^T); the same prefill with a per-key-channel gate (KDA-style g
 [T, H, dk]) as tokens/s and its state kernel's time; the prefill->decode handoff workload (256 sequences, H=32,
 d=128: 2048-token chunked prefix with QDQ, then 512 single-token decode steps
-each writing the state through per-tile QDQ) as decode-step HBM GB/s, and the
+each writing the state through per-tile QDQ) as decode-step HBM GB/s (and the
+same steps with the INT8 block-32 codec), and the
 CPU oracle's throughput on the prefill workload (all 64 (sequence, head) pairs
 by default).
 
@@ -374,6 +375,22 @@ def main():
                                       "algorithmic_bytes_per_launch": dby,
                                       "traffic": load_traffic("decode_step_handoff", dsrc),
                                       "kernel": "decode_step_kernel<128, bf16, bf16>"}}
+
+        # the same decode steps with the INT8 block-32 codec (reported)
+        def dstep8():
+            i = it["i"] % steps4
+            api.decode_step(tok["q"][i], tok["k"][i], tok["v"][i], tok["beta"][i], tok["g"][i],
+                            state, qdq=True, o=od, int8=True)
+            it["i"] += 1
+
+        _, dper8 = time_launches(dstep8, steps4 - dwarm, dwarm)
+        dms8 = float(np.mean(dper8))
+        out["decode_int8"] = {"codec": "INT8, one scale per 32 key columns of a state row",
+                              "ms_per_step": round(dms8, 5),
+                              "tokens_per_s": round(N4 / (dms8 * 1e-3), 1),
+                              "hbm_gbs": round(dby / (dms8 * 1e-3) / 1e9, 1),
+                              "hbm_frac": round(dby / (dms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "kernel": "decode_step_kernel<128, bf16, bf16, int8>"}
         del tok, state
         torch.cuda.empty_cache()
 
