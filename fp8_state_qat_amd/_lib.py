@@ -20,7 +20,7 @@ GDN_BF16 = 1
 
 GDN_QDQ_CHUNK = 1
 GDN_QDQ_WRITE = 2
-GDN_QDQ_W = 4        # W QDQ in every chunk of the chunked prefix (scalar gate)
+GDN_QDQ_W = 4        # W QDQ in every chunk of the chunked prefix
 GDN_QDQ_INT8 = 8     # decode step: INT8 block-32 per-write QDQ instead of FP8 per tile
 
 GDN_SCHEDULE_AUTO = 0

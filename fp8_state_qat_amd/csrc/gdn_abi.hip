@@ -164,8 +164,6 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   if (st != GDN_OK) return st;
   if (shape->qdq_flags & GDN_QDQ_INT8)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_INT8 is a decode-step codec (gdn_decode_step, gdn_state_qdq_int8)");
-  if ((shape->qdq_flags & GDN_QDQ_W) && shape->gate_per_channel)
-    return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_W is supported with the scalar gate only");
   const size_t need = gdn::prep_workspace_bytes(*shape);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,

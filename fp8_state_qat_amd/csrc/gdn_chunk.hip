@@ -173,24 +173,6 @@ __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* sme
 }
 
 
-// A fragment of bf16 values (the W codes) as the engine's operand.
-template <class Eng>
-__device__ __forceinline__ typename Eng::Fr ld_bf16_frag(const uint16_t* p) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  if constexpr (Eng::kSplit) {
-    return __builtin_bit_cast(typename Eng::Fr, u);
-  } else {
-    typename Eng::Fr f;
-    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f.v[2 * q] = __uint_as_float(w4[q] << 16);
-      f.v[2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
-    }
-    return f;
-  }
-}
-
 template <int DK, class Eng, typename TIO, typename TO, bool kFused, bool kW>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs args) {
   using Ls = Lds<DK, Eng, kW>;

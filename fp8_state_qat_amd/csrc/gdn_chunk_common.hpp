@@ -180,6 +180,24 @@ struct EngF32 {
   }
 };
 
+// A fragment of bf16 values (the W codes) as the engine's operand.
+template <class Eng>
+__device__ __forceinline__ typename Eng::Fr ld_bf16_frag(const uint16_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  if constexpr (Eng::kSplit) {
+    return __builtin_bit_cast(typename Eng::Fr, u);
+  } else {
+    typename Eng::Fr f;
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f.v[2 * q] = __uint_as_float(w4[q] << 16);
+      f.v[2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
+    }
+    return f;
+  }
+}
+
 // Key-channel order of the state.  The chain waves hold S^T in accumulator
 // tiles whose rows are "state rows" sr = 16 t + 4 (l/16) + i; state row sr
 // carries key channel

@@ -68,7 +68,8 @@ __device__ __forceinline__ float row_shift1(float v) {
 //   V   [64][64 + 16 bytes]   the tile's v rows
 //   T, P  the prep kernel's records, copied as is
 //   EC  exp(gamma_C) by state row [dk];  red  the four waves' amax
-template <int DK, class Eng>
+//   W   (kW only) the chunk's W record as is (codes, then row scales)
+template <int DK, class Eng, bool kW = false>
 struct KdaLds {
   using E = typename Eng::E;
   static constexpr int NKB = DK / 32, NP = Eng::kPlanes;
@@ -83,8 +84,10 @@ struct KdaLds {
   static constexpr size_t oP = oT + 6 * NP * F;
   static constexpr size_t oEC = oP + 6 * NP * F;
   static constexpr size_t oRed = oEC + DK * sizeof(float);
-  static constexpr size_t bytes = oRed + 8 * sizeof(float);
+  static constexpr size_t oW = oRed + 8 * sizeof(float);
+  static constexpr size_t bytes = oW + (kW ? (size_t)w_rec_bytes(DK) : 0);
   static_assert(6 * NP * F == kTRecBytes, "record and its LDS copy differ");
+  static_assert(oW % 16 == 0, "direct loads need 16-byte aligned LDS");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
   static_assert((3 * DK + 64 + 8) * sizeof(float) <= oV, "suffix buffers do not fit");
 };
@@ -93,12 +96,13 @@ struct KdaLds {
 // (chunk, head) for a per-key-channel gate, one item at a time, published
 // through the ready flags exactly as the scalar-gate producers do (same
 // item order and XCD assignment, same flag bits; see gdn_chunk.hip).
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool kW>
 __device__ __forceinline__ void produce_kda_records(const ChunkArgs& args, char* smem) {
   PrepArgs a;
   a.q = args.q; a.k = args.k; a.beta = args.beta; a.g = args.g; a.cu_seqlens = args.cu_seqlens;
   a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
   a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
+  a.W = const_cast<void*>(args.Wrec); a.w_pre = args.w_pre; a.w_post = args.w_post;
   const int tid = threadIdx.x;
   const int H = args.H, NH = args.N * args.H;
   const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
@@ -118,7 +122,7 @@ __device__ __forceinline__ void produce_kda_records(const ChunkArgs& args, char*
     // the item's lane-dependent LDS addresses live across the whole loop
     int tid_i = tid;
     asm volatile("" : "+v"(tid_i));
-    kda_prep_item<DK, TIO>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, tid_i);
+    kda_prep_item<DK, TIO, kW>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, tid_i);
     wait_vmem();      // this wave's record stores are complete
     __syncthreads();  // ... in every wave; the LDS is free again
     if (tid == 0) {
@@ -132,9 +136,9 @@ __device__ __forceinline__ void produce_kda_records(const ChunkArgs& args, char*
   }
 }
 
-template <int DK, class Eng, typename TIO, typename TO, bool kFused>
+template <int DK, class Eng, typename TIO, typename TO, bool kFused, bool kW>
 __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args) {
-  using Ls = KdaLds<DK, Eng>;
+  using Ls = KdaLds<DK, Eng, kW>;
   using E = typename Eng::E;
   using Fr = typename Eng::Fr;
   constexpr int NT = DK / 16;
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   extern __shared__ __align__(16) char smem[];
   if constexpr (kFused) {
     if ((int)blockIdx.x < args.n_prep) {
-      produce_kda_records<DK, TIO>(args, smem);
+      produce_kda_records<DK, TIO, kW>(args, smem);
       return;
     }
   }
@@ -156,6 +160,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   E* sP = reinterpret_cast<E*>(smem + Ls::oP);
   float* sEC = reinterpret_cast<float*>(smem + Ls::oEC);
   float* sRed = reinterpret_cast<float*>(smem + Ls::oRed);
+  uint16_t* sW = reinterpret_cast<uint16_t*>(smem + Ls::oW);  // kW only
 
   const uint32_t lds0 = lds_base_u32(smem);
   auto lds_of = [&](const void* p) { return lds0 + (uint32_t)(reinterpret_cast<const char*>(p) - smem); };
@@ -301,9 +306,11 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
         E* pq = sQa + (f * 64 + lf) * 8;
         if constexpr (kSplit) {
           Fr hi, lo;
-          Eng::split(ka, hi, lo);
-          Eng::st(pa, hi);
-          Eng::st(pa + PLANE, lo);
+          if constexpr (!kW) {  // with W QDQ the W codes take the place of K o exp(gamma)
+            Eng::split(ka, hi, lo);
+            Eng::st(pa, hi);
+            Eng::st(pa + PLANE, lo);
+          }
           Eng::split(qa, hi, lo);
           Eng::st(pq, hi);
           Eng::st(pq + PLANE, lo);
@@ -312,7 +319,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
           Eng::st(pc, hi);
           Eng::st(pc + PLANE, lo);
         } else {
-          Eng::st(pa, Eng::round(ka));
+          if constexpr (!kW) Eng::st(pa, Eng::round(ka));
           Eng::st(pq, Eng::round(qa));
           // transposed fragment f = 2 dt + kb: lane 16 g + sr % 16 holds
           // token 32 kb + kperm(g, j) of state row sr = 16 dt + sr % 16
@@ -364,6 +371,15 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
       lds_load16(trec, (uint32_t)((idx * 64 + lane) * 16), lds_of(sT) + idx * 1024);
       lds_load16(prec, (uint32_t)((idx * 64 + lane) * 16), lds_of(sP) + idx * 1024);
     }
+    if constexpr (kW) {
+      constexpr int NI = w_rec_bytes(DK) / 1024;
+      const char* wrec = reinterpret_cast<const char*>(args.Wrec) + ((int64_t)(chunk0 + cc) * H + h) * w_rec_bytes(DK);
+#pragma unroll
+      for (int ii = 0; ii < (NI + 3) / 4; ++ii) {
+        const int idx = w + 4 * ii;
+        if (idx < NI) lds_load16(wrec, (uint32_t)((idx * 64 + lane) * 16), lds_of(sW) + idx * 1024);
+      }
+    }
   };
 
   // ---- B: one chunk's products for this wave's 16 value rows
@@ -382,7 +398,8 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     } else {
       state_frags(s_hi, s_lo);
     }
-    // (K o exp(gamma)) S^T: A = Ka rows (tokens), B = the state
+    // (K o exp(gamma)) S^T: A = Ka rows (tokens), B = the state; with W QDQ
+    // W_codes S^T (A = the W codes, exact in bf16: one plane)
     f32x4 acc[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -390,13 +407,52 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const Fr a = Eng::ld(slot(sKa, tt * NKB + kb));
-        Eng::mma(acc[tt], a, s_hi[kb]);
-        if constexpr (kSplit) {
-          Eng::mma(acc[tt], Eng::ld(slot(sKa + PLANE, tt * NKB + kb)), s_hi[kb]);
-          if (two) Eng::mma(acc[tt], a, s_lo[kb]);
+        if constexpr (kW) {
+          const Fr a = ld_bf16_frag<Eng>(sW + ((tt * NKB + kb) * 64 + lane) * 8);
+          Eng::mma(acc[tt], a, s_hi[kb]);
+          if constexpr (kSplit) {
+            if (two) Eng::mma(acc[tt], a, s_lo[kb]);
+          }
+        } else {
+          const Fr a = Eng::ld(slot(sKa, tt * NKB + kb));
+          Eng::mma(acc[tt], a, s_hi[kb]);
+          if constexpr (kSplit) {
+            Eng::mma(acc[tt], Eng::ld(slot(sKa + PLANE, tt * NKB + kb)), s_hi[kb]);
+            if (two) Eng::mma(acc[tt], a, s_lo[kb]);
+          }
         }
       }
+    f32x4 uacc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) uacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kW) {
+      // U' = T V - s w_s[t] (W S^T)[t][v]: V exact as the B operand
+      Fr vf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float v8[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v8[4 * hh + i] = Eng::to_f(sV[(32 * kb + 16 * hh + 4 * gq + i) * RSV + 16 * c4 + ln]);
+        vf[kb] = Eng::round(v8);
+      }
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        Eng::mma(uacc[ti], Eng::ld(slot(sT, p)), vf[kb]);
+        if constexpr (kSplit) Eng::mma(uacc[ti], Eng::ld(slot(sT, 6 + p)), vf[kb]);
+      }
+      const float* wsc = reinterpret_cast<const float*>(sW + 4 * NKB * 512);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wsc + 16 * tt + 4 * gq);
+        uacc[tt][0] = fmaf(-sc * w4.x, acc[tt][0], uacc[tt][0]);
+        uacc[tt][1] = fmaf(-sc * w4.y, acc[tt][1], uacc[tt][1]);
+        uacc[tt][2] = fmaf(-sc * w4.z, acc[tt][2], uacc[tt][2]);
+        uacc[tt][3] = fmaf(-sc * w4.w, acc[tt][3], uacc[tt][3]);
+      }
+    } else {
     // X[t][v] = V[t][v] - s (Ka S^T)[t][v], t = 16tt + 4gq + i
     Fr xh[2], xl[2];
 #pragma unroll
@@ -412,9 +468,6 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
       Eng::split(x8, xh[kb], xl[kb]);
     }
     // U' = T X over the lower-triangular pairs (ti, kb): (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
-    f32x4 uacc[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) uacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < 6; ++p) {
       const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
@@ -425,6 +478,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
         Eng::mma(uacc[ti], Eng::ld(slot(sT, 6 + p)), xh[kb]);
       }
     }
+    }  // kW
     // U' fragments: A of U'^T P^T and B of the state update (the same registers)
     Fr uh[2], ul[2];
 #pragma unroll
@@ -701,11 +755,12 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     io<TO>::st(go_ + (int64_t)(seg0 + r) * v_row + (int64_t)h * dv + kTileRows * vt + lane, 0.f);
 }
 
-template <int DK, class Eng, typename TIO, typename TO, bool kFused>
+template <int DK, class Eng, typename TIO, typename TO, bool kFused, bool kW>
 static hipError_t launch_kda_typed(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  auto kern = kda_fwd_kernel<DK, Eng, TIO, TO, kFused>;
-  constexpr size_t prep_lds = KdaPrepLds<DK, TIO>::bytes;  // a producer's item
-  constexpr size_t lds = (kFused && prep_lds > KdaLds<DK, Eng>::bytes) ? prep_lds : KdaLds<DK, Eng>::bytes;
+  auto kern = kda_fwd_kernel<DK, Eng, TIO, TO, kFused, kW>;
+  constexpr size_t prep_lds = KdaPrepLds<DK, TIO, kW>::bytes;  // a producer's item
+  constexpr size_t state_lds = KdaLds<DK, Eng, kW>::bytes;
+  constexpr size_t lds = (kFused && prep_lds > state_lds) ? prep_lds : state_lds;
   static_assert(lds <= 160 * 1024, "LDS budget exceeded");
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
@@ -720,8 +775,11 @@ static hipError_t launch_kda_typed(const gdn_shape_t& s, const ChunkArgs& a, hip
 
 template <int DK, class Eng, typename TIO, typename TO>
 static hipError_t launch_kda_sched(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {
-  return a.fused ? launch_kda_typed<DK, Eng, TIO, TO, true>(s, a, stream)
-                 : launch_kda_typed<DK, Eng, TIO, TO, false>(s, a, stream);
+  if (a.Wrec != nullptr)
+    return a.fused ? launch_kda_typed<DK, Eng, TIO, TO, true, true>(s, a, stream)
+                   : launch_kda_typed<DK, Eng, TIO, TO, false, true>(s, a, stream);
+  return a.fused ? launch_kda_typed<DK, Eng, TIO, TO, true, false>(s, a, stream)
+                 : launch_kda_typed<DK, Eng, TIO, TO, false, false>(s, a, stream);
 }
 
 hipError_t launch_kda_state(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream) {

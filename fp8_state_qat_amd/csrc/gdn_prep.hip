@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, kW ? 2 : 3) void chunk_prep_kernel(PrepAr
 // summed channel by channel from the differences.  T and P are written as
 // two records per (chunk, head) in the layout above.
 // ---------------------------------------------------------------------------
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool kW>
 __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int H = a.H;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   const int seg0 = a.cu_seqlens[n];
   const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
   const int P = a.prefix_lens ? a.prefix_lens[n] : L;
-  kda_prep_item<DK, TIO>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, threadIdx.x);
+  kda_prep_item<DK, TIO, kW>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, threadIdx.x);
 }
 
 PrepLayout prep_layout(const gdn_shape_t& s, void* workspace) {
@@ -181,10 +181,10 @@ static hipError_t launch_chunk_prep(dim3 grid, const PrepArgs& a, hipStream_t st
   return hipGetLastError();
 }
 
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool kW>
 static hipError_t launch_kda_prep(dim3 grid, const PrepArgs& a, hipStream_t stream) {
-  auto kern = kda_prep_kernel<DK, TIO>;
-  constexpr size_t lds = KdaPrepLds<DK, TIO>::bytes;
+  auto kern = kda_prep_kernel<DK, TIO, kW>;
+  constexpr size_t lds = KdaPrepLds<DK, TIO, kW>::bytes;
   static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -211,11 +211,16 @@ hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const
   const dim3 grid((unsigned)L.items);
   const bool wq = L.W != nullptr;
   if (s.gate_per_channel) {
-    if (s.io_dtype == GDN_BF16)
-      return s.dk == 128 ? launch_kda_prep<128, uint16_t>(grid, a, stream)
-                         : launch_kda_prep<64, uint16_t>(grid, a, stream);
+    if (s.io_dtype == GDN_BF16) {
+      if (s.dk == 128)
+        return wq ? launch_kda_prep<128, uint16_t, true>(grid, a, stream)
+                  : launch_kda_prep<128, uint16_t, false>(grid, a, stream);
+      return wq ? launch_kda_prep<64, uint16_t, true>(grid, a, stream)
+                : launch_kda_prep<64, uint16_t, false>(grid, a, stream);
+    }
     if (s.dk != 64) return hipErrorNotSupported;  // fp32 inputs: dk = 64 only
-    return launch_kda_prep<64, float>(grid, a, stream);
+    return wq ? launch_kda_prep<64, float, true>(grid, a, stream)
+              : launch_kda_prep<64, float, false>(grid, a, stream);
   }
   if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)

@@ -142,6 +142,74 @@ __device__ __forceinline__ void store_record(const float* M, const float* colsca
   }
 }
 
+// The W record of chunk j, head h from W in accumulator layout (wave w of
+// the item holds rows 16w + 4gq + i, i = 0..3, at columns 16ct + ln): a
+// scale per row (amax over the row's dk columns, one 16-lane row across the
+// dk/16 tiles, by DPP), the codes by the exact quotient and the hardware
+// E4M3 conversion, then codes and scales staged in LDS (stage: 64 x dk bf16,
+// ssc: 64 floats, both free once every wave is past the first barrier here)
+// and stored as the record; the optional debug record too.  Contains two
+// workgroup barriers; with active false the waves only take part in them.
+template <int DK>
+__device__ __forceinline__ void store_w_record(const PrepArgs& a, int j, int h, const f32x4 (&wacc)[DK / 16],
+                                               uint16_t* stage, float* ssc, int tid, bool active) {
+  constexpr int NT = DK / 16, NKB = DK / 32;
+  const int w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
+  const int H = a.H;
+  float sc[4], rc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) m = fmaxf(m, fabsf(wacc[ct][i]));
+    sc[i] = qdq_scale(row16_max_dpp(m));
+    rc[i] = 1.0f / sc[i];
+  }
+  float cw[NT][4];
+#pragma unroll
+  for (int ct = 0; ct < NT; ct += 2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn(wacc[ct][i], sc[i], rc[i]),
+                                                    div_rn(wacc[ct + 1][i], sc[i], rc[i]), 0, false);
+      cw[ct][i] = __builtin_amdgcn_cvt_f32_fp8(p, 0);
+      cw[ct + 1][i] = __builtin_amdgcn_cvt_f32_fp8(p, 1);
+    }
+  if (active && (a.w_pre != nullptr || a.w_post != nullptr)) {
+    const int64_t base = ((int64_t)j * H + h) * 64 * DK;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (16 * w + 4 * gq + i) * DK + 16 * ct + ln;
+        if (a.w_pre) a.w_pre[base + e] = wacc[ct][i];
+        if (a.w_post) a.w_post[base + e] = cw[ct][i] * sc[i];
+      }
+  }
+  __syncthreads();  // every wave is done with the operands of W
+  if (active) {
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stage[(16 * w + 4 * gq + i) * DK + 16 * ct + ln] = float_to_bf16_bits(cw[ct][i]);
+    if (ln == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ssc[16 * w + 4 * gq + i] = sc[i];
+    }
+  }
+  __syncthreads();
+  if (active) {
+    char* wrec = reinterpret_cast<char*>(a.W) + ((int64_t)j * H + h) * w_rec_bytes(DK);
+    constexpr int NF = 4 * NKB;  // fragments: f = tt * NKB + kb
+    for (int slot = tid; slot < NF * 64; slot += kThreads) {
+      const int f = slot >> 6, l = slot & 63;
+      const int r = 16 * (f / NKB) + (l & 15), c0 = 32 * (f % NKB) + 8 * (l >> 4);
+      *reinterpret_cast<uint4*>(wrec + slot * 16) = *reinterpret_cast<const uint4*>(stage + r * DK + c0);
+    }
+    if (tid < 64) reinterpret_cast<float*>(wrec + NF * 1024)[tid] = ssc[tid];
+  }
+}
+
 // LDS of one scalar-gate item (bytes): k and q rows unpadded, 16-byte pieces
 // XOR-swizzled by row (piece p of row r at slot p ^ (r % PPR)), so that
 // direct loads fill them 1 KiB at a time and the fragment reads of 16 rows at
@@ -380,66 +448,12 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t
         }
       }
     }
-    // row scales (a row is one lane row of 16 across the NT tiles) and codes
-    float sc[4], rc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float m = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) m = fmaxf(m, fabsf(wacc[ct][i]));
-      sc[i] = qdq_scale(row16_max_dpp(m));
-      rc[i] = 1.0f / sc[i];
-    }
-    float cw[NT][4];
-#pragma unroll
-    for (int ct = 0; ct < NT; ct += 2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn(wacc[ct][i], sc[i], rc[i]),
-                                                      div_rn(wacc[ct + 1][i], sc[i], rc[i]), 0, false);
-        cw[ct][i] = __builtin_amdgcn_cvt_f32_fp8(p, 0);
-        cw[ct + 1][i] = __builtin_amdgcn_cvt_f32_fp8(p, 1);
-      }
-    if (active && (a.w_pre != nullptr || a.w_post != nullptr)) {
-      const int64_t base = ((int64_t)j * H + h) * 64 * DK;
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = (16 * w + 4 * gq + i) * DK + 16 * ct + ln;
-          if (a.w_pre) a.w_pre[base + e] = wacc[ct][i];
-          if (a.w_post) a.w_post[base + e] = cw[ct][i] * sc[i];
-        }
-    }
-    __syncthreads();  // every wave is done with K and X
-    // codes as bf16 (exact) row-major over the k rows, row scales over the q rows
-    uint16_t* stage = reinterpret_cast<uint16_t*>(lds);
-    float* ssc = reinterpret_cast<float*>(lds + 64 * RB);
-    if (active) {
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) stage[(16 * w + 4 * gq + i) * DK + 16 * ct + ln] = float_to_bf16_bits(cw[ct][i]);
-      if (ln == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ssc[16 * w + 4 * gq + i] = sc[i];
-      }
-    }
-    __syncthreads();
-    if (active) {
-      char* wrec = reinterpret_cast<char*>(a.W) + ((int64_t)j * H + h) * w_rec_bytes(DK);
-      constexpr int NF = 4 * NKB;  // fragments: f = tt * NKB + kb
-      for (int slot = tid; slot < NF * 64; slot += kThreads) {
-        const int f = slot >> 6, l = slot & 63;
-        const int r = 16 * (f / NKB) + (l & 15), c0 = 32 * (f % NKB) + 8 * (l >> 4);
-        *reinterpret_cast<uint4*>(wrec + slot * 16) = *reinterpret_cast<const uint4*>(stage + r * DK + c0);
-      }
-      if (tid < 64) reinterpret_cast<float*>(wrec + NF * 1024)[tid] = ssc[tid];
-    }
+    store_w_record<DK>(a, j, h, wacc, reinterpret_cast<uint16_t*>(lds), reinterpret_cast<float*>(lds + 64 * RB),
+                       tid, active);
   }
 }
 
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool kW = false>
 struct KdaPrepLds {
   static constexpr int LX = DK + 16 / (int)sizeof(TIO);  // k, q row stride (elements)
   static constexpr int LG = DK + 4;                      // gamma row stride (floats)
@@ -450,10 +464,12 @@ struct KdaPrepLds {
   static constexpr size_t oP = oA + 64 * kL64 * sizeof(float);
   static constexpr size_t oTot = oP + 64 * kL64 * sizeof(float);
   static constexpr size_t oBeta = oTot + kThreads * sizeof(float);
-  static constexpr size_t bytes = oBeta + 64 * sizeof(float);
-  // once A and P are formed, the solve's X overlays k and q
-  static constexpr size_t oX = oK;
+  // once A and P are formed, the solve's X overlays k and q (with W QDQ,
+  // whose product still reads k and the gates, X has a block of its own)
+  static constexpr size_t oX = kW ? oBeta + 64 * sizeof(float) : oK;
+  static constexpr size_t bytes = oBeta + 64 * sizeof(float) + (kW ? 64 * kL64 * sizeof(float) : 0);
   static_assert(64 * kL64 * sizeof(float) <= oG - oK, "X does not fit over k and q");
+  static_assert(64 * DK * 2 <= oQ - oK && 64 * sizeof(float) <= oG - oQ, "W staging over k and q");
 };
 
 template <typename TIO>
@@ -471,10 +487,10 @@ __device__ __forceinline__ void load4f(const TIO* p, float (&x)[4]) {
 // per-key-channel gate, on one workgroup of four waves (thread index tid)
 // with the LDS block smem (KdaPrepLds bytes).  Contains workgroup barriers.
 // On return this wave's record stores may still be in flight.
-template <int DK, typename TIO>
+template <int DK, typename TIO, bool kW = false>
 __device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, int t0, int nv, char* smem,
                                               int tid) {
-  using Ls = KdaPrepLds<DK, TIO>;
+  using Ls = KdaPrepLds<DK, TIO, kW>;
   constexpr bool kBF = sizeof(TIO) == 2;
   constexpr int LX = Ls::LX, LG = Ls::LG, L64 = kL64, NKB = DK / 32;
   TIO* sK = reinterpret_cast<TIO*>(smem + Ls::oK);
@@ -634,6 +650,41 @@ __device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, i
   store_record<kBF>(sP, nullptr, reinterpret_cast<char*>(a.P) + rec, tid);
   solve_unit_lower(sA, sX, tid);
   store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + rec, tid);
+
+  if constexpr (kW) {
+    // ---- W = X diag(beta) (K o exp(gamma)) on the fp32 MFMA (the second
+    // operand is not exact in bf16): wave w forms rows 16w .. 16w + 15, A =
+    // X' rows (k = tokens s, block-lower part only), B[s][c] =
+    // k[s][c] exp(gamma[s][c]), read element by element.
+    constexpr int NT = DK / 16;
+    f32x4 wacc[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) wacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wr = 16 * w + ln;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (2 * kb > w) break;  // wave-uniform: the block-upper part of X is zero
+      float xa[8];
+      int sj[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        sj[jj] = 32 * kb + (jj < 4 ? 4 * gq + jj : 16 + 4 * gq + (jj - 4));
+        xa[jj] = ((sj[jj] >> 4) <= w) ? sX[wr * L64 + sj[jj]] * sBeta[sj[jj]] : 0.f;
+      }
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        float bv[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int c = 16 * ct + ln;
+          bv[jj] = io<TIO>::ld(sK + sj[jj] * LX + c) * __builtin_amdgcn_exp2f(sG[sj[jj] * LG + c]);
+        }
+        mma_f32(wacc[ct], xa, bv);
+      }
+    }
+    store_w_record<DK>(a, j, h, wacc, reinterpret_cast<uint16_t*>(smem + Ls::oK),
+                       reinterpret_cast<float*>(smem + Ls::oQ), tid, true);
+  }
 }
 
 }  // namespace gdn

@@ -24,7 +24,9 @@
  *   - Optional W QDQ (#2497 "What does this PR do?": independent dynamic FP8
  *     fake QDQ of the WY-transformed W; Usage: grouping per token and head):
  *     per chunk W = T (K * exp(gamma)) with T = (I + A)^-1 diag(beta) and
- *     gamma the in-chunk cumulative log-gate; every row of W (one token of
+ *     gamma the in-chunk cumulative log-gate (per key channel with a
+ *     per-channel gate: #2506 "What does this PR do?" and "Usage", the KDA
+ *     state/W controls and the KDA W quantizer); every row of W (one token of
  *     one head, all dk keys) gets its own scale amax / 448 (same zero guard)
  *     and W <- RNE_E4M3(W / s) * s before the pseudo-values
  *     U' = T V - W S^T use it.
@@ -68,7 +70,7 @@ typedef enum {
 /* qdq_flags bits */
 #define GDN_QDQ_CHUNK 1u   /* QDQ after every 64-token chunk of the chunked prefix and at its end (t = P) */
 #define GDN_QDQ_WRITE 2u   /* QDQ at the handoff t = P and after every recurrent write t > P */
-#define GDN_QDQ_W 4u       /* W QDQ in every chunk of the chunked prefix (scalar gate only; */
+#define GDN_QDQ_W 4u       /* W QDQ in every chunk of the chunked prefix (either gate; */
                            /* gdn_decode_step and the recurrent suffix have no W and ignore it) */
 #define GDN_QDQ_INT8 8u    /* gdn_decode_step only: each per-write QDQ is INT8 block-32 */
                            /* (see gdn_state_qdq_int8) instead of FP8 per tile */

@@ -107,14 +107,14 @@ def test_workspace_size_and_checks():
 
 def test_w_qdq_flag():
     """GDN_QDQ_W adds one W record per chunk and head (the codes of 64 rows x
-    dk as bf16 and a 1 KiB block for the row scales); it is rejected with a
-    per-key-channel gate, and unknown flag bits stay rejected."""
+    dk as bf16 and a 1 KiB block for the row scales), for either gate;
+    unknown flag bits stay rejected."""
     base = _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130))
     for dk in (64, 128):
         w = _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, dk=dk, qdq_flags=3 | _lib.GDN_QDQ_W))
         assert w == base + (3 + 3) * 2 * (dk * 128 + 1024)
-    assert _chunk(_shape(gate_per_channel=1, qdq_flags=_lib.GDN_QDQ_W)) == 2
-    assert "scalar gate" in _lib.last_error()
+    assert _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, gate_per_channel=1, qdq_flags=7)) == \
+        _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, qdq_flags=7))
     assert _chunk(_shape(qdq_flags=16)) == 1
     dbg = GdnDebug(None, None, None, None, None, None, 0, ctypes.c_void_p(FAKE), None)  # W record without offsets
     assert _chunk(_shape(qdq_flags=7), dbg=ctypes.byref(dbg)) == 1

@@ -160,6 +160,18 @@ def test_w_qdq_bf16(d, dv):
     print(f"free-running (reported): o_rel={o_rel:.3e} S_rel={s_rel:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("io,d", [(gi.F32, 64), (gi.BF16, 64), (gi.BF16, 128)])
+def test_w_qdq_per_channel_gate(io, d):
+    """A per-key-channel gate (KDA): W = T (K o exp(gamma)) with gamma per
+    channel, formed on the fp32 MFMA by the per-channel prep."""
+    w = gi.make_packed([300, 129, 1, 64], 2, d, d, io_dtype=io, per_channel=True, g_scale=0.05,
+                       seed=57 + d)
+    gpu = run_w_gpu(w, 3 | GDN_QDQ_W)
+    check_w(w, gpu, 3, TOL[io])
+    o_rel, s_rel = free_running(w, gpu, 3)
+    print(f"free-running (reported): o_rel={o_rel:.3e} S_rel={s_rel:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("io", [gi.F32, gi.BF16])
 def test_w_qdq_initial_state(io):
     """A supplied initial state enters the first chunk unquantized (as an
@@ -207,23 +219,25 @@ def test_w_qdq_prefix_suffix(flags):
         assert o_rel <= TOL[gi.F32] and s_rel <= TOL[gi.F32]
 
 
+@pytest.mark.parametrize("pc", [False, True])
 @pytest.mark.parametrize("io", [gi.F32, gi.BF16])
-def test_w_qdq_single_chunk_from_zero_state_changes_nothing(io):
+def test_w_qdq_single_chunk_from_zero_state_changes_nothing(io, pc):
     """From the zero state a one-chunk sequence never meets W S^T: with W QDQ
     on the GPU gives the bits it gives with W QDQ off."""
     d = 64 if io == gi.F32 else 128
-    w = gi.make_packed([64, 1, 40], 2, d, d, io_dtype=io, seed=51)
+    w = gi.make_packed([64, 1, 40], 2, d, d, io_dtype=io, seed=51, per_channel=pc, g_scale=0.05)
     a = run_w_gpu(w, 3, record=False)
     b = run_w_gpu(w, 3 | GDN_QDQ_W, record=False)
     np.testing.assert_array_equal(a["o"], b["o"])
     np.testing.assert_array_equal(a["S"], b["S"])
 
 
-def test_w_qdq_fused_equals_split():
-    """B=4, T=4096, H=16, d=128, bf16, state and W QDQ: the fused launch (W
-    formed on its producer workgroups) and the split one give the same bits,
-    W records included."""
-    w_dev = gi.device_packed([4096] * 4, 16, 128, 128, seed=53)
+@pytest.mark.parametrize("pc", [False, True])
+def test_w_qdq_fused_equals_split(pc):
+    """B=4, T=4096, H=16, d=128, bf16, state and W QDQ, scalar and
+    per-channel gate: the fused launch (W formed on its producer workgroups)
+    and the split one give the same bits, W records included."""
+    w_dev = gi.device_packed([4096] * 4, 16, 128, 128, seed=53, per_channel=pc, g_scale=0.05)
     outs = []
     for sched in (GDN_SCHEDULE_SPLIT, GDN_SCHEDULE_FUSED):
         nan = float("nan")
