@@ -313,19 +313,30 @@ def main():
         ktot, _ = time_launches(kstep, args.steps, args.warmup)
         kms = ktot / args.steps
         kkern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evk[args.warmup:]]))
-        kfl = state_kernel_flops_per_token_head(64, dk, dv) * token_heads
-        kby = (prefill_bytes(token_heads, B * H, dk, dv, 2, 2, gate_floats=dk)
-               + n_chunk_heads * 2 * T_RECORD_BYTES)  # T and P records
+        # the fused launch does every flop of the step and moves the prefill's bytes
+        # (g is [T, H, dk]; the records stay inside the launch)
+        kfl = flops_per_token_head(64, dk, dv) * token_heads
+        kby = prefill_bytes(token_heads, B * H, dk, dv, 2, 2, gate_floats=dk)
+
+        def kstep_w():
+            api.chunk_fwd(dk_["q"], dk_["k"], dk_["v"], dk_["beta"], dk_["g"], dk_["cu_seqlens"],
+                          qdq_flags=flags | GDN_QDQ_W, out=o, final_state=fin)
+
+        kwtot, _ = time_launches(kstep_w, args.steps, args.warmup)
         out["kda"] = {"workload": "per-key-channel gate prefill, B=4 T=4096 H=16 dk=dv=128, bf16 "
                                   "q/k/v and o, fp32 g [T, H, dk] and state, FP8-E4M3 state QDQ "
                                   "at every boundary",
                       "ms_per_step": round(kms, 5), "tokens_per_s": round(tokens / (kms * 1e-3), 1),
-                      "state_kernel": {"kernel": "kda_fwd_kernel<128, EngBF16, bf16, bf16>",
+                      "fused_launch": {"kernel": "kda_fwd_kernel<128, EngBF16, bf16, bf16, fused> "
+                                                 "(128 producer + 128 state workgroups)",
                                        "avg_launch_ms": round(kkern, 5),
                                        "mfma_tflops": round(kfl / (kkern * 1e-3) / 1e12, 2),
                                        "mfma_frac": round(kfl / (kkern * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                                        "hbm_gbs": round(kby / (kkern * 1e-3) / 1e9, 1),
-                                       "algorithmic_bytes_per_launch": kby}}
+                                       "algorithmic_bytes_per_launch": kby},
+                      "w_qdq": {"qdq_flags": flags | GDN_QDQ_W,
+                                "ms_per_step": round(kwtot / args.steps, 5),
+                                "tokens_per_s": round(tokens / (kwtot / args.steps * 1e-3), 1)}}
         del dk_
         torch.cuda.empty_cache()
 
