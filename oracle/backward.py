@@ -1,0 +1,80 @@
+"""State gradients of the gated delta rule (reverse recurrence), fp64.
+
+TEST INFRASTRUCTURE ONLY: the tests compare the library's chunked backward
+state recurrence against this.
+
+The pages train through the state QDQ with identity straight-through
+gradients (#2497 page, "What does this PR do?": "identity straight-through
+gradients for QAT/QAD"), so in the backward every QDQ is the identity map.
+For a loss that is linear in the outputs and the final state,
+    L = sum_t o_t . do_t + <S_L, dS_L>,
+the gradient with respect to any state is then that of the plain recurrence
+    S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t,
+and does not depend on the states themselves.  Written out token by token
+backwards (G the gradient with respect to S_t):
+    G <- dS_L
+    for t = L .. 1:   G <- G + do_t q_t^T                (o_t = S_t q_t)
+                      G <- a_t G (I - beta_t k_t k_t^T)   (now d L / d S_{t-1})
+The state entering chunk c of the chunked prefix is S_{64c}; its gradient
+dh_c is G right after token 64c + 1 has been taken back.  A per-key-channel
+gate (S_{t-1} diag(a_t) in place of a_t S_{t-1}) gives G <- G (I - beta k
+k^T) diag(a_t).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+CHUNK = 64
+
+
+def state_grads(q, k, beta, g, do, dS_L=None, *, chunk=CHUNK):
+    """One (sequence, head).  q, k: [L, dk]; beta: [L]; g: [L] or [L, dk];
+    do: [L, dv]; dS_L: [dv, dk] or None (zero).  float64.
+
+    Returns (dh [ceil(L / chunk), dv, dk] the gradient of each chunk's
+    entering state, dS0 [dv, dk] the gradient of the initial state)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    beta = np.asarray(beta, np.float64)
+    g = np.asarray(g, np.float64)
+    do = np.asarray(do, np.float64)
+    L, dk = k.shape
+    dv = do.shape[1]
+    G = np.zeros((dv, dk)) if dS_L is None else np.array(dS_L, dtype=np.float64)
+    nb = (L + chunk - 1) // chunk
+    dh = np.zeros((nb, dv, dk))
+    for t in range(L, 0, -1):
+        i = t - 1
+        G = G + np.outer(do[i], q[i])
+        Gk = G @ k[i]
+        G = G - beta[i] * np.outer(Gk, k[i])
+        G = G * np.exp(g[i]) if g.ndim == 1 else G * np.exp(g[i])[None, :]
+        if (t - 1) % chunk == 0:
+            dh[(t - 1) // chunk] = G
+    return dh, G
+
+
+def packed_state_grads(q, k, beta, g, do, cu_seqlens, *, seq_lens=None, dS_L=None):
+    """Packed layout: q, k [T, H, dk], beta [T, H], g [T, H] or [T, H, dk],
+    do [T, H, dv], dS_L [N, H, dv, dk] or None.  Returns (dh [n_bounds, H,
+    dv, dk] with chunk b of sequence n at b = sum_{m<n} ceil(L_m/64) + i,
+    dS0 [N, H, dv, dk])."""
+    cu = np.asarray(cu_seqlens, np.int64)
+    N = cu.size - 1
+    H, dk = k.shape[1], k.shape[2]
+    dv = do.shape[2]
+    lens = (cu[1:] - cu[:-1]) if seq_lens is None else np.asarray(seq_lens, np.int64)
+    nbs = [(int(L) + CHUNK - 1) // CHUNK for L in lens]
+    offs = np.concatenate([[0], np.cumsum(nbs)]).astype(np.int64)
+    dh = np.zeros((int(offs[-1]), H, dv, dk))
+    dS0 = np.zeros((N, H, dv, dk))
+    for n in range(N):
+        s0, L = int(cu[n]), int(lens[n])
+        sl = slice(s0, s0 + L)
+        for h in range(H):
+            gg = g[sl, h] if g.ndim == 2 else g[sl, h, :]
+            r_dh, r_0 = state_grads(q[sl, h], k[sl, h], beta[sl, h], gg, do[sl, h],
+                                    None if dS_L is None else dS_L[n, h])
+            dh[offs[n]:offs[n + 1], h] = r_dh
+            dS0[n, h] = r_0
+    return dh, dS0

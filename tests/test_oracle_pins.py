@@ -570,3 +570,57 @@ def test_int8_power_of_two_and_sign_invariance():
     rn = orc.gdn_sequence(q, k, -v, b, g, prefix_len=0, flags=f)
     np.testing.assert_array_equal(r4["o"], 4.0 * r["o"])
     np.testing.assert_array_equal(rn["o"], -r["o"])
+
+
+# ---------------------------------------------------------------------------
+# State gradients (reverse recurrence; identity straight-through QDQ)
+# ---------------------------------------------------------------------------
+from oracle.backward import state_grads  # noqa: E402
+
+
+def _loss(q, k, v, b, g, do, dS, S0):
+    """L = sum_t o_t . do_t + <S_L, dS> by the forward oracle (QDQ off)."""
+    r = orc.gdn_sequence(q, k, v, b, g, flags=0, S0=S0)
+    return float(np.sum(r["o"] * do) + np.sum(r["S"] * dS))
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_state_grads_against_forward_differences(per_channel):
+    """L is affine in any state, so <dh_c, S> = L_c(S) - L_c(0), where L_c
+    runs the forward oracle from chunk c's first token with entering state S
+    -- for every chunk and the initial state, on random directions S and on
+    single entries.  Catches a missing decay, a transposed k k^T term, a
+    dropped output term or an off-by-one chunk boundary."""
+    L, dk, dv = 150, 64, 64
+    q, k, v, b, g = _seq(L, dk, dv, per_channel=per_channel, seed=81,
+                         g_scale=0.05 if per_channel else 0.1)
+    rng = np.random.default_rng(82)
+    do = rng.standard_normal((L, dv))
+    dS = rng.standard_normal((dv, dk))
+    dh, dS0 = state_grads(q, k, b, g, do, dS)
+    assert dh.shape == (3, dv, dk)
+    np.testing.assert_array_equal(dh[0], dS0)
+    for c in range(3):
+        sl = slice(64 * c, L)
+        base = _loss(q[sl], k[sl], v[sl], b[sl], g[sl], do[sl], dS, None)
+        S = rng.standard_normal((dv, dk))
+        lin = _loss(q[sl], k[sl], v[sl], b[sl], g[sl], do[sl], dS, S) - base
+        assert abs(lin - np.sum(dh[c] * S)) <= 1e-9 * max(1.0, abs(lin)), (c, lin)
+        for (i, j) in ((0, 0), (5, 17), (63, 63)):
+            E = np.zeros((dv, dk))
+            E[i, j] = 1.0
+            d = _loss(q[sl], k[sl], v[sl], b[sl], g[sl], do[sl], dS, E) - base
+            assert abs(d - dh[c, i, j]) <= 1e-10 * max(1.0, abs(d)), (c, i, j)
+
+
+def test_state_grads_one_token_closed_form():
+    """One token from S_0: o = S_1 q with S_1 = a S_0 (I - b k k^T) + b v k^T,
+    so dL/dS_0 = a (do q^T + dS) (I - b k k^T)."""
+    q, k, v, b, g = _seq(1, 64, 64, seed=83)
+    rng = np.random.default_rng(84)
+    do = rng.standard_normal((1, 64))
+    dS = rng.standard_normal((64, 64))
+    _, dS0 = state_grads(q, k, b, g, do, dS)
+    a = np.exp(g[0])
+    want = a * (np.outer(do[0], q[0]) + dS) @ (np.eye(64) - b[0] * np.outer(k[0], k[0]))
+    np.testing.assert_allclose(dS0, want, rtol=1e-13, atol=1e-13)
