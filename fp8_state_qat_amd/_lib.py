@@ -29,7 +29,8 @@ GDN_SCHEDULE_FUSED = 2
 GDN_SCHEDULE_FUSED_NO_PRODUCERS = 3   # test hook: every wait for a ready flag runs out
 
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_state_qdq", "gdn_state_qdq_int8",
-           "gdn_decode_step", "gdn_status_string", "gdn_last_error")
+           "gdn_decode_step", "gdn_chunk_bwd_dh", "gdn_chunk_bwd_workspace_bytes", "gdn_status_string",
+           "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
@@ -87,6 +88,10 @@ def lib():
     L.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_state_qdq.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
     L.gdn_state_qdq.restype = ctypes.c_int
+    L.gdn_chunk_bwd_dh.argtypes = [ctypes.POINTER(GdnShape)] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
+    L.gdn_chunk_bwd_dh.restype = ctypes.c_int
+    L.gdn_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
+    L.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_state_qdq_int8.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
     L.gdn_state_qdq_int8.restype = ctypes.c_int
     L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,

@@ -193,4 +193,40 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   return GDN_OK;
 }
 
+size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape_t* shape) {
+  g_err[0] = 0;
+  if (check_shape(shape, false) != GDN_OK) return 0;
+  return gdn::bwd_workspace_bytes(*shape);
+}
+
+gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape, const void* q, const void* k, const float* beta,
+                              const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
+                              const void* d_o, const float* d_final_state, float* dh, float* d_initial_state,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  gdn_status_t st = check_shape(shape, false);
+  if (st != GDN_OK) return st;
+  if (shape->io_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh takes bf16 q, k and d_o");
+  if (shape->gate_per_channel) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh supports the scalar gate only");
+  const size_t need = gdn::bwd_workspace_bytes(*shape);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (!cu_seqlens) return fail(GDN_ERR_INVALID_ARG, "cu_seqlens must be non-NULL");
+  if (!dh && !d_initial_state) return fail(GDN_ERR_INVALID_ARG, "dh and d_initial_state are both NULL");
+  if (shape->total_tokens > 0 && (!q || !k || !beta || !g || !d_o))
+    return fail(GDN_ERR_INVALID_ARG, "q, k, beta, g and d_o must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(d_o, 16) || !aligned(dh, 16) ||
+      !aligned(d_initial_state, 16) || !aligned(d_final_state, 16) || !aligned(beta, 4) || !aligned(g, 4) ||
+      !aligned(cu_seqlens, 4))
+    return fail(GDN_ERR_INVALID_ARG, "misaligned buffer (q, k, d_o and states need 16 bytes)");
+  st = check_device();
+  if (st != GDN_OK) return st;
+  hipError_t e = gdn::launch_chunk_bwd_dh(*shape, q, k, beta, g, cu_seqlens, seq_lens, d_o, d_final_state, dh,
+                                          d_initial_state, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
 }  // extern "C"

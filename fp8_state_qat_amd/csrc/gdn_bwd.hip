@@ -1,0 +1,401 @@
+// gdn_bwd.hip -- the backward state recurrence of the chunked gated delta
+// rule with identity straight-through gradients through every QDQ
+// (Model-Optimizer #2497 "What does this PR do?": QAT/QAD with identity
+// straight-through gradients).  With the QDQ the identity in the backward,
+// the gradient of L = sum_t o_t . do_t + <S_L, dS_L> with respect to the
+// state entering chunk c, dh_c, follows from the chunk's forward algebra
+// (U' = T V - W h^T, O = (Q o e^gamma) h^T + P U', h' = e^{gamma_C} h +
+// U'^T (K o e^{gamma_C - gamma}), W = T (K o e^gamma)) backwards:
+//     dU'  = P^T dO + diag(e^{gamma_C - gamma}) (K dh_{c+1}^T)
+//     Y    = T^T dU'
+//     dh_c = e^{gamma_C} dh_{c+1} + dO^T (Q o e^gamma) - Y^T (K o e^gamma)
+// starting from dh = dS_L after the last chunk.  The states themselves do
+// not enter (L is linear in them), so neither does the QDQ.
+//
+// chunk_bwd_prep_kernel: per (chunk, head) in parallel, T^T and P^T as full
+// 64 x 64 records (prep_item_bwd).  chunk_bwd_dh_kernel: one workgroup of
+// four waves per (sequence, head, 64-row value tile), the chunks in reverse
+// order; wave w owns dh rows 16w .. 16w + 15 of the tile (dk/16 fp32
+// accumulator tiles, the forward state's layout) and runs every product for
+// them.  bf16 inputs; fp32 operands enter the bf16 MFMA as hi + lo pairs.
+#include "gdn_prep_item.hpp"
+
+namespace gdn {
+
+constexpr int kBwdThreads = 256;
+
+// LDS of the dh kernel (bytes): the k and q dumps of the chunk (the forward's
+// rotated fragment layout, so K^T and Q^T come back by transpose reads), the
+// tile's dO rows (padded rows, zero past the chunk's end), the T^T and P^T
+// records, and the gates.
+template <int DK>
+struct BwdLds {
+  static constexpr int NKB = DK / 32;
+  static constexpr size_t F = 64 * 8 * 2;
+  static constexpr size_t RS = 64 + 8;                 // padded dO row (elements)
+  static constexpr size_t oK = 0;
+  static constexpr size_t oQ = oK + 4 * NKB * F;
+  static constexpr size_t oO = oQ + 4 * NKB * F;
+  static constexpr size_t oTT = oO + 64 * RS * 2;
+  static constexpr size_t oPT = oTT + kBRecBytes;
+  static constexpr size_t oVec = oPT + kBRecBytes;     // e^gamma [64], e^{gamma_C - gamma} [64], e^{gamma_C}
+  static constexpr size_t bytes = oVec + (2 * 64 + 4) * sizeof(float);
+  static_assert(oTT % 16 == 0 && oPT % 16 == 0, "direct loads need 16-byte aligned LDS");
+  static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <int DK>
+__global__ __launch_bounds__(kThreads, 2) void chunk_bwd_prep_kernel(PrepArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  const int H = a.H;
+  const int j = blockIdx.x / H, h = blockIdx.x % H;
+  const int total = a.offs[a.N];
+  if (j >= total) return;  // grid is sized for the worst case
+  int lo = 0, hi = a.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.offs[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  const int n = lo, c = j - a.offs[n];
+  const int seg0 = a.cu_seqlens[n];
+  const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
+  prep_item_bwd<DK>(a, j, h, seg0 + c * kChunk, min(kChunk, L - c * kChunk), lds, threadIdx.x);
+}
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const float* g;
+  const uint16_t* dout;
+  const float* dfin;      // [N, H, dv, dk] or null
+  const int32_t* cu_seqlens;
+  const int32_t* seq_lens;
+  const int32_t* chunk_offs;
+  const char* TT;         // one T^T record per (chunk, head)
+  const char* PT;         // one P^T record per (chunk, head)
+  float* dh;              // [n_bounds, H, dv, dk] or null
+  float* dinit;           // [N, H, dv, dk] or null
+  int H;
+  int dv;
+};
+
+template <int DK>
+__global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs args) {
+  using Ls = BwdLds<DK>;
+  using Fr = bf16x8;
+  constexpr int NT = DK / 16, NKB = DK / 32;
+  constexpr int RS = (int)Ls::RS;
+  extern __shared__ __align__(16) char smem[];
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + Ls::oK);
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + Ls::oQ);
+  uint16_t* sO = reinterpret_cast<uint16_t*>(smem + Ls::oO);
+  const uint16_t* sTT = reinterpret_cast<const uint16_t*>(smem + Ls::oTT);
+  const uint16_t* sPT = reinterpret_cast<const uint16_t*>(smem + Ls::oPT);
+  float* vec = reinterpret_cast<float*>(smem + Ls::oVec);
+  const uint32_t lds0 = lds_base_u32(smem);
+
+  const int tid = threadIdx.x;
+  const int w = uniform(tid >> 6);
+  const int lane = tid & 63, gq = lane >> 4, ln = lane & 15;
+  const int H = args.H, dv = args.dv, tiles = dv / kTileRows;
+  const int vt = (int)blockIdx.x % tiles;
+  const int nh = (int)blockIdx.x / tiles;
+  const int h = nh % H, n = nh / H;
+  const int seg0 = args.cu_seqlens[n];
+  const int L = args.seq_lens ? args.seq_lens[n] : (args.cu_seqlens[n + 1] - seg0);
+  const int n_chunks = (L + kChunk - 1) / kChunk;
+  const int chunk0 = args.chunk_offs[n];
+  const int vcol0 = kTileRows * vt + 16 * w + ln;  // this lane's dh row (value channel)
+  const int64_t qk_row = (int64_t)H * DK;
+  const int64_t v_row = (int64_t)H * dv;
+
+  auto frag = [lane](const uint16_t* base, int f) { return *reinterpret_cast<const Fr*>(base + (f * 64 + lane) * 8); };
+  const int qs = rot_slot(lane);
+  auto qfrag = [qs](const uint16_t* base, int f) { return *reinterpret_cast<const Fr*>(base + (f * 64 + qs) * 8); };
+  // element offset of x[t][d] in a k/q dump
+  auto kpos = [](int t, int d) {
+    return (((t >> 4) * NKB + (d >> 5)) * 64 + rot_slot(((d & 31) >> 3) * 16 + (t & 15))) * 8 + (d & 7);
+  };
+
+  // ---- dh of this lane: dst[t][i] = dh[vcol0][dkmap(16t + 4gq + i)]
+  f32x4 dst[NT];
+  {
+    const int64_t base = ((int64_t)nh * dv + vcol0) * DK;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (args.dfin) {
+        const float4 x = *reinterpret_cast<const float4*>(args.dfin + base + dkmap(16 * t + 4 * gq));
+        dst[t] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+        dst[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+
+  for (int c = n_chunks - 1; c >= 0; --c) {
+    const int t0 = seg0 + c * kChunk;
+    const int nv = min(kChunk, L - c * kChunk);
+    // ---- stage the chunk: k and q dumps and the two records by direct
+    // loads, dO rows (zero past nv) and the log-gates by plain loads
+    {
+      const uint16_t* gk = args.k + (int64_t)t0 * qk_row + (int64_t)h * DK;
+      const uint16_t* gqv = args.q + (int64_t)t0 * qk_row + (int64_t)h * DK;
+#pragma unroll
+      for (int ii = 0; ii < NKB; ++ii) {
+        const int i = w + 4 * ii;  // instruction: 64 lane slots of 16 bytes
+        const int u = i * 64 + lane;
+        const int f = u >> 6, l2 = rot_lane(u & 63);
+        const int r = 16 * (f / NKB) + (l2 & 15);
+        const int d = 32 * (f % NKB) + 8 * (l2 >> 4);
+        const uint32_t off = (uint32_t)((min(r, nv - 1) * (int)qk_row + d) * 2);
+        lds_load16(gk, off, lds0 + (uint32_t)Ls::oK + i * 1024);
+        lds_load16(gqv, off, lds0 + (uint32_t)Ls::oQ + i * 1024);
+      }
+      const char* tt = args.TT + ((int64_t)(chunk0 + c) * H + h) * kBRecBytes;
+      const char* pt = args.PT + ((int64_t)(chunk0 + c) * H + h) * kBRecBytes;
+#pragma unroll
+      for (int ii = 0; ii < kBRecBytes / 1024 / 4; ++ii) {
+        const int idx = w * (kBRecBytes / 1024 / 4) + ii;
+        lds_load16(tt, (uint32_t)((idx * 64 + lane) * 16), lds0 + (uint32_t)Ls::oTT + idx * 1024);
+        lds_load16(pt, (uint32_t)((idx * 64 + lane) * 16), lds0 + (uint32_t)Ls::oPT + idx * 1024);
+      }
+      // dO rows: 64 rows x 8 pieces of 16 bytes, two pieces per thread
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int piece = tid + kBwdThreads * pp, r = piece >> 3, pc = piece & 7;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (r < nv)
+          x = *reinterpret_cast<const uint4*>(args.dout + (int64_t)(t0 + r) * v_row + (int64_t)h * dv +
+                                              kTileRows * vt + 8 * pc);
+        *reinterpret_cast<uint4*>(sO + r * RS + 8 * pc) = x;
+      }
+      if (w == 0) {
+        const float gv = (lane < nv) ? args.g[(int64_t)(t0 + lane) * H + h] : 0.f;
+        const float x = wave_prefix_sum(gv);
+        const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+        vec[lane] = __builtin_amdgcn_exp2f(x * kLog2e);
+        vec[64 + lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
+        if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gC * kLog2e);
+      }
+      wait_vmem();
+    }
+    __syncthreads();
+
+    // ---- G = K dh^T (A = k rows, B = dh as hi + lo)
+    Fr dhh[NKB], dhl[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float x[8] = {dst[2 * kb][0], dst[2 * kb][1], dst[2 * kb][2], dst[2 * kb][3],
+                          dst[2 * kb + 1][0], dst[2 * kb + 1][1], dst[2 * kb + 1][2], dst[2 * kb + 1][3]};
+      EngBF16::split(x, dhh[kb], dhl[kb]);
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      Fr kf[4 * NKB];
+#pragma unroll
+      for (int f = 0; f < 4 * NKB; ++f) kf[f] = qfrag(sK, f);  // f = tt * NKB + kb
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          mma_bf16(acc[tt], kf[tt * NKB + kb], dhh[kb]);
+          mma_bf16(acc[tt], kf[tt * NKB + kb], dhl[kb]);
+        }
+    }
+    // ---- dO as B operands: element j of k-block kb = dO[32kb + kperm(gq, j)][16w + ln]
+    Fr of[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint2 r0 = lds_read_tr16(sO + (32 * kb + 4 * gq + (ln >> 2)) * RS + 16 * w + 4 * (ln & 3));
+      const uint2 r1 = lds_read_tr16(sO + (32 * kb + 16 + 4 * gq + (ln >> 2)) * RS + 16 * w + 4 * (ln & 3));
+      of[kb] = __builtin_bit_cast(Fr, make_uint4(r0.x, r0.y, r1.x, r1.y));
+    }
+    // ---- dU' = P^T dO + D G   (lane holds dU'[16ti + 4gq + i][16w + ln])
+    f32x4 uacc[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) uacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int ti = p >> 1, kb = p & 1;
+      mma_bf16(uacc[ti], frag(sPT, p), of[kb]);
+      mma_bf16(uacc[ti], frag(sPT, 8 + p), of[kb]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const float4 d4 = *reinterpret_cast<const float4*>(vec + 64 + 16 * tt + 4 * gq);
+      uacc[tt][0] = fmaf(d4.x, acc[tt][0], uacc[tt][0]);
+      uacc[tt][1] = fmaf(d4.y, acc[tt][1], uacc[tt][1]);
+      uacc[tt][2] = fmaf(d4.z, acc[tt][2], uacc[tt][2]);
+      uacc[tt][3] = fmaf(d4.w, acc[tt][3], uacc[tt][3]);
+    }
+    // ---- Y = T^T dU' (B = dU' as hi + lo: k-block kb from tiles 2kb, 2kb + 1)
+    Fr uh[2], ul[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float u8[8] = {uacc[2 * kb][0], uacc[2 * kb][1], uacc[2 * kb][2], uacc[2 * kb][3],
+                           uacc[2 * kb + 1][0], uacc[2 * kb + 1][1], uacc[2 * kb + 1][2], uacc[2 * kb + 1][3]};
+      EngBF16::split(u8, uh[kb], ul[kb]);
+    }
+    f32x4 yacc[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) yacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int ti = p >> 1, kb = p & 1;
+      const Fr th = frag(sTT, p);
+      mma_bf16(yacc[ti], th, uh[kb]);
+      mma_bf16(yacc[ti], th, ul[kb]);
+      mma_bf16(yacc[ti], frag(sTT, 8 + p), uh[kb]);
+    }
+    // ---- B operands of the update: e^gamma dO and -e^gamma Y, hi + lo
+    Fr boh[2], bol[2], byh[2], byl[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float4 e0 = *reinterpret_cast<const float4*>(vec + 32 * kb + 4 * gq);
+      const float4 e1 = *reinterpret_cast<const float4*>(vec + 32 * kb + 16 + 4 * gq);
+      const float e8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+      const uint4 ou = __builtin_bit_cast(uint4, of[kb]);
+      const uint32_t ow[4] = {ou.x, ou.y, ou.z, ou.w};
+      float o8[8], y8[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o8[2 * q] = e8[2 * q] * bf16_lo(ow[q]);
+        o8[2 * q + 1] = e8[2 * q + 1] * bf16_hi(ow[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y8[i] = -e8[i] * yacc[2 * kb][i];
+        y8[4 + i] = -e8[4 + i] * yacc[2 * kb + 1][i];
+      }
+      EngBF16::split(o8, boh[kb], bol[kb]);
+      EngBF16::split(y8, byh[kb], byl[kb]);
+    }
+    // ---- dh^T <- e^{gamma_C} dh^T + Q^T (e^gamma dO) + K^T (-e^gamma Y)
+    const float eC = vec[128];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[t][i] *= eC;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      // lane (gq, l) of each 16-lane group points at x[32kb + 16h + 4gq + l/4][dkmap(16t + 4(l%4)) .. +3]
+      const int d = dkmap(16 * t + 4 * (ln & 3));
+      const int tq = 4 * gq + (ln >> 2);
+      Fr qa[2], ka[2];
+      {
+        const uint2 x0 = lds_read_tr16(sQ + kpos(tq, d)), x1 = lds_read_tr16(sQ + kpos(tq + 16, d));
+        const uint2 y0 = lds_read_tr16(sQ + kpos(tq + 32, d)), y1 = lds_read_tr16(sQ + kpos(tq + 48, d));
+        qa[0] = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
+        qa[1] = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
+      }
+      {
+        const uint2 x0 = lds_read_tr16(sK + kpos(tq, d)), x1 = lds_read_tr16(sK + kpos(tq + 16, d));
+        const uint2 y0 = lds_read_tr16(sK + kpos(tq + 32, d)), y1 = lds_read_tr16(sK + kpos(tq + 48, d));
+        ka[0] = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
+        ka[1] = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        mma_bf16(dst[t], qa[kb], boh[kb]);
+        mma_bf16(dst[t], qa[kb], bol[kb]);
+        mma_bf16(dst[t], ka[kb], byh[kb]);
+        mma_bf16(dst[t], ka[kb], byl[kb]);
+      }
+    }
+    // ---- dh_c: the gradient of the state entering chunk c
+    if (args.dh) {
+      const int64_t base = (((int64_t)(chunk0 + c) * H + h) * dv + vcol0) * DK;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<float4*>(args.dh + base + dkmap(16 * t + 4 * gq)) =
+            make_float4(dst[t][0], dst[t][1], dst[t][2], dst[t][3]);
+    }
+    __syncthreads();  // the chunk's LDS is free for the next (earlier) chunk
+  }
+  if (args.dinit) {
+    const int64_t base = ((int64_t)nh * dv + vcol0) * DK;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<float4*>(args.dinit + base + dkmap(16 * t + 4 * gq)) =
+          make_float4(dst[t][0], dst[t][1], dst[t][2], dst[t][3]);
+  }
+}
+
+size_t bwd_workspace_bytes(const gdn_shape_t& s) {
+  const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
+  const size_t items = (size_t)(max_chunks * s.n_heads);
+  const size_t offs_bytes = ((size_t)(s.n_seqs + 2) * 4 + 255) / 256 * 256;
+  return offs_bytes + items * kBRecBytes * 2;
+}
+
+template <int DK>
+static hipError_t launch_bwd_dk(const gdn_shape_t& s, const PrepArgs& pa, const BwdArgs& ba, int64_t items,
+                                hipStream_t stream) {
+  {
+    auto kern = chunk_bwd_prep_kernel<DK>;
+    constexpr size_t lds = PrepBwdLds<DK>::bytes;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    if (items > 0) hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kThreads), lds, stream, pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  auto kern = chunk_bwd_dh_kernel<DK>;
+  constexpr size_t lds = BwdLds<DK>::bytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBwdThreads), lds, stream, ba);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
+                               const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
+                               const void* dout, const float* dfin, float* dh, float* dinit, void* workspace,
+                               hipStream_t stream) {
+  char* w = reinterpret_cast<char*>(workspace);
+  const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
+  const int64_t items = max_chunks * s.n_heads;
+  const size_t offs_bytes = ((size_t)(s.n_seqs + 2) * 4 + 255) / 256 * 256;
+  int32_t* offs = reinterpret_cast<int32_t*>(w);
+  char* TT = w + offs_bytes;
+  char* PT = TT + (size_t)items * kBRecBytes;
+  // chunk offsets of the whole sequences (prefix = length)
+  PrepLayout L{};
+  L.offs = offs;
+  L.ready = nullptr;
+  L.items = items;
+  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, nullptr, L, false, nullptr, nullptr, stream);
+  if (e != hipSuccess) return e;
+  PrepArgs pa{};
+  pa.q = q; pa.k = k; pa.beta = beta; pa.g = g; pa.cu_seqlens = cu_seqlens; pa.seq_lens = seq_lens;
+  pa.prefix_lens = nullptr; pa.offs = offs; pa.T = TT; pa.P = PT; pa.N = s.n_seqs; pa.H = s.n_heads;
+  BwdArgs ba{};
+  ba.q = reinterpret_cast<const uint16_t*>(q);
+  ba.k = reinterpret_cast<const uint16_t*>(k);
+  ba.g = g;
+  ba.dout = reinterpret_cast<const uint16_t*>(dout);
+  ba.dfin = dfin;
+  ba.cu_seqlens = cu_seqlens;
+  ba.seq_lens = seq_lens;
+  ba.chunk_offs = offs;
+  ba.TT = TT;
+  ba.PT = PT;
+  ba.dh = dh;
+  ba.dinit = dinit;
+  ba.H = s.n_heads;
+  ba.dv = s.dv;
+  return s.dk == 128 ? launch_bwd_dk<128>(s, pa, ba, items, stream) : launch_bwd_dk<64>(s, pa, ba, items, stream);
+}
+
+}  // namespace gdn

@@ -65,4 +65,12 @@ hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const
                        const int32_t* prefix_lens, const PrepLayout& L, bool records, float* w_pre,
                        float* w_post, hipStream_t stream);
 
+// Backward state recurrence (gdn_bwd.hip): workspace = chunk offsets, then
+// one T^T and one P^T record (16 KiB each) per (chunk, head).
+size_t bwd_workspace_bytes(const gdn_shape_t& s);
+hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
+                               const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
+                               const void* dout, const float* dfin, float* dh, float* dinit, void* workspace,
+                               hipStream_t stream);
+
 }  // namespace gdn

@@ -453,6 +453,144 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward records.  The reverse state recurrence needs T^T and P^T as the A
+// operand; both are block-upper, so they are stored as full 64 x 64 records:
+// pair p = 2 ti + kb (ti = 0..3, kb = 0..1), lane l of fragment p holds
+// M[16 ti + l % 16][32 kb + kperm(l / 16, j)], j = 0..7, bf16 hi plane (8
+// fragments) then lo plane.
+constexpr int kBRecBytes = 16384;
+
+// M^T of the 64 x 64 matrix src (row-major, stride kL64; only its
+// block-lower 16 x 16 blocks are read, the others count as zero), times
+// diag(colscale) of src when colscale is not null, as a backward record, on
+// four waves (item thread index tid).
+__device__ __forceinline__ void store_record_t(const float* src, const float* colscale, char* rec, int tid) {
+  constexpr int L64 = kL64;
+  for (int slot = tid; slot < 8 * 64; slot += kThreads) {
+    const int p = slot >> 6, l = slot & 63, gq = l >> 4;
+    const int ti = p >> 1, kb = p & 1;
+    const int m = 16 * ti + (l & 15);  // row of M = column of src
+    const float cs = colscale ? colscale[m] : 1.0f;
+    float t8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));  // column of M = row of src
+      t8[j] = ((k >> 4) >= (m >> 4)) ? src[k * L64 + m] * cs : 0.f;
+    }
+    uint32_t hv[4], lv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], lv[q]);
+    uint4* dst = reinterpret_cast<uint4*>(rec);
+    dst[p * 64 + l] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+    dst[(8 + p) * 64 + l] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+  }
+}
+
+// LDS of one backward item: k and q rows as in PrepItemLds (the solve's X
+// overlays them), A and P (64 x kL64 fp32 each), the scaled log-gates, beta.
+template <int DK>
+struct PrepBwdLds {
+  static constexpr int RB = DK * 2;
+  static constexpr int PPR = RB / 16;
+  static constexpr int KQ = 2 * 64 * RB;
+  static constexpr int KX = (KQ > 64 * kL64 * 4) ? KQ : 64 * kL64 * 4;
+  static constexpr int oA = KX;
+  static constexpr int oP = oA + 64 * kL64 * 4;
+  static constexpr int oG2 = oP + 64 * kL64 * 4;
+  static constexpr int oBeta = oG2 + 64 * 4;
+  static constexpr int bytes = oBeta + 64 * 4;
+};
+
+// The backward records of chunk j (tokens t0 .. t0 + nv - 1), head h (bf16
+// inputs): T^T with T = (I + A)^-1 diag(beta) into a.T, P^T into a.P.
+// Four waves (item thread index tid), LDS block lds of PrepBwdLds bytes.
+// Contains workgroup barriers.  On return this wave's record stores may
+// still be in flight.
+template <int DK>
+__device__ __forceinline__ void prep_item_bwd(const PrepArgs& a, int j, int h, int t0, int nv, char* lds, int tid) {
+  using IL = PrepBwdLds<DK>;
+  constexpr int L64 = kL64, NKB = DK / 32, RB = IL::RB, PPR = IL::PPR;
+  const char* sK = lds;
+  const char* sQ = lds + 64 * RB;
+  float* sX = reinterpret_cast<float*>(lds);
+  float* sA = reinterpret_cast<float*>(lds + IL::oA);
+  float* sP = reinterpret_cast<float*>(lds + IL::oP);
+  float* sG2 = reinterpret_cast<float*>(lds + IL::oG2);
+  float* sBeta = reinterpret_cast<float*>(lds + IL::oBeta);
+  auto kq_at = [](int r, int c) {
+    const int p = c * 2 / 16, within = c * 2 % 16;
+    return r * RB + ((p ^ (r & (PPR - 1))) * 16) + within;
+  };
+  const int H = a.H;
+  const int w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
+  {
+    const uint32_t lds0 = lds_base_u32(lds);
+    const uint16_t* gk = reinterpret_cast<const uint16_t*>(a.k) + ((int64_t)t0 * H + h) * DK;
+    const uint16_t* gqv = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t0 * H + h) * DK;
+    constexpr int NI = 64 * RB / 1024;
+#pragma unroll
+    for (int ii = 0; ii < NI / 4; ++ii) {
+      const int i = uniform(w) + 4 * ii;
+      const int u = i * 64 + lane, r = u / PPR, p = (u % PPR) ^ (r & (PPR - 1));
+      const uint32_t off = (uint32_t)((min(r, nv - 1) * H * DK) * 2 + p * 16);
+      lds_load16(gk, off, lds0 + i * 1024);
+      lds_load16(gqv, off, lds0 + 64 * RB + i * 1024);
+    }
+    if (w == 0) {
+      float gv = 0.f, bv = 0.f;
+      if (lane < nv) {
+        gv = a.g[(int64_t)(t0 + lane) * H + h];
+        bv = a.beta[(int64_t)(t0 + lane) * H + h];
+      }
+      sG2[lane] = wave_prefix_sum(gv) * kLog2e;
+      sBeta[lane] = bv;
+    }
+    wait_vmem();
+  }
+  __syncthreads();
+  // the ten tiles (R, S), S <= R: C[s][r] = x_s . y_r, lane holds s = 16S + 4gq + i, r = 16R + ln
+  for (int job = w; job < 10; job += 4) {
+    const int R = (job < 1) ? 0 : (job < 3) ? 1 : (job < 6) ? 2 : 3;
+    const int S = job - (R * (R + 1)) / 2;
+    const int r = 16 * R + ln, sr = 16 * S + ln;
+    f32x4 ca = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 af[NKB], bk[NKB], bq[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint2 a0 = *reinterpret_cast<const uint2*>(sK + kq_at(sr, 32 * kb + 4 * gq));
+      const uint2 a1 = *reinterpret_cast<const uint2*>(sK + kq_at(sr, 32 * kb + 16 + 4 * gq));
+      const uint2 k0 = *reinterpret_cast<const uint2*>(sK + kq_at(r, 32 * kb + 4 * gq));
+      const uint2 k1 = *reinterpret_cast<const uint2*>(sK + kq_at(r, 32 * kb + 16 + 4 * gq));
+      const uint2 q0 = *reinterpret_cast<const uint2*>(sQ + kq_at(r, 32 * kb + 4 * gq));
+      const uint2 q1 = *reinterpret_cast<const uint2*>(sQ + kq_at(r, 32 * kb + 16 + 4 * gq));
+      af[kb] = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+      bk[kb] = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+      bq[kb] = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      mma_bf16(ca, af[kb], bk[kb]);
+      mma_bf16(cp, af[kb], bq[kb]);
+    }
+    const float g2r = sG2[r], br = sBeta[r];
+    float va[4], vp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 16 * S + 4 * gq + i;
+      const float e = (s <= r) ? __builtin_amdgcn_exp2f(g2r - sG2[s]) : 0.f;
+      va[i] = (s < r) ? br * e * ca[i] : 0.f;
+      vp[i] = e * cp[i];
+    }
+    *reinterpret_cast<float4*>(sA + r * L64 + 16 * S + 4 * gq) = make_float4(va[0], va[1], va[2], va[3]);
+    *reinterpret_cast<float4*>(sP + r * L64 + 16 * S + 4 * gq) = make_float4(vp[0], vp[1], vp[2], vp[3]);
+  }
+  __syncthreads();
+  store_record_t(sP, nullptr, reinterpret_cast<char*>(a.P) + ((int64_t)j * H + h) * kBRecBytes, tid);
+  solve_unit_lower(sA, sX, tid);
+  store_record_t(sX, sBeta, reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kBRecBytes, tid);
+}
+
 template <int DK, typename TIO, bool kW = false>
 struct KdaPrepLds {
   static constexpr int LX = DK + 16 / (int)sizeof(TIO);  // k, q row stride (elements)

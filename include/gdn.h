@@ -216,6 +216,44 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
                              float* state, void* o,
                              float* state_pre, float* scales, void* stream);
 
+/*
+ * gdn_chunk_bwd_dh -- backward state recurrence of the chunked forward with
+ * identity straight-through gradients through every QDQ (#2497 "What does
+ * this PR do?": identity straight-through gradients for QAT/QAD).  For the
+ * loss L = sum_t o_t . d_o_t + <S_L, d_final_state> of each sequence, the
+ * gradient of the state entering every 64-token chunk, by the chunk form
+ * of the reverse recurrence (per chunk, from the last):
+ *     dU' = P^T dO + diag(e^{gamma_C - gamma}) K dh^T,   Y = T^T dU',
+ *     dh  <- e^{gamma_C} dh + dO^T (Q o e^gamma) - Y^T (K o e^gamma),
+ * with T, P, gamma as in the forward.  The straight-through QDQ leaves the
+ * states out of it, so no forward state is needed.  Whole sequences (no
+ * prefix/suffix split); scalar gate; bf16 q, k and d_o.
+ *   shape       as for gdn_chunk_fwd (io_dtype GDN_BF16, gate_per_channel 0;
+ *               o_dtype and qdq_flags are not used)
+ *   q, k        [total_tokens, H, dk] bf16;  beta, g [total_tokens, H] fp32
+ *   cu_seqlens, seq_lens   as for gdn_chunk_fwd (seq_lens nullable)
+ *   d_o         [total_tokens, H, dv] bf16, the gradient of o (padding rows ignored)
+ *   d_final_state  [N, H, dv, dk] fp32 or NULL (zero)
+ *   dh          [n_bounds, H, dv, dk] fp32 or NULL: chunk i of sequence n at
+ *               b = sum_{m<n} ceil(L_m / 64) + i, the gradient of the state
+ *               entering that chunk
+ *   d_initial_state [N, H, dv, dk] fp32 or NULL: the gradient of the initial
+ *               state (d_final_state for an empty sequence)
+ *   workspace   at least gdn_chunk_bwd_workspace_bytes(shape) bytes, 256-byte
+ *               aligned, caller-owned, contents ignored on entry.
+ */
+gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape,
+                              const void* q, const void* k, const float* beta, const float* g,
+                              const int32_t* cu_seqlens, const int32_t* seq_lens,
+                              const void* d_o, const float* d_final_state,
+                              float* dh, float* d_initial_state,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace bytes gdn_chunk_bwd_dh needs: the chunk offsets and, per
+ * (chunk, head) of the worst-case chunk count, T^T and P^T as full 64 x 64
+ * records (16 KiB each).  0 for an invalid shape. */
+size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape_t* shape);
+
 /* Static description of a status code. */
 const char* gdn_status_string(gdn_status_t status);
 

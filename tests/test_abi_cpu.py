@@ -158,3 +158,26 @@ def test_decode_rejects_bad_args():
 def test_valid_call_without_gpu_reports_device_error():
     assert _chunk(_shape()) == 3
     assert "device" in _lib.last_error().lower()
+
+
+def _bwd(shape, q=FAKE, do=FAKE, dh=FAKE, d0=FAKE, ws=FAKE, ws_bytes=None):
+    p = ctypes.c_void_p
+    L = _lib.lib()
+    if ws_bytes is None:
+        ws_bytes = L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(shape))
+    return L.gdn_chunk_bwd_dh(ctypes.byref(shape), p(q), p(FAKE), p(FAKE), p(FAKE), p(FAKE), None, p(do), None,
+                              p(dh) if dh else None, p(d0) if d0 else None, p(ws), ws_bytes, None)
+
+
+def test_chunk_bwd_dh_checks():
+    """Workspace: chunk offsets plus two 16 KiB records (T^T, P^T) per chunk
+    and head of the worst-case count; bf16 and the scalar gate only; at least
+    one output; buffers aligned."""
+    L = _lib.lib()
+    s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
+    assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(s)) == 256 + (3 + 3) * 2 * 2 * 16384
+    assert _bwd(_shape(io_dtype=0, dk=64)) == 2
+    assert _bwd(_shape(gate_per_channel=1)) == 2
+    assert _bwd(_shape(), dh=0, d0=0) == 1
+    assert _bwd(_shape(), q=FAKE + 8) == 1
+    assert _bwd(_shape(), ws_bytes=100) == 1
