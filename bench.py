@@ -70,6 +70,22 @@ def split_state_kernel_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes,
     return prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes) + n_chunk_heads * 2 * T_RECORD_BYTES
 
 
+def bwd_flops_per_token_head(C, dk, dv):
+    """Algorithmic flops of the backward state recurrence per token and head
+    (dense 64x64 tiles): K K^T and Q K^T for A and P (2C dk each), the solve
+    (C^2 / 3), K dh^T (2 dk dv), P^T dO and T^T dU' (2C dv each), and the two
+    update products Q^T (e dO), K^T (e Y) (2 dk dv each)."""
+    return 2 * C * (2 * dk + 2 * dv) + 6 * dk * dv + C * C / 3
+
+
+def bwd_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes):
+    """Algorithmic HBM bytes of the backward state recurrence: q, k, dO
+    read once, beta and g read once, dh written once per chunk, the final
+    state's gradient read and the initial state's written."""
+    return (T_heads * (io_bytes * (2 * dk + dv) + 8) + n_chunk_heads * dv * dk * 4
+            + 2 * n_states * dv * dk * 4)
+
+
 def decode_bytes(n_heads_seqs, dk, dv, io_bytes, o_bytes):
     """Per decode step: the fp32 state read and written once, q, k, v read,
     beta and g read, o written."""
@@ -290,6 +306,34 @@ def main():
                      "avg_launch_ms": round(w_kern, 5),
                      "mfma_tflops": round(w_tflops, 2),
                      "mfma_frac": round(w_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}}
+
+    # ---------------- backward state recurrence, same shape (reported) ----------------
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6)
+    d_o = torch.randn((w.total_tokens, H, dv), generator=gen, device=dev).to(torch.bfloat16)
+    dS_L = torch.randn((B, H, dv, dk), generator=gen, device=dev)
+    n_bounds = B * ((T + 63) // 64)
+    dh_out = torch.empty((n_bounds, H, dv, dk), device=dev)
+    d0_out = torch.empty((B, H, dv, dk), device=dev)
+
+    def step_bwd():
+        api.chunk_bwd_dh(d["q"], d["k"], d["beta"], d["g"], d["cu_seqlens"], d_o, d_final_state=dS_L,
+                         dh=dh_out, d_initial_state=d0_out)
+
+    bwd_ms, _ = time_launches(step_bwd, args.steps, args.warmup)
+    bwd_ms /= args.steps
+    bfl = bwd_flops_per_token_head(64, dk, dv) * token_heads
+    bby = bwd_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2)
+    out["bwd_dh"] = {"workload": "the same prefill workload: gradients of every chunk's entering state "
+                                 "and of the initial state for L = sum o . dO + <S_L, dS_L>, identity "
+                                 "straight-through QDQ",
+                     "ms_per_step": round(bwd_ms, 5), "tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
+                     "kernels": "chunk_offsets_kernel + chunk_bwd_prep_kernel<128> + chunk_bwd_dh_kernel<128>",
+                     "mfma_tflops": round(bfl / (bwd_ms * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(bfl / (bwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "hbm_gbs": round(bby / (bwd_ms * 1e-3) / 1e9, 1),
+                     "algorithmic_flops_per_step": bfl, "algorithmic_bytes_per_step": bby}
+    del d_o, dS_L, dh_out, d0_out
 
     # ---------------- per-key-channel gate (KDA) prefill, same shape (reported) ----------------
     if not args.no_kda:

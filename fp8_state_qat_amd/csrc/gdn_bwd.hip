@@ -17,17 +17,22 @@
 // four waves per (sequence, head, 64-row value tile), the chunks in reverse
 // order; wave w owns dh rows 16w .. 16w + 15 of the tile (dk/16 fp32
 // accumulator tiles, the forward state's layout) and runs every product for
-// them.  bf16 inputs; fp32 operands enter the bf16 MFMA as hi + lo pairs.
+// them.  The loads of chunk c - 1 (k and q dumps, dO rows, both records, by
+// direct global->LDS loads into the other of two buffers) are issued while
+// chunk c computes.  Rows past a chunk's end load its last valid row; the
+// P^T columns and the e^gamma entries of those rows are zero, so they reach
+// no result.  bf16 inputs; fp32 operands enter the bf16 MFMA as hi + lo
+// pairs.
 #include "gdn_prep_item.hpp"
 
 namespace gdn {
 
 constexpr int kBwdThreads = 256;
 
-// LDS of the dh kernel (bytes): the k and q dumps of the chunk (the forward's
-// rotated fragment layout, so K^T and Q^T come back by transpose reads), the
-// tile's dO rows (padded rows, zero past the chunk's end), the T^T and P^T
-// records, and the gates.
+// LDS of the dh kernel (bytes), two buffers by chunk parity: the k and q
+// dumps of the chunk (the forward's rotated fragment layout, so K^T and Q^T
+// come back by transpose reads), the tile's dO rows (padded rows), the T^T
+// and P^T records, and the gates.
 template <int DK>
 struct BwdLds {
   static constexpr int NKB = DK / 32;
@@ -38,9 +43,10 @@ struct BwdLds {
   static constexpr size_t oO = oQ + 4 * NKB * F;
   static constexpr size_t oTT = oO + 64 * RS * 2;
   static constexpr size_t oPT = oTT + kBRecBytes;
-  static constexpr size_t oVec = oPT + kBRecBytes;     // e^gamma [64], e^{gamma_C - gamma} [64], e^{gamma_C}
-  static constexpr size_t bytes = oVec + (2 * 64 + 4) * sizeof(float);
-  static_assert(oTT % 16 == 0 && oPT % 16 == 0, "direct loads need 16-byte aligned LDS");
+  static constexpr size_t oVec = oPT + kBRecBytes;     // e^gamma [64] (0 past the end), e^{gamma_C - gamma} [64], e^{gamma_C}
+  static constexpr size_t buf = oVec + (2 * 64 + 4) * sizeof(float);  // one buffer
+  static constexpr size_t bytes = 2 * buf;
+  static_assert(oTT % 16 == 0 && oPT % 16 == 0 && buf % 16 == 0, "direct loads need 16-byte aligned LDS");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -86,12 +92,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
   constexpr int NT = DK / 16, NKB = DK / 32;
   constexpr int RS = (int)Ls::RS;
   extern __shared__ __align__(16) char smem[];
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem + Ls::oK);
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem + Ls::oQ);
-  uint16_t* sO = reinterpret_cast<uint16_t*>(smem + Ls::oO);
-  const uint16_t* sTT = reinterpret_cast<const uint16_t*>(smem + Ls::oTT);
-  const uint16_t* sPT = reinterpret_cast<const uint16_t*>(smem + Ls::oPT);
-  float* vec = reinterpret_cast<float*>(smem + Ls::oVec);
   const uint32_t lds0 = lds_base_u32(smem);
 
   const int tid = threadIdx.x;
@@ -132,54 +132,74 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     }
   }
 
-  for (int c = n_chunks - 1; c >= 0; --c) {
-    const int t0 = seg0 + c * kChunk;
-    const int nv = min(kChunk, L - c * kChunk);
-    // ---- stage the chunk: k and q dumps and the two records by direct
-    // loads, dO rows (zero past nv) and the log-gates by plain loads
-    {
-      const uint16_t* gk = args.k + (int64_t)t0 * qk_row + (int64_t)h * DK;
-      const uint16_t* gqv = args.q + (int64_t)t0 * qk_row + (int64_t)h * DK;
+  // direct loads of chunk cc into buffer b: k and q dumps, dO rows (padded
+  // rows, 7 per instruction), the two records; wave 0 fetches the log-gates
+  float pg = 0.f;
+  auto issue = [&](int cc, int b) {
+    const int t0 = seg0 + cc * kChunk;
+    const int nv = min(kChunk, L - cc * kChunk);
+    const uint32_t base = lds0 + (uint32_t)(b * Ls::buf);
+    const uint16_t* gk = args.k + (int64_t)t0 * qk_row + (int64_t)h * DK;
+    const uint16_t* gqv = args.q + (int64_t)t0 * qk_row + (int64_t)h * DK;
 #pragma unroll
-      for (int ii = 0; ii < NKB; ++ii) {
-        const int i = w + 4 * ii;  // instruction: 64 lane slots of 16 bytes
-        const int u = i * 64 + lane;
-        const int f = u >> 6, l2 = rot_lane(u & 63);
-        const int r = 16 * (f / NKB) + (l2 & 15);
-        const int d = 32 * (f % NKB) + 8 * (l2 >> 4);
-        const uint32_t off = (uint32_t)((min(r, nv - 1) * (int)qk_row + d) * 2);
-        lds_load16(gk, off, lds0 + (uint32_t)Ls::oK + i * 1024);
-        lds_load16(gqv, off, lds0 + (uint32_t)Ls::oQ + i * 1024);
-      }
-      const char* tt = args.TT + ((int64_t)(chunk0 + c) * H + h) * kBRecBytes;
-      const char* pt = args.PT + ((int64_t)(chunk0 + c) * H + h) * kBRecBytes;
-#pragma unroll
-      for (int ii = 0; ii < kBRecBytes / 1024 / 4; ++ii) {
-        const int idx = w * (kBRecBytes / 1024 / 4) + ii;
-        lds_load16(tt, (uint32_t)((idx * 64 + lane) * 16), lds0 + (uint32_t)Ls::oTT + idx * 1024);
-        lds_load16(pt, (uint32_t)((idx * 64 + lane) * 16), lds0 + (uint32_t)Ls::oPT + idx * 1024);
-      }
-      // dO rows: 64 rows x 8 pieces of 16 bytes, two pieces per thread
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const int piece = tid + kBwdThreads * pp, r = piece >> 3, pc = piece & 7;
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (r < nv)
-          x = *reinterpret_cast<const uint4*>(args.dout + (int64_t)(t0 + r) * v_row + (int64_t)h * dv +
-                                              kTileRows * vt + 8 * pc);
-        *reinterpret_cast<uint4*>(sO + r * RS + 8 * pc) = x;
-      }
-      if (w == 0) {
-        const float gv = (lane < nv) ? args.g[(int64_t)(t0 + lane) * H + h] : 0.f;
-        const float x = wave_prefix_sum(gv);
-        const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-        vec[lane] = __builtin_amdgcn_exp2f(x * kLog2e);
-        vec[64 + lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
-        if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gC * kLog2e);
-      }
-      wait_vmem();
+    for (int ii = 0; ii < NKB; ++ii) {
+      const int i = w + 4 * ii;  // instruction: 64 lane slots of 16 bytes
+      const int u = i * 64 + lane;
+      const int f = u >> 6, l2 = rot_lane(u & 63);
+      const int r = 16 * (f / NKB) + (l2 & 15);
+      const int d = 32 * (f % NKB) + 8 * (l2 >> 4);
+      const uint32_t off = (uint32_t)((min(r, nv - 1) * (int)qk_row + d) * 2);
+      lds_load16(gk, off, base + (uint32_t)Ls::oK + i * 1024);
+      lds_load16(gqv, off, base + (uint32_t)Ls::oQ + i * 1024);
     }
-    __syncthreads();
+    const char* tt = args.TT + ((int64_t)(chunk0 + cc) * H + h) * kBRecBytes;
+    const char* pt = args.PT + ((int64_t)(chunk0 + cc) * H + h) * kBRecBytes;
+#pragma unroll
+    for (int ii = 0; ii < kBRecBytes / 1024 / 4; ++ii) {
+      const int idx = w * (kBRecBytes / 1024 / 4) + ii;
+      lds_load16(tt, (uint32_t)((idx * 64 + lane) * 16), base + (uint32_t)Ls::oTT + idx * 1024);
+      lds_load16(pt, (uint32_t)((idx * 64 + lane) * 16), base + (uint32_t)Ls::oPT + idx * 1024);
+    }
+    {
+      constexpr int RPI = 64 / 9, NI = (64 + RPI - 1) / RPI;  // 9 slots of 16 bytes per padded row
+      const uint16_t* src = args.dout + (int64_t)t0 * v_row + (int64_t)h * dv + kTileRows * vt;
+      const int rr = lane / 9, pc = lane % 9;
+      const int lane_off = min(pc, 7) * 8;
+#pragma unroll
+      for (int ii = 0; ii < (NI + 3) / 4; ++ii) {
+        const int i = w + 4 * ii;
+        const int r = i * RPI + rr;
+        if (i < NI && rr < RPI && r < 64)
+          lds_load16(src, (uint32_t)((min(r, nv - 1) * (int)v_row + lane_off) * 2),
+                     base + (uint32_t)Ls::oO + i * RPI * RS * 2);
+      }
+    }
+    if (w == 0) pg = (lane < nv) ? args.g[(int64_t)(t0 + lane) * H + h] : 0.f;
+  };
+  // wave 0: the gates of chunk cc from pg (e^gamma is zero past the chunk's end)
+  auto scan = [&](int cc, float* vec) {
+    const int nv = min(kChunk, L - cc * kChunk);
+    const float x = wave_prefix_sum(pg);
+    const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    vec[lane] = (lane < nv) ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;
+    vec[64 + lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
+    if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gC * kLog2e);
+  };
+
+  if (n_chunks > 0) issue(n_chunks - 1, (n_chunks - 1) & 1);
+  for (int c = n_chunks - 1; c >= 0; --c) {
+    const int b = c & 1;
+    char* bufp = smem + b * Ls::buf;
+    uint16_t* sK = reinterpret_cast<uint16_t*>(bufp + Ls::oK);
+    uint16_t* sQ = reinterpret_cast<uint16_t*>(bufp + Ls::oQ);
+    uint16_t* sO = reinterpret_cast<uint16_t*>(bufp + Ls::oO);
+    const uint16_t* sTT = reinterpret_cast<const uint16_t*>(bufp + Ls::oTT);
+    const uint16_t* sPT = reinterpret_cast<const uint16_t*>(bufp + Ls::oPT);
+    float* vec = reinterpret_cast<float*>(bufp + Ls::oVec);
+    if (w == 0) scan(c, vec);
+    wait_vmem();      // this wave's loads of chunk c are in LDS
+    __syncthreads();  // ... every wave's, and the gates; chunk c + 1's buffer is free
+    if (c > 0) issue(c - 1, b ^ 1);
 
     // ---- G = K dh^T (A = k rows, B = dh as hi + lo)
     Fr dhh[NKB], dhl[NKB];
@@ -312,7 +332,6 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
         *reinterpret_cast<float4*>(args.dh + base + dkmap(16 * t + 4 * gq)) =
             make_float4(dst[t][0], dst[t][1], dst[t][2], dst[t][3]);
     }
-    __syncthreads();  // the chunk's LDS is free for the next (earlier) chunk
   }
   if (args.dinit) {
     const int64_t base = ((int64_t)nh * dv + vcol0) * DK;

@@ -503,7 +503,8 @@ struct PrepBwdLds {
 };
 
 // The backward records of chunk j (tokens t0 .. t0 + nv - 1), head h (bf16
-// inputs): T^T with T = (I + A)^-1 diag(beta) into a.T, P^T into a.P.
+// inputs): T^T with T = (I + A)^-1 diag(beta) into a.T, P^T into a.P (the
+// rows of P past nv, i.e. the columns of P^T, zero).
 // Four waves (item thread index tid), LDS block lds of PrepBwdLds bytes.
 // Contains workgroup barriers.  On return this wave's record stores may
 // still be in flight.
@@ -580,7 +581,7 @@ __device__ __forceinline__ void prep_item_bwd(const PrepArgs& a, int j, int h, i
       const int s = 16 * S + 4 * gq + i;
       const float e = (s <= r) ? __builtin_amdgcn_exp2f(g2r - sG2[s]) : 0.f;
       va[i] = (s < r) ? br * e * ca[i] : 0.f;
-      vp[i] = e * cp[i];
+      vp[i] = (r < nv) ? e * cp[i] : 0.f;  // rows past the chunk's end are zero
     }
     *reinterpret_cast<float4*>(sA + r * L64 + 16 * S + 4 * gq) = make_float4(va[0], va[1], va[2], va[3]);
     *reinterpret_cast<float4*>(sP + r * L64 + 16 * S + 4 * gq) = make_float4(vp[0], vp[1], vp[2], vp[3]);
