@@ -85,3 +85,18 @@ def test_bwd_dh_full_size_sampled():
         r1, r0 = rel_l2(dh[64 * n:64 * (n + 1), h], r_dh), rel_l2(d0[n, h], r_0)
         print(f"(n, h)=({n}, {h}): dh rel={r1:.3e} d_initial rel={r0:.3e}", flush=True)
         assert r1 <= TOL and r0 <= TOL
+
+
+def test_bwd_dh_many_workgroups_against_oracle():
+    """192 dh workgroups (24 heads, 2 value tiles, uneven lengths): sampled
+    pairs against the oracle."""
+    w, do, dS = _case([300, 200, 64, 130], 24, 128, 128, seed=99)
+    dh, d0 = _run(w, do, dS)
+    q, k, b, g, dof = w.f64("q"), w.f64("k"), w.f64("beta"), w.f64("g"), _do_f64(do)
+    offs = np.concatenate([[0], np.cumsum([(int(L) + 63) // 64 for L in w.seq_lens])])
+    for (n, h) in [(0, 0), (1, 13), (3, 23)]:
+        sl = slice(int(w.cu_seqlens[n]), int(w.cu_seqlens[n]) + int(w.seq_lens[n]))
+        r_dh, r_0 = state_grads(q[sl, h], k[sl, h], b[sl, h], g[sl, h], dof[sl, h], dS[n, h])
+        r1, r0 = rel_l2(dh[offs[n]:offs[n + 1], h], r_dh), rel_l2(d0[n, h], r_0)
+        print(f"(n, h)=({n}, {h}): dh rel={r1:.3e} d_initial rel={r0:.3e}", flush=True)
+        assert r1 <= TOL and r0 <= TOL
