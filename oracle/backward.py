@@ -16,7 +16,9 @@ backwards (G the gradient with respect to S_t):
     for t = L .. 1:   G <- G + do_t q_t^T                (o_t = S_t q_t)
                       G <- a_t G (I - beta_t k_t k_t^T)   (now d L / d S_{t-1})
 The state entering chunk c of the chunked prefix is S_{64c}; its gradient
-dh_c is G right after token 64c + 1 has been taken back.  A per-key-channel
+dh_c is G right after token 64c + 1 has been taken back.  v_t enters only
+through beta_t v_t k_t^T, so its gradient is beta_t G k_t with G the
+gradient of S_t (before taking token t back).  A per-key-channel
 gate (S_{t-1} diag(a_t) in place of a_t S_{t-1}) gives G <- G (I - beta k
 k^T) diag(a_t).
 """
@@ -27,12 +29,13 @@ import numpy as np
 CHUNK = 64
 
 
-def state_grads(q, k, beta, g, do, dS_L=None, *, chunk=CHUNK):
+def state_grads(q, k, beta, g, do, dS_L=None, *, chunk=CHUNK, want_dv=False):
     """One (sequence, head).  q, k: [L, dk]; beta: [L]; g: [L] or [L, dk];
     do: [L, dv]; dS_L: [dv, dk] or None (zero).  float64.
 
     Returns (dh [ceil(L / chunk), dv, dk] the gradient of each chunk's
-    entering state, dS0 [dv, dk] the gradient of the initial state)."""
+    entering state, dS0 [dv, dk] the gradient of the initial state), and
+    with want_dv also dv [L, dv], the gradient of the values."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     beta = np.asarray(beta, np.float64)
@@ -43,14 +46,18 @@ def state_grads(q, k, beta, g, do, dS_L=None, *, chunk=CHUNK):
     G = np.zeros((dv, dk)) if dS_L is None else np.array(dS_L, dtype=np.float64)
     nb = (L + chunk - 1) // chunk
     dh = np.zeros((nb, dv, dk))
+    dvals = np.zeros((L, dv))
     for t in range(L, 0, -1):
         i = t - 1
         G = G + np.outer(do[i], q[i])
         Gk = G @ k[i]
+        dvals[i] = beta[i] * Gk
         G = G - beta[i] * np.outer(Gk, k[i])
         G = G * np.exp(g[i]) if g.ndim == 1 else G * np.exp(g[i])[None, :]
         if (t - 1) % chunk == 0:
             dh[(t - 1) // chunk] = G
+    if want_dv:
+        return dh, G, dvals
     return dh, G
 
 
@@ -58,7 +65,7 @@ def packed_state_grads(q, k, beta, g, do, cu_seqlens, *, seq_lens=None, dS_L=Non
     """Packed layout: q, k [T, H, dk], beta [T, H], g [T, H] or [T, H, dk],
     do [T, H, dv], dS_L [N, H, dv, dk] or None.  Returns (dh [n_bounds, H,
     dv, dk] with chunk b of sequence n at b = sum_{m<n} ceil(L_m/64) + i,
-    dS0 [N, H, dv, dk])."""
+    dS0 [N, H, dv, dk], dv [T, H, dv] with zero padding rows)."""
     cu = np.asarray(cu_seqlens, np.int64)
     N = cu.size - 1
     H, dk = k.shape[1], k.shape[2]
@@ -68,13 +75,15 @@ def packed_state_grads(q, k, beta, g, do, cu_seqlens, *, seq_lens=None, dS_L=Non
     offs = np.concatenate([[0], np.cumsum(nbs)]).astype(np.int64)
     dh = np.zeros((int(offs[-1]), H, dv, dk))
     dS0 = np.zeros((N, H, dv, dk))
+    dvals = np.zeros(do.shape)
     for n in range(N):
         s0, L = int(cu[n]), int(lens[n])
         sl = slice(s0, s0 + L)
         for h in range(H):
             gg = g[sl, h] if g.ndim == 2 else g[sl, h, :]
-            r_dh, r_0 = state_grads(q[sl, h], k[sl, h], beta[sl, h], gg, do[sl, h],
-                                    None if dS_L is None else dS_L[n, h])
+            r_dh, r_0, r_v = state_grads(q[sl, h], k[sl, h], beta[sl, h], gg, do[sl, h],
+                                         None if dS_L is None else dS_L[n, h], want_dv=True)
             dh[offs[n]:offs[n + 1], h] = r_dh
             dS0[n, h] = r_0
-    return dh, dS0
+            dvals[sl, h] = r_v
+    return dh, dS0, dvals

@@ -48,7 +48,7 @@ def test_bwd_dh_against_oracle(dk, dv):
     final-state gradient), one token, chunk multiples and tails."""
     w, do, dS = _case([300, 0, 1, 64, 129], 2, dk, dv, seed=91 + dk + dv)
     dh, d0 = _run(w, do, dS)
-    ref_dh, ref_d0 = packed_state_grads(w.f64("q"), w.f64("k"), w.f64("beta"), w.f64("g"), _do_f64(do),
+    ref_dh, ref_d0, _ = packed_state_grads(w.f64("q"), w.f64("k"), w.f64("beta"), w.f64("g"), _do_f64(do),
                                         w.cu_seqlens, seq_lens=w.seq_lens, dS_L=dS)
     r1, r0 = rel_l2(dh, ref_dh), rel_l2(d0, ref_d0)
     print(f"dk={dk} dv={dv}: dh rel={r1:.3e} d_initial rel={r0:.3e}", flush=True)
@@ -67,7 +67,7 @@ def test_bwd_dh_nan_padding_changes_nothing():
     do_nan[~valid] = 0x7FC0  # bf16 NaN
     dh, d0 = _run(w, do_nan, dS)
     assert np.all(np.isfinite(dh)) and np.all(np.isfinite(d0))
-    ref_dh, ref_d0 = packed_state_grads(np.nan_to_num(w.f64("q")), np.nan_to_num(w.f64("k")),
+    ref_dh, ref_d0, _ = packed_state_grads(np.nan_to_num(w.f64("q")), np.nan_to_num(w.f64("k")),
                                         np.nan_to_num(w.f64("beta")), np.nan_to_num(w.f64("g")),
                                         np.nan_to_num(_do_f64(do_nan)), w.cu_seqlens, seq_lens=w.seq_lens, dS_L=dS)
     assert rel_l2(dh, ref_dh) <= TOL and rel_l2(d0, ref_d0) <= TOL

@@ -613,6 +613,27 @@ def test_state_grads_against_forward_differences(per_channel):
             assert abs(d - dh[c, i, j]) <= 1e-10 * max(1.0, abs(d)), (c, i, j)
 
 
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_value_grads_against_forward_differences(per_channel):
+    """L is affine in every value vector, so <dv_t, u> = L(v + u e_t) - L(v)
+    for a random direction u at sampled tokens t (chunk ends and middles).
+    Catches a missing beta or a gradient taken before the output term."""
+    L, dk, dv = 150, 64, 64
+    q, k, v, b, g = _seq(L, dk, dv, per_channel=per_channel, seed=85,
+                         g_scale=0.05 if per_channel else 0.1)
+    rng = np.random.default_rng(86)
+    do = rng.standard_normal((L, dv))
+    dS = rng.standard_normal((dv, dk))
+    _, _, dvals = state_grads(q, k, b, g, do, dS, want_dv=True)
+    base = _loss(q, k, v, b, g, do, dS, None)
+    for t in (0, 63, 64, 100, 149):
+        u = rng.standard_normal(dv)
+        v2 = v.copy()
+        v2[t] += u
+        d = _loss(q, k, v2, b, g, do, dS, None) - base
+        assert abs(d - dvals[t] @ u) <= 1e-9 * max(1.0, abs(d)), (t, d, dvals[t] @ u)
+
+
 def test_state_grads_one_token_closed_form():
     """One token from S_0: o = S_1 q with S_1 = a S_0 (I - b k k^T) + b v k^T,
     so dL/dS_0 = a (do q^T + dS) (I - b k k^T)."""
