@@ -80,9 +80,10 @@ def bwd_flops_per_token_head(C, dk, dv):
 
 def bwd_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes):
     """Algorithmic HBM bytes of the backward state recurrence: q, k, dO
-    read once, beta and g read once, dh written once per chunk, the final
-    state's gradient read and the initial state's written."""
-    return (T_heads * (io_bytes * (2 * dk + dv) + 8) + n_chunk_heads * dv * dk * 4
+    read once, beta and g read once, the fp32 value gradient written once,
+    dh written once per chunk, the final state's gradient read and the
+    initial state's written."""
+    return (T_heads * (io_bytes * (2 * dk + dv) + 8 + 4 * dv) + n_chunk_heads * dv * dk * 4
             + 2 * n_states * dv * dk * 4)
 
 
@@ -315,17 +316,18 @@ def main():
     n_bounds = B * ((T + 63) // 64)
     dh_out = torch.empty((n_bounds, H, dv, dk), device=dev)
     d0_out = torch.empty((B, H, dv, dk), device=dev)
+    dv_out = torch.empty((w.total_tokens, H, dv), device=dev)
 
     def step_bwd():
         api.chunk_bwd_dh(d["q"], d["k"], d["beta"], d["g"], d["cu_seqlens"], d_o, d_final_state=dS_L,
-                         dh=dh_out, d_initial_state=d0_out)
+                         dh=dh_out, d_initial_state=d0_out, d_v=dv_out)
 
     bwd_ms, _ = time_launches(step_bwd, args.steps, args.warmup)
     bwd_ms /= args.steps
     bfl = bwd_flops_per_token_head(64, dk, dv) * token_heads
     bby = bwd_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2)
-    out["bwd_dh"] = {"workload": "the same prefill workload: gradients of every chunk's entering state "
-                                 "and of the initial state for L = sum o . dO + <S_L, dS_L>, identity "
+    out["bwd_dh"] = {"workload": "the same prefill workload: gradients of every chunk's entering state, "
+                                 "of the initial state and of v for L = sum o . dO + <S_L, dS_L>, identity "
                                  "straight-through QDQ",
                      "ms_per_step": round(bwd_ms, 5), "tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
                      "kernels": "chunk_offsets_kernel + chunk_bwd_prep_kernel<128> + chunk_bwd_dh_kernel<128>",
@@ -333,7 +335,7 @@ def main():
                      "mfma_frac": round(bfl / (bwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                      "hbm_gbs": round(bby / (bwd_ms * 1e-3) / 1e9, 1),
                      "algorithmic_flops_per_step": bfl, "algorithmic_bytes_per_step": bby}
-    del d_o, dS_L, dh_out, d0_out
+    del d_o, dS_L, dh_out, d0_out, dv_out
 
     # ---------------- per-key-channel gate (KDA) prefill, same shape (reported) ----------------
     if not args.no_kda:

@@ -88,7 +88,7 @@ def lib():
     L.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_state_qdq.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
     L.gdn_state_qdq.restype = ctypes.c_int
-    L.gdn_chunk_bwd_dh.argtypes = [ctypes.POINTER(GdnShape)] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
+    L.gdn_chunk_bwd_dh.argtypes = [ctypes.POINTER(GdnShape)] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
     L.gdn_chunk_bwd_dh.restype = ctypes.c_int
     L.gdn_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
     L.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t

@@ -110,18 +110,20 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
 
 
 def chunk_bwd_dh(q, k, beta, g, cu_seqlens, d_o, *, seq_lens=None, d_final_state=None, dh=None,
-                 d_initial_state=None, workspace=None):
+                 d_initial_state=None, d_v=None, want_dv=False, workspace=None):
     """gdn_chunk_bwd_dh: gradients of the state entering every 64-token chunk
     (dh [n_bounds, H, dv, dk]) and of the initial state ([N, H, dv, dk]) for
-    L = sum o . d_o + <S_L, d_final_state>, identity straight-through QDQ.
-    q, k: [T, H, dk] bf16; d_o: [T, H, dv] bf16; beta, g: [T, H] fp32."""
+    L = sum o . d_o + <S_L, d_final_state>, identity straight-through QDQ;
+    with want_dv (or a d_v tensor) also the gradient of v ([T, H, dv] fp32).
+    q, k: [T, H, dk] bf16; d_o: [T, H, dv] bf16; beta, g: [T, H] fp32.
+    Returns (dh, d_initial_state) or (dh, d_initial_state, d_v)."""
     T, H, dk = k.shape
     dv = d_o.shape[2]
     N = cu_seqlens.numel() - 1
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16), ("d_o", d_o, torch.bfloat16),
                         ("beta", beta, torch.float32), ("g", g, torch.float32),
                         ("cu_seqlens", cu_seqlens, torch.int32), ("seq_lens", seq_lens, torch.int32),
-                        ("d_final_state", d_final_state, torch.float32)):
+                        ("d_final_state", d_final_state, torch.float32), ("d_v", d_v, torch.float32)):
         _dev(t, name, dt)
     lens = seq_lens if seq_lens is not None else (cu_seqlens[1:] - cu_seqlens[:-1])
     n_bounds = int(((lens.to(torch.int64) + 63) // 64).sum().item()) if N else 0
@@ -129,6 +131,8 @@ def chunk_bwd_dh(q, k, beta, g, cu_seqlens, d_o, *, seq_lens=None, d_final_state
         dh = torch.empty((n_bounds, H, dv, dk), dtype=torch.float32, device=k.device)
     if d_initial_state is None:
         d_initial_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=k.device)
+    if want_dv and d_v is None:
+        d_v = torch.empty((T, H, dv), dtype=torch.float32, device=k.device)
     shape = _shape(N, H, dk, dv, T, k.dtype, k.dtype, g.dim() == 3, 0)
     ws_bytes = _lib.lib().gdn_chunk_bwd_workspace_bytes(ctypes.byref(shape))
     if ws_bytes == 0:
@@ -137,9 +141,11 @@ def chunk_bwd_dh(q, k, beta, g, cu_seqlens, d_o, *, seq_lens=None, d_final_state
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
     st = _lib.lib().gdn_chunk_bwd_dh(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(beta), _ptr(g),
                                      _ptr(cu_seqlens), _ptr(seq_lens), _ptr(d_o), _ptr(d_final_state),
-                                     _ptr(dh) if dh.numel() else None, _ptr(d_initial_state),
+                                     _ptr(dh) if dh.numel() else None, _ptr(d_initial_state), _ptr(d_v),
                                      _ptr(workspace), workspace.numel(), _stream())
     _lib.check(st)
+    if d_v is not None:
+        return dh, d_initial_state, d_v
     return dh, d_initial_state
 
 

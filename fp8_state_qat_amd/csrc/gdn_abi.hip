@@ -202,7 +202,7 @@ size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape_t* shape) {
 gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape, const void* q, const void* k, const float* beta,
                               const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
                               const void* d_o, const float* d_final_state, float* dh, float* d_initial_state,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              float* d_v, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
@@ -214,17 +214,18 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape, const void* q, const voi
                 workspace ? "" : ", NULL");
   if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (!cu_seqlens) return fail(GDN_ERR_INVALID_ARG, "cu_seqlens must be non-NULL");
-  if (!dh && !d_initial_state) return fail(GDN_ERR_INVALID_ARG, "dh and d_initial_state are both NULL");
+  if (!dh && !d_initial_state && !d_v) return fail(GDN_ERR_INVALID_ARG, "dh, d_initial_state and d_v are all NULL");
   if (shape->total_tokens > 0 && (!q || !k || !beta || !g || !d_o))
     return fail(GDN_ERR_INVALID_ARG, "q, k, beta, g and d_o must be non-NULL");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(d_o, 16) || !aligned(dh, 16) ||
-      !aligned(d_initial_state, 16) || !aligned(d_final_state, 16) || !aligned(beta, 4) || !aligned(g, 4) ||
+      !aligned(d_initial_state, 16) || !aligned(d_final_state, 16) || !aligned(d_v, 4) || !aligned(beta, 4) ||
+      !aligned(g, 4) ||
       !aligned(cu_seqlens, 4))
     return fail(GDN_ERR_INVALID_ARG, "misaligned buffer (q, k, d_o and states need 16 bytes)");
   st = check_device();
   if (st != GDN_OK) return st;
   hipError_t e = gdn::launch_chunk_bwd_dh(*shape, q, k, beta, g, cu_seqlens, seq_lens, d_o, d_final_state, dh,
-                                          d_initial_state, workspace, (hipStream_t)stream);
+                                          d_initial_state, d_v, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return GDN_OK;
 }

@@ -10,7 +10,8 @@
 //     Y    = T^T dU'
 //     dh_c = e^{gamma_C} dh_{c+1} + dO^T (Q o e^gamma) - Y^T (K o e^gamma)
 // starting from dh = dS_L after the last chunk.  The states themselves do
-// not enter (L is linear in them), so neither does the QDQ.
+// not enter (L is linear in them), so neither does the QDQ.  V enters a
+// chunk only through U = T V, so Y is also the gradient of its values.
 //
 // chunk_bwd_prep_kernel: per (chunk, head) in parallel, T^T and P^T as full
 // 64 x 64 records (prep_item_bwd).  chunk_bwd_dh_kernel: one workgroup of
@@ -81,6 +82,7 @@ struct BwdArgs {
   const char* PT;         // one P^T record per (chunk, head)
   float* dh;              // [n_bounds, H, dv, dk] or null
   float* dinit;           // [N, H, dv, dk] or null
+  float* dvals;           // [T, H, dv] or null
   int H;
   int dv;
 };
@@ -98,8 +100,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
   const int w = uniform(tid >> 6);
   const int lane = tid & 63, gq = lane >> 4, ln = lane & 15;
   const int H = args.H, dv = args.dv, tiles = dv / kTileRows;
-  const int vt = (int)blockIdx.x % tiles;
-  const int nh = (int)blockIdx.x / tiles;
+  // Workgroup b runs on XCD b % 8.  Each XCD takes a contiguous run of
+  // (sequence, head, value tile) items, so that the value tiles of a head
+  // share one L2 (their q, k, dO rows and records are fetched once) and the
+  // value-gradient rows one XCD writes span whole lines across its channels.
+  const int nb = (int)gridDim.x, xq = nb / 8, xr = nb % 8, xc = (int)blockIdx.x % 8;
+  const int item = xc * xq + min(xc, xr) + (int)blockIdx.x / 8;
+  const int vt = item % tiles;
+  const int nh = item / tiles;
   const int h = nh % H, n = nh / H;
   const int seg0 = args.cu_seqlens[n];
   const int L = args.seq_lens ? args.seq_lens[n] : (args.cu_seqlens[n + 1] - seg0);
@@ -186,6 +194,40 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gC * kLog2e);
   };
 
+  // The results of chunk c + 1 (dh_{c+1}, still in dst until the update at
+  // the end of chunk c, and its value gradient, kept in pend_y) are stored
+  // after chunk c's prefetch is issued, so that the wait at the top of the
+  // next chunk finds them long done instead of draining them.
+  f32x4 pend_y[4];
+  auto store_results = [&](int cs) {
+    if (args.dh) {
+      const int64_t base = (((int64_t)(chunk0 + cs) * H + h) * dv + vcol0) * DK;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<float4*>(args.dh + base + dkmap(16 * t + 4 * gq)) =
+            make_float4(dst[t][0], dst[t][1], dst[t][2], dst[t][3]);
+    }
+    // the value gradient: lane holds Y[16ti + 4gq + i][16w + ln]
+    if (args.dvals) {
+      const int nv = min(kChunk, L - cs * kChunk);
+      float* dvp = args.dvals + ((int64_t)(seg0 + cs * kChunk) * H + h) * dv + kTileRows * vt + 16 * w + ln;
+      if (nv == kChunk) {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dvp[(int64_t)(16 * ti + 4 * gq + i) * v_row] = pend_y[ti][i];
+      } else {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * ti + 4 * gq + i;
+            if (t < nv) dvp[(int64_t)t * v_row] = pend_y[ti][i];
+          }
+      }
+    }
+  };
+
   if (n_chunks > 0) issue(n_chunks - 1, (n_chunks - 1) & 1);
   for (int c = n_chunks - 1; c >= 0; --c) {
     const int b = c & 1;
@@ -200,6 +242,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     wait_vmem();      // this wave's loads of chunk c are in LDS
     __syncthreads();  // ... every wave's, and the gates; chunk c + 1's buffer is free
     if (c > 0) issue(c - 1, b ^ 1);
+    if (c + 1 < n_chunks) store_results(c + 1);
 
     // ---- G = K dh^T (A = k rows, B = dh as hi + lo)
     Fr dhh[NKB], dhl[NKB];
@@ -269,6 +312,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
       mma_bf16(yacc[ti], th, ul[kb]);
       mma_bf16(yacc[ti], frag(sTT, 8 + p), uh[kb]);
     }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) pend_y[ti] = yacc[ti];
     // ---- B operands of the update: e^gamma dO and -e^gamma Y, hi + lo
     Fr boh[2], bol[2], byh[2], byl[2];
 #pragma unroll
@@ -324,14 +369,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
         mma_bf16(dst[t], ka[kb], byl[kb]);
       }
     }
-    // ---- dh_c: the gradient of the state entering chunk c
-    if (args.dh) {
-      const int64_t base = (((int64_t)(chunk0 + c) * H + h) * dv + vcol0) * DK;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        *reinterpret_cast<float4*>(args.dh + base + dkmap(16 * t + 4 * gq)) =
-            make_float4(dst[t][0], dst[t][1], dst[t][2], dst[t][3]);
-    }
+    // dst now holds dh_c, the gradient of the state entering chunk c
+  }
+  if (n_chunks > 0) store_results(0);
+  if (args.dvals) {  // padding rows of the segment
+    const int seg_len = args.cu_seqlens[n + 1] - seg0;
+    for (int r = L + w; r < seg_len; r += kBwdThreads / 64)
+      args.dvals[((int64_t)(seg0 + r) * H + h) * dv + kTileRows * vt + lane] = 0.f;
   }
   if (args.dinit) {
     const int64_t base = ((int64_t)nh * dv + vcol0) * DK;
@@ -380,8 +424,8 @@ static hipError_t launch_bwd_dk(const gdn_shape_t& s, const PrepArgs& pa, const 
 
 hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                                const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
-                               const void* dout, const float* dfin, float* dh, float* dinit, void* workspace,
-                               hipStream_t stream) {
+                               const void* dout, const float* dfin, float* dh, float* dinit, float* dvals,
+                               void* workspace, hipStream_t stream) {
   char* w = reinterpret_cast<char*>(workspace);
   const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
   const int64_t items = max_chunks * s.n_heads;
@@ -412,6 +456,7 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
   ba.PT = PT;
   ba.dh = dh;
   ba.dinit = dinit;
+  ba.dvals = dvals;
   ba.H = s.n_heads;
   ba.dv = s.dv;
   return s.dk == 128 ? launch_bwd_dk<128>(s, pa, ba, items, stream) : launch_bwd_dk<64>(s, pa, ba, items, stream);

@@ -70,7 +70,7 @@ hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const
 size_t bwd_workspace_bytes(const gdn_shape_t& s);
 hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                                const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
-                               const void* dout, const float* dfin, float* dh, float* dinit, void* workspace,
-                               hipStream_t stream);
+                               const void* dout, const float* dfin, float* dh, float* dinit, float* dvals,
+                               void* workspace, hipStream_t stream);
 
 }  // namespace gdn

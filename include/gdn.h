@@ -221,8 +221,8 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
  * identity straight-through gradients through every QDQ (#2497 "What does
  * this PR do?": identity straight-through gradients for QAT/QAD).  For the
  * loss L = sum_t o_t . d_o_t + <S_L, d_final_state> of each sequence, the
- * gradient of the state entering every 64-token chunk, by the chunk form
- * of the reverse recurrence (per chunk, from the last):
+ * gradient of the state entering every 64-token chunk, and of v, by the
+ * chunk form of the reverse recurrence (per chunk, from the last):
  *     dU' = P^T dO + diag(e^{gamma_C - gamma}) K dh^T,   Y = T^T dU',
  *     dh  <- e^{gamma_C} dh + dO^T (Q o e^gamma) - Y^T (K o e^gamma),
  * with T, P, gamma as in the forward.  The straight-through QDQ leaves the
@@ -239,6 +239,9 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
  *               entering that chunk
  *   d_initial_state [N, H, dv, dk] fp32 or NULL: the gradient of the initial
  *               state (d_final_state for an empty sequence)
+ *   d_v         [total_tokens, H, dv] fp32 or NULL: the gradient of v (v enters a
+ *               chunk only through U = T V, so it is Y); rows of a segment past
+ *               L_n are written as 0, rows after cu_seqlens[N] are not written
  *   workspace   at least gdn_chunk_bwd_workspace_bytes(shape) bytes, 256-byte
  *               aligned, caller-owned, contents ignored on entry.
  */
@@ -246,7 +249,7 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape,
                               const void* q, const void* k, const float* beta, const float* g,
                               const int32_t* cu_seqlens, const int32_t* seq_lens,
                               const void* d_o, const float* d_final_state,
-                              float* dh, float* d_initial_state,
+                              float* dh, float* d_initial_state, float* d_v,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace bytes gdn_chunk_bwd_dh needs: the chunk offsets and, per

@@ -166,7 +166,7 @@ def _bwd(shape, q=FAKE, do=FAKE, dh=FAKE, d0=FAKE, ws=FAKE, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(shape))
     return L.gdn_chunk_bwd_dh(ctypes.byref(shape), p(q), p(FAKE), p(FAKE), p(FAKE), p(FAKE), None, p(do), None,
-                              p(dh) if dh else None, p(d0) if d0 else None, p(ws), ws_bytes, None)
+                              p(dh) if dh else None, p(d0) if d0 else None, None, p(ws), ws_bytes, None)
 
 
 def test_chunk_bwd_dh_checks():
