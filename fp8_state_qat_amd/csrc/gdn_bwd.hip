@@ -199,13 +199,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
   // after chunk c's prefetch is issued, so that the wait at the top of the
   // next chunk finds them long done instead of draining them.
   f32x4 pend_y[4];
+  // Results are written once and not read again here: non-temporal stores.
   auto store_results = [&](int cs) {
     if (args.dh) {
       const int64_t base = (((int64_t)(chunk0 + cs) * H + h) * dv + vcol0) * DK;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        *reinterpret_cast<float4*>(args.dh + base + dkmap(16 * t + 4 * gq)) =
-            make_float4(dst[t][0], dst[t][1], dst[t][2], dst[t][3]);
+        __builtin_nontemporal_store(dst[t], reinterpret_cast<f32x4*>(args.dh + base + dkmap(16 * t + 4 * gq)));
     }
     // the value gradient: lane holds Y[16ti + 4gq + i][16w + ln]
     if (args.dvals) {
@@ -215,14 +215,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dvp[(int64_t)(16 * ti + 4 * gq + i) * v_row] = pend_y[ti][i];
+          for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(pend_y[ti][i], dvp + (int64_t)(16 * ti + 4 * gq + i) * v_row);
       } else {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * ti + 4 * gq + i;
-            if (t < nv) dvp[(int64_t)t * v_row] = pend_y[ti][i];
+            if (t < nv) __builtin_nontemporal_store(pend_y[ti][i], dvp + (int64_t)t * v_row);
           }
       }
     }
