@@ -448,7 +448,21 @@ def main():
                               "hbm_gbs": round(dby / (dms8 * 1e-3) / 1e9, 1),
                               "hbm_frac": round(dby / (dms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "kernel": "decode_step_kernel<128, bf16, bf16, int8>"}
-        del tok, state
+
+        # the standalone state QDQ calls, in place on the same states (reported)
+        sc8 = torch.empty(state.shape[:-2] + (state.shape[-2] // 64,), dtype=torch.float32, device=dev)
+        sci = torch.empty(state.shape[:-1] + (state.shape[-1] // 32,), dtype=torch.float32, device=dev)
+        for name, fn, sc, kern in (("state_qdq", api.state_qdq, sc8, "state_qdq_kernel<8>"),
+                                   ("state_qdq_int8", api.state_qdq_int8, sci, "state_qdq_int8_kernel")):
+            qms, _ = time_launches(lambda: fn(state, out=state, scales=sc), args.steps, args.warmup)
+            qms /= args.steps
+            qby = 2 * state.numel() * 4 + sc.numel() * 4
+            out[name] = {"workload": f"{tuple(state.shape)} fp32 states, in place",
+                         "ms_per_call": round(qms, 5), "kernel": kern,
+                         "hbm_gbs": round(qby / (qms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(qby / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_call": qby}
+        del tok, state, sc8, sci
         torch.cuda.empty_cache()
 
     if args.copy_calibration_mib:

@@ -28,18 +28,6 @@
 
 namespace gdn {
 
-// The state is read once and written once per step and does not fit any
-// cache level: non-temporal accesses.
-typedef float f32x4_nt __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 ld_stream(const float4* p) {
-  const f32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void st_stream(float4* p, float4 x) {
-  const f32x4_nt v = {x.x, x.y, x.z, x.w};
-  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_nt*>(p));
-}
-
 template <int DK, typename TIO, typename TO, bool PC, bool kInt8>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,

@@ -4,8 +4,9 @@
 //
 // One workgroup of 256 threads per tile.  The tile (64 * dk fp32, 32 KiB at
 // dk = 128) is read once into registers with coalesced 16-byte loads, its
-// amax reduced in a fixed tree, then quantized and written back.  Memory
-// bound: 8 bytes of HBM traffic per state element.
+// amax reduced in a fixed tree, then quantized and written back, both with
+// non-temporal accesses.  Memory bound: 8 bytes of HBM traffic per state
+// element.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -21,16 +22,16 @@ __global__ __launch_bounds__(kThreads) void state_qdq_kernel(const float* in,
   const float4* src = reinterpret_cast<const float4*>(in) + tile * n4;
   float4* dst = reinterpret_cast<float4*>(out) + tile * n4;
   float4 x[V4];
-  float amax = 0.0f;
+  // every load is issued before the first use, so they are all in flight together
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
-    int idx = threadIdx.x + kThreads * j;
-    if (idx < n4) {
-      x[j] = src[idx];
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[j].x), fabsf(x[j].y)),
-                               fmaxf(fabsf(x[j].z), fabsf(x[j].w))));
-    }
+    const int idx = threadIdx.x + kThreads * j;
+    x[j] = idx < n4 ? ld_stream(src + idx) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < V4; ++j)
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[j].x), fabsf(x[j].y)), fmaxf(fabsf(x[j].z), fabsf(x[j].w))));
   amax = block_max(amax, red);
   const float s = qdq_scale(amax);
   const float r = 1.0f / s;
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void state_qdq_kernel(const float* in,
     int idx = threadIdx.x + kThreads * j;
     if (idx < n4) {
       qdq4(x[j], s, r);
-      dst[idx] = x[j];
+      st_stream(dst + idx, x[j]);
     }
   }
   if (scales != nullptr && threadIdx.x == 0) scales[tile] = s;
@@ -52,10 +53,10 @@ __global__ __launch_bounds__(kThreads) void state_qdq_kernel(const float* in,
 __global__ __launch_bounds__(kThreads) void state_qdq_int8_kernel(const float* in, float* out,
                                                                  float* __restrict__ scales, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // n4 is a multiple of 8 and of the block
-  float4 x = reinterpret_cast<const float4*>(in)[i];
+  float4 x = ld_stream(reinterpret_cast<const float4*>(in) + i);
   const float s = int8_scale(lane8_max_dpp(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)))));
   qdq_int8_4(x, s, 1.0f / s);
-  reinterpret_cast<float4*>(out)[i] = x;
+  st_stream(reinterpret_cast<float4*>(out) + i, x);
   if (scales != nullptr && (threadIdx.x & 7) == 0) scales[i >> 3] = s;
 }
 
