@@ -14,13 +14,14 @@
 // chunk only through U = T V, so Y is also the gradient of its values.
 //
 // chunk_bwd_prep_kernel: per (chunk, head) in parallel, T^T and P^T as full
-// 64 x 64 records (prep_item_bwd).  chunk_bwd_dh_kernel: one workgroup of
-// four waves per (sequence, head, 64-row value tile), the chunks in reverse
-// order; wave w owns dh rows 16w .. 16w + 15 of the tile (dk/16 fp32
+// 64 x 64 records (prep_item_bwd).  chunk_bwd_dh_kernel: one workgroup per
+// (sequence, head, 64-row value tile), the chunks in reverse order; compute
+// wave w (of four) owns dh rows 16w .. 16w + 15 of the tile (dk/16 fp32
 // accumulator tiles, the forward state's layout) and runs every product for
-// them.  The loads of chunk c - 1 (k and q dumps, dO rows, both records, by
-// direct global->LDS loads into the other of two buffers) are issued while
-// chunk c computes.  Rows past a chunk's end load its last valid row; the
+// them.  Two loader waves issue the loads of chunk c - 1 (k and q dumps, dO
+// rows, both records, by direct global->LDS loads into the other of two
+// buffers) while chunk c computes, and scan its gates, so that the compute
+// waves never wait for the load unit to take an instruction.  Rows past a chunk's end load its last valid row; the
 // P^T columns and the e^gamma entries of those rows are zero, so they reach
 // no result.  bf16 inputs; fp32 operands enter the bf16 MFMA as hi + lo
 // pairs.
@@ -28,7 +29,9 @@
 
 namespace gdn {
 
-constexpr int kBwdThreads = 256;
+// four compute waves own the dh rows; two loader waves issue every load
+constexpr int kBwdComputeWaves = 4, kBwdLoadWaves = 2;
+constexpr int kBwdThreads = 64 * (kBwdComputeWaves + kBwdLoadWaves);
 
 // LDS of the dh kernel (bytes), two buffers by chunk parity: the k and q
 // dumps of the chunk (the forward's rotated fragment layout, so K^T and Q^T
@@ -127,11 +130,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
 
   // ---- dh of this lane: dst[t][i] = dh[vcol0][dkmap(16t + 4gq + i)]
   f32x4 dst[NT];
+  const bool loader = w >= kBwdComputeWaves;
+  const int lw = w - kBwdComputeWaves;  // loader wave index
   {
     const int64_t base = ((int64_t)nh * dv + vcol0) * DK;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (args.dfin) {
+      if (args.dfin && !loader) {
         const float4 x = *reinterpret_cast<const float4*>(args.dfin + base + dkmap(16 * t + 4 * gq));
         dst[t] = f32x4{x.x, x.y, x.z, x.w};
       } else {
@@ -141,7 +146,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
   }
 
   // direct loads of chunk cc into buffer b: k and q dumps, dO rows (padded
-  // rows, 7 per instruction), the two records; wave 0 fetches the log-gates
+  // rows, 7 per instruction), the two records, spread over the loader waves;
+  // loader wave 0 fetches the log-gates
   float pg = 0.f;
   auto issue = [&](int cc, int b) {
     const int t0 = seg0 + cc * kChunk;
@@ -150,8 +156,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     const uint16_t* gk = args.k + (int64_t)t0 * qk_row + (int64_t)h * DK;
     const uint16_t* gqv = args.q + (int64_t)t0 * qk_row + (int64_t)h * DK;
 #pragma unroll
-    for (int ii = 0; ii < NKB; ++ii) {
-      const int i = w + 4 * ii;  // instruction: 64 lane slots of 16 bytes
+    for (int i = lw; i < 4 * NKB; i += kBwdLoadWaves) {  // instruction: 64 lane slots of 16 bytes
       const int u = i * 64 + lane;
       const int f = u >> 6, l2 = rot_lane(u & 63);
       const int r = 16 * (f / NKB) + (l2 & 15);
@@ -163,8 +168,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     const char* tt = args.TT + ((int64_t)(chunk0 + cc) * H + h) * kBRecBytes;
     const char* pt = args.PT + ((int64_t)(chunk0 + cc) * H + h) * kBRecBytes;
 #pragma unroll
-    for (int ii = 0; ii < kBRecBytes / 1024 / 4; ++ii) {
-      const int idx = w * (kBRecBytes / 1024 / 4) + ii;
+    for (int idx = lw; idx < (int)(kBRecBytes / 1024); idx += kBwdLoadWaves) {
       lds_load16(tt, (uint32_t)((idx * 64 + lane) * 16), base + (uint32_t)Ls::oTT + idx * 1024);
       lds_load16(pt, (uint32_t)((idx * 64 + lane) * 16), base + (uint32_t)Ls::oPT + idx * 1024);
     }
@@ -174,17 +178,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
       const int rr = lane / 9, pc = lane % 9;
       const int lane_off = min(pc, 7) * 8;
 #pragma unroll
-      for (int ii = 0; ii < (NI + 3) / 4; ++ii) {
-        const int i = w + 4 * ii;
+      for (int i = lw; i < NI; i += kBwdLoadWaves) {
         const int r = i * RPI + rr;
-        if (i < NI && rr < RPI && r < 64)
+        if (rr < RPI && r < 64)
           lds_load16(src, (uint32_t)((min(r, nv - 1) * (int)v_row + lane_off) * 2),
                      base + (uint32_t)Ls::oO + i * RPI * RS * 2);
       }
     }
-    if (w == 0) pg = (lane < nv) ? args.g[(int64_t)(t0 + lane) * H + h] : 0.f;
+    if (lw == 0) pg = (lane < nv) ? args.g[(int64_t)(t0 + lane) * H + h] : 0.f;
   };
-  // wave 0: the gates of chunk cc from pg (e^gamma is zero past the chunk's end)
+  // loader wave 0: the gates of chunk cc from pg (e^gamma is zero past the chunk's end)
   auto scan = [&](int cc, float* vec) {
     const int nv = min(kChunk, L - cc * kChunk);
     const float x = wave_prefix_sum(pg);
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     }
   };
 
-  if (n_chunks > 0) issue(n_chunks - 1, (n_chunks - 1) & 1);
+  if (loader && n_chunks > 0) issue(n_chunks - 1, (n_chunks - 1) & 1);
   for (int c = n_chunks - 1; c >= 0; --c) {
     const int b = c & 1;
     char* bufp = smem + b * Ls::buf;
@@ -238,10 +241,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     const uint16_t* sTT = reinterpret_cast<const uint16_t*>(bufp + Ls::oTT);
     const uint16_t* sPT = reinterpret_cast<const uint16_t*>(bufp + Ls::oPT);
     float* vec = reinterpret_cast<float*>(bufp + Ls::oVec);
-    if (w == 0) scan(c, vec);
+    if (lw == 0) scan(c, vec);
     wait_vmem();      // this wave's loads of chunk c are in LDS
     __syncthreads();  // ... every wave's, and the gates; chunk c + 1's buffer is free
-    if (c > 0) issue(c - 1, b ^ 1);
+    if (loader) {
+      if (c > 0) issue(c - 1, b ^ 1);
+      continue;
+    }
     if (c + 1 < n_chunks) store_results(c + 1);
 
     // ---- G = K dh^T (A = k rows, B = dh as hi + lo)
@@ -371,10 +377,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     }
     // dst now holds dh_c, the gradient of the state entering chunk c
   }
+  if (loader) return;
   if (n_chunks > 0) store_results(0);
   if (args.dvals) {  // padding rows of the segment
     const int seg_len = args.cu_seqlens[n + 1] - seg0;
-    for (int r = L + w; r < seg_len; r += kBwdThreads / 64)
+    for (int r = L + w; r < seg_len; r += kBwdComputeWaves)
       args.dvals[((int64_t)(seg0 + r) * H + h) * dv + kTileRows * vt + lane] = 0.f;
   }
   if (args.dinit) {
