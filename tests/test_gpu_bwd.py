@@ -103,3 +103,17 @@ def test_bwd_dh_many_workgroups_against_oracle():
         r1, r0 = rel_l2(dh[offs[n]:offs[n + 1], h], r_dh), rel_l2(d0[n, h], r_0)
         print(f"(n, h)=({n}, {h}): dh rel={r1:.3e} d_initial rel={r0:.3e}", flush=True)
         assert r1 <= TOL and r0 <= TOL
+
+
+def test_bwd_without_dh_output_same_results():
+    """dh NULL (no per-chunk state gradients stored): the initial state's
+    gradient and d_v are bit-identical to the call that stores dh."""
+    w, do, dS = _case([200, 64, 1], 2, 128, 128, seed=101)
+    dh, d0, dval = _run(w, do, dS, want_dv=True)
+    d = gi.device_tensors(w)
+    _, d0_b, dv_b = api.chunk_bwd_dh(d["q"], d["k"], d["beta"], d["g"], d["cu_seqlens"], gi.to_torch(do, "cuda"),
+                                     seq_lens=d["seq_lens"], d_final_state=torch.from_numpy(dS).cuda(),
+                                     dh=torch.empty(0, device="cuda"), want_dv=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d0_b.cpu().numpy(), d0)
+    np.testing.assert_array_equal(dv_b.cpu().numpy(), dval)
