@@ -12,14 +12,24 @@ object covers that launch, timed with HIP events recorded around it by the
 library; the split schedule (prep kernel, then the state kernel alone) is
 timed too and reported beside it.
 
+Timing: warmup steps, then exactly --steps steps between synchronizations
+(the headline value); per-launch HIP events give the mean (the roofline's
+average launch) and the median; a MALL-flushed median writes 512 MiB before
+each trial.  After every timed loop the workspace status word must be clean
+and the outputs finite.
+
 Also reported: the same prefill with W QDQ on top (each row of the
-WY-transformed W quantized to FP8 E4M3 before W S^T); the same prefill with a per-key-channel gate (KDA-style g
-[T, H, dk]) as tokens/s and its state kernel's time; the prefill->decode handoff workload (256 sequences, H=32,
-d=128: 2048-token chunked prefix with QDQ, then 512 single-token decode steps
-each writing the state through per-tile QDQ) as decode-step HBM GB/s (and the
-same steps with the INT8 block-32 codec), and the
-CPU oracle's throughput on the prefill workload (all 64 (sequence, head) pairs
-by default).
+WY-transformed W quantized to FP8 E4M3 before W S^T); the packed varlen
+workload at full size (16 sequences, lengths U{1..8192} plus padding); the
+backward state recurrence on the prefill shape; the same prefill with a
+per-key-channel gate (KDA-style g [T, H, dk]) as tokens/s and its launch's
+time; the prefill->decode handoff workload (256 sequences, H=32, d=128:
+2048-token chunked prefix with QDQ, then 512 single-token decode steps each
+writing the state through per-tile QDQ) as decode-step HBM GB/s (and the
+same steps with the INT8 block-32 codec), and the CPU oracle's throughput
+on the prefill workload (all 64 (sequence, head) pairs by default) on the
+cores this process may use (at most 16) and on one thread, with the host's
+CPU model.
 
 Prints one JSON line.
 """
@@ -101,6 +111,55 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+def med(xs):
+    return float(np.median(np.asarray(xs, np.float64)))
+
+
+def time_flushed(fn, events, trials, flush):
+    """MALL-flushed timing: before each trial a 512 MiB buffer is written
+    (more than the 256 MB MALL), so the call finds none of its inputs in the
+    last-level cache; returns the per-trial durations (ms) of the launch
+    bracketed by the (start, end) event pairs the call records."""
+    import torch
+    out = []
+    for i in range(trials):
+        flush.zero_()
+        torch.cuda.synchronize()
+        fn(events[i])
+        torch.cuda.synchronize()
+        out.append(events[i][0].elapsed_time(events[i][1]))
+    return out
+
+
+def check_outputs(api, ws, *tensors):
+    """After a timed loop: the workspace's status word is clean and every
+    output is finite (a run that went wrong must not yield a number)."""
+    import torch
+    if ws is not None:
+        api.workspace_status(ws)
+    for t in tensors:
+        if not bool(torch.isfinite(t).all()):
+            raise RuntimeError("non-finite output after the timed loop")
+
+
+def host_info():
+    """Cores this process may use, the machine's logical CPUs, and the CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "usable": usable, "model": model}
+
+
 def time_launches(fn, steps, warmup):
     """Warm up, then time exactly `steps` calls between synchronizations with
     HIP events on torch's current stream (the stream the library launches
@@ -139,6 +198,12 @@ def cpu_baseline(w, flags, n_pairs, threads, repeats):
                       f"{dt:.1f} s wall on {threads} threads"}
 
 
+def launch_stats(pairs):
+    """Mean and median (ms) of the durations between (start, end) event pairs."""
+    xs = [e0.elapsed_time(e1) for e0, e1 in pairs]
+    return float(np.mean(xs)), med(xs)
+
+
 def load_traffic(kernel_key, src_hash):
     """HBM traffic per launch from a committed rocprofv3 PMC summary, if the
     kernel source has not changed since the counters were taken."""
@@ -160,6 +225,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kda", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=64,
                     help="(sequence, head) pairs the oracle runs (64 = the whole workload)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
@@ -191,19 +257,35 @@ def main():
           for _ in range(args.steps + args.warmup)]
     it = {"i": 0}
 
+    ws = torch.empty(api.chunk_workspace_bytes(B, H, dk, dv, w.total_tokens, qdq_flags=flags),
+                     dtype=torch.uint8, device=dev)
+
     def step():
         e0, e1 = ev[it["i"]]
         it["i"] += 1
         api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=flags,
-                      out=o, final_state=fin, debug={"kernel_start": e0, "kernel_end": e1})
+                      out=o, final_state=fin, workspace=ws, debug={"kernel_start": e0, "kernel_end": e1})
 
     for e0, e1 in ev:  # create the HIP events outside the timed region
         e0.record()
         e1.record()
     torch.cuda.synchronize()
     total_ms, per = time_launches(step, args.steps, args.warmup)
+    check_outputs(api, ws, o, fin)
     ms_step = total_ms / args.steps
-    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev[args.warmup:]]))
+    kern_ms, kern_med = launch_stats(ev[args.warmup:])
+    # MALL-flushed: a 512 MiB write before each trial, the launch timed alone
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+
+    def step_f(e):
+        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=flags,
+                      out=o, final_state=fin, workspace=ws, debug={"kernel_start": e[0], "kernel_end": e[1]})
+
+    flushed = time_flushed(step_f, evf, args.steps, flush)
+    check_outputs(api, ws, o, fin)
+    del flush
     tokens = B * T
     token_heads = tokens * H
     n_chunk_heads = B * H * ((T + 63) // 64)
@@ -225,6 +307,9 @@ def main():
                 "algorithmic_flops_per_launch": fl_all,
                 "flops_per_token_head": flops_per_token_head(64, dk, dv),
                 "avg_launch_ms": round(kern_ms, 5),
+                "median_launch_ms": round(kern_med, 5),
+                "mall_flushed_median_launch_ms": round(med(flushed), 5),
+                "mall_flushed_frac": round(fl_all / (med(flushed) * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                 "hbm": {"achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
                         "algorithmic_bytes_per_launch": by}}
@@ -278,6 +363,7 @@ def main():
         e1.record()
     torch.cuda.synchronize()
     w_ms, _ = time_launches(step_w, args.steps, args.warmup)
+    check_outputs(api, None, o, fin)
     w_kern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evw[args.warmup:]]))
     w_tflops = fl_all / (w_kern * 1e-3) / 1e12
 
@@ -323,6 +409,7 @@ def main():
                          dh=dh_out, d_initial_state=d0_out, d_v=dv_out)
 
     bwd_ms, _ = time_launches(step_bwd, args.steps, args.warmup)
+    check_outputs(api, None, dh_out, d0_out, dv_out)
     bwd_ms /= args.steps
     bfl = bwd_flops_per_token_head(64, dk, dv) * token_heads
     bby = bwd_bytes(token_heads, n_chunk_heads, B * H, dk, dv, 2)
@@ -336,6 +423,55 @@ def main():
                      "hbm_gbs": round(bby / (bwd_ms * 1e-3) / 1e9, 1),
                      "algorithmic_flops_per_step": bfl, "algorithmic_bytes_per_step": bby}
     del d_o, dS_L, dh_out, d0_out, dv_out
+
+    # ---------------- packed varlen prefill at full size (reported) ----------------
+    if not args.no_varlen:
+        wv = gi.varlen()
+        dvl = gi.device_tensors(wv, dev)
+        Tv, Nv = wv.total_tokens, wv.n_seqs
+        ov = torch.empty((Tv, H, dv), dtype=torch.bfloat16, device=dev)
+        finv = torch.empty((Nv, H, dv, dk), dtype=torch.float32, device=dev)
+        wsv = torch.empty(api.chunk_workspace_bytes(Nv, H, dk, dv, Tv, qdq_flags=flags), dtype=torch.uint8,
+                          device=dev)
+        evv = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps + args.warmup)]
+        itv = {"i": 0}
+
+        def vstep():
+            e0, e1 = evv[itv["i"]]
+            itv["i"] += 1
+            api.chunk_fwd(dvl["q"], dvl["k"], dvl["v"], dvl["beta"], dvl["g"], dvl["cu_seqlens"],
+                          seq_lens=dvl["seq_lens"], qdq_flags=flags, out=ov, final_state=finv, workspace=wsv,
+                          debug={"kernel_start": e0, "kernel_end": e1})
+
+        for e0, e1 in evv:
+            e0.record()
+            e1.record()
+        torch.cuda.synchronize()
+        vtot, _ = time_launches(vstep, args.steps, args.warmup)
+        check_outputs(api, wsv, finv)
+        vkern, vkern_med = launch_stats(evv[args.warmup:])
+        valid = int(np.sum(wv.seq_lens))
+        vfl = flops_per_token_head(64, dk, dv) * valid * H
+        # q, k, v, beta, g of the valid rows read; every row of o written (padding rows as 0); final states
+        vby = prefill_bytes(valid * H, Nv * H, dk, dv, 2, 2) + (Tv - valid) * H * dv * 2
+        out["varlen"] = {"workload": f"packed varlen prefill: {Nv} sequences, lengths U{{1..8192}} "
+                                     f"(longest {int(np.max(wv.seq_lens))}, {valid} valid tokens) plus "
+                                     f"U{{0..63}} padding rows each ({Tv} rows), H=16, dk=dv=128, bf16, QDQ on",
+                         "ms_per_step": round(vtot / args.steps, 5),
+                         "tokens_per_s": round(valid / (vtot / args.steps * 1e-3), 1),
+                         "roofline": {"bound": "mfma", "avg_launch_ms": round(vkern, 5),
+                                      "median_launch_ms": round(vkern_med, 5),
+                                      "achieved": round(vfl / (vkern * 1e-3) / 1e12, 2),
+                                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": round(vfl / (vkern * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                      "algorithmic_flops_per_launch": vfl,
+                                      "hbm_gbs": round(vby / (vkern * 1e-3) / 1e9, 1),
+                                      "hbm_frac": round(vby / (vkern * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "algorithmic_bytes_per_launch": vby,
+                                      "critical_path_chunks": int(-(-int(np.max(wv.seq_lens)) // 64))}}
+        del dvl, ov, finv, wsv
+        torch.cuda.empty_cache()
 
     # ---------------- per-key-channel gate (KDA) prefill, same shape (reported) ----------------
     if not args.no_kda:
@@ -358,7 +494,8 @@ def main():
         torch.cuda.synchronize()
         ktot, _ = time_launches(kstep, args.steps, args.warmup)
         kms = ktot / args.steps
-        kkern = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evk[args.warmup:]]))
+        check_outputs(api, None, o, fin)
+        kkern, kkern_med = launch_stats(evk[args.warmup:])
         # the fused launch does every flop of the step and moves the prefill's bytes
         # (g is [T, H, dk]; the records stay inside the launch)
         kfl = flops_per_token_head(64, dk, dv) * token_heads
@@ -376,6 +513,7 @@ def main():
                       "fused_launch": {"kernel": "kda_fwd_kernel<128, EngBF16, bf16, bf16, fused> "
                                                  "(128 producer + 128 state workgroups)",
                                        "avg_launch_ms": round(kkern, 5),
+                                       "median_launch_ms": round(kkern_med, 5),
                                        "mfma_tflops": round(kfl / (kkern * 1e-3) / 1e12, 2),
                                        "mfma_frac": round(kfl / (kkern * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                                        "hbm_gbs": round(kby / (kkern * 1e-3) / 1e9, 1),
@@ -414,7 +552,9 @@ def main():
 
         dwarm = 8
         dtot, dper = time_launches(dstep, steps4 - dwarm, dwarm)
+        check_outputs(api, None, od, state)
         dms = float(np.mean(dper))
+        dmed = med(dper)
         dby = decode_bytes(N4 * H4, 128, 128, 2, 2)
         dsrc = source_hash([os.path.join(ROOT, "fp8_state_qat_amd", "csrc", f)
                             for f in ("gdn_decode.hip", "gdn_device.hpp")])
@@ -425,6 +565,7 @@ def main():
                          "prefill_tokens_per_s": round(N4 * P4 / (pre_ms * 1e-3), 1),
                          "decode_steps_timed": steps4 - dwarm,
                          "ms_per_step": round(dms, 5),
+                         "median_ms_per_step": round(dmed, 5),
                          "tokens_per_s": round(N4 / (dms * 1e-3), 1),
                          "roofline": {"bound": "hbm", "achieved": round(dby / (dms * 1e-3) / 1e9, 1),
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -441,9 +582,11 @@ def main():
             it["i"] += 1
 
         _, dper8 = time_launches(dstep8, steps4 - dwarm, dwarm)
+        check_outputs(api, None, od, state)
         dms8 = float(np.mean(dper8))
         out["decode_int8"] = {"codec": "INT8, one scale per 32 key columns of a state row",
                               "ms_per_step": round(dms8, 5),
+                              "median_ms_per_step": round(med(dper8), 5),
                               "tokens_per_s": round(N4 / (dms8 * 1e-3), 1),
                               "hbm_gbs": round(dby / (dms8 * 1e-3) / 1e9, 1),
                               "hbm_frac": round(dby / (dms8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -475,8 +618,14 @@ def main():
         out["copy_calibration_bytes"] = n * 4
 
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        out["cpu_baseline"] = cpu_baseline(w, flags, args.cpu_pairs, threads, args.cpu_repeats)
+        # all the cores this process may use (the GPU's share of the host, at most 16), and one
+        hi = host_info()
+        threads = max(1, min(16, hi["usable"]))
+        cb = cpu_baseline(w, flags, args.cpu_pairs, threads, args.cpu_repeats)
+        one = cpu_baseline(w, flags, max(1, args.cpu_pairs // 16), 1, 1)
+        cb["one_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+        cb["host"] = hi
+        out["cpu_baseline"] = cb
 
     print(json.dumps(out), flush=True)
 

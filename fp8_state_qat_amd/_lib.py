@@ -28,9 +28,9 @@ GDN_SCHEDULE_SPLIT = 1
 GDN_SCHEDULE_FUSED = 2
 GDN_SCHEDULE_FUSED_NO_PRODUCERS = 3   # test hook: every wait for a ready flag runs out
 
-EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_state_qdq", "gdn_state_qdq_int8",
-           "gdn_decode_step", "gdn_chunk_bwd_dh", "gdn_chunk_bwd_workspace_bytes", "gdn_status_string",
-           "gdn_last_error")
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_workspace_status", "gdn_state_qdq",
+           "gdn_state_qdq_int8", "gdn_decode_step", "gdn_chunk_bwd_dh", "gdn_chunk_bwd_workspace_bytes",
+           "gdn_status_string", "gdn_last_error")
 
 
 class GdnShape(ctypes.Structure):
@@ -58,6 +58,10 @@ class GdnDebug(ctypes.Structure):
         ("schedule", ctypes.c_int32),
         ("w_pre", ctypes.c_void_p),
         ("w_post", ctypes.c_void_p),
+        ("suffix_offsets", ctypes.c_void_p),
+        ("suffix_pre", ctypes.c_void_p),
+        ("suffix_post", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
     ]
 
 
@@ -94,8 +98,10 @@ def lib():
     L.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_state_qdq_int8.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
     L.gdn_state_qdq_int8.restype = ctypes.c_int
-    L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+    L.gdn_decode_step.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp]
+    L.gdn_workspace_status.argtypes = [_vp, _vp]
+    L.gdn_workspace_status.restype = ctypes.c_int
     L.gdn_decode_step.restype = ctypes.c_int
     L.gdn_status_string.argtypes = [ctypes.c_int]
     L.gdn_status_string.restype = ctypes.c_char_p

@@ -127,8 +127,8 @@ gdn_status_t gdn_state_qdq_int8(const float* in, float* out, float* scales, int6
 }
 
 gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void* k,
-                             const void* v, const float* beta, const float* g, float* state,
-                             void* o, float* state_pre, float* scales, void* stream) {
+                             const void* v, const float* beta, const float* g, const int32_t* active,
+                             float* state, void* o, float* state_pre, float* scales, void* stream) {
   g_err[0] = 0;
   gdn_status_t st = check_shape(shape, true);
   if (st != GDN_OK) return st;
@@ -137,13 +137,32 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape, const void* q, const void
   const uintptr_t ea = shape->io_dtype == GDN_BF16 ? 8 : 16;
   if (!aligned(q, ea) || !aligned(k, ea) || !aligned(v, 4) || !aligned(state, 16) ||
       (state_pre && !aligned(state_pre, 16)) || !aligned(beta, 4) || !aligned(g, 4) ||
-      !aligned(o, shape->o_dtype == GDN_BF16 ? 2 : 4))
+      !aligned(active, 4) || !aligned(o, shape->o_dtype == GDN_BF16 ? 2 : 4))
     return fail(GDN_ERR_INVALID_ARG, "misaligned buffer");
   st = check_device();
   if (st != GDN_OK) return st;
-  hipError_t e = gdn::launch_decode_step(*shape, q, k, v, beta, g, state, o, state_pre, scales,
+  hipError_t e = gdn::launch_decode_step(*shape, q, k, v, beta, g, active, state, o, state_pre, scales,
                                          (hipStream_t)stream);
   if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return GDN_OK;
+}
+
+gdn_status_t gdn_workspace_status(const void* workspace, void* stream) {
+  g_err[0] = 0;
+  if (workspace == nullptr) return fail(GDN_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  gdn_status_t st = check_device();
+  if (st != GDN_OK) return st;
+  int32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "reading the status word failed: %s", hipGetErrorString(e));
+  if (word & gdn::kStatusBadIndex)
+    return fail(GDN_ERR_INVALID_ARG, "the device found the index arrays (cu_seqlens, seq_lens, prefix_lens) "
+                                     "out of contract; nothing was computed");
+  if (word & gdn::kStatusWaitTimeout)
+    return fail(GDN_ERR_DEVICE, "a bounded wait for a per-chunk record ran out; the affected outputs are NaN");
+  if (word != 0) return fail(GDN_ERR_DEVICE, "unknown status word 0x%x", (unsigned)word);
   return GDN_OK;
 }
 
@@ -179,6 +198,12 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
   if (debug && (debug->bound_pre || debug->bound_post || debug->scales || debug->w_pre || debug->w_post) &&
       !debug->bound_offsets)
     return fail(GDN_ERR_INVALID_ARG, "debug record needs bound_offsets");
+  if (debug && (debug->suffix_pre || debug->suffix_post) && !debug->suffix_offsets)
+    return fail(GDN_ERR_INVALID_ARG, "suffix record needs suffix_offsets");
+  if (debug && (!aligned(debug->bound_pre, 16) || !aligned(debug->bound_post, 16) ||
+                !aligned(debug->suffix_pre, 16) || !aligned(debug->suffix_post, 16) ||
+                !aligned(debug->status, 4)))
+    return fail(GDN_ERR_INVALID_ARG, "misaligned debug record (states need 16 bytes)");
   if (debug && (debug->schedule < GDN_SCHEDULE_AUTO || debug->schedule > GDN_SCHEDULE_FUSED_NO_PRODUCERS))
     return fail(GDN_ERR_INVALID_ARG, "debug schedule must be GDN_SCHEDULE_AUTO, _SPLIT, _FUSED or _FUSED_NO_PRODUCERS");
   if (shape->io_dtype == GDN_F32 && shape->dk != 64)
@@ -207,6 +232,10 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape, const void* q, const voi
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
   if (shape->io_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh takes bf16 q, k and d_o");
+  if (shape->qdq_flags & GDN_QDQ_W)
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh: the backward of a GDN_QDQ_W forward is not built");
+  if (shape->qdq_flags & GDN_QDQ_INT8)
+    return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_INT8 is a decode-step codec");
   if (shape->gate_per_channel) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh supports the scalar gate only");
   const size_t need = gdn::bwd_workspace_bytes(*shape);
   if (workspace == nullptr || workspace_bytes < need)

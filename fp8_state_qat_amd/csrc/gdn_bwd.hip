@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_bwd_prep_kernel(PrepArgs a)
   extern __shared__ __align__(16) char lds[];
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
+  if (index_check_failed(a.status)) return;
   const int total = a.offs[a.N];
   if (j >= total) return;  // grid is sized for the worst case
   int lo = 0, hi = a.N - 1;
@@ -86,6 +87,7 @@ struct BwdArgs {
   float* dh;              // [n_bounds, H, dv, dk] or null
   float* dinit;           // [N, H, dv, dk] or null
   float* dvals;           // [T, H, dv] or null
+  const int32_t* status;  // the workspace's status word (index check)
   int H;
   int dv;
 };
@@ -97,6 +99,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
   constexpr int NT = DK / 16, NKB = DK / 32;
   constexpr int RS = (int)Ls::RS;
   extern __shared__ __align__(16) char smem[];
+  if (index_check_failed(args.status)) return;
   const uint32_t lds0 = lds_base_u32(smem);
 
   const int tid = threadIdx.x;
@@ -397,7 +400,7 @@ size_t bwd_workspace_bytes(const gdn_shape_t& s) {
   const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
   const size_t items = (size_t)(max_chunks * s.n_heads);
   const size_t offs_bytes = ((size_t)(s.n_seqs + 2) * 4 + 255) / 256 * 256;
-  return offs_bytes + items * kBRecBytes * 2;
+  return kStatusBytes + offs_bytes + items * kBRecBytes * 2;
 }
 
 template <int DK>
@@ -437,11 +440,13 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
   const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
   const int64_t items = max_chunks * s.n_heads;
   const size_t offs_bytes = ((size_t)(s.n_seqs + 2) * 4 + 255) / 256 * 256;
-  int32_t* offs = reinterpret_cast<int32_t*>(w);
-  char* TT = w + offs_bytes;
+  int32_t* status = reinterpret_cast<int32_t*>(w);
+  int32_t* offs = reinterpret_cast<int32_t*>(w + kStatusBytes);
+  char* TT = w + kStatusBytes + offs_bytes;
   char* PT = TT + (size_t)items * kBRecBytes;
-  // chunk offsets of the whole sequences (prefix = length)
+  // chunk offsets of the whole sequences (prefix = length), status word
   PrepLayout L{};
+  L.status = status;
   L.offs = offs;
   L.ready = nullptr;
   L.items = items;
@@ -450,6 +455,7 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
   PrepArgs pa{};
   pa.q = q; pa.k = k; pa.beta = beta; pa.g = g; pa.cu_seqlens = cu_seqlens; pa.seq_lens = seq_lens;
   pa.prefix_lens = nullptr; pa.offs = offs; pa.T = TT; pa.P = PT; pa.N = s.n_seqs; pa.H = s.n_heads;
+  pa.status = status;
   BwdArgs ba{};
   ba.q = reinterpret_cast<const uint16_t*>(q);
   ba.k = reinterpret_cast<const uint16_t*>(k);
@@ -464,6 +470,7 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
   ba.dh = dh;
   ba.dinit = dinit;
   ba.dvals = dvals;
+  ba.status = status;
   ba.H = s.n_heads;
   ba.dv = s.dv;
   return s.dk == 128 ? launch_bwd_dk<128>(s, pa, ba, items, stream) : launch_bwd_dk<64>(s, pa, ba, items, stream);

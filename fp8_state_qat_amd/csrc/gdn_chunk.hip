@@ -130,6 +130,7 @@ __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* sme
   a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
   a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
   a.W = const_cast<void*>(args.Wrec); a.w_pre = args.w_pre; a.w_post = args.w_post;
+  a.status = args.status;
   const int H = args.H, NH = args.N * args.H;
   const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
   const unsigned xcd = xcd_id();
@@ -183,6 +184,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   constexpr int NP = Eng::kPlanes;
   constexpr bool kSplit = Eng::kSplit;
   extern __shared__ __align__(16) char smem[];
+  if (index_check_failed(args.status)) return;
   if constexpr (kFused) {
     if ((int)blockIdx.x < args.n_prep) {
       produce_records<DK, TIO, kW>(args, smem);
@@ -408,7 +410,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   // one on another XCD must have released them device-wide, and then this
   // wave invalidates its caches (device-scope acquire).  A wait that runs
   // out, or a record that cannot be trusted, sets the decay multiplier
-  // misc[2] to NaN, so the state and every later output show it.
+  // misc[2] to NaN, so the state and every later output show it, and sets
+  // kStatusWaitTimeout in the workspace's status word.
   unsigned pend = 0u;     // helper wave 1: a ready flag read ahead (used after a wait_vmem)
   bool poisoned = false;
   auto ready_ptr = [&](int cc) { return args.ready + ((int64_t)(chunk0 + cc) * H + h); };
@@ -417,7 +420,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   const unsigned xcd_self = kFused ? xcd_id() : 0u;
   auto poison = [&](float* vecb) {
     poisoned = true;
-    if (lane == 0) vecb[194] = __builtin_nanf("");
+    if (lane == 0) {
+      vecb[194] = __builtin_nanf("");
+      report_wait_timeout(args.status);
+    }
   };
   auto await_ready = [&](int cc, unsigned v0, float* vecb) {
     if (!poisoned && !await_ready_flag(ready_ptr(cc), v0, xcd_self)) poison(vecb);
@@ -847,6 +853,18 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   }
 
   // ---------------- recurrent suffix, tokens P < t <= L ----------------
+  // optional per-token record: the chain wave's rows of the state after each
+  // suffix token, before (sfx_pre) and after (sfx_post) its QDQ
+  float* const sfx_pre = args.sfx_offsets ? args.sfx_pre : nullptr;
+  float* const sfx_post = args.sfx_offsets ? args.sfx_post : nullptr;
+  const int64_t sfx0 = args.sfx_offsets ? args.sfx_offsets[n] : 0;
+  const int64_t sfx_stride = (int64_t)H * dv * DK;
+  auto store_state = [&](float* base) {  // base: record entry of one token
+#pragma unroll
+    for (int t2 = 0; t2 < NT; ++t2)
+      *reinterpret_cast<float4*>(base + ((int64_t)h * dv + vcol0) * DK + dkmap(16 * t2 + 4 * gq)) =
+          make_float4(st[t2][0], st[t2][1], st[t2][2], st[t2][3]);
+  };
   if (P < L) {
     float* sq = reinterpret_cast<float*>(smem + Ls::oK);  // q_t, k_t: DK each; v_t: 64; g_t, beta_t
     float* sk = sq + DK;
@@ -892,6 +910,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
         if (gq == 0) io<TO>::st(go_ + row * v_row + (int64_t)h * dv + vcol0, z);
+        if (sfx_pre) store_state(sfx_pre + (sfx0 + t - P) * sfx_stride);
         if (flags & GDN_QDQ_WRITE) {
           float amax = 0.f;
 #pragma unroll
@@ -909,6 +928,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int t2 = 0; t2 < NT; ++t2) qdq4(st[t2], s, r);
       }
+      if (chain && sfx_post) store_state(sfx_post + (sfx0 + t - P) * sfx_stride);
     }
   }
 
@@ -1007,6 +1027,10 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   a.bound_scales = debug ? debug->scales : nullptr;
   a.H = s.n_heads; a.dv = s.dv; a.flags = s.qdq_flags;
   a.N = s.n_seqs; a.ready = L.ready; a.n_prep = n_prep; a.fused = fused ? 1 : 0;
+  a.status = L.status;
+  a.sfx_offsets = debug ? debug->suffix_offsets : nullptr;
+  a.sfx_pre = debug ? debug->suffix_pre : nullptr;
+  a.sfx_post = debug ? debug->suffix_post : nullptr;
   const bool ob = s.o_dtype == GDN_BF16;
   if (debug && debug->kernel_start) {
     e = hipEventRecord((hipEvent_t)debug->kernel_start, stream);
@@ -1029,6 +1053,7 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   }
   if (e == hipSuccess && debug && debug->kernel_end)
     e = hipEventRecord((hipEvent_t)debug->kernel_end, stream);
+  if (e == hipSuccess && debug && debug->status) e = launch_copy_status(L.status, debug->status, stream);
   return e;
 }
 

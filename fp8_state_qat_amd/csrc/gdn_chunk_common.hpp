@@ -242,6 +242,10 @@ struct ChunkArgs {
   int fused;           // the fused instantiation runs (its waits on the ready flags included)
   unsigned* ready;     // fused launch: one ready flag per (chunk, head), cleared before the launch
   int n_prep;          // fused launch: workgroups 0 .. n_prep - 1 produce the T and P records
+  int32_t* status;     // the workspace's status word (index check, failed waits)
+  const int32_t* sfx_offsets;  // optional per-token record of the recurrent suffix:
+  float* sfx_pre;              // state after each suffix token before its QDQ
+  float* sfx_post;             // and after it ([sfx_offsets[n] + t - P_n, H, dv, dk])
 };
 
 // XCD (accelerator complex die) that runs the calling wave: hardware
@@ -283,6 +287,19 @@ __device__ __forceinline__ bool await_ready_flag(const unsigned* flag, unsigned 
     wait_vmem();
   }
   return true;
+}
+
+// True when the index check of this call failed (the status word that
+// chunk_offsets_kernel wrote earlier on the stream); the caller then returns
+// without touching memory.
+__device__ __forceinline__ bool index_check_failed(const int32_t* status) {
+  return status != nullptr && (__builtin_amdgcn_readfirstlane(*status) & kStatusBadIndex) != 0;
+}
+
+// A consumer's bounded wait ran out: record it in the status word (vector
+// atomic; several workgroups may report).
+__device__ __forceinline__ void report_wait_timeout(int32_t* status) {
+  if (status != nullptr) __hip_atomic_fetch_or(status, kStatusWaitTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The sequential kernel for a per-key-channel gate (gdn_kda.hip); the prep

@@ -9,6 +9,11 @@
 //     o  = z + (k . q) u               (= S' q with S' = S~ + u k^T)
 //     S' = S~ + u k^T ;  S <- QDQ(S')  (one scale for the tile)
 //
+// A nullable active mask [N] skips whole sequences: their state, o and
+// records are left as they are (a batch whose sequences end at different
+// lengths, #2519 "What does this PR do?": prefill and full sequence lengths
+// per sequence).
+//
 // Memory bound: the tile is read once and written once (2 * 4 * 64 * dk
 // bytes); q, k, v, beta, g and o are a few hundred bytes per head.  One
 // workgroup (256 threads) per tile.  Thread t owns the float4 column group
@@ -31,9 +36,9 @@ namespace gdn {
 template <int DK, typename TIO, typename TO, bool PC, bool kInt8>
 __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
-    const float* __restrict__ beta, const float* __restrict__ g, float* __restrict__ state,
-    TO* __restrict__ o, float* __restrict__ state_pre, float* __restrict__ scales, int dv,
-    int do_qdq) {
+    const float* __restrict__ beta, const float* __restrict__ g, const int32_t* __restrict__ active,
+    float* __restrict__ state, TO* __restrict__ o, float* __restrict__ state_pre,
+    float* __restrict__ scales, int H, int dv, int do_qdq) {
   constexpr int F = DK / 4;         // float4 per state row
   constexpr int RPP = kThreads / F; // rows covered by one pass of the block
   constexpr int NP = kTileRows / RPP;
@@ -43,6 +48,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   const int tiles = dv / kTileRows;
   const int vt = blockIdx.x % tiles;
   const int64_t nh = blockIdx.x / tiles;  // n * H + h
+  // an inactive sequence (finished, or padding of a batch): nothing is read or written
+  if (active != nullptr && __builtin_amdgcn_readfirstlane(active[nh / H]) == 0) return;
   const int t = threadIdx.x;
   const int c4 = t % F;
   const int rr = t / F;
@@ -126,14 +133,14 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 
 template <int DK, typename TIO, typename TO>
 static void launch_dk_io_o(const gdn_shape_t& s, const void* q, const void* k, const void* v,
-                           const float* beta, const float* g, float* state, void* o,
-                           float* state_pre, float* scales, hipStream_t stream) {
+                           const float* beta, const float* g, const int32_t* active, float* state,
+                           void* o, float* state_pre, float* scales, hipStream_t stream) {
   const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
   const int qdq = (s.qdq_flags & GDN_QDQ_WRITE) ? 1 : 0;
   const bool i8 = (s.qdq_flags & GDN_QDQ_INT8) != 0;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, (const TIO*)q, (const TIO*)k,
-                       (const TIO*)v, beta, g, state, (TO*)o, state_pre, scales, s.dv, qdq);
+                       (const TIO*)v, beta, g, active, state, (TO*)o, state_pre, scales, s.n_heads, s.dv, qdq);
   };
   if (s.gate_per_channel) {
     if (i8) go(decode_step_kernel<DK, TIO, TO, true, true>);
@@ -146,26 +153,26 @@ static void launch_dk_io_o(const gdn_shape_t& s, const void* q, const void* k, c
 
 template <int DK>
 static void launch_dk(const gdn_shape_t& s, const void* q, const void* k, const void* v,
-                      const float* beta, const float* g, float* state, void* o, float* state_pre,
-                      float* scales, hipStream_t stream) {
+                      const float* beta, const float* g, const int32_t* active, float* state, void* o,
+                      float* state_pre, float* scales, hipStream_t stream) {
   const bool ib = s.io_dtype == GDN_BF16, ob = s.o_dtype == GDN_BF16;
   if (ib && ob)
-    launch_dk_io_o<DK, uint16_t, uint16_t>(s, q, k, v, beta, g, state, o, state_pre, scales, stream);
+    launch_dk_io_o<DK, uint16_t, uint16_t>(s, q, k, v, beta, g, active, state, o, state_pre, scales, stream);
   else if (ib)
-    launch_dk_io_o<DK, uint16_t, float>(s, q, k, v, beta, g, state, o, state_pre, scales, stream);
+    launch_dk_io_o<DK, uint16_t, float>(s, q, k, v, beta, g, active, state, o, state_pre, scales, stream);
   else if (ob)
-    launch_dk_io_o<DK, float, uint16_t>(s, q, k, v, beta, g, state, o, state_pre, scales, stream);
+    launch_dk_io_o<DK, float, uint16_t>(s, q, k, v, beta, g, active, state, o, state_pre, scales, stream);
   else
-    launch_dk_io_o<DK, float, float>(s, q, k, v, beta, g, state, o, state_pre, scales, stream);
+    launch_dk_io_o<DK, float, float>(s, q, k, v, beta, g, active, state, o, state_pre, scales, stream);
 }
 
 hipError_t launch_decode_step(const gdn_shape_t& s, const void* q, const void* k, const void* v,
-                              const float* beta, const float* g, float* state, void* o,
-                              float* state_pre, float* scales, hipStream_t stream) {
+                              const float* beta, const float* g, const int32_t* active, float* state,
+                              void* o, float* state_pre, float* scales, hipStream_t stream) {
   if (s.dk == 64)
-    launch_dk<64>(s, q, k, v, beta, g, state, o, state_pre, scales, stream);
+    launch_dk<64>(s, q, k, v, beta, g, active, state, o, state_pre, scales, stream);
   else
-    launch_dk<128>(s, q, k, v, beta, g, state, o, state_pre, scales, stream);
+    launch_dk<128>(s, q, k, v, beta, g, active, state, o, state_pre, scales, stream);
   return hipGetLastError();
 }
 

@@ -103,6 +103,7 @@ __device__ __forceinline__ void produce_kda_records(const ChunkArgs& args, char*
   a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
   a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
   a.W = const_cast<void*>(args.Wrec); a.w_pre = args.w_pre; a.w_post = args.w_post;
+  a.status = args.status;
   const int tid = threadIdx.x;
   const int H = args.H, NH = args.N * args.H;
   const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
@@ -146,6 +147,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   constexpr bool kSplit = Eng::kSplit;
   constexpr int PLANE = 4 * NKB * 64 * 8;  // elements of one operand plane
   extern __shared__ __align__(16) char smem[];
+  if (index_check_failed(args.status)) return;
   if constexpr (kFused) {
     if ((int)blockIdx.x < args.n_prep) {
       produce_kda_records<DK, TIO, kW>(args, smem);
@@ -635,7 +637,10 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   auto await_ready = [&](int cc, unsigned v0) {
     if (!poisoned && !await_ready_flag(ready_ptr(cc), v0, xcd_self)) {
       poisoned = true;
-      if (lane == 0) sRed[4] = __builtin_nanf("");
+      if (lane == 0) {
+        sRed[4] = __builtin_nanf("");
+        report_wait_timeout(args.status);
+      }
     }
   };
 
@@ -687,6 +692,18 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   }
 
   // ---------------- recurrent suffix, tokens P < t <= L ----------------
+  // optional per-token record: this wave's rows of the state after each
+  // suffix token, before (sfx_pre) and after (sfx_post) its QDQ
+  float* const sfx_pre = args.sfx_offsets ? args.sfx_pre : nullptr;
+  float* const sfx_post = args.sfx_offsets ? args.sfx_post : nullptr;
+  const int64_t sfx0 = args.sfx_offsets ? args.sfx_offsets[n] : 0;
+  const int64_t sfx_stride = (int64_t)H * dv * DK;
+  auto store_state = [&](float* base) {  // base: record entry of one token
+#pragma unroll
+    for (int t2 = 0; t2 < NT; ++t2)
+      *reinterpret_cast<float4*>(base + ((int64_t)h * dv + vcol0) * DK + dkmap(16 * t2 + 4 * gq)) =
+          make_float4(st[t2][0], st[t2][1], st[t2][2], st[t2][3]);
+  };
   if (P < L) {
     float* sq = reinterpret_cast<float*>(smem + Ls::oKa);  // q_t, k_t, g_t: DK each; v_t: 64; beta_t
     float* sk = sq + DK;
@@ -729,6 +746,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
       z += __shfl_xor(z, 16, 64);
       z += __shfl_xor(z, 32, 64);
       if (gq == 0) io<TO>::st(go_ + row * v_row + (int64_t)h * dv + vcol0, z);
+      if (sfx_pre) store_state(sfx_pre + (sfx0 + t - P) * sfx_stride);
       if (flags & GDN_QDQ_WRITE) {
         float amax = 0.f;
 #pragma unroll
@@ -743,6 +761,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
 #pragma unroll
         for (int t2 = 0; t2 < NT; ++t2) qdq4(st[t2], s, r);
       }
+      if (sfx_post) store_state(sfx_post + (sfx0 + t - P) * sfx_stride);
     }
   }
 

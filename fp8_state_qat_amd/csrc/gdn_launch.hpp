@@ -17,8 +17,14 @@ hipError_t launch_state_qdq_int8(const float* in, float* out, float* scales, int
                                  hipStream_t stream);
 
 hipError_t launch_decode_step(const gdn_shape_t& s, const void* q, const void* k, const void* v,
-                              const float* beta, const float* g, float* state, void* o,
-                              float* state_pre, float* scales, hipStream_t stream);
+                              const float* beta, const float* g, const int32_t* active, float* state,
+                              void* o, float* state_pre, float* scales, hipStream_t stream);
+
+// Status word at byte 0 of a chunk workspace (forward and backward): 0 after
+// a clean call; the bits below are set by the device during the call.
+constexpr int32_t kStatusWaitTimeout = 1;  // a fused consumer's bounded wait ran out
+constexpr int32_t kStatusBadIndex = 2;     // index arrays out of contract: nothing ran
+constexpr size_t kStatusBytes = 256;       // the status block ahead of the chunk offsets
 
 hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, const void* v,
                             const float* beta, const float* g, const int32_t* cu_seqlens,
@@ -39,12 +45,14 @@ constexpr int kTRecBytes = 12288;
 // row scales.
 constexpr int w_rec_bytes(int dk) { return dk * 128 + 1024; }
 
-// The chunk workspace: int32 chunk offsets [N + 1] and the largest chunk
-// count of a sequence (padded to 256 bytes), one uint32 ready flag per
+// The chunk workspace: the status word (padded to 256 bytes), int32 chunk
+// offsets [N + 1] and the largest chunk count of a sequence (padded to 256
+// bytes), one uint32 ready flag per
 // (chunk, head) (padded to 256 bytes; used by the fused launch), then the T
 // records, the P records and, with W QDQ, the W records, all sized for the
 // worst-case chunk count ceil(total_tokens / 64) + N.
 struct PrepLayout {
+  int32_t* status;
   int32_t* offs;
   unsigned* ready;
   void* T;
@@ -56,17 +64,22 @@ struct PrepLayout {
 PrepLayout prep_layout(const gdn_shape_t& s, void* workspace);
 size_t prep_workspace_bytes(const gdn_shape_t& s);
 
-// Chunk offsets, then (records true) the T and P (and W) records of every
-// (chunk, head); with records false the ready flags are cleared instead, for
-// a fused launch that produces the records itself.  w_pre / w_post: the
+// Chunk offsets (and the status word: cleared, then the index arrays are
+// checked against total_tokens), then (records true) the T and P (and W)
+// records of every (chunk, head); with records false the ready flags are
+// cleared instead, for a fused launch that produces the records itself.  w_pre / w_post: the
 // optional W record of the debug struct (null when absent).
 hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                        const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,
                        const int32_t* prefix_lens, const PrepLayout& L, bool records, float* w_pre,
                        float* w_post, hipStream_t stream);
 
-// Backward state recurrence (gdn_bwd.hip): workspace = chunk offsets, then
-// one T^T and one P^T record (16 KiB each) per (chunk, head).
+// Copy the status word of a workspace to a caller's device int32 (one thread).
+hipError_t launch_copy_status(const int32_t* status, int32_t* dst, hipStream_t stream);
+
+// Backward state recurrence (gdn_bwd.hip): workspace = the status word,
+// chunk offsets, then one T^T and one P^T record (16 KiB each) per (chunk,
+// head).
 size_t bwd_workspace_bytes(const gdn_shape_t& s);
 hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* k, const float* beta,
                                const float* g, const int32_t* cu_seqlens, const int32_t* seq_lens,

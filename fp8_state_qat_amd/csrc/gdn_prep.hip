@@ -11,9 +11,9 @@
 // blocks level by level, X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj, on the fp32
 // MFMA.
 //
-// Workspace layout: int32 chunk offsets [N + 1] (prefix sums of
-// ceil(P_n / 64)) and the largest chunk count of a sequence, padded to 256
-// bytes; one uint32 ready flag per (chunk, head) (used by the fused launch of
+// Workspace layout: the int32 status word, padded to 256 bytes; int32 chunk
+// offsets [N + 1] (prefix sums of ceil(P_n / 64)) and the largest chunk count
+// of a sequence, padded to 256 bytes; one uint32 ready flag per (chunk, head) (used by the fused launch of
 // the scalar-gate kernel), padded to 256 bytes; then one 12 KiB T record per
 // (chunk, head), then one P record per (chunk, head) of the same layout, then
 // with W QDQ one W record per (chunk, head) (layout in gdn_launch.hpp).  A
@@ -35,12 +35,19 @@ namespace gdn {
 // ---------------------------------------------------------------------------
 // chunk offsets: offs[n] = sum_{m < n} ceil(P_m / 64), offs[N + 1] = the
 // largest ceil(P_n / 64), in workgroup 0; every workgroup clears its share of
-// the n_ready ready flags (none when ready is null).
+// the n_ready ready flags (none when ready is null).  Workgroup 0 also checks
+// the index arrays against their contract (0 <= cu[n] <= cu[n + 1] <=
+// total_tokens, 0 <= L_n <= cu[n + 1] - cu[n], 0 <= P_n <= L_n) and writes
+// the status word: kStatusBadIndex when any of them is violated, else 0.
+// The kernels that follow on the stream read it first and do nothing on a
+// violation, so out-of-contract indices never become out-of-bounds accesses.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void chunk_offsets_kernel(const int32_t* __restrict__ cu,
                                                                  const int32_t* __restrict__ seq_lens,
                                                                  const int32_t* __restrict__ prefix_lens,
-                                                                 int N, int32_t* __restrict__ offs,
+                                                                 int N, int64_t total_tokens,
+                                                                 int32_t* __restrict__ offs,
+                                                                 int32_t* __restrict__ status,
                                                                  unsigned* __restrict__ ready, int64_t n_ready) {
   if (ready != nullptr) {
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_ready; i += (int64_t)gridDim.x * kThreads)
@@ -48,20 +55,23 @@ __global__ __launch_bounds__(kThreads) void chunk_offsets_kernel(const int32_t* 
   }
   if (blockIdx.x != 0) return;
   __shared__ int32_t part[kThreads];
-  __shared__ int32_t carry, most;
+  __shared__ int32_t carry, most, bad;
   if (threadIdx.x == 0) {
     carry = 0;
     most = 0;
+    bad = (cu[0] < 0) ? 1 : 0;
   }
   __syncthreads();
-  int32_t my_most = 0;
+  int32_t my_most = 0, my_bad = 0;
   for (int base = 0; base < N; base += kThreads) {
     const int n = base + threadIdx.x;
     int32_t cnt = 0;
     if (n < N) {
-      const int32_t L = seq_lens ? seq_lens[n] : (cu[n + 1] - cu[n]);
+      const int32_t c0 = cu[n], c1 = cu[n + 1];
+      const int32_t L = seq_lens ? seq_lens[n] : (c1 - c0);
       const int32_t P = prefix_lens ? prefix_lens[n] : L;
-      cnt = (P + kChunk - 1) / kChunk;
+      if (c1 < c0 || (int64_t)c1 > total_tokens || L < 0 || L > c1 - c0 || P < 0 || P > L) my_bad = 1;
+      cnt = my_bad ? 0 : (P + kChunk - 1) / kChunk;
     }
     my_most = max(my_most, cnt);
     part[threadIdx.x] = cnt;
@@ -79,10 +89,12 @@ __global__ __launch_bounds__(kThreads) void chunk_offsets_kernel(const int32_t* 
     __syncthreads();
   }
   atomicMax(&most, my_most);
+  if (my_bad) atomicOr(&bad, 1);
   __syncthreads();
   if (threadIdx.x == 0) {
     offs[N] = carry;
     offs[N + 1] = most;
+    if (status != nullptr) status[0] = bad ? kStatusBadIndex : 0;
   }
 }
 
@@ -93,6 +105,7 @@ __global__ __launch_bounds__(kThreads, kW ? 2 : 3) void chunk_prep_kernel(PrepAr
   extern __shared__ __align__(16) char lds[];
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
+  if (index_check_failed(a.status)) return;
   const int total = a.offs[a.N];
   if (j >= total) return;  // grid is sized for the worst case
   // sequence of chunk j: last n with offs[n] <= j
@@ -129,6 +142,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int H = a.H;
   const int j = blockIdx.x / H, h = blockIdx.x % H;
+  if (index_check_failed(a.status)) return;
   const int total = a.offs[a.N];
   if (j >= total) return;
   int lo = 0, hi = a.N - 1;
@@ -143,6 +157,15 @@ __global__ __launch_bounds__(kThreads, 1) void kda_prep_kernel(PrepArgs a) {
   kda_prep_item<DK, TIO, kW>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, threadIdx.x);
 }
 
+__global__ void copy_status_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst) {
+  if (threadIdx.x == 0) dst[0] = src[0];
+}
+
+hipError_t launch_copy_status(const int32_t* status, int32_t* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, stream, status, dst);
+  return hipGetLastError();
+}
+
 PrepLayout prep_layout(const gdn_shape_t& s, void* workspace) {
   PrepLayout L;
   char* w = reinterpret_cast<char*>(workspace);
@@ -150,18 +173,21 @@ PrepLayout prep_layout(const gdn_shape_t& s, void* workspace) {
   L.items = max_chunks * s.n_heads;
   const size_t offs_bytes = ((size_t)(s.n_seqs + 2) * 4 + 255) / 256 * 256;
   const size_t ready_bytes = ((size_t)L.items * 4 + 255) / 256 * 256;
+  L.status = nullptr;
   L.offs = nullptr;
   L.ready = nullptr;
   L.T = L.P = L.W = nullptr;
   const size_t w_bytes = (s.qdq_flags & GDN_QDQ_W) ? (size_t)L.items * w_rec_bytes(s.dk) : 0;
   if (w != nullptr) {
+    L.status = reinterpret_cast<int32_t*>(w);
+    w += kStatusBytes;
     L.offs = reinterpret_cast<int32_t*>(w);
     L.ready = reinterpret_cast<unsigned*>(w + offs_bytes);
     L.T = w + offs_bytes + ready_bytes;
     L.P = w + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes;
     if (w_bytes) L.W = w + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2;
   }
-  L.bytes = offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2 + w_bytes;
+  L.bytes = kStatusBytes + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2 + w_bytes;
   return L;
 }
 
@@ -202,12 +228,13 @@ hipError_t launch_prep(const gdn_shape_t& s, const void* q, const void* k, const
   // with records false the fused launch produces them and needs cleared ready flags
   const int64_t zero_blocks = records ? 1 : std::min<int64_t>(64, std::max<int64_t>(1, (L.items + 4095) / 4096));
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3((unsigned)zero_blocks), dim3(kThreads), 0, stream, cu_seqlens,
-                     seq_lens, prefix_lens, s.n_seqs, L.offs, records ? nullptr : L.ready, L.items);
+                     seq_lens, prefix_lens, s.n_seqs, (int64_t)s.total_tokens, L.offs, L.status,
+                     records ? nullptr : L.ready, L.items);
   if (!records || L.items == 0) return hipGetLastError();
   PrepArgs a;
   a.q = q; a.k = k; a.beta = beta; a.g = g; a.cu_seqlens = cu_seqlens; a.seq_lens = seq_lens;
   a.prefix_lens = prefix_lens; a.offs = L.offs; a.T = L.T; a.P = L.P; a.N = s.n_seqs; a.H = s.n_heads;
-  a.W = L.W; a.w_pre = w_pre; a.w_post = w_post;
+  a.W = L.W; a.w_pre = w_pre; a.w_post = w_post; a.status = L.status;
   const dim3 grid((unsigned)L.items);
   const bool wq = L.W != nullptr;
   if (s.gate_per_channel) {

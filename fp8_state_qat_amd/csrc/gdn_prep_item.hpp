@@ -36,6 +36,7 @@ struct PrepArgs {
   void* W;        // W QDQ: one W record (w_rec_bytes(dk)) per (chunk, head)
   float* w_pre;   // optional debug record of W before / after its QDQ,
   float* w_post;  // [chunk, head, 64, dk]
+  const int32_t* status;  // the workspace's status word (index check), or null
   int N;
   int H;
 };

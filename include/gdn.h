@@ -13,7 +13,8 @@
  *         u  = beta_t (v_t - S k_t);   S <- S + u k_t^T;   o_t = S q_t
  *   - Computed chunk-parallel in 64-token chunks (#2497 "What does this PR
  *     do?": fused path with chunk size 64) with WY/UT-transformed W and U and
- *     an exact triangular solve (#2506: "the exact solve remains the default").
+ *     an exact triangular solve (the default of #2506 "Add KDA prefill
+ *     numerical emulation for QAT", "What does this PR do?").
  *   - State QDQ (#2497 "What does this PR do?"): at every chunk boundary, for
  *     every tile of 64 value rows x all dk key columns of every (sequence,
  *     head), scale s = amax / 448 (zero guard: s = 1 when amax / 448 is not
@@ -59,7 +60,8 @@ typedef enum {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned buffer, bad flag */
     GDN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head size, dtype combo) */
-    GDN_ERR_DEVICE = 3         /* no gfx950 device current, or a HIP launch failed */
+    GDN_ERR_DEVICE = 3         /* no gfx950 device current, a HIP call failed, or (from */
+                               /* gdn_workspace_status) a device-side wait ran out */
 } gdn_status_t;
 
 typedef enum {
@@ -104,6 +106,14 @@ typedef struct {
     float* w_pre;                  /* [n_bounds, H, 64, dk] W of chunk b before its QDQ (GDN_QDQ_W) */
     float* w_post;                 /* [n_bounds, H, 64, dk] W after QDQ; rows past the chunk's */
                                    /* end are 0.  Both written only with GDN_QDQ_W. */
+    /* Per-token record of the recurrent suffix (tokens P_n < t <= L_n): token t of
+     * sequence n at s = suffix_offsets[n] + (t - 1 - P_n).  Needs suffix_offsets. */
+    const int32_t* suffix_offsets; /* [N + 1] device; prefix sums of L_n - P_n */
+    float* suffix_pre;             /* [n_suffix, H, dv, dk] state after token t, before its QDQ */
+    float* suffix_post;            /* [n_suffix, H, dv, dk] state after its QDQ (= pre when none) */
+    int32_t* status;               /* device int32 or NULL: receives the call's status word once */
+                                   /* its kernels are done (0 clean; 1 a bounded wait ran out; */
+                                   /* 2 index arrays out of contract), on the call's stream */
 } gdn_debug_t;
 
 /* gdn_debug_t.schedule.  The per-chunk solve (T and P records of every chunk
@@ -141,9 +151,19 @@ typedef struct {
  *   final_state [N, H, dv, dk] fp32 (output), may alias initial_state.
  *   workspace   device scratch of at least gdn_chunk_fwd_workspace_bytes(shape)
  *               bytes, 256-byte aligned, owned by the caller; its contents on entry
- *               are ignored and on return are unspecified.  Two calls that share a
- *               workspace must not overlap in time.
+ *               are ignored.  On return it holds the call's status word (read it
+ *               with gdn_workspace_status); the rest is unspecified.  Two calls that
+ *               share a workspace must not overlap in time.
  *   debug  NULL or a per-boundary record (see gdn_debug_t).
+ *
+ * Device-side failures (the call itself returned GDN_OK; gdn_workspace_status
+ * reports them once the stream has run the call):
+ *   - index arrays out of contract (cu_seqlens decreasing or beyond
+ *     total_tokens, a length above its segment, P_n > L_n, a negative entry):
+ *     every kernel of the call returns before touching o or final_state;
+ *   - a bounded wait of the single-launch schedule for a producer's record
+ *     ran out (200 ms, e.g. when the GPU is shared): that (sequence, head)'s
+ *     state and outputs from then on are NaN.
  *
  * QDQ placement for token t of a sequence (1-based): after token t when
  * (GDN_QDQ_CHUNK and t <= P and (t % 64 == 0 or t == P)) or
@@ -161,12 +181,24 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape,
                            const gdn_debug_t* debug, void* stream);
 
 /*
+ * gdn_workspace_status -- the status word a gdn_chunk_fwd or gdn_chunk_bwd_dh
+ * call left in its workspace.  Reads the 4 bytes at the workspace's start on
+ * `stream` (the stream of that call) and synchronizes it, so it is not for
+ * code under graph capture.  Returns GDN_OK when the call
+ * ran cleanly, GDN_ERR_INVALID_ARG when the device found its index arrays out
+ * of contract (nothing was computed), GDN_ERR_DEVICE when a bounded wait ran
+ * out (outputs hold NaN) or the read failed; gdn_last_error() says which.
+ *   workspace   the workspace passed to that call (device pointer)
+ */
+gdn_status_t gdn_workspace_status(const void* workspace, void* stream);
+
+/*
  * gdn_chunk_fwd_workspace_bytes -- bytes of device workspace gdn_chunk_fwd
  * needs for this shape: the per-chunk solve T = (I + A)^-1 diag(beta) and the
  * decayed, masked P = Q K^T of every (chunk, head) (12 KiB each, for the
  * worst-case chunk count ceil(total_tokens / 64) + n_seqs), with GDN_QDQ_W
  * the quantized W of every (chunk, head) (dk * 128 + 1024 bytes each), plus
- * the chunk offsets and one ready flag per (chunk, head).  Returns 0 for an
+ * the status word, the chunk offsets and one ready flag per (chunk, head).  Returns 0 for an
  * invalid shape (gdn_last_error() says why).
  */
 size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape);
@@ -204,6 +236,11 @@ gdn_status_t gdn_state_qdq_int8(const float* in, float* out, float* scales,
  *   shape->total_tokens must equal shape->n_seqs; GDN_QDQ_CHUNK is ignored.
  *   q, k  [N, H, dk] io_dtype;  v [N, H, dv] io_dtype
  *   beta  [N, H] fp32;  g [N, H] or [N, H, dk] fp32
+ *   active [N] int32 or NULL (all active): sequence n takes the step when
+ *          active[n] != 0; for the others nothing is read or written (state, o,
+ *          state_pre and scales keep their contents) -- sequences of a batch
+ *          that end at different lengths (#2519 "What does this PR do?": prefill
+ *          and full lengths per sequence)
  *   state [N, H, dv, dk] fp32, read and written in place
  *   o     [N, H, dv] o_dtype
  *   state_pre  [N, H, dv, dk] fp32 or NULL: the updated state before QDQ (parity record)
@@ -212,7 +249,7 @@ gdn_status_t gdn_state_qdq_int8(const float* in, float* out, float* scales,
  */
 gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
                              const void* q, const void* k, const void* v,
-                             const float* beta, const float* g,
+                             const float* beta, const float* g, const int32_t* active,
                              float* state, void* o,
                              float* state_pre, float* scales, void* stream);
 
@@ -229,7 +266,10 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
  * states out of it, so no forward state is needed.  Whole sequences (no
  * prefix/suffix split); scalar gate; bf16 q, k and d_o.
  *   shape       as for gdn_chunk_fwd (io_dtype GDN_BF16, gate_per_channel 0;
- *               o_dtype and qdq_flags are not used)
+ *               o_dtype is not used).  qdq_flags are those of the forward: the
+ *               state QDQ flags (CHUNK, WRITE) do not change the gradient under
+ *               the identity straight-through rule; GDN_QDQ_W does (its W enters
+ *               the state path) and returns GDN_ERR_UNSUPPORTED.
  *   q, k        [total_tokens, H, dk] bf16;  beta, g [total_tokens, H] fp32
  *   cu_seqlens, seq_lens   as for gdn_chunk_fwd (seq_lens nullable)
  *   d_o         [total_tokens, H, dv] bf16, the gradient of o (padding rows ignored)
@@ -243,7 +283,9 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
  *               chunk only through U = T V, so it is Y); rows of a segment past
  *               L_n are written as 0, rows after cu_seqlens[N] are not written
  *   workspace   at least gdn_chunk_bwd_workspace_bytes(shape) bytes, 256-byte
- *               aligned, caller-owned, contents ignored on entry.
+ *               aligned, caller-owned, contents ignored on entry; holds the call's
+ *               status word on return (gdn_workspace_status; index arrays out of
+ *               contract: nothing is written).
  */
 gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape,
                               const void* q, const void* k, const float* beta, const float* g,
@@ -252,7 +294,7 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape,
                               float* dh, float* d_initial_state, float* d_v,
                               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device workspace bytes gdn_chunk_bwd_dh needs: the chunk offsets and, per
+/* Device workspace bytes gdn_chunk_bwd_dh needs: the status word, the chunk offsets and, per
  * (chunk, head) of the worst-case chunk count, T^T and P^T as full 64 x 64
  * records (16 KiB each).  0 for an invalid shape. */
 size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape_t* shape);

@@ -90,14 +90,14 @@ def test_chunk_fwd_rejects_null_and_misaligned():
 
 def test_workspace_size_and_checks():
     """Workspace: for the worst-case chunk count ceil(T/64) + N, two records
-    of 12 KiB (T and P) per chunk and head, one ready flag per chunk and head
-    and the chunk offsets, each region padded to 256 bytes; too small, NULL
-    or misaligned is rejected."""
+    of 12 KiB (T and P) per chunk and head, one ready flag per chunk and head,
+    the chunk offsets and the status word, each region padded to 256 bytes;
+    too small, NULL or misaligned is rejected."""
     s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
     n = _ws(s)
-    assert n == 256 + 256 + (3 + 3) * 2 * 2 * 12288
+    assert n == 256 + 256 + 256 + (3 + 3) * 2 * 2 * 12288   # status, offsets, flags, records
     big = _shape(n_seqs=70, n_heads=3, total_tokens=64 * 100)   # 72 offsets, 510 flags
-    assert _ws(big) == 512 + 2048 + 170 * 3 * 2 * 12288
+    assert _ws(big) == 256 + 512 + 2048 + 170 * 3 * 2 * 12288
     assert _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, gate_per_channel=1)) == n
     assert _ws(_shape(dv=96)) == 0 and _lib.last_error()
     assert _chunk(s, ws_bytes=n - 1) == 1
@@ -146,12 +146,41 @@ def test_state_qdq_int8_rejects_bad_args():
 def test_decode_rejects_bad_args():
     L = _lib.lib()
     p = ctypes.c_void_p
+    # q, k, v, beta, g, active, state, o, state_pre, scales, stream
     s = _shape(total_tokens=3)     # decode needs total_tokens == n_seqs
-    args = [p(FAKE)] * 7 + [None, None, None]
+    args = [p(FAKE)] * 5 + [None, p(FAKE), p(FAKE), None, None, None]
     assert L.gdn_decode_step(ctypes.byref(s), *args) == 1
     s = _shape(total_tokens=2)
-    bad = [p(FAKE)] * 5 + [None, p(FAKE), None, None, None]   # state NULL
+    bad = [p(FAKE)] * 5 + [None, None, p(FAKE), None, None, None]   # state NULL
     assert L.gdn_decode_step(ctypes.byref(s), *bad) == 1
+    bad = [p(FAKE)] * 5 + [p(FAKE + 2), p(FAKE), p(FAKE), None, None, None]   # misaligned active
+    assert L.gdn_decode_step(ctypes.byref(s), *bad) == 1
+    assert "misaligned" in _lib.last_error()
+
+
+def test_suffix_record_and_debug_alignment():
+    """The recurrent suffix's per-token record needs its offsets; every state
+    record must be 16-byte aligned."""
+    f = ctypes.c_void_p(FAKE)
+    # bound_offsets, bound_pre, bound_post, scales, kernel_start, kernel_end, schedule,
+    # w_pre, w_post, suffix_offsets, suffix_pre, suffix_post
+    dbg = GdnDebug(None, None, None, None, None, None, 0, None, None, None, f, None)
+    assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
+    assert "suffix_offsets" in _lib.last_error()
+    dbg = GdnDebug(None, None, None, None, None, None, 0, None, None, f, None, ctypes.c_void_p(FAKE + 4))
+    assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
+    dbg = GdnDebug(f, ctypes.c_void_p(FAKE + 8), None, None, None, None, 0, None, None, None, None, None)
+    assert _chunk(_shape(), dbg=ctypes.byref(dbg)) == 1
+
+
+def test_workspace_status_checks():
+    """gdn_workspace_status takes the call's workspace: NULL or misaligned is
+    rejected on the host; without a GPU the read reports a device error."""
+    L = _lib.lib()
+    assert L.gdn_workspace_status(None, None) == 1
+    assert L.gdn_workspace_status(ctypes.c_void_p(FAKE + 16), None) == 1
+    if not HAS_GPU:
+        assert L.gdn_workspace_status(ctypes.c_void_p(FAKE), None) == 3
 
 
 @pytest.mark.skipif(HAS_GPU, reason="would launch with stand-in pointers on a GPU")
@@ -170,14 +199,17 @@ def _bwd(shape, q=FAKE, do=FAKE, dh=FAKE, d0=FAKE, ws=FAKE, ws_bytes=None):
 
 
 def test_chunk_bwd_dh_checks():
-    """Workspace: chunk offsets plus two 16 KiB records (T^T, P^T) per chunk
-    and head of the worst-case count; bf16 and the scalar gate only; at least
-    one output; buffers aligned."""
+    """Workspace: the status word and chunk offsets plus two 16 KiB records
+    (T^T, P^T) per chunk and head of the worst-case count; bf16 and the
+    scalar gate only; a W-QDQ forward is refused; at least one output;
+    buffers aligned."""
     L = _lib.lib()
     s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
-    assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(s)) == 256 + (3 + 3) * 2 * 2 * 16384
+    assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(s)) == 256 + 256 + (3 + 3) * 2 * 2 * 16384
     assert _bwd(_shape(io_dtype=0, dk=64)) == 2
     assert _bwd(_shape(gate_per_channel=1)) == 2
+    assert _bwd(_shape(qdq_flags=3 | _lib.GDN_QDQ_W)) == 2   # the W-QDQ forward's backward
+    assert "GDN_QDQ_W" in _lib.last_error()
     assert _bwd(_shape(), dh=0, d0=0) == 1
     assert _bwd(_shape(), q=FAKE + 8) == 1
     assert _bwd(_shape(), ws_bytes=100) == 1

@@ -18,7 +18,7 @@ import pytest
 from fp8_state_qat_amd import inputs as gi
 from oracle import oracle as orc
 
-from helpers import TOL, check_prefix_suffix, rel_l2, run_chunk_gpu, run_chunk_oracle, teacher_forced
+from helpers import TOL, check_codes, check_prefix_suffix, rel_l2, run_chunk_gpu, run_chunk_oracle, teacher_forced
 from helpers import check_g1 as _check_g1, check_g2 as _check_g2
 
 pytestmark = pytest.mark.gpu
@@ -74,23 +74,41 @@ def test_varlen_padding_is_isolated():
 @pytest.mark.parametrize("flags", [1, 2, 3])
 def test_prefix_suffix_fp32(flags):
     """Chunked prefix P then recurrent suffix up to L (fp32), with the
-    three QDQ placements."""
+    three QDQ placements: prefix teacher-forced per boundary, suffix
+    teacher-forced per token."""
     w = gi.make_packed([150, 70, 9], 2, 64, 64, io_dtype=gi.F32, seed=7 + flags,
                        prefix_lens=[128, 33, 0])
-    gpu = run_chunk_gpu(w, flags, record=True)
+    gpu = run_chunk_gpu(w, flags, record=True, suffix_record=True)
     check_prefix_suffix(w, gpu, flags, TOL[gi.F32])
 
 
-def test_prefix_suffix_bf16_no_suffix_qdq():
-    w = gi.make_packed([200, 100], 2, 128, 128, io_dtype=gi.BF16, seed=11,
-                       prefix_lens=[130, 64])
-    gpu = run_chunk_gpu(w, 1, o_dtype="f32")
-    ref = run_chunk_oracle(w, 1)
-    # prefix rows with QDQ are checked teacher-forced elsewhere; here the
-    # state and suffix use a chunk-only flag, so compare free-running loosely
-    o_rel, s_rel = rel_l2(gpu["o"], ref["o"]), rel_l2(gpu["S"], ref["S"])
-    print(f"o_rel={o_rel:.3e} S_rel={s_rel:.3e}", flush=True)
-    assert o_rel <= 2e-2 and s_rel <= 2e-2
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("d,dv", [(128, 128), (64, 192)])
+def test_prefix_suffix_bf16(flags, d, dv):
+    """bf16 inputs, prefix/suffix split (#2519: chunked prefix, then a
+    recurrent write per token with QDQ at the handoff and after each write
+    under flags 2 and 3): a suffix after a whole chunk, after a partial
+    chunk, with no prefix at all, and an empty suffix.  Prefix teacher-forced
+    per boundary, suffix teacher-forced per token (o and the pre-QDQ state
+    within 2e-3; the stored state is the oracle's QDQ of the GPU's pre-QDQ
+    state bit for bit)."""
+    w = gi.make_packed([200, 100, 45, 64], 2, d, dv, io_dtype=gi.BF16, seed=11 + flags + d,
+                       prefix_lens=[130, 64, 0, 64])
+    gpu = run_chunk_gpu(w, flags, o_dtype="f32", record=True, suffix_record=True)
+    check_prefix_suffix(w, gpu, flags, TOL[gi.BF16])
+
+
+@pytest.mark.parametrize("flags", [2, 3])
+def test_full_size_prefix_suffix_sampled(flags):
+    """The full GDN prefill shape (B=4, T=4096, H=16, d=128, bf16) with a
+    recurrent suffix: prefixes of 4059, 4032, 4096 and 4000 tokens (a partial
+    last chunk, whole chunks, no suffix, 96 suffix tokens), in the
+    benchmark's launch configuration.  Sampled pairs, prefix teacher-forced
+    per boundary and suffix per token."""
+    w = gi.gdn_prefill()
+    w.prefix_lens = np.array([4059, 4032, 4096, 4000], np.int32)
+    gpu = run_chunk_gpu(w, flags, o_dtype="bf16", record=True, suffix_record=True)
+    check_prefix_suffix(w, gpu, flags, TOL[gi.BF16], pairs=[(0, 3), (1, 9), (2, 0), (3, 15)])
 
 
 def test_initial_state_fp32():
@@ -158,6 +176,7 @@ def test_full_size_gdn_prefill_sampled(flags):
         print("G2 sampled", r, flush=True)
         assert r["o_rel"] <= TOL[gi.BF16] and r["pre_rel"] <= TOL[gi.BF16]
         assert r["gpu_code_mismatch"] == 0 and r["scale_mismatch"] == 0
+        check_codes(r)
 
 
 @pytest.mark.parametrize("io,d", [(gi.F32, 64), (gi.BF16, 128)])
@@ -204,6 +223,7 @@ def test_full_size_varlen_sampled(flags):
         print("G2 sampled", r, flush=True)
         assert r["o_rel"] <= TOL[gi.BF16] and r["pre_rel"] <= TOL[gi.BF16]
         assert r["gpu_code_mismatch"] == 0 and r["scale_mismatch"] == 0
+        check_codes(r)
 
 
 def test_full_size_varlen_nan_padding_changes_nothing():

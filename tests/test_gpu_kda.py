@@ -97,8 +97,17 @@ def test_kda_prefix_suffix_fp32(flags):
     """Chunked prefix P, then the recurrent suffix up to L with the
     per-channel decay, under the three QDQ placements."""
     w = _kda([150, 70, 9], 2, 64, 64, gi.F32, seed=59 + flags, prefix_lens=[128, 33, 0])
-    gpu = run_chunk_gpu(w, flags, record=True)
+    gpu = run_chunk_gpu(w, flags, record=True, suffix_record=True)
     check_prefix_suffix(w, gpu, flags, TOL[gi.F32])
+
+
+@pytest.mark.parametrize("flags", [2, 3])
+def test_kda_prefix_suffix_bf16(flags):
+    """bf16, d=128: the per-channel decay through the prefix/suffix split,
+    both teacher-forced (per boundary, per suffix token)."""
+    w = _kda([200, 100, 45], 2, 128, 128, gi.BF16, seed=67 + flags, prefix_lens=[130, 64, 0])
+    gpu = run_chunk_gpu(w, flags, o_dtype="f32", record=True, suffix_record=True)
+    check_prefix_suffix(w, gpu, flags, TOL[gi.BF16])
 
 
 def test_kda_initial_state_fp32():

@@ -8,7 +8,7 @@ from fp8_state_qat_amd import api
 from fp8_state_qat_amd import inputs as gi
 from oracle import oracle as orc
 
-from helpers import np64, rel_l2
+from helpers import _code_fields, check_codes, code_mismatch_stats, np64, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -165,8 +165,45 @@ def test_decode_step_teacher_forced(dk, dv, io, pc, o_dt, qdq):
         pre_np = pre.cpu().numpy()
         assert rel_l2(pre_np, pre_ref) <= 1e-6
         if qdq:
-            want, sc, _ = orc.qdq_states(pre_np)
+            want, sc, codes_gpu = orc.qdq_states(pre_np)
             np.testing.assert_array_equal(state.cpu().numpy().view(np.uint32), want.view(np.uint32))
             np.testing.assert_array_equal(scales.cpu().numpy(), sc)
+            # the oracle's own codes on its own pre-QDQ state (G3)
+            _, sc_o, codes_orc = orc.qdq_states(pre_ref.astype(np.float32))
+            r = _code_fields()
+            y = pre_ref / np.repeat(sc_o.astype(np.float64), 64, axis=-1)[..., None]
+            code_mismatch_stats(r, codes_orc, codes_gpu, y)
+            check_codes(r)
         else:
             np.testing.assert_array_equal(state.cpu().numpy(), pre_np)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_decode_active_mask(int8):
+    """Sequences whose active flag is 0 are skipped: their state, o row and
+    records keep their contents bit for bit; the active ones take the step
+    exactly as in a call without a mask (bit-identical)."""
+    N, H, dk, dv = 6, 3, 128, 128
+    S0, toks = _decode_case(N, H, dk, dv, gi.BF16, False, 1, torch.float32, True, seed=97)
+    dev = {k_: gi.to_torch(a, "cuda") for k_, a in toks[0].items()}
+    active_np = np.array([1, 0, 1, 1, 0, 0], np.int32)
+    sc_shape = (N, H, dv, dk // 32) if int8 else (N, H, dv // 64)
+    ref_state = torch.from_numpy(S0).cuda()
+    ref_pre = torch.full_like(ref_state, 3.0)
+    ref_sc = torch.full(sc_shape, 3.0, device="cuda")
+    ref_o = api.decode_step(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], ref_state, qdq=True,
+                            o_dtype=torch.float32, state_pre=ref_pre, scales=ref_sc, int8=int8)
+    state = torch.from_numpy(S0).cuda()
+    pre = torch.full_like(state, 3.0)
+    sc = torch.full(sc_shape, 3.0, device="cuda")
+    o = torch.full((N, H, dv), 5.0, device="cuda")
+    api.decode_step(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], state, qdq=True, o=o,
+                    state_pre=pre, scales=sc, int8=int8, active=torch.from_numpy(active_np).cuda())
+    torch.cuda.synchronize()
+    on = torch.from_numpy(active_np.astype(bool)).cuda()
+    bits = lambda t: t.view(torch.int32)  # noqa: E731
+    assert torch.equal(bits(state[on]), bits(ref_state[on])) and torch.equal(bits(pre[on]), bits(ref_pre[on]))
+    assert torch.equal(bits(o[on]), bits(ref_o[on])) and torch.equal(bits(sc[on]), bits(ref_sc[on]))
+    off = ~on
+    assert torch.equal(bits(state[off]), bits(torch.from_numpy(S0).cuda()[off]))
+    assert bool((pre[off] == 3.0).all()) and bool((sc[off] == 3.0).all()) and bool((o[off] == 5.0).all())

@@ -15,8 +15,8 @@ import torch
 
 from fp8_state_qat_amd import api
 from fp8_state_qat_amd import inputs as gi
-from fp8_state_qat_amd._lib import (GDN_SCHEDULE_AUTO, GDN_SCHEDULE_FUSED, GDN_SCHEDULE_FUSED_NO_PRODUCERS,
-                                    GDN_SCHEDULE_SPLIT)
+from fp8_state_qat_amd._lib import (GDN_ERR_DEVICE, GDN_ERR_INVALID_ARG, GDN_SCHEDULE_AUTO, GDN_SCHEDULE_FUSED,
+                                    GDN_SCHEDULE_FUSED_NO_PRODUCERS, GDN_SCHEDULE_SPLIT, GdnError)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +89,7 @@ def test_workspace_reuse_and_garbage():
     # every (chunk, head) of the call was produced and flagged: bit 0 ready,
     # bits 4:1 the producer's XCD, bit 8 a device-wide release (producer off
     # its XCD, expected never)
-    hdr = ((2 + 2) * 4 + 255) // 256 * 256   # chunk offsets and the largest chunk count
+    hdr = 256 + ((2 + 2) * 4 + 255) // 256 * 256   # status word; chunk offsets and the largest chunk count
     n_items = (32 + 24) * 8                    # (chunk, head) pairs of the call
     flags = ws[hdr:hdr + 4 * n_items].view(torch.int32).cpu().numpy()
     assert np.all(flags & 1 == 1) and np.all(flags >> 9 == 0)
@@ -134,15 +134,95 @@ def test_fused_wait_runs_out_and_poisons(per_channel):
     unaffected."""
     kw = dict(per_channel=True, g_scale=0.05) if per_channel else {}
     d = gi.device_packed([200, 64, 130], 2, 64, 64, seed=31, **kw)
+    ws = torch.empty(api.chunk_workspace_bytes(3, 2, 64, 64, 394), dtype=torch.uint8, device="cuda")
+    st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     t0 = time.perf_counter()
-    o, S = _run(d, 3, GDN_SCHEDULE_FUSED_NO_PRODUCERS, o_dtype=torch.float32)
+    o, S = api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=3,
+                         o_dtype=torch.float32, workspace=ws,
+                         debug={"schedule": GDN_SCHEDULE_FUSED_NO_PRODUCERS, "status": st})
+    torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    assert int(st.item()) == 1   # the status word, copied out on the stream
     print(f"per_channel={per_channel}: call with no producers took {dt:.3f} s; "
           f"NaN state elements {int(torch.isnan(S).sum())} of {S.numel()}", flush=True)
     assert torch.isnan(S).all()
     assert torch.isnan(o).any()
     assert dt < 30.0
-    a = _run(d, 3, GDN_SCHEDULE_SPLIT, o_dtype=torch.float32)
-    b = _run(d, 3, GDN_SCHEDULE_FUSED, o_dtype=torch.float32)
+    # the call returned GDN_OK (it was enqueued); its status word says what happened
+    with pytest.raises(GdnError) as e:
+        api.workspace_status(ws)
+    assert e.value.status == GDN_ERR_DEVICE and "wait" in str(e.value)
+    a = _run(d, 3, GDN_SCHEDULE_SPLIT, o_dtype=torch.float32, workspace=ws)
+    api.workspace_status(ws)
+    b = _run(d, 3, GDN_SCHEDULE_FUSED, o_dtype=torch.float32, workspace=ws)
+    api.workspace_status(ws)   # cleared by the next call
     assert torch.isfinite(a[1]).all() and torch.isfinite(a[0]).all()
     _same(a, b, f"after the failed waits, per_channel={per_channel}")
+
+
+BAD_INDEX_CASES = {
+    "cu_seqlens decreasing": dict(cu=[0, 150, 80, 200]),
+    "cu_seqlens beyond total_tokens": dict(cu=[0, 80, 150, 260]),
+    "cu_seqlens negative": dict(cu=[-5, 80, 150, 200]),
+    "length above its segment": dict(seq=[81, 70, 50]),
+    "negative length": dict(seq=[-1, 70, 50]),
+    "prefix above the length": dict(pre=[80, 71, 50]),
+    "negative prefix": dict(pre=[80, -64, 50]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BAD_INDEX_CASES))
+@pytest.mark.parametrize("sched", [GDN_SCHEDULE_SPLIT, GDN_SCHEDULE_AUTO])
+def test_out_of_contract_index_arrays_run_nothing(case, sched):
+    """Index arrays whose contents break the contract (checked on the device
+    by the offsets kernel, before any other kernel reads them): every kernel
+    of the call returns at once, o and the final state keep their contents,
+    and the workspace's status word reports GDN_ERR_INVALID_ARG.  The next
+    valid call on the same workspace runs normally."""
+    c = BAD_INDEX_CASES[case]
+    w = gi.make_packed([80, 70, 50], 2, 64, 64, io_dtype=gi.BF16, seed=37)
+    d = gi.device_tensors(w)
+    cu = torch.tensor(c.get("cu", [0, 80, 150, 200]), dtype=torch.int32, device="cuda")
+    seq = torch.tensor(c["seq"], dtype=torch.int32, device="cuda") if "seq" in c else None
+    pre = torch.tensor(c["pre"], dtype=torch.int32, device="cuda") if "pre" in c else None
+    ws = torch.empty(api.chunk_workspace_bytes(3, 2, 64, 64, 200), dtype=torch.uint8, device="cuda")
+    o = torch.full((200, 2, 64), 7.0, dtype=torch.float32, device="cuda")
+    S = torch.full((3, 2, 64, 64), -3.0, dtype=torch.float32, device="cuda")
+    for per_channel in (False, True):
+        g = d["g"] if not per_channel else torch.full((200, 2, 64), -0.05, device="cuda")
+        st = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], g, cu, seq_lens=seq, prefix_lens=pre, qdq_flags=3,
+                      out=o, final_state=S, workspace=ws, debug={"schedule": sched, "status": st})
+        with pytest.raises(GdnError) as e:
+            api.workspace_status(ws)
+        assert e.value.status == GDN_ERR_INVALID_ARG
+        assert int(st.item()) == 2   # the same word, copied out on the stream
+        assert bool((o == 7.0).all()) and bool((S == -3.0).all()), f"{case}: outputs were written"
+    api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], qdq_flags=3, out=o,
+                  final_state=S, workspace=ws, debug={"schedule": sched})
+    api.workspace_status(ws)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
+
+
+@pytest.mark.parametrize("case", sorted(k for k in BAD_INDEX_CASES if "pre" not in BAD_INDEX_CASES[k]))
+def test_bwd_out_of_contract_index_arrays_run_nothing(case):
+    """The same device-side index check guards the backward: nothing is
+    written and the status word reports GDN_ERR_INVALID_ARG."""
+    c = BAD_INDEX_CASES[case]
+    w = gi.make_packed([80, 70, 50], 2, 64, 64, io_dtype=gi.BF16, seed=41)
+    d = gi.device_tensors(w)
+    cu = torch.tensor(c.get("cu", [0, 80, 150, 200]), dtype=torch.int32, device="cuda")
+    seq = torch.tensor(c["seq"], dtype=torch.int32, device="cuda") if "seq" in c else None
+    d_o = torch.ones((200, 2, 64), dtype=torch.bfloat16, device="cuda")
+    d0 = torch.full((3, 2, 64, 64), 5.0, device="cuda")
+    dv = torch.full((200, 2, 64), 9.0, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    api.chunk_bwd_dh(d["q"], d["k"], d["beta"], d["g"], cu, d_o, seq_lens=seq, d_initial_state=d0, d_v=dv,
+                     workspace=ws)
+    with pytest.raises(GdnError) as e:
+        api.workspace_status(ws)
+    assert e.value.status == GDN_ERR_INVALID_ARG
+    assert bool((d0 == 5.0).all()) and bool((dv == 9.0).all())
+    api.chunk_bwd_dh(d["q"], d["k"], d["beta"], d["g"], d["cu_seqlens"], d_o, d_initial_state=d0, d_v=dv,
+                     workspace=ws, check_status=True)
+    assert bool(torch.isfinite(d0).all()) and not bool((d0 == 5.0).all())

@@ -28,7 +28,8 @@ from fp8_state_qat_amd._lib import GDN_QDQ_W, GDN_SCHEDULE_AUTO, GDN_SCHEDULE_FU
 from oracle import oracle as orc
 from oracle.chunked import chunk_step, gdn_chunked
 
-from helpers import CHUNK, TOL, midpoint_distance, n_bounds, np64, rel_l2, valid_rows
+from helpers import (CHUNK, TOL, canon_codes, midpoint_distance, midpoint_distance_range, n_bounds, np64,
+                     rel_l2, valid_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,7 @@ def check_w(w, gpu, flags, tol, *, initial_state=None, pairs=None):
     cu, offs = w.cu_seqlens, gpu["offsets"]
     if pairs is None:
         pairs = [(n, h) for n in range(w.n_seqs) for h in range(w.n_heads)]
-    st = dict(w_bits=0, w_codes=0, w_mism=0, w_far=0, s_bits=0, s_scale=0, pad=0)
+    st = dict(w_bits=0, w_codes=0, w_mism=0, w_far=0, w_far_rel=0, w_max_dist=0.0, s_bits=0, s_scale=0, pad=0)
     acc = np.zeros(6)   # W err, W ref, o err, o ref, pre err, pre ref (squared sums)
     for (n, h) in pairs:
         P, s0 = int(w.prefix_lens[n]), int(cu[n])
@@ -94,12 +95,15 @@ def check_w(w, gpu, flags, tol, *, initial_state=None, pairs=None):
             want, _, codes_g = orc.qdq_rows(Wg)
             st["w_bits"] += int(np.sum(want.view(np.uint32) != Wqg.view(np.uint32)))
             _, sc_o, codes_o = orc.qdq_rows(r["W"].astype(np.float32))
-            mism = codes_o != codes_g
+            mism = canon_codes(codes_o) != canon_codes(codes_g)
             st["w_codes"] += codes_o.size
             st["w_mism"] += int(mism.sum())
             if mism.any():
                 y = r["W"] / sc_o.astype(np.float64)[:, None]
-                st["w_far"] += int(np.sum(midpoint_distance(y[mism]) > 1e-6))
+                st["w_far"] += int(np.sum(midpoint_distance_range(y[mism]) > 1e-6))
+                dist = midpoint_distance(y[mism])
+                st["w_far_rel"] += int(np.sum(dist > 1e-6))
+                st["w_max_dist"] = max(st["w_max_dist"], float(dist.max()))
             # GW3
             pre_g = gpu["bound_pre"][bidx, h]
             acc[2:] += [np.sum((gpu["o"][sl, h] - r["o"]) ** 2), np.sum(r["o"] ** 2),
