@@ -48,7 +48,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-T_RECORD_BYTES = 12288         # per (chunk, head) and record: T = (I + A)^-1 diag(beta), and P; hi + lo bf16 planes
+T_RECORD_BYTES = 18432         # per (chunk, head): T = (I + A)^-1 diag(beta) as hi, mid, lo bf16 planes
+P_RECORD_BYTES = 12288         # per (chunk, head): the decayed, masked P = Q K^T as hi + lo bf16 planes
 BF16_MFMA_PEAK_TFLOPS = 2516.6 # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "GDN chunked-prefill tokens/s + MFMA %peak; decode step HBM GB/s, 1×MI355X"
 
@@ -75,9 +76,10 @@ def prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes, gate_floats=1):
 
 def split_state_kernel_bytes(T_heads, n_chunk_heads, n_states, dk, dv, io_bytes, o_bytes):
     """Algorithmic HBM bytes of the sequential state kernel: the prefill bytes
-    plus one read of the two per-chunk records the prep kernel writes (T and
-    P, 12 KiB each per chunk and head)."""
-    return prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes) + n_chunk_heads * 2 * T_RECORD_BYTES
+    plus one read of the two per-chunk records the prep kernel writes (T,
+    18 KiB, and P, 12 KiB, per chunk and head)."""
+    return (prefill_bytes(T_heads, n_states, dk, dv, io_bytes, o_bytes)
+            + n_chunk_heads * (T_RECORD_BYTES + P_RECORD_BYTES))
 
 
 def bwd_flops_per_token_head(C, dk, dv):

@@ -70,9 +70,10 @@ constexpr int kHelperThreads = 256;  // waves 4..7
 //                  fragments (fp32 engine; the bf16 engine reads these
 //                  fragments from K with transpose reads)
 //   V   [64][64 + 16 bytes]  the tile's v rows, row-major, padded rows
-//   T   [plane][p] 6 fragments per plane (the prep kernel's record, copied as is)
-//   P   2 x [plane][p]  the prep kernel's P record, same layout, double-buffered
-//                  by chunk parity
+//   T   [plane][p] 6 fragments per plane, three planes (bf16) or one (fp32):
+//                  the T record, copied as is
+//   P   2 x [plane][p]  the P record (two planes), double-buffered by chunk
+//                  parity (one buffer with W QDQ, whose W record needs the room)
 //   XU  [c][plane*2 + kb]     U' as the A operand of U'^T P^T, per chain wave
 //   XS  [c][plane*NKB + kb]   the state as the A operand of S Q^T, per chain wave
 //   vec (unused), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
@@ -83,6 +84,8 @@ template <int DK, class Eng, bool kW = false>
 struct Lds {
   using E = typename Eng::E;
   static constexpr int NKB = DK / 32, NT = DK / 16, NP = Eng::kPlanes;
+  static constexpr int NPT = Eng::kSplit ? 3 : 1;     // planes of the T record
+  static constexpr int PBUF = kW ? 1 : 2;             // P buffers
   static constexpr size_t F = 64 * 8 * sizeof(E);
   static constexpr size_t RV = 64 * sizeof(E) + 16;    // padded v row (bytes)
   static constexpr size_t oK = 0;                      // 2 buffers by chunk parity
@@ -90,14 +93,14 @@ struct Lds {
   static constexpr size_t oKT = oQ + 4 * NKB * F;
   static constexpr size_t oV = oKT + (Eng::kTrRead ? 0 : 2 * NT * F);
   static constexpr size_t oT = oV + 64 * RV;
-  static constexpr size_t oP = oT + 6 * NP * F;
-  static constexpr size_t oXU = oP + 2 * 6 * NP * F;  // 2 buffers by chunk parity
+  static constexpr size_t oP = oT + 6 * NPT * F;
+  static constexpr size_t oXU = oP + PBUF * 6 * NP * F;
   static constexpr size_t oXS = oXU + 4 * 2 * NP * F;
   static constexpr size_t oVec = oXS + 4 * NKB * NP * F;
   static constexpr size_t oRed = oVec + (3 * 64 + 8) * sizeof(float);
   static constexpr size_t oW = oRed + 8 * sizeof(float);
   static constexpr size_t bytes = oW + (kW ? (size_t)w_rec_bytes(DK) : 0);
-  static_assert(6 * NP * F == kTRecBytes, "T record and its LDS copy differ");
+  static_assert(6 * NPT * F <= kTRecBytes && 6 * NP * F == kPRecBytes, "records and their LDS copies differ");
   static_assert(oW % 16 == 0, "direct loads need 16-byte aligned LDS");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
   static_assert(oK + (2 * DK + 64 + 8) * sizeof(float) <= oQ, "suffix buffers do not fit");
@@ -345,10 +348,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const int64_t row0 = seg0 + cc * kChunk;
     load_rows(gv_ + row0 * v_row + (int64_t)h * dv + kTileRows * vt, (int)v_row, vdst, nv, wi);
     const char* rec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
+    constexpr int NTI = (int)(6 * Ls::NPT * Ls::F / 1024);  // 1 KiB pieces of the T record
 #pragma unroll
-    for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
-      const int idx = wi * (kTRecBytes / 1024 / 4) + ii;
-      lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(tdst) + idx * 1024);
+    for (int ii = 0; ii < (NTI + 3) / 4; ++ii) {
+      const int idx = wi + 4 * ii;
+      if (idx < NTI) lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(tdst) + idx * 1024);
     }
   };
   auto issue_w = [&](int cc, uint16_t* wdst, int wi) {  // the W record of chunk cc (kW)
@@ -366,10 +370,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     load_dump(gq_ + row0 * qk_row + (int64_t)h * DK, qdst, nv, hw);
   };
   auto issue_p = [&](int cc, E* pdst) {  // the P record of chunk cc
-    const char* rec = reinterpret_cast<const char*>(args.Prec) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
+    const char* rec = reinterpret_cast<const char*>(args.Prec) + ((int64_t)(chunk0 + cc) * H + h) * kPRecBytes;
 #pragma unroll
-    for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
-      const int idx = hw * (kTRecBytes / 1024 / 4) + ii;
+    for (int ii = 0; ii < kPRecBytes / 1024 / 4; ++ii) {
+      const int idx = hw * (kPRecBytes / 1024 / 4) + ii;
       lds_load16(rec, (uint32_t)((idx * 64 + lane) * 16), lds_of(pdst) + idx * 1024);
     }
   };
@@ -524,11 +528,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) Eng::mma(acc[tt], kf[tt * NKB + kb], sh[kb]);
       }
-      Fr tf[6], tl[6];
+      Fr tf[6], tm[6], tl[6];  // T as hi, mid, lo planes (bf16 engine)
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         tf[p] = Eng::ld(slot(tb, p));
-        if constexpr (kSplit) tl[p] = Eng::ld(slot(tb, 6 + p));
+        if constexpr (kSplit) {
+          tm[p] = Eng::ld(slot(tb, 6 + p));
+          tl[p] = Eng::ld(slot(tb, 12 + p));
+        }
       }
       if constexpr (kW) {
         // U' = T V - s w_s[t] (W S^T)[t][v]: V enters exactly, as the B
@@ -554,8 +561,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int p = 0; p < 6; ++p) {
           const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+          if constexpr (kSplit) {
+            Eng::mma(uacc[ti], tl[p], vf[kb]);
+            Eng::mma(uacc[ti], tm[p], vf[kb]);
+          }
           Eng::mma(uacc[ti], tf[p], vf[kb]);
-          if constexpr (kSplit) Eng::mma(uacc[ti], tl[p], vf[kb]);
         }
         const float* wsc = reinterpret_cast<const float*>(wb + 4 * NKB * 512);
 #pragma unroll
@@ -568,7 +578,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         }
       } else {
       // X[t][v] = V[t][v] - s exp(gamma_t) (K S^T)[t][v], t = 16tt + 4gq + i
-      Fr xh[2], xl[2];
+      Fr xh[2], xm[2], xl[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float x8[8];
@@ -595,19 +605,24 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           x8[4 * hh + 2] = fmaf(-sc * e4.z, acc[tt][2], vv[2]);
           x8[4 * hh + 3] = fmaf(-sc * e4.w, acc[tt][3], vv[3]);
         }
-        Eng::split(x8, xh[kb], xl[kb]);
+        Eng::split3(x8, xh[kb], xm[kb], xl[kb]);
       }
-      // U' = T X over the lower-triangular T pairs (ti, kb): (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
+      // U' = T X over the lower-triangular T pairs (ti, kb): (0,0) (1,0) (2,0)
+      // (3,0) (2,1) (3,1).  bf16: T and X as three planes each (24 bits), the
+      // six partial products down to 2^-16 of the leading one, smallest first
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) uacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-        Eng::mma(uacc[ti], tf[p], xh[kb]);
         if constexpr (kSplit) {
           Eng::mma(uacc[ti], tf[p], xl[kb]);
           Eng::mma(uacc[ti], tl[p], xh[kb]);
+          Eng::mma(uacc[ti], tm[p], xm[kb]);
+          Eng::mma(uacc[ti], tf[p], xm[kb]);
+          Eng::mma(uacc[ti], tm[p], xh[kb]);
         }
+        Eng::mma(uacc[ti], tf[p], xh[kb]);
       }
       }  // kW
       // U' as the A operand of U'^T P^T, for the helper wave
@@ -623,7 +638,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       }
     } else {
       if (c + 1 < n_chunks) {
-        issue_p(c + 1, pn);  // the other P buffer
+        if constexpr (Ls::PBUF == 2) issue_p(c + 1, pn);  // the other P buffer
         if (hw == 0) fetch_g(c + 1);
       }
       transform(kc, kt);
@@ -660,8 +675,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 
     // ======== phase 1b ========
     if (chain) {
-      // S^T <- exp(gamma_C) S^T + K^T (exp(gamma_C - gamma) * U')
-      Fr bh[2], bl[2];
+      // S^T <- exp(gamma_C) S^T + K^T (exp(gamma_C - gamma) * U'), the
+      // decayed U' as three bf16 planes (K enters exactly)
+      Fr bh[2], bm[2], bl[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const float4 e0 = *reinterpret_cast<const float4*>(gegc + 32 * kb + 4 * gq);
@@ -670,7 +686,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
                              e0.w * uacc[2 * kb][3], e1.x * uacc[2 * kb + 1][0],
                              e1.y * uacc[2 * kb + 1][1], e1.z * uacc[2 * kb + 1][2],
                              e1.w * uacc[2 * kb + 1][3]};
-        Eng::split(u8, bh[kb], bl[kb]);
+        Eng::split3(u8, bh[kb], bm[kb], bl[kb]);
       }
       float aC = st_coded ? gmisc[0] * s_cur : gmisc[0];  // decay, and the scale of a coded state
       if constexpr (kFused) aC *= gmisc[2];  // NaN after a failed wait for a ready flag
@@ -702,12 +718,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const Fr a0 = ka0[t], a1 = ka1[t];
-        Eng::mma(st[t], a0, bh[0]);
-        Eng::mma(st[t], a1, bh[1]);
         if constexpr (kSplit) {
           Eng::mma(st[t], a0, bl[0]);
           Eng::mma(st[t], a1, bl[1]);
+          Eng::mma(st[t], a0, bm[0]);
+          Eng::mma(st[t], a1, bm[1]);
         }
+        Eng::mma(st[t], a0, bh[0]);
+        Eng::mma(st[t], a1, bh[1]);
       }
       if (args.bound_pre) {
         const int bidx = bound0 + c;
@@ -825,6 +843,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       }
       if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
     } else {
+      // one P buffer: every helper has read it in phase 1b; the next chunk's P lands before the barrier
+      if constexpr (Ls::PBUF == 1) {
+        if (c + 1 < n_chunks) issue_p(c + 1, pb);
+      }
       if (c + 1 < n_chunks && hw == 0) scan(c + 1, vec);  // gates of the next chunk
       wait_vmem();  // this wave's loads (k of the next chunk included) are in LDS before the barrier
       if constexpr (kFused) {
@@ -839,7 +861,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     E* k0 = sK;
     E* k1 = sK + 64 * DK;
     E* p0 = sP;
-    E* p1 = sP + 6 * NP * 64 * 8;
+    E* p1 = sP + (Ls::PBUF - 1) * 6 * NP * 64 * 8;
     step(c, odd ? k1 : k0, sQ, sT, sV, odd ? p1 : p0, odd ? p0 : p1, sXU, sXS,
          Eng::kTrRead ? nullptr : sKT, sG2, sRed, sW);
   }

@@ -111,6 +111,19 @@ struct EngBF16 {
     hi = __builtin_bit_cast(Fr, make_uint4(h[0], h[1], h[2], h[3]));
     lo = __builtin_bit_cast(Fr, make_uint4(l[0], l[1], l[2], l[3]));
   }
+  // three planes: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid)
+  // (24 significant bits)
+  static __device__ __forceinline__ void split3(const float (&x)[8], Fr& hi, Fr& mid, Fr& lo) {
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+      split_bf16x2(x[2 * j] - bf16_lo(h[j]), x[2 * j + 1] - bf16_hi(h[j]), m[j], l[j]);
+    }
+    hi = __builtin_bit_cast(Fr, make_uint4(h[0], h[1], h[2], h[3]));
+    mid = __builtin_bit_cast(Fr, make_uint4(m[0], m[1], m[2], m[3]));
+    lo = __builtin_bit_cast(Fr, make_uint4(l[0], l[1], l[2], l[3]));
+  }
   // fragment from two 4-element pieces (k slots 0..3 and 4..7)
   static __device__ __forceinline__ Fr ld2(const E* a, const E* b) {
     const uint2 u = *reinterpret_cast<const uint2*>(a);
@@ -162,6 +175,11 @@ struct EngF32 {
   }
   static __device__ __forceinline__ void split(const float (&x)[8], Fr& hi, Fr& lo) {
     hi = round(x);
+    (void)lo;
+  }
+  static __device__ __forceinline__ void split3(const float (&x)[8], Fr& hi, Fr& mid, Fr& lo) {
+    hi = round(x);
+    (void)mid;
     (void)lo;
   }
   static __device__ __forceinline__ Fr ld2(const E* a, const E* b) {

@@ -86,7 +86,7 @@ struct KdaLds {
   static constexpr size_t oRed = oEC + DK * sizeof(float);
   static constexpr size_t oW = oRed + 8 * sizeof(float);
   static constexpr size_t bytes = oW + (kW ? (size_t)w_rec_bytes(DK) : 0);
-  static_assert(6 * NP * F == kTRecBytes, "record and its LDS copy differ");
+  static_assert(6 * NP * F == kPRecBytes && 6 * NP * F <= kTRecBytes, "records and their LDS copies differ");
   static_assert(oW % 16 == 0, "direct loads need 16-byte aligned LDS");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
   static_assert((3 * DK + 64 + 8) * sizeof(float) <= oV, "suffix buffers do not fit");
@@ -364,12 +364,12 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
                      lds_of(sV) + i * RPI * (PPV + 1) * EPP * (int)sizeof(E));
       }
     }
-    const int64_t rec = ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
-    const char* trec = reinterpret_cast<const char*>(args.T) + rec;
-    const char* prec = reinterpret_cast<const char*>(args.Prec) + rec;
+    // T: its first two planes (hi, mid), P: both of its planes
+    const char* trec = reinterpret_cast<const char*>(args.T) + ((int64_t)(chunk0 + cc) * H + h) * kTRecBytes;
+    const char* prec = reinterpret_cast<const char*>(args.Prec) + ((int64_t)(chunk0 + cc) * H + h) * kPRecBytes;
 #pragma unroll
-    for (int ii = 0; ii < kTRecBytes / 1024 / 4; ++ii) {
-      const int idx = w * (kTRecBytes / 1024 / 4) + ii;
+    for (int ii = 0; ii < kPRecBytes / 1024 / 4; ++ii) {
+      const int idx = w * (kPRecBytes / 1024 / 4) + ii;
       lds_load16(trec, (uint32_t)((idx * 64 + lane) * 16), lds_of(sT) + idx * 1024);
       lds_load16(prec, (uint32_t)((idx * 64 + lane) * 16), lds_of(sP) + idx * 1024);
     }

@@ -33,9 +33,12 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             void* workspace, const gdn_debug_t* debug, hipStream_t stream);
 
 // Two records per (chunk, head): T = (I + A)^-1 diag(beta) and the decayed,
-// masked P = Q K^T, each in MFMA fragment order (see gdn_prep.hip), 12 KiB
-// for both engines.
-constexpr int kTRecBytes = 12288;
+// masked P = Q K^T, each in MFMA fragment order (see gdn_prep.hip).  T: three
+// bf16 planes (hi, mid, lo: 24 significant bits, so the state update keeps
+// fp32 accuracy) or fp32, in an 18 KiB slot; P: two bf16 planes (hi, lo: it
+// only reaches the outputs) or fp32, 12 KiB.
+constexpr int kTRecBytes = 18432;
+constexpr int kPRecBytes = 12288;
 
 // With W QDQ, a third record per (chunk, head): the E4M3 codes of the
 // row-quantized W = T (K * exp(gamma)) as bf16 values (exact), in the
@@ -49,7 +52,8 @@ constexpr int w_rec_bytes(int dk) { return dk * 128 + 1024; }
 // offsets [N + 1] and the largest chunk count of a sequence (padded to 256
 // bytes), one uint32 ready flag per
 // (chunk, head) (padded to 256 bytes; used by the fused launch), then the T
-// records, the P records and, with W QDQ, the W records, all sized for the
+// records (kTRecBytes each), the P records (kPRecBytes each) and, with W QDQ,
+// the W records, all sized for the
 // worst-case chunk count ceil(total_tokens / 64) + N.
 struct PrepLayout {
   int32_t* status;

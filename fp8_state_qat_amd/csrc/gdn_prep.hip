@@ -15,14 +15,16 @@
 // offsets [N + 1] (prefix sums of ceil(P_n / 64)) and the largest chunk count
 // of a sequence, padded to 256 bytes; one uint32 ready flag per (chunk, head) (used by the fused launch of
 // the scalar-gate kernel), padded to 256 bytes; then one 12 KiB T record per
-// (chunk, head), then one P record per (chunk, head) of the same layout, then
-// with W QDQ one W record per (chunk, head) (layout in gdn_launch.hpp).  A
-// record holds the six nonzero 16 x 32 fragments of a block lower-triangular
-// 64 x 64 matrix M, pair p = (ti, kb) in (0,0) (1,0) (2,0) (3,0) (2,1) (3,1):
-// lane l of fragment p holds M[16 ti + l % 16][32 kb + kperm(l / 16, j)] for
-// j = 0..7 (kperm as in gdn_device.hpp), fragments stored one after the
-// other, lane-major.  bf16 inputs store hi = bf16(M) (six fragments) then
-// lo = bf16(M - hi) (six more); fp32 inputs store M in fp32.  The sequential
+// (chunk, head) (18 KiB slots), then one P record per (chunk, head) of the
+// same layout (12 KiB), then with W QDQ one W record per (chunk, head)
+// (layout in gdn_launch.hpp).  A record holds the six nonzero 16 x 32
+// fragments of a block lower-triangular 64 x 64 matrix M, pair p = (ti, kb)
+// in (0,0) (1,0) (2,0) (3,0) (2,1) (3,1): lane l of fragment p holds
+// M[16 ti + l % 16][32 kb + kperm(l / 16, j)] for j = 0..7 (kperm as in
+// gdn_device.hpp), fragments stored one after the other, lane-major.  bf16
+// inputs store planes of six fragments each: hi = bf16(M), then mid =
+// bf16(M - hi), and for T a third, lo = bf16(M - hi - mid) (24 significant
+// bits in all); fp32 inputs store M in fp32.  The sequential
 // kernels copy a record into LDS unchanged and read each fragment with one
 // lane-linear load (T as the A operand of T X, P as the B operand of
 // U'^T P^T).
@@ -185,9 +187,9 @@ PrepLayout prep_layout(const gdn_shape_t& s, void* workspace) {
     L.ready = reinterpret_cast<unsigned*>(w + offs_bytes);
     L.T = w + offs_bytes + ready_bytes;
     L.P = w + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes;
-    if (w_bytes) L.W = w + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2;
+    if (w_bytes) L.W = w + offs_bytes + ready_bytes + (size_t)L.items * (kTRecBytes + kPRecBytes);
   }
-  L.bytes = kStatusBytes + offs_bytes + ready_bytes + (size_t)L.items * kTRecBytes * 2 + w_bytes;
+  L.bytes = kStatusBytes + offs_bytes + ready_bytes + (size_t)L.items * (kTRecBytes + kPRecBytes) + w_bytes;
   return L;
 }
 

@@ -108,8 +108,9 @@ __device__ __forceinline__ void solve_unit_lower(const float* sA, float* sX, int
 // kL64, zeros above the diagonal of its diagonal blocks), times diag(colscale)
 // when colscale is not null, as one record in MFMA fragment order, on the
 // four waves whose item thread index is tid (0..255).
-template <bool kBF>
+template <bool kBF, int kPl = 2>
 __device__ __forceinline__ void store_record(const float* M, const float* colscale, char* rec, int tid) {
+  static_assert(kPl == 2 || kPl == 3, "two or three bf16 planes");
   constexpr int L64 = kL64;
   for (int slot = tid; slot < 6 * 64; slot += kThreads) {
     const int p = slot >> 6, l = slot & 63, g4 = l >> 4;
@@ -129,12 +130,20 @@ __device__ __forceinline__ void store_record(const float* M, const float* colsca
       t8[4 * half + 3] = x4.w * b4.w;
     }
     if constexpr (kBF) {
-      uint32_t hv[4], lv[4];
+      uint32_t hv[4], mv[4], lv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) split_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], lv[q]);
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (kPl == 3) {
+          hv[q] = pack_bf16x2(t8[2 * q], t8[2 * q + 1]);
+          split_bf16x2(t8[2 * q] - bf16_lo(hv[q]), t8[2 * q + 1] - bf16_hi(hv[q]), mv[q], lv[q]);
+        } else {
+          split_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], mv[q]);
+        }
+      }
       uint4* dst = reinterpret_cast<uint4*>(rec);
       dst[p * 64 + l] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-      dst[(6 + p) * 64 + l] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+      dst[(6 + p) * 64 + l] = make_uint4(mv[0], mv[1], mv[2], mv[3]);
+      if constexpr (kPl == 3) dst[(12 + p) * 64 + l] = make_uint4(lv[0], lv[1], lv[2], lv[3]);
     } else {
       float4* dst = reinterpret_cast<float4*>(rec) + 2 * (p * 64 + l);
       dst[0] = make_float4(t8[0], t8[1], t8[2], t8[3]);
@@ -336,7 +345,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t
   // whole 16-byte slots and every store instruction whole cache lines.
   // Waves: 0 takes pairs 0 and 5, 1 pairs 1 and 4, 2 pair 2, 3 pair 3 (three
   // nonzero tiles at most per wave).
-  char* prec = reinterpret_cast<char*>(a.P) + ((int64_t)j * H + h) * kTRecBytes;
+  char* prec = reinterpret_cast<char*>(a.P) + ((int64_t)j * H + h) * kPRecBytes;
   if (active) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -383,7 +392,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t
   __syncthreads();
 
   solve_unit_lower(sA, sX, tid, active);
-  if (active) store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes, tid);
+  if (active) store_record<kBF, 3>(sX, sBeta, reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes, tid);
 
   if constexpr (kW) {
     // ---- W = X diag(beta exp(gamma)) K on the MFMA: wave w forms rows
@@ -786,10 +795,9 @@ __device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, i
   }
   __syncthreads();
 
-  const int64_t rec = ((int64_t)j * H + h) * kTRecBytes;
-  store_record<kBF>(sP, nullptr, reinterpret_cast<char*>(a.P) + rec, tid);
+  store_record<kBF>(sP, nullptr, reinterpret_cast<char*>(a.P) + ((int64_t)j * H + h) * kPRecBytes, tid);
   solve_unit_lower(sA, sX, tid);
-  store_record<kBF>(sX, sBeta, reinterpret_cast<char*>(a.T) + rec, tid);
+  store_record<kBF, 3>(sX, sBeta, reinterpret_cast<char*>(a.T) + ((int64_t)j * H + h) * kTRecBytes, tid);
 
   if constexpr (kW) {
     // ---- W = X diag(beta) (K o exp(gamma)) on the fp32 MFMA (the second

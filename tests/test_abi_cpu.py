@@ -90,14 +90,15 @@ def test_chunk_fwd_rejects_null_and_misaligned():
 
 def test_workspace_size_and_checks():
     """Workspace: for the worst-case chunk count ceil(T/64) + N, two records
-    of 12 KiB (T and P) per chunk and head, one ready flag per chunk and head,
-    the chunk offsets and the status word, each region padded to 256 bytes;
-    too small, NULL or misaligned is rejected."""
+    per chunk and head (T in an 18 KiB slot: three bf16 planes; P: 12 KiB),
+    one ready flag per chunk and head, the chunk offsets and the status word,
+    each region padded to 256 bytes; too small, NULL or misaligned is
+    rejected."""
     s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
     n = _ws(s)
-    assert n == 256 + 256 + 256 + (3 + 3) * 2 * 2 * 12288   # status, offsets, flags, records
+    assert n == 256 + 256 + 256 + (3 + 3) * 2 * (18432 + 12288)   # status, offsets, flags, records
     big = _shape(n_seqs=70, n_heads=3, total_tokens=64 * 100)   # 72 offsets, 510 flags
-    assert _ws(big) == 256 + 512 + 2048 + 170 * 3 * 2 * 12288
+    assert _ws(big) == 256 + 512 + 2048 + 170 * 3 * (18432 + 12288)
     assert _ws(_shape(n_seqs=3, n_heads=2, total_tokens=130, gate_per_channel=1)) == n
     assert _ws(_shape(dv=96)) == 0 and _lib.last_error()
     assert _chunk(s, ws_bytes=n - 1) == 1

@@ -13,7 +13,7 @@ import pytest
 
 from fp8_state_qat_amd import inputs as gi
 
-from helpers import (TOL, check_g1, check_g2, check_prefix_suffix, rel_l2, run_chunk_gpu,
+from helpers import (KDA_CODES, TOL, check_codes, check_g1, check_g2, check_prefix_suffix, rel_l2, run_chunk_gpu,
                      run_chunk_oracle, teacher_forced)
 
 pytestmark = pytest.mark.gpu
@@ -53,7 +53,7 @@ def test_kda_bf16_qdq_off(d, o_dtype):
 def test_kda_bf16_qdq_on_teacher_forced(d, dv):
     w = _kda([300, 129, 1], 2, d, dv, gi.BF16, seed=43 + d + dv)
     gpu = run_chunk_gpu(w, 3, o_dtype="f32", record=True)
-    check_g2(w, gpu, 3, TOL[gi.BF16])
+    check_g2(w, gpu, 3, TOL[gi.BF16], codes=KDA_CODES)
     ref = run_chunk_oracle(w, 3)
     print(f"free-running QDQ on (reported): o_rel={rel_l2(gpu['o'], ref['o']):.3e} "
           f"S_rel={rel_l2(gpu['S'], ref['S']):.3e}", flush=True)
@@ -107,7 +107,7 @@ def test_kda_prefix_suffix_bf16(flags):
     both teacher-forced (per boundary, per suffix token)."""
     w = _kda([200, 100, 45], 2, 128, 128, gi.BF16, seed=67 + flags, prefix_lens=[130, 64, 0])
     gpu = run_chunk_gpu(w, flags, o_dtype="f32", record=True, suffix_record=True)
-    check_prefix_suffix(w, gpu, flags, TOL[gi.BF16])
+    check_prefix_suffix(w, gpu, flags, TOL[gi.BF16], codes=KDA_CODES)
 
 
 def test_kda_initial_state_fp32():
@@ -149,3 +149,4 @@ def test_full_size_kda_prefill_sampled(flags):
         print("G2 sampled", r, flush=True)
         assert r["o_rel"] <= TOL[gi.BF16] and r["pre_rel"] <= TOL[gi.BF16]
         assert r["gpu_code_mismatch"] == 0 and r["scale_mismatch"] == 0
+        check_codes(r, **KDA_CODES)
