@@ -28,7 +28,10 @@ GDN_SCHEDULE_SPLIT = 1
 GDN_SCHEDULE_FUSED = 2
 GDN_SCHEDULE_FUSED_NO_PRODUCERS = 3   # test hook: every wait for a ready flag runs out
 
-EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_workspace_status", "gdn_state_qdq",
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES
+
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_workspace_bytes", "gdn_workspace_status",
+           "gdn_state_qdq",
            "gdn_state_qdq_int8", "gdn_decode_step", "gdn_chunk_bwd_dh", "gdn_chunk_bwd_workspace_bytes",
            "gdn_status_string", "gdn_last_error")
 
@@ -88,6 +91,9 @@ def lib():
     L.gdn_chunk_fwd.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, ctypes.c_size_t, ctypes.POINTER(GdnDebug), _vp]
     L.gdn_chunk_fwd.restype = ctypes.c_int
+    L.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GdnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, ctypes.POINTER(GdnDebug), _vp]
+    L.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     L.gdn_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(GdnShape)]
     L.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     L.gdn_state_qdq.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]

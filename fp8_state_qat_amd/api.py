@@ -90,7 +90,7 @@ def workspace_status(workspace):
 
 def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
               initial_state=None, qdq_flags=GDN_QDQ_CHUNK | GDN_QDQ_WRITE, o_dtype=None,
-              out=None, final_state=None, workspace=None, debug=None, check_status=False):
+              out=None, final_state=None, workspace=None, debug=None, check_status=False, noalloc=False):
     """gdn_chunk_fwd.  q, k: [T, H, dk]; v: [T, H, dv] (fp32 or bf16); beta:
     [T, H] fp32; g: [T, H] or [T, H, dk] fp32; cu_seqlens: [N+1] int32;
     seq_lens, prefix_lens: [N] int32 or None; initial_state: [N, H, dv, dk]
@@ -110,7 +110,15 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     kernel's launch; _FUSED_NO_PRODUCERS, a test hook whose bounded waits all
     run out).  check_status: read the workspace's status word after the call
     (synchronizes; raises GdnError on a device-side failure).
+    noalloc: call gdn_chunk_fwd_noalloc instead, whose workspace is the
+    library's static per-GPU scratch (out and final_state must be given, no
+    workspace; the status word comes back through debug["status"]).
     Returns (o, final_state)."""
+    if noalloc:
+        if workspace is not None or check_status:
+            raise ValueError("noalloc takes no workspace (pass debug['status'] for the status word)")
+        if out is None or final_state is None:
+            raise ValueError("noalloc needs out and final_state")
     _dev(k, "k")
     if k.dim() != 3:
         raise ValueError(f"k must be [T, H, dk], got shape {tuple(k.shape)}")
@@ -146,15 +154,16 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     if final_state is None:
         final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=k.device)
     shape = _shape(N, H, dk, dv, T, k.dtype, o_dtype, per_channel, qdq_flags)
-    ws_bytes = _lib.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape))
-    if ws_bytes == 0:
-        _lib.check(_lib.GDN_ERR_INVALID_ARG)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
-    _dev(workspace, "workspace", torch.uint8)
-    _on_device(k=k, workspace=workspace)
-    if workspace.dim() != 1:
-        raise ValueError("workspace must be a 1-D uint8 tensor")
+    if not noalloc:
+        ws_bytes = _lib.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape))
+        if ws_bytes == 0:
+            _lib.check(_lib.GDN_ERR_INVALID_ARG)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
+        _dev(workspace, "workspace", torch.uint8)
+        _on_device(k=k, workspace=workspace)
+        if workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
     dbg = None
     if debug is not None:
         unknown = set(debug) - {"bound_offsets", "bound_pre", "bound_post", "scales", "kernel_start",
@@ -192,11 +201,14 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
                        _ptr(debug.get("w_pre")), _ptr(debug.get("w_post")),
                        _ptr(debug.get("suffix_offsets")), _ptr(debug.get("suffix_pre")),
                        _ptr(debug.get("suffix_post")), _ptr(debug.get("status")))
-    st = _lib.lib().gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                                  _ptr(g), _ptr(cu_seqlens), _ptr(seq_lens), _ptr(prefix_lens),
-                                  _ptr(initial_state), _ptr(out), _ptr(final_state),
-                                  _ptr(workspace), workspace.numel(),
-                                  ctypes.byref(dbg) if dbg is not None else None, _stream())
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(cu_seqlens), _ptr(seq_lens), _ptr(prefix_lens),
+            _ptr(initial_state), _ptr(out), _ptr(final_state))
+    dbg_p = ctypes.byref(dbg) if dbg is not None else None
+    if noalloc:
+        st = _lib.lib().gdn_chunk_fwd_noalloc(ctypes.byref(shape), *args, dbg_p, _stream())
+    else:
+        st = _lib.lib().gdn_chunk_fwd(ctypes.byref(shape), *args, _ptr(workspace), workspace.numel(), dbg_p,
+                                      _stream())
     _lib.check(st)
     if check_status:
         workspace_status(workspace)

@@ -10,6 +10,11 @@
 #include "gdn.h"
 #include "gdn_launch.hpp"
 
+// Workspace of gdn_chunk_fwd_noalloc: one array on every GPU the library runs
+// on, held until the process ends.  In host code `scratch` is only a stand-in
+// symbol; its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -43,6 +48,19 @@ gdn_status_t check_device() {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Device address of `scratch` on the current device (dev), looked up on the
+// first call on that device and kept; null when the lookup fails.
+std::atomic<void*> g_scratch[kMaxDevices];
+
+void* scratch_address(int dev) {
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
 
 gdn_status_t check_shape(const gdn_shape_t* s, bool decode) {
   if (s == nullptr) return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
@@ -172,22 +190,20 @@ size_t gdn_chunk_fwd_workspace_bytes(const gdn_shape_t* shape) {
   return gdn::prep_workspace_bytes(*shape);
 }
 
-gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
-                           const float* beta, const float* g, const int32_t* cu_seqlens,
-                           const int32_t* seq_lens, const int32_t* prefix_lens,
-                           const float* initial_state, void* o, float* final_state,
-                           void* workspace, size_t workspace_bytes,
-                           const gdn_debug_t* debug, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Host checks of gdn_chunk_fwd and gdn_chunk_fwd_noalloc other than the
+// workspace and the device.
+gdn_status_t check_chunk_args(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                              const float* beta, const float* g, const int32_t* cu_seqlens,
+                              const float* initial_state, const void* o, const float* final_state,
+                              const gdn_debug_t* debug) {
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
   if (shape->qdq_flags & GDN_QDQ_INT8)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_INT8 is a decode-step codec (gdn_decode_step, gdn_state_qdq_int8)");
-  const size_t need = gdn::prep_workspace_bytes(*shape);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
-                workspace ? "" : ", NULL");
-  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (!cu_seqlens || !final_state) return fail(GDN_ERR_INVALID_ARG, "cu_seqlens and final_state must be non-NULL");
   if (shape->total_tokens > 0 && (!q || !k || !v || !beta || !g || !o))
     return fail(GDN_ERR_INVALID_ARG, "q, k, v, beta, g and o must be non-NULL");
@@ -208,14 +224,69 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* 
     return fail(GDN_ERR_INVALID_ARG, "debug schedule must be GDN_SCHEDULE_AUTO, _SPLIT, _FUSED or _FUSED_NO_PRODUCERS");
   if (shape->io_dtype == GDN_F32 && shape->dk != 64)
     return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs are supported with dk = 64 only");
-  st = check_device();
-  if (st != GDN_OK) return st;
+  return GDN_OK;
+}
+
+gdn_status_t run_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, const int32_t* cu_seqlens,
+                           const int32_t* seq_lens, const int32_t* prefix_lens,
+                           const float* initial_state, void* o, float* final_state,
+                           void* workspace, const gdn_debug_t* debug, void* stream) {
   hipError_t e = gdn::launch_chunk_fwd(*shape, q, k, v, beta, g, cu_seqlens, seq_lens, prefix_lens,
                                        initial_state, o, final_state, workspace, debug,
                                        (hipStream_t)stream);
   if (e == hipErrorNotSupported) return fail(GDN_ERR_UNSUPPORTED, "configuration not supported");
   if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, const int32_t* cu_seqlens,
+                           const int32_t* seq_lens, const int32_t* prefix_lens,
+                           const float* initial_state, void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes,
+                           const gdn_debug_t* debug, void* stream) {
+  g_err[0] = 0;
+  gdn_status_t st = check_chunk_args(shape, q, k, v, beta, g, cu_seqlens, initial_state, o, final_state, debug);
+  if (st != GDN_OK) return st;
+  const size_t need = gdn::prep_workspace_bytes(*shape);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  st = check_device();
+  if (st != GDN_OK) return st;
+  return run_chunk_fwd(shape, q, k, v, beta, g, cu_seqlens, seq_lens, prefix_lens, initial_state, o, final_state,
+                       workspace, debug, stream);
+}
+
+gdn_status_t gdn_chunk_fwd_noalloc(const gdn_shape_t* shape, const void* q, const void* k, const void* v,
+                                   const float* beta, const float* g, const int32_t* cu_seqlens,
+                                   const int32_t* seq_lens, const int32_t* prefix_lens,
+                                   const float* initial_state, void* o, float* final_state,
+                                   const gdn_debug_t* debug, void* stream) {
+  g_err[0] = 0;
+  gdn_status_t st = check_chunk_args(shape, q, k, v, beta, g, cu_seqlens, initial_state, o, final_state, debug);
+  if (st != GDN_OK) return st;
+  const size_t need = gdn::prep_workspace_bytes(*shape);
+  if (need > GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of workspace; the static scratch holds %zu "
+                "(use gdn_chunk_fwd with a caller-owned workspace)",
+                need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  st = check_device();
+  if (st != GDN_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(GDN_ERR_DEVICE, "no current HIP device");
+  void* ws = scratch_address(dev);
+  if (ws == nullptr) return fail(GDN_ERR_DEVICE, "hipGetSymbolAddress of the static scratch failed on device %d", dev);
+  return run_chunk_fwd(shape, q, k, v, beta, g, cu_seqlens, seq_lens, prefix_lens, initial_state, o, final_state,
+                       ws, debug, stream);
 }
 
 size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape_t* shape) {

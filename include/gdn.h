@@ -181,6 +181,32 @@ gdn_status_t gdn_chunk_fwd(const gdn_shape_t* shape,
                            const gdn_debug_t* debug, void* stream);
 
 /*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and checks as gdn_chunk_fwd,
+ * without the workspace: the call uses a static device array of
+ * GDN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, and calls no allocating routine.
+ *   - A shape whose gdn_chunk_fwd_workspace_bytes exceeds
+ *     GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_UNSUPPORTED before anything is
+ *     launched (use gdn_chunk_fwd with a caller workspace).
+ *   - Every call on a GPU shares that GPU's array: calls that overlap in time
+ *     on one GPU (other streams, other threads) race.  Each call clears what
+ *     must start at zero; the array keeps the last call's contents.
+ *   - The call's status word lives in the array: pass debug->status to receive
+ *     it on the stream (gdn_workspace_status has no pointer to read).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status_t gdn_chunk_fwd_noalloc(const gdn_shape_t* shape,
+                                   const void* q, const void* k, const void* v,
+                                   const float* beta, const float* g,
+                                   const int32_t* cu_seqlens, const int32_t* seq_lens,
+                                   const int32_t* prefix_lens,
+                                   const float* initial_state,
+                                   void* o, float* final_state,
+                                   const gdn_debug_t* debug, void* stream);
+
+/*
  * gdn_workspace_status -- the status word a gdn_chunk_fwd or gdn_chunk_bwd_dh
  * call left in its workspace.  Reads the 4 bytes at the workspace's start on
  * `stream` (the stream of that call) and synchronizes it, so it is not for

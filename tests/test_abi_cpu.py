@@ -214,3 +214,24 @@ def test_chunk_bwd_dh_checks():
     assert _bwd(_shape(), dh=0, d0=0) == 1
     assert _bwd(_shape(), q=FAKE + 8) == 1
     assert _bwd(_shape(), ws_bytes=100) == 1
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """gdn_chunk_fwd_noalloc runs in the library's static 64 MiB scratch: a
+    shape whose workspace is larger is refused on the host (UNSUPPORTED,
+    nothing launched); argument checks are those of gdn_chunk_fwd."""
+    L = _lib.lib()
+    p = ctypes.c_void_p
+    big = _shape(n_seqs=4, n_heads=16, total_tokens=4 * 4096)   # about 124 MiB of records
+    assert _ws(big) > _lib.NOALLOC_SCRATCH_BYTES
+    args = [p(FAKE)] * 6 + [None, None, None, p(FAKE), p(FAKE), None, None]
+    assert L.gdn_chunk_fwd_noalloc(ctypes.byref(big), *args) == 2
+    assert "scratch" in _lib.last_error()
+    small = _shape(n_seqs=2, n_heads=4, total_tokens=1000)
+    assert _ws(small) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert L.gdn_chunk_fwd_noalloc(ctypes.byref(_shape(dv=96)), *args) == 1
+    bad = [p(FAKE + 8)] + [p(FAKE)] * 5 + [None, None, None, p(FAKE), p(FAKE), None, None]   # misaligned q
+    assert L.gdn_chunk_fwd_noalloc(ctypes.byref(small), *bad) == 1
+    assert "misaligned" in _lib.last_error()
+    if not HAS_GPU:
+        assert L.gdn_chunk_fwd_noalloc(ctypes.byref(small), *args) == 3   # no device here
