@@ -228,6 +228,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-kda", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="the headline prefill step alone (for profiler runs): no other workloads, no CPU baseline")
     ap.add_argument("--cpu-pairs", type=int, default=64,
                     help="(sequence, head) pairs the oracle runs (64 = the whole workload)")
     ap.add_argument("--cpu-repeats", type=int, default=3)
@@ -240,6 +242,8 @@ def main():
                                    "not part of it", "n_gpus": args.gpus}))
         sys.exit(2)
 
+    if args.only_prefill:
+        args.no_decode = args.no_kda = args.no_varlen = args.no_cpu_baseline = True
     import torch
     from fp8_state_qat_amd import api, inputs as gi
     from fp8_state_qat_amd._lib import GDN_QDQ_CHUNK, GDN_QDQ_W, GDN_QDQ_WRITE, GDN_SCHEDULE_SPLIT
@@ -305,7 +309,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                 "traffic": traffic,
-                "kernel": "chunk_fwd_kernel<128, EngBF16, bf16, bf16, fused> (128 producer + 128 state workgroups)",
+                "kernel": "chunk_bf16_kernel<128, bf16 out, fused> (128 producer + 128 state workgroups)",
                 "algorithmic_flops_per_launch": fl_all,
                 "flops_per_token_head": flops_per_token_head(64, dk, dv),
                 "avg_launch_ms": round(kern_ms, 5),
@@ -321,6 +325,11 @@ def main():
             "frac": round(step_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "algorithmic_flops_per_step": fl_all,
             "flops_per_token_head": flops_per_token_head(64, dk, dv)}
+
+    if args.only_prefill:
+        print(json.dumps({"metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
+                          "ms_per_step": round(ms_step, 5), "roofline": roofline}), flush=True)
+        return
 
     # QDQ off, same workload (reported)
     def step_off():
@@ -383,7 +392,7 @@ def main():
                        "tokens_per_s": round(tokens / (off_ms / args.steps * 1e-3), 1)},
            "split_schedule": {"ms_per_step": round(split_ms / args.steps, 5),
                               "tokens_per_s": round(tokens / (split_ms / args.steps * 1e-3), 1),
-                              "state_kernel": "chunk_fwd_kernel<128, EngBF16, bf16, bf16>",
+                              "state_kernel": "chunk_bf16_kernel<128, bf16 out>",
                               "state_kernel_avg_launch_ms": round(split_kern, 5),
                               "state_kernel_mfma_tflops": round(fl / (split_kern * 1e-3) / 1e12, 2),
                               "state_kernel_hbm_gbs": round(split_by / (split_kern * 1e-3) / 1e9, 1),

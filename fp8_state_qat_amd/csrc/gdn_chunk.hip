@@ -18,16 +18,17 @@
 // produce the outputs and stage the next chunk, so each SIMD runs one wave of
 // each kind and the two overlap.  With gamma the in-chunk cumulative log-gate
 // and s the scale of the state entering the chunk (1 when it is not coded),
-// one chunk of n <= 64 tokens (rows past n are zero) goes through three
+// one chunk of n <= 64 tokens (rows past n are zero) goes through two
 // phases separated by workgroup barriers:
 //
-//   1a  chain : X = V - s exp(gamma) * (K S^T), U' = T X            (MFMA)
+//   A   chain : X = V - s exp(gamma) * (K S^T), U' = T X            (MFMA)
 //       helper: s exp(gamma) * (Q S^T), from the state the chain left in LDS
-//   1b  chain : S^T <- exp(gamma_C) S^T + K^T diag(exp(gamma_C - gamma)) U'
-//               and the tile amax
-//       helper: O += P U', stored to o
-//   2   chain : QDQ: s = amax / 448, S <- RNE_E4M3(S / s) s
-//       helper: the gate scan of the next chunk
+//   B   chain : S^T <- exp(gamma_C) S^T + K^T diag(exp(gamma_C - gamma)) U'
+//               and the tile amax; the four chain waves exchange their amax
+//               through LDS among themselves (no workgroup barrier), then
+//               the QDQ: s = amax / 448, S <- RNE_E4M3(S / s) s
+//       helper: O += P U', stored to o; the gate scan of the next chunk and
+//               the wait for the next chunk's loads
 // T = (I + A)^-1 diag(beta) and P[r][s] = exp(gamma_r - gamma_s) q_r . k_s
 // (s <= r) arrive as records; the next chunk's k (two chunks ahead), q, v, T
 // and P arrive by direct global->LDS loads issued as soon as their buffers
@@ -65,7 +66,7 @@ constexpr int kHelperThreads = 256;  // waves 4..7
 //   K   2 x [tt][kb]  dump, double-buffered by chunk parity: lane l holds
 //                  k[16tt + l%16][32kb + 8(l/16) .. +7] in slot rot_slot(l);
 //                  A of K S^T, A of P, K^T by transpose reads   4 NKB fragments
-//   Q   [tt][kb]   the same for q (read in phase 1a only); B of S Q^T
+//   Q   [tt][kb]   the same for q (read in phase A only); B of S Q^T
 //   KT  [dt][kb]   dump: A of the state update (row = state row), 2 NT
 //                  fragments (fp32 engine; the bf16 engine reads these
 //                  fragments from K with transpose reads)
@@ -76,8 +77,11 @@ constexpr int kHelperThreads = 256;  // waves 4..7
 //                  parity (one buffer with W QDQ, whose W record needs the room)
 //   XU  [c][plane*2 + kb]     U' as the A operand of U'^T P^T, per chain wave
 //   XS  [c][plane*NKB + kb]   the state as the A operand of S Q^T, per chain wave
-//   vec (unused), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8]
-//   red the four chain waves' amax
+//   vec 2 x: (unused), exp(gamma), exp(gamma_C - gamma) [64] each; misc[8],
+//       by chunk parity (the next chunk's gates are scanned while the
+//       current ones are still read)
+//   red the four chain waves' amax by chunk parity [2][4], their tags [4]
+//       (the chunk each wave has published), the poison multiplier
 //   W   (kW only) the W record of the chunk as is: 4 NKB bf16 fragments of
 //       codes (A of W S^T, both engines), then the 64 row scales
 template <int DK, class Eng, bool kW = false>
@@ -97,8 +101,8 @@ struct Lds {
   static constexpr size_t oXU = oP + PBUF * 6 * NP * F;
   static constexpr size_t oXS = oXU + 4 * 2 * NP * F;
   static constexpr size_t oVec = oXS + 4 * NKB * NP * F;
-  static constexpr size_t oRed = oVec + (3 * 64 + 8) * sizeof(float);
-  static constexpr size_t oW = oRed + 8 * sizeof(float);
+  static constexpr size_t oRed = oVec + 2 * (3 * 64 + 8) * sizeof(float);
+  static constexpr size_t oW = oRed + 16 * sizeof(float);
   static constexpr size_t bytes = oW + (kW ? (size_t)w_rec_bytes(DK) : 0);
   static_assert(6 * NPT * F <= kTRecBytes && 6 * NP * F == kPRecBytes, "records and their LDS copies differ");
   static_assert(oW % 16 == 0, "direct loads need 16-byte aligned LDS");
@@ -106,75 +110,6 @@ struct Lds {
   static_assert(oK + (2 * DK + 64 + 8) * sizeof(float) <= oQ, "suffix buffers do not fit");
 };
 
-
-
-// Fused launch, workgroups 0 .. n_prep - 1: the T and P records of every
-// (chunk, head), two at a time (waves 0..3 and waves 4..7 each take one item).
-// Producer p serves the (sequence, head) pairs nh with nh % 8 == p % 8, in
-// chunk-major order: the R = n_prep / 8 producers of a class take its items
-// m = r, r + R, r + 2R, ... (r = p / 8), item m being chunk m / M of the
-// class's (m % M)-th pair, M the pairs in the class.  n_prep is a multiple
-// of 8 and the state part maps nh to blocks on XCD nh % 8, so producer and
-// consumers of a record share one L2: the record stores complete in that L2
-// (every wave waits for its stores, then the workgroup barrier), then the
-// flag is stored at device scope, past the L1.  A producer that finds itself
-// off its XCD writes its L2 back first and says so in the flag, and a
-// consumer on another XCD then invalidates its caches before reading
-// (device-scope release and acquire).  Producers never wait, so the
-// consumers' waits end once every producer has been dispatched; producers
-// have the lower workgroup ids.
-template <int DK, typename TIO, bool kW>
-__device__ __forceinline__ void produce_records(const ChunkArgs& args, char* smem) {
-  using IL = PrepItemLds<DK, TIO, kW>;
-  const int half = uniform((int)threadIdx.x >> 8), tid = threadIdx.x & 255;  // half: wave-uniform
-  char* lds = smem + half * IL::bytes;
-  PrepArgs a;
-  a.q = args.q; a.k = args.k; a.beta = args.beta; a.g = args.g; a.cu_seqlens = args.cu_seqlens;
-  a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
-  a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
-  a.W = const_cast<void*>(args.Wrec); a.w_pre = args.w_pre; a.w_post = args.w_post;
-  a.status = args.status;
-  const int H = args.H, NH = args.N * args.H;
-  const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
-  const unsigned xcd = xcd_id();
-  const bool home = xcd == (unsigned)x;
-  const int M = NH > x ? (NH - x + 7) >> 3 : 0;
-  const int64_t total = (int64_t)args.chunk_offs[args.N + 1] * M;
-  for (int64_t m0 = r; m0 < total; m0 += 2 * R) {
-    const int64_t m = m0 + (int64_t)half * R;
-    bool active = m < total;
-    int j = 0, h = 0, t0 = 0, nv = 0;
-    if (active) {
-      const int c = (int)(m / M), nh = x + 8 * (int)(m % M);
-      const int n = nh / H;
-      h = nh % H;
-      const int seg0 = args.cu_seqlens[n];
-      const int L = args.seq_lens ? args.seq_lens[n] : (args.cu_seqlens[n + 1] - seg0);
-      const int P = args.prefix_lens ? args.prefix_lens[n] : L;
-      active = c * kChunk < P;
-      if (active) {
-        j = args.chunk_offs[n] + c;
-        t0 = seg0 + c * kChunk;
-        nv = min(kChunk, P - c * kChunk);
-      }
-    }
-    // a fresh copy of the lane index per item keeps the compiler from holding
-    // the item's lane-dependent LDS addresses live across the whole loop
-    int tid_i = tid;
-    asm volatile("" : "+v"(tid_i));
-    prep_item<DK, TIO, kW>(a, j, h, t0, nv, lds, tid_i, active);
-    wait_vmem();      // this wave's record stores are complete
-    __syncthreads();  // ... in every wave of the item; the LDS blocks are free again
-    if (active && tid == 0) {
-      unsigned flag = 1u | (xcd << 1);
-      if (!home) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        flag |= kReadyReleased;
-      }
-      __hip_atomic_store(args.ready + ((int64_t)j * H + h), flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
 
 
 template <int DK, class Eng, typename TIO, typename TO, bool kFused, bool kW>
@@ -270,7 +205,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   Fr sh[NKB];            // after a chunk QDQ: the codes as the MFMA operand (bf16 engine)
   float s_cur = 1.0f;    // scale of the coded state
   bool st_coded = false; // bf16 engine after a chunk QDQ: st holds the E4M3 codes, the state is st * s_cur
-  f32x4 uacc[4];         // U'[16tt + 4gq + i][vcol0], phase 1a -> 1b
+  f32x4 uacc[4];         // U'[16tt + 4gq + i][vcol0], phase A -> B
 
   // uncoded state -> operand fragments: hi + lo (bf16 engine) / exact fp32
   auto state_frags = [&](Fr (&hi)[NKB], Fr (&lo)[NKB]) {
@@ -333,9 +268,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     }
   };
   // Loads of chunk cc, by buffer lifetime: k and P have two buffers (chunk
-  // parity); P of the next chunk is issued at the start of phase 1a, k two
-  // chunks ahead in phase 2 once the update has read it; v, T and q (one
-  // buffer each) in phase 1b, once phase 1a has read them.  In the loop the
+  // parity); P and k of the next chunk are issued at the start of phase A
+  // (k into the buffer of the previous chunk, whose update has read it; with
+  // one P buffer, P of the chunk itself, and k at the end of phase B); v, T
+  // and q (one buffer each) in phase B, once phase A has read them.  In the loop the
   // helper waves issue all of them; helper wave 0 fetches the log-gates into
   // a register.
   auto issue_k = [&](int cc, E* kdst, int wi) {
@@ -391,7 +327,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     vecb[128 + lane] = __builtin_amdgcn_exp2f((gC - x) * kLog2e);
     if (lane == 0) vecb[192] = __builtin_amdgcn_exp2f(gC * kLog2e);
   };
-  // fp32 engine, helper waves, phase 1a: the K^T dump of the current chunk
+  // fp32 engine, helper waves, phase A: the K^T dump of the current chunk
   // (fragment f = 2 dt + kb, lane l holds k[32 kb + kperm(l/16, j)][dkmap(16 dt + l%16)]).
   auto transform = [&](const E* kd, E* ktd) {
     if constexpr (!Eng::kTrRead) {
@@ -422,24 +358,26 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   auto load_ready = [&](int cc) { return __hip_atomic_load(ready_ptr(cc), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto read_ready = [&](int cc) { return (unsigned)__builtin_amdgcn_readfirstlane((int)load_ready(cc)); };
   const unsigned xcd_self = kFused ? xcd_id() : 0u;
-  auto poison = [&](float* vecb) {
+  float* const psn = sRed + 12;  // decay multiplier: 1, or NaN once a wait has run out
+  auto poison = [&]() {
     poisoned = true;
     if (lane == 0) {
-      vecb[194] = __builtin_nanf("");
+      *psn = __builtin_nanf("");
       report_wait_timeout(args.status);
     }
   };
-  auto await_ready = [&](int cc, unsigned v0, float* vecb) {
-    if (!poisoned && !await_ready_flag(ready_ptr(cc), v0, xcd_self)) poison(vecb);
+  auto await_ready = [&](int cc, unsigned v0) {
+    if (!poisoned && !await_ready_flag(ready_ptr(cc), v0, xcd_self)) poison();
   };
 
 
   // ---------------- prologue ----------------
+  if (tid < 12) sRed[tid] = 0.0f;  // amax slots, tags (0: no chunk published yet)
   if constexpr (kFused) {
+    if (hw == 1 && lane == 0) *psn = 1.0f;  // before this wave's own waits can poison it
     if (hw == 1 && n_chunks > 0) {
-      if (lane == 0) sG2[194] = 1.0f;
-      await_ready(0, read_ready(0), sG2);
-      if (n_chunks > 1) await_ready(1, read_ready(1), sG2);
+      await_ready(0, read_ready(0));
+      if (n_chunks > 1) await_ready(1, read_ready(1));
     }
     barrier_lds();
   }
@@ -476,13 +414,68 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
   }
   barrier_lds();
 
+  // The boundary QDQ of chunk c on the chain waves (rd: the four waves' amax
+  // of the chunk), the state fragments for the helpers' next S Q^T, the scale
+  // for the next chunk's gate vector vn, and the optional records.
+  auto chain_qdq = [&](const int c, const float* __restrict__ rd, E* __restrict__ xsb,
+                       float* __restrict__ vn, const bool do_qdq, const bool last) {
+    float s_new = 1.0f;
+    if (do_qdq) {
+      const float amax = fmaxf(fmaxf(rd[0], rd[1]), fmaxf(rd[2], rd[3]));
+      s_new = qdq_scale(amax);
+      const float r = 1.0f / s_new;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float c0[4], c1[4];
+        if constexpr (kSplit) {
+          // keep the codes; the scale is folded into the next decay multiply
+          e4m3_codes4(st[2 * kb], s_new, r, c0);
+          e4m3_codes4(st[2 * kb + 1], s_new, r, c1);
+          st[2 * kb] = f32x4{c0[0], c0[1], c0[2], c0[3]};
+          st[2 * kb + 1] = f32x4{c1[0], c1[1], c1[2], c1[3]};
+          const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+          sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
+        } else {
+          qdq4c(st[2 * kb], c0, s_new, r);
+          qdq4c(st[2 * kb + 1], c1, s_new, r);
+        }
+      }
+      s_cur = s_new;
+      st_coded = kSplit;
+    }
+    if (!last) {
+      if (kSplit && do_qdq) {
+        write_xs(xsb, sh, sh, false);
+      } else {
+        Fr hi[NKB], lo[NKB];
+        state_frags(hi, lo);
+        write_xs(xsb, hi, lo, true);
+        if constexpr (!kSplit) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];  // fp32 engine: the exact state
+        }
+      }
+      if (c4 == 0 && lane == 0) vn[193] = s_new;  // the scale of the state entering the next chunk
+    }
+    const int bidx = bound0 + c;
+    if (args.bound_post) {
+      const float f = st_coded ? s_cur : 1.0f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
+                                   dkmap(16 * t + 4 * gq)) = make_float4(st[t][0] * f, st[t][1] * f,
+                                                                         st[t][2] * f, st[t][3] * f);
+    }
+    if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
+  };
+
   // One chunk.  Every LDS buffer it touches arrives as a __restrict__
   // pointer, so the compiler can tell the buffers apart and does not hold LDS
   // reads behind the direct loads in flight into other buffers.
-  auto step = [&](const int c, E* __restrict__ kc, E* __restrict__ qc, E* __restrict__ tb,
-                  E* __restrict__ vb, E* __restrict__ pb, E* __restrict__ pn, E* __restrict__ xu,
-                  E* __restrict__ xs, E* __restrict__ kt, float* __restrict__ vec,
-                  float* __restrict__ red, uint16_t* __restrict__ wb) {
+  auto step = [&](const int c, E* __restrict__ kc, E* __restrict__ kn, E* __restrict__ qc,
+                  E* __restrict__ tb, E* __restrict__ vb, E* __restrict__ pb, E* __restrict__ pn,
+                  E* __restrict__ xu, E* __restrict__ xs, E* __restrict__ kt, float* __restrict__ vec,
+                  float* __restrict__ vecn, float* __restrict__ red, uint16_t* __restrict__ wb) {
     float* geg = vec + 64;    // exp(gamma)
     float* gegc = vec + 128;  // exp(gamma_C - gamma)
     float* gmisc = vec + 192; // [0] exp(gamma_C), [1] scale of the state entering the chunk
@@ -494,8 +487,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     const bool last = (c == n_chunks - 1);
     const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
 
-    f32x4 oacc[4];  // helper waves: O^T of this chunk, phase 1a -> 1b
-    // ======== phase 1a ========
+    f32x4 oacc[4];  // helper waves: O^T of this chunk, phase A -> B
+    // ======== phase A ========
     if (chain) {
       // K S^T: A = K rows (tokens), B = the state
       const float sc = coded_in ? s_cur : 1.0f;
@@ -637,13 +630,18 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         if constexpr (kSplit) Eng::st(slot(xu, c4 * 2 * NP + 2 + kb), ul);
       }
     } else {
+      if constexpr (Ls::PBUF == 1) {
+        if (c > 0) issue_p(c, pb);  // one P buffer: every helper read the last one in the previous step
+      }
       if (c + 1 < n_chunks) {
         if constexpr (Ls::PBUF == 2) issue_p(c + 1, pn);  // the other P buffer
+        // k of the next chunk into the buffer of the previous one (read by its update, before the barrier)
+        if (Ls::PBUF == 2 && c > 0) issue_k(c + 1, kn, hw);
         if (hw == 0) fetch_g(c + 1);
       }
       transform(kc, kt);
       // O^T[v][t] = s exp(gamma_t) (S Q^T)[v][t] + (U'^T P^T)[v][t], v in block c4;
-      // the first term here (XS holds the state entering the chunk), the second in phase 1b
+      // the first term here (XS holds the state entering the chunk), the second in phase B
       const float sc = coded_in ? gmisc[1] : 1.0f;
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -670,10 +668,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[ti][i] *= egt;
       }
+      if constexpr (Ls::PBUF == 1) wait_vmem();  // P of this chunk is read in the second phase
     }
     barrier_lds();
 
-    // ======== phase 1b ========
+    // ======== phase B ========
     if (chain) {
       // S^T <- exp(gamma_C) S^T + K^T (exp(gamma_C - gamma) * U'), the
       // decayed U' as three bf16 planes (K enters exactly)
@@ -689,7 +688,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         Eng::split3(u8, bh[kb], bm[kb], bl[kb]);
       }
       float aC = st_coded ? gmisc[0] * s_cur : gmisc[0];  // decay, and the scale of a coded state
-      if constexpr (kFused) aC *= gmisc[2];  // NaN after a failed wait for a ready flag
+      if constexpr (kFused) aC *= *psn;  // NaN after a failed wait for a ready flag
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -718,13 +717,16 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const Fr a0 = ka0[t], a1 = ka1[t];
+        // the first 32 tokens' planes smallest first, then the second 32's
         if constexpr (kSplit) {
           Eng::mma(st[t], a0, bl[0]);
-          Eng::mma(st[t], a1, bl[1]);
           Eng::mma(st[t], a0, bm[0]);
-          Eng::mma(st[t], a1, bm[1]);
         }
         Eng::mma(st[t], a0, bh[0]);
+        if constexpr (kSplit) {
+          Eng::mma(st[t], a1, bl[1]);
+          Eng::mma(st[t], a1, bm[1]);
+        }
         Eng::mma(st[t], a1, bh[1]);
       }
       if (args.bound_pre) {
@@ -741,15 +743,33 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
 #pragma unroll
           for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(st[t][i]));
         amax = wave_max_dpp(amax);
-        if (lane == 0) red[c4] = amax;
+        // publish this wave's amax (slot of this chunk's parity), then its tag
+        int* tags = reinterpret_cast<int*>(red + 8);
+        if (lane == 0) {
+          red[(c & 1) * 4 + c4] = amax;
+          __hip_atomic_store(tags + c4, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        // wait until the four chain waves have published this chunk's amax
+        // (the chain waves only; the helpers go on with their own work).
+        // Every chain wave gets here in every chunk; the bound only keeps a
+        // broken invariant from hanging the GPU.
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          int tmin = __hip_atomic_load(tags + 0, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+          for (int q = 1; q < 4; ++q)
+            tmin = min(tmin, __hip_atomic_load(tags + q, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+          if (uniform(tmin) > c) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
       }
+      chain_qdq(c, red + (c & 1) * 4, xs, vecn, do_qdq, last);
     } else {
       if (c + 1 < n_chunks) {
-        issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase 1a
+        issue_v(c + 1, vb, tb, hw);  // v and T were last read in phase A
         if constexpr (kW) issue_w(c + 1, wb, hw);  // and W
       }
       if constexpr (kFused) {
-        if (hw == 1 && c + 2 < n_chunks) pend = load_ready(c + 2);  // checked in phase 2
+        if (hw == 1 && c + 2 < n_chunks) pend = load_ready(c + 2);  // checked at the end of the phase
       }
       Fr uh[2], ul[2];
 #pragma unroll
@@ -765,7 +785,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
         phs[p] = Eng::ld(slot(pb, p));
         if constexpr (kSplit) pls[p] = Eng::ld(slot(pb, 6 + p));
       }
-      if (c + 1 < n_chunks) issue_q(c + 1, qc);  // q was last read in phase 1a
+      if (c + 1 < n_chunks) issue_q(c + 1, qc);  // q was last read in phase A
 #pragma unroll
       for (int p = 0; p < 6; ++p) {
         const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
@@ -789,70 +809,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
           }
         }
       }
-    }
-    barrier_lds();
-
-    // ======== phase 2 ========
-    if (chain) {
-      float s_new = 1.0f;
-      if (do_qdq) {
-        const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        s_new = qdq_scale(amax);
-        const float r = 1.0f / s_new;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          float c0[4], c1[4];
-          if constexpr (kSplit) {
-            // keep the codes; the scale is folded into the next decay multiply
-            e4m3_codes4(st[2 * kb], s_new, r, c0);
-            e4m3_codes4(st[2 * kb + 1], s_new, r, c1);
-            st[2 * kb] = f32x4{c0[0], c0[1], c0[2], c0[3]};
-            st[2 * kb + 1] = f32x4{c1[0], c1[1], c1[2], c1[3]};
-            const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-            sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
-          } else {
-            qdq4c(st[2 * kb], c0, s_new, r);
-            qdq4c(st[2 * kb + 1], c1, s_new, r);
-          }
-        }
-        s_cur = s_new;
-        st_coded = kSplit;
-      }
-      if (!last) {
-        if (kSplit && do_qdq) {
-          write_xs(xs, sh, sh, false);
-        } else {
-          Fr hi[NKB], lo[NKB];
-          state_frags(hi, lo);
-          write_xs(xs, hi, lo, true);
-          if constexpr (!kSplit) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) sh[kb] = hi[kb];  // fp32 engine: the exact state
-          }
-        }
-        if (c4 == 0 && lane == 0) gmisc[1] = s_new;
-      }
-      const int bidx = bound0 + c;
-      if (args.bound_post) {
-        const float f = st_coded ? s_cur : 1.0f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          *reinterpret_cast<float4*>(args.bound_post + ((int64_t)bidx * H * dv + (int64_t)h * dv + vcol0) * DK +
-                                     dkmap(16 * t + 4 * gq)) = make_float4(st[t][0] * f, st[t][1] * f,
-                                                                           st[t][2] * f, st[t][3] * f);
-      }
-      if (args.bound_scales && tid == 0) args.bound_scales[((int64_t)bidx * H + h) * tiles + vt] = s_new;
-    } else {
-      // one P buffer: every helper has read it in phase 1b; the next chunk's P lands before the barrier
-      if constexpr (Ls::PBUF == 1) {
-        if (c + 1 < n_chunks) issue_p(c + 1, pb);
-      }
-      if (c + 1 < n_chunks && hw == 0) scan(c + 1, vec);  // gates of the next chunk
-      wait_vmem();  // this wave's loads (k of the next chunk included) are in LDS before the barrier
+      if (Ls::PBUF == 1 && c + 1 < n_chunks) issue_k(c + 1, kn, hw);  // the update reads only this chunk's k
+      if (c + 1 < n_chunks && hw == 0) scan(c + 1, vecn);  // gates of the next chunk, into the other vector
+      wait_vmem();  // this wave's loads for the next chunk are in LDS before the barrier
       if constexpr (kFused) {
-        if (hw == 1 && c + 2 < n_chunks) await_ready(c + 2, pend, vec);  // P and T of chunk c + 2 load in the next step
+        if (hw == 1 && c + 2 < n_chunks) await_ready(c + 2, pend);  // P and T of chunk c + 2 load in the next step
       }
-      if (c + 2 < n_chunks) issue_k(c + 2, kc, hw);  // k of this chunk has been read
     }
     barrier_lds();
   };
@@ -862,8 +824,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     E* k1 = sK + 64 * DK;
     E* p0 = sP;
     E* p1 = sP + (Ls::PBUF - 1) * 6 * NP * 64 * 8;
-    step(c, odd ? k1 : k0, sQ, sT, sV, odd ? p1 : p0, odd ? p0 : p1, sXU, sXS,
-         Eng::kTrRead ? nullptr : sKT, sG2, sRed, sW);
+    float* v0 = sG2;
+    float* v1 = sG2 + 3 * 64 + 8;
+    step(c, odd ? k1 : k0, odd ? k0 : k1, sQ, sT, sV, odd ? p1 : p0, odd ? p0 : p1, sXU, sXS,
+         Eng::kTrRead ? nullptr : sKT, odd ? v1 : v0, odd ? v0 : v1, sRed, sW);
   }
 
   if (st_coded) {  // back to the state values: code * s
@@ -1060,6 +1024,8 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   }
   if (s.gate_per_channel) {
     e = launch_kda_state(s, a, stream);
+  } else if (s.io_dtype == GDN_BF16 && a.Wrec == nullptr) {
+    e = launch_chunk_bf16(s, a, stream);
   } else if (s.io_dtype == GDN_BF16) {
     if (s.dk == 128)
       e = ob ? launch_sched<128, EngBF16, uint16_t, uint16_t>(s, a, stream)

@@ -64,8 +64,15 @@ __device__ __forceinline__ uint32_t lds_base_u32(const char* smem) {
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)smem);
 }
 // Wait until this wave's outstanding vector memory operations (including
-// direct LDS loads) have completed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// direct LDS loads) have completed.  The asm wait covers the direct loads
+// (issued from asm, so the compiler does not count them); the same wait as a
+// builtin tells the compiler's wait-count tracking that nothing is in flight
+// after it (an asm wait is opaque to it), so that it adds no waits for loads
+// that have long completed (which on gfx9 would also wait for stores).
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited
+}
 // Workgroup barrier that orders LDS accesses only: it does not wait for the
 // wave's direct LDS loads or global memory operations in flight.
 __device__ __forceinline__ void barrier_lds() {
@@ -116,10 +123,7 @@ struct EngBF16 {
   static __device__ __forceinline__ void split3(const float (&x)[8], Fr& hi, Fr& mid, Fr& lo) {
     uint32_t h[4], m[4], l[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
-      split_bf16x2(x[2 * j] - bf16_lo(h[j]), x[2 * j + 1] - bf16_hi(h[j]), m[j], l[j]);
-    }
+    for (int j = 0; j < 4; ++j) split3_bf16x2(x[2 * j], x[2 * j + 1], h[j], m[j], l[j]);
     hi = __builtin_bit_cast(Fr, make_uint4(h[0], h[1], h[2], h[3]));
     mid = __builtin_bit_cast(Fr, make_uint4(m[0], m[1], m[2], m[3]));
     lo = __builtin_bit_cast(Fr, make_uint4(l[0], l[1], l[2], l[3]));
@@ -323,5 +327,7 @@ __device__ __forceinline__ void report_wait_timeout(int32_t* status) {
 // The sequential kernel for a per-key-channel gate (gdn_kda.hip); the prep
 // kernel has filled a.T and a.Prec.
 hipError_t launch_kda_state(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream);
+// the scalar-gate state part for bf16 q, k, v without W QDQ (gdn_chunk_bf16.hip)
+hipError_t launch_chunk_bf16(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream);
 
 }  // namespace gdn

@@ -217,10 +217,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+// Residuals of a bf16 pair h = bf16x2(a, b): a - h.lo and b - h.hi, each one
+// v_dot2_f32_bf16 of h with (-1, 0) or (0, -1) accumulated onto a or b.  The
+// product is exact and the difference is exactly representable (h.lo is a
+// rounded to 8 significant bits), so the result is the exact residual, the
+// same bits as the unpack-and-subtract it replaces, in one instruction.  The
+// two masks come from scalar registers set in asm: folded as constants, the
+// (-1, 0) mask has been turned into the inline constant -1.0, whose 32-bit
+// pattern is the (0, -1) mask.
+__device__ __forceinline__ void bf16x2_residuals(uint32_t h, float a, float b, float& ra, float& rb) {
+  uint32_t m_lo, m_hi;
+  asm("s_mov_b32 %0, 0xbf80" : "=s"(m_lo));
+  asm("s_mov_b32 %0, 0xbf800000" : "=s"(m_hi));
+  const bf16x2 hv = __builtin_bit_cast(bf16x2, h);
+  ra = __builtin_amdgcn_fdot2_f32_bf16(hv, __builtin_bit_cast(bf16x2, m_lo), a, false);
+  rb = __builtin_amdgcn_fdot2_f32_bf16(hv, __builtin_bit_cast(bf16x2, m_hi), b, false);
+}
 // hi + lo split of two values: hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = pack_bf16x2(a, b);
-  lo = pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
+  float ra, rb;
+  bf16x2_residuals(hi, a, b, ra, rb);
+  lo = pack_bf16x2(ra, rb);
+}
+// three planes of two values: hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid)
+__device__ __forceinline__ void split3_bf16x2(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  float ra, rb;
+  bf16x2_residuals(hi, a, b, ra, rb);
+  split_bf16x2(ra, rb, mid, lo);
 }
 
 // Element loads/stores by I/O type.

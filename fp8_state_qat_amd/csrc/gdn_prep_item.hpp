@@ -134,8 +134,7 @@ __device__ __forceinline__ void store_record(const float* M, const float* colsca
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if constexpr (kPl == 3) {
-          hv[q] = pack_bf16x2(t8[2 * q], t8[2 * q + 1]);
-          split_bf16x2(t8[2 * q] - bf16_lo(hv[q]), t8[2 * q + 1] - bf16_hi(hv[q]), mv[q], lv[q]);
+          split3_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], mv[q], lv[q]);
         } else {
           split_bf16x2(t8[2 * q], t8[2 * q + 1], hv[q], mv[q]);
         }
@@ -420,10 +419,7 @@ __device__ __forceinline__ void prep_item(const PrepArgs& a, int j, int h, int t
           // accuracy, so its codes differ from the oracle's only at midpoints
           uint32_t hv[4], mv[4], lv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            hv[q] = pack_bf16x2(xa[2 * q], xa[2 * q + 1]);
-            split_bf16x2(xa[2 * q] - bf16_lo(hv[q]), xa[2 * q + 1] - bf16_hi(hv[q]), mv[q], lv[q]);
-          }
+          for (int q = 0; q < 4; ++q) split3_bf16x2(xa[2 * q], xa[2 * q + 1], hv[q], mv[q], lv[q]);
           const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
           const bf16x8 am = __builtin_bit_cast(bf16x8, make_uint4(mv[0], mv[1], mv[2], mv[3]));
           const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
@@ -832,6 +828,74 @@ __device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, i
     }
     store_w_record<DK>(a, j, h, wacc, reinterpret_cast<uint16_t*>(smem + Ls::oK),
                        reinterpret_cast<float*>(smem + Ls::oQ), tid, true);
+  }
+}
+
+// Fused launch, workgroups 0 .. n_prep - 1: the T and P records of every
+// (chunk, head), two at a time (waves 0..3 and waves 4..7 each take one item).
+// Producer p serves the (sequence, head) pairs nh with nh % 8 == p % 8, in
+// chunk-major order: the R = n_prep / 8 producers of a class take its items
+// m = r, r + R, r + 2R, ... (r = p / 8), item m being chunk m / M of the
+// class's (m % M)-th pair, M the pairs in the class.  n_prep is a multiple
+// of 8 and the state part maps nh to blocks on XCD nh % 8, so producer and
+// consumers of a record share one L2: the record stores complete in that L2
+// (every wave waits for its stores, then the workgroup barrier), then the
+// flag is stored at device scope, past the L1.  A producer that finds itself
+// off its XCD writes its L2 back first and says so in the flag, and a
+// consumer on another XCD then invalidates its caches before reading
+// (device-scope release and acquire).  Producers never wait, so the
+// consumers' waits end once every producer has been dispatched; producers
+// have the lower workgroup ids.
+template <int DK, typename TIO, bool kW>
+__device__ __forceinline__ void produce_records(const ChunkArgs& args, char* smem) {
+  using IL = PrepItemLds<DK, TIO, kW>;
+  const int half = uniform((int)threadIdx.x >> 8), tid = threadIdx.x & 255;  // half: wave-uniform
+  char* lds = smem + half * IL::bytes;
+  PrepArgs a;
+  a.q = args.q; a.k = args.k; a.beta = args.beta; a.g = args.g; a.cu_seqlens = args.cu_seqlens;
+  a.seq_lens = args.seq_lens; a.prefix_lens = args.prefix_lens; a.offs = args.chunk_offs;
+  a.T = const_cast<void*>(args.T); a.P = const_cast<void*>(args.Prec); a.N = args.N; a.H = args.H;
+  a.W = const_cast<void*>(args.Wrec); a.w_pre = args.w_pre; a.w_post = args.w_post;
+  a.status = args.status;
+  const int H = args.H, NH = args.N * args.H;
+  const int p = blockIdx.x, x = p & 7, r = p >> 3, R = args.n_prep >> 3;
+  const unsigned xcd = xcd_id();
+  const bool home = xcd == (unsigned)x;
+  const int M = NH > x ? (NH - x + 7) >> 3 : 0;
+  const int64_t total = (int64_t)args.chunk_offs[args.N + 1] * M;
+  for (int64_t m0 = r; m0 < total; m0 += 2 * R) {
+    const int64_t m = m0 + (int64_t)half * R;
+    bool active = m < total;
+    int j = 0, h = 0, t0 = 0, nv = 0;
+    if (active) {
+      const int c = (int)(m / M), nh = x + 8 * (int)(m % M);
+      const int n = nh / H;
+      h = nh % H;
+      const int seg0 = args.cu_seqlens[n];
+      const int L = args.seq_lens ? args.seq_lens[n] : (args.cu_seqlens[n + 1] - seg0);
+      const int P = args.prefix_lens ? args.prefix_lens[n] : L;
+      active = c * kChunk < P;
+      if (active) {
+        j = args.chunk_offs[n] + c;
+        t0 = seg0 + c * kChunk;
+        nv = min(kChunk, P - c * kChunk);
+      }
+    }
+    // a fresh copy of the lane index per item keeps the compiler from holding
+    // the item's lane-dependent LDS addresses live across the whole loop
+    int tid_i = tid;
+    asm volatile("" : "+v"(tid_i));
+    prep_item<DK, TIO, kW>(a, j, h, t0, nv, lds, tid_i, active);
+    wait_vmem();      // this wave's record stores are complete
+    __syncthreads();  // ... in every wave of the item; the LDS blocks are free again
+    if (active && tid == 0) {
+      unsigned flag = 1u | (xcd << 1);
+      if (!home) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        flag |= kReadyReleased;
+      }
+      __hip_atomic_store(args.ready + ((int64_t)j * H + h), flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
