@@ -47,6 +47,7 @@ class GdnShape(ctypes.Structure):
         ("o_dtype", ctypes.c_int32),
         ("gate_per_channel", ctypes.c_int32),
         ("qdq_flags", ctypes.c_uint32),
+        ("gate_grid_log2", ctypes.c_int32),
     ]
 
 

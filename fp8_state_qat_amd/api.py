@@ -57,8 +57,8 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _shape(N, H, dk, dv, T, io_dt, o_dt, per_channel, flags):
-    return GdnShape(N, H, dk, dv, T, _DT[io_dt], _DT[o_dt], 1 if per_channel else 0, int(flags))
+def _shape(N, H, dk, dv, T, io_dt, o_dt, per_channel, flags, grid=0):
+    return GdnShape(N, H, dk, dv, T, _DT[io_dt], _DT[o_dt], 1 if per_channel else 0, int(flags), int(grid))
 
 
 def _offsets_total(offs, N, name):
@@ -90,7 +90,8 @@ def workspace_status(workspace):
 
 def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
               initial_state=None, qdq_flags=GDN_QDQ_CHUNK | GDN_QDQ_WRITE, o_dtype=None,
-              out=None, final_state=None, workspace=None, debug=None, check_status=False, noalloc=False):
+              out=None, final_state=None, workspace=None, debug=None, check_status=False, noalloc=False,
+              gate_grid_log2=0):
     """gdn_chunk_fwd.  q, k: [T, H, dk]; v: [T, H, dv] (fp32 or bf16); beta:
     [T, H] fp32; g: [T, H] or [T, H, dk] fp32; cu_seqlens: [N+1] int32;
     seq_lens, prefix_lens: [N] int32 or None; initial_state: [N, H, dv, dk]
@@ -113,6 +114,8 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
     noalloc: call gdn_chunk_fwd_noalloc instead, whose workspace is the
     library's static per-GPU scratch (out and final_state must be given, no
     workspace; the status word comes back through debug["status"]).
+    gate_grid_log2: 0, or k in 1..24: the log-gates of the recurrent suffix
+    rounded to multiples of 2^-k (the log-retention grid).
     Returns (o, final_state)."""
     if noalloc:
         if workspace is not None or check_status:
@@ -153,7 +156,7 @@ def chunk_fwd(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
         out = torch.empty((T, H, dv), dtype=o_dtype, device=k.device)
     if final_state is None:
         final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=k.device)
-    shape = _shape(N, H, dk, dv, T, k.dtype, o_dtype, per_channel, qdq_flags)
+    shape = _shape(N, H, dk, dv, T, k.dtype, o_dtype, per_channel, qdq_flags, gate_grid_log2)
     if not noalloc:
         ws_bytes = _lib.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(shape))
         if ws_bytes == 0:
@@ -318,12 +321,14 @@ def state_qdq_int8(x, out=None, scales=None, want_scales=True):
 
 
 def decode_step(q, k, v, beta, g, state, *, qdq=True, o=None, o_dtype=None, state_pre=None,
-                scales=None, int8=False, active=None):
+                scales=None, int8=False, active=None, gate_grid_log2=0):
     """gdn_decode_step.  q, k: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; g: [N, H]
     or [N, H, dk]; state [N, H, dv, dk] fp32 updated in place.  int8: the
     per-write QDQ is INT8 block-32 (scales [N, H, dv, dk/32]) instead of FP8
     per tile (scales [N, H, dv/64]).  active: optional [N] int32; sequences
     with active[n] == 0 are left untouched (state, o and the records).
+    gate_grid_log2: 0, or k in 1..24: the log-gates rounded to multiples of
+    2^-k (the log-retention grid).
     Returns o."""
     _dev(k, "k")
     if k.dim() != 3:
@@ -356,7 +361,7 @@ def decode_step(q, k, v, beta, g, state, *, qdq=True, o=None, o_dtype=None, stat
     if o is None:
         o = torch.empty((N, H, dv), dtype=o_dtype, device=k.device)
     shape = GdnShape(N, H, dk, dv, N, _DT[k.dtype], _DT[o_dtype], 1 if per_channel else 0,
-                     (GDN_QDQ_WRITE if qdq else 0) | (_lib.GDN_QDQ_INT8 if int8 else 0))
+                     (GDN_QDQ_WRITE if qdq else 0) | (_lib.GDN_QDQ_INT8 if int8 else 0), int(gate_grid_log2))
     st = _lib.lib().gdn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                     _ptr(g), _ptr(active), _ptr(state), _ptr(o), _ptr(state_pre),
                                     _ptr(scales), _stream())

@@ -78,6 +78,8 @@ gdn_status_t check_shape(const gdn_shape_t* s, bool decode) {
     return fail(GDN_ERR_INVALID_ARG, "gate_per_channel must be 0 or 1");
   if (s->qdq_flags & ~(GDN_QDQ_CHUNK | GDN_QDQ_WRITE | GDN_QDQ_W | GDN_QDQ_INT8))
     return fail(GDN_ERR_INVALID_ARG, "unknown qdq_flags bits 0x%x", s->qdq_flags);
+  if (s->gate_grid_log2 < 0 || s->gate_grid_log2 > 24)
+    return fail(GDN_ERR_INVALID_ARG, "gate_grid_log2 must be 0 (off) or 1 .. 24 (got %d)", s->gate_grid_log2);
   const int64_t blocks = (int64_t)s->n_seqs * s->n_heads * (s->dv / 64);
   if (blocks >= (int64_t)1 << 31) return fail(GDN_ERR_UNSUPPORTED, "too many (sequence, head, tile) units");
   // the chunk kernel addresses one 64-token chunk of a head with 32-bit byte offsets
@@ -308,6 +310,9 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape, const void* q, const voi
   if (shape->qdq_flags & GDN_QDQ_INT8)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_INT8 is a decode-step codec");
   if (shape->gate_per_channel) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh supports the scalar gate only");
+  if (shape->gate_grid_log2 != 0)
+    return fail(GDN_ERR_INVALID_ARG, "gdn_chunk_bwd_dh covers fully chunked sequences, which have no "
+                "recurrent writes: gate_grid_log2 must be 0");
   const size_t need = gdn::bwd_workspace_bytes(*shape);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(GDN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,

@@ -872,7 +872,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
       }
       __syncthreads();
       if (chain) {
-        const float a = expf(sgb[0]);
+        const float a = expf(grid_gate(sgb[0], args.grid_log2));
         const float b = sgb[1];
         float y = 0.f;
 #pragma unroll
@@ -1014,6 +1014,7 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   a.H = s.n_heads; a.dv = s.dv; a.flags = s.qdq_flags;
   a.N = s.n_seqs; a.ready = L.ready; a.n_prep = n_prep; a.fused = fused ? 1 : 0;
   a.status = L.status;
+  a.grid_log2 = s.gate_grid_log2;
   a.sfx_offsets = debug ? debug->suffix_offsets : nullptr;
   a.sfx_pre = debug ? debug->suffix_pre : nullptr;
   a.sfx_post = debug ? debug->suffix_post : nullptr;

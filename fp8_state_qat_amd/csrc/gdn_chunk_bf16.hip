@@ -672,7 +672,7 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
       }
       __syncthreads();
       if (chain) {
-        const float a = expf(sgb[0]);
+        const float a = expf(grid_gate(sgb[0], args.grid_log2));
         const float b = sgb[1];
         float y = 0.f;
 #pragma unroll

@@ -265,6 +265,7 @@ struct ChunkArgs {
   unsigned* ready;     // fused launch: one ready flag per (chunk, head), cleared before the launch
   int n_prep;          // fused launch: workgroups 0 .. n_prep - 1 produce the T and P records
   int32_t* status;     // the workspace's status word (index check, failed waits)
+  int grid_log2;       // log-retention grid of the recurrent suffix (0: off)
   const int32_t* sfx_offsets;  // optional per-token record of the recurrent suffix:
   float* sfx_pre;              // state after each suffix token before its QDQ
   float* sfx_post;             // and after it ([sfx_offsets[n] + t - P_n, H, dv, dk])

@@ -4,7 +4,8 @@
 // quantizes the state before storing it for the next token).
 //
 // Per (sequence, head) and 64-row value tile of the state S (64 x dk fp32):
-//     S~ = S * a                       (a = exp(g); per-key-channel: S diag(exp(g)))
+//     S~ = S * a                       (a = exp(g); per-key-channel: S diag(exp(g));
+//                                       g on the log-retention grid when one is set)
 //     y  = S~ k ;  z = S~ q ;  u = beta (v - y)
 //     o  = z + (k . q) u               (= S' q with S' = S~ + u k^T)
 //     S' = S~ + u k^T ;  S <- QDQ(S')  (one scale for the tile)
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ g, const int32_t* __restrict__ active,
     float* __restrict__ state, TO* __restrict__ o, float* __restrict__ state_pre,
-    float* __restrict__ scales, int H, int dv, int do_qdq) {
+    float* __restrict__ scales, int H, int dv, int do_qdq, int grid_log2) {
   constexpr int F = DK / 4;         // float4 per state row
   constexpr int RPP = kThreads / F; // rows covered by one pass of the block
   constexpr int NP = kTileRows / RPP;
@@ -65,9 +66,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
   }
   if constexpr (PC) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dec[j] = expf(g[nh * DK + 4 * c4 + j]);
+    for (int j = 0; j < 4; ++j) dec[j] = expf(grid_gate(g[nh * DK + 4 * c4 + j], grid_log2));
   } else {
-    const float a = expf(g[nh]);
+    const float a = expf(grid_gate(g[nh], grid_log2));
 #pragma unroll
     for (int j = 0; j < 4; ++j) dec[j] = a;
   }
@@ -140,7 +141,8 @@ static void launch_dk_io_o(const gdn_shape_t& s, const void* q, const void* k, c
   const bool i8 = (s.qdq_flags & GDN_QDQ_INT8) != 0;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), 0, stream, (const TIO*)q, (const TIO*)k,
-                       (const TIO*)v, beta, g, active, state, (TO*)o, state_pre, scales, s.n_heads, s.dv, qdq);
+                       (const TIO*)v, beta, g, active, state, (TO*)o, state_pre, scales, s.n_heads, s.dv, qdq,
+                       s.gate_grid_log2);
   };
   if (s.gate_per_channel) {
     if (i8) go(decode_step_kernel<DK, TIO, TO, true, true>);

@@ -41,6 +41,13 @@ constexpr int kThreads = 256;  // 4 waves of 64
 // steps q is the correctly rounded quotient (results in the fp32 subnormal
 // range, which all map to code 0, excepted).
 // ---------------------------------------------------------------------------
+// Log-gate of a recurrent write on the log-retention grid 2^-k (k = 0: as
+// given): the nearest multiple of 2^-k, ties to even.  Scaling by a power of
+// two and rint are exact in fp32, so the result is a function of g alone.
+__device__ __forceinline__ float grid_gate(float g, int k) {
+  return k ? ldexpf(__builtin_rintf(ldexpf(g, k)), -k) : g;
+}
+
 __device__ __forceinline__ float qdq_scale(float amax) {
   float s = amax / 448.0f;
   return (s > 0.0f) ? s : 1.0f;

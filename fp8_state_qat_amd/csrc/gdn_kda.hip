@@ -728,7 +728,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = dkmap(16 * t2 + 4 * gq + i);
-          st[t2][i] *= expf(sg[d]);
+          st[t2][i] *= expf(grid_gate(sg[d], args.grid_log2));
           y += st[t2][i] * sk[d];
         }
       y += __shfl_xor(y, 16, 64);

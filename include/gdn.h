@@ -87,7 +87,22 @@ typedef struct {
     int32_t o_dtype;           /* gdn_dtype_t of o */
     int32_t gate_per_channel;  /* 0: g is [T, H]; 1: g is [T, H, dk] (per-key-channel gate) */
     uint32_t qdq_flags;        /* GDN_QDQ_* bits */
+    int32_t gate_grid_log2;    /* 0, or k in 1 .. 24: log-retention grid of the recurrent */
+                               /* writes (see below) */
 } gdn_shape_t;
+
+/*
+ * Log-retention grid (#2509 "Add experimental GDN/KDA decode and replay QAT",
+ * "What does this PR do?": an optional rounding of the log-retention among
+ * the per-token decode policies; its pilot selected a grid of 1/256).  With
+ * gate_grid_log2 = k > 0, every recurrent write -- each gdn_decode_step token
+ * and each token P < t <= L of gdn_chunk_fwd's recurrent suffix -- uses the
+ * log-gate rounded to the nearest multiple of 2^-k, ties to even:
+ *   g~ = 2^-k * rint(2^k * g)   (per key channel for a per-channel gate)
+ * and decays by exp(g~).  The chunked prefix t <= P is unchanged.  With a
+ * power-of-two step every operation of the rounding is exact in fp32, so g~
+ * is a pure function of the stored fp32 gate.
+ */
 
 /* Optional per-boundary record of the chunked prefix, for parity checks, and
  * a timing hook.  Boundary b of sequence n is b = bound_offsets[n] + i for its

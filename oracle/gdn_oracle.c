@@ -42,6 +42,14 @@
  *    A token that satisfies both is quantized once.  A supplied initial state
  *    is used as given.
  *
+ *  - Log-retention grid (#2509 page "What does this PR do?": an optional
+ *    rounding of the log-retention among the per-token decode policies; its
+ *    pilot selected a grid of 1/256).  The page gives no formula; this
+ *    oracle's reading: with grid_log2 = k > 0 every recurrent write (token
+ *    t > P) decays with g rounded to the nearest multiple of 2^-k, ties to
+ *    even (per key channel for the per-channel gate); the chunked prefix
+ *    t <= P is unchanged.
+ *
  *  - INT8 block-32 state QDQ (#2519 page: dynamic INT8 state recipes, one of
  *    them with 32-element blocks; the page gives no formula, so what follows
  *    is this oracle's reading): with ORC_QDQ_INT8 every QDQ of the state
@@ -245,6 +253,13 @@ static void qdq_state_f64(double* S, int dv, int dk, float* tmp, float* scales)
     for (int64_t i = 0; i < n; ++i) S[i] = (double)tmp[i];
 }
 
+/* Log-gate on the grid 2^-k: the nearest multiple, ties to even (k = 0: g). */
+double orc_grid_gate(double g, int k)
+{
+    if (k <= 0) return g;
+    return ldexp(nearbyint(ldexp(g, k)), -k);   /* default rounding: to nearest, ties to even */
+}
+
 /* ------------------------------------------------------------------------ */
 /* Recurrence for one (sequence, head).                                     */
 /*   q, k : [L][dk]   v : [L][dv]   beta : [L]   g : [L] or [L][dk]         */
@@ -254,6 +269,7 @@ static void qdq_state_f64(double* S, int dv, int dk, float* tmp, float* scales)
 /* prefix boundary b (t <= P and t % 64 == 0 or t == P), bound_pre[b] is the  */
 /* state after token t before QDQ, bound_post[b] after it (equal to pre when  */
 /* CHUNK QDQ is off), bound_scales[b][dv/64] the scales (1 when no QDQ).     */
+/* grid_log2 > 0: tokens t > P decay with orc_grid_gate(g, grid_log2).       */
 /* Returns the number of prefix boundaries (ceil(P/64)), or -1 on bad args.  */
 /* ------------------------------------------------------------------------ */
 int orc_gdn_sequence(int L, int P, int dk, int dv, int per_channel, unsigned flags,
@@ -261,7 +277,7 @@ int orc_gdn_sequence(int L, int P, int dk, int dv, int per_channel, unsigned fla
                      const double* beta, const double* g, const double* S0,
                      double* o, double* S_out,
                      int max_bounds, double* bound_pre, double* bound_post,
-                     float* bound_scales)
+                     float* bound_scales, int grid_log2)
 {
     if (L < 0 || P < 0 || P > L || dk <= 0 || dv <= 0) return -1;
     if (flags && dv % ORC_TILE_ROWS) return -1;     /* QDQ tiles are 64 value rows */
@@ -283,13 +299,14 @@ int orc_gdn_sequence(int L, int P, int dk, int dv, int per_channel, unsigned fla
         const double* vt = v + (int64_t)(t - 1) * dv;
         double bt = beta[t - 1];
 
-        /* decay */
+        /* decay (a recurrent write t > P on the log-retention grid when one is set) */
+        int kg = (t > P) ? grid_log2 : 0;
         if (per_channel) {
-            for (int c = 0; c < dk; ++c) dec[c] = exp(g[(int64_t)(t - 1) * dk + c]);
+            for (int c = 0; c < dk; ++c) dec[c] = exp(orc_grid_gate(g[(int64_t)(t - 1) * dk + c], kg));
             for (int r = 0; r < dv; ++r)
                 for (int c = 0; c < dk; ++c) S[(int64_t)r * dk + c] *= dec[c];
         } else {
-            double a = exp(g[t - 1]);
+            double a = exp(orc_grid_gate(g[t - 1], kg));
             for (int64_t i = 0; i < n; ++i) S[i] *= a;
         }
         /* delta correction against the decayed state */

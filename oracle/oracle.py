@@ -59,8 +59,10 @@ def _load():
     lib.orc_gdn_sequence.argtypes = [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
         _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
-        ctypes.c_int, _dp, _dp, _fp]
+        ctypes.c_int, _dp, _dp, _fp, ctypes.c_int]
     lib.orc_gdn_sequence.restype = ctypes.c_int
+    lib.orc_grid_gate.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.orc_grid_gate.restype = ctypes.c_double
     _lib = lib
     return lib
 
@@ -155,8 +157,13 @@ def qdq_int8_blocks(x, block=INT8_BLOCK):
 # --------------------------------------------------------------------------
 # Recurrence
 # --------------------------------------------------------------------------
+def grid_gate(g, k):
+    """Log-gate on the log-retention grid 2^-k (the oracle's orc_grid_gate)."""
+    return _load().orc_grid_gate(float(g), int(k))
+
+
 def gdn_sequence(q, k, v, beta, g, *, prefix_len=None, flags=QDQ_CHUNK | QDQ_WRITE,
-                 S0=None, record=False):
+                 S0=None, record=False, grid_log2=0):
     """Run one (sequence, head).
 
     q, k: [L, dk]; v: [L, dv]; beta: [L]; g: [L] (scalar gate) or [L, dk]
@@ -183,7 +190,7 @@ def gdn_sequence(q, k, v, beta, g, *, prefix_len=None, flags=QDQ_CHUNK | QDQ_WRI
     nb = lib.orc_gdn_sequence(L, P, dk, dv, per_channel, flags,
                               _ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(beta, _dp),
                               _ptr(g, _dp), _ptr(S0a, _dp), _ptr(o, _dp), _ptr(S, _dp),
-                              nb_max, _ptr(pre, _dp), _ptr(post, _dp), _ptr(sc, _fp))
+                              nb_max, _ptr(pre, _dp), _ptr(post, _dp), _ptr(sc, _fp), int(grid_log2))
     if nb < 0:
         raise ValueError("oracle rejected arguments")
     res = {"o": o, "S": S}
@@ -193,7 +200,8 @@ def gdn_sequence(q, k, v, beta, g, *, prefix_len=None, flags=QDQ_CHUNK | QDQ_WRI
 
 
 def gdn_packed(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
-               flags=QDQ_CHUNK | QDQ_WRITE, S0=None, pairs=None, threads=1, record=False):
+               flags=QDQ_CHUNK | QDQ_WRITE, S0=None, pairs=None, threads=1, record=False,
+               grid_log2=0):
     """Packed varlen layout, as the library takes it.
 
     q, k: [T, H, dk]; v: [T, H, dv]; beta: [T, H]; g: [T, H] or [T, H, dk];
@@ -220,7 +228,7 @@ def gdn_packed(q, k, v, beta, g, cu_seqlens, *, seq_lens=None, prefix_lens=None,
         gg = g[sl, h] if g.ndim == 2 else g[sl, h, :]
         r = gdn_sequence(q[sl, h, :], k[sl, h, :], v[sl, h, :], beta[sl, h], gg,
                          prefix_len=int(pref[n]), flags=flags,
-                         S0=None if S0 is None else S0[n, h], record=record)
+                         S0=None if S0 is None else S0[n, h], record=record, grid_log2=grid_log2)
         return nh, sl, r
 
     if threads > 1:

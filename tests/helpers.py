@@ -34,7 +34,7 @@ def suffix_offsets(w: gi.Workload):
 
 
 def run_chunk_gpu(w: gi.Workload, flags, *, o_dtype=None, record=False, initial_state=None,
-                  use_prefix=True, use_seq_lens=True, suffix_record=False, schedule=None):
+                  use_prefix=True, use_seq_lens=True, suffix_record=False, schedule=None, grid_log2=0):
     """Run gdn_chunk_fwd on workload w; returns numpy dict (o, S and, when
     record, bound_pre/bound_post/scales [nb_total, H, dv(/64), dk]; when
     suffix_record, suffix_pre/suffix_post [n_suffix, H, dv, dk] and
@@ -70,7 +70,7 @@ def run_chunk_gpu(w: gi.Workload, flags, *, o_dtype=None, record=False, initial_
                          seq_lens=d["seq_lens"] if use_seq_lens else None,
                          prefix_lens=d["prefix_lens"] if use_prefix else None,
                          initial_state=init, qdq_flags=flags, o_dtype=o_dt, debug=dbg,
-                         check_status=True)
+                         check_status=True, gate_grid_log2=grid_log2)
     torch.cuda.synchronize()
     res = {"o": np64(o), "S": S.cpu().numpy(), "offsets": offs, "suffix_offsets": soffs}
     if record:
@@ -260,7 +260,7 @@ def check_codes(r, cap=1e-4, far_tol=1e-6):
             assert r["oracle_mismatch_max_dist"] <= far_tol, r
 
 
-def suffix_teacher_forced(w: gi.Workload, gpu, flags, pairs, *, initial_state=None):
+def suffix_teacher_forced(w: gi.Workload, gpu, flags, pairs, *, initial_state=None, grid_log2=0):
     """Teacher-forced check of the recurrent suffix (tokens P_n < t <= L_n),
     one token at a time like the decode step: token t restarts the oracle
     from the GPU's own state after token t - 1 (its post-QDQ record; for the
@@ -269,7 +269,8 @@ def suffix_teacher_forced(w: gi.Workload, gpu, flags, pairs, *, initial_state=No
     no QDQ.  Compared: o_t and the pre-QDQ state (rel-L2 over all tokens, and
     the worst token); the GPU's post-QDQ state = the oracle's QDQ of the
     GPU's pre-QDQ state bit for bit (when the suffix quantizes; else post =
-    pre); the oracle's own codes on its own pre-QDQ state against the GPU's."""
+    pre); the oracle's own codes on its own pre-QDQ state against the GPU's.
+    grid_log2: the log-retention grid of the recurrent writes."""
     q, k, v, b, g = (w.f64(x) for x in ("q", "k", "v", "beta", "g"))
     cu, offs, soffs = w.cu_seqlens, gpu["offsets"], gpu["suffix_offsets"]
     qdq = bool(flags & orc.QDQ_WRITE)
@@ -289,7 +290,7 @@ def suffix_teacher_forced(w: gi.Workload, gpu, flags, pairs, *, initial_state=No
             row = s0 + t
             gg = g[row:row + 1, h] if g.ndim == 2 else g[row:row + 1, h, :]
             r = orc.gdn_sequence(q[row:row + 1, h], k[row:row + 1, h], v[row:row + 1, h], b[row:row + 1, h],
-                                 gg, prefix_len=0, flags=0, S0=S0)
+                                 gg, prefix_len=0, flags=0, S0=S0, grid_log2=grid_log2)
             pre_gpu, post_gpu = gpu["suffix_pre"][si, h], gpu["suffix_post"][si, h]
             o_gpu = gpu["o"][row, h]
             out["o_rel_max"] = max(out["o_rel_max"], rel_l2(o_gpu, r["o"][0]))
@@ -310,7 +311,7 @@ def suffix_teacher_forced(w: gi.Workload, gpu, flags, pairs, *, initial_state=No
     return out
 
 
-def check_prefix_suffix(w, gpu, flags, tol, pairs=None, initial_state=None, codes=None):
+def check_prefix_suffix(w, gpu, flags, tol, pairs=None, initial_state=None, codes=None, grid_log2=0):
     """Prefix P_n then recurrent suffix up to L_n, both teacher-forced: the
     chunked prefix per boundary (G2), the suffix per token from the GPU's own
     records (suffix_teacher_forced).  gpu must hold the boundary record and
@@ -324,7 +325,7 @@ def check_prefix_suffix(w, gpu, flags, tol, pairs=None, initial_state=None, code
         assert r["o_rel"] <= tol and r["pre_rel"] <= tol
         assert r["gpu_code_mismatch"] == 0 and r["scale_mismatch"] == 0
         check_codes(r, **(codes or {}))
-    r = suffix_teacher_forced(w, gpu, flags, pairs, initial_state=initial_state)
+    r = suffix_teacher_forced(w, gpu, flags, pairs, initial_state=initial_state, grid_log2=grid_log2)
     print("suffix, teacher-forced per token", r, flush=True)
     assert r["o_rel"] <= tol and r["pre_rel"] <= tol
     assert r["gpu_code_mismatch"] == 0

@@ -67,6 +67,7 @@ def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None, ws=FAKE, ws_by
     (dict(dk=32), 2), (dict(dv=512), 2), (dict(total_tokens=-1), 1), (dict(io_dtype=7), 1),
     (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=16), 1), (dict(qdq_flags=8 | 3), 2),
     (dict(io_dtype=0, dk=128), 2), (dict(io_dtype=0, dk=128, gate_per_channel=1), 2),
+    (dict(gate_grid_log2=-1), 1), (dict(gate_grid_log2=25), 1),
 ])
 def test_chunk_fwd_rejects_bad_shape(kw, status):
     assert _chunk(_shape(**kw)) == status
@@ -211,6 +212,8 @@ def test_chunk_bwd_dh_checks():
     assert _bwd(_shape(gate_per_channel=1)) == 2
     assert _bwd(_shape(qdq_flags=3 | _lib.GDN_QDQ_W)) == 2   # the W-QDQ forward's backward
     assert "GDN_QDQ_W" in _lib.last_error()
+    assert _bwd(_shape(gate_grid_log2=8)) == 1   # no recurrent writes in a fully chunked backward
+    assert "gate_grid_log2" in _lib.last_error()
     assert _bwd(_shape(), dh=0, d0=0) == 1
     assert _bwd(_shape(), q=FAKE + 8) == 1
     assert _bwd(_shape(), ws_bytes=100) == 1

@@ -98,6 +98,27 @@ def test_prefix_suffix_bf16(flags, d, dv):
     check_prefix_suffix(w, gpu, flags, TOL[gi.BF16])
 
 
+@pytest.mark.parametrize("io,d,dv", [(gi.BF16, 128, 128), (gi.F32, 64, 64)])
+@pytest.mark.parametrize("grid", [3, 8])
+def test_prefix_suffix_log_grid(io, d, dv, grid):
+    """Log-retention grid (#2509): the recurrent suffix decays with each
+    log-gate rounded to a multiple of 2^-grid, the chunked prefix as given.
+    Prefix teacher-forced per boundary, suffix per token against the
+    oracle's grid reading (flags 3; grid 3 is coarse enough that a kernel
+    ignoring the grid fails the per-token gate); the prefix boundary records
+    are those of the same run without the grid, bit for bit, and the suffix
+    outputs differ from it."""
+    w = gi.make_packed([150, 100, 45], 2, d, dv, io_dtype=io, seed=31 + grid + d,
+                       prefix_lens=[128, 37, 0])
+    tol = TOL[io]
+    gpu = run_chunk_gpu(w, 3, o_dtype="f32", record=True, suffix_record=True, grid_log2=grid)
+    check_prefix_suffix(w, gpu, 3, tol, grid_log2=grid)
+    plain = run_chunk_gpu(w, 3, o_dtype="f32", record=True, suffix_record=True)
+    for key in ("bound_pre", "bound_post", "scales"):
+        np.testing.assert_array_equal(gpu[key], plain[key])
+    assert not np.array_equal(gpu["suffix_pre"], plain["suffix_pre"])
+
+
 @pytest.mark.parametrize("flags", [2, 3])
 def test_full_size_prefix_suffix_sampled(flags):
     """The full GDN prefill shape (B=4, T=4096, H=16, d=128, bf16) with a

@@ -110,6 +110,15 @@ def test_kda_prefix_suffix_bf16(flags):
     check_prefix_suffix(w, gpu, flags, TOL[gi.BF16], codes=KDA_CODES)
 
 
+def test_kda_prefix_suffix_log_grid_fp32():
+    """Log-retention grid (#2509) with the per-channel gate: every key
+    channel's log-gate of a recurrent suffix token rounded to a multiple of
+    2^-3; prefix and suffix teacher-forced against the oracle's grid reading."""
+    w = _kda([150, 70, 9], 2, 64, 64, gi.F32, seed=71, prefix_lens=[128, 33, 0])
+    gpu = run_chunk_gpu(w, 3, record=True, suffix_record=True, grid_log2=3)
+    check_prefix_suffix(w, gpu, 3, TOL[gi.F32], grid_log2=3)
+
+
 def test_kda_initial_state_fp32():
     w = _kda([130, 64], 2, 64, 64, gi.F32, seed=61)
     rng = np.random.default_rng(61)

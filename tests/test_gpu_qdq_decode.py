@@ -207,3 +207,44 @@ def test_decode_active_mask(int8):
     off = ~on
     assert torch.equal(bits(state[off]), bits(torch.from_numpy(S0).cuda()[off]))
     assert bool((pre[off] == 3.0).all()) and bool((sc[off] == 3.0).all()) and bool((o[off] == 5.0).all())
+
+
+@pytest.mark.parametrize("pc", [False, True])
+@pytest.mark.parametrize("grid", [3, 8])
+def test_decode_step_log_grid(pc, grid):
+    """Log-retention grid (#2509): each decode token decays with its
+    log-gate rounded to a multiple of 2^-grid.  Teacher-forced per step
+    against the oracle's grid reading (o and the pre-QDQ state, the stored
+    state bit for bit as the oracle's QDQ of the GPU's pre-QDQ state); grid 3
+    is coarse enough that a kernel ignoring the grid fails the pre-QDQ gate."""
+    N, H, dk, dv, steps = 4, 3, 128, 128, 3
+    S0, toks = _decode_case(N, H, dk, dv, gi.BF16, pc, steps, torch.float32, True, seed=211 + grid + pc)
+    state = torch.from_numpy(S0).cuda()
+    pre = torch.empty_like(state)
+    scales = torch.empty((N, H, dv // 64), device="cuda")
+    for t in range(steps):
+        tk = toks[t]
+        dev = {k_: gi.to_torch(a, "cuda") for k_, a in tk.items()}
+        S_before = state.cpu().numpy().astype(np.float64)
+        o = api.decode_step(dev["q"], dev["k"], dev["v"], dev["beta"], dev["g"], state, qdq=True,
+                            o_dtype=torch.float32, state_pre=pre, scales=scales, gate_grid_log2=grid)
+        torch.cuda.synchronize()
+        f64 = {k_: (gi.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+               for k_, a in tk.items()}
+        o_ref = np.zeros((N, H, dv))
+        pre_ref = np.zeros((N, H, dv, dk))
+        for n in range(N):
+            for h in range(H):
+                g = f64["g"][n, h] if not pc else f64["g"][n, h][None, :]
+                r = orc.gdn_sequence(f64["q"][n, h][None], f64["k"][n, h][None],
+                                     f64["v"][n, h][None], f64["beta"][n, h][None],
+                                     np.atleast_1d(g) if not pc else g, prefix_len=0, flags=0,
+                                     S0=S_before[n, h], grid_log2=grid)
+                o_ref[n, h] = r["o"][0]
+                pre_ref[n, h] = r["S"]
+        assert rel_l2(np64(o), o_ref) <= 1e-5
+        pre_np = pre.cpu().numpy()
+        assert rel_l2(pre_np, pre_ref) <= 1e-6
+        want, sc, _ = orc.qdq_states(pre_np)
+        np.testing.assert_array_equal(state.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        np.testing.assert_array_equal(scales.cpu().numpy(), sc)

@@ -645,3 +645,87 @@ def test_state_grads_one_token_closed_form():
     a = np.exp(g[0])
     want = a * (np.outer(do[0], q[0]) + dS) @ (np.eye(64) - b[0] * np.outer(k[0], k[0]))
     np.testing.assert_allclose(dS0, want, rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Log-retention grid of the recurrent writes (the decode/replay page #2509:
+# an optional rounding of the log-retention; its pilot selected 1/256).
+# Reading (parity unpinned against the pages, which give no formula): each
+# recurrent write t > P decays with g rounded to the nearest multiple of
+# 2^-k, ties to even.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("g_units,k,want_units", [
+    (-1.5, 8, -2.0), (-2.5, 8, -2.0), (-0.5, 8, -0.0), (0.5, 8, 0.0), (-0.896, 8, -1.0),
+    (-77.49, 8, -77.0), (-77.5, 8, -78.0), (-76.5, 8, -76.0), (3.5, 1, 4.0), (-1.0, 24, -1.0),
+])
+def test_grid_gate_rounding_table(g_units, k, want_units):
+    """Hand-derived: g = g_units * 2^-k goes to want_units * 2^-k (nearest
+    multiple of the step, ties to the even multiple)."""
+    got = orc.grid_gate(g_units * 2.0 ** -k, k)
+    assert got == want_units * 2.0 ** -k
+    assert orc.grid_gate(g_units * 2.0 ** -k, 0) == g_units * 2.0 ** -k   # k = 0: off
+
+
+def _two_token(q, k, v, b, a2):
+    """Zero state, two tokens, no QDQ, decay a2 at token 2 (the decay of
+    token 1 meets the zero state): S_1 = b1 v1 k1^T, o_1 = S_1 q1;
+    S~ = a2 S_1, u = b2 (v2 - S~ k2), S_2 = S~ + u k2^T, o_2 = S_2 q2."""
+    S1 = b[0] * np.outer(v[0], k[0])
+    St = a2 * S1
+    u = b[1] * (v[1] - St @ k[1])
+    S2 = St + np.outer(u, k[1])
+    return np.stack([S1 @ q[0], S2 @ q[1]]), S2
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_grid_two_token_closed_form(per_channel):
+    """From the zero state with P = 0, token 2's decay is exp of its gate on
+    the grid: g = -0.3 at k = 8 is -77/256 (scalar); per channel each key
+    channel's gate is rounded on its own.  The expected values retype the
+    closed form, not the oracle's code."""
+    q, k, v, b, _ = _seq(2, 64, 64, seed=91)
+    if per_channel:
+        g = np.full((2, 64), -0.3)
+        g[1, ::2] = -0.1                          # 25.6 -> 26 units
+        a2 = np.where(np.arange(64) % 2 == 0, np.exp(-26 / 256), np.exp(-77 / 256))
+        r = orc.gdn_sequence(q, k, v, b, g, prefix_len=0, flags=0, grid_log2=8)
+        S1 = b[0] * np.outer(v[0], k[0])
+        St = S1 * a2[None, :]
+        u = b[1] * (v[1] - St @ k[1])
+        S2 = St + np.outer(u, k[1])
+        o = np.stack([S1 @ q[0], S2 @ q[1]])
+    else:
+        g = np.array([-0.3, -0.3])
+        r = orc.gdn_sequence(q, k, v, b, g, prefix_len=0, flags=0, grid_log2=8)
+        o, S2 = _two_token(q, k, v, b, np.exp(-77 / 256))
+    np.testing.assert_allclose(r["o"], o, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(r["S"], S2, rtol=1e-13, atol=1e-15)
+
+
+def test_grid_leaves_the_chunked_prefix_and_on_grid_gates_alone():
+    """The grid only touches recurrent writes: with P = L (no suffix) the
+    result is bitwise the one without the grid; with gates already on the
+    grid it is bitwise unchanged for any P; with off-grid gates and a suffix
+    it changes, and only from the first suffix token on."""
+    q, k, v, b, g = _seq(150, 64, 64, seed=92)
+    base = orc.gdn_sequence(q, k, v, b, g, prefix_len=150, flags=3)
+    grid = orc.gdn_sequence(q, k, v, b, g, prefix_len=150, flags=3, grid_log2=8)
+    assert np.array_equal(base["o"], grid["o"]) and np.array_equal(base["S"], grid["S"])
+    g_on = np.round(g * 256) / 256
+    base = orc.gdn_sequence(q, k, v, b, g_on, prefix_len=70, flags=3)
+    grid = orc.gdn_sequence(q, k, v, b, g_on, prefix_len=70, flags=3, grid_log2=8)
+    assert np.array_equal(base["o"], grid["o"]) and np.array_equal(base["S"], grid["S"])
+    base = orc.gdn_sequence(q, k, v, b, g, prefix_len=70, flags=3)
+    grid = orc.gdn_sequence(q, k, v, b, g, prefix_len=70, flags=3, grid_log2=3)
+    assert np.array_equal(base["o"][:70], grid["o"][:70])
+    assert not np.array_equal(base["o"][70], grid["o"][70])
+
+
+def test_grid_fine_step_approaches_no_grid():
+    """At k = 24 each gate moves by at most 2^-25, so the whole suffix moves
+    by about that relative amount (QDQ off)."""
+    q, k, v, b, g = _seq(100, 64, 64, seed=93)
+    base = orc.gdn_sequence(q, k, v, b, g, prefix_len=10, flags=0)
+    fine = orc.gdn_sequence(q, k, v, b, g, prefix_len=10, flags=0, grid_log2=24)
+    rel = np.linalg.norm(fine["S"] - base["S"]) / np.linalg.norm(base["S"])
+    assert 0 < rel < 1e-6
