@@ -226,7 +226,8 @@ def chunk_bwd_dh(q, k, beta, g, cu_seqlens, d_o, *, seq_lens=None, d_final_state
     L = sum o . d_o + <S_L, d_final_state>, identity straight-through QDQ;
     with want_dv (or a d_v tensor) also the gradient of v ([T, H, dv] fp32).
     q, k: [T, H, dk] bf16; d_o: [T, H, dv] bf16; beta, g: [T, H] fp32.
-    qdq_flags: those of the forward (GDN_QDQ_W is refused by the library).
+    qdq_flags: those of the forward (with GDN_QDQ_W, the backward of the W-QDQ
+    forward: its quantized W enters the state gradient).
     dh: an empty tensor asks for no per-chunk gradient.
     Returns (dh, d_initial_state) or (dh, d_initial_state, d_v)."""
     _dev(k, "k", torch.bfloat16)

@@ -305,8 +305,6 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape, const void* q, const voi
   gdn_status_t st = check_shape(shape, false);
   if (st != GDN_OK) return st;
   if (shape->io_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh takes bf16 q, k and d_o");
-  if (shape->qdq_flags & GDN_QDQ_W)
-    return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh: the backward of a GDN_QDQ_W forward is not built");
   if (shape->qdq_flags & GDN_QDQ_INT8)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_INT8 is a decode-step codec");
   if (shape->gate_per_channel) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh supports the scalar gate only");

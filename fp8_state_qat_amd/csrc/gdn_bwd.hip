@@ -25,6 +25,17 @@
 // P^T columns and the e^gamma entries of those rows are zero, so they reach
 // no result.  bf16 inputs; fp32 operands enter the bf16 MFMA as hi + lo
 // pairs.
+//
+// The backward of a W-QDQ forward (kW): the forward's U' = T V - Wq h^T uses
+// Wq, the row-quantized W, and the quantizer's identity straight-through
+// rule leaves Wq fixed in the gradient of h, so the last term becomes
+//     dh_c = ... - dU'^T Wq      (in place of - Y^T (K o e^gamma) = - dU'^T W)
+// with Wq = diag(w_s) codes: the forward's own producer code writes the W
+// records (codes and row scales, bit for bit the forward's) into the
+// workspace first, and the row scales go into the B operand (- w_s o dU').
+// The codes come into LDS in place of the chunk's k dump once K dh^T has read
+// it (two more barriers per chunk); the k dump's other use, the key term of
+// the update, is the one they replace.
 #include "gdn_prep_item.hpp"
 
 namespace gdn {
@@ -48,9 +59,12 @@ struct BwdLds {
   static constexpr size_t oTT = oO + 64 * RS * 2;
   static constexpr size_t oPT = oTT + kBRecBytes;
   static constexpr size_t oVec = oPT + kBRecBytes;     // e^gamma [64] (0 past the end), e^{gamma_C - gamma} [64], e^{gamma_C}
-  static constexpr size_t buf = oVec + (2 * 64 + 4) * sizeof(float);  // one buffer
+  static constexpr size_t oWs = oVec + (2 * 64 + 4) * sizeof(float);  // the W record's row scales [64] (kW)
+  static constexpr size_t buf = oWs + 64 * sizeof(float);  // one buffer
   static constexpr size_t bytes = 2 * buf;
-  static_assert(oTT % 16 == 0 && oPT % 16 == 0 && buf % 16 == 0, "direct loads need 16-byte aligned LDS");
+  static_assert(oTT % 16 == 0 && oPT % 16 == 0 && oWs % 16 == 0 && buf % 16 == 0,
+                "direct loads need 16-byte aligned LDS");
+  static_assert(4 * NKB * F == (size_t)w_rec_bytes(DK) - 1024, "the W codes take the k dump's place");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -87,12 +101,13 @@ struct BwdArgs {
   float* dh;              // [n_bounds, H, dv, dk] or null
   float* dinit;           // [N, H, dv, dk] or null
   float* dvals;           // [T, H, dv] or null
+  const char* W;          // kW: one W record per (chunk, head)
   const int32_t* status;  // the workspace's status word (index check)
   int H;
   int dv;
 };
 
-template <int DK>
+template <int DK, bool kW>
 __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs args) {
   using Ls = BwdLds<DK>;
   using Fr = bf16x8;
@@ -129,6 +144,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
   // element offset of x[t][d] in a k/q dump
   auto kpos = [](int t, int d) {
     return (((t >> 4) * NKB + (d >> 5)) * 64 + rot_slot(((d & 31) >> 3) * 16 + (t & 15))) * 8 + (d & 7);
+  };
+  // element offset of W[t][d] in a W record (the k dump's order without its rotation)
+  auto wpos = [](int t, int d) {
+    return (((t >> 4) * NKB + (d >> 5)) * 64 + ((d & 31) >> 3) * 16 + (t & 15)) * 8 + (d & 7);
   };
 
   // ---- dh of this lane: dst[t][i] = dh[vcol0][dkmap(16t + 4gq + i)]
@@ -189,6 +208,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
       }
     }
     if (lw == 0) pg = (lane < nv) ? args.g[(int64_t)(t0 + lane) * H + h] : 0.f;
+    if constexpr (kW) {  // the chunk's W row scales (16 lanes of 16 bytes)
+      const char* wr = args.W + ((int64_t)(chunk0 + cc) * H + h) * w_rec_bytes(DK) + 4 * NKB * 1024;
+      if (lw == 1 && lane < 16) lds_load16(wr, (uint32_t)(lane * 16), base + (uint32_t)Ls::oWs);
+    }
+  };
+  // kW: the W codes of chunk cc into the k dump's place of buffer b (once K dh^T has read it)
+  auto issue_w = [&](int cc, int b) {
+    const char* wr = args.W + ((int64_t)(chunk0 + cc) * H + h) * w_rec_bytes(DK);
+    const uint32_t base = lds0 + (uint32_t)(b * Ls::buf) + (uint32_t)Ls::oK;
+#pragma unroll
+    for (int i = lw; i < 4 * NKB; i += kBwdLoadWaves)
+      lds_load16(wr, (uint32_t)((i * 64 + lane) * 16), base + i * 1024);
   };
   // loader wave 0: the gates of chunk cc from pg (e^gamma is zero past the chunk's end)
   auto scan = [&](int cc, float* vec) {
@@ -249,6 +280,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     __syncthreads();  // ... every wave's, and the gates; chunk c + 1's buffer is free
     if (loader) {
       if (c > 0) issue(c - 1, b ^ 1);
+      if constexpr (kW) {
+        __syncthreads();  // every compute wave has read the k dump of chunk c
+        issue_w(c, b);
+        wait_vmem();
+        __syncthreads();  // the W codes are in LDS
+      }
       continue;
     }
     if (c + 1 < n_chunks) store_results(c + 1);
@@ -276,6 +313,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
           mma_bf16(acc[tt], kf[tt * NKB + kb], dhl[kb]);
         }
     }
+    if constexpr (kW) __syncthreads();  // the k dump of chunk c is read: its place takes the W codes
     // ---- dO as B operands: element j of k-block kb = dO[32kb + kperm(gq, j)][16w + ln]
     Fr of[2];
 #pragma unroll
@@ -323,7 +361,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) pend_y[ti] = yacc[ti];
-    // ---- B operands of the update: e^gamma dO and -e^gamma Y, hi + lo
+    // ---- B operands of the update: e^gamma dO, and -e^gamma Y (kW: -w_s dU'), hi + lo
+    const float* ws = reinterpret_cast<const float*>(bufp + Ls::oWs);
     Fr boh[2], bol[2], byh[2], byl[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -338,44 +377,76 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
         o8[2 * q] = e8[2 * q] * bf16_lo(ow[q]);
         o8[2 * q + 1] = e8[2 * q + 1] * bf16_hi(ow[q]);
       }
+      if constexpr (kW) {
+        const float4 s0 = *reinterpret_cast<const float4*>(ws + 32 * kb + 4 * gq);
+        const float4 s1 = *reinterpret_cast<const float4*>(ws + 32 * kb + 16 + 4 * gq);
+        const float s8[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        y8[i] = -e8[i] * yacc[2 * kb][i];
-        y8[4 + i] = -e8[4 + i] * yacc[2 * kb + 1][i];
+        for (int i = 0; i < 4; ++i) {
+          y8[i] = -s8[i] * uacc[2 * kb][i];
+          y8[4 + i] = -s8[4 + i] * uacc[2 * kb + 1][i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y8[i] = -e8[i] * yacc[2 * kb][i];
+          y8[4 + i] = -e8[4 + i] * yacc[2 * kb + 1][i];
+        }
       }
       EngBF16::split(o8, boh[kb], bol[kb]);
       EngBF16::split(y8, byh[kb], byl[kb]);
     }
     // ---- dh^T <- e^{gamma_C} dh^T + Q^T (e^gamma dO) + K^T (-e^gamma Y)
+    //      (kW: + codes^T (-w_s dU'), the codes in the k dump's place)
     const float eC = vec[128];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[t][i] *= eC;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      // lane (gq, l) of each 16-lane group points at x[32kb + 16h + 4gq + l/4][dkmap(16t + 4(l%4)) .. +3]
+    // lane (gq, l) of each 16-lane group points at x[32kb + 16h + 4gq + l/4][dkmap(16t + 4(l%4)) .. +3]
+    auto tr_frags = [&](const uint16_t* base, auto pos, int t, Fr (&a)[2]) {
       const int d = dkmap(16 * t + 4 * (ln & 3));
       const int tq = 4 * gq + (ln >> 2);
-      Fr qa[2], ka[2];
-      {
-        const uint2 x0 = lds_read_tr16(sQ + kpos(tq, d)), x1 = lds_read_tr16(sQ + kpos(tq + 16, d));
-        const uint2 y0 = lds_read_tr16(sQ + kpos(tq + 32, d)), y1 = lds_read_tr16(sQ + kpos(tq + 48, d));
-        qa[0] = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
-        qa[1] = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
-      }
-      {
-        const uint2 x0 = lds_read_tr16(sK + kpos(tq, d)), x1 = lds_read_tr16(sK + kpos(tq + 16, d));
-        const uint2 y0 = lds_read_tr16(sK + kpos(tq + 32, d)), y1 = lds_read_tr16(sK + kpos(tq + 48, d));
-        ka[0] = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
-        ka[1] = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
-      }
+      const uint2 x0 = lds_read_tr16(base + pos(tq, d)), x1 = lds_read_tr16(base + pos(tq + 16, d));
+      const uint2 y0 = lds_read_tr16(base + pos(tq + 32, d)), y1 = lds_read_tr16(base + pos(tq + 48, d));
+      a[0] = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
+      a[1] = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
+    };
+    if constexpr (kW) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        mma_bf16(dst[t], qa[kb], boh[kb]);
-        mma_bf16(dst[t], qa[kb], bol[kb]);
-        mma_bf16(dst[t], ka[kb], byh[kb]);
-        mma_bf16(dst[t], ka[kb], byl[kb]);
+      for (int t = 0; t < NT; ++t) {
+        Fr qa[2];
+        tr_frags(sQ, kpos, t, qa);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          mma_bf16(dst[t], qa[kb], boh[kb]);
+          mma_bf16(dst[t], qa[kb], bol[kb]);
+        }
+      }
+      __syncthreads();  // the W codes of chunk c are in LDS
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        Fr wa[2];
+        tr_frags(sK, wpos, t, wa);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          mma_bf16(dst[t], wa[kb], byh[kb]);
+          mma_bf16(dst[t], wa[kb], byl[kb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        Fr qa[2], ka[2];
+        tr_frags(sQ, kpos, t, qa);
+        tr_frags(sK, kpos, t, ka);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          mma_bf16(dst[t], qa[kb], boh[kb]);
+          mma_bf16(dst[t], qa[kb], bol[kb]);
+          mma_bf16(dst[t], ka[kb], byh[kb]);
+          mma_bf16(dst[t], ka[kb], byl[kb]);
+        }
       }
     }
     // dst now holds dh_c, the gradient of the state entering chunk c
@@ -400,10 +471,12 @@ size_t bwd_workspace_bytes(const gdn_shape_t& s) {
   const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
   const size_t items = (size_t)(max_chunks * s.n_heads);
   const size_t offs_bytes = ((size_t)(s.n_seqs + 2) * 4 + 255) / 256 * 256;
-  return kStatusBytes + offs_bytes + items * kBRecBytes * 2;
+  // with W QDQ the forward's records too (its producer writes the W records)
+  const size_t fwd = (s.qdq_flags & GDN_QDQ_W) ? (size_t)(kTRecBytes + kPRecBytes + w_rec_bytes(s.dk)) : 0;
+  return kStatusBytes + offs_bytes + items * (kBRecBytes * 2 + fwd);
 }
 
-template <int DK>
+template <int DK, bool kW>
 static hipError_t launch_bwd_dk(const gdn_shape_t& s, const PrepArgs& pa, const BwdArgs& ba, int64_t items,
                                 hipStream_t stream) {
   {
@@ -419,7 +492,7 @@ static hipError_t launch_bwd_dk(const gdn_shape_t& s, const PrepArgs& pa, const 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  auto kern = chunk_bwd_dh_kernel<DK>;
+  auto kern = chunk_bwd_dh_kernel<DK, kW>;
   constexpr size_t lds = BwdLds<DK>::bytes;
   static bool attr_set = false;
   if (!attr_set) {
@@ -444,13 +517,20 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
   int32_t* offs = reinterpret_cast<int32_t*>(w + kStatusBytes);
   char* TT = w + kStatusBytes + offs_bytes;
   char* PT = TT + (size_t)items * kBRecBytes;
-  // chunk offsets of the whole sequences (prefix = length), status word
+  const bool wq = (s.qdq_flags & GDN_QDQ_W) != 0;
+  // chunk offsets of the whole sequences (prefix = length), status word; with
+  // W QDQ also the forward's records (T, P, W), by the forward's producer code
   PrepLayout L{};
   L.status = status;
   L.offs = offs;
   L.ready = nullptr;
   L.items = items;
-  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, nullptr, L, false, nullptr, nullptr, stream);
+  if (wq) {
+    L.T = PT + (size_t)items * kBRecBytes;
+    L.P = reinterpret_cast<char*>(L.T) + (size_t)items * kTRecBytes;
+    L.W = reinterpret_cast<char*>(L.P) + (size_t)items * kPRecBytes;
+  }
+  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, nullptr, L, wq, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   PrepArgs pa{};
   pa.q = q; pa.k = k; pa.beta = beta; pa.g = g; pa.cu_seqlens = cu_seqlens; pa.seq_lens = seq_lens;
@@ -471,9 +551,13 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
   ba.dinit = dinit;
   ba.dvals = dvals;
   ba.status = status;
+  ba.W = reinterpret_cast<const char*>(L.W);
   ba.H = s.n_heads;
   ba.dv = s.dv;
-  return s.dk == 128 ? launch_bwd_dk<128>(s, pa, ba, items, stream) : launch_bwd_dk<64>(s, pa, ba, items, stream);
+  if (wq) return s.dk == 128 ? launch_bwd_dk<128, true>(s, pa, ba, items, stream)
+                             : launch_bwd_dk<64, true>(s, pa, ba, items, stream);
+  return s.dk == 128 ? launch_bwd_dk<128, false>(s, pa, ba, items, stream)
+                     : launch_bwd_dk<64, false>(s, pa, ba, items, stream);
 }
 
 }  // namespace gdn

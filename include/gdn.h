@@ -306,11 +306,17 @@ gdn_status_t gdn_decode_step(const gdn_shape_t* shape,
  * with T, P, gamma as in the forward.  The straight-through QDQ leaves the
  * states out of it, so no forward state is needed.  Whole sequences (no
  * prefix/suffix split); scalar gate; bf16 q, k and d_o.
- *   shape       as for gdn_chunk_fwd (io_dtype GDN_BF16, gate_per_channel 0;
- *               o_dtype is not used).  qdq_flags are those of the forward: the
- *               state QDQ flags (CHUNK, WRITE) do not change the gradient under
- *               the identity straight-through rule; GDN_QDQ_W does (its W enters
- *               the state path) and returns GDN_ERR_UNSUPPORTED.
+ * The backward of a W-QDQ forward (GDN_QDQ_W): the forward's U' = T V -
+ * Wq h^T takes the row-quantized Wq = Q(W), which the quantizer's identity
+ * straight-through rule holds fixed in the gradient of h, so the last term
+ * is - dU'^T Wq; the call recomputes Wq with the forward's own code (bit for
+ * bit the forward's W records).  Y = T^T dU' stays the gradient of v.
+ *   shape       as for gdn_chunk_fwd (io_dtype GDN_BF16, gate_per_channel 0,
+ *               gate_grid_log2 0; o_dtype is not used).  qdq_flags are those of
+ *               the forward: the state QDQ flags (CHUNK, WRITE) do not change
+ *               the gradient under the identity straight-through rule;
+ *               GDN_QDQ_W selects the backward of the W-QDQ forward;
+ *               GDN_QDQ_INT8 (a decode-step codec) is refused.
  *   q, k        [total_tokens, H, dk] bf16;  beta, g [total_tokens, H] fp32
  *   cu_seqlens, seq_lens   as for gdn_chunk_fwd (seq_lens nullable)
  *   d_o         [total_tokens, H, dv] bf16, the gradient of o (padding rows ignored)
@@ -337,7 +343,8 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape,
 
 /* Device workspace bytes gdn_chunk_bwd_dh needs: the status word, the chunk offsets and, per
  * (chunk, head) of the worst-case chunk count, T^T and P^T as full 64 x 64
- * records (16 KiB each).  0 for an invalid shape. */
+ * records (16 KiB each), and with GDN_QDQ_W the forward's T, P and W records
+ * of gdn_chunk_fwd's workspace.  0 for an invalid shape. */
 size_t gdn_chunk_bwd_workspace_bytes(const gdn_shape_t* shape);
 
 /* Static description of a status code. */

@@ -87,3 +87,75 @@ def packed_state_grads(q, k, beta, g, do, cu_seqlens, *, seq_lens=None, dS_L=Non
             dS0[n, h] = r_0
             dvals[sl, h] = r_v
     return dh, dS0, dvals
+
+
+def chunked_state_grads(q, k, beta, g, do, dS_L=None, *, w_qdq=False, want_dv=False, Wq=None):
+    """The same gradients through the chunk-level forward of the chunked
+    prefix (one (sequence, head), the whole sequence chunked by 64), which is
+    where W QDQ lives.  Per chunk with entering state h, the forward
+    (oracle.chunked.chunk_step) is
+        U' = T V - Wq h^T,   O = (Q o e^gamma) h^T + P U',
+        h' = h e^{gamma_n} + U'^T (K o e^{gamma_n - gamma})
+    with Wq = Q(W) under W QDQ (else W = T (K o e^gamma)); the quantizer's
+    identity straight-through rule (#2497 page, "What does this PR do?")
+    makes the gradient of h the one of that linear map with Wq fixed, so
+    with G' = dL/dh' and dO the chunk's output gradient, backwards:
+        dU' = P^T dO + (K o e^{gamma_n - gamma}) G'^T
+        dh  = G' e^{gamma_n} + dO^T (Q o e^gamma) - dU'^T Wq
+        dV  = T^T dU'                     (V enters only through U = T V)
+    (e^{gamma_n} multiplies columns, i.e. key channels, for the
+    per-key-channel gate).  Without W QDQ this equals state_grads.  Wq:
+    optional [n_chunks, 64, dk] matrices used as each chunk's Wq (rows past
+    the chunk's end ignored; teacher forcing).  Returns (dh [n_chunks, dv,
+    dk], dS0) and with want_dv also dv [L, dv]."""
+    from .chunked import chunk_operators
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    beta = np.asarray(beta, np.float64)
+    g = np.asarray(g, np.float64)
+    do = np.asarray(do, np.float64)
+    L, dk = k.shape
+    dv = do.shape[1]
+    G = np.zeros((dv, dk)) if dS_L is None else np.array(dS_L, dtype=np.float64)
+    nb = (L + CHUNK - 1) // CHUNK
+    dh = np.zeros((nb, dv, dk))
+    dvals = np.zeros((L, dv))
+    for c in range(nb - 1, -1, -1):
+        c0, c1 = c * CHUNK, min(L, (c + 1) * CHUNK)
+        op = chunk_operators(q[c0:c1], k[c0:c1], beta[c0:c1], g[c0:c1], w_qdq=w_qdq,
+                             Wq=None if Wq is None else np.asarray(Wq[c][:c1 - c0], np.float64))
+        dO = do[c0:c1]
+        dU = op["Pm"].T @ dO + (k[c0:c1] * op["egn"]) @ G.T
+        dvals[c0:c1] = op["T"].T @ dU
+        G = G * op["end"] + dO.T @ (q[c0:c1] * op["eg"]) - dU.T @ op["Wq"]
+        dh[c] = G
+    if want_dv:
+        return dh, G, dvals
+    return dh, G
+
+
+def packed_chunked_state_grads(q, k, beta, g, do, cu_seqlens, *, seq_lens=None, dS_L=None, w_qdq=False):
+    """packed_state_grads through chunked_state_grads (the W-QDQ forward's
+    gradients with w_qdq)."""
+    cu = np.asarray(cu_seqlens, np.int64)
+    N = cu.size - 1
+    H, dk = k.shape[1], k.shape[2]
+    dv = do.shape[2]
+    lens = (cu[1:] - cu[:-1]) if seq_lens is None else np.asarray(seq_lens, np.int64)
+    nbs = [(int(L) + CHUNK - 1) // CHUNK for L in lens]
+    offs = np.concatenate([[0], np.cumsum(nbs)]).astype(np.int64)
+    dh = np.zeros((int(offs[-1]), H, dv, dk))
+    dS0 = np.zeros((N, H, dv, dk))
+    dvals = np.zeros(do.shape)
+    for n in range(N):
+        s0, L = int(cu[n]), int(lens[n])
+        sl = slice(s0, s0 + L)
+        for h in range(H):
+            gg = g[sl, h] if g.ndim == 2 else g[sl, h, :]
+            r_dh, r_0, r_v = chunked_state_grads(q[sl, h], k[sl, h], beta[sl, h], gg, do[sl, h],
+                                                 None if dS_L is None else dS_L[n, h], w_qdq=w_qdq,
+                                                 want_dv=True)
+            dh[offs[n]:offs[n + 1], h] = r_dh
+            dS0[n, h] = r_0
+            dvals[sl, h] = r_v
+    return dh, dS0, dvals

@@ -47,13 +47,13 @@ def qdq_w(W):
     return out.astype(np.float64), sc
 
 
-def chunk_step(Q, K, V, b, g, S, *, w_qdq=False, Wq=None):
-    """One chunk of n <= 64 tokens from state S (dv x dk), all fp64.
-
-    g: [n] (scalar gate) or [n, dk].  Wq: optional n x dk matrix used in
-    place of the (quantized) W (teacher forcing).  Returns dict(o [n, dv],
-    S [dv, dk] before any boundary QDQ, W [n, dk] before QDQ, Wq [n, dk]
-    the matrix that entered W S^T, w_scales [n] or None)."""
+def chunk_operators(Q, K, b, g, *, w_qdq=False, Wq=None):
+    """The state-independent operators of one chunk of n <= 64 tokens, fp64:
+    T = (I + A)^-1 diag(b), W = T (K o e^gamma), Wq (the quantized W with
+    w_qdq, else W; a given Wq is used as is), Pm (P[r][s] = e^{gamma_r -
+    gamma_s} q_r . k_s for s <= r), eg = e^gamma, egn = e^{gamma_n - gamma}
+    ([n, 1] for the scalar gate, [n, dk] per channel) and end = e^{gamma_n}
+    (the decay of the entering state)."""
     n = K.shape[0]
     lower = np.tril(np.ones((n, n), dtype=bool), -1)
     if g.ndim == 2:
@@ -78,13 +78,26 @@ def chunk_step(Q, K, V, b, g, S, *, w_qdq=False, Wq=None):
         end = np.exp(gam[-1])
     T = np.linalg.solve(np.eye(n) + A, np.diag(b))
     W = T @ (K * eg)
-    U = T @ V
     w_scales = None
     if Wq is None:
         if w_qdq:
             Wq, w_scales = qdq_w(W)
         else:
             Wq = W
+    return dict(T=T, W=W, Wq=Wq, w_scales=w_scales, Pm=Pm, eg=eg, egn=egn, end=end)
+
+
+def chunk_step(Q, K, V, b, g, S, *, w_qdq=False, Wq=None):
+    """One chunk of n <= 64 tokens from state S (dv x dk), all fp64.
+
+    g: [n] (scalar gate) or [n, dk].  Wq: optional n x dk matrix used in
+    place of the (quantized) W (teacher forcing).  Returns dict(o [n, dv],
+    S [dv, dk] before any boundary QDQ, W [n, dk] before QDQ, Wq [n, dk]
+    the matrix that entered W S^T, w_scales [n] or None)."""
+    op = chunk_operators(Q, K, b, g, w_qdq=w_qdq, Wq=Wq)
+    T, W, Wq, w_scales = op["T"], op["W"], op["Wq"], op["w_scales"]
+    Pm, eg, egn, end = op["Pm"], op["eg"], op["egn"], op["end"]
+    U = T @ V
     Up = U - Wq @ S.T
     o = (Q * eg) @ S.T + Pm @ Up
     S_new = S * end + Up.T @ (K * egn)

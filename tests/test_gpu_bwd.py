@@ -14,7 +14,8 @@ import torch
 
 from fp8_state_qat_amd import api
 from fp8_state_qat_amd import inputs as gi
-from oracle.backward import packed_state_grads, state_grads
+from fp8_state_qat_amd import _lib
+from oracle.backward import chunked_state_grads, packed_state_grads, state_grads
 
 from helpers import rel_l2
 
@@ -31,10 +32,11 @@ def _case(lens, H, dk, dv, seed, pads=None, pad_fill=None):
     return w, do, dS
 
 
-def _run(w, do, dS, want_dv=False):
+def _run(w, do, dS, want_dv=False, flags=0):
     d = gi.device_tensors(w)
     out = api.chunk_bwd_dh(d["q"], d["k"], d["beta"], d["g"], d["cu_seqlens"], gi.to_torch(do, "cuda"),
-                           seq_lens=d["seq_lens"], d_final_state=torch.from_numpy(dS).cuda(), want_dv=want_dv)
+                           seq_lens=d["seq_lens"], d_final_state=torch.from_numpy(dS).cuda(), want_dv=want_dv,
+                           qdq_flags=flags)
     torch.cuda.synchronize()
     return tuple(x.cpu().numpy() for x in out)
 
@@ -117,3 +119,55 @@ def test_bwd_without_dh_output_same_results():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(d0_b.cpu().numpy(), d0)
     np.testing.assert_array_equal(dv_b.cpu().numpy(), dval)
+
+
+def _forward_wq(w):
+    """The W-QDQ forward's quantized W of every chunk ([n_bounds, H, 64, dk]
+    fp32, debug w_post) and the chunk offsets."""
+    d = gi.device_tensors(w)
+    nb = [(int(L) + 63) // 64 for L in w.seq_lens]
+    offs = np.concatenate([[0], np.cumsum(nb)]).astype(np.int32)
+    wpost = torch.zeros((int(offs[-1]), w.n_heads, 64, w.dk), device="cuda")
+    api.chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["cu_seqlens"], seq_lens=d["seq_lens"],
+                  qdq_flags=3 | _lib.GDN_QDQ_W,
+                  debug=dict(bound_offsets=torch.from_numpy(offs).cuda(), w_post=wpost))
+    torch.cuda.synchronize()
+    return wpost.cpu().numpy(), offs
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 256)])
+def test_bwd_dh_w_qdq_against_oracle(dk, dv):
+    """The backward of a W-QDQ forward (identity straight-through rule on the
+    W quantizer): the state term takes the forward's quantized W.  The
+    oracle's chunk-level backward (pinned by exact differences of the W-QDQ
+    forward oracle) runs with the GPU forward's own quantized W (teacher
+    forcing, so a W code that rounds the other way at a tie does not count):
+    dh, the initial-state gradient and d_v within 1e-4 (the measured error
+    is about 1e-6; W QDQ itself moves the gradient by about 3e-3, so a
+    backward that used the unquantized W fails).  Free-running (the oracle
+    quantizes its own W) within the bf16 gate.  Ragged lengths, an empty
+    sequence, one token."""
+    w, do, dS = _case([300, 0, 1, 64, 129], 2, dk, dv, seed=131 + dk + dv)
+    dh, d0, dval = _run(w, do, dS, want_dv=True, flags=3 | _lib.GDN_QDQ_W)
+    wq, offs = _forward_wq(w)
+    q, k, b, g, dof = w.f64("q"), w.f64("k"), w.f64("beta"), w.f64("g"), _do_f64(do)
+    ref_dh, ref_d0, ref_dv = np.zeros_like(dh), np.zeros_like(d0), np.zeros_like(dval)
+    own_dh = np.zeros_like(dh)
+    for n in range(len(w.seq_lens)):
+        s0, L = int(w.cu_seqlens[n]), int(w.seq_lens[n])
+        sl = slice(s0, s0 + L)
+        for h in range(w.n_heads):
+            r_dh, r_0, r_v = chunked_state_grads(q[sl, h], k[sl, h], b[sl, h], g[sl, h], dof[sl, h], dS[n, h],
+                                                 w_qdq=True, want_dv=True, Wq=wq[offs[n]:offs[n + 1], h])
+            ref_dh[offs[n]:offs[n + 1], h], ref_d0[n, h], ref_dv[sl, h] = r_dh, r_0, r_v
+            own_dh[offs[n]:offs[n + 1], h] = chunked_state_grads(q[sl, h], k[sl, h], b[sl, h], g[sl, h],
+                                                                 dof[sl, h], dS[n, h], w_qdq=True)[0]
+    r1, r0, rv = rel_l2(dh, ref_dh), rel_l2(d0, ref_d0), rel_l2(dval, ref_dv)
+    plain, _ = packed_state_grads(q, k, b, g, dof, w.cu_seqlens, seq_lens=w.seq_lens, dS_L=dS)[:2]
+    print(f"dk={dk} dv={dv} W QDQ: teacher-forced dh rel={r1:.3e} d_initial rel={r0:.3e} d_v rel={rv:.3e}; "
+          f"free-running dh rel={rel_l2(dh, own_dh):.3e}; against the plain backward {rel_l2(dh, plain):.3e}",
+          flush=True)
+    assert r1 <= 1e-4 and r0 <= 1e-4 and rv <= 1e-4
+    assert rel_l2(dh, own_dh) <= TOL
+    assert rel_l2(dh, plain) > 10 * r1
+    np.testing.assert_array_equal(d0[1], dS[1])

@@ -729,3 +729,66 @@ def test_grid_fine_step_approaches_no_grid():
     fine = orc.gdn_sequence(q, k, v, b, g, prefix_len=10, flags=0, grid_log2=24)
     rel = np.linalg.norm(fine["S"] - base["S"]) / np.linalg.norm(base["S"])
     assert 0 < rel < 1e-6
+
+
+# --------------------------------------------------------------------------
+# The backward of the W-QDQ forward (identity straight-through rule on the
+# W quantizer): the chunk-level reverse recurrence.
+# --------------------------------------------------------------------------
+from oracle.backward import chunked_state_grads  # noqa: E402
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_chunked_grads_equal_token_grads_without_w_qdq(per_channel):
+    """Without W QDQ the chunk-level backward is the token backward
+    regrouped (an algebraic identity): dh per chunk, dS0 and dv agree to
+    1e-12 relative."""
+    L, dk, dv = 150, 64, 64
+    q, k, v, b, g = _seq(L, dk, dv, per_channel=per_channel, seed=101,
+                         g_scale=0.05 if per_channel else 0.1)
+    rng = np.random.default_rng(102)
+    do = rng.standard_normal((L, dv))
+    dS = rng.standard_normal((dv, dk))
+    t_dh, t_0, t_v = state_grads(q, k, b, g, do, dS, want_dv=True)
+    c_dh, c_0, c_v = chunked_state_grads(q, k, b, g, do, dS, want_dv=True)
+    for x, y in ((c_dh, t_dh), (c_0, t_0), (c_v, t_v)):
+        assert np.linalg.norm(x - y) <= 1e-12 * np.linalg.norm(y)
+
+
+def _wq_loss(q, k, v, b, g, do, dS, S0):
+    """L = sum_t o_t . do_t + <S_L, dS> by the chunked forward oracle with W
+    QDQ and no state QDQ: affine in S0 and in v, since the quantized W
+    depends on k, beta and g alone."""
+    r = gdn_chunked(q, k, v, b, g, qdq=False, w_qdq=True, S0=S0)
+    return float(np.sum(r["o"] * do) + np.sum(r["S"] * dS))
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_w_qdq_grads_against_forward_differences(per_channel):
+    """The W-QDQ forward is affine in the initial state and the values, so
+    <dS0, U> = L(S0 + U) - L(S0) and <dv_t, u> = L(v + u e_t) - L(v) hold
+    exactly (to fp64 rounding) for the gradient of that forward.  Catches a
+    backward that uses the unquantized W (the difference is the W
+    quantization error, far above the bound) or drops a term."""
+    L, dk, dv = 150, 64, 64
+    q, k, v, b, g = _seq(L, dk, dv, per_channel=per_channel, seed=103,
+                         g_scale=0.05 if per_channel else 0.1)
+    rng = np.random.default_rng(104)
+    do = rng.standard_normal((L, dv))
+    dS = rng.standard_normal((dv, dk))
+    S0 = rng.standard_normal((dv, dk)) * 0.3
+    _, dS0, dvals = chunked_state_grads(q, k, b, g, do, dS, w_qdq=True, want_dv=True)
+    base = _wq_loss(q, k, v, b, g, do, dS, S0)
+    for _ in range(3):
+        U = rng.standard_normal((dv, dk))
+        d = _wq_loss(q, k, v, b, g, do, dS, S0 + U) - base
+        assert abs(d - np.sum(dS0 * U)) <= 1e-9 * max(1.0, abs(d))
+    for t in (0, 63, 64, 149):
+        u = rng.standard_normal(dv)
+        v2 = v.copy()
+        v2[t] += u
+        d = _wq_loss(q, k, v2, b, g, do, dS, S0) - base
+        assert abs(d - dvals[t] @ u) <= 1e-9 * max(1.0, abs(d))
+    # the plain backward is not the gradient of this forward
+    _, dS0_plain = state_grads(q, k, b, g, do, dS)
+    assert np.linalg.norm(dS0_plain - dS0) > 1e-4 * np.linalg.norm(dS0)
