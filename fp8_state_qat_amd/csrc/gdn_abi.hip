@@ -307,7 +307,9 @@ gdn_status_t gdn_chunk_bwd_dh(const gdn_shape_t* shape, const void* q, const voi
   if (shape->io_dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh takes bf16 q, k and d_o");
   if (shape->qdq_flags & GDN_QDQ_INT8)
     return fail(GDN_ERR_UNSUPPORTED, "GDN_QDQ_INT8 is a decode-step codec");
-  if (shape->gate_per_channel) return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh supports the scalar gate only");
+  if (shape->gate_per_channel && (shape->qdq_flags & GDN_QDQ_W))
+    return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_bwd_dh: the per-key-channel gate's backward is the token "
+                "recurrence, which has no W; the backward of a per-channel W-QDQ forward is not built");
   if (shape->gate_grid_log2 != 0)
     return fail(GDN_ERR_INVALID_ARG, "gdn_chunk_bwd_dh covers fully chunked sequences, which have no "
                 "recurrent writes: gate_grid_log2 must be 0");

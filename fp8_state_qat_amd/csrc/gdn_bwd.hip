@@ -467,10 +467,150 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
   }
 }
 
+// ---------------------------------------------------------------------------
+// Per-key-channel gate: the reverse token recurrence itself (the oracle's
+// form, written out per token; the gradient is linear in the states, so no
+// forward state enters).  With G the gradient of the state after token t
+// (rows: the tile's 64 value channels, columns: dk key channels), from
+// G = d_final_state, for t = L .. 1:
+//     G  += do_t q_t^T                      (o_t = S_t q_t)
+//     y   = G k_t,   d_v[t] = beta_t y      (v_t enters through beta_t v_t k_t^T)
+//     G  <- (G - beta_t y k_t^T) diag(exp(g_t))   (now the gradient of S_{t-1})
+// and dh of chunk c is G once token 64c + 1 is taken back.  One workgroup
+// (256 threads) per (sequence, head, 64-row value tile) with G in registers,
+// in the decode step's layout (thread t: float4 column group t % (dk/4) of
+// rows t / (dk/4) + p * 256 / (dk/4)); row dot products by the decode step's
+// fixed DPP tree.  The tokens of a chunk are staged in LDS as fp32 (q, k,
+// exp(g), the tile's d_o columns, beta) and its value gradients leave from
+// LDS as whole rows.  Vector ALU bound (about 4 * 64 * dk FMAs per token and
+// tile); no split-bf16 products, so fp32 throughout.
+template <int DK>
+struct KdaBwdLds {
+  static constexpr size_t oQ = 0, oK = oQ + 64 * DK, oE = oK + 64 * DK, oO = oE + 64 * DK;
+  static constexpr size_t oB = oO + 64 * 64, oDV = oB + 64;
+  static constexpr size_t floats = oDV + 64 * 64;
+  static constexpr size_t bytes = floats * sizeof(float);
+  static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
+};
+
+struct KdaBwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const float* beta;
+  const float* g;         // [T, H, dk]
+  const uint16_t* dout;
+  const float* dfin;
+  const int32_t* cu_seqlens;
+  const int32_t* seq_lens;
+  const int32_t* chunk_offs;
+  float* dh;
+  float* dinit;
+  float* dvals;
+  const int32_t* status;
+  int H;
+  int dv;
+};
+
+template <int DK>
+__global__ __launch_bounds__(kThreads) void kda_bwd_token_kernel(KdaBwdArgs a) {
+  using Ls = KdaBwdLds<DK>;
+  constexpr int F = DK / 4;          // float4 per state row
+  constexpr int RPP = kThreads / F;  // rows per pass
+  constexpr int NP = kTileRows / RPP;
+  extern __shared__ __align__(16) float kb_smem[];
+  if (index_check_failed(a.status)) return;
+  float* sq = kb_smem + Ls::oQ;
+  float* sk = kb_smem + Ls::oK;
+  float* se = kb_smem + Ls::oE;
+  float* so = kb_smem + Ls::oO;
+  float* sb = kb_smem + Ls::oB;
+  float* sdv = kb_smem + Ls::oDV;
+  const int t = threadIdx.x, c4 = t % F, rr = t / F;
+  const int H = a.H, dv = a.dv, tiles = dv / kTileRows;
+  const int vt = (int)blockIdx.x % tiles, nh = (int)blockIdx.x / tiles;
+  const int h = nh % H, n = nh / H;
+  const int seg0 = a.cu_seqlens[n];
+  const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
+  const int n_chunks = (L + kChunk - 1) / kChunk;
+  const int chunk0 = a.chunk_offs[n];
+  const int64_t qk_row = (int64_t)H * DK, v_row = (int64_t)H * dv;
+  const int64_t tile = ((int64_t)nh * dv + kTileRows * vt) * DK;  // row 0 of the tile in [N, H, dv, dk]
+
+  float4 G[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    G[p] = a.dfin ? reinterpret_cast<const float4*>(a.dfin + tile)[t + kThreads * p] : make_float4(0.f, 0.f, 0.f, 0.f);
+
+  for (int c = n_chunks - 1; c >= 0; --c) {
+    const int t0 = c * kChunk;
+    const int nv = min(kChunk, L - t0);
+    __syncthreads();  // the last chunk's staged tokens and value gradients are consumed
+    for (int i = t; i < kChunk * DK; i += kThreads) {
+      const int tok = i / DK, col = i % DK;
+      const bool ok = tok < nv;
+      const int64_t row = seg0 + t0 + tok;
+      sq[i] = ok ? bf16_bits_to_float(a.q[row * qk_row + (int64_t)h * DK + col]) : 0.f;
+      sk[i] = ok ? bf16_bits_to_float(a.k[row * qk_row + (int64_t)h * DK + col]) : 0.f;
+      se[i] = ok ? expf(a.g[row * qk_row + (int64_t)h * DK + col]) : 1.f;
+    }
+    for (int i = t; i < kChunk * kTileRows; i += kThreads) {
+      const int tok = i / kTileRows, r = i % kTileRows;
+      so[i] = tok < nv ? bf16_bits_to_float(a.dout[(seg0 + t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + r])
+                       : 0.f;
+    }
+    if (t < kChunk) sb[t] = t < nv ? a.beta[(int64_t)(seg0 + t0 + t) * H + h] : 0.f;
+    __syncthreads();
+    for (int tok = nv - 1; tok >= 0; --tok) {
+      const float4 qv = reinterpret_cast<const float4*>(sq + tok * DK)[c4];
+      const float4 kv = reinterpret_cast<const float4*>(sk + tok * DK)[c4];
+      const float4 ev = reinterpret_cast<const float4*>(se + tok * DK)[c4];
+      const float b = sb[tok];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int r = rr + RPP * p;
+        const float dor = so[tok * kTileRows + r];
+        G[p].x = fmaf(dor, qv.x, G[p].x);
+        G[p].y = fmaf(dor, qv.y, G[p].y);
+        G[p].z = fmaf(dor, qv.z, G[p].z);
+        G[p].w = fmaf(dor, qv.w, G[p].w);
+        const float y = group_sum<F>(G[p].x * kv.x + G[p].y * kv.y + G[p].z * kv.z + G[p].w * kv.w);
+        const float by = b * y;
+        if (c4 == 0) sdv[tok * kTileRows + r] = by;
+        G[p].x = (G[p].x - by * kv.x) * ev.x;
+        G[p].y = (G[p].y - by * kv.y) * ev.y;
+        G[p].z = (G[p].z - by * kv.z) * ev.z;
+        G[p].w = (G[p].w - by * kv.w) * ev.w;
+      }
+    }
+    if (a.dh) {  // the gradient of the state entering chunk c
+      float4* dst = reinterpret_cast<float4*>(a.dh + (((int64_t)(chunk0 + c) * H + h) * dv + kTileRows * vt) * DK);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) dst[t + kThreads * p] = G[p];
+    }
+    __syncthreads();  // the chunk's value gradients are in LDS
+    if (a.dvals) {
+      for (int i = t; i < nv * kTileRows; i += kThreads) {
+        const int tok = i / kTileRows, r = i % kTileRows;
+        a.dvals[(seg0 + t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + r] = sdv[i];
+      }
+    }
+  }
+  if (a.dinit) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) reinterpret_cast<float4*>(a.dinit + tile)[t + kThreads * p] = G[p];
+  }
+  if (a.dvals) {  // padding rows of the segment
+    const int seg_len = a.cu_seqlens[n + 1] - seg0;
+    for (int i = L * kTileRows + t; i < seg_len * kTileRows; i += kThreads)
+      a.dvals[(seg0 + i / kTileRows) * v_row + (int64_t)h * dv + kTileRows * vt + i % kTileRows] = 0.f;
+  }
+}
+
 size_t bwd_workspace_bytes(const gdn_shape_t& s) {
   const int64_t max_chunks = (s.total_tokens + kChunk - 1) / kChunk + s.n_seqs;
   const size_t items = (size_t)(max_chunks * s.n_heads);
   const size_t offs_bytes = ((size_t)(s.n_seqs + 2) * 4 + 255) / 256 * 256;
+  if (s.gate_per_channel) return kStatusBytes + offs_bytes;  // the token recurrence needs no records
   // with W QDQ the forward's records too (its producer writes the W records)
   const size_t fwd = (s.qdq_flags & GDN_QDQ_W) ? (size_t)(kTRecBytes + kPRecBytes + w_rec_bytes(s.dk)) : 0;
   return kStatusBytes + offs_bytes + items * (kBRecBytes * 2 + fwd);
@@ -532,6 +672,33 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
   }
   hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, nullptr, L, wq, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
+  if (s.gate_per_channel) {
+    KdaBwdArgs ka{};
+    ka.q = reinterpret_cast<const uint16_t*>(q);
+    ka.k = reinterpret_cast<const uint16_t*>(k);
+    ka.beta = beta;
+    ka.g = g;
+    ka.dout = reinterpret_cast<const uint16_t*>(dout);
+    ka.dfin = dfin;
+    ka.cu_seqlens = cu_seqlens;
+    ka.seq_lens = seq_lens;
+    ka.chunk_offs = offs;
+    ka.dh = dh;
+    ka.dinit = dinit;
+    ka.dvals = dvals;
+    ka.status = status;
+    ka.H = s.n_heads;
+    ka.dv = s.dv;
+    const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
+    auto go = [&](auto kern, size_t lds) {
+      hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e2 != hipSuccess) return e2;
+      hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreads), lds, stream, ka);
+      return hipGetLastError();
+    };
+    return s.dk == 128 ? go(kda_bwd_token_kernel<128>, KdaBwdLds<128>::bytes)
+                       : go(kda_bwd_token_kernel<64>, KdaBwdLds<64>::bytes);
+  }
   PrepArgs pa{};
   pa.q = q; pa.k = k; pa.beta = beta; pa.g = g; pa.cu_seqlens = cu_seqlens; pa.seq_lens = seq_lens;
   pa.prefix_lens = nullptr; pa.offs = offs; pa.T = TT; pa.P = PT; pa.N = s.n_seqs; pa.H = s.n_heads;

@@ -204,8 +204,9 @@ def test_chunk_bwd_dh_checks():
     """Workspace: the status word and chunk offsets plus two 16 KiB records
     (T^T, P^T) per chunk and head of the worst-case count, and for the
     backward of a W-QDQ forward also the forward's T (18 KiB), P (12 KiB)
-    and W (dk * 128 + 1 KiB) records; bf16 and the scalar gate only; the
-    INT8 decode codec refused; at least one output; buffers aligned."""
+    and W (dk * 128 + 1 KiB) records (the per-channel gate's token
+    recurrence needs none, and has no W-QDQ backward); bf16 only; the INT8
+    decode codec refused; at least one output; buffers aligned."""
     L = _lib.lib()
     s = _shape(n_seqs=3, n_heads=2, total_tokens=130)
     assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(s)) == 256 + 256 + (3 + 3) * 2 * 2 * 16384
@@ -213,7 +214,10 @@ def test_chunk_bwd_dh_checks():
     assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(sw)) == \
         256 + 256 + (3 + 3) * 2 * (2 * 16384 + 18432 + 12288 + 128 * 128 + 1024)
     assert _bwd(_shape(io_dtype=0, dk=64)) == 2
-    assert _bwd(_shape(gate_per_channel=1)) == 2
+    sp = _shape(n_seqs=3, n_heads=2, total_tokens=130, gate_per_channel=1)
+    assert L.gdn_chunk_bwd_workspace_bytes(ctypes.byref(sp)) == 256 + 256   # the token recurrence: no records
+    assert _bwd(_shape(gate_per_channel=1, qdq_flags=3 | _lib.GDN_QDQ_W)) == 2
+    assert _bwd(_shape(gate_per_channel=1)) == 3   # accepted on the host; no device here
     assert _bwd(_shape(qdq_flags=3 | _lib.GDN_QDQ_INT8)) == 2
     assert _bwd(_shape(gate_grid_log2=8)) == 1   # no recurrent writes in a fully chunked backward
     assert "gate_grid_log2" in _lib.last_error()

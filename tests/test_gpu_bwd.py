@@ -24,8 +24,9 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _case(lens, H, dk, dv, seed, pads=None, pad_fill=None):
-    w = gi.make_packed(lens, H, dk, dv, io_dtype=gi.BF16, seed=seed, pads=pads, pad_fill=pad_fill)
+def _case(lens, H, dk, dv, seed, pads=None, pad_fill=None, per_channel=False):
+    w = gi.make_packed(lens, H, dk, dv, io_dtype=gi.BF16, seed=seed, pads=pads, pad_fill=pad_fill,
+                       per_channel=per_channel, g_scale=0.05 if per_channel else 0.1)
     rng = np.random.default_rng(seed + 1)
     do = gi._round_io(rng.standard_normal((w.total_tokens, H, dv)), gi.BF16)
     dS = rng.standard_normal((len(lens), H, dv, dk)).astype(np.float32)
@@ -171,3 +172,40 @@ def test_bwd_dh_w_qdq_against_oracle(dk, dv):
     assert rel_l2(dh, own_dh) <= TOL
     assert rel_l2(dh, plain) > 10 * r1
     np.testing.assert_array_equal(d0[1], dS[1])
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 256)])
+def test_bwd_per_channel_gate_against_oracle(dk, dv):
+    """The per-key-channel gate's backward (the reverse token recurrence on
+    the GPU): dh of every chunk, the initial-state gradient and d_v against
+    the oracle's token backward (pinned by exact differences of the forward
+    oracle with the per-channel gate).  fp32 arithmetic on bf16-valued
+    inputs, so within the fp32 gate of 1e-5 (measured: about 1e-7); ragged lengths,
+    an empty sequence, one token; padding rows of d_v zero."""
+    w, do, dS = _case([300, 0, 1, 64, 129], 2, dk, dv, seed=151 + dk + dv, per_channel=True)
+    dh, d0, dval = _run(w, do, dS, want_dv=True)
+    ref_dh, ref_d0, ref_dv = packed_state_grads(w.f64("q"), w.f64("k"), w.f64("beta"), w.f64("g"), _do_f64(do),
+                                                w.cu_seqlens, seq_lens=w.seq_lens, dS_L=dS)
+    r1, r0, rv = rel_l2(dh, ref_dh), rel_l2(d0, ref_d0), rel_l2(dval, ref_dv)
+    print(f"per-channel dk={dk} dv={dv}: dh rel={r1:.3e} d_initial rel={r0:.3e} d_v rel={rv:.3e}", flush=True)
+    assert dh.shape == ref_dh.shape and dval.shape == ref_dv.shape
+    assert r1 <= 1e-5 and r0 <= 1e-5 and rv <= 1e-5
+    np.testing.assert_array_equal(d0[1], dS[1])
+
+
+def test_bwd_per_channel_gate_nan_padding_changes_nothing():
+    """Per-channel gate: NaN in every padding row of q, k, v, beta, g and d_o
+    changes no gradient, and d_v's padding rows are zero."""
+    lens, pads = [130, 5, 64], [3, 61, 0]
+    w, do, dS = _case(lens, 2, 128, 128, seed=157, pads=pads, per_channel=True)
+    wn, _, _ = _case(lens, 2, 128, 128, seed=157, pads=pads, pad_fill=np.nan, per_channel=True)
+    valid = np.zeros(w.total_tokens, bool)
+    for n in range(3):
+        valid[w.cu_seqlens[n]:w.cu_seqlens[n] + w.seq_lens[n]] = True
+    don = do.copy()
+    don[~valid] = gi._round_io(np.full(don[~valid].shape, np.nan), gi.BF16)
+    a = _run(w, do, dS, want_dv=True)
+    b = _run(wn, don, dS, want_dv=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert np.all(b[2][~valid] == 0)
