@@ -51,6 +51,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 T_RECORD_BYTES = 18432         # per (chunk, head): T = (I + A)^-1 diag(beta) as hi, mid, lo bf16 planes
 P_RECORD_BYTES = 12288         # per (chunk, head): the decayed, masked P = Q K^T as hi + lo bf16 planes
 BF16_MFMA_PEAK_TFLOPS = 2516.6 # MI355X dense bf16 MFMA, TFLOP/s
+# MI355X fp32 vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed fp32) x 2.4 GHz;
+# without packed fp32 instructions (not used here) the ceiling is half of it
+FP32_VALU_PEAK_TFLOPS = 157.3
 METRIC = "GDN chunked-prefill tokens/s + MFMA %peak; decode step HBM GB/s, 1×MI355X"
 
 
@@ -103,6 +106,24 @@ def decode_bytes(n_heads_seqs, dk, dv, io_bytes, o_bytes):
     """Per decode step: the fp32 state read and written once, q, k, v read,
     beta and g read, o written."""
     return n_heads_seqs * (2 * 4 * dv * dk + io_bytes * (2 * dk + dv) + 8 + o_bytes * dv)
+
+
+# the sources of the headline launch (its traffic summary is keyed by their hash)
+PREFILL_SOURCES = ("gdn_chunk_bf16.hip", "gdn_chunk.hip", "gdn_chunk_common.hpp", "gdn_device.hpp",
+                   "gdn_prep_item.hpp")
+
+
+def copy_calibration(dev, mib):
+    """One plain device copy of mib MiB (the PMC byte counters read for it
+    calibrate those of the kernels).  Returns the bytes copied."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    return n * 4
 
 
 def source_hash(paths):
@@ -232,7 +253,8 @@ def main():
                     help="the headline prefill step alone (for profiler runs): no other workloads, no CPU baseline")
     ap.add_argument("--cpu-pairs", type=int, default=64,
                     help="(sequence, head) pairs the oracle runs (64 = the whole workload)")
-    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--cpu-repeats", type=int, default=20,
+                    help="repeats of the oracle sample (about 10 s on 16 cores of the GPU box)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also launch one plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
@@ -301,8 +323,7 @@ def main():
     # (the records stay inside it: written and read back through the L2)
     by = prefill_bytes(token_heads, B * H, dk, dv, 2, 2)
     src = source_hash([os.path.join(ROOT, "fp8_state_qat_amd", "csrc", f)
-                       for f in ("gdn_chunk.hip", "gdn_chunk_common.hpp", "gdn_device.hpp",
-                                 "gdn_prep_item.hpp")])
+                       for f in PREFILL_SOURCES])
     traffic = load_traffic("chunk_fwd_gdn_prefill", src)
     tflops = fl_all / (kern_ms * 1e-3) / 1e12
     hbm_gbs = by / (kern_ms * 1e-3) / 1e9
@@ -327,8 +348,11 @@ def main():
             "flops_per_token_head": flops_per_token_head(64, dk, dv)}
 
     if args.only_prefill:
-        print(json.dumps({"metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
-                          "ms_per_step": round(ms_step, 5), "roofline": roofline}), flush=True)
+        line = {"metric": METRIC, "value": round(tokens / (ms_step * 1e-3), 1), "unit": "tokens/s",
+                "ms_per_step": round(ms_step, 5), "roofline": roofline}
+        if args.copy_calibration_mib:
+            line["copy_calibration_bytes"] = copy_calibration(dev, args.copy_calibration_mib)
+        print(json.dumps(line), flush=True)
         return
 
     # QDQ off, same workload (reported)
@@ -433,6 +457,20 @@ def main():
                      "mfma_frac": round(bfl / (bwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                      "hbm_gbs": round(bby / (bwd_ms * 1e-3) / 1e9, 1),
                      "algorithmic_flops_per_step": bfl, "algorithmic_bytes_per_step": bby}
+
+    # the backward of the W-QDQ forward (the forward's quantized W in the state term)
+    def step_bwd_w():
+        api.chunk_bwd_dh(d["q"], d["k"], d["beta"], d["g"], d["cu_seqlens"], d_o, d_final_state=dS_L,
+                         dh=dh_out, d_initial_state=d0_out, d_v=dv_out, qdq_flags=flags | GDN_QDQ_W)
+
+    bwdw_ms, _ = time_launches(step_bwd_w, args.steps, args.warmup)
+    check_outputs(api, None, dh_out, d0_out, dv_out)
+    bwdw_ms /= args.steps
+    out["bwd_dh"]["w_qdq"] = {"qdq_flags": flags | GDN_QDQ_W, "ms_per_step": round(bwdw_ms, 5),
+                              "kernels": "chunk_offsets_kernel + chunk_prep_kernel<128, bf16, true> (the "
+                                         "forward's W records) + chunk_bwd_prep_kernel<128> + "
+                                         "chunk_bwd_dh_kernel<128, true>",
+                              "mfma_frac": round(bfl / (bwdw_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
     del d_o, dS_L, dh_out, d0_out, dv_out
 
     # ---------------- packed varlen prefill at full size (reported) ----------------
@@ -532,6 +570,32 @@ def main():
                       "w_qdq": {"qdq_flags": flags | GDN_QDQ_W,
                                 "ms_per_step": round(kwtot / args.steps, 5),
                                 "tokens_per_s": round(tokens / (kwtot / args.steps * 1e-3), 1)}}
+
+        # its backward: the reverse token recurrence (fp32 vector ALU)
+        genk = torch.Generator(device=dev)
+        genk.manual_seed(7)
+        d_ok = torch.randn((wk.total_tokens, H, dv), generator=genk, device=dev).to(torch.bfloat16)
+        dS_k = torch.randn((B, H, dv, dk), generator=genk, device=dev)
+        dh_k = torch.empty((B * ((T + 63) // 64), H, dv, dk), device=dev)
+        d0_k = torch.empty((B, H, dv, dk), device=dev)
+        dv_k = torch.empty((wk.total_tokens, H, dv), device=dev)
+
+        def kstep_bwd():
+            api.chunk_bwd_dh(dk_["q"], dk_["k"], dk_["beta"], dk_["g"], dk_["cu_seqlens"], d_ok,
+                             d_final_state=dS_k, dh=dh_k, d_initial_state=d0_k, d_v=dv_k)
+
+        kb_ms, _ = time_launches(kstep_bwd, args.steps, args.warmup)
+        check_outputs(api, None, dh_k, d0_k, dv_k)
+        kb_ms /= args.steps
+        # per token and head: G += do q^T, y = G k, G -= beta y k^T (2 dv dk flops each), G *= exp(g) (dv dk)
+        kb_fl = 7 * dv * dk * token_heads
+        out["kda"]["bwd_dh"] = {"ms_per_step": round(kb_ms, 5), "tokens_per_s": round(tokens / (kb_ms * 1e-3), 1),
+                                "kernels": "chunk_offsets_kernel + kda_bwd_token_kernel<128>",
+                                "roofline": {"bound": "alu", "achieved": round(kb_fl / (kb_ms * 1e-3) / 1e12, 2),
+                                             "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                             "frac": round(kb_fl / (kb_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
+                                             "algorithmic_flops_per_step": kb_fl}}
+        del d_ok, dS_k, dh_k, d0_k, dv_k
         del dk_
         torch.cuda.empty_cache()
 
@@ -620,13 +684,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = n * 4
+        out["copy_calibration_bytes"] = copy_calibration(dev, args.copy_calibration_mib)
 
     if not args.no_cpu_baseline:
         # all the cores this process may use (the GPU's share of the host, at most 16), and one

@@ -477,18 +477,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
 //     y   = G k_t,   d_v[t] = beta_t y      (v_t enters through beta_t v_t k_t^T)
 //     G  <- (G - beta_t y k_t^T) diag(exp(g_t))   (now the gradient of S_{t-1})
 // and dh of chunk c is G once token 64c + 1 is taken back.  One workgroup
-// (256 threads) per (sequence, head, 64-row value tile) with G in registers,
+// (256 threads) per (sequence, head, 32 rows of a value tile) with G in registers,
 // in the decode step's layout (thread t: float4 column group t % (dk/4) of
 // rows t / (dk/4) + p * 256 / (dk/4)); row dot products by the decode step's
 // fixed DPP tree.  The tokens of a chunk are staged in LDS as fp32 (q, k,
 // exp(g), the tile's d_o columns, beta) and its value gradients leave from
 // LDS as whole rows.  Vector ALU bound (about 4 * 64 * dk FMAs per token and
 // tile); no split-bf16 products, so fp32 throughout.
+// The rows of G are independent (the backward has no QDQ to couple them),
+// so a workgroup takes kKdaBwdRows rows of a value tile: twice the
+// workgroups of one per tile, so that a full-size call fills the GPU.
+constexpr int kKdaBwdRows = 32;
+
 template <int DK>
 struct KdaBwdLds {
+  static constexpr int R = kKdaBwdRows;
   static constexpr size_t oQ = 0, oK = oQ + 64 * DK, oE = oK + 64 * DK, oO = oE + 64 * DK;
-  static constexpr size_t oB = oO + 64 * 64, oDV = oB + 64;
-  static constexpr size_t floats = oDV + 64 * 64;
+  static constexpr size_t oB = oO + 64 * R, oDV = oB + 64;
+  static constexpr size_t floats = oDV + 64 * R;
   static constexpr size_t bytes = floats * sizeof(float);
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
 };
@@ -514,9 +520,11 @@ struct KdaBwdArgs {
 template <int DK>
 __global__ __launch_bounds__(kThreads) void kda_bwd_token_kernel(KdaBwdArgs a) {
   using Ls = KdaBwdLds<DK>;
+  constexpr int R = kKdaBwdRows;
   constexpr int F = DK / 4;          // float4 per state row
   constexpr int RPP = kThreads / F;  // rows per pass
-  constexpr int NP = kTileRows / RPP;
+  constexpr int NP = R / RPP;        // passes over the workgroup's rows
+  static_assert(NP >= 1 && R % RPP == 0, "row geometry");
   extern __shared__ __align__(16) float kb_smem[];
   if (index_check_failed(a.status)) return;
   float* sq = kb_smem + Ls::oQ;
@@ -526,83 +534,126 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_token_kernel(KdaBwdArgs a) {
   float* sb = kb_smem + Ls::oB;
   float* sdv = kb_smem + Ls::oDV;
   const int t = threadIdx.x, c4 = t % F, rr = t / F;
-  const int H = a.H, dv = a.dv, tiles = dv / kTileRows;
-  const int vt = (int)blockIdx.x % tiles, nh = (int)blockIdx.x / tiles;
+  const int H = a.H, dv = a.dv, parts = dv / R;
+  const int rb = (int)blockIdx.x % parts, nh = (int)blockIdx.x / parts;
   const int h = nh % H, n = nh / H;
   const int seg0 = a.cu_seqlens[n];
   const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);
   const int n_chunks = (L + kChunk - 1) / kChunk;
   const int chunk0 = a.chunk_offs[n];
   const int64_t qk_row = (int64_t)H * DK, v_row = (int64_t)H * dv;
-  const int64_t tile = ((int64_t)nh * dv + kTileRows * vt) * DK;  // row 0 of the tile in [N, H, dv, dk]
+  const int row0 = R * rb;                                     // first value row of the workgroup
+  const int64_t blk = ((int64_t)nh * dv + row0) * DK;          // row row0 of (n, h) in [N, H, dv, dk]
 
   float4 G[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
-    G[p] = a.dfin ? reinterpret_cast<const float4*>(a.dfin + tile)[t + kThreads * p] : make_float4(0.f, 0.f, 0.f, 0.f);
+    G[p] = a.dfin ? reinterpret_cast<const float4*>(a.dfin + blk)[t + kThreads * p] : make_float4(0.f, 0.f, 0.f, 0.f);
 
   for (int c = n_chunks - 1; c >= 0; --c) {
     const int t0 = c * kChunk;
     const int nv = min(kChunk, L - t0);
+    // every load of the chunk issued before any is used: rows past its end
+    // read its last valid row (in bounds) and are replaced by 0 (by 1 for
+    // exp(g)) when stored
+    constexpr int NI = kChunk * DK / kThreads, NO = kChunk * R / kThreads;
+    uint16_t rq[NI], rk[NI], ro[NO];
+    float rg[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int i = t + kThreads * j, tok = i / DK, col = i % DK;
+      const int64_t off = (seg0 + t0 + min(tok, nv - 1)) * qk_row + (int64_t)h * DK + col;
+      rq[j] = a.q[off];
+      rk[j] = a.k[off];
+      rg[j] = a.g[off];
+    }
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int i = t + kThreads * j, tok = i / R, r = i % R;
+      ro[j] = a.dout[(seg0 + t0 + min(tok, nv - 1)) * v_row + (int64_t)h * dv + row0 + r];
+    }
+    const float rbeta = t < kChunk ? a.beta[(int64_t)(seg0 + t0 + min(t, nv - 1)) * H + h] : 0.f;
     __syncthreads();  // the last chunk's staged tokens and value gradients are consumed
-    for (int i = t; i < kChunk * DK; i += kThreads) {
-      const int tok = i / DK, col = i % DK;
-      const bool ok = tok < nv;
-      const int64_t row = seg0 + t0 + tok;
-      sq[i] = ok ? bf16_bits_to_float(a.q[row * qk_row + (int64_t)h * DK + col]) : 0.f;
-      sk[i] = ok ? bf16_bits_to_float(a.k[row * qk_row + (int64_t)h * DK + col]) : 0.f;
-      se[i] = ok ? expf(a.g[row * qk_row + (int64_t)h * DK + col]) : 1.f;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int i = t + kThreads * j;
+      const bool ok = i / DK < nv;
+      sq[i] = ok ? bf16_bits_to_float(rq[j]) : 0.f;
+      sk[i] = ok ? bf16_bits_to_float(rk[j]) : 0.f;
+      se[i] = ok ? expf(rg[j]) : 1.f;
     }
-    for (int i = t; i < kChunk * kTileRows; i += kThreads) {
-      const int tok = i / kTileRows, r = i % kTileRows;
-      so[i] = tok < nv ? bf16_bits_to_float(a.dout[(seg0 + t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + r])
-                       : 0.f;
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int i = t + kThreads * j;
+      so[i] = i / R < nv ? bf16_bits_to_float(ro[j]) : 0.f;
     }
-    if (t < kChunk) sb[t] = t < nv ? a.beta[(int64_t)(seg0 + t0 + t) * H + h] : 0.f;
+    if (t < kChunk) sb[t] = t < nv ? rbeta : 0.f;
     __syncthreads();
+    // the operands of token tok, read one token ahead of their use
+    float4 qv, kv, ev;
+    float b, dor[NP];
+    auto read_token = [&](int tok) {
+      qv = reinterpret_cast<const float4*>(sq + tok * DK)[c4];
+      kv = reinterpret_cast<const float4*>(sk + tok * DK)[c4];
+      ev = reinterpret_cast<const float4*>(se + tok * DK)[c4];
+      b = sb[tok];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) dor[p] = so[tok * R + rr + RPP * p];
+    };
+    read_token(nv - 1);
     for (int tok = nv - 1; tok >= 0; --tok) {
-      const float4 qv = reinterpret_cast<const float4*>(sq + tok * DK)[c4];
-      const float4 kv = reinterpret_cast<const float4*>(sk + tok * DK)[c4];
-      const float4 ev = reinterpret_cast<const float4*>(se + tok * DK)[c4];
-      const float b = sb[tok];
+      const float4 q4 = qv, k4 = kv, e4 = ev;
+      const float bt = b;
+      float d4[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) d4[p] = dor[p];
+      if (tok > 0) read_token(tok - 1);
+      // the rows are independent: each step for all of them before the next,
+      // so that their dependent chains (the reductions above all) overlap
+      float dot[NP], by[NP];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int r = rr + RPP * p;
-        const float dor = so[tok * kTileRows + r];
-        G[p].x = fmaf(dor, qv.x, G[p].x);
-        G[p].y = fmaf(dor, qv.y, G[p].y);
-        G[p].z = fmaf(dor, qv.z, G[p].z);
-        G[p].w = fmaf(dor, qv.w, G[p].w);
-        const float y = group_sum<F>(G[p].x * kv.x + G[p].y * kv.y + G[p].z * kv.z + G[p].w * kv.w);
-        const float by = b * y;
-        if (c4 == 0) sdv[tok * kTileRows + r] = by;
-        G[p].x = (G[p].x - by * kv.x) * ev.x;
-        G[p].y = (G[p].y - by * kv.y) * ev.y;
-        G[p].z = (G[p].z - by * kv.z) * ev.z;
-        G[p].w = (G[p].w - by * kv.w) * ev.w;
+        G[p].x = fmaf(d4[p], q4.x, G[p].x);
+        G[p].y = fmaf(d4[p], q4.y, G[p].y);
+        G[p].z = fmaf(d4[p], q4.z, G[p].z);
+        G[p].w = fmaf(d4[p], q4.w, G[p].w);
+        dot[p] = G[p].x * k4.x + G[p].y * k4.y + G[p].z * k4.z + G[p].w * k4.w;
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) by[p] = bt * group_sum<F>(dot[p]);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        G[p].x = (G[p].x - by[p] * k4.x) * e4.x;
+        G[p].y = (G[p].y - by[p] * k4.y) * e4.y;
+        G[p].z = (G[p].z - by[p] * k4.z) * e4.z;
+        G[p].w = (G[p].w - by[p] * k4.w) * e4.w;
+      }
+      if (c4 == 0) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) sdv[tok * R + rr + RPP * p] = by[p];
       }
     }
     if (a.dh) {  // the gradient of the state entering chunk c
-      float4* dst = reinterpret_cast<float4*>(a.dh + (((int64_t)(chunk0 + c) * H + h) * dv + kTileRows * vt) * DK);
+      float4* dst = reinterpret_cast<float4*>(a.dh + (((int64_t)(chunk0 + c) * H + h) * dv + row0) * DK);
 #pragma unroll
       for (int p = 0; p < NP; ++p) dst[t + kThreads * p] = G[p];
     }
     __syncthreads();  // the chunk's value gradients are in LDS
     if (a.dvals) {
-      for (int i = t; i < nv * kTileRows; i += kThreads) {
-        const int tok = i / kTileRows, r = i % kTileRows;
-        a.dvals[(seg0 + t0 + tok) * v_row + (int64_t)h * dv + kTileRows * vt + r] = sdv[i];
+      for (int i = t; i < nv * R; i += kThreads) {
+        const int tok = i / R, r = i % R;
+        a.dvals[(seg0 + t0 + tok) * v_row + (int64_t)h * dv + row0 + r] = sdv[i];
       }
     }
   }
   if (a.dinit) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) reinterpret_cast<float4*>(a.dinit + tile)[t + kThreads * p] = G[p];
+    for (int p = 0; p < NP; ++p) reinterpret_cast<float4*>(a.dinit + blk)[t + kThreads * p] = G[p];
   }
   if (a.dvals) {  // padding rows of the segment
     const int seg_len = a.cu_seqlens[n + 1] - seg0;
-    for (int i = L * kTileRows + t; i < seg_len * kTileRows; i += kThreads)
-      a.dvals[(seg0 + i / kTileRows) * v_row + (int64_t)h * dv + kTileRows * vt + i % kTileRows] = 0.f;
+    for (int i = L * R + t; i < seg_len * R; i += kThreads)
+      a.dvals[(seg0 + i / R) * v_row + (int64_t)h * dv + row0 + i % R] = 0.f;
   }
 }
 
@@ -689,7 +740,7 @@ hipError_t launch_chunk_bwd_dh(const gdn_shape_t& s, const void* q, const void* 
     ka.status = status;
     ka.H = s.n_heads;
     ka.dv = s.dv;
-    const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
+    const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kKdaBwdRows);
     auto go = [&](auto kern, size_t lds) {
       hipError_t e2 = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e2 != hipSuccess) return e2;

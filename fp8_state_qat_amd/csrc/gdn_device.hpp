@@ -178,8 +178,11 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
 
 // Sum over each group of F consecutive lanes (F = 16 or 32, groups aligned),
 // every lane of a group receiving it: quad swaps and rotations by 4 and 8
-// inside each row of 16 lanes (DPP), then for F = 32 a swizzle that swaps
-// the two rows of each 32-lane half.  The order of the additions is fixed.
+// inside each row of 16 lanes (DPP), then for F = 32 the two rows of each
+// 32-lane half added, one row's sum brought to the other by
+// v_permlane16_swap (in the vector ALU; the two operands of the last
+// addition are the same in every lane, so each lane's sum is the same
+// value).  The order of the additions is fixed.
 template <int F>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(F == 16 || F == 32, "group of 16 or 32 lanes");
@@ -187,8 +190,10 @@ __device__ __forceinline__ float group_sum(float v) {
   v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
   v = dpp_add<0x124, 0xF>(v);  // row_ror:4
   v = dpp_add<0x128, 0xF>(v);  // row_ror:8
-  if constexpr (F == 32)       // bit-mode swizzle: and 0x1f, or 0, xor 0x10
-    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  if constexpr (F == 32) {     // rows 2i and 2i + 1 of each half: swap and add
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   return v;
 }
 
