@@ -8,7 +8,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+# GDN_LIB: another build of the same sources (the host-sanitized one)
+LIB_PATH = os.environ.get("GDN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 
 GDN_OK = 0
 GDN_ERR_INVALID_ARG = 1

@@ -22,7 +22,8 @@ CHUNK = 64
 TILE_ROWS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libgdn_oracle.so")
+# GDN_ORACLE_LIB: another build of the same source (the sanitized one)
+_LIB_PATH = os.environ.get("GDN_ORACLE_LIB") or os.path.join(_HERE, "libgdn_oracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
