@@ -198,7 +198,10 @@ def time_launches(fn, steps, warmup):
         evs[i + 1].record()
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return evs[0].elapsed_time(evs[-1]), per
+    total = evs[0].elapsed_time(evs[-1])
+    print(f"timed {steps} calls of {getattr(fn, '__name__', 'step')}: {total / max(steps, 1):.4f} ms each",
+          file=sys.stderr, flush=True)
+    return total, per
 
 
 def cpu_baseline(w, flags, n_pairs, threads, repeats):
@@ -690,6 +693,7 @@ def main():
         # all the cores this process may use (the GPU's share of the host, at most 16), and one
         hi = host_info()
         threads = max(1, min(16, hi["usable"]))
+        print(f"oracle on {threads} host threads", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, flags, args.cpu_pairs, threads, args.cpu_repeats)
         one = cpu_baseline(w, flags, max(1, args.cpu_pairs // 16), 1, 1)
         cb["one_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
