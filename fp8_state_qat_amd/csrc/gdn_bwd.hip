@@ -535,7 +535,21 @@ __global__ __launch_bounds__(kThreads) void kda_bwd_token_kernel(KdaBwdArgs a) {
   float* sdv = kb_smem + Ls::oDV;
   const int t = threadIdx.x, c4 = t % F, rr = t / F;
   const int H = a.H, dv = a.dv, parts = dv / R;
-  const int rb = (int)blockIdx.x % parts, nh = (int)blockIdx.x / parts;
+  // the row blocks of a (sequence, head) on one XCD (workgroup b runs on XCD
+  // b % 8) when the grid comes in groups of 8 pairs, so that the chunk's q, k
+  // and g reach the other blocks from that XCD's L2
+  int rb, nh;
+  {
+    const int b = (int)blockIdx.x;
+    if (parts > 1 && (int)gridDim.x % (8 * parts) == 0) {
+      const int slot8 = b >> 3;
+      rb = slot8 % parts;
+      nh = (slot8 / parts) * 8 + (b & 7);
+    } else {
+      rb = b % parts;
+      nh = b / parts;
+    }
+  }
   const int h = nh % H, n = nh / H;
   const int seg0 = a.cu_seqlens[n];
   const int L = a.seq_lens ? a.seq_lens[n] : (a.cu_seqlens[n + 1] - seg0);

@@ -63,6 +63,9 @@ constexpr int kThreadsWg = 64 * kWaves;
 //         [128..191] exp(gamma_C - gamma), [192] exp(gamma_C)
 //   red   [0..7] the chain waves' amax by chunk parity, [12] the decay
 //         multiplier (1, or NaN once a wait for a record has run out)
+//   O     2 x [64][64] bf16 by chunk parity: the chunk's outputs of the tile
+//         (bf16 o), 16-byte piece u of row r at piece u ^ (r % 8), stored
+//         to HBM by the loader waves as whole 128-byte rows
 template <int DK>
 struct LdsB {
   static constexpr int NKB = DK / 32;
@@ -78,7 +81,9 @@ struct LdsB {
   static constexpr size_t oVec = oP + 2 * (size_t)kPRecBytes;
   static constexpr size_t VEC = 200;
   static constexpr size_t oRed = oVec + 2 * VEC * sizeof(float);
-  static constexpr size_t bytes = oRed + 16 * sizeof(float);
+  static constexpr size_t OBUF = 64 * 64 * 2;
+  static constexpr size_t oO = oRed + 16 * sizeof(float);
+  static constexpr size_t bytes = oO + 2 * OBUF;
   static_assert(18 * F == (size_t)kTRecBytes && 12 * F == (size_t)kPRecBytes, "record geometry");
   static_assert(bytes <= 160 * 1024, "LDS budget exceeded");
   static_assert(oK + (2 * DK + 64 + 8) * sizeof(float) <= oQ, "suffix buffers do not fit");
@@ -130,6 +135,8 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
   float* const sVec = reinterpret_cast<float*>(smem + Ls::oVec);
   float* const sRed = reinterpret_cast<float*>(smem + Ls::oRed);
   float* const psn = sRed + 12;
+  char* const sO = smem + Ls::oO;
+  constexpr bool kStageO = sizeof(TO) == 2;  // bf16 o goes out through LDS
 
   const uint32_t lds0 = lds_base_u32(smem);
   auto lds_of = [&](const void* p) { return lds0 + (uint32_t)(reinterpret_cast<const char*>(p) - smem); };
@@ -259,6 +266,24 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
       }
     }
   };
+  // bf16 o of chunk cc, staged in LDS by the chain waves before the barrier
+  // that ended it: each loader wave stores 16 of its 64 rows, a row as 8
+  // lanes x 16 bytes (rows past the chunk's end are not stored)
+  auto store_o = [&](int cc) {
+    if constexpr (kStageO) {
+      const int nv = min(kChunk, P - cc * kChunk);
+      const char* ob = sO + (cc & 1) * Ls::OBUF;
+      const int u = lane & 7;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int r = 8 * (hw + 4 * ii) + (lane >> 3);
+        const uint4 x = *reinterpret_cast<const uint4*>(ob + r * 128 + ((u ^ (r & 7)) << 4));
+        if (r < nv)
+          *reinterpret_cast<uint4*>(go_ + (int64_t)(seg0 + cc * kChunk + r) * v_row + (int64_t)h * dv +
+                                    kTileRows * vt + 8 * u) = x;
+      }
+    }
+  };
   // every load of chunk cc into the buffers of parity cc & 1, and its gates
   auto load_chunk = [&](int cc) {
     const int par = cc & 1;
@@ -297,13 +322,13 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
   // the four chain waves' amax of boundary c (published before the barrier after chunk c)
   auto tile_scale = [&](const int c) {
     const float* rd = sRed + (c & 1) * 4;
-    return qdq_scale(fmaxf(fmaxf(rd[0], rd[1]), fmaxf(rd[2], rd[3])));
+    return qdq_scale_f64(fmaxf(fmaxf(rd[0], rd[1]), fmaxf(rd[2], rd[3])));
   };
-  // E4M3 codes of k-block kb of the state (scale s, r = RN(1 / s)) into st and sh
-  auto code_block = [&](const int kb, const float s, const float r) {
+  // E4M3 codes of k-block kb of the state (r: 1 / scale in fp64) into st and sh
+  auto code_block = [&](const int kb, const double r) {
     float c0[4], c1[4];
-    e4m3_codes4(st[2 * kb], s, r, c0);
-    e4m3_codes4(st[2 * kb + 1], s, r, c1);
+    e4m3_codes4_f64(st[2 * kb], r, c0);
+    e4m3_codes4_f64(st[2 * kb + 1], r, c1);
     st[2 * kb] = f32x4{c0[0], c0[1], c0[2], c0[3]};
     st[2 * kb + 1] = f32x4{c1[0], c1[1], c1[2], c1[3]};
     const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
@@ -318,6 +343,7 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
   // the other half run, and each half of U' while the update of the other
   // half runs.  Returns nothing; leaves the output in oacc and pacc.
   f32x4 oacc[4], pacc[4];  // S Q^T and U'^T P^T of the chunk, o = s exp(gamma) oacc + pacc
+  float amax_w = 0.f;      // the wave's amax of the state after the chunk
   float sc = 1.0f;         // scale of the state entering the chunk
   auto chain_chunk = [&](auto coded_tag, const int c) {
     constexpr bool kCoded = decltype(coded_tag)::value;
@@ -388,11 +414,11 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
     // coded chunk opens with the QDQ of the boundary before it, one k-block
     // at a time: the codes of block kb + 1 are formed beside the products of
     // block kb.  Each step below is its own scheduling region.
-    float rs = 1.0f;
+    double rs = 1.0;
     sc = 1.0f;
     if constexpr (kCoded) {
       sc = tile_scale(c - 1);
-      rs = 1.0f / sc;
+      rs = rcp_f64(sc);
     }
     f32x4 acc[4];
 #pragma unroll
@@ -411,7 +437,7 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
     Fr lo[NKB];  // uncoded state: its lo plane
     auto form_state = [&](const int kb) {
       if constexpr (kCoded) {
-        code_block(kb, sc, rs);
+        code_block(kb, rs);
       } else {
         const float x[8] = {st[2 * kb][0], st[2 * kb][1], st[2 * kb][2], st[2 * kb][3],
                             st[2 * kb + 1][0], st[2 * kb + 1][1], st[2 * kb + 1][2], st[2 * kb + 1][3]};
@@ -514,6 +540,9 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
       Eng::mma(st[t], ka1[t], bm[1]);
       Eng::mma(st[t], ka1[t], bh[1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // the products U'^T P^T beside the amax of the updated state (a tree of
+    // depth 5, then a DPP wave max), which only waits for the update
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) pacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -523,6 +552,19 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
       Eng::mma(pacc[ti], ul[kb], phs[p]);
       Eng::mma(pacc[ti], uh[kb], pls[p]);
     }
+    float m16[2 * NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      m16[2 * t] = fmaxf(fabsf(st[t][0]), fabsf(st[t][1]));
+      m16[2 * t + 1] = fmaxf(fabsf(st[t][2]), fabsf(st[t][3]));
+    }
+#pragma unroll
+    for (int w2 = NT; w2 >= 1; w2 /= 2)
+#pragma unroll
+      for (int k = 0; k < w2; ++k) m16[k] = fmaxf(m16[k], m16[k + w2]);
+    amax_w = wave_max_dpp(m16[0]);
+    sched_interleave<18, 3>();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // o row of this lane's first output (token ln of the sequence), hoisted out
@@ -535,19 +577,7 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
     const int par = c & 1;
     const float* geg = sVec + par * Ls::VEC + 64;
     const int nv = min(kChunk, P - c * kChunk);
-    // amax of the wave's state values as a tree of depth 5
-    float m16[16];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      m16[2 * t] = fmaxf(fabsf(st[t][0]), fabsf(st[t][1]));
-      m16[2 * t + 1] = fmaxf(fabsf(st[t][2]), fabsf(st[t][3]));
-    }
-#pragma unroll
-    for (int w2 = 2 * NT / 2; w2 >= 1; w2 /= 2)
-#pragma unroll
-      for (int k = 0; k < w2; ++k) m16[k] = fmaxf(m16[k], m16[k + w2]);
-    const float amax = wave_max_dpp(m16[0]);
-    if (lane == 0) sRed[par * 4 + c4] = amax;
+    if (lane == 0) sRed[par * 4 + c4] = amax_w;
     // lane holds o[tok = 16ti + ln][16c4 + 4gq .. +3] of this tile
     float egt[4];
 #pragma unroll
@@ -557,18 +587,22 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
       for (int i = 0; i < 4; ++i) o16[ti][i] = fmaf(egt[ti], oacc[ti][i], pacc[ti][i]);
-    TO* const oc = o_lane + (int64_t)(c * kChunk) * v_row;
+    if constexpr (kStageO) {
+      // row 16ti + ln, columns 16c4 + 4gq .. +3: half gq % 2 of piece 2c4 + gq / 2
+      char* const ob = sO + par * Ls::OBUF;
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      if (16 * ti + ln < nv) {
-        TO* dst = oc + (int64_t)(16 * ti) * v_row;
-        if constexpr (sizeof(TO) == 2) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o16[ti][0], o16[ti][1]),
-                                                      pack_bf16x2(o16[ti][2], o16[ti][3]));
-        } else {
-          *reinterpret_cast<float4*>(dst) = make_float4(o16[ti][0], o16[ti][1], o16[ti][2], o16[ti][3]);
-        }
+      for (int ti = 0; ti < 4; ++ti) {
+        const int r = 16 * ti + ln;
+        *reinterpret_cast<uint2*>(ob + r * 128 + (((2 * c4 + (gq >> 1)) ^ (r & 7)) << 4) + 8 * (gq & 1)) =
+            make_uint2(pack_bf16x2(o16[ti][0], o16[ti][1]), pack_bf16x2(o16[ti][2], o16[ti][3]));
       }
+    } else {
+      TO* const oc = o_lane + (int64_t)(c * kChunk) * v_row;
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+        if (16 * ti + ln < nv)
+          *reinterpret_cast<float4*>(oc + (int64_t)(16 * ti) * v_row) =
+              make_float4(o16[ti][0], o16[ti][1], o16[ti][2], o16[ti][3]);
     }
     if (args.bound_pre) {
       const int bidx = bound0 + c;
@@ -584,9 +618,9 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
   // The boundary QDQ after the last chunk (the QDQ of the others opens the next chunk).
   auto chain_qdq_last = [&](const int c) {
     const float s_new = tile_scale(c);
-    const float r = 1.0f / s_new;
+    const double r = rcp_f64(s_new);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) code_block(kb, s_new, r);
+    for (int kb = 0; kb < NKB; ++kb) code_block(kb, r);
     s_cur = s_new;
     st_coded = true;
     record_post(c, s_new, s_new);
@@ -623,11 +657,13 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
       else
         chain_chunk(std::false_type{}, c);
       chain_finish(c);
-    } else if (c + 1 < n_chunks) {
-      load_chunk(c + 1);  // into the other half of every buffer
+    } else {
+      if (c > 0) store_o(c - 1);
+      if (c + 1 < n_chunks) load_chunk(c + 1);  // into the other half of every buffer
     }
     barrier_lds();
   }
+  if (!chain && n_chunks > 0) store_o(n_chunks - 1);
   if (chain && n_chunks > 0 && (flags & (GDN_QDQ_CHUNK | GDN_QDQ_WRITE))) chain_qdq_last(n_chunks - 1);
 
   if (st_coded) {  // back to the state values: code * s
