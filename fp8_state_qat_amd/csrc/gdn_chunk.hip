@@ -1013,6 +1013,8 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   a.bound_scales = debug ? debug->scales : nullptr;
   a.H = s.n_heads; a.dv = s.dv; a.flags = s.qdq_flags;
   a.N = s.n_seqs; a.ready = L.ready; a.n_prep = n_prep; a.fused = fused ? 1 : 0;
+  // the bf16 state kernel forms the first chunk's records itself when fused
+  a.prep_c0 = (fused && !s.gate_per_channel && s.io_dtype == GDN_BF16 && L.W == nullptr) ? 1 : 0;
   a.status = L.status;
   a.grid_log2 = s.gate_grid_log2;
   a.sfx_offsets = debug ? debug->suffix_offsets : nullptr;

@@ -255,6 +255,7 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
   const unsigned xcd_self = kFused ? xcd_id() : 0u;
   auto await_records = [&](int cc) {
     if constexpr (kFused) {
+      if (cc < args.prep_c0) return;  // formed by this workgroup
       const unsigned* flag = args.ready + ((int64_t)(chunk0 + cc) * H + h);
       if (!poisoned &&
           !await_ready_flag(flag, __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), xcd_self)) {
@@ -641,6 +642,22 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
     }
   }
   barrier_lds();  // the poison word is set before any wait can overwrite it
+  if constexpr (kFused) {
+    // The first chunk's records: formed here by the loader waves (the chain
+    // waves only take part in the item's barriers) instead of waiting for a
+    // producer's first round; the LDS block at 0 is free until chunk 0 is
+    // loaded.  Both value tiles of a pair write the same bytes to its slot.
+    if (args.prep_c0 > 0 && n_chunks > 0) {
+      PrepArgs pa;
+      pa.q = args.q; pa.k = args.k; pa.beta = args.beta; pa.g = args.g; pa.cu_seqlens = args.cu_seqlens;
+      pa.seq_lens = args.seq_lens; pa.prefix_lens = args.prefix_lens; pa.offs = args.chunk_offs;
+      pa.T = const_cast<void*>(args.T); pa.P = const_cast<void*>(args.Prec); pa.N = args.N; pa.H = H;
+      pa.W = nullptr; pa.w_pre = nullptr; pa.w_post = nullptr; pa.status = args.status;
+      prep_item<DK, TIO, false>(pa, chunk0, h, seg0, min(kChunk, P), smem, chain ? tid : tid - 256, !chain);
+      wait_vmem();      // this wave's record stores are complete
+      __syncthreads();  // ... in every wave
+    }
+  }
   if (!chain && n_chunks > 0) load_chunk(0);
   barrier_lds();
 

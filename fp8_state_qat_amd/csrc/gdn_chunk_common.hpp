@@ -296,6 +296,8 @@ struct ChunkArgs {
   int fused;           // the fused instantiation runs (its waits on the ready flags included)
   unsigned* ready;     // fused launch: one ready flag per (chunk, head), cleared before the launch
   int n_prep;          // fused launch: workgroups 0 .. n_prep - 1 produce the T and P records
+  int prep_c0;         // fused launch: the producers start at this chunk of every sequence (the
+                       // state workgroups form the chunks before it themselves)
   int32_t* status;     // the workspace's status word (index check, failed waits)
   int grid_log2;       // log-retention grid of the recurrent suffix (0: off)
   const int32_t* sfx_offsets;  // optional per-token record of the recurrent suffix:

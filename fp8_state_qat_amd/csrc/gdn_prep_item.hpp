@@ -862,13 +862,14 @@ __device__ __forceinline__ void produce_records(const ChunkArgs& args, char* sme
   const unsigned xcd = xcd_id();
   const bool home = xcd == (unsigned)x;
   const int M = NH > x ? (NH - x + 7) >> 3 : 0;
-  const int64_t total = (int64_t)args.chunk_offs[args.N + 1] * M;
+  const int c0 = args.prep_c0;
+  const int64_t total = (int64_t)max(args.chunk_offs[args.N + 1] - c0, 0) * M;
   for (int64_t m0 = r; m0 < total; m0 += 2 * R) {
     const int64_t m = m0 + (int64_t)half * R;
     bool active = m < total;
     int j = 0, h = 0, t0 = 0, nv = 0;
     if (active) {
-      const int c = (int)(m / M), nh = x + 8 * (int)(m % M);
+      const int c = c0 + (int)(m / M), nh = x + 8 * (int)(m % M);
       const int n = nh / H;
       h = nh % H;
       const int seg0 = args.cu_seqlens[n];
