@@ -475,12 +475,12 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
       record_post(c - 1, sc, sc);
     }
 
-    // ---- stage B: the decay of the state (exp(gamma_C), times the scale of
-    // a coded state) and the first half of X; then U' = T X over the
+    // ---- stage B: the first half of X; then U' = T X over the
     // lower-triangular T pairs (ti, kb) (0,0) (1,0) (2,0) (3,0) (2,1) (3,1),
     // the six partial products down to 2^-16 of the leading one: the second
-    // half of X beside the pairs of the first, the split of U' rows 0..31
-    // beside the last two pairs
+    // half of X and the decay of the state (exp(gamma_C), times the scale of
+    // a coded state) beside the pairs of the first, the split of U' rows
+    // 0..31 beside the last two pairs
     Fr tf[6], tm[6], tl[6];
 #pragma unroll
     for (int p = 0; p < 6; ++p) {
@@ -490,11 +490,6 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
     }
     float aC = vec[192] * sc;
     if constexpr (kFused) aC *= *psn;  // NaN after a failed wait for a record
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[t][i] *= aC;
-    st_coded = false;
     Fr xh[2], xm[2], xl[2];
     form_x(0, acc, xh[0], xm[0], xl[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -504,9 +499,15 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
 #pragma unroll
     for (int p = 0; p < 4; ++p) tx_pair(p, uacc, tf, tm, tl, xh, xm, xl);
     form_x(1, acc, xh[1], xm[1], xl[1]);
+    // the decay of the state, beside the products (the update adds to it later)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[t][i] *= aC;
+    st_coded = false;
     Fr ka0[NT];
     read_kt(0, ka0);
-    sched_interleave<24, 2>();
+    sched_interleave<24, 3>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 4; p < 6; ++p) tx_pair(p, uacc, tf, tm, tl, xh, xm, xl);
