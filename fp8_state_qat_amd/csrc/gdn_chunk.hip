@@ -1017,6 +1017,11 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
   a.prep_c0 = (fused && !s.gate_per_channel && s.io_dtype == GDN_BF16 && L.W == nullptr) ? 1 : 0;
   a.status = L.status;
   a.grid_log2 = s.gate_grid_log2;
+  {
+    // state workgroups in more than one round: longest sequences first
+    const int64_t n_state = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
+    a.longest_first = (!fused && s.n_seqs > 1 && s.n_seqs <= 1024 && n_state > device_cu_count()) ? 1 : 0;
+  }
   a.sfx_offsets = debug ? debug->suffix_offsets : nullptr;
   a.sfx_pre = debug ? debug->suffix_pre : nullptr;
   a.sfx_post = debug ? debug->suffix_post : nullptr;

@@ -165,7 +165,12 @@ __global__ __launch_bounds__(kThreadsWg, 1) void chunk_bf16_kernel(ChunkArgs arg
   {
     const int b = (int)blockIdx.x - (kFused ? args.n_prep : 0);
     const int G = (int)gridDim.x - (kFused ? args.n_prep : 0);
-    if (tiles > 1 && G % (8 * tiles) == 0) {
+    if (!kFused && args.longest_first) {
+      const int per_seq = H * tiles;
+      const int n0 = rank_sequence(args.cu_seqlens, args.seq_lens, args.N, b / per_seq, reinterpret_cast<int*>(smem));
+      nh = n0 * H + (b % per_seq) / tiles;
+      vt = b % tiles;
+    } else if (tiles > 1 && G % (8 * tiles) == 0) {
       const int slot8 = b >> 3;
       vt = slot8 % tiles;
       nh = (slot8 / tiles) * 8 + (b & 7);

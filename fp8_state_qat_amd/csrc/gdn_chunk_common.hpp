@@ -300,6 +300,8 @@ struct ChunkArgs {
                        // state workgroups form the chunks before it themselves)
   int32_t* status;     // the workspace's status word (index check, failed waits)
   int grid_log2;       // log-retention grid of the recurrent suffix (0: off)
+  int longest_first;   // the state workgroups outnumber the compute units: workgroups take the
+                       // sequences longest first (see rank_sequence)
   const int32_t* sfx_offsets;  // optional per-token record of the recurrent suffix:
   float* sfx_pre;              // state after each suffix token before its QDQ
   float* sfx_post;             // and after it ([sfx_offsets[n] + t - P_n, H, dv, dk])
@@ -344,6 +346,30 @@ __device__ __forceinline__ bool await_ready_flag(const unsigned* flag, unsigned 
     wait_vmem();
   }
   return true;
+}
+
+// Longest first: when the state workgroups come in several rounds, the
+// sequence that workgroup-rank r works on is the one of rank r by length
+// (longest first, ties by index), so that the long chains start in the first
+// round.  Every thread of the workgroup takes part; `slot` is one LDS word.
+// O(N^2 / blockDim) comparisons, so the host asks for it only for modest N.
+__device__ __forceinline__ int rank_sequence(const int32_t* cu, const int32_t* seq_lens, int N, int r, int* slot) {
+  auto len = [&](int m) { return seq_lens ? seq_lens[m] : (cu[m + 1] - cu[m]); };
+  if (threadIdx.x == 0) *slot = 0;
+  __syncthreads();
+  for (int m = threadIdx.x; m < N; m += blockDim.x) {
+    const int lm = len(m);
+    int rank = 0;
+    for (int j = 0; j < N; ++j) {
+      const int lj = len(j);
+      rank += (lj > lm || (lj == lm && j < m)) ? 1 : 0;
+    }
+    if (rank == r) *slot = m;
+  }
+  __syncthreads();
+  const int n = *slot;
+  __syncthreads();  // the word is free again
+  return n;
 }
 
 // True when the index check of this call failed (the status word that
