@@ -93,10 +93,10 @@ struct LdsB {
 
 // Instruction-order hints for the chain waves' scheduling regions: a group
 // of kCount instructions of one kind (kMfma: matrix products, kValu: other
-// vector ALU, kDsRead: LDS reads), placed in the order the hints are given.
+// vector ALU), placed in the order the hints are given.
 // The chain is one serial dependence per chunk, so each vector ALU stage is
 // placed beside matrix products it does not depend on.
-constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+constexpr int kMfma = 0x008, kValu = 0x002;
 template <int kMask, int kCount>
 __device__ __forceinline__ void sched_group() {
   __builtin_amdgcn_sched_group_barrier(kMask, kCount, 0);
