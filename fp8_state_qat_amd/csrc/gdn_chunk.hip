@@ -422,22 +422,22 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_fwd_kernel(ChunkArgs a
     float s_new = 1.0f;
     if (do_qdq) {
       const float amax = fmaxf(fmaxf(rd[0], rd[1]), fmaxf(rd[2], rd[3]));
-      s_new = qdq_scale(amax);
-      const float r = 1.0f / s_new;
+      s_new = qdq_scale_f64(amax);
+      const double r = rcp_f64(s_new);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float c0[4], c1[4];
         if constexpr (kSplit) {
           // keep the codes; the scale is folded into the next decay multiply
-          e4m3_codes4(st[2 * kb], s_new, r, c0);
-          e4m3_codes4(st[2 * kb + 1], s_new, r, c1);
+          e4m3_codes4_f64(st[2 * kb], r, c0);
+          e4m3_codes4_f64(st[2 * kb + 1], r, c1);
           st[2 * kb] = f32x4{c0[0], c0[1], c0[2], c0[3]};
           st[2 * kb + 1] = f32x4{c1[0], c1[1], c1[2], c1[3]};
           const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
           sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
         } else {
-          qdq4c(st[2 * kb], c0, s_new, r);
-          qdq4c(st[2 * kb + 1], c1, s_new, r);
+          qdq4c_f64(st[2 * kb], c0, s_new, r);
+          qdq4c_f64(st[2 * kb + 1], c1, s_new, r);
         }
       }
       s_cur = s_new;

@@ -80,6 +80,13 @@ __device__ __forceinline__ void e4m3_codes4_f64(const f32x4& x, double r, float 
   c[2] = b[0];
   c[3] = b[1];
 }
+// QDQ of four values through the fp64 quotients (r: 1 / s in fp64): x <- the
+// E4M3 value of x / s times s, with the sign of x; cv receives the codes.
+__device__ __forceinline__ void qdq4c_f64(f32x4& v, float (&cv)[4], float s, double r) {
+  e4m3_codes4_f64(v, r, cv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = copysignf(cv[i] * s, v[i]);
+}
 // The tile scale RN(amax / 448) (1 when amax is 0) through fp64: amax / 448 =
 // amax / 7 / 64 is at least 2^-27 (relative) from any rounding boundary of
 // fp32, and the product with the fp64 value of 1/448 is within 2^-52 of it.

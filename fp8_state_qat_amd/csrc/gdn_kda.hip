@@ -601,13 +601,13 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     float s_new = 1.0f;
     if (do_qdq) {
       const float amax = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
-      s_new = qdq_scale(amax);
-      const float r = 1.0f / s_new;
+      s_new = qdq_scale_f64(amax);
+      const double r = rcp_f64(s_new);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         float c0[4], c1[4];
-        qdq4c(st[2 * kb], c0, s_new, r);
-        qdq4c(st[2 * kb + 1], c1, s_new, r);
+        qdq4c_f64(st[2 * kb], c0, s_new, r);
+        qdq4c_f64(st[2 * kb + 1], c1, s_new, r);
         if constexpr (kSplit) {
           const float x[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
           sh[kb] = Eng::round(x);  // E4M3 values are exact in bf16
