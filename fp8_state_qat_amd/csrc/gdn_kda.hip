@@ -233,23 +233,34 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   const bool builder = cg < NCG;
   uint4 rk[4][UPS], rq[4][UPS];
   float4 rg[4][2];
-  auto fetch = [&](int cc) {  // raw k, q, g of chunk cc into registers
+  // raw k, q, g of chunk cc into registers (builder lanes), per token slot t
+  auto row_of = [&](int cc, int t) {
+    const int nv = min(kChunk, P - cc * kChunk);
+    return seg0 + cc * kChunk + (int64_t)min(4 * ln + t, nv - 1);
+  };
+  auto fetch_kq = [&](int cc, int t) {
+    const int64_t row = row_of(cc, t);
+    const uint4* kp = reinterpret_cast<const uint4*>(gk_ + row * qk_row + (int64_t)h * DK + 8 * cg);
+    const uint4* qp = reinterpret_cast<const uint4*>(gq_ + row * qk_row + (int64_t)h * DK + 8 * cg);
+#pragma unroll
+    for (int u = 0; u < UPS; ++u) {
+      rk[t][u] = kp[u];
+      rq[t][u] = qp[u];
+    }
+  };
+  auto fetch_g = [&](int cc) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float4* gp = reinterpret_cast<const float4*>(args.g + (row_of(cc, t) * H + h) * DK + 8 * cg);
+      rg[t][0] = gp[0];
+      rg[t][1] = gp[1];
+    }
+  };
+  auto fetch = [&](int cc) {
     if (builder) {
-      const int nv = min(kChunk, P - cc * kChunk);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t row = seg0 + cc * kChunk + min(4 * ln + t, nv - 1);
-        const uint4* kp = reinterpret_cast<const uint4*>(gk_ + row * qk_row + (int64_t)h * DK + 8 * cg);
-        const uint4* qp = reinterpret_cast<const uint4*>(gq_ + row * qk_row + (int64_t)h * DK + 8 * cg);
-#pragma unroll
-        for (int u = 0; u < UPS; ++u) {
-          rk[t][u] = kp[u];
-          rq[t][u] = qp[u];
-        }
-        const float4* gp = reinterpret_cast<const float4*>(args.g + (row * H + h) * DK + 8 * cg);
-        rg[t][0] = gp[0];
-        rg[t][1] = gp[1];
-      }
+      for (int t = 0; t < 4; ++t) fetch_kq(cc, t);
+      fetch_g(cc);
     }
   };
   auto unpack8 = [](const uint4 (&u)[UPS], float (&x)[8]) {
@@ -266,7 +277,11 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
       for (int j = 0; j < 8; ++j) x[j] = __uint_as_float(wd[j]);
     }
   };
-  auto build = [&](int cc) {
+  // The operands of chunk cc from the raw values in registers; the raw
+  // values of chunk nxt (if >= 0) are loaded into the same registers as soon
+  // as each is consumed, so that those loads leave the load unit one at a time
+  // between the build's arithmetic instead of stalling the wave in a burst.
+  auto build = [&](int cc, int nxt) {
     if (builder) {
       const int nv = min(kChunk, P - cc * kChunk);
       float cum[4][8];  // prefix of the gate over this lane's tokens, natural log
@@ -278,6 +293,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
 #pragma unroll
         for (int m = 0; m < 8; ++m) cum[t][m] = (t ? cum[t - 1][m] : 0.f) + (valid ? gv[m] : 0.f);
       }
+      if (nxt >= 0) fetch_g(nxt);
       float ex[8], gC[8];  // sum over the earlier lanes of the row; the chunk total
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -291,6 +307,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
         float kf[8], qf[8];
         unpack8(rk[t], kf);
         unpack8(rq[t], qf);
+        if (nxt >= 0) fetch_kq(nxt, t);
         float ka[8], qa[8], kc[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -666,10 +683,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
 #pragma unroll
     for (int t = 0; t < NT; ++t) st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (n_chunks > 0) {
-    build(0);
-    if (n_chunks > 1) fetch(1);
-  }
+  if (n_chunks > 0) build(0, n_chunks > 1 ? 1 : -1);
   // Chunk c: B reads the operands built for c and the v/T/P loads of c; the
   // operands of c + 1 are built once every wave is past the second barrier.
   for (int c = 0; c < n_chunks; ++c) {
@@ -684,8 +698,7 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     }
     barrier_lds();
     if (c + 1 < n_chunks) {
-      build(c + 1);
-      if (c + 2 < n_chunks) fetch(c + 2);
+      build(c + 1, c + 2 < n_chunks ? c + 2 : -1);
       issue_vtp(c + 1);
     }
     qdq_step(c);
