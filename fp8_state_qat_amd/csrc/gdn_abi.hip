@@ -224,8 +224,8 @@ gdn_status_t check_chunk_args(const gdn_shape_t* shape, const void* q, const voi
     return fail(GDN_ERR_INVALID_ARG, "misaligned debug record (states need 16 bytes)");
   if (debug && (debug->schedule < GDN_SCHEDULE_AUTO || debug->schedule > GDN_SCHEDULE_FUSED_NO_PRODUCERS))
     return fail(GDN_ERR_INVALID_ARG, "debug schedule must be GDN_SCHEDULE_AUTO, _SPLIT, _FUSED or _FUSED_NO_PRODUCERS");
-  if (shape->io_dtype == GDN_F32 && shape->dk != 64)
-    return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs are supported with dk = 64 only");
+  if (shape->io_dtype == GDN_F32 && shape->dk == 128 && (shape->qdq_flags & GDN_QDQ_W))
+    return fail(GDN_ERR_UNSUPPORTED, "fp32 inputs with dk = 128 take no W QDQ (the token recurrence has no W)");
   return GDN_OK;
 }
 

@@ -994,11 +994,13 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
                             void* workspace, const gdn_debug_t* debug, hipStream_t stream) {
   ChunkArgs a;
   const PrepLayout L = prep_layout(s, workspace);
-  const int n_prep = producer_workgroups(s, debug);
+  // fp32 inputs with dk = 128: the token recurrence (no per-chunk records)
+  const bool token_path = s.io_dtype == GDN_F32 && s.dk == 128;
+  const int n_prep = token_path ? 0 : producer_workgroups(s, debug);
   // test hook: the fused instantiation without its producers (every wait for a ready flag runs out)
-  const bool no_producers = debug && debug->schedule == GDN_SCHEDULE_FUSED_NO_PRODUCERS;
+  const bool no_producers = !token_path && debug && debug->schedule == GDN_SCHEDULE_FUSED_NO_PRODUCERS;
   const bool fused = n_prep > 0 || no_producers;
-  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, L, !fused,
+  hipError_t e = launch_prep(s, q, k, beta, g, cu_seqlens, seq_lens, prefix_lens, L, !fused && !token_path,
                              debug ? debug->w_pre : nullptr, debug ? debug->w_post : nullptr, stream);
   if (e != hipSuccess) return e;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = g;
@@ -1030,7 +1032,9 @@ hipError_t launch_chunk_fwd(const gdn_shape_t& s, const void* q, const void* k, 
     e = hipEventRecord((hipEvent_t)debug->kernel_start, stream);
     if (e != hipSuccess) return e;
   }
-  if (s.gate_per_channel) {
+  if (token_path) {
+    e = launch_chunk_token(s, a, stream);
+  } else if (s.gate_per_channel) {
     e = launch_kda_state(s, a, stream);
   } else if (s.io_dtype == GDN_BF16 && a.Wrec == nullptr) {
     e = launch_chunk_bf16(s, a, stream);

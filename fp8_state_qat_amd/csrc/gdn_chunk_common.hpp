@@ -397,5 +397,8 @@ __device__ __forceinline__ void report_wait_timeout(int32_t* status) {
 hipError_t launch_kda_state(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream);
 // the scalar-gate state part for bf16 q, k, v without W QDQ (gdn_chunk_bf16.hip)
 hipError_t launch_chunk_bf16(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream);
+// fp32 q, k, v with dk = 128, either gate, no W QDQ: the token recurrence
+// with the chunked form's QDQ points (gdn_token.hip)
+hipError_t launch_chunk_token(const gdn_shape_t& s, const ChunkArgs& a, hipStream_t stream);
 
 }  // namespace gdn

@@ -180,6 +180,11 @@ typedef struct {
  *     ran out (200 ms, e.g. when the GPU is shared): that (sequence, head)'s
  *     state and outputs from then on are NaN.
  *
+ * fp32 q, k, v with dk = 128 run as the token recurrence with the same QDQ
+ * points and records (the chunked form regrouped, identical up to rounding;
+ * slower, for reference precision); they take no GDN_QDQ_W
+ * (GDN_ERR_UNSUPPORTED).
+ *
  * QDQ placement for token t of a sequence (1-based): after token t when
  * (GDN_QDQ_CHUNK and t <= P and (t % 64 == 0 or t == P)) or
  * (GDN_QDQ_WRITE and t >= max(P, 1)); chunks start at each sequence's first

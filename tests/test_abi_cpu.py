@@ -66,7 +66,8 @@ def _chunk(shape, q=FAKE, beta=FAKE, cu=FAKE, fin=FAKE, dbg=None, ws=FAKE, ws_by
     (dict(n_seqs=0), 1), (dict(n_heads=0), 1), (dict(dv=96), 1), (dict(dk=96), 2),
     (dict(dk=32), 2), (dict(dv=512), 2), (dict(total_tokens=-1), 1), (dict(io_dtype=7), 1),
     (dict(o_dtype=-1), 1), (dict(gate_per_channel=2), 1), (dict(qdq_flags=16), 1), (dict(qdq_flags=8 | 3), 2),
-    (dict(io_dtype=0, dk=128), 2), (dict(io_dtype=0, dk=128, gate_per_channel=1), 2),
+    (dict(io_dtype=0, dk=128, qdq_flags=3 | _lib.GDN_QDQ_W), 2),
+    (dict(io_dtype=0, dk=128, gate_per_channel=1, qdq_flags=3 | _lib.GDN_QDQ_W), 2),
     (dict(gate_grid_log2=-1), 1), (dict(gate_grid_log2=25), 1),
 ])
 def test_chunk_fwd_rejects_bad_shape(kw, status):
@@ -189,6 +190,16 @@ def test_workspace_status_checks():
 def test_valid_call_without_gpu_reports_device_error():
     assert _chunk(_shape()) == 3
     assert "device" in _lib.last_error().lower()
+
+
+def test_fp32_dk128_takes_no_w_qdq():
+    """fp32 inputs with dk = 128 (the token-recurrence path) refuse W QDQ on
+    the host (UNSUPPORTED); without it the call passes the host checks."""
+    assert _chunk(_shape(io_dtype=0, o_dtype=0, qdq_flags=3 | _lib.GDN_QDQ_W)) == 2
+    assert "W QDQ" in _lib.last_error()
+    if not HAS_GPU:
+        assert _chunk(_shape(io_dtype=0, o_dtype=0, qdq_flags=3)) == 3   # no device here
+        assert _chunk(_shape(io_dtype=0, o_dtype=0, gate_per_channel=1, qdq_flags=3)) == 3
 
 
 def _bwd(shape, q=FAKE, do=FAKE, dh=FAKE, d0=FAKE, ws=FAKE, ws_bytes=None):

@@ -35,10 +35,30 @@ def test_tiny_fp32_qdq_on():
     assert o_rel <= 1e-5 and s_rel <= 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("lens", [[256], [200, 1, 64, 65, 130]])
-def test_fp32_qdq_off(lens):
-    w = gi.make_packed(lens, 2, 64, 64, io_dtype=gi.F32, seed=len(lens))
+def test_fp32_qdq_off(lens, d):
+    """fp32 inputs; at d = 128 the token-recurrence kernel (gdn_token.hip)."""
+    w = gi.make_packed(lens, 2, d, d, io_dtype=gi.F32, seed=len(lens) + d)
     _check_g1(w, run_chunk_gpu(w, 0), run_chunk_oracle(w, 0), TOL[gi.F32])
+
+
+@pytest.mark.parametrize("dv", [128, 256])
+@pytest.mark.parametrize("o_dtype", ["f32", "bf16"])
+def test_fp32_d128_qdq_on_teacher_forced(dv, o_dtype):
+    """fp32 inputs with dk = 128 (token recurrence, the chunked form's QDQ
+    points): teacher-forced per boundary against the oracle (G2), ragged
+    lengths with a one-token and a one-chunk sequence, padding rows.  The
+    free-running result is reported: the token steps round differently from
+    the chunked products, so an E4M3 decision near a midpoint can flip and
+    the trajectories part (G2 bounds those flips)."""
+    w = gi.make_packed([300, 1, 64, 129], 2, 128, dv, io_dtype=gi.F32, seed=dv + len(o_dtype),
+                       pads=[3, 0, 5, 0])
+    gpu = run_chunk_gpu(w, 3, o_dtype=o_dtype, record=True)
+    _check_g2(w, gpu, 3, TOL[gi.F32] if o_dtype == "f32" else TOL[gi.BF16])
+    ref = run_chunk_oracle(w, 3)
+    print(f"free-running QDQ on (reported): o_rel={rel_l2(gpu['o'], ref['o']):.3e} "
+          f"S_rel={rel_l2(gpu['S'], ref['S']):.3e}", flush=True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -71,12 +91,13 @@ def test_varlen_padding_is_isolated():
     assert np.all(gpu["S"][1] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("flags", [1, 2, 3])
-def test_prefix_suffix_fp32(flags):
+def test_prefix_suffix_fp32(flags, d):
     """Chunked prefix P then recurrent suffix up to L (fp32), with the
     three QDQ placements: prefix teacher-forced per boundary, suffix
     teacher-forced per token."""
-    w = gi.make_packed([150, 70, 9], 2, 64, 64, io_dtype=gi.F32, seed=7 + flags,
+    w = gi.make_packed([150, 70, 9], 2, d, d, io_dtype=gi.F32, seed=7 + flags + d,
                        prefix_lens=[128, 33, 0])
     gpu = run_chunk_gpu(w, flags, record=True, suffix_record=True)
     check_prefix_suffix(w, gpu, flags, TOL[gi.F32])
@@ -98,7 +119,7 @@ def test_prefix_suffix_bf16(flags, d, dv):
     check_prefix_suffix(w, gpu, flags, TOL[gi.BF16])
 
 
-@pytest.mark.parametrize("io,d,dv", [(gi.BF16, 128, 128), (gi.F32, 64, 64)])
+@pytest.mark.parametrize("io,d,dv", [(gi.BF16, 128, 128), (gi.F32, 64, 64), (gi.F32, 128, 128)])
 @pytest.mark.parametrize("grid", [3, 8])
 def test_prefix_suffix_log_grid(io, d, dv, grid):
     """Log-retention grid (#2509): the recurrent suffix decays with each
@@ -132,10 +153,11 @@ def test_full_size_prefix_suffix_sampled(flags):
     check_prefix_suffix(w, gpu, flags, TOL[gi.BF16], pairs=[(0, 3), (1, 9), (2, 0), (3, 15)])
 
 
-def test_initial_state_fp32():
-    w = gi.make_packed([130, 64], 2, 64, 64, io_dtype=gi.F32, seed=13)
+@pytest.mark.parametrize("d", [64, 128])
+def test_initial_state_fp32(d):
+    w = gi.make_packed([130, 64], 2, d, d, io_dtype=gi.F32, seed=13 + d)
     rng = np.random.default_rng(13)
-    S0 = (rng.standard_normal((2, 2, 64, 64)) * 0.5).astype(np.float32)
+    S0 = (rng.standard_normal((2, 2, d, d)) * 0.5).astype(np.float32)
     gpu = run_chunk_gpu(w, 3, record=True, initial_state=S0)
     _check_g2(w, gpu, 3, TOL[gi.F32], initial_state=S0)
     gpu0 = run_chunk_gpu(w, 0, initial_state=S0)

@@ -24,16 +24,19 @@ def _kda(lens, H, dk, dv, io, seed, g_scale=0.05, **kw):
                           seed=seed, **kw)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("lens", [[256], [200, 1, 64, 65, 130]])
-def test_kda_fp32_qdq_off(lens):
-    w = _kda(lens, 2, 64, 64, gi.F32, seed=31 + len(lens))
+def test_kda_fp32_qdq_off(lens, d):
+    """fp32 inputs; at d = 128 the token-recurrence kernel (gdn_token.hip)."""
+    w = _kda(lens, 2, d, d, gi.F32, seed=31 + len(lens) + d)
     check_g1(w, run_chunk_gpu(w, 0), run_chunk_oracle(w, 0), TOL[gi.F32])
 
 
-def test_kda_fp32_qdq_on():
+@pytest.mark.parametrize("d", [64, 128])
+def test_kda_fp32_qdq_on(d):
     """Teacher-forced per boundary, and free-running (fp32 compute keeps
     the code decisions of the oracle here)."""
-    w = _kda([256, 100], 2, 64, 64, gi.F32, seed=37)
+    w = _kda([256, 100], 2, d, d, gi.F32, seed=37 + d)
     gpu = run_chunk_gpu(w, 3, record=True)
     check_g2(w, gpu, 3, TOL[gi.F32])
     ref = run_chunk_oracle(w, 3)
@@ -92,11 +95,12 @@ def test_kda_varlen_padding_is_isolated():
     assert np.all(gpu["S"][1] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("flags", [1, 2, 3])
-def test_kda_prefix_suffix_fp32(flags):
+def test_kda_prefix_suffix_fp32(flags, d):
     """Chunked prefix P, then the recurrent suffix up to L with the
     per-channel decay, under the three QDQ placements."""
-    w = _kda([150, 70, 9], 2, 64, 64, gi.F32, seed=59 + flags, prefix_lens=[128, 33, 0])
+    w = _kda([150, 70, 9], 2, d, d, gi.F32, seed=59 + flags + d, prefix_lens=[128, 33, 0])
     gpu = run_chunk_gpu(w, flags, record=True, suffix_record=True)
     check_prefix_suffix(w, gpu, flags, TOL[gi.F32])
 
