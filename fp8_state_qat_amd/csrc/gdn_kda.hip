@@ -507,6 +507,40 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
                            uacc[2 * kb + 1][3]};
       Eng::split(u8, uh[kb], ul[kb]);
     }
+    // S^T <- diag(exp(gamma_C)) S^T + (K o exp(gamma_C - gamma))^T U'
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float4 e = *reinterpret_cast<const float4*>(sEC + 16 * t + 4 * gq);
+      st[t][0] *= e.x;
+      st[t][1] *= e.y;
+      st[t][2] *= e.z;
+      st[t][3] *= e.w;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (Eng::kTrRead) {
+        // lane (gq, l) of each 16-lane group points at Kc[32kb + 16h + 4gq + l/4][dkmap(16t + 4(l%4)) .. +3]
+        const int d = dkmap(16 * t + 4 * (ln & 3));
+        const int tq = 4 * gq + (ln >> 2);
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+          const E* kc = sKc + pl * PLANE;
+          const uint2 x0 = lds_read_tr16(kc + kpos(tq, d)), x1 = lds_read_tr16(kc + kpos(tq + 16, d));
+          const uint2 y0 = lds_read_tr16(kc + kpos(tq + 32, d)), y1 = lds_read_tr16(kc + kpos(tq + 48, d));
+          const Fr a0 = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
+          const Fr a1 = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
+          Eng::mma(st[t], a0, uh[0]);
+          Eng::mma(st[t], a1, uh[1]);
+          if (pl == 0) {
+            Eng::mma(st[t], a0, ul[0]);
+            Eng::mma(st[t], a1, ul[1]);
+          }
+        }
+      } else {
+        Eng::mma(st[t], Eng::ld(slot(sKc, 2 * t)), uh[0]);
+        Eng::mma(st[t], Eng::ld(slot(sKc, 2 * t + 1)), uh[1]);
+      }
+    }
     // O^T[v][t] = s (S (Q o exp(gamma))^T)[v][t] + (U'^T P^T)[v][t]
     f32x4 oacc[4];
 #pragma unroll
@@ -548,40 +582,6 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
         } else {
           *reinterpret_cast<float4*>(dst) = make_float4(oacc[ti][0], oacc[ti][1], oacc[ti][2], oacc[ti][3]);
         }
-      }
-    }
-    // S^T <- diag(exp(gamma_C)) S^T + (K o exp(gamma_C - gamma))^T U'
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float4 e = *reinterpret_cast<const float4*>(sEC + 16 * t + 4 * gq);
-      st[t][0] *= e.x;
-      st[t][1] *= e.y;
-      st[t][2] *= e.z;
-      st[t][3] *= e.w;
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if constexpr (Eng::kTrRead) {
-        // lane (gq, l) of each 16-lane group points at Kc[32kb + 16h + 4gq + l/4][dkmap(16t + 4(l%4)) .. +3]
-        const int d = dkmap(16 * t + 4 * (ln & 3));
-        const int tq = 4 * gq + (ln >> 2);
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl) {
-          const E* kc = sKc + pl * PLANE;
-          const uint2 x0 = lds_read_tr16(kc + kpos(tq, d)), x1 = lds_read_tr16(kc + kpos(tq + 16, d));
-          const uint2 y0 = lds_read_tr16(kc + kpos(tq + 32, d)), y1 = lds_read_tr16(kc + kpos(tq + 48, d));
-          const Fr a0 = __builtin_bit_cast(Fr, make_uint4(x0.x, x0.y, x1.x, x1.y));
-          const Fr a1 = __builtin_bit_cast(Fr, make_uint4(y0.x, y0.y, y1.x, y1.y));
-          Eng::mma(st[t], a0, uh[0]);
-          Eng::mma(st[t], a1, uh[1]);
-          if (pl == 0) {
-            Eng::mma(st[t], a0, ul[0]);
-            Eng::mma(st[t], a1, ul[1]);
-          }
-        }
-      } else {
-        Eng::mma(st[t], Eng::ld(slot(sKc, 2 * t)), uh[0]);
-        Eng::mma(st[t], Eng::ld(slot(sKc, 2 * t + 1)), uh[1]);
       }
     }
     if (args.bound_pre) {
