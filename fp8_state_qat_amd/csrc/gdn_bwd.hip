@@ -687,24 +687,16 @@ static hipError_t launch_bwd_dk(const gdn_shape_t& s, const PrepArgs& pa, const 
   {
     auto kern = chunk_bwd_prep_kernel<DK>;
     constexpr size_t lds = PrepBwdLds<DK>::bytes;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static PerDeviceOnce lds_attr;
+    if (hipError_t e = set_dyn_lds_once(lds_attr, (const void*)kern, lds); e != hipSuccess) return e;
     if (items > 0) hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(kThreads), lds, stream, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   auto kern = chunk_bwd_dh_kernel<DK, kW>;
   constexpr size_t lds = BwdLds<DK>::bytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static PerDeviceOnce lds_attr;
+  if (hipError_t e = set_dyn_lds_once(lds_attr, (const void*)kern, lds); e != hipSuccess) return e;
   const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBwdThreads), lds, stream, ba);
   return hipGetLastError();

@@ -795,12 +795,8 @@ static hipError_t launch_bf16_typed(const gdn_shape_t& s, const ChunkArgs& a, hi
   constexpr size_t state_lds = LdsB<DK>::bytes;
   constexpr size_t lds = (kFused && item_lds > state_lds) ? item_lds : state_lds;
   static_assert(lds <= 160 * 1024, "LDS budget exceeded");
-  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static PerDeviceOnce lds_attr;
+  if (hipError_t e = set_dyn_lds_once(lds_attr, (const void*)kern, lds); e != hipSuccess) return e;
   const int64_t blocks = (int64_t)s.n_seqs * s.n_heads * (s.dv / kTileRows) + (kFused ? a.n_prep : 0);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kThreadsWg), lds, stream, a);
   return hipGetLastError();

@@ -5,9 +5,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gdn.h"
 
 namespace gdn {
+
+// A kernel's dynamic-LDS limit (hipFuncAttributeMaxDynamicSharedMemorySize)
+// belongs to each device's copy of the function: set it once per device, so a
+// process that drives several GPUs sets it on every one it launches on.
+struct PerDeviceOnce {
+  std::atomic<uint64_t> done{0};  // bit d: set on device d (devices 0..63)
+};
+inline hipError_t set_dyn_lds_once(PerDeviceOnce& once, const void* kern, size_t lds) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+  if (bit && (once.done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess && bit) once.done.fetch_or(bit, std::memory_order_release);
+  return e;  // concurrent first calls on one device both set it: harmless
+}
 
 hipError_t launch_state_qdq(const float* in, float* out, float* scales, int64_t n_tiles, int dk,
                             hipStream_t stream);

@@ -199,12 +199,8 @@ template <int DK, typename TIO, bool kW>
 static hipError_t launch_chunk_prep(dim3 grid, const PrepArgs& a, hipStream_t stream) {
   auto kern = chunk_prep_kernel<DK, TIO, kW>;
   constexpr size_t lds = PrepItemLds<DK, TIO, kW>::bytes;
-  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static PerDeviceOnce lds_attr;
+  if (hipError_t e = set_dyn_lds_once(lds_attr, (const void*)kern, lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
@@ -213,12 +209,8 @@ template <int DK, typename TIO, bool kW>
 static hipError_t launch_kda_prep(dim3 grid, const PrepArgs& a, hipStream_t stream) {
   auto kern = kda_prep_kernel<DK, TIO, kW>;
   constexpr size_t lds = KdaPrepLds<DK, TIO, kW>::bytes;
-  static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static PerDeviceOnce lds_attr;
+  if (hipError_t e = set_dyn_lds_once(lds_attr, (const void*)kern, lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
