@@ -32,6 +32,8 @@
 // workgroups of this same launch (produce_kda_records).  Then the
 // recurrent suffix (tokens P_n < t <= L_n, QDQ after every write) and the
 // final state store.
+#include <type_traits>
+
 #include "gdn_prep_item.hpp"
 
 namespace gdn {
@@ -402,16 +404,20 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
   };
 
   // ---- B: one chunk's products for this wave's 16 value rows
-  auto phase_b = [&](int c) {
+  // two_tag: the state enters as hi + lo (the split engine and no QDQ at the
+  // boundary before the chunk), else as one plane (its E4M3 codes, or fp32);
+  // a compile-time choice, so that no branch splits the products and the
+  // operand reads can run ahead of them
+  auto phase_b = [&](auto two_tag, int c) {
     const int t0 = seg0 + c * kChunk;
     const int nv = min(kChunk, P - c * kChunk);
-    const bool coded_in = kSplit && c > 0 && (flags & GDN_QDQ_CHUNK);
-    const bool two = kSplit && !coded_in;  // state operand as hi + lo
+    constexpr bool two = decltype(two_tag)::value;
+    constexpr bool coded_in = kSplit && !two;
     const bool last = (c == n_chunks - 1);
     const bool do_qdq = (flags & GDN_QDQ_CHUNK) || ((flags & GDN_QDQ_WRITE) && last);
     const float sc = coded_in ? s_cur : 1.0f;
     Fr s_hi[NKB], s_lo[NKB];
-    if (coded_in) {
+    if constexpr (coded_in) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) s_hi[kb] = sh[kb];
     } else {
@@ -422,25 +428,37 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     f32x4 acc[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kW) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if constexpr (kW) {
+        for (int tt = 0; tt < 4; ++tt) {
           const Fr a = ld_bf16_frag<Eng>(sW + ((tt * NKB + kb) * 64 + lane) * 8);
           Eng::mma(acc[tt], a, s_hi[kb]);
           if constexpr (kSplit) {
-            if (two) Eng::mma(acc[tt], a, s_lo[kb]);
+            if constexpr (two) Eng::mma(acc[tt], a, s_lo[kb]);
           }
-        } else {
-          const Fr a = Eng::ld(slot(sKa, tt * NKB + kb));
-          Eng::mma(acc[tt], a, s_hi[kb]);
+        }
+    } else {
+      // the fragments of a k-block are read together, then its products run
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        Fr a[4], al[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          a[tt] = Eng::ld(slot(sKa, tt * NKB + kb));
+          if constexpr (kSplit) al[tt] = Eng::ld(slot(sKa + PLANE, tt * NKB + kb));
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          Eng::mma(acc[tt], a[tt], s_hi[kb]);
           if constexpr (kSplit) {
-            Eng::mma(acc[tt], Eng::ld(slot(sKa + PLANE, tt * NKB + kb)), s_hi[kb]);
-            if (two) Eng::mma(acc[tt], a, s_lo[kb]);
+            Eng::mma(acc[tt], al[tt], s_hi[kb]);
+            if constexpr (two) Eng::mma(acc[tt], a[tt], s_lo[kb]);
           }
         }
       }
+    }
     f32x4 uacc[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) uacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -487,14 +505,24 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
       Eng::split(x8, xh[kb], xl[kb]);
     }
     // U' = T X over the lower-triangular pairs (ti, kb): (0,0) (1,0) (2,0) (3,0) (2,1) (3,1)
+    // (T's fragments three pairs at a time, read before their products)
 #pragma unroll
-    for (int p = 0; p < 6; ++p) {
-      const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-      const Fr tf = Eng::ld(slot(sT, p));
-      Eng::mma(uacc[ti], tf, xh[kb]);
-      if constexpr (kSplit) {
-        Eng::mma(uacc[ti], tf, xl[kb]);
-        Eng::mma(uacc[ti], Eng::ld(slot(sT, 6 + p)), xh[kb]);
+    for (int p0 = 0; p0 < 6; p0 += 3) {
+      Fr tf[3], tl[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        tf[j] = Eng::ld(slot(sT, p0 + j));
+        if constexpr (kSplit) tl[j] = Eng::ld(slot(sT, 6 + p0 + j));
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int p = p0 + j;
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        Eng::mma(uacc[ti], tf[j], xh[kb]);
+        if constexpr (kSplit) {
+          Eng::mma(uacc[ti], tf[j], xl[kb]);
+          Eng::mma(uacc[ti], tl[j], xh[kb]);
+        }
       }
     }
     }  // kW
@@ -546,28 +574,43 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) oacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      Fr bq[4], bql[4];
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const Fr bq = Eng::ld(slot(sQa, ti * NKB + kb));
-        Eng::mma(oacc[ti], s_hi[kb], bq);
+        bq[ti] = Eng::ld(slot(sQa, ti * NKB + kb));
+        if constexpr (kSplit) bql[ti] = Eng::ld(slot(sQa + PLANE, ti * NKB + kb));
+      }
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        Eng::mma(oacc[ti], s_hi[kb], bq[ti]);
         if constexpr (kSplit) {
-          Eng::mma(oacc[ti], s_hi[kb], Eng::ld(slot(sQa + PLANE, ti * NKB + kb)));
-          if (two) Eng::mma(oacc[ti], s_lo[kb], bq);
+          Eng::mma(oacc[ti], s_hi[kb], bql[ti]);
+          if constexpr (two) Eng::mma(oacc[ti], s_lo[kb], bq[ti]);
         }
       }
+    }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[ti][i] *= sc;
 #pragma unroll
-    for (int p = 0; p < 6; ++p) {
-      const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
-      const Fr ph = Eng::ld(slot(sP, p));
-      Eng::mma(oacc[ti], uh[kb], ph);
-      if constexpr (kSplit) {
-        Eng::mma(oacc[ti], ul[kb], ph);
-        Eng::mma(oacc[ti], uh[kb], Eng::ld(slot(sP, 6 + p)));
+    for (int p0 = 0; p0 < 6; p0 += 3) {
+      Fr ph[3], pl[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        ph[j] = Eng::ld(slot(sP, p0 + j));
+        if constexpr (kSplit) pl[j] = Eng::ld(slot(sP, 6 + p0 + j));
+      }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int p = p0 + j;
+        const int ti = p < 4 ? p : p - 2, kb = p < 4 ? 0 : 1;
+        Eng::mma(oacc[ti], uh[kb], ph[j]);
+        if constexpr (kSplit) {
+          Eng::mma(oacc[ti], ul[kb], ph[j]);
+          Eng::mma(oacc[ti], uh[kb], pl[j]);
+        }
       }
     }
     // lane holds o[tok = 16ti + ln][16c4 + 4gq .. +3] of this tile
@@ -692,7 +735,10 @@ __global__ __launch_bounds__(kKdaThreads, 1) void kda_fwd_kernel(ChunkArgs args)
     if constexpr (kFused) {
       if (w == 0 && c + 1 < n_chunks) pend = load_ready(c + 1);  // examined after phase B
     }
-    phase_b(c);
+    if (kSplit && !(c > 0 && (flags & GDN_QDQ_CHUNK)))
+      phase_b(std::true_type{}, c);
+    else
+      phase_b(std::false_type{}, c);
     if constexpr (kFused) {
       if (w == 0 && c + 1 < n_chunks) await_ready(c + 1, pend);  // T and P of chunk c + 1 load after the barrier
     }
