@@ -326,11 +326,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
     f32x4 uacc[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) uacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // (the record's fragments four pairs at a time, read before their products)
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int ti = p >> 1, kb = p & 1;
-      mma_bf16(uacc[ti], frag(sPT, p), of[kb]);
-      mma_bf16(uacc[ti], frag(sPT, 8 + p), of[kb]);
+    for (int p0 = 0; p0 < 8; p0 += 4) {
+      Fr ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ph[j] = frag(sPT, p0 + j);
+        pl[j] = frag(sPT, 8 + p0 + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of the products
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ti = (p0 + j) >> 1, kb = (p0 + j) & 1;
+        mma_bf16(uacc[ti], ph[j], of[kb]);
+        mma_bf16(uacc[ti], pl[j], of[kb]);
+      }
     }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -352,12 +363,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void chunk_bwd_dh_kernel(BwdArgs ar
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) yacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int ti = p >> 1, kb = p & 1;
-      const Fr th = frag(sTT, p);
-      mma_bf16(yacc[ti], th, uh[kb]);
-      mma_bf16(yacc[ti], th, ul[kb]);
-      mma_bf16(yacc[ti], frag(sTT, 8 + p), uh[kb]);
+    for (int p0 = 0; p0 < 8; p0 += 4) {
+      Fr th[4], tl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        th[j] = frag(sTT, p0 + j);
+        tl[j] = frag(sTT, 8 + p0 + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of the products
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ti = (p0 + j) >> 1, kb = (p0 + j) & 1;
+        mma_bf16(yacc[ti], th[j], uh[kb]);
+        mma_bf16(yacc[ti], th[j], ul[kb]);
+        mma_bf16(yacc[ti], tl[j], uh[kb]);
+      }
     }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) pend_y[ti] = yacc[ti];
