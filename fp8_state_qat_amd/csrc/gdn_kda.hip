@@ -113,19 +113,46 @@ __device__ __forceinline__ void produce_kda_records(const ChunkArgs& args, char*
   const bool home = xcd == (unsigned)x;
   const int M = NH > x ? (NH - x + 7) >> 3 : 0;
   const int64_t total = (int64_t)args.chunk_offs[args.N + 1] * M;
-  for (int64_t m = r; m < total; m += R) {
+  // item m: chunk m / M of the class's (m % M)-th pair; an item past its
+  // sequence's prefix is skipped (the same for the whole workgroup)
+  struct Item {
+    int j, h, t0, nv;
+  };
+  auto item_at = [&](int64_t m, Item& it) {
     const int c = (int)(m / M), nh = x + 8 * (int)(m % M);
-    const int n = nh / H, h = nh % H;
+    const int n = nh / H;
     const int seg0 = args.cu_seqlens[n];
     const int L = args.seq_lens ? args.seq_lens[n] : (args.cu_seqlens[n + 1] - seg0);
     const int P = args.prefix_lens ? args.prefix_lens[n] : L;
-    if (c * kChunk >= P) continue;  // the same for the whole workgroup
-    const int j = args.chunk_offs[n] + c;
+    if (c * kChunk >= P) return false;
+    it.j = args.chunk_offs[n] + c;
+    it.h = nh % H;
+    it.t0 = seg0 + c * kChunk;
+    it.nv = min(kChunk, P - c * kChunk);
+    return true;
+  };
+  auto next_item = [&](int64_t m, Item& it) {  // the first item at or after m, or total
+    while (m < total && !item_at(m, it)) m += R;
+    return m;
+  };
+  // The inputs of the next item are loaded into registers as soon as the
+  // current item's are staged in LDS, so that they land while it computes.
+  KdaRaw<DK, TIO> raw;
+  Item cur{}, nxt{};
+  int64_t m = next_item(r, cur);
+  if (m < total) kda_fetch<DK, TIO>(a, cur.h, cur.t0, cur.nv, tid, raw);
+  while (m < total) {
+    const int64_t mn = next_item(m + R, nxt);
     // a fresh copy of the lane index per item keeps the compiler from holding
     // the item's lane-dependent LDS addresses live across the whole loop
     int tid_i = tid;
     asm volatile("" : "+v"(tid_i));
-    kda_prep_item<DK, TIO, kW>(a, j, h, seg0 + c * kChunk, min(kChunk, P - c * kChunk), smem, tid_i);
+    kda_prep_item_from<DK, TIO, kW>(a, cur.j, cur.h, cur.nv, smem, tid_i, raw, [&] {
+      if (mn < total) kda_fetch<DK, TIO>(a, nxt.h, nxt.t0, nxt.nv, tid, raw);
+    });
+    const int j = cur.j, h = cur.h;
+    cur = nxt;
+    m = mn;
     wait_vmem();      // this wave's record stores are complete
     __syncthreads();  // ... in every wave; the LDS is free again
     if (tid == 0) {

@@ -628,13 +628,57 @@ __device__ __forceinline__ void load4f(const TIO* p, float (&x)[4]) {
   }
 }
 
+// A thread's share of one per-key-channel prep item's inputs, loaded from
+// HBM into registers: 16-byte pieces of k and q rows (rows past nv zero),
+// the gates of one channel over TPP consecutive tokens, one beta.
+template <int DK, typename TIO>
+struct KdaRaw {
+  static constexpr int EPS = 16 / (int)sizeof(TIO);
+  static constexpr int SPR = DK / EPS;                    // 16-byte pieces per row
+  static constexpr int NJ = 64 * SPR / kThreads;          // pieces per thread
+  static constexpr int NPART = kThreads / DK, TPP = 64 / NPART;  // token parts of the per-channel scan
+  static_assert(64 * SPR % kThreads == 0, "staging geometry");
+  uint4 kv[NJ], qv[NJ];
+  float gv[TPP];
+  float beta;
+};
+template <int DK, typename TIO>
+__device__ __forceinline__ void kda_fetch(const PrepArgs& a, int h, int t0, int nv, int tid, KdaRaw<DK, TIO>& x) {
+  using Raw = KdaRaw<DK, TIO>;
+  const int H = a.H;
+  const TIO* gk = reinterpret_cast<const TIO*>(a.k);
+  const TIO* gqv = reinterpret_cast<const TIO*>(a.q);
+#pragma unroll
+  for (int jj = 0; jj < Raw::NJ; ++jj) {
+    const int seg = tid + kThreads * jj;
+    const int r = seg / Raw::SPR, c0 = (seg % Raw::SPR) * Raw::EPS;
+    x.kv[jj] = make_uint4(0u, 0u, 0u, 0u);
+    x.qv[jj] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < nv) {
+      const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c0;
+      x.kv[jj] = *reinterpret_cast<const uint4*>(gk + off);
+      x.qv[jj] = *reinterpret_cast<const uint4*>(gqv + off);
+    }
+  }
+  x.beta = (tid < nv) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;  // used by tid < 64
+  const int d = tid % DK, part = tid / DK;
+#pragma unroll
+  for (int i = 0; i < Raw::TPP; ++i) {
+    const int r = part * Raw::TPP + i;
+    x.gv[i] = (r < nv) ? a.g[((int64_t)(t0 + r) * H + h) * DK + d] : 0.f;
+  }
+}
+
 // The records of chunk j (tokens t0 .. t0 + nv - 1), head h, for a
 // per-key-channel gate, on one workgroup of four waves (thread index tid)
-// with the LDS block smem (KdaPrepLds bytes).  Contains workgroup barriers.
-// On return this wave's record stores may still be in flight.
-template <int DK, typename TIO, bool kW = false>
-__device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, int t0, int nv, char* smem,
-                                              int tid) {
+// with the LDS block smem (KdaPrepLds bytes), from the inputs x that
+// kda_fetch loaded.  Once x is staged in LDS, next() runs (a caller may load
+// its next item into x there, so that those loads land during this item).
+// Contains workgroup barriers.  On return this wave's record stores (and
+// whatever next() issued) may still be in flight.
+template <int DK, typename TIO, bool kW, typename Next>
+__device__ __forceinline__ void kda_prep_item_from(const PrepArgs& a, int j, int h, int nv, char* smem, int tid,
+                                                   KdaRaw<DK, TIO>& x, Next&& next) {
   using Ls = KdaPrepLds<DK, TIO, kW>;
   constexpr bool kBF = sizeof(TIO) == 2;
   constexpr int LX = Ls::LX, LG = Ls::LG, L64 = kL64, NKB = DK / 32;
@@ -651,44 +695,29 @@ __device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, i
   const int w = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
 
   // ---- stage k and q (rows past nv are zero), beta, and the per-channel gate prefix
+  using Raw = KdaRaw<DK, TIO>;
+  constexpr int TPP = Raw::TPP;
   {
-    constexpr int EPS = 16 / (int)sizeof(TIO);
-    constexpr int SPR = DK / EPS;
-    const TIO* gk = reinterpret_cast<const TIO*>(a.k);
-    const TIO* gqv = reinterpret_cast<const TIO*>(a.q);
-    static_assert(64 * SPR % kThreads == 0, "staging geometry");
 #pragma unroll
-    for (int jj = 0; jj < 64 * SPR / kThreads; ++jj) {
+    for (int jj = 0; jj < Raw::NJ; ++jj) {
       const int seg = tid + kThreads * jj;
-      const int r = seg / SPR, c0 = (seg % SPR) * EPS;
-      uint4 kv = make_uint4(0u, 0u, 0u, 0u), qv = make_uint4(0u, 0u, 0u, 0u);
-      if (r < nv) {
-        const int64_t off = ((int64_t)(t0 + r) * H + h) * DK + c0;
-        kv = *reinterpret_cast<const uint4*>(gk + off);
-        qv = *reinterpret_cast<const uint4*>(gqv + off);
-      }
-      *reinterpret_cast<uint4*>(sK + r * LX + c0) = kv;
-      *reinterpret_cast<uint4*>(sQ + r * LX + c0) = qv;
+      const int r = seg / Raw::SPR, c0 = (seg % Raw::SPR) * Raw::EPS;
+      *reinterpret_cast<uint4*>(sK + r * LX + c0) = x.kv[jj];
+      *reinterpret_cast<uint4*>(sQ + r * LX + c0) = x.qv[jj];
     }
-    if (tid < 64) sBeta[tid] = (tid < nv) ? a.beta[(int64_t)(t0 + tid) * H + h] : 0.f;
+    if (tid < 64) sBeta[tid] = x.beta;
   }
-  constexpr int NPART = kThreads / DK, TPP = 64 / NPART;  // token parts of the per-channel scan
   {
     const int d = tid % DK, part = tid / DK;
-    float gv[TPP];  // all loads in flight before the scan
-#pragma unroll
-    for (int i = 0; i < TPP; ++i) {
-      const int r = part * TPP + i;
-      gv[i] = (r < nv) ? a.g[((int64_t)(t0 + r) * H + h) * DK + d] : 0.f;
-    }
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < TPP; ++i) {
-      run += gv[i];
+      run += x.gv[i];
       sG[(part * TPP + i) * LG + d] = run;
     }
     sTot[tid] = run;
   }
+  next();  // x is free
   __syncthreads();
   {
     const int d = tid % DK, part = tid / DK;
@@ -829,6 +858,15 @@ __device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, i
     store_w_record<DK>(a, j, h, wacc, reinterpret_cast<uint16_t*>(smem + Ls::oK),
                        reinterpret_cast<float*>(smem + Ls::oQ), tid, true);
   }
+}
+
+// One item from HBM to its records (kda_fetch, then kda_prep_item_from).
+template <int DK, typename TIO, bool kW = false>
+__device__ __forceinline__ void kda_prep_item(const PrepArgs& a, int j, int h, int t0, int nv, char* smem,
+                                              int tid) {
+  KdaRaw<DK, TIO> x;
+  kda_fetch<DK, TIO>(a, h, t0, nv, tid, x);
+  kda_prep_item_from<DK, TIO, kW>(a, j, h, nv, smem, tid, x, [] {});
 }
 
 // Fused launch, workgroups 0 .. n_prep - 1: the T and P records of every
