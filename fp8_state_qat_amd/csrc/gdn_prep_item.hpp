@@ -18,6 +18,8 @@
 // as a third record (codes and row scales, layout in gdn_launch.hpp).
 #pragma once
 
+#include <type_traits>
+
 #include "gdn_chunk_common.hpp"
 
 namespace gdn {
@@ -746,22 +748,50 @@ __device__ __forceinline__ void kda_prep_item_from(const PrepArgs& a, int j, int
     const int s = 16 * S + ln, r = 16 * R + ln;  // A-operand row s, B-operand column r of this lane
     f32x4 ca = {0.f, 0.f, 0.f, 0.f}, cp = {0.f, 0.f, 0.f, 0.f};
     float span = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float av[8], bk[8], bq[8];
+    // The LDS operands of k-block kb + 1 are read while block kb computes
+    // (two buffers), so that the reads' round trip is not spent between the
+    // blocks.
+    using Raw4 = typename std::conditional<sizeof(TIO) == 2, uint2, float4>::type;
+    struct KbIn {
+      float4 gs[2], gm[2], gr[2];
+      Raw4 ks[2], kr[2], qr[2];
+    };
+    auto load_kb = [&](const int kb, KbIn& in) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int c0 = 32 * kb + 16 * hh + 4 * gq;  // channels kperm(gq, 4 hh .. 4 hh + 3)
-        const float4 gs4 = *reinterpret_cast<const float4*>(sG + s * LG + c0);
-        const float4 gm4 = *reinterpret_cast<const float4*>(sG + m * LG + c0);
-        const float4 gr4 = *reinterpret_cast<const float4*>(sG + r * LG + c0);
-        const float gs[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-        const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w};
-        const float gr[4] = {gr4.x, gr4.y, gr4.z, gr4.w};
+        in.gs[hh] = *reinterpret_cast<const float4*>(sG + s * LG + c0);
+        in.gm[hh] = *reinterpret_cast<const float4*>(sG + m * LG + c0);
+        in.gr[hh] = *reinterpret_cast<const float4*>(sG + r * LG + c0);
+        in.ks[hh] = *reinterpret_cast<const Raw4*>(sK + s * LX + c0);
+        in.kr[hh] = *reinterpret_cast<const Raw4*>(sK + r * LX + c0);
+        in.qr[hh] = *reinterpret_cast<const Raw4*>(sQ + r * LX + c0);
+      }
+    };
+    auto unpack4 = [](const Raw4& u, float (&x)[4]) {
+      if constexpr (sizeof(TIO) == 2) {
+        x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+      } else {
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+      }
+    };
+    KbIn kin[2];
+    load_kb(0, kin[0]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (kb + 1 < NKB) load_kb(kb + 1, kin[(kb + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // those reads are issued before this block's arithmetic
+      const KbIn& in = kin[kb & 1];
+      float av[8], bk[8], bq[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float gs[4] = {in.gs[hh].x, in.gs[hh].y, in.gs[hh].z, in.gs[hh].w};
+        const float gm[4] = {in.gm[hh].x, in.gm[hh].y, in.gm[hh].z, in.gm[hh].w};
+        const float gr[4] = {in.gr[hh].x, in.gr[hh].y, in.gr[hh].z, in.gr[hh].w};
         float ks[4], kr[4], qr[4];
-        load4f(sK + s * LX + c0, ks);
-        load4f(sK + r * LX + c0, kr);
-        load4f(sQ + r * LX + c0, qr);
+        unpack4(in.ks[hh], ks);
+        unpack4(in.kr[hh], kr);
+        unpack4(in.qr[hh], qr);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           span = fmaxf(span, fmaxf(fabsf(gm[i] - gs[i]), fabsf(gr[i] - gm[i])));
