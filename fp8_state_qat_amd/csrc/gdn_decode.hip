@@ -119,10 +119,15 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     __syncthreads();  // s_o
   } else if (do_qdq) {
     amax = block_max(amax, red);  // its barriers also publish s_o
-    s = qdq_scale(amax);
-    const float r = 1.0f / s;
+    s = qdq_scale_f64(amax);
+    const double r = rcp_f64(s);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) qdq4(x[p], s, r);
+    for (int p = 0; p < NP; ++p) {
+      f32x4 v = {x[p].x, x[p].y, x[p].z, x[p].w};
+      float cv[4];
+      qdq4c_f64(v, cv, s, r);
+      x[p] = make_float4(v[0], v[1], v[2], v[3]);
+    }
   } else {
     __syncthreads();  // s_o
   }

@@ -97,6 +97,45 @@ __device__ __forceinline__ void qdq4c(f32x4& v, float (&cv)[4], float s, float r
   v = f32x4{a, b, c, d};
 }
 
+// The same codes from the quotients formed in fp64.  For fp32 x and s the
+// quotient x / s is never within 2^-49 (relative) of a rounding boundary of
+// fp32 without being on it, and it is never on one (a boundary has 25
+// significant bits, x * 2^k / s would need them); the fp64 product x * r with
+// r within 2^-52 of 1 / s is within 2^-51 of x / s, so its rounding to fp32
+// is the correctly rounded quotient: three instructions per value where the
+// fp32 corrections take five.
+__device__ __forceinline__ double rcp_f64(float s) {
+  const double d = s;
+  double r = __builtin_amdgcn_rcp(d);  // relative error below 2^-22
+  r = fma(r, fma(-d, r, 1.0), r);      // ... 2^-44
+  return fma(r, fma(-d, r, 1.0), r);   // ... 2^-52
+}
+__device__ __forceinline__ float div_rn_f64(float x, double r) { return (float)((double)x * r); }
+__device__ __forceinline__ void e4m3_codes4_f64(const f32x4& x, double r, float (&c)[4]) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn_f64(x[0], r), div_rn_f64(x[1], r), 0, false);
+  const int p = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn_f64(x[2], r), div_rn_f64(x[3], r), lo, true);
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(p, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(p, true);
+  c[0] = a[0];
+  c[1] = a[1];
+  c[2] = b[0];
+  c[3] = b[1];
+}
+// QDQ of four values through the fp64 quotients (r: 1 / s in fp64): x <- the
+// E4M3 value of x / s times s, with the sign of x; cv receives the codes.
+__device__ __forceinline__ void qdq4c_f64(f32x4& v, float (&cv)[4], float s, double r) {
+  e4m3_codes4_f64(v, r, cv);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = copysignf(cv[i] * s, v[i]);
+}
+// The tile scale RN(amax / 448) (1 when amax is 0) through fp64: amax / 448 =
+// amax / 7 / 64 is at least 2^-27 (relative) from any rounding boundary of
+// fp32, and the product with the fp64 value of 1/448 is within 2^-52 of it.
+__device__ __forceinline__ float qdq_scale_f64(float amax) {
+  const float s = (float)((double)amax * (1.0 / 448.0));
+  return (s > 0.0f) ? s : 1.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Reductions in a fixed order (the same tree on every call).
 // ---------------------------------------------------------------------------

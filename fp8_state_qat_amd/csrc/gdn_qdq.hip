@@ -33,14 +33,16 @@ __global__ __launch_bounds__(kThreads) void state_qdq_kernel(const float* in,
   for (int j = 0; j < V4; ++j)
     amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[j].x), fabsf(x[j].y)), fmaxf(fabsf(x[j].z), fabsf(x[j].w))));
   amax = block_max(amax, red);
-  const float s = qdq_scale(amax);
-  const float r = 1.0f / s;
+  const float s = qdq_scale_f64(amax);
+  const double r = rcp_f64(s);
 #pragma unroll
   for (int j = 0; j < V4; ++j) {
     int idx = threadIdx.x + kThreads * j;
     if (idx < n4) {
-      qdq4(x[j], s, r);
-      st_stream(dst + idx, x[j]);
+      f32x4 v = {x[j].x, x[j].y, x[j].z, x[j].w};
+      float cv[4];
+      qdq4c_f64(v, cv, s, r);
+      st_stream(dst + idx, make_float4(v[0], v[1], v[2], v[3]));
     }
   }
   if (scales != nullptr && threadIdx.x == 0) scales[tile] = s;
