@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const float bm = lane8_max_dpp(fmaxf(fmaxf(fabsf(x[p].x), fabsf(x[p].y)), fmaxf(fabsf(x[p].z), fabsf(x[p].w))));
-      const float sb = int8_scale(bm);
-      qdq_int8_4(x[p], sb, 1.0f / sb);
+      const float sb = int8_scale_f64(bm);
+      qdq_int8_4_f64(x[p], sb);
       if (scales != nullptr && (c4 & 7) == 0)
         scales[(nh * dv + kTileRows * vt + rr + RPP * p) * (DK / 32) + (c4 >> 3)] = sb;
     }

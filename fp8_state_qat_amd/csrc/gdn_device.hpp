@@ -131,6 +131,11 @@ __device__ __forceinline__ void qdq4c_f64(f32x4& v, float (&cv)[4], float s, dou
 // The tile scale RN(amax / 448) (1 when amax is 0) through fp64: amax / 448 =
 // amax / 7 / 64 is at least 2^-27 (relative) from any rounding boundary of
 // fp32, and the product with the fp64 value of 1/448 is within 2^-52 of it.
+// Where the quotient is subnormal it is either exactly a tie of fp32, which
+// has few significant bits, so the fp64 product rounds onto it and the
+// conversion breaks it to even as the division does, or at least 2^-33
+// (relative) away from one (checked against the division for every amax of
+// six binades down to the smallest subnormal).
 __device__ __forceinline__ float qdq_scale_f64(float amax) {
   const float s = (float)((double)amax * (1.0 / 448.0));
   return (s > 0.0f) ? s : 1.0f;
@@ -176,6 +181,23 @@ __device__ __forceinline__ void qdq_int8_4(float4& v, float s, float r) {
   v.y = qdq_int8_1(v.y, s, r);
   v.z = qdq_int8_1(v.z, s, r);
   v.w = qdq_int8_1(v.w, s, r);
+}
+// The same through fp64: the block scale fl32(amax * fl64(1/127)) equals
+// fl32(amax / 127) (a 24-bit significand over 127 is never on an fp32
+// rounding boundary and at least 2^-32 (relative) away from one; subnormal
+// quotients as in qdq_scale_f64), and each quotient is the correctly rounded
+// one as in qdq4c_f64.
+__device__ __forceinline__ float int8_scale_f64(float amax) {
+  const float s = (float)((double)amax * (1.0 / 127.0));
+  return (s > 0.0f) ? s : 1.0f;
+}
+__device__ __forceinline__ void qdq_int8_4_f64(float4& v, float s) {
+  const double r = rcp_f64(s);
+  auto one = [&](float x) { return fminf(fmaxf(__builtin_rintf(div_rn_f64(x, r)), -127.0f), 127.0f) * s; };
+  v.x = one(v.x);
+  v.y = one(v.y);
+  v.z = one(v.z);
+  v.w = one(v.w);
 }
 
 // Max over each row of 16 lanes; every lane of the row receives it.

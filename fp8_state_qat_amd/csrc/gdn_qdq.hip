@@ -56,8 +56,8 @@ __global__ __launch_bounds__(kThreads) void state_qdq_int8_kernel(const float* i
                                                                  float* __restrict__ scales, int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // n4 is a multiple of 8 and of the block
   float4 x = ld_stream(reinterpret_cast<const float4*>(in) + i);
-  const float s = int8_scale(lane8_max_dpp(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)))));
-  qdq_int8_4(x, s, 1.0f / s);
+  const float s = int8_scale_f64(lane8_max_dpp(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)))));
+  qdq_int8_4_f64(x, s);
   st_stream(reinterpret_cast<float4*>(out) + i, x);
   if (scales != nullptr && (threadIdx.x & 7) == 0) scales[i >> 3] = s;
 }

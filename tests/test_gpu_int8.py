@@ -56,6 +56,28 @@ def test_state_qdq_int8_bit_exact(dv, dk):
     assert np.all(codes[0, :, 1:] % 2 == 0)
 
 
+def test_state_qdq_int8_subnormal_scales_bit_exact():
+    """Blocks whose amax / 127 is a subnormal fp32 number (amax of random
+    significands between 2^-135 and 2^-119, some of them subnormal
+    themselves): the device's block scales and values equal the oracle's
+    IEEE division bit for bit.  (amax / 127 cannot be a tie there: that needs
+    an odd multiple of 127 times 2^-150, which fp32 cannot hold.)"""
+    rng = np.random.default_rng(78)
+    n, dv, dk = 4, 64, 128
+    amax = (rng.uniform(1.0, 2.0, size=(n, dv, dk // 32)) *
+            np.exp2(rng.integers(-135, -119, size=(n, dv, dk // 32)))).astype(np.float32)
+    x = (rng.uniform(-1.0, 1.0, size=(n, dv, dk // 32, 32)) * amax[..., None].astype(np.float64)).astype(np.float32)
+    x[..., 0] = amax
+    x = x.reshape(n, dv, dk)
+    want, sc, _ = orc.qdq_int8_blocks(x)
+    assert np.all(sc.reshape(amax.shape) == amax / np.float32(127.0))
+    assert np.all(sc < np.float32(2.0 ** -126))
+    out, scales = api.state_qdq_int8(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), sc.view(np.uint32))
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
 def _half_integer_distance(y):
     a = np.abs(np.asarray(y, np.float64))
     return np.abs(a - (np.floor(a) + 0.5)) / 127.0

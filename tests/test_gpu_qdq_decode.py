@@ -62,6 +62,29 @@ def test_state_qdq_many_scales_bit_exact():
     np.testing.assert_array_equal(scales.cpu().numpy().ravel(), sc.ravel())
 
 
+def test_state_qdq_subnormal_scale_ties_bit_exact():
+    """Tiles whose amax / 448 is a subnormal fp32 number lying exactly on a
+    rounding tie (amax = 7 (2k + 1) 2^-144, so amax / 448 = (k + 1/2) 2^-149):
+    the device's scale and codes equal the oracle's IEEE division (ties to
+    even) bit for bit."""
+    rng = np.random.default_rng(77)
+    n = 256
+    k = rng.integers(0, 1 << 20, n)
+    amax = (7.0 * (2 * k + 1) * 2.0 ** -144).astype(np.float32)
+    assert np.all(amax.astype(np.float64) == 7.0 * (2 * k + 1) * 2.0 ** -144)
+    x = (rng.uniform(-1.0, 1.0, size=(n, 64 * 128)) * amax[:, None].astype(np.float64)).astype(np.float32)
+    x[:, 0] = amax
+    x = x.reshape(n, 64, 128)
+    want, sc, _ = orc.qdq_states(x)
+    assert np.all(sc.ravel() == (amax / np.float32(448.0)))
+    out, scales = api.state_qdq(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales.cpu().numpy().ravel().view(np.uint32), sc.ravel().view(np.uint32))
+    got = out.cpu().numpy()
+    bad = np.flatnonzero(got.view(np.uint32).ravel() != want.view(np.uint32).ravel())
+    assert bad.size == 0, (bad.size, x.ravel()[bad[:4]], got.ravel()[bad[:4]], want.ravel()[bad[:4]])
+
+
 def test_state_qdq_in_place_and_already_e4m3():
     rng = np.random.default_rng(1)
     grid = orc.e4m3_decode(np.arange(127, dtype=np.uint8))
